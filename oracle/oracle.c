@@ -1,0 +1,398 @@
+/*
+ * Lightning attention CPU oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py
+ * may load this library.  The product path (the HIP library and its Python
+ * binding) never calls it and shares no code with it.
+ *
+ * What it computes (causal linear attention with a per-head scalar decay,
+ * no normalisation, no activation, no gate):
+ *
+ *   MiniMax-01 technical report (full Chinese translation, blog.csdn.net),
+ *   section 2.2.1 "Lightning Attention":
+ *     - the causal left product (eq. 4): O = [(Q K^T) (.) M] V with
+ *       M[t][s] = 1 when t >= s, else 0 (the diagonal is included);
+ *     - the right-product recurrence (eq. 5): kv_t = kv_{t-1} + k_t^T v_t,
+ *       o_t = q_t kv_t, with kv_0 = 0;
+ *     - normalisation, SiLU and the gate are deliberately left out of the
+ *       derivation there, so they are left out here too.
+ *   Section 2.2.4 (eq. 12) gives lightning attention's recurrent (RNN)
+ *   form; section 3.2.2 (Fig. 12) initialises a diagonal decay matrix; the
+ *   K3 reading notes (cutenote.app, "solution 1: add a position decay term")
+ *   name the RetNet-style decay.  With a per-head decay lambda these read
+ *
+ *     S_t = lambda * S_{t-1} + k_t^T v_t          (S_t is d x d, S_{-1} = S_init)
+ *     o_t = q_t S_t                               (o_t[j] = sum_i q_t[i] S_t[i][j])
+ *
+ *   and, unrolled (the decayed left product),
+ *
+ *     o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s + lambda^(t+1) q_t S_init.
+ *
+ * Arithmetic is IEEE double throughout.  Inputs arrive as float32 arrays: the
+ * exact values handed to the GPU (bf16 values widen to float32 exactly); the
+ * decay arrives as the float32 lambda the GPU gets, widened to double.
+ *
+ * Layouts (row-major, d fastest):
+ *   fixed length : q, k, v, out  [B][H][N][d];  states [B][H][d][d]
+ *   packed varlen: q, k, v, out  [H][total][d]; sequence j occupies tokens
+ *                  cu[j] .. cu[j+1]-1 of every head; states [S][H][d][d]
+ *   states are S[i][j] with i the key feature and j the value feature.
+ *
+ * Every function is threaded over independent (sequence, head) units with
+ * pthreads; nthreads <= 0 means "all CPUs this process may run on".
+ */
+#define _GNU_SOURCE
+#include <math.h>
+#include <pthread.h>
+#include <sched.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ---------------------------------------------------------------- threads */
+
+typedef void (*unit_fn)(void *ctx, int64_t unit);
+
+typedef struct {
+  unit_fn fn;
+  void *ctx;
+  int64_t n_units;
+  int64_t next;
+  pthread_mutex_t lock;
+} pool_t;
+
+static void *pool_worker(void *arg) {
+  pool_t *p = (pool_t *)arg;
+  for (;;) {
+    pthread_mutex_lock(&p->lock);
+    int64_t u = p->next++;
+    pthread_mutex_unlock(&p->lock);
+    if (u >= p->n_units) break;
+    p->fn(p->ctx, u);
+  }
+  return NULL;
+}
+
+int oracle_default_threads(void) {
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+    int c = CPU_COUNT(&set);
+    if (c > 0) return c;
+  }
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+/* Runs fn(ctx, u) for u in [0, n_units); returns the thread count used. */
+static int run_units(unit_fn fn, void *ctx, int64_t n_units, int nthreads) {
+  if (nthreads <= 0) nthreads = oracle_default_threads();
+  if ((int64_t)nthreads > n_units) nthreads = (int)(n_units > 0 ? n_units : 1);
+  pool_t p;
+  p.fn = fn;
+  p.ctx = ctx;
+  p.n_units = n_units;
+  p.next = 0;
+  pthread_mutex_init(&p.lock, NULL);
+  if (nthreads <= 1) {
+    pool_worker(&p);
+  } else {
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i)
+      if (pthread_create(&tid[i], NULL, pool_worker, &p) == 0) ++started;
+    if (started == 0) pool_worker(&p);
+    for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+    free(tid);
+    if (started > 0) nthreads = started; else nthreads = 1;
+  }
+  pthread_mutex_destroy(&p.lock);
+  return nthreads;
+}
+
+/* ------------------------------------------------- one sequence, one head */
+
+/* ORACLE_PLANT selects a deliberately wrong recurrence; it is only ever set
+ * by the CPU test that checks the oracle's pins catch such mistakes.
+ * 0 = correct; 1 = decay applied after the add; 2 = transposed outer product;
+ * 3 = output read before the update; 4 = decay dropped; 5 = output contracts
+ * the state's other index. */
+#ifndef ORACLE_PLANT
+#define ORACLE_PLANT 0
+#endif
+
+/*
+ * The recurrence (eq. 5 with the per-head decay) over n tokens of one head.
+ * q, k, v point at row 0 of the sequence ([n][d], d fastest).  S (d*d) holds
+ * the state entering the sequence and is left holding the state after its
+ * last token.  out ([n][d]) may be NULL when only the state is wanted.
+ */
+static void recur_one(const float *q, const float *k, const float *v, double lam, int64_t n,
+                      int d, double *S, double *out, double *orow) {
+  for (int64_t t = 0; t < n; ++t) {
+    const float *kt = k + t * d, *vt = v + t * d, *qt = q + t * d;
+    /* S_t = lambda S_{t-1} + k_t^T v_t */
+    if (ORACLE_PLANT == 3 && out) {
+      for (int j = 0; j < d; ++j) orow[j] = 0.0;
+      for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) orow[j] += (double)qt[i] * S[(int64_t)i * d + j];
+    }
+    for (int i = 0; i < d; ++i) {
+      double ki = (double)kt[i];
+      double *Si = S + (int64_t)i * d;
+      for (int j = 0; j < d; ++j) {
+        if (ORACLE_PLANT == 1) Si[j] = lam * (Si[j] + ki * (double)vt[j]);
+        else if (ORACLE_PLANT == 2) Si[j] = lam * Si[j] + (double)kt[j] * (double)vt[i];
+        else if (ORACLE_PLANT == 4) Si[j] = Si[j] + ki * (double)vt[j];
+        else Si[j] = lam * Si[j] + ki * (double)vt[j];
+      }
+    }
+    if (!out) continue;
+    /* o_t = q_t S_t */
+    if (ORACLE_PLANT != 3) {
+      for (int j = 0; j < d; ++j) orow[j] = 0.0;
+      for (int i = 0; i < d; ++i) {
+        double qi = (double)qt[i];
+        const double *Si = S + (int64_t)i * d;
+        for (int j = 0; j < d; ++j) {
+          if (ORACLE_PLANT == 5) orow[j] += qi * S[(int64_t)j * d + i];
+          else orow[j] += qi * Si[j];
+        }
+      }
+    }
+    memcpy(out + t * d, orow, sizeof(double) * (size_t)d);
+  }
+}
+
+/* ------------------------------------------------------ fixed-length fwd */
+
+typedef struct {
+  const float *q, *k, *v, *decay;
+  int B, H, d;
+  int64_t N;
+  const double *init;
+  double *out, *fin;
+} fwd_ctx;
+
+static void fwd_unit(void *vctx, int64_t u) {
+  fwd_ctx *c = (fwd_ctx *)vctx;
+  int d = c->d;
+  int h = (int)(u % c->H);
+  int64_t base = u * c->N * d;
+  int64_t dd = (int64_t)d * d;
+  double *S = (double *)malloc(sizeof(double) * (size_t)dd);
+  double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+  if (c->init) memcpy(S, c->init + u * dd, sizeof(double) * (size_t)dd);
+  else memset(S, 0, sizeof(double) * (size_t)dd);
+  recur_one(c->q + base, c->k + base, c->v + base, (double)c->decay[h], c->N, d, S,
+            c->out ? c->out + base : NULL, orow);
+  if (c->fin) memcpy(c->fin + u * dd, S, sizeof(double) * (size_t)dd);
+  free(orow);
+  free(S);
+}
+
+/* Prefill over [B][H][N][d]; init may be NULL (zero state); out or fin may
+ * be NULL.  Returns the number of threads used. */
+int oracle_fwd_f64(const float *q, const float *k, const float *v, const float *decay, int B,
+                   int H, int64_t N, int d, const double *init, double *out, double *fin,
+                   int nthreads) {
+  fwd_ctx c = {q, k, v, decay, B, H, d, N, init, out, fin};
+  return run_units(fwd_unit, &c, (int64_t)B * H, nthreads);
+}
+
+/* ------------------------------------------------------------ varlen fwd */
+
+typedef struct {
+  const float *q, *k, *v, *decay;
+  const int32_t *cu;
+  int S, H, d;
+  int64_t total;
+  const double *init;
+  double *out, *fin;
+} var_ctx;
+
+static void var_unit(void *vctx, int64_t u) {
+  var_ctx *c = (var_ctx *)vctx;
+  int d = c->d;
+  int64_t j = u / c->H;
+  int h = (int)(u % c->H);
+  int64_t t0 = c->cu[j], n = (int64_t)c->cu[j + 1] - c->cu[j];
+  int64_t base = ((int64_t)h * c->total + t0) * d;
+  int64_t dd = (int64_t)d * d;
+  int64_t sidx = (j * c->H + h) * dd;
+  double *S = (double *)malloc(sizeof(double) * (size_t)dd);
+  double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+  if (c->init) memcpy(S, c->init + sidx, sizeof(double) * (size_t)dd);
+  else memset(S, 0, sizeof(double) * (size_t)dd);
+  recur_one(c->q + base, c->k + base, c->v + base, (double)c->decay[h], n, d, S,
+            c->out ? c->out + base : NULL, orow);
+  if (c->fin) memcpy(c->fin + sidx, S, sizeof(double) * (size_t)dd);
+  free(orow);
+  free(S);
+}
+
+/* Packed variable-length prefill: the state starts afresh (from init[j] or
+ * zero) at every sequence start, as data packing requires (MiniMax-01 report,
+ * section 3.2 "data packing"; section 3.2.2 varlen for LASP+). */
+int oracle_fwd_varlen_f64(const float *q, const float *k, const float *v, const float *decay,
+                          const int32_t *cu_seqlens, int num_seqs, int H, int64_t total, int d,
+                          const double *init, double *out, double *fin, int nthreads) {
+  var_ctx c = {q, k, v, decay, cu_seqlens, num_seqs, H, d, total, init, out, fin};
+  return run_units(var_unit, &c, (int64_t)num_seqs * H, nthreads);
+}
+
+/* ---------------------------------------------------------------- decode */
+
+typedef struct {
+  const float *q, *k, *v, *decay;
+  int H, d;
+  double *state, *out;
+} dec_ctx;
+
+static void dec_unit(void *vctx, int64_t u) {
+  dec_ctx *c = (dec_ctx *)vctx;
+  int d = c->d;
+  int h = (int)(u % c->H);
+  double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+  recur_one(c->q + u * d, c->k + u * d, c->v + u * d, (double)c->decay[h], 1, d,
+            c->state + u * (int64_t)d * d, c->out + u * d, orow);
+  free(orow);
+}
+
+/* One recurrent (RNN-form) step for [B][H] heads: state <- lambda state +
+ * k^T v, then out = q state (the output reads the updated state, so decoding
+ * token t from the state after t-1 tokens reproduces prefill row t).
+ * state is [B][H][d][d] double, updated in place; q, k, v, out are [B][H][d]. */
+int oracle_decode_f64(const float *q, const float *k, const float *v, const float *decay, int B,
+                      int H, int d, double *state, double *out, int nthreads) {
+  dec_ctx c = {q, k, v, decay, H, d, state, out};
+  return run_units(dec_unit, &c, (int64_t)B * H, nthreads);
+}
+
+/* ------------------------------------------------ decayed left product */
+
+typedef struct {
+  const float *q, *k, *v, *decay;
+  int H, d;
+  int64_t N;
+  const double *init;
+  double *out, *fin;
+} bf_ctx;
+
+static void bf_unit(void *vctx, int64_t u) {
+  bf_ctx *c = (bf_ctx *)vctx;
+  int d = c->d;
+  int64_t N = c->N;
+  double lam = (double)c->decay[u % c->H];
+  int64_t base = u * N * d, dd = (int64_t)d * d;
+  const float *q = c->q + base, *k = c->k + base, *v = c->v + base;
+  const double *S0 = c->init ? c->init + u * dd : NULL;
+  for (int64_t t = 0; t < N; ++t) {
+    double *o = c->out + base + t * d;
+    for (int j = 0; j < d; ++j) o[j] = 0.0;
+    /* masked, decayed scores: [(Q K^T) (.) M_lambda]_{t,s} for s <= t */
+    for (int64_t s = 0; s <= t; ++s) {
+      double score = 0.0;
+      for (int i = 0; i < d; ++i) score += (double)q[t * d + i] * (double)k[s * d + i];
+      score *= pow(lam, (double)(t - s));
+      for (int j = 0; j < d; ++j) o[j] += score * (double)v[s * d + j];
+    }
+    if (S0) {
+      double a = pow(lam, (double)(t + 1));
+      for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) o[j] += a * (double)q[t * d + i] * S0[i * d + j];
+    }
+  }
+  if (c->fin) {
+    double *S = c->fin + u * dd;
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        double acc = S0 ? pow(lam, (double)N) * S0[i * d + j] : 0.0;
+        for (int64_t s = 0; s < N; ++s)
+          acc += pow(lam, (double)(N - 1 - s)) * (double)k[s * d + i] * (double)v[s * d + j];
+        S[i * d + j] = acc;
+      }
+  }
+}
+
+/* The left-product form (eq. 4 with the decay folded into the mask):
+ * O(N^2 d) per head, for small inputs only.  Same layout as oracle_fwd_f64;
+ * out must not be NULL. */
+int oracle_bruteforce_f64(const float *q, const float *k, const float *v, const float *decay,
+                          int B, int H, int64_t N, int d, const double *init, double *out,
+                          double *fin, int nthreads) {
+  bf_ctx c = {q, k, v, decay, H, d, N, init, out, fin};
+  return run_units(bf_unit, &c, (int64_t)B * H, nthreads);
+}
+
+/* --------------------------------------------- sampled outputs, large N */
+
+typedef struct {
+  const float *q, *k, *v;
+  double lam;
+  int d;
+  const int64_t *rows;
+  const double *init;
+  double *out;
+} row_ctx;
+
+static void row_unit(void *vctx, int64_t u) {
+  row_ctx *c = (row_ctx *)vctx;
+  int d = c->d;
+  int64_t t = c->rows[u];
+  const float *qt = c->q + t * d;
+  double *o = c->out + u * d;
+  for (int j = 0; j < d; ++j) o[j] = 0.0;
+  for (int64_t s = 0; s <= t; ++s) {
+    double score = 0.0;
+    for (int i = 0; i < d; ++i) score += (double)qt[i] * (double)c->k[s * d + i];
+    score *= pow(c->lam, (double)(t - s));
+    for (int j = 0; j < d; ++j) o[j] += score * (double)c->v[s * d + j];
+  }
+  if (c->init) {
+    double a = pow(c->lam, (double)(t + 1));
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) o[j] += a * (double)qt[i] * c->init[i * d + j];
+  }
+}
+
+/* Output rows rows[0..n_rows) of one head, each from the decayed left
+ * product directly (O(t d) per row), so single rows of very long sequences
+ * can be checked.  q, k, v point at row 0 of the head ([N][d]); init is the
+ * head's d x d initial state or NULL; out is [n_rows][d]. */
+int oracle_rows_f64(const float *q, const float *k, const float *v, float decay, int d,
+                    const int64_t *rows, int64_t n_rows, const double *init, double *out,
+                    int nthreads) {
+  row_ctx c = {q, k, v, (double)decay, d, rows, init, out};
+  return run_units(row_unit, &c, n_rows, nthreads);
+}
+
+typedef struct {
+  const float *k, *v;
+  double lam;
+  int d;
+  int64_t N;
+  const int32_t *ij;
+  const double *init;
+  double *out;
+} ent_ctx;
+
+static void ent_unit(void *vctx, int64_t u) {
+  ent_ctx *c = (ent_ctx *)vctx;
+  int d = c->d, i = c->ij[2 * u], j = c->ij[2 * u + 1];
+  double acc = c->init ? pow(c->lam, (double)c->N) * c->init[i * d + j] : 0.0;
+  for (int64_t s = 0; s < c->N; ++s)
+    acc += pow(c->lam, (double)(c->N - 1 - s)) * (double)c->k[s * d + i] * (double)c->v[s * d + j];
+  c->out[u] = acc;
+}
+
+/* Entries (i, j) of one head's state after N tokens, each as the decayed sum
+ * S[i][j] = lambda^N S_init[i][j] + sum_s lambda^(N-1-s) k_s[i] v_s[j]
+ * (O(N) per entry).  ij holds n pairs (i, j); out is [n]. */
+int oracle_state_entries_f64(const float *k, const float *v, float decay, int d, int64_t N,
+                             const int32_t *ij, int64_t n, const double *init, double *out,
+                             int nthreads) {
+  ent_ctx c = {k, v, (double)decay, d, N, ij, init, out};
+  return run_units(ent_unit, &c, n, nthreads);
+}

@@ -1,0 +1,279 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+The pages (MiniMax-01 report, section 2.2.1 and 2.2.4; K3 reading notes,
+"position decay term" and "CP for linear attention") print no worked example
+and no output values, so the pins are closed forms, special cases that reduce
+to a textbook computation done here with numpy, exact rational arithmetic on
+tiny inputs, and the invariants the pages state (block split, chunk split,
+initial state, recurrent decode form, packing).  test_planted_mistakes_are_caught
+builds deliberately broken oracles and checks these pins reject every one.
+"""
+import math
+import os
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from linear_attention_lightning_amd import inputs
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.abs(b).max()
+    return float(np.abs(a - b).max() / (den if den > 0 else 1.0))
+
+
+def rand_qkv(B, H, N, d, seed):
+    q, k, v = inputs.host_qkv((B, H, N, d), seed, dtype="fp32")
+    return q, k, v
+
+
+# ---------------------------------------------------------------- pins
+
+
+@pytest.mark.parametrize("N,d,lams", [
+    (1, 4, [0.5]), (7, 1, [0.9]), (33, 2, [1.0, 0.25]), (64, 8, [0.996, 0.4]),
+    (97, 16, [0.9394, 1e-3]),
+])
+@pytest.mark.parametrize("with_init", [False, True])
+def test_recurrence_equals_decayed_left_product(N, d, lams, with_init):
+    """Eq. 5 (recurrence) against eq. 4 (masked left product), both with the
+    decay lambda^(t-s), on small random inputs."""
+    H = len(lams)
+    q, k, v = rand_qkv(2, H, N, d, seed=11 + N + d)
+    lam = np.asarray(lams, np.float32)
+    init = inputs.host_state((2, H, d, d), 5).astype(np.float64) if with_init else None
+    o, f, _ = oracle.fwd(q, k, v, lam, init=init)
+    ob, fb = oracle.bruteforce(q, k, v, lam, init=init)
+    assert rel_err(o, ob) < 1e-12
+    assert rel_err(f, fb) < 1e-12
+
+
+def test_lambda_one_is_plain_causal_linear_attention():
+    """lambda = 1 gives [(Q K^T) (.) M] V with M lower triangular including
+    the diagonal (eq. 4), computed here with numpy matrix products."""
+    B, H, N, d = 2, 3, 80, 12
+    q, k, v = rand_qkv(B, H, N, d, seed=3)
+    lam = np.ones(H, np.float32)
+    o, f, _ = oracle.fwd(q, k, v, lam)
+    Q, K, V = (x.astype(np.float64) for x in (q, k, v))
+    M = np.tril(np.ones((N, N)))
+    ref = ((Q @ K.transpose(0, 1, 3, 2)) * M) @ V
+    assert rel_err(o, ref) < 1e-12
+    assert rel_err(f, K.transpose(0, 1, 3, 2) @ V) < 1e-12
+
+
+def test_tiny_decay_keeps_only_the_diagonal():
+    """lambda -> 0: o_t = (q_t . k_t) v_t and S = k_{N-1}^T v_{N-1}."""
+    B, H, N, d = 1, 2, 40, 8
+    q, k, v = rand_qkv(B, H, N, d, seed=4)
+    lam = np.full(H, 1e-20, np.float32)
+    o, f, _ = oracle.fwd(q, k, v, lam)
+    Q, K, V = (x.astype(np.float64) for x in (q, k, v))
+    ref = np.sum(Q * K, axis=-1, keepdims=True) * V
+    assert rel_err(o, ref) < 1e-12
+    last = K[:, :, -1, :, None] * V[:, :, -1, None, :]
+    assert rel_err(f, last) < 1e-12
+
+
+def test_single_token_closed_form():
+    """N = 1: o = lambda q S_init + (q . k) v and S = lambda S_init + k^T v."""
+    d, H = 16, 2
+    q, k, v = rand_qkv(1, H, 1, d, seed=8)
+    lam = np.asarray([0.75, 0.3], np.float32)
+    S0 = inputs.host_state((1, H, d, d), 9).astype(np.float64)
+    o, f, _ = oracle.fwd(q, k, v, lam, init=S0)
+    for h in range(H):
+        qh, kh, vh = (x[0, h, 0].astype(np.float64) for x in (q, k, v))
+        L = float(lam[h])
+        assert rel_err(o[0, h, 0], L * qh @ S0[0, h] + (qh @ kh) * vh) < 1e-13
+        assert rel_err(f[0, h], L * S0[0, h] + np.outer(kh, vh)) < 1e-13
+
+
+def test_geometric_series_with_unit_vectors():
+    """q_t = e_a, k_t = e_b, v_t = e_c for every t: the state is
+    c_t e_b e_c^T with c_t = (1 - lambda^(t+1)) / (1 - lambda), so o_t = c_t e_c
+    when a = b and o_t = 0 otherwise.  Catches a transposed outer product,
+    a transposed contraction and a wrong decay exponent."""
+    N, d = 50, 4
+    for lamv in (0.5, 0.9, 0.999):
+        lam = np.asarray([lamv], np.float32)
+        L = float(lam[0])
+        e = np.eye(d, dtype=np.float32)
+        for a, b, c in ((1, 1, 2), (0, 1, 2)):
+            q = np.broadcast_to(e[a], (1, 1, N, d)).copy()
+            k = np.broadcast_to(e[b], (1, 1, N, d)).copy()
+            v = np.broadcast_to(e[c], (1, 1, N, d)).copy()
+            o, f, _ = oracle.fwd(q, k, v, lam)
+            ct = np.array([(1 - L ** (t + 1)) / (1 - L) for t in range(N)])
+            ref = np.zeros((N, d))
+            if a == b:
+                ref[:, c] = ct
+            np.testing.assert_allclose(o[0, 0], ref, rtol=1e-13, atol=1e-13)
+            Sref = np.zeros((d, d))
+            Sref[b, c] = ct[-1]
+            np.testing.assert_allclose(f[0, 0], Sref, rtol=1e-13, atol=1e-13)
+
+
+def test_exact_rational_arithmetic():
+    """Small integer inputs and lambda = 3/4 (exact in binary): every output
+    is a dyadic rational that double arithmetic reproduces closely; computed
+    here with Python Fractions from the decayed sum."""
+    rng = np.random.default_rng(12)
+    N, d = 12, 3
+    q = rng.integers(-3, 4, (1, 1, N, d)).astype(np.float32)
+    k = rng.integers(-3, 4, (1, 1, N, d)).astype(np.float32)
+    v = rng.integers(-3, 4, (1, 1, N, d)).astype(np.float32)
+    lam = Fraction(3, 4)
+    o, f, _ = oracle.fwd(q, k, v, np.asarray([0.75], np.float32))
+    for t in range(N):
+        for j in range(d):
+            acc = Fraction(0)
+            for s in range(t + 1):
+                dot = sum(Fraction(int(q[0, 0, t, i])) * int(k[0, 0, s, i]) for i in range(d))
+                acc += lam ** (t - s) * dot * int(v[0, 0, s, j])
+            assert abs(Fraction(o[0, 0, t, j]) - acc) <= abs(acc) * Fraction(1, 2 ** 48) + Fraction(1, 2 ** 60)
+
+
+def test_split_run_with_initial_state():
+    """A run over tokens [0, N) equals a run over [0, m) followed by a run over
+    [m, N) started from the first run's final state (block expansion,
+    section 2.2.1; kv_0 = 0 only for the first block)."""
+    B, H, N, d = 2, 2, 90, 8
+    q, k, v = rand_qkv(B, H, N, d, seed=21)
+    lam = np.asarray([0.97, 0.6], np.float32)
+    o, f, _ = oracle.fwd(q, k, v, lam)
+    for m in (1, 37, 64, 89):
+        o1, f1, _ = oracle.fwd(q[:, :, :m], k[:, :, :m], v[:, :, :m], lam)
+        o2, f2, _ = oracle.fwd(q[:, :, m:], k[:, :, m:], v[:, :, m:], lam, init=f1)
+        assert rel_err(np.concatenate([o1, o2], axis=2), o) < 1e-12
+        assert rel_err(f2, f) < 1e-12
+
+
+def test_decode_steps_equal_prefill_rows():
+    """Recurrent (RNN-form, eq. 12) decode of token t from the state after
+    t tokens reproduces prefill row t; the final states agree."""
+    B, H, N, d = 2, 3, 20, 8
+    q, k, v = rand_qkv(B, H, N, d, seed=31)
+    lam = inputs.decay_schedule(H)
+    S0 = inputs.host_state((B, H, d, d), 32).astype(np.float64)
+    o, f, _ = oracle.fwd(q, k, v, lam, init=S0)
+    S = S0.copy()
+    for t in range(N):
+        ot, _ = oracle.decode(q[:, :, t], k[:, :, t], v[:, :, t], lam, S)
+        assert rel_err(ot, o[:, :, t]) < 1e-12
+    assert rel_err(S, f) < 1e-12
+
+
+def test_varlen_equals_independent_sequences():
+    """Packing sequences end to end (section 3.2) with the state reset at each
+    boundary equals running every sequence on its own; zero-length sequences
+    return their initial state."""
+    H, d = 2, 8
+    lens = [5, 0, 17, 1, 40, 0]
+    cu = inputs.cu_seqlens(lens)
+    total = int(cu[-1])
+    q, k, v = inputs.host_qkv((H, total, d), 41, dtype="fp32")
+    lam = np.asarray([0.9, 0.5], np.float32)
+    init = inputs.host_state((len(lens), H, d, d), 42).astype(np.float64)
+    o, f, _ = oracle.fwd_varlen(q, k, v, lam, cu, init=init)
+    for j, n in enumerate(lens):
+        a, b = int(cu[j]), int(cu[j + 1])
+        oj, fj, _ = oracle.fwd(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], lam,
+                               init=init[j][None])
+        if n:
+            assert rel_err(o[:, a:b], oj[0]) < 1e-13
+        assert rel_err(f[j], fj[0]) < 1e-13
+        if n == 0:
+            assert np.array_equal(f[j], init[j])
+
+
+def test_linearity_in_values():
+    B, H, N, d = 1, 2, 30, 8
+    q, k, v = rand_qkv(B, H, N, d, seed=51)
+    _, _, w = rand_qkv(B, H, N, d, seed=52)
+    lam = np.asarray([0.8, 0.95], np.float32)
+    o1, f1, _ = oracle.fwd(q, k, v, lam)
+    o2, f2, _ = oracle.fwd(q, k, w, lam)
+    o3, f3, _ = oracle.fwd(q, k, (v.astype(np.float64) + 2 * w.astype(np.float64)).astype(np.float32), lam)
+    # v + 2w is exact in float32 only approximately; compare against the sum
+    assert rel_err(o3, o1 + 2 * o2) < 1e-6
+    assert rel_err(f3, f1 + 2 * f2) < 1e-6
+
+
+def test_sampled_rows_and_state_entries():
+    """The per-row and per-entry functions used at full sizes agree with the
+    recurrence."""
+    H, N, d = 2, 300, 16
+    q, k, v = rand_qkv(1, H, N, d, seed=61)
+    lam = np.asarray([0.99, 0.45], np.float32)
+    S0 = inputs.host_state((1, H, d, d), 62).astype(np.float64)
+    o, f, _ = oracle.fwd(q, k, v, lam, init=S0)
+    rows = np.array([0, 1, 127, 128, 299])
+    ij = np.array([[0, 0], [3, 7], [15, 15], [9, 2]])
+    for h in range(H):
+        r = oracle.rows(q[0, h], k[0, h], v[0, h], lam[h], rows, init=S0[0, h])
+        assert rel_err(r, o[0, h, rows]) < 1e-12
+        e = oracle.state_entries(k[0, h], v[0, h], lam[h], ij, init=S0[0, h])
+        assert rel_err(e, f[0, h][ij[:, 0], ij[:, 1]]) < 1e-12
+
+
+def test_decay_schedule_values():
+    """lambda_h = exp(-2^(-8(h+1)/H)) rounded once to float32; spot values."""
+    for H in (2, 8, 64):
+        lam = inputs.decay_schedule(H)
+        assert lam.dtype == np.float32
+        for h in range(H):
+            assert lam[h] == np.float32(math.exp(-(2.0 ** (-8.0 * (h + 1) / H))))
+        assert abs(float(lam[-1]) - math.exp(-1 / 256)) < 1e-7
+    assert abs(float(inputs.decay_schedule(64)[0]) - 0.399715) < 1e-6
+    assert abs(float(inputs.decay_schedule(8)[0]) - 0.606531) < 1e-6
+    assert abs(float(inputs.decay_schedule(2)[0]) - 0.939413) < 1e-6
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    x = np.random.default_rng(0).standard_normal(4096).astype(np.float32) * 3
+    x[:4] = [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]  # ties go to even
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(inputs.round_to_bf16(x), ref)
+
+
+def test_varlen_lengths_recipe():
+    lens = inputs.varlen_lengths()
+    assert sum(lens) == 65536 and min(lens) >= 1 and max(lens) <= 32768
+    assert lens == inputs.varlen_lengths()
+
+
+# ------------------------------------------------- planted-mistake check
+
+
+def _pins_pass(lib):
+    """Runs the cheapest pins against `lib`; True only if all hold."""
+    rng_q, rng_k, rng_v = rand_qkv(1, 2, 24, 4, seed=71)
+    lam = np.asarray([0.8, 0.5], np.float32)
+    o, f, _ = oracle.fwd(rng_q, rng_k, rng_v, lam, lib=lib)
+    ob, fb = oracle.bruteforce(rng_q, rng_k, rng_v, lam, lib=lib)
+    # the brute-force path in a planted library is untouched, so compare
+    # the planted recurrence with it and with the numpy lambda=1 form
+    ok = rel_err(o, ob) < 1e-12 and rel_err(f, fb) < 1e-12
+    ones = np.ones(2, np.float32)
+    o1, _, _ = oracle.fwd(rng_q, rng_k, rng_v, ones, lib=lib)
+    Q, K, V = (x.astype(np.float64) for x in (rng_q, rng_k, rng_v))
+    ref = ((Q @ K.transpose(0, 1, 3, 2)) * np.tril(np.ones((24, 24)))) @ V
+    ok = ok and rel_err(o1, ref) < 1e-12
+    return ok
+
+
+def test_planted_mistakes_are_caught():
+    assert _pins_pass(oracle.load())
+    with tempfile.TemporaryDirectory() as tmp:
+        for plant in (1, 2, 3, 4, 5):
+            path = oracle_build.build(out=os.path.join(tmp, "lib%d.so" % plant), plant=plant)
+            lib = oracle.load(path)
+            assert not _pins_pass(lib), "planted mistake %d not caught" % plant

@@ -1,0 +1,150 @@
+/*
+ * lightning_attn.h -- C ABI of the MI355X (gfx950) lightning attention library.
+ *
+ * What is computed: causal linear attention with a per-head scalar decay, in
+ * the blockwise ("lightning") form.  For every (sequence, head) with decay
+ * lambda in (0, 1], rows q_t, k_t, v_t in R^d and a d x d state S:
+ *
+ *     S_t = lambda * S_{t-1} + k_t^T v_t,      o_t = q_t S_t,
+ *
+ * i.e. o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s + lambda^(t+1) q_t S_init.
+ * Sources: MiniMax-01 technical report (full Chinese translation on
+ * blog.csdn.net), section 2.2.1 "Lightning Attention" (causal left product,
+ * eq. 4, with the diagonal included; right-product recurrence, eq. 5; block
+ * split into a left product inside blocks and a right product between
+ * blocks, with the block state carried forward and kv_0 = 0), section 2.2.4
+ * (recurrent form, eq. 12, used for decoding), section 3.2.2 and Fig. 12
+ * (diagonal decay matrix; LASP+ local prefix states combined into global
+ * ones), section 3.3.1-3.3.2 (fused prefill front end; fused decode state
+ * update; prefill and decode as separate kernels); K3 reading notes
+ * (cutenote.app), "position decay term" and "CP for linear attention" (any
+ * chunking gives the same result).  Normalisation, SiLU and the output gate
+ * are outside this library (the report leaves them out of the derivation).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates device memory, never synchronises, keeps no state
+ *     between calls and is re-entrant; every kernel is launched asynchronously
+ *     on `hip_stream` (a hipStream_t; NULL = the null stream).
+ *   - Arrays are dense and row-major with d fastest.  Outputs must not alias
+ *     inputs (decode's `state` is read-modify-write by design).
+ *   - q, k, v and out share one element type: LA_BF16 (bfloat16) or LA_FP32.
+ *     States (init, final, decode state) are always float32, laid out
+ *     S[i][j] with i the key feature (row) and j the value feature.
+ *   - decay[h] is head h's lambda as float32; 0 < lambda <= 1 is a
+ *     precondition the library does not check (it would need a device read).
+ *   - Arithmetic: bf16 inputs run on bf16 MFMA with float32 accumulation and
+ *     a float32 state (the state and the masked scores are rounded to bf16 as
+ *     MFMA operands); float32 inputs run in float32 throughout.
+ *   - Errors: arguments are validated before anything is launched; a failed
+ *     validation launches nothing and leaves every buffer untouched.  After
+ *     the launches, a HIP launch error maps to LA_ERR_HIP.  Faults inside a
+ *     kernel surface at the caller's next synchronisation, as usual for HIP.
+ *     No C++ exception crosses this interface.
+ */
+#ifndef LIGHTNING_ATTN_H
+#define LIGHTNING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1,  /* NULL pointer where data is needed, negative size */
+  LA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, block not in {16..256}, dtype */
+  LA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than *_workspace_size */
+  LA_ERR_HIP = 4           /* a HIP launch reported an error */
+} la_status;
+
+typedef enum { LA_FP32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *lightning_attn_status_string(la_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int lightning_attn_version(void);
+
+/*
+ * Prefill over fixed-length sequences (MiniMax-01 report, section 2.2.1,
+ * block expansion; section 3.2.2 for the sequence-parallel state scan).
+ *
+ *   q, k, v, out : [B][H][N][d] of `dt`.
+ *   decay        : [H] float32.
+ *   block        : block (chunk) length of the blockwise form, one of
+ *                  16, 32, 64, 128, 256.  Any block length gives the same
+ *                  result up to rounding (K3 notes, CP for linear
+ *                  attention); the kernels run 128-token chunks for bf16 and
+ *                  32-token chunks for float32, so `block` is validated and
+ *                  otherwise does not change the arithmetic.
+ *   init_state   : [B][H][d][d] float32, or NULL for a zero initial state.
+ *   final_state  : [B][H][d][d] float32 state after token N-1 (equal to the
+ *                  initial state when N == 0), or NULL if not wanted.
+ *   segment_tokens: 0 = automatic.  Otherwise the length, in tokens, of the
+ *                  independent segments the token axis is cut into (results
+ *                  are identical up to rounding for every value).  A value
+ *                  equal to N keeps every sequence in one segment and needs
+ *                  no workspace.
+ *   workspace    : device scratch of at least
+ *                  lightning_attn_fwd_workspace_size(...) bytes (may be NULL
+ *                  when that size is 0).  Its contents on entry do not matter.
+ *
+ * B, H >= 0, N >= 0, d in {64, 128}.  B*H == 0 is a no-op.  q, k, v, out may
+ * be NULL only when N == 0.
+ */
+size_t lightning_attn_fwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
+                                         int64_t segment_tokens);
+
+la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const float *decay,
+                             int B, int H, int64_t N, int d, int block, la_dtype dt,
+                             const float *init_state, void *out, float *final_state,
+                             int64_t segment_tokens, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
+/*
+ * Prefill over packed variable-length sequences ("data packing", MiniMax-01
+ * report section 3.2; varlen support for LASP+, section 3.2.2).  Sequence j
+ * occupies tokens cu_seqlens[j] .. cu_seqlens[j+1]-1 of every head; the state
+ * starts afresh at every sequence (from init_states[j], or zero), and no
+ * padding is needed or applied.
+ *
+ *   q, k, v, out : [H][total_N][d] of `dt`.
+ *   cu_seqlens   : [num_seqs + 1] int32 DEVICE array, non-decreasing, with
+ *                  cu_seqlens[0] == 0 and cu_seqlens[num_seqs] == total_N
+ *                  (a precondition; not checked, it lives on the device).
+ *                  Zero-length sequences are allowed.
+ *   init_states  : [num_seqs][H][d][d] float32 or NULL (zero).
+ *   final_states : [num_seqs][H][d][d] float32 or NULL.
+ *   Other arguments as for lightning_attn_fwd.
+ */
+size_t lightning_attn_fwd_varlen_workspace_size(int num_seqs, int H, int64_t total_N, int d,
+                                                int block, la_dtype dt, int64_t segment_tokens);
+
+la_status lightning_attn_fwd_varlen(const void *q, const void *k, const void *v,
+                                    const float *decay, const int32_t *cu_seqlens, int num_seqs,
+                                    int H, int64_t total_N, int d, int block, la_dtype dt,
+                                    const float *init_states, void *out, float *final_states,
+                                    int64_t segment_tokens, void *workspace,
+                                    size_t workspace_bytes, void *hip_stream);
+
+/*
+ * One recurrent decode step (MiniMax-01 report, section 2.2.4, eq. 12;
+ * section 3.3.1, fused decode state update):
+ *     state <- lambda_h * state + k^T v,   out = q state   (updated state).
+ *
+ *   q, k, v, out : [B][H][d] of `dt`.
+ *   state        : [B][H][d][d] float32, read and rewritten in place.
+ *   B, H >= 0 (B*H == 0 is a no-op), d in {64, 128}.
+ */
+la_status lightning_attn_decode(const void *q, const void *k, const void *v, const float *decay,
+                                float *state, void *out, int B, int H, int d, la_dtype dt,
+                                void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_ATTN_H */

@@ -1,0 +1,207 @@
+"""Lightning attention for AMD MI355X (gfx950): Python binding.
+
+Thin ctypes layer over liblightning_attn.so (C ABI in include/lightning_attn.h).
+It only checks tensors, allocates outputs and workspace with torch (device
+memory and streams are all torch is used for) and passes raw pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+
+Entry points (same names as the C ABI):
+  lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, ...) -> (out, final_state)
+  lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, ...) -> (out, final_states)
+  lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
+"""
+import ctypes
+import os
+
+__all__ = ["lightning_attn_fwd", "lightning_attn_fwd_varlen", "lightning_attn_decode",
+           "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
+           "LightningAttnError", "load_library", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightning_attn.so")
+
+LA_FP32, LA_BF16 = 0, 1
+_STATUS = {0: "LA_OK", 1: "LA_ERR_INVALID_ARG", 2: "LA_ERR_UNSUPPORTED", 3: "LA_ERR_WORKSPACE",
+           4: "LA_ERR_HIP"}
+
+_lib = None
+
+
+class LightningAttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        name = _STATUS.get(status, str(status))
+        msg = load_library().lightning_attn_status_string(status).decode()
+        super().__init__("%s failed: %s (%s)" % (where, name, msg))
+
+
+def load_library(path=None):
+    """Loads liblightning_attn.so (built in-tree by
+    `python -m linear_attention_lightning_amd.build`)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("HIP library %s is not built; run "
+                           "`python -m linear_attention_lightning_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    P, I, L, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.lightning_attn_status_string.argtypes = [I]
+    lib.lightning_attn_status_string.restype = ctypes.c_char_p
+    lib.lightning_attn_version.restype = I
+    lib.lightning_attn_fwd_workspace_size.argtypes = [I, I, L, I, I, I, L]
+    lib.lightning_attn_fwd_workspace_size.restype = Z
+    lib.lightning_attn_fwd.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P]
+    lib.lightning_attn_fwd.restype = I
+    lib.lightning_attn_fwd_varlen_workspace_size.argtypes = [I, I, L, I, I, I, L]
+    lib.lightning_attn_fwd_varlen_workspace_size.restype = Z
+    lib.lightning_attn_fwd_varlen.argtypes = [P, P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P]
+    lib.lightning_attn_fwd_varlen.restype = I
+    lib.lightning_attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
+    lib.lightning_attn_decode.restype = I
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_FP32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t.shape != shape:
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def lightning_attn_fwd_workspace_size(B, H, N, d, block=128, dtype=LA_BF16, segment_tokens=0):
+    return load_library().lightning_attn_fwd_workspace_size(B, H, N, d, block, dtype,
+                                                             segment_tokens)
+
+
+def lightning_attn_fwd_varlen_workspace_size(num_seqs, H, total, d, block=128, dtype=LA_BF16,
+                                             segment_tokens=0):
+    return load_library().lightning_attn_fwd_varlen_workspace_size(num_seqs, H, total, d, block,
+                                                                    dtype, segment_tokens)
+
+
+def lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, segment_tokens=0, out=None,
+                       final_state=None, workspace=None):
+    """Causal decayed linear attention over q, k, v [B, H, N, d] (bf16 or
+    float32, contiguous, on one GPU).  decay: [H] float32.  Returns
+    (out [B, H, N, d] in the input dtype, final_state [B, H, d, d] float32)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, N, d = q.shape
+    dev = q.device
+    _check(k, "k", q.shape, q.dtype, dev)
+    _check(v, "v", q.shape, q.dtype, dev)
+    _check(q, "q", q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (B, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", (B, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    ws_bytes = lib.lightning_attn_fwd_workspace_size(B, H, N, d, block, dt, segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), B, H, N, d, block, dt,
+                                _ptr(init_state), _ptr(out), _ptr(final_state), segment_tokens,
+                                _ptr(workspace), ws_have, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd")
+    return out, final_state
+
+
+def lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, init_states=None,
+                              segment_tokens=0, out=None, final_states=None, workspace=None):
+    """Packed variable-length form: q, k, v [H, total, d]; cu_seqlens int32
+    [num_seqs + 1] on the same device (0 first, total last, non-decreasing).
+    Returns (out [H, total, d], final_states [num_seqs, H, d, d] float32)."""
+    torch = _torch()
+    lib = load_library()
+    H, total, d = q.shape
+    dev = q.device
+    _check(k, "k", q.shape, q.dtype, dev)
+    _check(v, "v", q.shape, q.dtype, dev)
+    _check(q, "q", q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 offsets")
+    S = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32, dev)
+    if init_states is not None:
+        _check(init_states, "init_states", (S, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_states is None:
+        final_states = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_states, "final_states", (S, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    ws_bytes = lib.lightning_attn_fwd_varlen_workspace_size(S, H, total, d, block, dt,
+                                                            segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(cu_seqlens),
+                                       S, H, total, d, block, dt, _ptr(init_states), _ptr(out),
+                                       _ptr(final_states), segment_tokens, _ptr(workspace),
+                                       ws_have, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd_varlen")
+    return out, final_states
+
+
+def lightning_attn_decode(q, k, v, decay, state, out=None):
+    """One decode step: q, k, v [B, H, d]; state [B, H, d, d] float32 is
+    updated in place (state <- lambda state + k^T v); returns out = q state."""
+    torch = _torch()
+    lib = load_library()
+    B, H, d = q.shape
+    dev = q.device
+    _check(k, "k", q.shape, q.dtype, dev)
+    _check(v, "v", q.shape, q.dtype, dev)
+    _check(q, "q", q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    _check(state, "state", (B, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.shape, q.dtype, dev)
+    st = lib.lightning_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state), _ptr(out),
+                                   B, H, d, _dtype_code(q), _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_decode")
+    return out

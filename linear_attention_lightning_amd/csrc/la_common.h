@@ -1,0 +1,121 @@
+// Shared device-side definitions for the lightning attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define LA_LDS __attribute__((address_space(3)))
+
+// 2^x on the hardware exponential unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// lambda^n for a non-negative integer n, as 2^(n log2 lambda); 0 when the
+// power underflows float32 (those terms are below float32 resolution).
+__device__ __forceinline__ float pow_lam(float log2lam, float n) { return fast_exp2(n * log2lam); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Where every sequence lives.  Tokens of one head are numbered in the
+// concatenation of all sequences ("virtual" token index); sequence j holds
+// virtual tokens start(j) .. start(j+1)-1.  Row g of head h in sequence j is
+// at element offset row_base(h, j) + g * d of q, k, v and out.
+//   fixed length [B][H][N][d]: start(j) = j N, head_stride = N d,
+//                              seq_extra = (H - 1) N d.
+//   packed [H][total][d]     : start(j) = cu[j], head_stride = total d,
+//                              seq_extra = 0.
+struct SeqMap {
+  const int32_t *cu;  // device cu_seqlens, or nullptr for uniform length N
+  int64_t N;
+  int num_seqs;
+  int H;
+  int64_t total;  // tokens per head
+  int64_t head_stride;
+  int64_t seq_extra;
+
+  __device__ __forceinline__ int64_t start(int j) const {
+    return cu ? (int64_t)cu[j] : (int64_t)j * N;
+  }
+  // The sequence holding virtual token tok (0 <= tok < total): the largest j
+  // with start(j) <= tok, which skips zero-length sequences.
+  __device__ __forceinline__ int seq_of(int64_t tok) const {
+    if (!cu) return (int)(tok / N);
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)cu[mid] <= tok) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  }
+  __device__ __forceinline__ int64_t row_base(int h, int j) const {
+    return (int64_t)h * head_stride + (int64_t)j * seq_extra;
+  }
+};
+
+// A chunk [c0, c1) of at most T tokens inside segment [a, b), within the
+// piece of sequence j that the segment holds.  Chunks restart at every
+// sequence start and stop at every sequence end and at the segment end.
+struct Cursor {
+  int64_t c0, c1;
+  int64_t pend;     // end of the current piece: min(b, seq_end)
+  int64_t seq_end;  // start(j + 1)
+  int j;
+  bool valid;
+};
+
+__device__ __forceinline__ Cursor first_chunk(const SeqMap &m, int64_t a, int64_t b, int T) {
+  Cursor c;
+  c.valid = a < b;
+  c.j = c.valid ? m.seq_of(a) : 0;
+  c.seq_end = c.valid ? m.start(c.j + 1) : b;
+  c.pend = c.seq_end < b ? c.seq_end : b;
+  c.c0 = a;
+  c.c1 = (a + T < c.pend) ? a + T : c.pend;
+  return c;
+}
+
+__device__ __forceinline__ Cursor next_chunk(const SeqMap &m, const Cursor &c, int64_t b, int T) {
+  Cursor n = c;
+  n.c0 = c.c1;
+  if (n.c0 >= b) {
+    n.valid = false;
+    return n;
+  }
+  if (n.c0 >= c.pend) {  // the piece ended at a sequence end: next sequence
+    n.j = m.seq_of(n.c0);
+    n.seq_end = m.start(n.j + 1);
+    n.pend = n.seq_end < b ? n.seq_end : b;
+  }
+  n.c1 = (n.c0 + T < n.pend) ? n.c0 + T : n.pend;
+  n.valid = true;
+  return n;
+}
+
+// Arguments shared by the prefill kernels.
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *out;
+  const float *decay;
+  SeqMap m;
+  int64_t seg_len;   // segment length in tokens
+  int nseg;          // segments per head
+  const float *init; // [S][H][d][d] or nullptr
+  float *fin;        // [S][H][d][d] or nullptr
+  float *ws;         // [nseg][H][d][d] segment states (scan mode) or nullptr
+};
+
+}  // namespace la

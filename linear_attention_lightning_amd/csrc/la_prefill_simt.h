@@ -1,0 +1,156 @@
+// Vector-ALU prefill for float32 inputs (and bf16 inputs with d = 64):
+// the same blockwise schedule as the MFMA path, in float32 throughout, with
+// 32-token chunks and the d x d state held in LDS.
+//   P = (Q K^T) (.) D,   O = diag(a) Q S + P V,   S = lambda^L S + (diag(b) K)^T V
+// (MiniMax-01 report, section 2.2.1: left product inside a block, right
+// product between blocks.)
+#pragma once
+
+#include "la_common.h"
+
+namespace la {
+namespace simt {
+
+constexpr int T = 32;    // tokens per chunk
+constexpr int NT = 256;  // threads per workgroup
+
+template <int D>
+struct Smem {
+  float Q[T][D];
+  float K[T][D];
+  float V[T][D];
+  float S[D][D];
+  float P[T][T + 1];
+  float bw[T];
+};
+
+template <typename Tin, int D>
+__device__ __forceinline__ void load_rows(float (*dst)[D], const Tin *src, int L, int tid) {
+  for (int e = tid; e < T * D; e += NT) {
+    int r = e / D, c = e - (e / D) * D;
+    dst[r][c] = r < L ? to_f32(src[(int64_t)r * D + c]) : 0.f;
+  }
+}
+
+template <typename Tin, int D>
+__global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
+  __shared__ Smem<D> sm;
+  const int tid = threadIdx.x;
+  const SeqMap &m = p.m;
+  const int H = m.H;
+  const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const float log2lam = log2f(p.decay[h]);
+  const int64_t a = (int64_t)s * p.seg_len;
+  const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
+  const int64_t DD = (int64_t)D * D;
+  Cursor cur = first_chunk(m, a, b, T);
+  if (!cur.valid) return;
+  {
+    const float *s0 = p.ws ? p.ws + ((int64_t)s * H + h) * DD
+                           : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
+    for (int e = tid; e < D * D; e += NT) (&sm.S[0][0])[e] = s0 ? s0[e] : 0.f;
+  }
+  constexpr int RSTEP = NT / D;  // output rows handled per pass
+  while (true) {
+    const int L = (int)(cur.c1 - cur.c0);
+    const int64_t base = m.row_base(h, cur.j) + cur.c0 * D;
+    load_rows<Tin, D>(sm.Q, (const Tin *)p.q + base, L, tid);
+    load_rows<Tin, D>(sm.K, (const Tin *)p.k + base, L, tid);
+    load_rows<Tin, D>(sm.V, (const Tin *)p.v + base, L, tid);
+    if (tid < T) sm.bw[tid] = tid < L ? pow_lam(log2lam, (float)(L - 1 - tid)) : 0.f;
+    __syncthreads();
+    // masked, decayed scores
+    for (int e = tid; e < T * T; e += NT) {
+      int r = e / T, c = e - (e / T) * T;
+      float acc = 0.f;
+      if (c <= r && r < L) {
+        for (int i = 0; i < D; ++i) acc += sm.Q[r][i] * sm.K[c][i];
+        acc *= pow_lam(log2lam, (float)(r - c));
+      }
+      sm.P[r][c] = acc;
+    }
+    __syncthreads();
+    // outputs
+    {
+      const int j = tid % D;
+      Tin *obase = (Tin *)p.out + base;
+      for (int r = tid / D; r < L; r += RSTEP) {
+        float inter = 0.f;
+        for (int i = 0; i < D; ++i) inter += sm.Q[r][i] * sm.S[i][j];
+        float intra = 0.f;
+        for (int c = 0; c <= r; ++c) intra += sm.P[r][c] * sm.V[c][j];
+        obase[(int64_t)r * D + j] = from_f32<Tin>(pow_lam(log2lam, (float)(r + 1)) * inter + intra);
+      }
+    }
+    __syncthreads();
+    const Cursor nxt = next_chunk(m, cur, b, T);
+    const bool seq_done = (cur.c1 == cur.seq_end);
+    const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
+    if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
+      const float gL = pow_lam(log2lam, (float)L);
+      for (int e = tid; e < D * D; e += NT) {
+        int i = e / D, j = e - (e / D) * D;
+        float acc = 0.f;
+        for (int c = 0; c < L; ++c) acc += (sm.bw[c] * sm.K[c][i]) * sm.V[c][j];
+        sm.S[i][j] = gL * sm.S[i][j] + acc;
+      }
+      __syncthreads();
+      if (seq_done && p.fin) {
+        float *dst = p.fin + ((int64_t)cur.j * H + h) * DD;
+        for (int e = tid; e < D * D; e += NT) dst[e] = (&sm.S[0][0])[e];
+      }
+    }
+    if (!nxt.valid) break;
+    __syncthreads();
+    if (new_piece) {
+      const float *s0 = p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr;
+      for (int e = tid; e < D * D; e += NT) (&sm.S[0][0])[e] = s0 ? s0[e] : 0.f;
+    }
+    cur = nxt;
+  }
+}
+
+// Local state of each segment's last piece, from zero (phase A).
+template <typename Tin, int D>
+__global__ __launch_bounds__(NT) void local_state_kernel(FwdArgs p) {
+  __shared__ float Ks[T][D];
+  __shared__ float Vs[T][D];
+  __shared__ float wv[T];
+  const int tid = threadIdx.x;
+  const SeqMap &m = p.m;
+  const int H = m.H;
+  const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const float log2lam = log2f(p.decay[h]);
+  const int64_t a = (int64_t)s * p.seg_len;
+  const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
+  if (a >= b) return;
+  const int jl = m.seq_of(b - 1);
+  const int64_t ps0 = m.start(jl);
+  const int64_t ps = ps0 > a ? ps0 : a;
+  const int64_t base = m.row_base(h, jl);
+  constexpr int PER = D * D / NT;
+  float acc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) acc[u] = 0.f;
+  for (int64_t t0 = ps; t0 < b; t0 += T) {
+    const int L = (int)((b - t0) < T ? (b - t0) : T);
+    load_rows<Tin, D>(Ks, (const Tin *)p.k + base + t0 * D, L, tid);
+    load_rows<Tin, D>(Vs, (const Tin *)p.v + base + t0 * D, L, tid);
+    if (tid < T) wv[tid] = tid < L ? pow_lam(log2lam, (float)(b - 1 - t0 - tid)) : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      int e = u * NT + tid, i = e / D, j = e - (e / D) * D;
+      float sacc = 0.f;
+      for (int c = 0; c < L; ++c) sacc += (wv[c] * Ks[c][i]) * Vs[c][j];
+      acc[u] += sacc;
+    }
+    __syncthreads();
+  }
+  float *dst = p.ws + ((int64_t)s * H + h) * (int64_t)D * D;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) dst[u * NT + tid] = acc[u];
+}
+
+}  // namespace simt
+}  // namespace la

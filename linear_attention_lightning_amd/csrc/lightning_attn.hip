@@ -1,0 +1,288 @@
+// Host side of the lightning attention library: argument checks, the
+// segment plan, kernel launches and the exported C ABI (lightning_attn.h).
+#include "lightning_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "la_common.h"
+#include "la_prefill_mfma.h"
+#include "la_prefill_simt.h"
+#include "la_scan_decode.h"
+
+namespace {
+
+using la::bf16;
+
+constexpr int kVersion = 100;    // 0.1.0
+constexpr int kTargetGroups = 512;  // aim for >= 2 workgroups per CU on 256 CUs
+
+bool valid_block(int b) { return b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
+bool valid_d(int d) { return d == 64 || d == 128; }
+bool valid_dtype(la_dtype dt) { return dt == LA_FP32 || dt == LA_BF16; }
+
+// bf16 with d = 128 runs on MFMA; everything else on the vector ALUs.
+bool use_mfma(int d, la_dtype dt) { return dt == LA_BF16 && d == 128; }
+int chunk_tokens(int d, la_dtype dt) { return use_mfma(d, dt) ? la::mfma::T : la::simt::T; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int64_t seg;   // segment length (tokens)
+  int64_t nseg;  // segments per head
+  bool scan;     // phases A and B needed
+  size_t ws_bytes;
+};
+
+size_t state_bytes(int64_t count, int d) { return (size_t)count * (size_t)d * (size_t)d * 4; }
+
+// Fixed-length plan.  Without a scan each sequence is one segment.  With
+// one, the token axis of every head is cut into equal segments so that
+// about kTargetGroups workgroups run per phase.
+Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tokens) {
+  Plan p{N, B, false, 0};
+  const int64_t total = (int64_t)B * N;
+  if (total == 0) {
+    p.nseg = 0;
+    return p;
+  }
+  const int T = chunk_tokens(d, dt);
+  int64_t seg = N;
+  if (segment_tokens > 0) {
+    seg = segment_tokens;
+  } else {
+    const int64_t bh = (int64_t)B * H;
+    int64_t G = ceil_div(kTargetGroups, bh);
+    const int64_t maxG = ceil_div(N, T);
+    if (G > maxG) G = maxG;
+    if (G > 1) {
+      seg = ceil_div(ceil_div(N, G), T) * T;
+      if (seg >= N) seg = N;
+    }
+  }
+  p.seg = seg;
+  p.scan = (seg != N);
+  p.nseg = ceil_div(total, seg);
+  p.ws_bytes = p.scan ? state_bytes(p.nseg * H, d) : 0;
+  return p;
+}
+
+Plan plan_varlen(int H, int64_t total, int d, la_dtype dt, int64_t segment_tokens) {
+  Plan p{1, 0, true, 0};
+  if (total == 0) return p;
+  const int T = chunk_tokens(d, dt);
+  int64_t seg = segment_tokens;
+  if (seg <= 0) {
+    const int64_t G = ceil_div(kTargetGroups, H);
+    seg = ceil_div(ceil_div(total, G), T) * T;
+  }
+  p.seg = seg;
+  p.nseg = ceil_div(total, seg);
+  p.ws_bytes = state_bytes(p.nseg * H, d);
+  return p;
+}
+
+la_status launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+template <typename Tin, int D>
+void launch_simt(const la::FwdArgs &a, const Plan &pl, hipStream_t st, bool phase_a) {
+  dim3 grid((unsigned)(pl.nseg * a.m.H));
+  if (phase_a)
+    hipLaunchKernelGGL((la::simt::local_state_kernel<Tin, D>), grid, dim3(la::simt::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((la::simt::prefill_chunk_kernel<Tin, D>), grid, dim3(la::simt::NT), 0, st,
+                       a);
+}
+
+void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipStream_t st,
+                  bool phase_a) {
+  dim3 grid((unsigned)(pl.nseg * a.m.H));
+  if (use_mfma(d, dt)) {
+    if (phase_a)
+      hipLaunchKernelGGL(la::mfma::local_state_kernel, grid, dim3(la::mfma::NT), 0, st, a);
+    else
+      hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, a);
+  } else if (dt == LA_BF16) {
+    launch_simt<bf16, 64>(a, pl, st, phase_a);
+  } else if (d == 64) {
+    launch_simt<float, 64>(a, pl, st, phase_a);
+  } else {
+    launch_simt<float, 128>(a, pl, st, phase_a);
+  }
+}
+
+// Runs the whole prefill for a planned problem (fixed or packed).
+la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, bool has_empty,
+                  hipStream_t st) {
+  la::FwdArgs a = base;
+  const int H = a.m.H;
+  if (pl.scan && pl.nseg > 0) {
+    launch_phase(a, pl, d, dt, st, /*phase_a=*/true);
+  }
+  if (pl.scan || has_empty) {
+    la::ScanArgs s;
+    s.m = a.m;
+    s.decay = a.decay;
+    s.seg_len = pl.seg;
+    s.nseg = pl.scan ? (int)pl.nseg : 0;
+    s.d = d;
+    s.init = a.init;
+    s.fin = a.fin;
+    s.ws = a.ws;
+    dim3 grid((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024));
+    hipLaunchKernelGGL(la::segment_scan_kernel, grid, dim3(256), 0, st, s);
+  }
+  if (pl.nseg > 0) {
+    if (!pl.scan) a.ws = nullptr;
+    launch_phase(a, pl, d, dt, st, /*phase_a=*/false);
+  }
+  return launch_status();
+}
+
+la_status check_common(int H, int d, int block, la_dtype dt, int64_t segment_tokens) {
+  if (H < 0 || segment_tokens < 0) return LA_ERR_INVALID_ARG;
+  if (!valid_dtype(dt) || !valid_d(d) || !valid_block(block)) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lightning_attn_status_string(la_status s) {
+  switch (s) {
+    case LA_OK: return "ok";
+    case LA_ERR_INVALID_ARG: return "invalid argument";
+    case LA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int lightning_attn_version(void) { return kVersion; }
+
+size_t lightning_attn_fwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
+                                         int64_t segment_tokens) {
+  if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
+  if ((int64_t)B * H == 0) return 0;
+  return plan_fixed(B, H, N, d, dt, segment_tokens).ws_bytes;
+}
+
+la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const float *decay,
+                             int B, int H, int64_t N, int d, int block, la_dtype dt,
+                             const float *init_state, void *out, float *final_state,
+                             int64_t segment_tokens, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+  if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st != LA_OK) return st;
+  if ((int64_t)B * H == 0) return LA_OK;
+  if (!decay) return LA_ERR_INVALID_ARG;
+  if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+  if (N == 0 && !final_state) return LA_OK;
+
+  la::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.decay = decay;
+  a.m.cu = nullptr;
+  a.m.N = N;
+  a.m.num_seqs = B;
+  a.m.H = H;
+  a.m.total = (int64_t)B * N;
+  a.m.head_stride = N * d;
+  a.m.seq_extra = (int64_t)(H - 1) * N * d;
+  a.seg_len = pl.seg;
+  a.nseg = (int)pl.nseg;
+  a.init = init_state;
+  a.fin = final_state;
+  a.ws = (float *)workspace;
+  return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream);
+}
+
+size_t lightning_attn_fwd_varlen_workspace_size(int num_seqs, int H, int64_t total_N, int d,
+                                                int block, la_dtype dt, int64_t segment_tokens) {
+  if (num_seqs < 0 || total_N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK)
+    return 0;
+  if ((int64_t)num_seqs * H == 0) return 0;
+  return plan_varlen(H, total_N, d, dt, segment_tokens).ws_bytes;
+}
+
+la_status lightning_attn_fwd_varlen(const void *q, const void *k, const void *v,
+                                    const float *decay, const int32_t *cu_seqlens, int num_seqs,
+                                    int H, int64_t total_N, int d, int block, la_dtype dt,
+                                    const float *init_states, void *out, float *final_states,
+                                    int64_t segment_tokens, void *workspace,
+                                    size_t workspace_bytes, void *hip_stream) {
+  if (num_seqs < 0 || total_N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st != LA_OK) return st;
+  if ((int64_t)num_seqs * H == 0) return total_N == 0 ? LA_OK : LA_ERR_INVALID_ARG;
+  if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
+  if (total_N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_varlen(H, total_N, d, dt, segment_tokens);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+
+  la::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.decay = decay;
+  a.m.cu = cu_seqlens;
+  a.m.N = 0;
+  a.m.num_seqs = num_seqs;
+  a.m.H = H;
+  a.m.total = total_N;
+  a.m.head_stride = total_N * d;
+  a.m.seq_extra = 0;
+  a.seg_len = pl.seg;
+  a.nseg = (int)pl.nseg;
+  a.init = init_states;
+  a.fin = final_states;
+  a.ws = (float *)workspace;
+  return run_fwd(a, pl, d, dt, /*has_empty=*/true, (hipStream_t)hip_stream);
+}
+
+la_status lightning_attn_decode(const void *q, const void *k, const void *v, const float *decay,
+                                float *state, void *out, int B, int H, int d, la_dtype dt,
+                                void *hip_stream) {
+  if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+  if (!valid_dtype(dt) || !valid_d(d)) return LA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H == 0) return LA_OK;
+  if (!q || !k || !v || !decay || !state || !out) return LA_ERR_INVALID_ARG;
+  if ((int64_t)B * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)hip_stream;
+  dim3 grid((unsigned)((int64_t)B * H));
+  if (dt == LA_BF16) {
+    if (d == 128)
+      hipLaunchKernelGGL((la::decode_kernel<bf16, 128>), grid, dim3(256), 0, st, (const bf16 *)q,
+                         (const bf16 *)k, (const bf16 *)v, decay, state, (bf16 *)out, H);
+    else
+      hipLaunchKernelGGL((la::decode_kernel<bf16, 64>), grid, dim3(256), 0, st, (const bf16 *)q,
+                         (const bf16 *)k, (const bf16 *)v, decay, state, (bf16 *)out, H);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((la::decode_kernel<float, 128>), grid, dim3(256), 0, st,
+                         (const float *)q, (const float *)k, (const float *)v, decay, state,
+                         (float *)out, H);
+    else
+      hipLaunchKernelGGL((la::decode_kernel<float, 64>), grid, dim3(256), 0, st,
+                         (const float *)q, (const float *)k, (const float *)v, decay, state,
+                         (float *)out, H);
+  }
+  return launch_status();
+}
+
+}  // extern "C"

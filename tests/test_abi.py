@@ -1,0 +1,132 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/lightning_attn.h declares, and rejects bad arguments with the
+documented status codes before launching anything (no GPU needed: every
+call here returns during validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_lightning_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lightning_attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FP32, BF16 = 0, 1
+DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lightning_attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return la.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "lightning_attn_fwd" in names and "lightning_attn_decode" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    for s in range(5):
+        assert lib.lightning_attn_status_string(s)
+    assert lib.lightning_attn_status_string(99) == b"unknown status"
+    assert lib.lightning_attn_version() >= 100
+
+
+def fwd(lib, **kw):
+    a = dict(q=DUMMY, k=DUMMY, v=DUMMY, decay=DUMMY, B=1, H=2, N=256, d=128, block=128, dt=BF16,
+             init=None, out=DUMMY, fin=DUMMY, seg=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.lightning_attn_fwd(a["q"], a["k"], a["v"], a["decay"], a["B"], a["H"], a["N"],
+                                  a["d"], a["block"], a["dt"], a["init"], a["out"], a["fin"],
+                                  a["seg"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    assert fwd(lib, d=96) == UNSUPPORTED
+    assert fwd(lib, d=256) == UNSUPPORTED
+    assert fwd(lib, block=48) == UNSUPPORTED
+    assert fwd(lib, block=512) == UNSUPPORTED
+    assert fwd(lib, dt=7) == UNSUPPORTED
+    assert fwd(lib, B=-1) == INVALID
+    assert fwd(lib, N=-5) == INVALID
+    assert fwd(lib, H=-2) == INVALID
+    assert fwd(lib, seg=-1) == INVALID
+    assert fwd(lib, q=None) == INVALID
+    assert fwd(lib, out=None) == INVALID
+    assert fwd(lib, decay=None) == INVALID
+    # B*H == 0 and N == 0 without a state to write are no-ops
+    assert fwd(lib, B=0) == OK
+    assert fwd(lib, H=0, decay=None) == OK
+    assert fwd(lib, N=0, q=None, k=None, v=None, out=None, fin=None) == OK
+
+
+def test_fwd_workspace_checks(lib):
+    # a long single sequence on few heads is cut into segments: needs workspace
+    need = lib.lightning_attn_fwd_workspace_size(1, 8, 1 << 20, 128, 256, BF16, 0)
+    assert need > 0 and need % (128 * 128 * 4) == 0
+    assert fwd(lib, H=8, N=1 << 20, block=256, ws=None, wsb=0) == WORKSPACE
+    assert fwd(lib, H=8, N=1 << 20, block=256, ws=DUMMY, wsb=need - 1) == WORKSPACE
+    # one segment per sequence needs none
+    assert lib.lightning_attn_fwd_workspace_size(4, 64, 4096, 128, 128, BF16, 4096) == 0
+    # explicit segment lengths
+    n = lib.lightning_attn_fwd_workspace_size(1, 2, 1000, 64, 64, FP32, 256)
+    assert n == 4 * 2 * 64 * 64 * 4
+    assert lib.lightning_attn_fwd_workspace_size(1, 2, 1000, 96, 64, FP32, 256) == 0
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    f = lib.lightning_attn_fwd_varlen
+    args = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 3, 4, 1000, 128, 128, BF16, None, DUMMY, DUMMY, 0,
+            None, 0, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["q", "k", "v", "decay", "cu", "S", "H", "total", "d", "block", "dt", "init",
+                 "out", "fin", "seg", "ws", "wsb", "stream"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+
+    assert call(cu=None) == INVALID
+    assert call(S=-1) == INVALID
+    assert call(total=-1) == INVALID
+    assert call(d=32) == UNSUPPORTED
+    assert call(block=100) == UNSUPPORTED
+    assert call() == WORKSPACE
+    assert call(S=0) == INVALID  # tokens but no sequences
+    assert call(S=0, total=0) == OK
+    need = lib.lightning_attn_fwd_varlen_workspace_size(3, 4, 1000, 128, 128, BF16, 0)
+    assert need > 0
+
+
+def test_decode_rejects_bad_arguments(lib):
+    f = lib.lightning_attn_decode
+    base = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 2, 4, 128, BF16, None]
+    for idx in range(6):
+        a = list(base)
+        a[idx] = None
+        assert f(*a) == INVALID
+    a = list(base); a[8] = 80
+    assert f(*a) == UNSUPPORTED
+    a = list(base); a[9] = 3
+    assert f(*a) == UNSUPPORTED
+    a = list(base); a[6] = -1
+    assert f(*a) == INVALID
+    a = list(base); a[6] = 0
+    assert f(*a) == OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        la.load_library(str(tmp_path / "missing.so"))

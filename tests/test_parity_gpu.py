@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path (through the C ABI, via the Python binding)
+against the double-precision CPU oracle, on the same seeded inputs.
+
+Bar (max |o - o_ref| / max |o_ref| over the compared set, and the same for
+the final state): <= 1e-4 for float32 inputs, <= 2e-2 for bf16 inputs.
+Small and mid sizes compare every element; the full-size workloads compare
+whole heads, whole sequences or single rows and state entries the oracle
+computes one by one, in the launch configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import linear_attention_lightning_amd as la
+from linear_attention_lightning_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.abs(b).max()
+    return float(np.abs(a - b).max() / (den if den > 0 else 1.0))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    torch = torch_mod()
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def dev_inputs(shape, seed, dtype):
+    """Seeded host inputs (numpy), copied to the GPU in the compute dtype."""
+    torch = torch_mod()
+    q, k, v = inputs.host_qkv(shape, seed, dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return [torch.from_numpy(x).to("cuda").to(tdt) for x in (q, k, v)], (q, k, v)
+
+
+def run_fwd_case(B, H, N, d, dtype, seed, block=128, seg=0, with_init=False, lam=None):
+    torch = torch_mod()
+    say("case fwd B=%d H=%d N=%d d=%d %s seg=%d init=%s" % (B, H, N, d, dtype, seg, with_init))
+    (tq, tk, tv), (q, k, v) = dev_inputs((B, H, N, d), seed, dtype)
+    lam = inputs.decay_schedule(H) if lam is None else np.asarray(lam, np.float32)
+    tl = torch.from_numpy(lam).to("cuda")
+    init = inputs.host_state((B, H, d, d), seed + 1) if with_init else None
+    ti = torch.from_numpy(init).to("cuda") if with_init else None
+    out, fin = la.lightning_attn_fwd(tq, tk, tv, tl, block=block, init_state=ti,
+                                     segment_tokens=seg)
+    torch.cuda.synchronize()
+    o_ref, f_ref, _ = oracle.fwd(q, k, v, lam, init=init)
+    eo, ef = rel_err(host(out), o_ref), rel_err(host(fin), f_ref)
+    say("   err out %.3e state %.3e" % (eo, ef))
+    assert np.isfinite(host(out)).all()
+    assert eo <= TOL[dtype] and ef <= TOL[dtype], (eo, ef)
+    return eo, ef
+
+
+def test_tiny_fp32_workload():
+    """B=1 H=2 N=256 d=64 block=64, float32: every element."""
+    run_fwd_case(1, 2, 256, 64, "fp32", seed=1, block=64)
+
+
+def test_mid_bf16_workload():
+    """B=2 H=8 N=4096 d=128 block=64, bf16: every element."""
+    run_fwd_case(2, 8, 4096, 128, "bf16", seed=2, block=64)
+
+
+@pytest.mark.parametrize("seg", [4096, 128, 640, 1000, 8192])
+def test_segment_split_invariance_bf16(seg):
+    """Any cut of the token axis into segments (on-device LASP+ scan) gives
+    the oracle's result: segments of one block, ragged segments, segments
+    spanning two sequences."""
+    run_fwd_case(2, 4, 4096, 128, "bf16", seed=20, seg=seg)
+
+
+@pytest.mark.parametrize("N", [1, 2, 127, 128, 129, 300, 1000])
+def test_ragged_tails_bf16(N):
+    run_fwd_case(2, 3, N, 128, "bf16", seed=30 + N, with_init=True,
+                 lam=[0.9961, 0.3997, 0.75])
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])
+@pytest.mark.parametrize("N,seg", [(300, 0), (300, 64), (77, 0)])
+def test_vector_alu_paths(d, dtype, N, seg):
+    run_fwd_case(1, 3, N, d, dtype, seed=40 + N + d, seg=seg, with_init=True,
+                 lam=[0.999, 0.5, 0.9])
+
+
+def test_initial_state_bf16():
+    run_fwd_case(1, 4, 2048, 128, "bf16", seed=50, with_init=True, seg=512)
+
+
+def test_zero_length_returns_initial_state():
+    torch = torch_mod()
+    B, H, d = 2, 3, 128
+    init = torch.randn(B, H, d, d, device="cuda")
+    q = torch.empty(B, H, 0, d, device="cuda", dtype=torch.bfloat16)
+    out, fin = la.lightning_attn_fwd(q, q.clone(), q.clone(),
+                                     torch.from_numpy(inputs.decay_schedule(H)).cuda(),
+                                     init_state=init)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, init)
+    out, fin = la.lightning_attn_fwd(q, q.clone(), q.clone(),
+                                     torch.from_numpy(inputs.decay_schedule(H)).cuda())
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fin).item() == 0
+
+
+def test_deterministic_bitwise():
+    torch = torch_mod()
+    (tq, tk, tv), _ = dev_inputs((1, 8, 8192, 128), 60, "bf16")
+    tl = torch.from_numpy(inputs.decay_schedule(8)).cuda()
+    o1, f1 = la.lightning_attn_fwd(tq, tk, tv, tl)
+    o2, f2 = la.lightning_attn_fwd(tq, tk, tv, tl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+# ------------------------------------------------------------------ varlen
+
+
+def run_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True):
+    torch = torch_mod()
+    say("case varlen lens=%s H=%d d=%d %s seg=%d" % (lens[:8], H, d, dtype, seg))
+    cu = inputs.cu_seqlens(lens)
+    total = int(cu[-1])
+    (tq, tk, tv), (q, k, v) = dev_inputs((H, total, d), seed, dtype)
+    lam = inputs.decay_schedule(H)
+    init = inputs.host_state((len(lens), H, d, d), seed + 1) if with_init else None
+    ti = torch.from_numpy(init).cuda() if with_init else None
+    out, fin = la.lightning_attn_fwd_varlen(tq, tk, tv, torch.from_numpy(lam).cuda(),
+                                            torch.from_numpy(cu).cuda(), init_states=ti,
+                                            segment_tokens=seg)
+    torch.cuda.synchronize()
+    o_ref, f_ref, _ = oracle.fwd_varlen(q, k, v, lam, cu, init=init)
+    eo = rel_err(host(out), o_ref) if total else 0.0
+    ef = rel_err(host(fin), f_ref)
+    say("   err out %.3e state %.3e" % (eo, ef))
+    assert eo <= TOL[dtype] and ef <= TOL[dtype], (eo, ef)
+
+
+@pytest.mark.parametrize("seg", [0, 128, 200, 100000])
+def test_varlen_bf16(seg):
+    run_varlen_case([300, 0, 1, 129, 1024, 5, 0, 640, 2000], 4, 128, "bf16", seed=70, seg=seg)
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])
+def test_varlen_vector_alu(d, dtype):
+    run_varlen_case([33, 0, 64, 1, 100], 2, d, dtype, seed=71, seg=48)
+
+
+def test_varlen_all_empty():
+    torch = torch_mod()
+    H, d = 2, 128
+    cu = torch.zeros(4, dtype=torch.int32, device="cuda")
+    q = torch.empty(H, 0, d, dtype=torch.bfloat16, device="cuda")
+    init = torch.randn(3, H, d, d, device="cuda")
+    out, fin = la.lightning_attn_fwd_varlen(q, q.clone(), q.clone(),
+                                            torch.from_numpy(inputs.decay_schedule(H)).cuda(), cu,
+                                            init_states=init)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, init)
+
+
+# ------------------------------------------------------------------ decode
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (128, "fp32"), (64, "fp32")])
+def test_decode_steps(d, dtype):
+    torch = torch_mod()
+    B, H, steps = 3, 4, 12
+    say("case decode B=%d H=%d d=%d %s" % (B, H, d, dtype))
+    (tq, tk, tv), (q, k, v) = dev_inputs((steps, B, H, d), 80 + d, dtype)
+    lam = inputs.decay_schedule(H)
+    S0 = inputs.host_state((B, H, d, d), 81)
+    st = torch.from_numpy(S0).cuda()
+    tl = torch.from_numpy(lam).cuda()
+    S = S0.astype(np.float64)
+    worst = 0.0
+    for t in range(steps):
+        o = la.lightning_attn_decode(tq[t], tk[t], tv[t], tl, st)
+        o_ref, _ = oracle.decode(q[t], k[t], v[t], lam, S)
+        worst = max(worst, rel_err(host(o), o_ref))
+    torch.cuda.synchronize()
+    es = rel_err(host(st), S)
+    say("   err out %.3e state %.3e" % (worst, es))
+    assert worst <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_decode_matches_prefill_rows():
+    """Decoding token t from the prefill state after t tokens reproduces
+    prefill row t (recurrent form, eq. 12)."""
+    torch = torch_mod()
+    B, H, N, d = 2, 4, 200, 128
+    (tq, tk, tv), _ = dev_inputs((B, H, N + 1, d), 90, "bf16")
+    tl = torch.from_numpy(inputs.decay_schedule(H)).cuda()
+    out, fin = la.lightning_attn_fwd(tq[:, :, :N].contiguous(), tk[:, :, :N].contiguous(),
+                                     tv[:, :, :N].contiguous(), tl)
+    full, _ = la.lightning_attn_fwd(tq, tk, tv, tl)
+    o = la.lightning_attn_decode(tq[:, :, N].contiguous(), tk[:, :, N].contiguous(),
+                                 tv[:, :, N].contiguous(), tl, fin)
+    torch.cuda.synchronize()
+    assert rel_err(host(o), host(full[:, :, N])) < 2e-2

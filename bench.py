@@ -1,0 +1,279 @@
+"""Benchmark: lightning attention prefill (and decode) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+
+A step is one prefill pass of the headline workload -- B=1, H=64, N=32768,
+d=128, block 128, bf16 inputs, float32 state -- through the C ABI, with its
+inputs already resident in HBM.  W untimed steps, then K steps timed with
+HIP events on the stream the library launches on.  Prints ONE JSON line:
+the headline tokens/s, TFLOP/s and fraction of the bf16 MFMA peak, the HBM
+roofline of the step, the CPU oracle timed on a bounded sample, and (unless
+--no-extras) the decode, packed varlen and million-token workloads.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s & TFLOP/s (% MFMA peak) at H=64 d=128; decode state GB/s"
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def prefill_flops(B, H, N, d, C):
+    """Dense-block FLOPs of the blockwise form: Q K^T and P V inside blocks
+    (4 C d per token) plus Q S and K^T V per token (4 d^2)."""
+    return B * H * N * 4 * d * (C + d)
+
+
+def prefill_bytes(B, H, N, d, in_bytes=2, out_bytes=2):
+    """Algorithmic HBM bytes: q, k, v read once, out written once, final
+    state written once, decay read once."""
+    return B * H * N * d * (3 * in_bytes + out_bytes) + B * H * d * d * 4 + 4 * H
+
+
+def decode_bytes(B, H, d, io_bytes=2):
+    """Per decode step: the float32 state read and written once, plus q, k,
+    v and out."""
+    return 2 * B * H * d * d * 4 + 4 * B * H * d * io_bytes
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_lightning_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per step from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_step")
+
+
+def time_steps(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup):
+    import torch
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.device_qkv((B, H, N, d), seed, "bf16", device=dev)
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    out = torch.empty_like(q)
+    fin = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    nws = la.lightning_attn_fwd_workspace_size(B, H, N, d, block)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        la.lightning_attn_fwd(q, k, v, decay, block=block, out=out, final_state=fin,
+                              workspace=ws)
+
+    ms = time_steps(step, steps, warmup, stream)
+    return ms, (q, k, v, decay, out, fin)
+
+
+def bench_varlen(la, inputs, steps, warmup):
+    import torch
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["layer_h64_varlen64k"]
+    H, total, d, block = w["H"], w["total"], w["d"], w["block"]
+    lens = inputs.varlen_lengths(total=total, seed=w["seed"])
+    cu = torch.from_numpy(inputs.cu_seqlens(lens)).to(dev)
+    q, k, v = inputs.device_qkv((H, total, d), w["seed"], "bf16", device=dev)
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    out = torch.empty_like(q)
+    fin = torch.empty((len(lens), H, d, d), dtype=torch.float32, device=dev)
+    nws = la.lightning_attn_fwd_varlen_workspace_size(len(lens), H, total, d, block)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        la.lightning_attn_fwd_varlen(q, k, v, decay, cu, block=block, out=out, final_states=fin,
+                                     workspace=ws)
+
+    ms = time_steps(step, steps, warmup, torch.cuda.current_stream(dev))
+    byt = H * total * d * 8 + len(lens) * H * d * d * 4
+    return {"workload": "layer_h64_varlen64k", "num_seqs": len(lens), "H": H, "total": total,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(total / (ms * 1e-3), 1),
+            "tflops": round(prefill_flops(1, H, total, d, 128) / (ms * 1e-3) / 1e12, 2),
+            "hbm_gbs_algorithmic": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def bench_million(la, inputs, steps, warmup):
+    w = inputs.WORKLOADS["million_h8"]
+    B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
+    ms, _ = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], steps, warmup)
+    byt = prefill_bytes(B, H, N, d)
+    return {"workload": "million_h8", "B": B, "H": H, "N": N, "block": block,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+            "tflops_at_block": round(prefill_flops(B, H, N, d, block) / (ms * 1e-3) / 1e12, 2),
+            "tflops_executed_chunk128": round(prefill_flops(B, H, N, d, 128) / (ms * 1e-3) / 1e12, 2),
+            "hbm_gbs_algorithmic": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def bench_decode(la, inputs, reps, warmup):
+    import torch
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["decode_b128_h64"]
+    B, H, d, T = w["B"], w["H"], w["d"], w["steps"]
+    q, k, v = inputs.device_qkv((T, B, H, d), w["seed"], "bf16", device=dev)
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    state0 = inputs.device_state((B, H, d, d), w["seed"] + 1, device=dev)
+    state = state0.clone()
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():  # 256 consecutive one-token steps
+        for t in range(T):
+            la.lightning_attn_decode(q[t], k[t], v[t], decay, state, out=out)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        run()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    ms = min(times) / T
+    gbs = decode_bytes(B, H, d) / (ms * 1e-3) / 1e9
+    return {"workload": "decode_b128_h64", "B": B, "H": H, "d": d, "steps": T,
+            "ms_per_token_step": round(ms, 5), "state_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def cpu_baseline(gpu_tensors, H, N, d, heads):
+    """The oracle (untuned) on the host cores: `heads` of the H heads, all N
+    tokens, on the same inputs; scaled to whole-workload tokens/s."""
+    import numpy as np
+    import torch
+    import oracle
+    from linear_attention_lightning_amd import inputs
+    q, k, v = (t[:, :heads].float().cpu().numpy() for t in gpu_tensors[:3])
+    lam = inputs.decay_schedule(H)[:heads]
+    t0 = time.perf_counter()
+    _, _, used = oracle.fwd(q, k, v, lam)
+    dt = time.perf_counter() - t0
+    frac = heads / H
+    return {"value": round(N / (dt / frac), 1), "unit": "tokens/s", "cores": used,
+            "kind": "oracle",
+            "sample": "%d of %d heads, all %d tokens of the B=1 H=64 N=32768 d=128 workload "
+                      "(double-precision recurrence), %.1f s wall; scaled to all heads"
+                      % (heads, H, N, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this size once (a plain "
+                         "copy kernel of known size, to scale HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(shard (batch, head) pairs or sequence segments across GPUs as DESIGN.md "
+              "describes)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_lightning_amd as la
+    from linear_attention_lightning_amd import inputs
+
+    la.load_library()
+    w = inputs.WORKLOADS["layer_h64_n32k"]
+    B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
+    ms, tensors = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], args.steps, args.warmup)
+    sec = ms * 1e-3
+    flops = prefill_flops(B, H, N, d, block)
+    tflops = flops / sec / 1e12
+    alg = prefill_bytes(B, H, N, d)
+    gbs = alg / sec / 1e9
+    traffic = measured_traffic("layer_h64_n32k")
+    res = {
+        "metric": METRIC,
+        "value": round(B * N / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "layer_h64_n32k", "B": B, "H": H, "N": N, "d": d,
+                   "block": block, "state": "fp32"},
+        "tflops": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "whole prefill step (local-state, segment-scan and chunk "
+                               "kernels), algorithmic bytes %d per step" % alg},
+    }
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = nbytes
+        del src, dst
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(tensors, H, N, d, min(args.cpu_heads, H))
+    del tensors
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        res["decode"] = bench_decode(la, inputs, reps=3, warmup=1)
+        torch.cuda.empty_cache()
+        res["varlen"] = bench_varlen(la, inputs, steps=max(5, args.steps // 2), warmup=2)
+        torch.cuda.empty_cache()
+        res["million"] = bench_million(la, inputs, steps=5, warmup=1)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

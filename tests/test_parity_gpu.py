@@ -216,3 +216,120 @@ def test_decode_matches_prefill_rows():
                                  tv[:, :, N].contiguous(), tl, fin)
     torch.cuda.synchronize()
     assert rel_err(host(o), host(full[:, :, N])) < 2e-2
+
+
+# ------------------------------------------------- full-size workloads
+# Same sizes, seeds and launch configuration as bench.py; inputs drawn on
+# the GPU (seeded Philox), the compared part copied back for the oracle.
+
+
+def test_full_layer_h64_n32k():
+    """B=1 H=64 N=32768 d=128 block=128: whole heads 0, 1, 31, 62, 63
+    (outputs and final states) against the oracle's recurrence."""
+    torch = torch_mod()
+    w = inputs.WORKLOADS["layer_h64_n32k"]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    say("case full layer_h64_n32k")
+    tq, tk, tv = inputs.device_qkv((B, H, N, d), w["seed"], "bf16")
+    lam = inputs.decay_schedule(H)
+    out, fin = la.lightning_attn_fwd(tq, tk, tv, torch.from_numpy(lam).cuda(), block=w["block"])
+    torch.cuda.synchronize()
+    heads = [0, 1, 31, 62, 63]
+    q, k, v = (host(t[:, heads]) for t in (tq, tk, tv))
+    o_ref, f_ref, _ = oracle.fwd(q, k, v, lam[heads])
+    eo, ef = rel_err(host(out[:, heads]), o_ref), rel_err(host(fin[:, heads]), f_ref)
+    say("   err out %.3e state %.3e" % (eo, ef))
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+def test_full_varlen_h64_65536():
+    """65536 packed tokens, lognormal lengths, H=64: whole sequences (first,
+    last, shortest, longest) on heads 0 and 63."""
+    torch = torch_mod()
+    w = inputs.WORKLOADS["layer_h64_varlen64k"]
+    H, total, d = w["H"], w["total"], w["d"]
+    lens = inputs.varlen_lengths(total=total, seed=w["seed"])
+    cu = inputs.cu_seqlens(lens)
+    say("case full varlen: %d sequences, max %d" % (len(lens), max(lens)))
+    tq, tk, tv = inputs.device_qkv((H, total, d), w["seed"], "bf16")
+    lam = inputs.decay_schedule(H)
+    out, fin = la.lightning_attn_fwd_varlen(tq, tk, tv, torch.from_numpy(lam).cuda(),
+                                            torch.from_numpy(cu).cuda(), block=w["block"])
+    torch.cuda.synchronize()
+    seqs = sorted({0, len(lens) - 1, int(np.argmin(lens)), int(np.argmax(lens))})
+    for h in (0, H - 1):
+        outs, refs, fs, frefs = [], [], [], []
+        for j in seqs:
+            a, b = int(cu[j]), int(cu[j + 1])
+            q, k, v = (host(t[h:h + 1, a:b])[None] for t in (tq, tk, tv))
+            o_ref, f_ref, _ = oracle.fwd(q, k, v, lam[h:h + 1])
+            outs.append(host(out[h, a:b]).ravel())
+            refs.append(o_ref.ravel())
+            fs.append(host(fin[j, h]).ravel())
+            frefs.append(f_ref.ravel())
+        eo = rel_err(np.concatenate(outs), np.concatenate(refs))
+        ef = rel_err(np.concatenate(fs), np.concatenate(frefs))
+        say("   head %d err out %.3e state %.3e" % (h, eo, ef))
+        assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+def test_full_million_h8():
+    """B=1 H=8 N=1048576 d=128 block=256 (4096 blocks carried in one
+    sequence): the first 8192 rows of heads 0 and 7 in full, single rows up to
+    the last token from the decayed left product, and final-state entries."""
+    torch = torch_mod()
+    w = inputs.WORKLOADS["million_h8"]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    say("case full million_h8")
+    tq, tk, tv = inputs.device_qkv((B, H, N, d), w["seed"], "bf16")
+    lam = inputs.decay_schedule(H)
+    out, fin = la.lightning_attn_fwd(tq, tk, tv, torch.from_numpy(lam).cuda(), block=w["block"])
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 4095, 4096, 65535, 65536, 524287, 524288, N - 2, N - 1])
+    rng = np.random.default_rng(0)
+    ij = rng.integers(0, d, (24, 2))
+    for h in (0, H - 1):
+        P = 8192
+        q, k, v = (host(t[:, h:h + 1, :P]) for t in (tq, tk, tv))
+        o_ref, _, _ = oracle.fwd(q, k, v, lam[h:h + 1])
+        e_pre = rel_err(host(out[:, h:h + 1, :P]), o_ref)
+        qh, kh, vh = (host(t[0, h]) for t in (tq, tk, tv))
+        r_ref = oracle.rows(qh, kh, vh, lam[h], rows)
+        e_rows = rel_err(host(out[0, h, rows]), r_ref)
+        s_ref = oracle.state_entries(kh, vh, lam[h], ij)
+        e_st = rel_err(host(fin[0, h])[ij[:, 0], ij[:, 1]], s_ref)
+        say("   head %d err prefix %.3e rows %.3e state %.3e" % (h, e_pre, e_rows, e_st))
+        assert max(e_pre, e_rows, e_st) <= TOL["bf16"]
+        del qh, kh, vh
+
+
+def test_full_decode_b128_h64():
+    """128 sequences x 64 heads, d=128, 256 consecutive steps from a
+    N(0, 0.1^2) state: all 256 outputs and the final state of 16 sampled
+    (sequence, head) pairs."""
+    torch = torch_mod()
+    w = inputs.WORKLOADS["decode_b128_h64"]
+    B, H, d, T = w["B"], w["H"], w["d"], w["steps"]
+    say("case full decode_b128_h64")
+    tq, tk, tv = inputs.device_qkv((T, B, H, d), w["seed"], "bf16")
+    lam = inputs.decay_schedule(H)
+    tl = torch.from_numpy(lam).cuda()
+    state = inputs.device_state((B, H, d, d), w["seed"] + 1)
+    rng = np.random.default_rng(1)
+    pairs = [(0, 0), (B - 1, H - 1)] + [tuple(x) for x in rng.integers(0, [B, H], (14, 2))]
+    bi = [p[0] for p in pairs]
+    hi = [p[1] for p in pairs]
+    S = host(state[bi, hi]).astype(np.float64)[None]  # [1, P, d, d]
+    outs = []
+    for t in range(T):
+        o = la.lightning_attn_decode(tq[t], tk[t], tv[t], tl, state)
+        outs.append(o[bi, hi].clone())
+    torch.cuda.synchronize()
+    worst = 0.0
+    for t in range(T):
+        q, k, v = (host(x[t][bi, hi])[None] for x in (tq, tk, tv))
+        o_ref, _ = oracle.decode(q, k, v, lam[hi], S)
+        worst = max(worst, rel_err(host(outs[t])[None], o_ref))
+    es = rel_err(host(state[bi, hi])[None], S)
+    say("   err out %.3e state %.3e" % (worst, es))
+    assert worst <= TOL["bf16"] and es <= TOL["bf16"]

@@ -68,6 +68,10 @@ const char *lightning_attn_status_string(la_status s);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int lightning_attn_version(void);
 
+/* Diagnostic: the HIP error string behind the most recent LA_ERR_HIP
+ * returned on the calling thread ("no HIP error" if none).  Static storage. */
+const char *lightning_attn_last_hip_error(void);
+
 /*
  * Prefill over fixed-length sequences (MiniMax-01 report, section 2.2.1,
  * block expansion; section 3.2.2 for the sequence-parallel state scan).

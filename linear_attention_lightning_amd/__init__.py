@@ -32,7 +32,10 @@ class LightningAttnError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
         name = _STATUS.get(status, str(status))
-        msg = load_library().lightning_attn_status_string(status).decode()
+        lib = load_library()
+        msg = lib.lightning_attn_status_string(status).decode()
+        if status == 4:
+            msg += ": " + lib.lightning_attn_last_hip_error().decode()
         super().__init__("%s failed: %s (%s)" % (where, name, msg))
 
 
@@ -51,6 +54,7 @@ def load_library(path=None):
     lib.lightning_attn_status_string.argtypes = [I]
     lib.lightning_attn_status_string.restype = ctypes.c_char_p
     lib.lightning_attn_version.restype = I
+    lib.lightning_attn_last_hip_error.restype = ctypes.c_char_p
     lib.lightning_attn_fwd_workspace_size.argtypes = [I, I, L, I, I, I, L]
     lib.lightning_attn_fwd_workspace_size.restype = Z
     lib.lightning_attn_fwd.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P]

@@ -81,8 +81,11 @@ Plan plan_varlen(int H, int64_t total, int d, la_dtype dt, int64_t segment_token
   return p;
 }
 
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
 la_status launch_status() {
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) g_last_hip_error = e;
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
@@ -101,7 +104,7 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
   dim3 grid((unsigned)(pl.nseg * a.m.H));
   if (use_mfma(d, dt)) {
     if (phase_a)
-      hipLaunchKernelGGL(la::mfma::local_state_kernel, grid, dim3(la::mfma::NT), 0, st, a);
+      hipLaunchKernelGGL(la::mfma::local_state_kernel, grid, dim3(la::mfma::NT_LOCAL), 0, st, a);
     else
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, a);
   } else if (dt == LA_BF16) {
@@ -163,6 +166,10 @@ const char *lightning_attn_status_string(la_status s) {
 }
 
 int lightning_attn_version(void) { return kVersion; }
+
+const char *lightning_attn_last_hip_error(void) {
+  return g_last_hip_error == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip_error);
+}
 
 size_t lightning_attn_fwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
                                          int64_t segment_tokens) {

@@ -18,6 +18,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 2^x on the hardware exponential unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A value that is the same in every lane, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 // lambda^n for a non-negative integer n, as 2^(n log2 lambda); 0 when the
 // power underflows float32 (those terms are below float32 resolution).
 __device__ __forceinline__ float pow_lam(float log2lam, float n) { return fast_exp2(n * log2lam); }

@@ -14,13 +14,15 @@
 //     NEXT chunk while the state waves store that chunk's K/V tiles;
 //   state waves 4-7: wave 4+u owns state rows 32u..32u+31 in float32 MFMA
 //     accumulators; they stream K/V tiles HBM -> registers -> LDS one chunk
-//     ahead, update the state, and publish it as bf16 S^T in a second LDS
-//     buffer for the output waves.
+//     ahead, update the state, and publish it as bf16 S^T in LDS (written
+//     after the output waves have read the previous one for this chunk's
+//     inter term, read after the end-of-chunk barrier for the next one).
 // Everything is computed transposed so the query row is each lane's fixed
 // MFMA column: the K Q^T accumulator (register quads hold 4 consecutive
 // keys) feeds V^T (K Q^T) directly as the B operand, with V read in the same
-// key order by ds_read_b64_tr_b16; a_r is one scalar per lane; outputs leave
-// as 8-byte stores of 4 consecutive features.
+// key order by ds_read_b64_tr_b16; a_r is one scalar per lane.  Each output
+// wave stages its 32 x 128 output tile in a private LDS region and writes it
+// back as whole rows (16-byte stores, 8 KB contiguous per wave).
 //
 // MFMA 32x32x16 operand layout (lane l, l32 = l % 32, g = l / 32):
 //   A[m][k]: lane holds m = l32, k = 8g .. 8g+7
@@ -46,10 +48,11 @@ constexpr int T = 128;           // tokens per chunk
 constexpr int NT = 512;          // threads per workgroup of the chunk kernel (8 waves)
 constexpr int NT_LOCAL = 256;    // threads per workgroup of the local-state kernel
 constexpr int RSK = 2 * D + 32;  // LDS row stride (bytes) of K and V tiles
-constexpr int RST = 2 * D + 16;  // LDS row stride (bytes) of S^T
+constexpr int RST = 2 * D + 16;  // LDS row stride (bytes) of S^T and output staging
 constexpr int LDS_K = T * RSK;
 constexpr int LDS_ST = D * RST;
-constexpr int LDS_BYTES = 2 * LDS_K + 2 * LDS_ST;
+constexpr int LDS_O = T * RST;   // output staging: 32 rows per output wave
+constexpr int LDS_BYTES = 2 * LDS_K + LDS_ST + LDS_O;
 constexpr float kFastLog2 = -15.f;  // factored powers when log2(lambda) > this
 
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -200,7 +203,7 @@ __device__ __forceinline__ void inter_term(f32x16 (&acc)[4], const char *STs, co
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_chunk_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  char *Ks = smem, *Vs = smem + LDS_K, *ST0 = Vs + LDS_K;
+  char *Ks = smem, *Vs = smem + LDS_K, *STs = Vs + LDS_K, *Os = STs + LDS_ST;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool out_wave = wave < 4;
   const int w = wave & 3;  // output rows 32w.. or state rows 32w..
@@ -208,7 +211,7 @@ void prefill_chunk_kernel(FwdArgs p) {
   const SeqMap &m = p.m;
   const int H = m.H;
   const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  const float l2 = log2f(p.decay[h]);
+  const float l2 = uniform(log2f(p.decay[h]));
   const bool fast = l2 > kFastLog2;
   const int64_t a = (int64_t)s * p.seg_len;
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
@@ -219,7 +222,7 @@ void prefill_chunk_kernel(FwdArgs p) {
 
   float tail[8];  // lambda^(7-s) for s = 0..7 (also lambda^(3-m) = tail[4+m])
 #pragma unroll
-  for (int i = 0; i < 8; ++i) tail[i] = fast_exp2((float)(7 - i) * l2);
+  for (int i = 0; i < 8; ++i) tail[i] = uniform(fast_exp2((float)(7 - i) * l2));
 
   const int row = 32 * w + l32;  // output waves: this lane's query row
   const int tr_sub = (i16 >> 2) * RSK + (16 * (G16 & 1) + 4 * (i16 & 3)) * 2;
@@ -247,11 +250,10 @@ void prefill_chunk_kernel(FwdArgs p) {
     load_tile<256>(pv, (const bf16 *)p.v + base, L0, ts);
     store_tile<256>(Ks, pk, ts);
     store_tile<256>(Vs, pv, ts);
-    write_st(ST0, S, w, l32, g);
+    write_st(STs, S, w, l32, g);
   }
   __syncthreads();
-  int buf = 0;  // S^T buffer holding the state entering the current chunk
-  if (out_wave) inter_term(acc, ST0, qf, fast_exp2((float)(row + 1) * l2), l32, g);
+  if (out_wave) inter_term(acc, STs, qf, fast_exp2((float)(row + 1) * l2), l32, g);
 
   while (true) {
     const Cursor nxt = next_chunk(m, cur, b, T);
@@ -299,17 +301,27 @@ void prefill_chunk_kernel(FwdArgs p) {
           }
         }
       }
-      // Store: acc[jt] registers 4rq..4rq+3 hold features 32jt + 8rq + 4g + 0..3.
-      if (row < L) {
-        bf16 *orow = (bf16 *)p.out + m.row_base(h, cur.j) + (cur.c0 + row) * D;
+      // Stage the tile in this wave's LDS rows (acc[jt] registers 4rq..4rq+3
+      // hold features 32jt + 8rq + 4g + 0..3 of `row`), then write whole rows.
+      {
+        char *orow_lds = Os + row * RST;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
             bf16x4 v = {(bf16)acc[jt][4 * rq], (bf16)acc[jt][4 * rq + 1],
                         (bf16)acc[jt][4 * rq + 2], (bf16)acc[jt][4 * rq + 3]};
-            *(bf16x4 *)(orow + 32 * jt + 8 * rq + 4 * g) = v;
+            *(bf16x4 *)(orow_lds + (32 * jt + 8 * rq + 4 * g) * 2) = v;
           }
+        // the wave's own 32 rows: lane reads 16 bytes of row 32w + 4it + lane/16
+        const int r0 = 32 * w + (lane >> 4), c16 = lane & 15;
+        bf16 *obase = (bf16 *)p.out + m.row_base(h, cur.j) + (cur.c0 + r0) * D + c16 * 8;
+        const char *lbase = Os + r0 * RST + c16 * 16;
+#pragma unroll 2
+        for (int it = 0; it < 8; ++it) {
+          const uint4 x = *(const uint4 *)(lbase + 4 * it * RST);
+          if (r0 + 4 * it < L) *(uint4 *)(obase + 4 * it * D) = x;
+        }
       }
     } else {
       if (nxt.valid) {
@@ -329,15 +341,14 @@ void prefill_chunk_kernel(FwdArgs p) {
       }
       if (new_piece)
         load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, w, l32, g);
-      if (nxt.valid) write_st(ST0 + (buf ^ 1) * LDS_ST, S, w, l32, g);
+      if (nxt.valid) write_st(STs, S, w, l32, g);
     }
     __syncthreads();  // this chunk's K/V reads are done; next S^T is published
     if (!nxt.valid) break;
-    buf ^= 1;
     if (out_wave) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) qf[ks] = qn[ks];
-      inter_term(acc, ST0 + buf * LDS_ST, qf, fast_exp2((float)(row + 1) * l2), l32, g);
+      inter_term(acc, STs, qf, fast_exp2((float)(row + 1) * l2), l32, g);
     } else {
       store_tile<256>(Ks, pk, ts);
       store_tile<256>(Vs, pv, ts);
@@ -358,18 +369,21 @@ void local_state_kernel(FwdArgs p) {
   const SeqMap &m = p.m;
   const int H = m.H;
   const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  const float l2 = log2f(p.decay[h]);
+  const float l2 = uniform(log2f(p.decay[h]));
   const bool fast = l2 > kFastLog2;
   const int64_t a = (int64_t)s * p.seg_len;
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
   if (a >= b) return;
   const int jl = m.seq_of(b - 1);
+  // A segment whose last piece ends its sequence hands no state onward: the
+  // scan never uses its local state.
+  if (m.start(jl + 1) == b) return;
   const int64_t ps0 = m.start(jl);
   const int64_t ps = ps0 > a ? ps0 : a;
   const int64_t base = m.row_base(h, jl);
   float tail[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) tail[i] = fast_exp2((float)(7 - i) * l2);
+  for (int i = 0; i < 8; ++i) tail[i] = uniform(fast_exp2((float)(7 - i) * l2));
 
   f32x16 S[4];
 #pragma unroll

@@ -125,6 +125,9 @@ __global__ __launch_bounds__(NT) void local_state_kernel(FwdArgs p) {
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
   if (a >= b) return;
   const int jl = m.seq_of(b - 1);
+  // A segment whose last piece ends its sequence hands no state onward: the
+  // scan never uses its local state.
+  if (m.start(jl + 1) == b) return;
   const int64_t ps0 = m.start(jl);
   const int64_t ps = ps0 > a ? ps0 : a;
   const int64_t base = m.row_base(h, jl);

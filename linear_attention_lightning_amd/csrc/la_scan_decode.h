@@ -51,7 +51,9 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
     const int64_t ps = ps0 > a ? ps0 : a;
     const float gam = pow_lam(log2lam, (float)(b - ps));
     const f32x4 base = (ps == a) ? sin : init4(jl);
-    carry = gam * base + loc;
+    // When the segment's last sequence ends at b, loc was never written and
+    // the carry is unused: the next segment starts a new sequence.
+    carry = (m.start(jl + 1) == b) ? (f32x4){0.f, 0.f, 0.f, 0.f} : gam * base + loc;
   }
   if (p.fin) {
     for (int j = 0; j < m.num_seqs; ++j)

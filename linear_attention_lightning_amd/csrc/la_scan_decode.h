@@ -67,7 +67,10 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
 //   S <- lambda S + k^T v;  o = q S.
 // The state is streamed once: thread (rg, cg) owns columns 4cg..4cg+3 of
 // D/RG consecutive rows; all its loads are issued before any store, and the
-// per-row-group partial outputs are summed through LDS.
+// per-row-group partial outputs are summed through LDS.  State loads and
+// stores are non-temporal: each byte is touched once per step and a batch's
+// state (512 MiB at 128 x 64 heads) is larger than the 256 MB Infinity Cache,
+// so keeping it out of the caches frees them for everything else.
 template <typename Tin, int D>
 __global__ __launch_bounds__(256) void decode_kernel(const Tin *__restrict__ q,
                                                      const Tin *__restrict__ k,
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const Tin *__restrict__ q,
   f32x4 *S = (f32x4 *)(state + bh * (int64_t)D * D);
   f32x4 sv[RPT];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) sv[r] = S[(rg * RPT + r) * CG + cg];
+  for (int r = 0; r < RPT; ++r) sv[r] = __builtin_nontemporal_load(&S[(rg * RPT + r) * CG + cg]);
   __syncthreads();
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const Tin *__restrict__ q,
     const int i = rg * RPT + r;
     sv[r] = lam * sv[r] + ks[i] * vv;
     o += qs[i] * sv[r];
-    S[i * CG + cg] = sv[r];
+    __builtin_nontemporal_store(sv[r], &S[i * CG + cg]);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) red[rg][4 * cg + u] = o[u];

@@ -199,67 +199,87 @@ __device__ __forceinline__ void inter_term(f32x16 (&acc)[4], const char *STs, co
   for (int jt = 0; jt < 4; ++jt) acc[jt] *= a_row;
 }
 
-// Phase C: outputs (and final states) for one (segment, head).
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_chunk_kernel(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+// Per-workgroup constants and lane coordinates of the 8-wave layout.
+struct Lanes {
+  int tid, lane, wave, w, l32, g, G16, i16, row, tr_sub, ts;
+  bool out_wave;
+  __device__ __forceinline__ Lanes() {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = tid >> 6;
+    out_wave = wave < 4;
+    w = wave & 3;  // output rows 32w.. or state rows 32w..
+    l32 = lane & 31;
+    g = lane >> 5;
+    G16 = lane >> 4;
+    i16 = lane & 15;
+    row = 32 * w + l32;  // output waves: this lane's query row in the chunk
+    tr_sub = (i16 >> 2) * RSK + (16 * (G16 & 1) + 4 * (i16 & 3)) * 2;
+    ts = tid - 256;  // state waves: index among the 256 loaders
+  }
+};
+
+struct Decay {
+  float l2;       // log2(lambda), uniform
+  bool fast;      // factored powers allowed
+  float tail[8];  // lambda^(7-s), s = 0..7 (also lambda^(3-m) = tail[4+m])
+  __device__ __forceinline__ explicit Decay(float lam) {
+    l2 = uniform(log2f(lam));
+    fast = l2 > kFastLog2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tail[i] = uniform(fast_exp2((float)(7 - i) * l2));
+  }
+};
+
+// Issues this chunk's loads: Q^T fragments for output waves, K and V rows for
+// state waves (Y as qf or pk/pv).
+__device__ __forceinline__ void issue_chunk_loads(const FwdArgs &p, int h, const Cursor &c,
+                                                  uint4 *Y, const Lanes &ln) {
+  const SeqMap &m = p.m;
+  const int Lc = (int)(c.c1 - c.c0);
+  if (ln.out_wave) {
+    load_qf(Y, (const bf16 *)p.q + m.row_base(h, c.j) + (c.c0 + ln.row) * D, ln.row < Lc, ln.g);
+  } else {
+    const int64_t base = m.row_base(h, c.j) + c.c0 * D;
+    load_tile<256>(Y, (const bf16 *)p.k + base, Lc, ln.ts);
+    load_tile<256>(Y + 8, (const bf16 *)p.v + base, Lc, ln.ts);
+  }
+}
+
+// The chunk loop over segment [cur.c0, b) of head h.  On entry the state
+// waves hold the state entering the segment in X, and the first chunk's
+// loads are in flight into Y (issue_chunk_loads).  Writes outputs and, at
+// every sequence end inside the segment, that sequence's final state.
+__device__ __forceinline__ void chunk_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
+                                           f32x16 (&X)[4], uint4 (&Y)[16], char *smem,
+                                           const Decay &dc, const Lanes &ln) {
   char *Ks = smem, *Vs = smem + LDS_K, *STs = Vs + LDS_K, *Os = STs + LDS_ST;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool out_wave = wave < 4;
-  const int w = wave & 3;  // output rows 32w.. or state rows 32w..
-  const int l32 = lane & 31, g = lane >> 5, G16 = lane >> 4, i16 = lane & 15;
   const SeqMap &m = p.m;
   const int H = m.H;
-  const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  const float l2 = uniform(log2f(p.decay[h]));
-  const bool fast = l2 > kFastLog2;
-  const int64_t a = (int64_t)s * p.seg_len;
-  const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
   const int64_t DD = (int64_t)D * D;
-
-  Cursor cur = first_chunk(m, a, b, T);
-  if (!cur.valid) return;
-
-  float tail[8];  // lambda^(7-s) for s = 0..7 (also lambda^(3-m) = tail[4+m])
-#pragma unroll
-  for (int i = 0; i < 8; ++i) tail[i] = uniform(fast_exp2((float)(7 - i) * l2));
-
-  const int row = 32 * w + l32;  // output waves: this lane's query row
-  const int tr_sub = (i16 >> 2) * RSK + (16 * (G16 & 1) + 4 * (i16 & 3)) * 2;
-  const int ts = tid - 256;      // state waves: index among the 256 loaders
-
+  const int w = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane, row = ln.row;
+  const float l2 = dc.l2;
+  const bool fast = dc.fast;
   // The two roles share registers: X is the output accumulator (output
   // waves) or the state (state waves); Y holds this and the next chunk's Q^T
   // fragments (output waves) or the next chunk's K and V (state waves).
-  f32x16 X[4];
-  uint4 Y[16];
   f32x16 (&acc)[4] = X;
   f32x16 (&S)[4] = X;
   uint4 *qf = Y, *qn = Y + 8, *pk = Y, *pv = Y + 8;
 
-  if (out_wave) {
-    const int L0 = (int)(cur.c1 - cur.c0);
-    load_qf(qf, (const bf16 *)p.q + m.row_base(h, cur.j) + (cur.c0 + row) * D, row < L0, g);
-  } else {
-    const float *s0 = p.ws ? p.ws + ((int64_t)s * H + h) * DD
-                           : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
-    load_state(S, s0, w, l32, g);
-    const int64_t base = m.row_base(h, cur.j) + cur.c0 * D;
-    const int L0 = (int)(cur.c1 - cur.c0);
-    load_tile<256>(pk, (const bf16 *)p.k + base, L0, ts);
-    load_tile<256>(pv, (const bf16 *)p.v + base, L0, ts);
-    store_tile<256>(Ks, pk, ts);
-    store_tile<256>(Vs, pv, ts);
+  if (!ln.out_wave) {
+    store_tile<256>(Ks, pk, ln.ts);
+    store_tile<256>(Vs, pv, ln.ts);
     write_st(STs, S, w, l32, g);
   }
   __syncthreads();
-  if (out_wave) inter_term(acc, STs, qf, fast_exp2((float)(row + 1) * l2), l32, g);
+  if (ln.out_wave) inter_term(acc, STs, qf, fast_exp2((float)(row + 1) * l2), l32, g);
 
   while (true) {
     const Cursor nxt = next_chunk(m, cur, b, T);
     const int L = (int)(cur.c1 - cur.c0);
     __syncthreads();  // K/V of this chunk are in LDS; inter term done
-    if (out_wave) {
+    if (ln.out_wave) {
       if (nxt.valid) {
         const int Ln = (int)(nxt.c1 - nxt.c0);
         load_qf(qn, (const bf16 *)p.q + m.row_base(h, nxt.j) + (nxt.c0 + row) * D, row < Ln, g);
@@ -279,7 +299,7 @@ void prefill_chunk_kernel(FwdArgs p) {
             const float e = fast_exp2((float)(n0 - 3) * l2);
 #pragma unroll
             for (int mm = 0; mm < 4; ++mm)
-              pt[4 * q + mm] = (n0 >= mm) ? pt[4 * q + mm] * (e * tail[4 + mm]) : 0.f;
+              pt[4 * q + mm] = (n0 >= mm) ? pt[4 * q + mm] * (e * dc.tail[4 + mm]) : 0.f;
           } else {
 #pragma unroll
             for (int mm = 0; mm < 4; ++mm)
@@ -296,7 +316,7 @@ void prefill_chunk_kernel(FwdArgs p) {
           const int c0 = 32 * kc + 16 * q2 + 4 * g;
 #pragma unroll
           for (int jt = 0; jt < 4; ++jt) {
-            bf16x8 vf = tr_read8(Vs + c0 * RSK + (32 * jt) * 2 + tr_sub, 8 * RSK);
+            bf16x8 vf = tr_read8(Vs + c0 * RSK + (32 * jt) * 2 + ln.tr_sub, 8 * RSK);
             acc[jt] = mma(vf, pb, acc[jt]);
           }
         }
@@ -327,8 +347,8 @@ void prefill_chunk_kernel(FwdArgs p) {
       if (nxt.valid) {
         const int64_t base = m.row_base(h, nxt.j) + nxt.c0 * D;
         const int Ln = (int)(nxt.c1 - nxt.c0);
-        load_tile<256>(pk, (const bf16 *)p.k + base, Ln, ts);
-        load_tile<256>(pv, (const bf16 *)p.v + base, Ln, ts);
+        load_tile<256>(pk, (const bf16 *)p.k + base, Ln, ln.ts);
+        load_tile<256>(pv, (const bf16 *)p.v + base, Ln, ln.ts);
       }
       const bool seq_done = (cur.c1 == cur.seq_end);
       const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
@@ -336,7 +356,7 @@ void prefill_chunk_kernel(FwdArgs p) {
         const float gL = fast_exp2((float)L * l2);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) S[nt] *= gL;
-        state_update(S, Ks, Vs, L, L - 1, l2, fast, tail, w, lane);
+        state_update(S, Ks, Vs, L, L - 1, l2, fast, dc.tail, w, lane);
         if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
       }
       if (new_piece)
@@ -345,16 +365,207 @@ void prefill_chunk_kernel(FwdArgs p) {
     }
     __syncthreads();  // this chunk's K/V reads are done; next S^T is published
     if (!nxt.valid) break;
-    if (out_wave) {
+    if (ln.out_wave) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) qf[ks] = qn[ks];
       inter_term(acc, STs, qf, fast_exp2((float)(row + 1) * l2), l32, g);
     } else {
-      store_tile<256>(Ks, pk, ts);
-      store_tile<256>(Vs, pv, ts);
+      store_tile<256>(Ks, pk, ln.ts);
+      store_tile<256>(Vs, pv, ln.ts);
     }
     cur = nxt;
   }
+}
+
+// Phase C: outputs (and final states) for one (segment, head), from the
+// segment's entering state (scan result, initial state or zero).
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_chunk_kernel(FwdArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  const Lanes ln;
+  const SeqMap &m = p.m;
+  const int H = m.H;
+  const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const Decay dc(p.decay[h]);
+  const int64_t a = (int64_t)s * p.seg_len;
+  const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
+  const int64_t DD = (int64_t)D * D;
+  const Cursor cur = first_chunk(m, a, b, T);
+  if (!cur.valid) return;
+  f32x16 X[4];
+  uint4 Y[16];
+  if (!ln.out_wave) {
+    const float *s0 = p.ws ? p.ws + ((int64_t)s * H + h) * DD
+                           : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
+    load_state(X, s0, ln.w, ln.l32, ln.g);
+  }
+  issue_chunk_loads(p, h, cur, Y, ln);
+  chunk_loop(p, h, b, cur, X, Y, smem, dc, ln);
+}
+
+// Single-pass prefill with the segment scan folded in (MiniMax-01 report,
+// section 3.2.2, LASP+: local prefix state, combine with the preceding
+// prefix, local outputs -- here between segments of one GPU).  Workgroups
+// take segments in ticket order (segment-major, heads fastest); each one
+//   1. computes its segment's local state L (K/V streamed from HBM),
+//   2. receives the state entering its segment from the workgroup of the
+//      previous segment of the same head (a flag and a float32 record in the
+//      workspace), and publishes its own end state gamma * S_in + L,
+//   3. runs the chunk loop from that entering state; its K/V re-reads come
+//      from the Infinity Cache, since segments are short enough for every
+//      resident workgroup's K/V to stay there.
+// A workgroup only ever waits on a lower ticket, which a running workgroup
+// already holds, so the waits cannot deadlock; a wait that exceeds
+// kSpinLimit polls gives up, sets *err and continues (wrong output, no hang).
+struct FusedArgs {
+  FwdArgs f;         // f.ws: end-state records [nseg][H][D][D]
+  unsigned *flags;   // [nseg * H], zero on entry: record published
+  unsigned *ticket;  // zero on entry
+  unsigned *err;     // set to 1 if a wait timed out
+};
+
+constexpr int kSpinLimit = 1 << 18;
+
+__global__ void fused_reset_kernel(unsigned *words, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) words[i] = 0u;
+}
+
+// Hand-off records and flags use device-scope (agent) atomic accesses, which
+// bypass the XCD-private L2, so publishing one needs no L2-wide write-back
+// and reading one no L2-wide invalidation -- both of which would stall every
+// workgroup on the XCD.
+__device__ __forceinline__ float load_handoff(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_handoff(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// X (local state L on entry) <- the state entering the segment, read from
+// `prev` (the previous segment's record when `prev_is_record`, else the
+// sequence's initial state, or zero when NULL).  When `publish`, also writes
+// gamma * base + L to the record `rec`, with base = the entering state
+// (from_prev) or the last piece's own initial state `ini_last`.
+__device__ __forceinline__ void combine_states(f32x16 (&X)[4], const float *prev,
+                                               bool prev_is_record, const float *ini_last,
+                                               bool from_prev, bool publish, float gam,
+                                               float *rec, int u, int l32, int g) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int off = (32 * u + 8 * q + 4 * g) * D + l32;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const int o = off + mm * D + 32 * nt;
+        const float in = !prev ? 0.f : prev_is_record ? load_handoff(prev + o) : prev[o];
+        if (publish) {
+          const float base = from_prev ? in : (ini_last ? ini_last[o] : 0.f);
+          store_handoff(rec + o, gam * base + X[nt][4 * q + mm]);
+        }
+        X[nt][4 * q + mm] = in;
+      }
+  }
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_fused_kernel(FusedArgs fa) {
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  __shared__ unsigned sh_ticket;
+  const FwdArgs &p = fa.f;
+  const Lanes ln;
+  const SeqMap &m = p.m;
+  const int H = m.H;
+  if (ln.tid == 0)
+    sh_ticket = __hip_atomic_fetch_add(fa.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const unsigned t = sh_ticket;
+  const int s = (int)(t / (unsigned)H), h = (int)(t - (t / (unsigned)H) * (unsigned)H);
+  const Decay dc(p.decay[h]);
+  const int64_t a = (int64_t)s * p.seg_len;
+  const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
+  const int64_t DD = (int64_t)D * D;
+  const Cursor cur = first_chunk(m, a, b, T);
+  if (!cur.valid) return;
+  char *Ks = smem, *Vs = smem + LDS_K;
+  const int jf = cur.j;
+  const bool need_in = m.start(jf) < a;   // the segment starts inside a sequence
+  const int jl = m.seq_of(b - 1);
+  const int64_t ps0 = m.start(jl);
+  const int64_t ps = ps0 > a ? ps0 : a;   // start of the segment's last piece
+  const bool need_out = m.start(jl + 1) > b;  // that sequence continues after b
+  f32x16 X[4];
+  uint4 Y[16];
+
+  // 1. L = sum over the last piece of lambda^(b-1-c) k_c^T v_c: state waves
+  //    accumulate, output waves stream the K/V tiles through LDS.
+  if (need_out) {
+    if (!ln.out_wave) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) X[nt] = (f32x16){};
+    }
+    const int64_t kvb = m.row_base(h, jl);
+    int64_t t0 = ps;
+    int Lt = (int)((b - t0) < T ? (b - t0) : T);
+    if (ln.out_wave) {
+      load_tile<256>(Y, (const bf16 *)p.k + kvb + t0 * D, Lt, ln.tid);
+      load_tile<256>(Y + 8, (const bf16 *)p.v + kvb + t0 * D, Lt, ln.tid);
+    }
+    while (t0 < b) {
+      if (ln.out_wave) {
+        store_tile<256>(Ks, Y, ln.tid);
+        store_tile<256>(Vs, Y + 8, ln.tid);
+      }
+      __syncthreads();
+      const int Lc = Lt;
+      const int64_t t1 = t0 + T;
+      if (t1 < b) {
+        Lt = (int)((b - t1) < T ? (b - t1) : T);
+        if (ln.out_wave) {
+          load_tile<256>(Y, (const bf16 *)p.k + kvb + t1 * D, Lt, ln.tid);
+          load_tile<256>(Y + 8, (const bf16 *)p.v + kvb + t1 * D, Lt, ln.tid);
+        }
+      }
+      if (!ln.out_wave)
+        state_update(X, Ks, Vs, Lc, (int)(b - 1 - t0), dc.l2, dc.fast, dc.tail, ln.w, ln.lane);
+      __syncthreads();
+      t0 = t1;
+    }
+  }
+
+  // 2. The first chunk's loads go out while waiting for the entering state.
+  issue_chunk_loads(p, h, cur, Y, ln);
+  if (need_in && ln.tid == 0) {
+    const unsigned *fl = fa.flags + (size_t)(s - 1) * H + h;
+    int it = 0;
+    while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (++it > kSpinLimit) {
+        *fa.err = 1u;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();  // the record loads below are issued after the flag was seen
+  if (!ln.out_wave) {
+    const float *prev = need_in ? p.ws + ((int64_t)(s - 1) * H + h) * DD
+                                : (p.init ? p.init + ((int64_t)jf * H + h) * DD : nullptr);
+    const float *ini_last = p.init ? p.init + ((int64_t)jl * H + h) * DD : nullptr;
+    const float gam = fast_exp2((float)(b - ps) * dc.l2);
+    combine_states(X, prev, need_in, ini_last, ps == a, need_out, gam,
+                   p.ws + ((int64_t)s * H + h) * DD, ln.w, ln.l32, ln.g);
+  }
+  if (need_out) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's record stores have completed
+    __syncthreads();
+    if (ln.tid == 0)
+      __hip_atomic_store(fa.flags + (size_t)s * H + h, 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 3. Outputs from the entering state.
+  chunk_loop(p, h, b, cur, X, Y, smem, dc, ln);
 }
 
 // Phase A: the local state of each segment's last piece, from zero:
@@ -368,7 +579,9 @@ void local_state_kernel(FwdArgs p) {
   const int l32 = lane & 31, g = lane >> 5;
   const SeqMap &m = p.m;
   const int H = m.H;
-  const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  // Segments in reverse dispatch order: the K/V read last are the first
+  // segments', which the output pass reads first (Infinity Cache hits).
+  const int s = p.nseg - 1 - (int)(blockIdx.x / H), h = blockIdx.x - (blockIdx.x / H) * H;
   const float l2 = uniform(log2f(p.decay[h]));
   const bool fast = l2 > kFastLog2;
   const int64_t a = (int64_t)s * p.seg_len;

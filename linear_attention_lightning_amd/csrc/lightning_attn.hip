@@ -3,6 +3,8 @@
 #include "lightning_attn.h"
 
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "la_common.h"
 #include "la_prefill_mfma.h"
@@ -29,17 +31,44 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Plan {
   int64_t seg;   // segment length (tokens)
   int64_t nseg;  // segments per head
-  bool scan;     // phases A and B needed
+  bool scan;     // segments must hand states on (a scan is needed)
+  bool fused;    // single-pass kernel hands states on itself (else 3 phases)
   size_t ws_bytes;
 };
 
 size_t state_bytes(int64_t count, int d) { return (size_t)count * (size_t)d * (size_t)d * 4; }
 
+// Workspace of the single-pass kernel: end-state records, then one flag per
+// (segment, head), a ticket counter and an error word.
+size_t fused_ws_bytes(int64_t nseg, int H, int d) {
+  return state_bytes(nseg * H, d) + (size_t)(nseg * H + 2) * 4;
+}
+
+// Prefill path.  The three-phase path (local states, scan, outputs) is the
+// default.  The single-pass kernel (hand-offs between segments through the
+// workspace, K/V re-reads from the Infinity Cache) moves a third less HBM
+// traffic but serialises each workgroup's local-state pass, hand-off and
+// outputs; on MI355X it measured level with the default at its best segment
+// length (0.70 ms at B1 H64 N32768), so it is opt-in:
+// LIGHTNING_ATTN_PREFILL=fused selects it (MFMA path only), =phased forces
+// the default.  Results agree up to rounding.
+bool want_fused(int H, int d, la_dtype dt) {
+  (void)H;
+  if (!use_mfma(d, dt)) return false;
+  const char *e = getenv("LIGHTNING_ATTN_PREFILL");
+  return e && strcmp(e, "fused") == 0;
+}
+
+// Segment length of the single-pass kernel: one round of 256 resident
+// workgroups at the 64-head layer shape (fewest hand-offs), while the K/V of
+// a round (256 x seg x 512 B) mostly stay in the 256 MB Infinity Cache.
+constexpr int64_t kFusedSeg = 8192;
+
 // Fixed-length plan.  Without a scan each sequence is one segment.  With
 // one, the token axis of every head is cut into equal segments so that
 // about kTargetGroups workgroups run per phase.
 Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tokens) {
-  Plan p{N, B, false, 0};
+  Plan p{N, B, false, false, 0};
   const int64_t total = (int64_t)B * N;
   if (total == 0) {
     p.nseg = 0;
@@ -59,25 +88,31 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
       if (seg >= N) seg = N;
     }
   }
+  const bool fused = want_fused(H, d, dt);
+  if (fused && segment_tokens <= 0 && seg != N && seg > kFusedSeg) seg = kFusedSeg;
   p.seg = seg;
   p.scan = (seg != N);
+  p.fused = p.scan && fused;
   p.nseg = ceil_div(total, seg);
-  p.ws_bytes = p.scan ? state_bytes(p.nseg * H, d) : 0;
+  p.ws_bytes = !p.scan ? 0 : p.fused ? fused_ws_bytes(p.nseg, H, d) : state_bytes(p.nseg * H, d);
   return p;
 }
 
 Plan plan_varlen(int H, int64_t total, int d, la_dtype dt, int64_t segment_tokens) {
-  Plan p{1, 0, true, 0};
+  Plan p{1, 0, true, false, 0};
   if (total == 0) return p;
   const int T = chunk_tokens(d, dt);
+  const bool fused = want_fused(H, d, dt);
   int64_t seg = segment_tokens;
   if (seg <= 0) {
     const int64_t G = ceil_div(kTargetGroups, H);
     seg = ceil_div(ceil_div(total, G), T) * T;
+    if (fused && seg > kFusedSeg) seg = kFusedSeg;
   }
   p.seg = seg;
+  p.fused = fused;
   p.nseg = ceil_div(total, seg);
-  p.ws_bytes = state_bytes(p.nseg * H, d);
+  p.ws_bytes = fused ? fused_ws_bytes(p.nseg, H, d) : state_bytes(p.nseg * H, d);
   return p;
 }
 
@@ -121,6 +156,22 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
                   hipStream_t st) {
   la::FwdArgs a = base;
   const int H = a.m.H;
+  if (pl.fused && pl.nseg > 0) {
+    // flags, ticket and error word live right after the end-state records
+    unsigned *words = (unsigned *)((char *)a.ws + state_bytes(pl.nseg * H, d));
+    const int nwords = (int)(pl.nseg * H + 2);
+    hipLaunchKernelGGL(la::mfma::fused_reset_kernel, dim3((unsigned)ceil_div(nwords, 256)),
+                       dim3(256), 0, st, words, nwords);
+    if (has_empty) {
+      la::ScanArgs s{a.m, a.decay, pl.seg, 0, d, a.init, a.fin, a.ws};
+      hipLaunchKernelGGL(la::segment_scan_kernel, dim3((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024)),
+                         dim3(256), 0, st, s);
+    }
+    la::mfma::FusedArgs fa{a, words, words + pl.nseg * H, words + pl.nseg * H + 1};
+    hipLaunchKernelGGL(la::mfma::prefill_fused_kernel, dim3((unsigned)(pl.nseg * H)),
+                       dim3(la::mfma::NT), 0, st, fa);
+    return launch_status();
+  }
   if (pl.scan && pl.nseg > 0) {
     launch_phase(a, pl, d, dt, st, /*phase_a=*/true);
   }

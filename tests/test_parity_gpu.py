@@ -21,6 +21,17 @@ pytestmark = pytest.mark.gpu
 TOL = {"fp32": 1e-4, "bf16": 2e-2}
 
 
+@pytest.fixture(params=["auto", "phased", "fused"])
+def prefill_path(request, monkeypatch):
+    """Runs a test once per prefill path: the library's own choice, the
+    three-phase segment scan, and the single-pass kernel (bf16, d = 128)."""
+    if request.param == "auto":
+        monkeypatch.delenv("LIGHTNING_ATTN_PREFILL", raising=False)
+    else:
+        monkeypatch.setenv("LIGHTNING_ATTN_PREFILL", request.param)
+    return request.param
+
+
 def torch_mod():
     import torch
     return torch
@@ -81,7 +92,7 @@ def test_mid_bf16_workload():
 
 
 @pytest.mark.parametrize("seg", [4096, 128, 640, 1000, 8192])
-def test_segment_split_invariance_bf16(seg):
+def test_segment_split_invariance_bf16(seg, prefill_path):
     """Any cut of the token axis into segments (on-device LASP+ scan) gives
     the oracle's result: segments of one block, ragged segments, segments
     spanning two sequences."""
@@ -89,7 +100,7 @@ def test_segment_split_invariance_bf16(seg):
 
 
 @pytest.mark.parametrize("N", [1, 2, 127, 128, 129, 300, 1000])
-def test_ragged_tails_bf16(N):
+def test_ragged_tails_bf16(N, prefill_path):
     run_fwd_case(2, 3, N, 128, "bf16", seed=30 + N, with_init=True,
                  lam=[0.9961, 0.3997, 0.75])
 
@@ -101,8 +112,9 @@ def test_vector_alu_paths(d, dtype, N, seg):
                  lam=[0.999, 0.5, 0.9])
 
 
-def test_initial_state_bf16():
+def test_initial_state_bf16(prefill_path):
     run_fwd_case(1, 4, 2048, 128, "bf16", seed=50, with_init=True, seg=512)
+    run_fwd_case(2, 40, 1500, 128, "bf16", seed=51, with_init=True)
 
 
 def test_zero_length_returns_initial_state():
@@ -121,10 +133,10 @@ def test_zero_length_returns_initial_state():
     assert torch.count_nonzero(fin).item() == 0
 
 
-def test_deterministic_bitwise():
+def test_deterministic_bitwise(prefill_path):
     torch = torch_mod()
-    (tq, tk, tv), _ = dev_inputs((1, 8, 8192, 128), 60, "bf16")
-    tl = torch.from_numpy(inputs.decay_schedule(8)).cuda()
+    (tq, tk, tv), _ = dev_inputs((1, 48, 8192, 128), 60, "bf16")
+    tl = torch.from_numpy(inputs.decay_schedule(48)).cuda()
     o1, f1 = la.lightning_attn_fwd(tq, tk, tv, tl)
     o2, f2 = la.lightning_attn_fwd(tq, tk, tv, tl)
     torch.cuda.synchronize()
@@ -155,7 +167,7 @@ def run_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True):
 
 
 @pytest.mark.parametrize("seg", [0, 128, 200, 100000])
-def test_varlen_bf16(seg):
+def test_varlen_bf16(seg, prefill_path):
     run_varlen_case([300, 0, 1, 129, 1024, 5, 0, 640, 2000], 4, 128, "bf16", seed=70, seg=seg)
 
 
@@ -223,7 +235,7 @@ def test_decode_matches_prefill_rows():
 # the GPU (seeded Philox), the compared part copied back for the oracle.
 
 
-def test_full_layer_h64_n32k():
+def test_full_layer_h64_n32k(prefill_path):
     """B=1 H=64 N=32768 d=128 block=128: whole heads 0, 1, 31, 62, 63
     (outputs and final states) against the oracle's recurrence."""
     torch = torch_mod()
@@ -242,7 +254,7 @@ def test_full_layer_h64_n32k():
     assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
 
 
-def test_full_varlen_h64_65536():
+def test_full_varlen_h64_65536(prefill_path):
     """65536 packed tokens, lognormal lengths, H=64: whole sequences (first,
     last, shortest, longest) on heads 0 and 63."""
     torch = torch_mod()

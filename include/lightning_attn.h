@@ -23,9 +23,14 @@
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers owned by the caller.  The library
- *     never allocates device memory, never synchronises, keeps no state
- *     between calls and is re-entrant; every kernel is launched asynchronously
- *     on `hip_stream` (a hipStream_t; NULL = the null stream).
+ *     never allocates device memory, never synchronises and is re-entrant; the
+ *     only state it keeps between calls is the per-thread diagnostic string of
+ *     lightning_attn_last_hip_error.  Every kernel is launched asynchronously
+ *     on `hip_stream` (a hipStream_t; NULL = the null stream).  The prefill
+ *     schedule may be chosen with the environment variable
+ *     LIGHTNING_ATTN_PREFILL=phased|fused (read at each call, the workspace
+ *     size queries included, so keep it fixed between a query and the call
+ *     it sizes; default phased); both give the same results up to rounding.
  *   - Arrays are dense and row-major with d fastest.  Outputs must not alias
  *     inputs (decode's `state` is read-modify-write by design).
  *   - q, k, v and out share one element type: LA_BF16 (bfloat16) or LA_FP32.

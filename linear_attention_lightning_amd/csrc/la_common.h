@@ -12,6 +12,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 raw bytes in four registers (a native vector, so register arrays of it
+// stay in registers where copies of HIP's struct-based uint4 can be lowered
+// to memory copies).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define LA_LDS __attribute__((address_space(3)))
 

@@ -47,9 +47,9 @@ constexpr int D = 128;
 constexpr int T = 128;           // tokens per chunk
 constexpr int NT = 512;          // threads per workgroup of the chunk kernel (8 waves)
 constexpr int NT_LOCAL = 256;    // threads per workgroup of the local-state kernel
-constexpr int RSK = 2 * D + 32;  // LDS row stride (bytes) of K and V tiles
+constexpr int KV_ROW = 2 * D;    // LDS row stride (bytes) of K and V tiles (swizzled)
 constexpr int RST = 2 * D + 16;  // LDS row stride (bytes) of S^T and output staging
-constexpr int LDS_K = T * RSK;
+constexpr int LDS_K = T * KV_ROW;
 constexpr int LDS_ST = D * RST;
 constexpr int LDS_O = T * RST;   // output staging: 32 rows per output wave
 constexpr int LDS_BYTES = 2 * LDS_K + LDS_ST + LDS_O;
@@ -59,12 +59,35 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Two transposed LDS reads (rows r0..r0+3 and r0+off..r0+off+3 of a
-// row-major bf16 tile, the lane's column); p is this lane's address for the
-// first read.
-__device__ __forceinline__ bf16x8 tr_read8(const char *p, int off_bytes) {
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS s16x4 *)(p));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS s16x4 *)(p + off_bytes));
+// K and V tiles: 128 rows of 256 bytes, unpadded; the 16-byte granule c of
+// row r is stored at granule c ^ kv_swz(r).  With this permutation every
+// access pattern used on the tiles reaches each of the 64 LDS banks once per
+// cycle (measured on gfx950: a row-per-lane 16-byte read runs at 5 clocks
+// per wave instruction instead of 8.5 with 288-byte rows, the transposed
+// read at 3 instead of 4.6):
+//   16 lanes reading one granule of 16 consecutive rows (MFMA A operand);
+//   ds_read_b64_tr_b16 over rows 4m..4m+3 and one 64-byte column block;
+//   16 lanes writing one whole row.
+// kv_swz depends on r mod 16 only, so adding 16 rows is adding 4096 bytes.
+__device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int kv_off(int r, int byte) {
+  return r * KV_ROW + ((((byte >> 4) ^ kv_swz(r)) << 4) | (byte & 15));
+}
+
+// This lane's address offset for ds_read_b64_tr_b16 over rows r4..r4+3
+// (r4 a multiple of 4) and columns 32 blk .. 32 blk + 31 of a K/V tile: in
+// each 16-lane group, lane i16 points at 4 consecutive elements of row
+// r4 + i16/4, columns 32 blk + 16 (G16 & 1) + 4 (i16 & 3) ...
+__device__ __forceinline__ int tr_off(int r4, int blk, int G16, int i16) {
+  return kv_off(r4 + (i16 >> 2), 64 * blk + 32 * (G16 & 1) + 8 * (i16 & 3));
+}
+
+// Two transposed LDS reads of a K/V tile at this lane's offsets o0 and o1
+// (two groups of 4 rows, the lane's column); base may add a multiple of 16
+// rows.
+__device__ __forceinline__ bf16x8 tr_read8(const char *base, int o0, int o1) {
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS s16x4 *)(base + o0));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS s16x4 *)(base + o1));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, r);
@@ -76,25 +99,28 @@ __device__ __forceinline__ bf16x8 cvt8(const float (&v)[8]) {
   return r;
 }
 
-// Global -> registers: rows [0, L) of a 128 x 128 bf16 tile starting at src,
-// moved by `nthr` threads (thread t of them moves 16 bytes of row
-// (it * nthr + t) / 16); rows >= L read as zero.
+// Global -> registers: a 128 x 128 bf16 tile starting at src, of which rows
+// [0, L) are valid (L >= 1), moved by `nthr` threads (thread t of them moves
+// 16 bytes of row (it * nthr + t) / 16).  Rows >= L repeat row L - 1: every
+// consumer masks those rows out or multiplies them by exact zeros, so any
+// finite values do, and the loads need no branches (a branch around a load
+// makes the compiler's memory-wait analysis far more conservative).
 template <int NTHR>
-__device__ __forceinline__ void load_tile(uint4 *r, const bf16 *src, int L, int t) {
+__device__ __forceinline__ void load_tile(u32x4 (&r)[T * 16 / NTHR], const bf16 *src, int L, int t) {
 #pragma unroll
   for (int it = 0; it < T * 16 / NTHR; ++it) {
-    int id = it * NTHR + t, row = id >> 4, c16 = id & 15;
-    if (row < L) r[it] = *(const uint4 *)(src + (int64_t)row * D + c16 * 8);
-    else r[it] = make_uint4(0, 0, 0, 0);
+    const int id = it * NTHR + t, row = id >> 4, c16 = id & 15;
+    const int rr = row < L ? row : L - 1;
+    r[it] = *(const u32x4 *)(src + (int64_t)rr * D + c16 * 8);
   }
 }
 
 template <int NTHR>
-__device__ __forceinline__ void store_tile(char *dst, const uint4 *r, int t) {
+__device__ __forceinline__ void store_tile(char *dst, const u32x4 (&r)[T * 16 / NTHR], int t) {
 #pragma unroll
   for (int it = 0; it < T * 16 / NTHR; ++it) {
     int id = it * NTHR + t, row = id >> 4, c16 = id & 15;
-    *(uint4 *)(dst + row * RSK + c16 * 16) = r[it];
+    *(u32x4 *)(dst + kv_off(row, c16 * 16)) = r[it];
   }
 }
 
@@ -151,11 +177,18 @@ __device__ __forceinline__ void state_update(f32x16 (&S)[4], const char *Ks, con
                                              int L, int e0, float l2, bool fast,
                                              const float (&tail8)[8], int u, int lane) {
   const int g = lane >> 5, G16 = lane >> 4, i16 = lane & 15;
-  const int sub = (i16 >> 2) * RSK + (16 * (G16 & 1) + 4 * (i16 & 3)) * 2;
+  // Rows 16 ks + 8 g + (0..3, 4..7): K columns 32u.., V columns 32 nt..
+  const int ko0 = tr_off(8 * g, u, G16, i16), ko1 = tr_off(8 * g + 4, u, G16, i16);
+  int vo0[4], vo1[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    vo0[nt] = tr_off(8 * g, nt, G16, i16);
+    vo1[nt] = tr_off(8 * g + 4, nt, G16, i16);
+  }
 #pragma unroll 2
   for (int ks = 0; ks < T / 16; ++ks) {
     const int c0 = 16 * ks + 8 * g;
-    bf16x8 kf = tr_read8(Ks + c0 * RSK + (32 * u) * 2 + sub, 4 * RSK);
+    bf16x8 kf = tr_read8(Ks + 16 * ks * KV_ROW, ko0, ko1);
     float wv[8];
     if (fast) {
       const float e = fast_exp2((float)(e0 - c0 - 7) * l2);
@@ -169,23 +202,22 @@ __device__ __forceinline__ void state_update(f32x16 (&S)[4], const char *Ks, con
     const bf16x8 a = cvt8(wv);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      bf16x8 b = tr_read8(Vs + c0 * RSK + (32 * nt) * 2 + sub, 4 * RSK);
+      bf16x8 b = tr_read8(Vs + 16 * ks * KV_ROW, vo0[nt], vo1[nt]);
       S[nt] = mma(a, b, S[nt]);
     }
   }
 }
 
-// Q^T fragments of 32 query rows (B operand, k = feature), straight from HBM.
-__device__ __forceinline__ void load_qf(uint4 *qf, const bf16 *qrow, bool valid, int g) {
+// Q^T fragments of one query row (B operand, k = feature), straight from HBM.
+__device__ __forceinline__ void load_qf(u32x4 (&qf)[8], const bf16 *qrow, int g) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    qf[ks] = valid ? *(const uint4 *)(qrow + 16 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const u32x4 *)(qrow + 16 * ks + 8 * g);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 // Inter-block term O^T = S^T Q^T for the wave's 32 rows, scaled by a_row.
-__device__ __forceinline__ void inter_term(f32x16 (&acc)[4], const char *STs, const uint4 *qf,
+__device__ __forceinline__ void inter_term(f32x16 (&acc)[4], const char *STs, const u32x4 *qf,
                                            float a_row, int l32, int g) {
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
@@ -199,14 +231,19 @@ __device__ __forceinline__ void inter_term(f32x16 (&acc)[4], const char *STs, co
   for (int jt = 0; jt < 4; ++jt) acc[jt] *= a_row;
 }
 
-// Per-workgroup constants and lane coordinates of the 8-wave layout.
+// Per-workgroup constants and lane coordinates of the 8-wave layout.  The
+// wave index lives in a scalar register, so the role test is a scalar branch
+// and each role runs a loop of its own.  (With one exec-masked instruction
+// stream for both roles, the compiler's memory-wait analysis sees the other
+// role's loads into the same registers and waits for every prefetch right
+// after issuing it.)
 struct Lanes {
-  int tid, lane, wave, w, l32, g, G16, i16, row, tr_sub, ts;
+  int tid, lane, wave, w, l32, g, G16, i16, row, ts;
   bool out_wave;
   __device__ __forceinline__ Lanes() {
     tid = threadIdx.x;
     lane = tid & 63;
-    wave = tid >> 6;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     out_wave = wave < 4;
     w = wave & 3;  // output rows 32w.. or state rows 32w..
     l32 = lane & 31;
@@ -214,7 +251,6 @@ struct Lanes {
     G16 = lane >> 4;
     i16 = lane & 15;
     row = 32 * w + l32;  // output waves: this lane's query row in the chunk
-    tr_sub = (i16 >> 2) * RSK + (16 * (G16 & 1) + 4 * (i16 & 3)) * 2;
     ts = tid - 256;  // state waves: index among the 256 loaders
   }
 };
@@ -231,148 +267,180 @@ struct Decay {
   }
 };
 
-// Issues this chunk's loads: Q^T fragments for output waves, K and V rows for
-// state waves (Y as qf or pk/pv).
-__device__ __forceinline__ void issue_chunk_loads(const FwdArgs &p, int h, const Cursor &c,
-                                                  uint4 *Y, const Lanes &ln) {
-  const SeqMap &m = p.m;
+// Q^T fragments of chunk c for this output wave's 32 rows.
+__device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cursor &c,
+                                              u32x4 (&qf)[8], const Lanes &ln) {
+  // Rows past the chunk's end read its last row: their outputs are never stored.
   const int Lc = (int)(c.c1 - c.c0);
-  if (ln.out_wave) {
-    load_qf(Y, (const bf16 *)p.q + m.row_base(h, c.j) + (c.c0 + ln.row) * D, ln.row < Lc, ln.g);
-  } else {
-    const int64_t base = m.row_base(h, c.j) + c.c0 * D;
-    load_tile<256>(Y, (const bf16 *)p.k + base, Lc, ln.ts);
-    load_tile<256>(Y + 8, (const bf16 *)p.v + base, Lc, ln.ts);
+  const int r = ln.row < Lc ? ln.row : Lc - 1;
+  load_qf(qf, (const bf16 *)p.q + p.m.row_base(h, c.j) + (c.c0 + r) * D, ln.g);
+}
+
+// K and V rows of chunk c, spread over the 256 threads of the state waves.
+__device__ __forceinline__ void issue_kv_loads(const FwdArgs &p, int h, const Cursor &c,
+                                               u32x4 (&pk)[8], u32x4 (&pv)[8], const Lanes &ln) {
+  const int Lc = (int)(c.c1 - c.c0);
+  const int64_t base = p.m.row_base(h, c.j) + c.c0 * D;
+  load_tile<256>(pk, (const bf16 *)p.k + base, Lc, ln.ts);
+  load_tile<256>(pv, (const bf16 *)p.v + base, Lc, ln.ts);
+}
+
+// Writes this output wave's 32 staged rows of chunk c (rows >= the chunk
+// length are skipped) as whole rows: lane reads 16 bytes of row
+// 32w + 4it + lane/16 from LDS and stores them.
+__device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor &c,
+                                           const char *Os, const Lanes &ln) {
+  const int L = (int)(c.c1 - c.c0);
+  const int r0 = 32 * ln.w + (ln.lane >> 4), c16 = ln.lane & 15;
+  bf16 *obase = (bf16 *)p.out + p.m.row_base(h, c.j) + (c.c0 + r0) * D + c16 * 8;
+  const char *lbase = Os + r0 * RST + c16 * 16;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const u32x4 x = *(const u32x4 *)(lbase + 4 * it * RST);
+    if (r0 + 4 * it < L) *(u32x4 *)(obase + 4 * it * D) = x;
   }
 }
 
-// The chunk loop over segment [cur.c0, b) of head h.  On entry the state
-// waves hold the state entering the segment in X, and the first chunk's
-// loads are in flight into Y (issue_chunk_loads).  Writes outputs and, at
-// every sequence end inside the segment, that sequence's final state.
-__device__ __forceinline__ void chunk_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
-                                           f32x16 (&X)[4], uint4 (&Y)[16], char *smem,
-                                           const Decay &dc, const Lanes &ln) {
-  char *Ks = smem, *Vs = smem + LDS_K, *STs = Vs + LDS_K, *Os = STs + LDS_ST;
+// The chunk loop over segment [cur.c0, b) of head h, output side.  On entry
+// qf holds (or is loading) the first chunk's Q^T fragments.  Per chunk: two
+// barriers, shared with state_loop, which must run the same chunk sequence.
+__device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
+                                            u32x4 (&qf)[8], char *smem, const Decay &dc,
+                                            const Lanes &ln) {
+  const char *Ks = smem, *Vs = smem + LDS_K, *STs = smem + 2 * LDS_K;
+  char *Os = smem + 2 * LDS_K + LDS_ST;
+  const SeqMap &m = p.m;
+  const int w = ln.w, l32 = ln.l32, g = ln.g, row = ln.row;
+  const float l2 = dc.l2;
+  const bool fast = dc.fast;
+  const float a_row = fast_exp2((float)(row + 1) * l2);
+  // K/V tile offsets of this lane: K rows 32kc + l32, 16-byte granule 2ks + g
+  // (A operand of K Q^T); V rows 32kc + 16q2 + 4g + (0..3, 8..11), columns
+  // 32jt.. (A operand of V^T P^T, transposed reads).
+  int ka[8], va0[4], va1[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) ka[ks] = kv_off(l32, 32 * ks + 16 * g);
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    va0[jt] = tr_off(4 * g, jt, ln.G16, ln.i16);
+    va1[jt] = tr_off(4 * g + 8, jt, ln.G16, ln.i16);
+  }
+  f32x16 acc[4];
+  u32x4 qn[8];
+  __syncthreads();  // the first chunk's K/V and the entering S^T are in LDS
+  inter_term(acc, STs, qf, a_row, l32, g);
+
+  while (true) {
+    const Cursor nxt = next_chunk(m, cur, b, T);
+    __syncthreads();  // this chunk's K/V are in LDS
+    if (nxt.valid) issue_q_loads(p, h, nxt, qn, ln);
+    // Intra-block term over key sub-blocks kc <= w (causal).
+    for (int kc = 0; kc <= w; ++kc) {
+      f32x16 pt = {};
+      const char *kblk = Ks + 32 * kc * KV_ROW;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        pt = mma(*(const bf16x8 *)(kblk + ka[ks]), as_bf16x8(qf[ks]), pt);
+      // pt register 4q+mm: key c = 32kc + 8q + 4g + mm, query `row`.
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n0 = row - (32 * kc + 8 * q + 4 * g);
+        if (fast) {
+          const float e = fast_exp2((float)(n0 - 3) * l2);
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm)
+            pt[4 * q + mm] = (n0 >= mm) ? pt[4 * q + mm] * (e * dc.tail[4 + mm]) : 0.f;
+        } else {
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm)
+            pt[4 * q + mm] = (n0 >= mm) ? pt[4 * q + mm] * fast_exp2((float)(n0 - mm) * l2) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        float pv8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv8[e] = pt[8 * q2 + e];
+        const bf16x8 pb = cvt8(pv8);
+        const char *vblk = Vs + (32 * kc + 16 * q2) * KV_ROW;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          bf16x8 vf = tr_read8(vblk, va0[jt], va1[jt]);
+          acc[jt] = mma(vf, pb, acc[jt]);
+        }
+      }
+    }
+    // Stage the tile in this wave's LDS rows (acc[jt] registers 4rq..4rq+3
+    // hold features 32jt + 8rq + 4g + 0..3 of `row`).
+    {
+      char *orow_lds = Os + row * RST;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          bf16x4 v = {(bf16)acc[jt][4 * rq], (bf16)acc[jt][4 * rq + 1], (bf16)acc[jt][4 * rq + 2],
+                      (bf16)acc[jt][4 * rq + 3]};
+          *(bf16x4 *)(orow_lds + (32 * jt + 8 * rq + 4 * g) * 2) = v;
+        }
+    }
+    __syncthreads();  // this chunk's K/V reads are done; the next S^T is published
+    if (!nxt.valid) {
+      write_rows(p, h, cur, Os, ln);
+      break;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = qn[ks];
+    inter_term(acc, STs, qf, a_row, l32, g);
+    // The staged rows go out only now: a wait for the next chunk's Q loads
+    // then never has to wait for these stores as well (the memory counter
+    // retires in issue order).
+    write_rows(p, h, cur, Os, ln);
+    cur = nxt;
+  }
+}
+
+// The chunk loop, state side.  On entry S holds the state entering the
+// segment and pk/pv hold (or are loading) the first chunk's K and V.  Writes
+// every sequence end's final state inside the segment.
+__device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
+                                           f32x16 (&S)[4], u32x4 (&pk)[8], u32x4 (&pv)[8],
+                                           char *smem, const Decay &dc, const Lanes &ln) {
+  char *Ks = smem, *Vs = smem + LDS_K, *STs = smem + 2 * LDS_K;
   const SeqMap &m = p.m;
   const int H = m.H;
   const int64_t DD = (int64_t)D * D;
-  const int w = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane, row = ln.row;
+  const int w = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane;
   const float l2 = dc.l2;
-  const bool fast = dc.fast;
-  // The two roles share registers: X is the output accumulator (output
-  // waves) or the state (state waves); Y holds this and the next chunk's Q^T
-  // fragments (output waves) or the next chunk's K and V (state waves).
-  f32x16 (&acc)[4] = X;
-  f32x16 (&S)[4] = X;
-  uint4 *qf = Y, *qn = Y + 8, *pk = Y, *pv = Y + 8;
-
-  if (!ln.out_wave) {
-    store_tile<256>(Ks, pk, ln.ts);
-    store_tile<256>(Vs, pv, ln.ts);
-    write_st(STs, S, w, l32, g);
-  }
-  __syncthreads();
-  if (ln.out_wave) inter_term(acc, STs, qf, fast_exp2((float)(row + 1) * l2), l32, g);
+  store_tile<256>(Ks, pk, ln.ts);
+  store_tile<256>(Vs, pv, ln.ts);
+  write_st(STs, S, w, l32, g);
+  __syncthreads();  // the first chunk's K/V and the entering S^T are in LDS
 
   while (true) {
     const Cursor nxt = next_chunk(m, cur, b, T);
     const int L = (int)(cur.c1 - cur.c0);
-    __syncthreads();  // K/V of this chunk are in LDS; inter term done
-    if (ln.out_wave) {
-      if (nxt.valid) {
-        const int Ln = (int)(nxt.c1 - nxt.c0);
-        load_qf(qn, (const bf16 *)p.q + m.row_base(h, nxt.j) + (nxt.c0 + row) * D, row < Ln, g);
-      }
-      // Intra-block term over key sub-blocks kc <= w (causal).
-      for (int kc = 0; kc <= w; ++kc) {
-        f32x16 pt = {};
-        const char *krow = Ks + (32 * kc + l32) * RSK + 16 * g;
+    __syncthreads();  // this chunk's K/V are in LDS; the output side has read S^T
+    if (nxt.valid) issue_kv_loads(p, h, nxt, pk, pv, ln);
+    const bool seq_done = (cur.c1 == cur.seq_end);
+    const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
+    if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
+      const float gL = fast_exp2((float)L * l2);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          pt = mma(*(const bf16x8 *)(krow + 32 * ks), as_bf16x8(qf[ks]), pt);
-        // pt register 4q+mm: key c = 32kc + 8q + 4g + mm, query `row`.
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n0 = row - (32 * kc + 8 * q + 4 * g);
-          if (fast) {
-            const float e = fast_exp2((float)(n0 - 3) * l2);
-#pragma unroll
-            for (int mm = 0; mm < 4; ++mm)
-              pt[4 * q + mm] = (n0 >= mm) ? pt[4 * q + mm] * (e * dc.tail[4 + mm]) : 0.f;
-          } else {
-#pragma unroll
-            for (int mm = 0; mm < 4; ++mm)
-              pt[4 * q + mm] =
-                  (n0 >= mm) ? pt[4 * q + mm] * fast_exp2((float)(n0 - mm) * l2) : 0.f;
-          }
-        }
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          float pv8[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv8[e] = pt[8 * q2 + e];
-          const bf16x8 pb = cvt8(pv8);
-          const int c0 = 32 * kc + 16 * q2 + 4 * g;
-#pragma unroll
-          for (int jt = 0; jt < 4; ++jt) {
-            bf16x8 vf = tr_read8(Vs + c0 * RSK + (32 * jt) * 2 + ln.tr_sub, 8 * RSK);
-            acc[jt] = mma(vf, pb, acc[jt]);
-          }
-        }
-      }
-      // Stage the tile in this wave's LDS rows (acc[jt] registers 4rq..4rq+3
-      // hold features 32jt + 8rq + 4g + 0..3 of `row`), then write whole rows.
-      {
-        char *orow_lds = Os + row * RST;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            bf16x4 v = {(bf16)acc[jt][4 * rq], (bf16)acc[jt][4 * rq + 1],
-                        (bf16)acc[jt][4 * rq + 2], (bf16)acc[jt][4 * rq + 3]};
-            *(bf16x4 *)(orow_lds + (32 * jt + 8 * rq + 4 * g) * 2) = v;
-          }
-        // the wave's own 32 rows: lane reads 16 bytes of row 32w + 4it + lane/16
-        const int r0 = 32 * w + (lane >> 4), c16 = lane & 15;
-        bf16 *obase = (bf16 *)p.out + m.row_base(h, cur.j) + (cur.c0 + r0) * D + c16 * 8;
-        const char *lbase = Os + r0 * RST + c16 * 16;
-#pragma unroll 2
-        for (int it = 0; it < 8; ++it) {
-          const uint4 x = *(const uint4 *)(lbase + 4 * it * RST);
-          if (r0 + 4 * it < L) *(uint4 *)(obase + 4 * it * D) = x;
-        }
-      }
-    } else {
-      if (nxt.valid) {
-        const int64_t base = m.row_base(h, nxt.j) + nxt.c0 * D;
-        const int Ln = (int)(nxt.c1 - nxt.c0);
-        load_tile<256>(pk, (const bf16 *)p.k + base, Ln, ln.ts);
-        load_tile<256>(pv, (const bf16 *)p.v + base, Ln, ln.ts);
-      }
-      const bool seq_done = (cur.c1 == cur.seq_end);
-      const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
-      if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
-        const float gL = fast_exp2((float)L * l2);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) S[nt] *= gL;
-        state_update(S, Ks, Vs, L, L - 1, l2, fast, dc.tail, w, lane);
-        if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
-      }
+      for (int nt = 0; nt < 4; ++nt) S[nt] *= gL;
+      state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane);
+      if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
+    }
+    // (A new piece's state load sits in the same block as the S^T write that
+    // consumes it, so no path reaches the next chunk with those loads open.)
+    if (nxt.valid) {
       if (new_piece)
         load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, w, l32, g);
-      if (nxt.valid) write_st(STs, S, w, l32, g);
+      write_st(STs, S, w, l32, g);
     }
-    __syncthreads();  // this chunk's K/V reads are done; next S^T is published
+    __syncthreads();  // this chunk's K/V reads are done; the next S^T is published
     if (!nxt.valid) break;
-    if (ln.out_wave) {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[ks] = qn[ks];
-      inter_term(acc, STs, qf, fast_exp2((float)(row + 1) * l2), l32, g);
-    } else {
-      store_tile<256>(Ks, pk, ln.ts);
-      store_tile<256>(Vs, pv, ln.ts);
-    }
+    store_tile<256>(Ks, pk, ln.ts);
+    store_tile<256>(Vs, pv, ln.ts);
     cur = nxt;
   }
 }
@@ -392,15 +460,19 @@ void prefill_chunk_kernel(FwdArgs p) {
   const int64_t DD = (int64_t)D * D;
   const Cursor cur = first_chunk(m, a, b, T);
   if (!cur.valid) return;
-  f32x16 X[4];
-  uint4 Y[16];
-  if (!ln.out_wave) {
+  if (ln.out_wave) {
+    u32x4 qf[8];
+    issue_q_loads(p, h, cur, qf, ln);
+    output_loop(p, h, b, cur, qf, smem, dc, ln);
+  } else {
+    f32x16 S[4];
     const float *s0 = p.ws ? p.ws + ((int64_t)s * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
-    load_state(X, s0, ln.w, ln.l32, ln.g);
+    load_state(S, s0, ln.w, ln.l32, ln.g);
+    u32x4 pk[8], pv[8];
+    issue_kv_loads(p, h, cur, pk, pv, ln);
+    state_loop(p, h, b, cur, S, pk, pv, smem, dc, ln);
   }
-  issue_chunk_loads(p, h, cur, Y, ln);
-  chunk_loop(p, h, b, cur, X, Y, smem, dc, ln);
 }
 
 // Single-pass prefill with the segment scan folded in (MiniMax-01 report,
@@ -480,7 +552,7 @@ void prefill_fused_kernel(FusedArgs fa) {
   if (ln.tid == 0)
     sh_ticket = __hip_atomic_fetch_add(fa.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  const unsigned t = sh_ticket;
+  const unsigned t = __builtin_amdgcn_readfirstlane(sh_ticket);
   const int s = (int)(t / (unsigned)H), h = (int)(t - (t / (unsigned)H) * (unsigned)H);
   const Decay dc(p.decay[h]);
   const int64_t a = (int64_t)s * p.seg_len;
@@ -495,77 +567,89 @@ void prefill_fused_kernel(FusedArgs fa) {
   const int64_t ps0 = m.start(jl);
   const int64_t ps = ps0 > a ? ps0 : a;   // start of the segment's last piece
   const bool need_out = m.start(jl + 1) > b;  // that sequence continues after b
-  f32x16 X[4];
-  uint4 Y[16];
+  const int64_t kvb = m.row_base(h, jl);
 
-  // 1. L = sum over the last piece of lambda^(b-1-c) k_c^T v_c: state waves
-  //    accumulate, output waves stream the K/V tiles through LDS.
-  if (need_out) {
-    if (!ln.out_wave) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) X[nt] = (f32x16){};
-    }
-    const int64_t kvb = m.row_base(h, jl);
-    int64_t t0 = ps;
-    int Lt = (int)((b - t0) < T ? (b - t0) : T);
-    if (ln.out_wave) {
-      load_tile<256>(Y, (const bf16 *)p.k + kvb + t0 * D, Lt, ln.tid);
-      load_tile<256>(Y + 8, (const bf16 *)p.v + kvb + t0 * D, Lt, ln.tid);
-    }
-    while (t0 < b) {
-      if (ln.out_wave) {
-        store_tile<256>(Ks, Y, ln.tid);
-        store_tile<256>(Vs, Y + 8, ln.tid);
-      }
-      __syncthreads();
-      const int Lc = Lt;
-      const int64_t t1 = t0 + T;
-      if (t1 < b) {
-        Lt = (int)((b - t1) < T ? (b - t1) : T);
-        if (ln.out_wave) {
-          load_tile<256>(Y, (const bf16 *)p.k + kvb + t1 * D, Lt, ln.tid);
-          load_tile<256>(Y + 8, (const bf16 *)p.v + kvb + t1 * D, Lt, ln.tid);
+  // Both roles pass the same barriers: two per tile of step 1, one after the
+  // wait of step 2, one more after the record stores when publishing, then
+  // the chunk loop's.
+  if (ln.out_wave) {
+    // 1. Stream the last piece's K/V tiles through LDS for the state waves.
+    if (need_out) {
+      u32x4 tk[8], tv[8];
+      int64_t t0 = ps;
+      int Lt = (int)((b - t0) < T ? (b - t0) : T);
+      load_tile<256>(tk, (const bf16 *)p.k + kvb + t0 * D, Lt, ln.tid);
+      load_tile<256>(tv, (const bf16 *)p.v + kvb + t0 * D, Lt, ln.tid);
+      while (t0 < b) {
+        store_tile<256>(Ks, tk, ln.tid);
+        store_tile<256>(Vs, tv, ln.tid);
+        __syncthreads();
+        const int64_t t1 = t0 + T;
+        if (t1 < b) {
+          Lt = (int)((b - t1) < T ? (b - t1) : T);
+          load_tile<256>(tk, (const bf16 *)p.k + kvb + t1 * D, Lt, ln.tid);
+          load_tile<256>(tv, (const bf16 *)p.v + kvb + t1 * D, Lt, ln.tid);
         }
+        __syncthreads();
+        t0 = t1;
       }
-      if (!ln.out_wave)
-        state_update(X, Ks, Vs, Lc, (int)(b - 1 - t0), dc.l2, dc.fast, dc.tail, ln.w, ln.lane);
-      __syncthreads();
-      t0 = t1;
     }
-  }
-
-  // 2. The first chunk's loads go out while waiting for the entering state.
-  issue_chunk_loads(p, h, cur, Y, ln);
-  if (need_in && ln.tid == 0) {
-    const unsigned *fl = fa.flags + (size_t)(s - 1) * H + h;
-    int it = 0;
-    while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-      if (++it > kSpinLimit) {
-        *fa.err = 1u;
-        break;
+    // 2. The first chunk's Q loads go out while waiting for the entering state.
+    u32x4 qf[8];
+    issue_q_loads(p, h, cur, qf, ln);
+    if (need_in && ln.tid == 0) {
+      const unsigned *fl = fa.flags + (size_t)(s - 1) * H + h;
+      int it = 0;
+      while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        if (++it > kSpinLimit) {
+          *fa.err = 1u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      __builtin_amdgcn_s_sleep(2);
     }
-  }
-  __syncthreads();  // the record loads below are issued after the flag was seen
-  if (!ln.out_wave) {
+    __syncthreads();  // the state waves' record loads are issued after the flag was seen
+    if (need_out) {
+      __syncthreads();  // the state waves' record stores have completed
+      if (ln.tid == 0)
+        __hip_atomic_store(fa.flags + (size_t)s * H + h, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // 3. Outputs from the entering state.
+    output_loop(p, h, b, cur, qf, smem, dc, ln);
+  } else {
+    // 1. L = sum over the last piece of lambda^(b-1-c) k_c^T v_c.
+    f32x16 S[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) S[nt] = (f32x16){};
+    if (need_out) {
+      int64_t t0 = ps;
+      while (t0 < b) {
+        const int Lc = (int)((b - t0) < T ? (b - t0) : T);
+        __syncthreads();
+        state_update(S, Ks, Vs, Lc, (int)(b - 1 - t0), dc.l2, dc.fast, dc.tail, ln.w, ln.lane);
+        __syncthreads();
+        t0 += T;
+      }
+    }
+    // 2. The first chunk's K/V loads go out while waiting for the entering
+    //    state; then S <- entering state, and the end state is published.
+    u32x4 pk[8], pv[8];
+    issue_kv_loads(p, h, cur, pk, pv, ln);
+    __syncthreads();  // the flag of the previous segment has been seen
     const float *prev = need_in ? p.ws + ((int64_t)(s - 1) * H + h) * DD
                                 : (p.init ? p.init + ((int64_t)jf * H + h) * DD : nullptr);
     const float *ini_last = p.init ? p.init + ((int64_t)jl * H + h) * DD : nullptr;
     const float gam = fast_exp2((float)(b - ps) * dc.l2);
-    combine_states(X, prev, need_in, ini_last, ps == a, need_out, gam,
+    combine_states(S, prev, need_in, ini_last, ps == a, need_out, gam,
                    p.ws + ((int64_t)s * H + h) * DD, ln.w, ln.l32, ln.g);
+    if (need_out) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's record stores have completed
+      __syncthreads();
+    }
+    // 3. Outputs from the entering state.
+    state_loop(p, h, b, cur, S, pk, pv, smem, dc, ln);
   }
-  if (need_out) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's record stores have completed
-    __syncthreads();
-    if (ln.tid == 0)
-      __hip_atomic_store(fa.flags + (size_t)s * H + h, 1u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  // 3. Outputs from the entering state.
-  chunk_loop(p, h, b, cur, X, Y, smem, dc, ln);
 }
 
 // Phase A: the local state of each segment's last piece, from zero:
@@ -601,7 +685,7 @@ void local_state_kernel(FwdArgs p) {
   f32x16 S[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) S[nt] = (f32x16){};
-  uint4 pk[8], pv[8];  // next tile of K and V
+  u32x4 pk[8], pv[8];  // next tile of K and V
   int L = (int)((b - ps) < T ? (b - ps) : T);
   load_tile<NT_LOCAL>(pk, (const bf16 *)p.k + base + ps * D, L, tid);
   load_tile<NT_LOCAL>(pv, (const bf16 *)p.v + base + ps * D, L, tid);

@@ -47,12 +47,12 @@ constexpr int D = 128;
 constexpr int T = 128;           // tokens per chunk
 constexpr int NT = 512;          // threads per workgroup of the chunk kernel (8 waves)
 constexpr int NT_LOCAL = 256;    // threads per workgroup of the local-state kernel
-constexpr int KV_ROW = 2 * D;    // LDS row stride (bytes) of K and V tiles (swizzled)
-constexpr int RST = 2 * D + 16;  // LDS row stride (bytes) of S^T and output staging
-constexpr int LDS_K = T * KV_ROW;
-constexpr int LDS_ST = D * RST;
-constexpr int LDS_O = T * RST;   // output staging: 32 rows per output wave
-constexpr int LDS_BYTES = 2 * LDS_K + LDS_ST + LDS_O;
+constexpr int KV_ROW = 2 * D;      // LDS row stride (bytes) of every 128 x 128 bf16 tile
+constexpr int LDS_K = T * KV_ROW;  // one K or V tile (32 KB, swizzled)
+constexpr int LDS_KV = 2 * LDS_K;  // the K and V tiles of one chunk
+constexpr int LDS_ST = D * KV_ROW; // S^T (32 KB, swizzled like the tiles)
+// The chunk kernel: two chunks' K/V tiles (double buffer) and S^T: 160 KB.
+constexpr int LDS_BYTES = 2 * LDS_KV + LDS_ST;
 constexpr float kFastLog2 = -15.f;  // factored powers when log2(lambda) > this
 
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -158,7 +158,7 @@ __device__ __forceinline__ void store_state(float *dst, const f32x16 (&S)[4], in
   }
 }
 
-// S^T (bf16) into LDS: row j holds S[0..127][j].
+// S^T (bf16) into LDS, swizzled like the K/V tiles: row j holds S[0..127][j].
 __device__ __forceinline__ void write_st(char *STs, const f32x16 (&S)[4], int u, int l32, int g) {
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
@@ -166,7 +166,7 @@ __device__ __forceinline__ void write_st(char *STs, const f32x16 (&S)[4], int u,
     for (int rq = 0; rq < 4; ++rq) {
       bf16x4 v = {(bf16)S[nt][4 * rq], (bf16)S[nt][4 * rq + 1], (bf16)S[nt][4 * rq + 2],
                   (bf16)S[nt][4 * rq + 3]};
-      *(bf16x4 *)(STs + (32 * nt + l32) * RST + (32 * u + 8 * rq + 4 * g) * 2) = v;
+      *(bf16x4 *)(STs + kv_off(32 * nt + l32, (32 * u + 8 * rq + 4 * g) * 2)) = v;
     }
 }
 
@@ -217,15 +217,16 @@ __device__ __forceinline__ void load_qf(u32x4 (&qf)[8], const bf16 *qrow, int g)
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 // Inter-block term O^T = S^T Q^T for the wave's 32 rows, scaled by a_row.
+// ka[ks] = kv_off(l32, 32 ks + 16 g): this lane's A-operand offsets.
 __device__ __forceinline__ void inter_term(f32x16 (&acc)[4], const char *STs, const u32x4 *qf,
-                                           float a_row, int l32, int g) {
+                                           float a_row, const int (&ka)[8]) {
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
     acc[jt] = (f32x16){};
-    const char *strow = STs + (32 * jt + l32) * RST + 16 * g;
+    const char *stblk = STs + 32 * jt * KV_ROW;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      acc[jt] = mma(*(const bf16x8 *)(strow + 32 * ks), as_bf16x8(qf[ks]), acc[jt]);
+      acc[jt] = mma(*(const bf16x8 *)(stblk + ka[ks]), as_bf16x8(qf[ks]), acc[jt]);
   }
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) acc[jt] *= a_row;
@@ -276,7 +277,8 @@ __device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cur
   load_qf(qf, (const bf16 *)p.q + p.m.row_base(h, c.j) + (c.c0 + r) * D, ln.g);
 }
 
-// K and V rows of chunk c, spread over the 256 threads of the state waves.
+// K and V rows of chunk c, spread over the 256 threads of a role (register
+// path, used by the single-pass kernel's local-state pass).
 __device__ __forceinline__ void issue_kv_loads(const FwdArgs &p, int h, const Cursor &c,
                                                u32x4 (&pk)[8], u32x4 (&pv)[8], const Lanes &ln) {
   const int Lc = (int)(c.c1 - c.c0);
@@ -285,38 +287,90 @@ __device__ __forceinline__ void issue_kv_loads(const FwdArgs &p, int h, const Cu
   load_tile<256>(pv, (const bf16 *)p.v + base, Lc, ln.ts);
 }
 
+// s_waitcnt vmcnt(N) (the other counters left alone).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// One global_load_lds_dwordx4: each lane's 16 bytes at gptr land in LDS at
+// lds + 16 x lane.  Issued from inline assembly so that the compiler's
+// memory-wait analysis does not see an LDS write: it would otherwise wait for
+// the load before every later LDS read and every barrier, serialising the
+// prefetch.  The caller waits for these loads itself (vm_wait) before the
+// barrier that hands the tile to other waves; the compiler's own waits can
+// only over-count them, never under-count.
+__device__ __forceinline__ void lds_dma16(const void *gptr, const char *lds) {
+  const unsigned a = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(const LA_LDS char *)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(a)
+               : "memory", "m0");
+}
+
+// Rows 32u..32u+31 of chunk c's tile of `src` (K or V) straight from HBM into
+// the swizzled LDS tile `tile` (global_load_lds_dwordx4: the data bypass the
+// registers, each lane's 16 bytes land at the instruction's LDS base + 16 x
+// lane).  Lane i of instruction k fills LDS row 4k + i/16, physical granule
+// i % 16, so it reads logical granule (i % 16) ^ kv_swz(row).  Rows past the
+// chunk's end repeat its last row (finite values that every consumer masks).
+// Eight memory instructions per call.
+__device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const FwdArgs &p, int h,
+                                              const Cursor &c, int u, int lane) {
+  const int Lc = (int)(c.c1 - c.c0);
+  const bf16 *base = (const bf16 *)src + p.m.row_base(h, c.j) + c.c0 * D;
+  const int sub = lane >> 4, pg = lane & 15;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = 32 * u + 4 * k + sub;
+    const int rr = r < Lc ? r : Lc - 1;
+    const bf16 *gp = base + (int64_t)rr * D + ((pg ^ kv_swz(r)) << 3);
+    lds_dma16(gp, tile + (32 * u + 4 * k) * KV_ROW);
+  }
+}
+
 // Writes this output wave's 32 staged rows of chunk c (rows >= the chunk
 // length are skipped) as whole rows: lane reads 16 bytes of row
-// 32w + 4it + lane/16 from LDS and stores them.
+// 32w + 4it + lane/16 from the swizzled staging tile and stores them.
 __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor &c,
                                            const char *Os, const Lanes &ln) {
   const int L = (int)(c.c1 - c.c0);
   const int r0 = 32 * ln.w + (ln.lane >> 4), c16 = ln.lane & 15;
   bf16 *obase = (bf16 *)p.out + p.m.row_base(h, c.j) + (c.c0 + r0) * D + c16 * 8;
-  const char *lbase = Os + r0 * RST + c16 * 16;
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
-    const u32x4 x = *(const u32x4 *)(lbase + 4 * it * RST);
+    const u32x4 x = *(const u32x4 *)(Os + kv_off(r0 + 4 * it, c16 * 16));
     if (r0 + 4 * it < L) *(u32x4 *)(obase + 4 * it * D) = x;
   }
 }
 
+// LDS use of the chunk loop.  Chunk n of the walk uses buffer n % 2 (its K
+// tile, then its V tile); S^T follows the two buffers.  The tiles arrive by
+// direct loads: chunk n + 1's K tile from output waves 0 and 1 once their
+// (short) intra-block work for chunk n is done, chunk n + 2's V tile from the
+// state waves right after the barrier that closes chunk n (when that
+// buffer's V tile is free).  Every tile has a good part of a chunk period to
+// arrive, no single burst of loads outgrows what the CU keeps in flight, and
+// no wave with work on the critical path stalls on issuing them.  After chunk
+// n closes, its K tile holds the output waves' staged output rows until they
+// are written back.
+//
 // The chunk loop over segment [cur.c0, b) of head h, output side.  On entry
 // qf holds (or is loading) the first chunk's Q^T fragments.  Per chunk: two
-// barriers, shared with state_loop, which must run the same chunk sequence.
+// barriers, shared with state_loop, which runs the same chunk sequence.
 __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                             u32x4 (&qf)[8], char *smem, const Decay &dc,
                                             const Lanes &ln) {
-  const char *Ks = smem, *Vs = smem + LDS_K, *STs = smem + 2 * LDS_K;
-  char *Os = smem + 2 * LDS_K + LDS_ST;
+  const char *STs = smem + 2 * LDS_KV;
   const SeqMap &m = p.m;
   const int w = ln.w, l32 = ln.l32, g = ln.g, row = ln.row;
   const float l2 = dc.l2;
   const bool fast = dc.fast;
   const float a_row = fast_exp2((float)(row + 1) * l2);
-  // K/V tile offsets of this lane: K rows 32kc + l32, 16-byte granule 2ks + g
-  // (A operand of K Q^T); V rows 32kc + 16q2 + 4g + (0..3, 8..11), columns
-  // 32jt.. (A operand of V^T P^T, transposed reads).
+  // Tile offsets of this lane: rows 32kc + l32 (or 32jt + l32 of S^T),
+  // 16-byte granule 2ks + g (A operand of K Q^T and S^T Q^T); V rows
+  // 32kc + 16q2 + 4g + (0..3, 8..11), columns 32jt.. (transposed reads).
   int ka[8], va0[4], va1[4];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) ka[ks] = kv_off(l32, 32 * ks + 16 * g);
@@ -327,20 +381,27 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
   }
   f32x16 acc[4];
   u32x4 qn[8];
+  int buf = 0;
   __syncthreads();  // the first chunk's K/V and the entering S^T are in LDS
-  inter_term(acc, STs, qf, a_row, l32, g);
+  inter_term(acc, STs, qf, a_row, ka);
 
   while (true) {
     const Cursor nxt = next_chunk(m, cur, b, T);
-    __syncthreads();  // this chunk's K/V are in LDS
+    const char *Ks = smem + buf * LDS_KV, *Vs = Ks + LDS_K;
+    __syncthreads();  // A: this chunk's K/V are in LDS
     if (nxt.valid) issue_q_loads(p, h, nxt, qn, ln);
     // Intra-block term over key sub-blocks kc <= w (causal).
     for (int kc = 0; kc <= w; ++kc) {
-      f32x16 pt = {};
+      // K Q^T as two interleaved MFMA chains (even and odd k steps), halving
+      // the dependent-issue latency of one 8-long chain.
+      f32x16 pt = {}, pt1 = {};
       const char *kblk = Ks + 32 * kc * KV_ROW;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 8; ks += 2) {
         pt = mma(*(const bf16x8 *)(kblk + ka[ks]), as_bf16x8(qf[ks]), pt);
+        pt1 = mma(*(const bf16x8 *)(kblk + ka[ks + 1]), as_bf16x8(qf[ks + 1]), pt1);
+      }
+      pt += pt1;
       // pt register 4q+mm: key c = 32kc + 8q + 4g + mm, query `row`.
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -370,57 +431,71 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
         }
       }
     }
-    // Stage the tile in this wave's LDS rows (acc[jt] registers 4rq..4rq+3
-    // hold features 32jt + 8rq + 4g + 0..3 of `row`).
-    {
-      char *orow_lds = Os + row * RST;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          bf16x4 v = {(bf16)acc[jt][4 * rq], (bf16)acc[jt][4 * rq + 1], (bf16)acc[jt][4 * rq + 2],
-                      (bf16)acc[jt][4 * rq + 3]};
-          *(bf16x4 *)(orow_lds + (32 * jt + 8 * rq + 4 * g) * 2) = v;
-        }
+    // Output waves 0 and 1 have the least intra-block work: they load the
+    // next chunk's K tile into the other buffer (free since the previous
+    // chunk's rows were written back).
+    if (w < 2 && nxt.valid) {
+      char *Kn = smem + (buf ^ 1) * LDS_KV;
+      dma_tile_rows(Kn, p.k, p, h, nxt, 2 * w, ln.lane);
+      dma_tile_rows(Kn, p.k, p, h, nxt, 2 * w + 1, ln.lane);
     }
-    __syncthreads();  // this chunk's K/V reads are done; the next S^T is published
+    __syncthreads();  // B: this chunk's K/V reads are done; the next S^T is published
+    // Stage the tile in this wave's rows of the chunk's K tile (acc[jt]
+    // registers 4rq..4rq+3 hold features 32jt + 8rq + 4g + 0..3 of `row`).
+    char *Os = smem + buf * LDS_KV;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 v = {(bf16)acc[jt][4 * rq], (bf16)acc[jt][4 * rq + 1], (bf16)acc[jt][4 * rq + 2],
+                    (bf16)acc[jt][4 * rq + 3]};
+        *(bf16x4 *)(Os + kv_off(row, (32 * jt + 8 * rq + 4 * g) * 2)) = v;
+      }
     if (!nxt.valid) {
       write_rows(p, h, cur, Os, ln);
       break;
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = qn[ks];
-    inter_term(acc, STs, qf, a_row, l32, g);
-    // The staged rows go out only now: a wait for the next chunk's Q loads
-    // then never has to wait for these stores as well (the memory counter
-    // retires in issue order).
+    inter_term(acc, STs, qf, a_row, ka);
+    // The next chunk's K tile has landed before the barrier that hands it
+    // over (the loads were issued a good part of a chunk period ago).
+    if (w < 2) vm_wait<0>();
+    // The staged rows go out last, after every load this wave waits for
+    // before them (the memory counter retires in issue order).
     write_rows(p, h, cur, Os, ln);
     cur = nxt;
+    buf ^= 1;
   }
 }
 
 // The chunk loop, state side.  On entry S holds the state entering the
-// segment and pk/pv hold (or are loading) the first chunk's K and V.  Writes
-// every sequence end's final state inside the segment.
+// segment.  Loads every K/V tile of the walk (see above), updates the state
+// and publishes it as S^T; writes every sequence end's final state inside
+// the segment.
 __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
-                                           f32x16 (&S)[4], u32x4 (&pk)[8], u32x4 (&pv)[8],
-                                           char *smem, const Decay &dc, const Lanes &ln) {
-  char *Ks = smem, *Vs = smem + LDS_K, *STs = smem + 2 * LDS_K;
+                                           f32x16 (&S)[4], char *smem, const Decay &dc,
+                                           const Lanes &ln) {
+  char *STs = smem + 2 * LDS_KV;
   const SeqMap &m = p.m;
   const int H = m.H;
   const int64_t DD = (int64_t)D * D;
   const int w = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane;
   const float l2 = dc.l2;
-  store_tile<256>(Ks, pk, ln.ts);
-  store_tile<256>(Vs, pv, ln.ts);
+  int buf = 0;
+  Cursor nxt = next_chunk(m, cur, b, T);
+  dma_tile_rows(smem, p.k, p, h, cur, w, lane);
+  dma_tile_rows(smem + LDS_K, p.v, p, h, cur, w, lane);
+  if (nxt.valid) dma_tile_rows(smem + LDS_KV + LDS_K, p.v, p, h, nxt, w, lane);
   write_st(STs, S, w, l32, g);
+  if (nxt.valid) vm_wait<8>();
+  else vm_wait<0>();
   __syncthreads();  // the first chunk's K/V and the entering S^T are in LDS
 
   while (true) {
-    const Cursor nxt = next_chunk(m, cur, b, T);
     const int L = (int)(cur.c1 - cur.c0);
-    __syncthreads();  // this chunk's K/V are in LDS; the output side has read S^T
-    if (nxt.valid) issue_kv_loads(p, h, nxt, pk, pv, ln);
+    char *Ks = smem + buf * LDS_KV, *Vs = Ks + LDS_K;
+    __syncthreads();  // A: this chunk's K/V are in LDS; the output side has read S^T
     const bool seq_done = (cur.c1 == cur.seq_end);
     const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
     if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
@@ -437,11 +512,18 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
         load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, w, l32, g);
       write_st(STs, S, w, l32, g);
     }
-    __syncthreads();  // this chunk's K/V reads are done; the next S^T is published
+    __syncthreads();  // B: this chunk's K/V reads are done; the next S^T is published
     if (!nxt.valid) break;
-    store_tile<256>(Ks, pk, ln.ts);
-    store_tile<256>(Vs, pv, ln.ts);
+    const Cursor nxt2 = next_chunk(m, nxt, b, T);
+    if (nxt2.valid) {
+      dma_tile_rows(Vs, p.v, p, h, nxt2, w, lane);
+      vm_wait<8>();  // the next chunk's V tile has landed (only these 8 may be open)
+    } else {
+      vm_wait<0>();
+    }
     cur = nxt;
+    nxt = nxt2;
+    buf ^= 1;
   }
 }
 
@@ -469,9 +551,7 @@ void prefill_chunk_kernel(FwdArgs p) {
     const float *s0 = p.ws ? p.ws + ((int64_t)s * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     load_state(S, s0, ln.w, ln.l32, ln.g);
-    u32x4 pk[8], pv[8];
-    issue_kv_loads(p, h, cur, pk, pv, ln);
-    state_loop(p, h, b, cur, S, pk, pv, smem, dc, ln);
+    state_loop(p, h, b, cur, S, smem, dc, ln);
   }
 }
 
@@ -544,15 +624,17 @@ __device__ __forceinline__ void combine_states(f32x16 (&X)[4], const float *prev
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_fused_kernel(FusedArgs fa) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  __shared__ unsigned sh_ticket;
+  // The ticket passes through the first word of the S^T area, which is not
+  // written before the chunk loop starts.
+  unsigned *sh_ticket = (unsigned *)(smem + 2 * LDS_KV);
   const FwdArgs &p = fa.f;
   const Lanes ln;
   const SeqMap &m = p.m;
   const int H = m.H;
   if (ln.tid == 0)
-    sh_ticket = __hip_atomic_fetch_add(fa.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sh_ticket = __hip_atomic_fetch_add(fa.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  const unsigned t = __builtin_amdgcn_readfirstlane(sh_ticket);
+  const unsigned t = __builtin_amdgcn_readfirstlane(*sh_ticket);
   const int s = (int)(t / (unsigned)H), h = (int)(t - (t / (unsigned)H) * (unsigned)H);
   const Decay dc(p.decay[h]);
   const int64_t a = (int64_t)s * p.seg_len;
@@ -632,10 +714,7 @@ void prefill_fused_kernel(FusedArgs fa) {
         t0 += T;
       }
     }
-    // 2. The first chunk's K/V loads go out while waiting for the entering
-    //    state; then S <- entering state, and the end state is published.
-    u32x4 pk[8], pv[8];
-    issue_kv_loads(p, h, cur, pk, pv, ln);
+    // 2. S <- the entering state, and the end state is published.
     __syncthreads();  // the flag of the previous segment has been seen
     const float *prev = need_in ? p.ws + ((int64_t)(s - 1) * H + h) * DD
                                 : (p.init ? p.init + ((int64_t)jf * H + h) * DD : nullptr);
@@ -648,7 +727,7 @@ void prefill_fused_kernel(FusedArgs fa) {
       __syncthreads();
     }
     // 3. Outputs from the entering state.
-    state_loop(p, h, b, cur, S, pk, pv, smem, dc, ln);
+    state_loop(p, h, b, cur, S, smem, dc, ln);
   }
 }
 

@@ -185,26 +185,33 @@ __device__ __forceinline__ void state_update(f32x16 (&S)[4], const char *Ks, con
     vo0[nt] = tr_off(8 * g, nt, G16, i16);
     vo1[nt] = tr_off(8 * g + 4, nt, G16, i16);
   }
-#pragma unroll 2
+  // Software-pipelined: the LDS reads of step ks + 1 go out before the
+  // arithmetic and MFMAs of step ks, so their latency overlaps work.
+  bf16x8 kf[2], vf[2][4];
+  auto fetch = [&](int ks, int slot) {
+    kf[slot] = tr_read8(Ks + 16 * ks * KV_ROW, ko0, ko1);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) vf[slot][nt] = tr_read8(Vs + 16 * ks * KV_ROW, vo0[nt], vo1[nt]);
+  };
+  fetch(0, 0);
+#pragma unroll
   for (int ks = 0; ks < T / 16; ++ks) {
+    const int sl = ks & 1;
+    if (ks + 1 < T / 16) fetch(ks + 1, sl ^ 1);
     const int c0 = 16 * ks + 8 * g;
-    bf16x8 kf = tr_read8(Ks + 16 * ks * KV_ROW, ko0, ko1);
     float wv[8];
     if (fast) {
       const float e = fast_exp2((float)(e0 - c0 - 7) * l2);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) wv[s] = (c0 + s < L) ? (float)kf[s] * (e * tail8[s]) : 0.f;
+      for (int s = 0; s < 8; ++s) wv[s] = (c0 + s < L) ? (float)kf[sl][s] * (e * tail8[s]) : 0.f;
     } else {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        wv[s] = (c0 + s < L) ? (float)kf[s] * fast_exp2((float)(e0 - c0 - s) * l2) : 0.f;
+        wv[s] = (c0 + s < L) ? (float)kf[sl][s] * fast_exp2((float)(e0 - c0 - s) * l2) : 0.f;
     }
     const bf16x8 a = cvt8(wv);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      bf16x8 b = tr_read8(Vs + 16 * ks * KV_ROW, vo0[nt], vo1[nt]);
-      S[nt] = mma(a, b, S[nt]);
-    }
+    for (int nt = 0; nt < 4; ++nt) S[nt] = mma(a, vf[sl][nt], S[nt]);
   }
 }
 

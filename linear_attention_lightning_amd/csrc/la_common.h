@@ -114,6 +114,19 @@ __device__ __forceinline__ Cursor next_chunk(const SeqMap &m, const Cursor &c, i
   return n;
 }
 
+// First chunk of a local-state pass over [ps, b) (chunks of T tokens
+// aligned to ps) that can carry a nonzero weight.  A token more than
+// 160 / |log2 lambda| before b has weight lambda^(b-1-c) < 2^-160; every
+// float32 step that forms such a weight (2^x of an exponent below -150, and
+// its products) yields exactly zero, so whole chunks of such tokens add
+// exactly nothing and are skipped: the result is bit-identical.  For
+// fast-decaying heads this leaves a few chunks of a segment; lambda = 1 skips
+// nothing.
+__device__ __forceinline__ int64_t first_weighted(int64_t ps, int64_t b, float log2lam, int T) {
+  const float far = (float)(b - ps) - 160.f / -log2lam;  // -inf when log2lam == 0
+  return far >= (float)T ? ps + (int64_t)(far / (float)T) * T : ps;
+}
+
 // Arguments shared by the prefill kernels.
 struct FwdArgs {
   const void *q, *k, *v;

@@ -665,7 +665,7 @@ void prefill_fused_kernel(FusedArgs fa) {
     // 1. Stream the last piece's K/V tiles through LDS for the state waves.
     if (need_out) {
       u32x4 tk[8], tv[8];
-      int64_t t0 = ps;
+      int64_t t0 = first_weighted(ps, b, dc.l2, T);
       int Lt = (int)((b - t0) < T ? (b - t0) : T);
       load_tile<256>(tk, (const bf16 *)p.k + kvb + t0 * D, Lt, ln.tid);
       load_tile<256>(tv, (const bf16 *)p.v + kvb + t0 * D, Lt, ln.tid);
@@ -712,7 +712,7 @@ void prefill_fused_kernel(FusedArgs fa) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) S[nt] = (f32x16){};
     if (need_out) {
-      int64_t t0 = ps;
+      int64_t t0 = first_weighted(ps, b, dc.l2, T);
       while (t0 < b) {
         const int Lc = (int)((b - t0) < T ? (b - t0) : T);
         __syncthreads();
@@ -772,10 +772,11 @@ void local_state_kernel(FwdArgs p) {
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) S[nt] = (f32x16){};
   u32x4 pk[8], pv[8];  // next tile of K and V
-  int L = (int)((b - ps) < T ? (b - ps) : T);
-  load_tile<NT_LOCAL>(pk, (const bf16 *)p.k + base + ps * D, L, tid);
-  load_tile<NT_LOCAL>(pv, (const bf16 *)p.v + base + ps * D, L, tid);
-  for (int64_t t0 = ps; t0 < b; t0 += T) {
+  const int64_t tf = first_weighted(ps, b, l2, T);
+  int L = (int)((b - tf) < T ? (b - tf) : T);
+  load_tile<NT_LOCAL>(pk, (const bf16 *)p.k + base + tf * D, L, tid);
+  load_tile<NT_LOCAL>(pv, (const bf16 *)p.v + base + tf * D, L, tid);
+  for (int64_t t0 = tf; t0 < b; t0 += T) {
     store_tile<NT_LOCAL>(Ks, pk, tid);
     store_tile<NT_LOCAL>(Vs, pv, tid);
     __syncthreads();

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(NT) void local_state_kernel(FwdArgs p) {
   float acc[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) acc[u] = 0.f;
-  for (int64_t t0 = ps; t0 < b; t0 += T) {
+  for (int64_t t0 = first_weighted(ps, b, log2lam, T); t0 < b; t0 += T) {
     const int L = (int)((b - t0) < T ? (b - t0) : T);
     load_rows<Tin, D>(Ks, (const Tin *)p.k + base + t0 * D, L, tid);
     load_rows<Tin, D>(Vs, (const Tin *)p.v + base + t0 * D, L, tid);

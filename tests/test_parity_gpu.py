@@ -112,6 +112,16 @@ def test_vector_alu_paths(d, dtype, N, seg):
                  lam=[0.999, 0.5, 0.9])
 
 
+@pytest.mark.parametrize("dtype,d,seg", [("bf16", 128, 2048), ("fp32", 64, 1024)])
+def test_local_state_zero_weight_chunks(dtype, d, seg, prefill_path):
+    """Local-state passes skip leading chunks whose decay weights are below
+    2^-160 (exactly zero in float32).  The decays put that cut inside the
+    segments for some heads (0.3, 0.8, 0.93) and beyond them for others, so a
+    misplaced cut changes the entering states and fails the comparison."""
+    run_fwd_case(1, 6, 6000, d, dtype, seed=60 + d, seg=seg, with_init=True,
+                 lam=[0.3, 0.8, 0.93, 0.97, 0.99, 0.999])
+
+
 def test_initial_state_bf16(prefill_path):
     run_fwd_case(1, 4, 2048, 128, "bf16", seed=50, with_init=True, seg=512)
     run_fwd_case(2, 40, 1500, 128, "bf16", seed=51, with_init=True)

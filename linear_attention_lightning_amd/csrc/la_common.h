@@ -137,7 +137,20 @@ struct FwdArgs {
   int nseg;          // segments per head
   const float *init; // [S][H][d][d] or nullptr
   float *fin;        // [S][H][d][d] or nullptr
-  float *ws;         // [nseg][H][d][d] segment states (scan mode) or nullptr
+  float *ws;         // segment states (scan mode) or nullptr: [nseg][r_split][H][d][d];
+                     // the state entering segment s is at slot (s, 0)
+  int r_split;       // pieces per segment of the local-state pass (>= 1)
 };
+
+// Piece r of R of a local-state range [ps, b) cut into chunks of C tokens
+// aligned to ps: chunks [r n / R, (r + 1) n / R) of its n chunks, as tokens
+// [*x0, *x1) (x1 capped at b).  Pieces may be empty when n < R.
+__device__ __forceinline__ void piece_bounds(int64_t ps, int64_t b, int C, int R, int r,
+                                             int64_t *x0, int64_t *x1) {
+  const int64_t n = (b - ps + C - 1) / C;
+  *x0 = ps + ((int64_t)r * n / R) * C;
+  const int64_t e = ps + ((int64_t)(r + 1) * n / R) * C;
+  *x1 = e < b ? e : b;
+}
 
 }  // namespace la

@@ -47,6 +47,7 @@ constexpr int D = 128;
 constexpr int T = 128;           // tokens per chunk
 constexpr int NT = 512;          // threads per workgroup of the chunk kernel (8 waves)
 constexpr int NT_LOCAL = 256;    // threads per workgroup of the local-state kernel
+constexpr int C_LOCAL = 64;      // tokens per chunk of the local-state kernel
 constexpr int KV_ROW = 2 * D;      // LDS row stride (bytes) of every 128 x 128 bf16 tile
 constexpr int LDS_K = T * KV_ROW;  // one K or V tile (32 KB, swizzled)
 constexpr int LDS_KV = 2 * LDS_K;  // the K and V tiles of one chunk
@@ -105,20 +106,21 @@ __device__ __forceinline__ bf16x8 cvt8(const float (&v)[8]) {
 // consumer masks those rows out or multiplies them by exact zeros, so any
 // finite values do, and the loads need no branches (a branch around a load
 // makes the compiler's memory-wait analysis far more conservative).
-template <int NTHR>
-__device__ __forceinline__ void load_tile(u32x4 (&r)[T * 16 / NTHR], const bf16 *src, int L, int t) {
+template <int NTHR, int ROWS = T>
+__device__ __forceinline__ void load_tile(u32x4 (&r)[ROWS * 16 / NTHR], const bf16 *src, int L,
+                                          int t) {
 #pragma unroll
-  for (int it = 0; it < T * 16 / NTHR; ++it) {
+  for (int it = 0; it < ROWS * 16 / NTHR; ++it) {
     const int id = it * NTHR + t, row = id >> 4, c16 = id & 15;
     const int rr = row < L ? row : L - 1;
     r[it] = *(const u32x4 *)(src + (int64_t)rr * D + c16 * 8);
   }
 }
 
-template <int NTHR>
-__device__ __forceinline__ void store_tile(char *dst, const u32x4 (&r)[T * 16 / NTHR], int t) {
+template <int NTHR, int ROWS = T>
+__device__ __forceinline__ void store_tile(char *dst, const u32x4 (&r)[ROWS * 16 / NTHR], int t) {
 #pragma unroll
-  for (int it = 0; it < T * 16 / NTHR; ++it) {
+  for (int it = 0; it < ROWS * 16 / NTHR; ++it) {
     int id = it * NTHR + t, row = id >> 4, c16 = id & 15;
     *(u32x4 *)(dst + kv_off(row, c16 * 16)) = r[it];
   }
@@ -170,9 +172,11 @@ __device__ __forceinline__ void write_st(char *STs, const f32x16 (&S)[4], int u,
     }
 }
 
-// S += (diag(wgt) K)^T V over the 128-row tile in LDS, for this wave's state
-// rows 32u..32u+31: wgt_c = lambda^(e0 - c) for chunk rows c < L, else 0.
+// S += (diag(wgt) K)^T V over the first 16 NKS rows of the tile in LDS, for
+// this wave's state rows 32u..32u+31: wgt_c = lambda^(e0 - c) for chunk rows
+// c < L, else 0.
 // tail8[s] = lambda^(7 - s) (fast path only).
+template <int NKS = T / 16, bool PIPE = true>
 __device__ __forceinline__ void state_update(f32x16 (&S)[4], const char *Ks, const char *Vs,
                                              int L, int e0, float l2, bool fast,
                                              const float (&tail8)[8], int u, int lane) {
@@ -185,33 +189,60 @@ __device__ __forceinline__ void state_update(f32x16 (&S)[4], const char *Ks, con
     vo0[nt] = tr_off(8 * g, nt, G16, i16);
     vo1[nt] = tr_off(8 * g + 4, nt, G16, i16);
   }
-  // Software-pipelined: the LDS reads of step ks + 1 go out before the
-  // arithmetic and MFMAs of step ks, so their latency overlaps work.
-  bf16x8 kf[2], vf[2][4];
-  auto fetch = [&](int ks, int slot) {
-    kf[slot] = tr_read8(Ks + 16 * ks * KV_ROW, ko0, ko1);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) vf[slot][nt] = tr_read8(Vs + 16 * ks * KV_ROW, vo0[nt], vo1[nt]);
-  };
-  fetch(0, 0);
-#pragma unroll
-  for (int ks = 0; ks < T / 16; ++ks) {
-    const int sl = ks & 1;
-    if (ks + 1 < T / 16) fetch(ks + 1, sl ^ 1);
+  // A operand of step ks: the weighted K^T fragment.
+  auto weighted = [&](bf16x8 kf, int ks) -> bf16x8 {
     const int c0 = 16 * ks + 8 * g;
     float wv[8];
     if (fast) {
       const float e = fast_exp2((float)(e0 - c0 - 7) * l2);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) wv[s] = (c0 + s < L) ? (float)kf[sl][s] * (e * tail8[s]) : 0.f;
+      for (int s = 0; s < 8; ++s) wv[s] = (c0 + s < L) ? (float)kf[s] * (e * tail8[s]) : 0.f;
     } else {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        wv[s] = (c0 + s < L) ? (float)kf[sl][s] * fast_exp2((float)(e0 - c0 - s) * l2) : 0.f;
+        wv[s] = (c0 + s < L) ? (float)kf[s] * fast_exp2((float)(e0 - c0 - s) * l2) : 0.f;
     }
-    const bf16x8 a = cvt8(wv);
+    return cvt8(wv);
+  };
+  if constexpr (PIPE) {
+    // Software-pipelined: the LDS reads of step ks + 1 go out before the
+    // arithmetic and MFMAs of step ks, so their latency overlaps work.
+    bf16x8 kf[2], vf[2][4];
+    auto fetch = [&](int ks, int slot) {
+      kf[slot] = tr_read8(Ks + 16 * ks * KV_ROW, ko0, ko1);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) S[nt] = mma(a, vf[sl][nt], S[nt]);
+      for (int nt = 0; nt < 4; ++nt)
+        vf[slot][nt] = tr_read8(Vs + 16 * ks * KV_ROW, vo0[nt], vo1[nt]);
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int sl = ks & 1;
+      if (ks + 1 < NKS) fetch(ks + 1, sl ^ 1);
+      const int c0 = 16 * ks + 8 * g;
+      float wv[8];
+      if (fast) {
+        const float e = fast_exp2((float)(e0 - c0 - 7) * l2);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) wv[s] = (c0 + s < L) ? (float)kf[sl][s] * (e * tail8[s]) : 0.f;
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          wv[s] = (c0 + s < L) ? (float)kf[sl][s] * fast_exp2((float)(e0 - c0 - s) * l2) : 0.f;
+      }
+      const bf16x8 a = cvt8(wv);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) S[nt] = mma(a, vf[sl][nt], S[nt]);
+    }
+  } else {
+    // Fewer registers (for kernels that run several workgroups per CU).
+#pragma unroll 2
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = weighted(tr_read8(Ks + 16 * ks * KV_ROW, ko0, ko1), ks);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        S[nt] = mma(a, tr_read8(Vs + 16 * ks * KV_ROW, vo0[nt], vo1[nt]), S[nt]);
+    }
   }
 }
 
@@ -555,7 +586,7 @@ void prefill_chunk_kernel(FwdArgs p) {
     output_loop(p, h, b, cur, qf, smem, dc, ln);
   } else {
     f32x16 S[4];
-    const float *s0 = p.ws ? p.ws + ((int64_t)s * H + h) * DD
+    const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     load_state(S, s0, ln.w, ln.l32, ln.g);
     state_loop(p, h, b, cur, S, smem, dc, ln);
@@ -740,18 +771,27 @@ void prefill_fused_kernel(FusedArgs fa) {
 
 // Phase A: the local state of each segment's last piece, from zero:
 //   L_s = sum_{c in [ps, b)} lambda^(b-1-c) k_c^T v_c, one decayed MFMA sum.
-// 4 waves; wave u owns state rows 32u..32u+31.
-__global__ __launch_bounds__(NT_LOCAL) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// The piece is cut into p.r_split sub-ranges [x0, x1) of whole 64-token
+// chunks (piece_bounds); one workgroup computes each partial state
+//   P_r = sum_{c in [x0, x1)} lambda^(x1-1-c) k_c^T v_c
+// into slot (s, r), and the scan forms L_s = sum_r lambda^(b - x1_r) P_r.
+// Small workgroups (4 waves, 32 KB of LDS, one chunk in flight) several to a
+// CU hide one another's load and arithmetic latency.  Chunks before
+// first_weighted(ps, b) carry exactly zero weight and are skipped; a partial
+// that lies entirely before that point is not computed (nor read).
+// Wave u owns state rows 32u..32u+31.
+__global__ __launch_bounds__(NT_LOCAL) __attribute__((amdgpu_waves_per_eu(3, 4)))
 void local_state_kernel(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * LDS_K];
-  char *Ks = smem, *Vs = smem + LDS_K;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C_LOCAL * KV_ROW];
+  char *Ks = smem, *Vs = smem + C_LOCAL * KV_ROW;
   const int tid = threadIdx.x, lane = tid & 63, u = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const SeqMap &m = p.m;
-  const int H = m.H;
-  // Segments in reverse dispatch order: the K/V read last are the first
-  // segments', which the output pass reads first (Infinity Cache hits).
-  const int s = p.nseg - 1 - (int)(blockIdx.x / H), h = blockIdx.x - (blockIdx.x / H) * H;
+  const int H = m.H, R = p.r_split;
+  // Segments (and pieces) in reverse dispatch order: the K/V read last are
+  // the first segments', which the output pass reads first (Infinity Cache).
+  const int idx = (int)(blockIdx.x / H), h = blockIdx.x - (blockIdx.x / H) * H;
+  const int s = p.nseg - 1 - idx / R, r = R - 1 - idx % R;
   const float l2 = uniform(log2f(p.decay[h]));
   const bool fast = l2 > kFastLog2;
   const int64_t a = (int64_t)s * p.seg_len;
@@ -764,6 +804,11 @@ void local_state_kernel(FwdArgs p) {
   const int64_t ps0 = m.start(jl);
   const int64_t ps = ps0 > a ? ps0 : a;
   const int64_t base = m.row_base(h, jl);
+  int64_t x0, x1;
+  piece_bounds(ps, b, C_LOCAL, R, r, &x0, &x1);
+  const int64_t tf = first_weighted(ps, b, l2, C_LOCAL);
+  const int64_t r0 = tf > x0 ? tf : x0;
+  if (r0 >= x1) return;
   float tail[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) tail[i] = uniform(fast_exp2((float)(7 - i) * l2));
@@ -771,27 +816,26 @@ void local_state_kernel(FwdArgs p) {
   f32x16 S[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) S[nt] = (f32x16){};
-  u32x4 pk[8], pv[8];  // next tile of K and V
-  const int64_t tf = first_weighted(ps, b, l2, T);
-  int L = (int)((b - tf) < T ? (b - tf) : T);
-  load_tile<NT_LOCAL>(pk, (const bf16 *)p.k + base + tf * D, L, tid);
-  load_tile<NT_LOCAL>(pv, (const bf16 *)p.v + base + tf * D, L, tid);
-  for (int64_t t0 = tf; t0 < b; t0 += T) {
-    store_tile<NT_LOCAL>(Ks, pk, tid);
-    store_tile<NT_LOCAL>(Vs, pv, tid);
+  u32x4 pk[C_LOCAL * 16 / NT_LOCAL], pv[C_LOCAL * 16 / NT_LOCAL];  // next chunk's K and V
+  int L = (int)((x1 - r0) < C_LOCAL ? (x1 - r0) : C_LOCAL);
+  load_tile<NT_LOCAL, C_LOCAL>(pk, (const bf16 *)p.k + base + r0 * D, L, tid);
+  load_tile<NT_LOCAL, C_LOCAL>(pv, (const bf16 *)p.v + base + r0 * D, L, tid);
+  for (int64_t t0 = r0; t0 < x1; t0 += C_LOCAL) {
+    store_tile<NT_LOCAL, C_LOCAL>(Ks, pk, tid);
+    store_tile<NT_LOCAL, C_LOCAL>(Vs, pv, tid);
     __syncthreads();
     const int Lc = L;
-    const int64_t t1 = t0 + T;
-    if (t1 < b) {
-      L = (int)((b - t1) < T ? (b - t1) : T);
-      load_tile<NT_LOCAL>(pk, (const bf16 *)p.k + base + t1 * D, L, tid);
-      load_tile<NT_LOCAL>(pv, (const bf16 *)p.v + base + t1 * D, L, tid);
+    const int64_t t1 = t0 + C_LOCAL;
+    if (t1 < x1) {
+      L = (int)((x1 - t1) < C_LOCAL ? (x1 - t1) : C_LOCAL);
+      load_tile<NT_LOCAL, C_LOCAL>(pk, (const bf16 *)p.k + base + t1 * D, L, tid);
+      load_tile<NT_LOCAL, C_LOCAL>(pv, (const bf16 *)p.v + base + t1 * D, L, tid);
     }
-    // weight of chunk row c: lambda^(b - 1 - (t0 + c))
-    state_update(S, Ks, Vs, Lc, (int)(b - 1 - t0), l2, fast, tail, u, lane);
+    // weight of chunk row c: lambda^(x1 - 1 - (t0 + c))
+    state_update<C_LOCAL / 16, false>(S, Ks, Vs, Lc, (int)(x1 - 1 - t0), l2, fast, tail, u, lane);
     __syncthreads();
   }
-  store_state(p.ws + ((int64_t)s * H + h) * (int64_t)D * D, S, u, l32, g);
+  store_state(p.ws + (((int64_t)s * R + r) * H + h) * (int64_t)D * D, S, u, l32, g);
 }
 
 }  // namespace mfma

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
   Cursor cur = first_chunk(m, a, b, T);
   if (!cur.valid) return;
   {
-    const float *s0 = p.ws ? p.ws + ((int64_t)s * H + h) * DD
+    const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     for (int e = tid; e < D * D; e += NT) (&sm.S[0][0])[e] = s0 ? s0[e] : 0.f;
   }

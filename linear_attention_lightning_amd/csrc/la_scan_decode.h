@@ -12,8 +12,10 @@ namespace la {
 //           = gamma_{s-1} base_{s-1} + L_{s-1}  otherwise,
 // with gamma = lambda^(length of the segment's last piece) and base the state
 // entering that piece (S_in of the segment, or init of the piece's sequence
-// when that sequence starts inside the segment).  ws holds L_s on entry and
-// S_in[s] on exit.  Also writes final states of zero-length sequences.
+// when that sequence starts inside the segment).  ws holds the partial local
+// states of each segment's pieces on entry (L_s is their decayed sum) and
+// S_in[s] at the segment's first slot on exit.  Also writes final states of
+// zero-length sequences.
 // Grid: (H, d*d / 1024); each thread owns 4 consecutive state elements.
 struct ScanArgs {
   SeqMap m;
@@ -23,39 +25,104 @@ struct ScanArgs {
   int d;
   const float *init;
   float *fin;
-  float *ws;
+  float *ws;     // [nseg][r_split][H][d][d]: partial local states in, S_in at slot (s, 0) out
+  int r_split;   // pieces per segment of the local-state pass: 1, 2 or 4
+  int C;         // chunk length of the local-state pass
 };
 
+// What the scan needs of segment s, computed once per workgroup.
+struct SegInfo {
+  int init_in;    // sequence whose initial state enters the segment, or -1 (carry)
+  int init_base;  // sequence whose initial state is the last piece's base, or -1
+                  // (the base is the entering state)
+  int hands_on;   // the segment's last sequence continues after it
+  int live;       // bit r: piece r of the local-state pass was computed
+  float gam;      // lambda^(length of the last piece)
+  float wt[4];    // lambda^(b - x1_r): weight of piece r in L_s
+};
+
+__device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, int s,
+                                            float log2lam, int lgR) {
+  SegInfo d;
+  const int64_t a = (int64_t)s * p.seg_len;
+  const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
+  const int jf = m.seq_of(a);
+  d.init_in = (m.start(jf) == a) ? jf : -1;
+  const int jl = m.seq_of(b - 1);
+  const int64_t ps0 = m.start(jl);
+  const int64_t ps = ps0 > a ? ps0 : a;
+  d.init_base = (ps == a) ? -1 : jl;
+  d.hands_on = m.start(jl + 1) != b;
+  d.gam = pow_lam(log2lam, (float)(b - ps));
+  // Pieces as in piece_bounds (R a power of two); a piece is computed when
+  // some of it lies at or after first_weighted and the state is handed on.
+  const int64_t tf = first_weighted(ps, b, log2lam, p.C);
+  const int64_t n = (b - ps + p.C - 1) / p.C;
+  d.live = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t x0 = ps + ((r * n) >> lgR) * p.C;
+    const int64_t e1 = ps + (((r + 1) * n) >> lgR) * p.C;
+    const int64_t x1 = e1 < b ? e1 : b;
+    const bool live = d.hands_on && r < p.r_split && (tf > x0 ? tf : x0) < x1;
+    d.live |= live ? (1 << r) : 0;
+    d.wt[r] = live ? pow_lam(log2lam, (float)(b - x1)) : 0.f;
+  }
+  return d;
+}
+
 __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
+  constexpr int MAXS = 256;  // segments described per pass
+  constexpr int BLK = 4;     // segments whose partial states are loaded together
+  __shared__ SegInfo info[MAXS];
   const SeqMap &m = p.m;
-  const int H = m.H, h = blockIdx.x;
+  const int H = m.H, h = blockIdx.x, R = p.r_split;
+  const int lgR = R == 4 ? 2 : R == 2 ? 1 : 0;
   const int64_t DD = (int64_t)p.d * p.d;
   const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
-  if (e >= DD) return;
+  const bool mine = e < DD;
   const float log2lam = log2f(p.decay[h]);
   auto init4 = [&](int j) -> f32x4 {
-    if (!p.init) return (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (!p.init || j < 0) return (f32x4){0.f, 0.f, 0.f, 0.f};
     return *(const f32x4 *)(p.init + ((int64_t)j * H + h) * DD + e);
   };
   f32x4 carry = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.nseg; ++s) {
-    const int64_t a = (int64_t)s * p.seg_len;
-    const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
-    const int jf = m.seq_of(a);
-    const f32x4 sin = (m.start(jf) == a) ? init4(jf) : carry;
-    f32x4 *slot = (f32x4 *)(p.ws + ((int64_t)s * H + h) * DD + e);
-    const f32x4 loc = *slot;
-    *slot = sin;
-    const int jl = m.seq_of(b - 1);
-    const int64_t ps0 = m.start(jl);
-    const int64_t ps = ps0 > a ? ps0 : a;
-    const float gam = pow_lam(log2lam, (float)(b - ps));
-    const f32x4 base = (ps == a) ? sin : init4(jl);
-    // When the segment's last sequence ends at b, loc was never written and
-    // the carry is unused: the next segment starts a new sequence.
-    carry = (m.start(jl + 1) == b) ? (f32x4){0.f, 0.f, 0.f, 0.f} : gam * base + loc;
+  for (int sb = 0; sb < p.nseg; sb += MAXS) {
+    const int cnt = (p.nseg - sb) < MAXS ? (p.nseg - sb) : MAXS;
+    __syncthreads();
+    if ((int)threadIdx.x < cnt) info[threadIdx.x] = describe(p, m, sb + threadIdx.x, log2lam, lgR);
+    __syncthreads();
+    if (!mine) continue;
+    for (int s0 = 0; s0 < cnt; s0 += BLK) {
+      // Every partial-state load of the block goes out before the
+      // (sequential, register-only) carry chain runs through it.
+      f32x4 pr[BLK][4];
+#pragma unroll
+      for (int i = 0; i < BLK; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool live = s0 + i < cnt && ((info[s0 + i].live >> r) & 1);
+          pr[i][r] = live ? *(const f32x4 *)(p.ws +
+                                             (((int64_t)(sb + s0 + i) * R + r) * H + h) * DD + e)
+                          : (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) {
+        if (s0 + i >= cnt) break;
+        const SegInfo &d = info[s0 + i];
+        const f32x4 sin = d.init_in >= 0 ? init4(d.init_in) : carry;
+        *(f32x4 *)(p.ws + ((int64_t)(sb + s0 + i) * R * H + h) * DD + e) = sin;
+        f32x4 loc = d.wt[0] * pr[i][0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r) loc += d.wt[r] * pr[i][r];
+        const f32x4 base = d.init_base >= 0 ? init4(d.init_base) : sin;
+        // When the segment's last sequence ends at b, the carry is unused:
+        // the next segment starts a new sequence.
+        carry = d.hands_on ? d.gam * base + loc : (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+    }
   }
-  if (p.fin) {
+  if (p.fin && mine) {
     for (int j = 0; j < m.num_seqs; ++j)
       if (m.start(j) == m.start(j + 1))
         *(f32x4 *)(p.fin + ((int64_t)j * H + h) * DD + e) = init4(j);

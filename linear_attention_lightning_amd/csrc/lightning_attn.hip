@@ -33,6 +33,7 @@ struct Plan {
   int64_t nseg;  // segments per head
   bool scan;     // segments must hand states on (a scan is needed)
   bool fused;    // single-pass kernel hands states on itself (else 3 phases)
+  int r_split;   // pieces per segment of the local-state pass
   size_t ws_bytes;
 };
 
@@ -67,8 +68,21 @@ constexpr int64_t kFusedSeg = 8192;
 // Fixed-length plan.  Without a scan each sequence is one segment.  With
 // one, the token axis of every head is cut into equal segments so that
 // about kTargetGroups workgroups run per phase.
+// Pieces per segment of the MFMA local-state pass: one small workgroup per
+// 8 or more 64-token chunks, at most 4, so that several workgroups share a
+// CU and hide one another's latency.  The vector-ALU pass uses one.
+int pieces(int64_t seg, int d, la_dtype dt) {
+  if (!use_mfma(d, dt)) return 1;
+  const int64_t r = seg / la::mfma::C_LOCAL / 8;
+  return r >= 4 ? 4 : r >= 2 ? 2 : 1;  // a power of two (the scan shifts by it)
+}
+
+size_t phased_ws_bytes(const Plan &p, int H, int d) {
+  return state_bytes(p.nseg * p.r_split * H, d);
+}
+
 Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tokens) {
-  Plan p{N, B, false, false, 0};
+  Plan p{N, B, false, false, 1, 0};
   const int64_t total = (int64_t)B * N;
   if (total == 0) {
     p.nseg = 0;
@@ -93,13 +107,14 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
   p.seg = seg;
   p.scan = (seg != N);
   p.fused = p.scan && fused;
+  p.r_split = (p.scan && !p.fused) ? pieces(seg, d, dt) : 1;
   p.nseg = ceil_div(total, seg);
-  p.ws_bytes = !p.scan ? 0 : p.fused ? fused_ws_bytes(p.nseg, H, d) : state_bytes(p.nseg * H, d);
+  p.ws_bytes = !p.scan ? 0 : p.fused ? fused_ws_bytes(p.nseg, H, d) : phased_ws_bytes(p, H, d);
   return p;
 }
 
 Plan plan_varlen(int H, int64_t total, int d, la_dtype dt, int64_t segment_tokens) {
-  Plan p{1, 0, true, false, 0};
+  Plan p{1, 0, true, false, 1, 0};
   if (total == 0) return p;
   const int T = chunk_tokens(d, dt);
   const bool fused = want_fused(H, d, dt);
@@ -111,8 +126,9 @@ Plan plan_varlen(int H, int64_t total, int d, la_dtype dt, int64_t segment_token
   }
   p.seg = seg;
   p.fused = fused;
+  p.r_split = fused ? 1 : pieces(seg, d, dt);
   p.nseg = ceil_div(total, seg);
-  p.ws_bytes = fused ? fused_ws_bytes(p.nseg, H, d) : state_bytes(p.nseg * H, d);
+  p.ws_bytes = fused ? fused_ws_bytes(p.nseg, H, d) : phased_ws_bytes(p, H, d);
   return p;
 }
 
@@ -139,7 +155,8 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
   dim3 grid((unsigned)(pl.nseg * a.m.H));
   if (use_mfma(d, dt)) {
     if (phase_a)
-      hipLaunchKernelGGL(la::mfma::local_state_kernel, grid, dim3(la::mfma::NT_LOCAL), 0, st, a);
+      hipLaunchKernelGGL(la::mfma::local_state_kernel, dim3(grid.x * (unsigned)a.r_split),
+                         dim3(la::mfma::NT_LOCAL), 0, st, a);
     else
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, a);
   } else if (dt == LA_BF16) {
@@ -156,6 +173,7 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
                   hipStream_t st) {
   la::FwdArgs a = base;
   const int H = a.m.H;
+  a.r_split = pl.r_split;
   if (pl.fused && pl.nseg > 0) {
     // flags, ticket and error word live right after the end-state records
     unsigned *words = (unsigned *)((char *)a.ws + state_bytes(pl.nseg * H, d));
@@ -163,7 +181,7 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
     hipLaunchKernelGGL(la::mfma::fused_reset_kernel, dim3((unsigned)ceil_div(nwords, 256)),
                        dim3(256), 0, st, words, nwords);
     if (has_empty) {
-      la::ScanArgs s{a.m, a.decay, pl.seg, 0, d, a.init, a.fin, a.ws};
+      la::ScanArgs s{a.m, a.decay, pl.seg, 0, d, a.init, a.fin, a.ws, 1, la::mfma::T};
       hipLaunchKernelGGL(la::segment_scan_kernel, dim3((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024)),
                          dim3(256), 0, st, s);
     }
@@ -185,6 +203,8 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
     s.init = a.init;
     s.fin = a.fin;
     s.ws = a.ws;
+    s.r_split = pl.r_split;
+    s.C = use_mfma(d, dt) ? la::mfma::C_LOCAL : la::simt::T;
     dim3 grid((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024));
     hipLaunchKernelGGL(la::segment_scan_kernel, grid, dim3(256), 0, st, s);
   }

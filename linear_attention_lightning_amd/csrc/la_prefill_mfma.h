@@ -38,6 +38,8 @@
 // exponentiated on its own.
 #pragma once
 
+#include <type_traits>
+
 #include "la_common.h"
 
 namespace la {
@@ -55,6 +57,10 @@ constexpr int LDS_ST = D * KV_ROW; // S^T (32 KB, swizzled like the tiles)
 // The chunk kernel: two chunks' K/V tiles (double buffer) and S^T: 160 KB.
 constexpr int LDS_BYTES = 2 * LDS_KV + LDS_ST;
 constexpr float kFastLog2 = -15.f;  // factored powers when log2(lambda) > this
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family
+// GPUs: 32-bit data format, no index addressing; an access at or past the
+// resource's byte range reads zero or writes nothing.
+constexpr int kRawBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -89,6 +95,31 @@ __device__ __forceinline__ int tr_off(int r4, int blk, int G16, int i16) {
 __device__ __forceinline__ bf16x8 tr_read8(const char *base, int o0, int o1) {
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS s16x4 *)(base + o0));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS s16x4 *)(base + o1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 32-bit LDS byte addresses.  The swizzle only permutes bits 4..7 of a
+// tile offset, so for a tile base aligned to 256 bytes, kv_off(r, B + 16 x)
+// = kv_off(r, B) ^ (x << 4) whenever B / 16 and x share no bits: the
+// per-fragment addresses of the output side are formed as one XOR of a
+// per-chunk base (which keeps the compiler from hoisting dozens of
+// loop-invariant offsets into registers).
+__device__ __forceinline__ unsigned lds_u32(const char *p) {
+  return (unsigned)(size_t)(const LA_LDS char *)p;
+}
+template <class T>
+__device__ __forceinline__ T lds_ld(unsigned a) {
+  return *(const LA_LDS T *)a;
+}
+template <class T>
+__device__ __forceinline__ void lds_st(unsigned a, T v) {
+  *(LA_LDS T *)a = v;
+}
+__device__ __forceinline__ bf16x8 tr_read8u(unsigned a0, unsigned a1) {
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS s16x4 *)a0);
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LA_LDS s16x4 *)a1);
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, r);
@@ -246,28 +277,45 @@ __device__ __forceinline__ void state_update(f32x16 (&S)[4], const char *Ks, con
   }
 }
 
-// Q^T fragments of one query row (B operand, k = feature), straight from HBM.
-__device__ __forceinline__ void load_qf(u32x4 (&qf)[8], const bf16 *qrow, int g) {
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const u32x4 *)(qrow + 16 * ks + 8 * g);
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// Inter-block term O^T = S^T Q^T for the wave's 32 rows, scaled by a_row.
-// ka[ks] = kv_off(l32, 32 ks + 16 g): this lane's A-operand offsets.
-__device__ __forceinline__ void inter_term(f32x16 (&acc)[4], const char *STs, const u32x4 *qf,
-                                           float a_row, const int (&ka)[8]) {
+// Inter-block term O^T = S^T Q^T for the wave's two 16-row query blocks,
+// block bi scaled by a[bi] = lambda^(row + 1) of this lane's query row.
+// acc[bi][jt] register r: feature 16 jt + 4 G + r of the lane's query.  One
+// S^T fragment (rows 16 jt + i16, features 32 ks + 8 G ..) serves both
+// blocks; st = LDS address of S^T + kv_off(i16, 16 G), so fragment (jt, ks)
+// sits at (st ^ (ks << 6)) + 4096 jt.
+__device__ __forceinline__ void inter_term(f32x4 (&acc)[2][8], unsigned st,
+                                           const u32x4 (&qf)[2][4], const float (&a)[2]) {
+  // Software-pipelined one feature tile ahead; the scheduling barriers keep
+  // the compiler from hoisting every tile's reads (128 registers) up front.
+  bf16x8 sf[2][4];
+  auto fetch = [&](int jt, int slot) {
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    acc[jt] = (f32x16){};
-    const char *stblk = STs + 32 * jt * KV_ROW;
+    for (int ks = 0; ks < 4; ++ks) sf[slot][ks] = lds_ld<bf16x8>((st ^ (ks << 6)) + 4096 * jt);
+  };
+  fetch(0, 0);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      acc[jt] = mma(*(const bf16x8 *)(stblk + ka[ks]), as_bf16x8(qf[ks]), acc[jt]);
+  for (int jt = 0; jt < 8; ++jt) {
+    if (jt + 1 < 8) fetch(jt + 1, (jt + 1) & 1);
+    acc[0][jt] = (f32x4){};
+    acc[1][jt] = (f32x4){};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      acc[0][jt] = mma16(sf[jt & 1][ks], as_bf16x8(qf[0][ks]), acc[0][jt]);
+      acc[1][jt] = mma16(sf[jt & 1][ks], as_bf16x8(qf[1][ks]), acc[1][jt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) acc[jt] *= a_row;
+  for (int jt = 0; jt < 8; ++jt) {
+    acc[0][jt] *= a[0];
+    acc[1][jt] *= a[1];
+  }
 }
 
 // Per-workgroup constants and lane coordinates of the 8-wave layout.  The
@@ -277,21 +325,22 @@ __device__ __forceinline__ void inter_term(f32x16 (&acc)[4], const char *STs, co
 // role's loads into the same registers and waits for every prefetch right
 // after issuing it.)
 struct Lanes {
-  int tid, lane, wave, w, l32, g, G16, i16, row, ts;
+  int tid, lane, wave, w, l32, g, G16, i16, ts;
   bool out_wave;
   __device__ __forceinline__ Lanes() {
     tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     out_wave = wave < 4;
-    w = wave & 3;  // output rows 32w.. or state rows 32w..
+    w = wave & 3;  // output query blocks w and 7 - w, or state rows 32w..
     l32 = lane & 31;
     g = lane >> 5;
     G16 = lane >> 4;
     i16 = lane & 15;
-    row = 32 * w + l32;  // output waves: this lane's query row in the chunk
     ts = tid - 256;  // state waves: index among the 256 loaders
   }
+  // Output waves: query block bi (0: rows 16w.., 1: rows 16(7-w)..).
+  __device__ __forceinline__ int qblock(int bi) const { return bi ? 7 - w : w; }
 };
 
 struct Decay {
@@ -306,13 +355,36 @@ struct Decay {
   }
 };
 
-// Q^T fragments of chunk c for this output wave's 32 rows.
-__device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cursor &c,
-                                              u32x4 (&qf)[8], const Lanes &ln) {
+// Lane coordinates of an output wave (query blocks w and 7 - w), derived
+// from the lane id after it passes through an empty asm statement.  Built
+// afresh where the chunk loop needs them, so the compiler cannot hoist the
+// derived offsets and row numbers out of the loop and keep a dozen more
+// registers alive across it.
+struct OutLane {
+  int lane, i16, G, w;
+  __device__ __forceinline__ OutLane(int lane_id, int wave) {
+    int l = lane_id;
+    asm volatile("" : "+v"(l));
+    lane = l;
+    i16 = l & 15;
+    G = l >> 4;
+    w = wave;
+  }
+  __device__ __forceinline__ int qblock(int bi) const { return bi ? 7 - w : w; }
+};
+
+// Q^T fragments of chunk c for query block bi of this output wave, straight
+// from HBM (B operand of the 16x16x32 products: qf[ks] holds features
+// 32 ks + 8 G .. + 7 of query row 16 qblock(bi) + i16).
+__device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cursor &c, int bi,
+                                              u32x4 (&qf)[4], const OutLane &o) {
   // Rows past the chunk's end read its last row: their outputs are never stored.
   const int Lc = (int)(c.c1 - c.c0);
-  const int r = ln.row < Lc ? ln.row : Lc - 1;
-  load_qf(qf, (const bf16 *)p.q + p.m.row_base(h, c.j) + (c.c0 + r) * D, ln.g);
+  const int row = 16 * o.qblock(bi) + o.i16;
+  const bf16 *qrow = (const bf16 *)p.q + p.m.row_base(h, c.j) +
+                     (c.c0 + (row < Lc ? row : Lc - 1)) * D + 8 * o.G;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const u32x4 *)(qrow + 32 * ks);
 }
 
 // K and V rows of chunk c, spread over the 256 threads of a role (register
@@ -368,149 +440,177 @@ __device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const
   }
 }
 
-// Writes this output wave's 32 staged rows of chunk c (rows >= the chunk
-// length are skipped) as whole rows: lane reads 16 bytes of row
-// 32w + 4it + lane/16 from the swizzled staging tile and stores them.
-__device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor &c,
-                                           const char *Os, const Lanes &ln) {
+// Writes this output wave's 32 staged rows of chunk c as whole rows: per
+// query block, lane reads 16 bytes of row 16 qblock + 4 it + lane/16 from the
+// swizzled staging tile at Os (LDS address, 256-byte aligned; row r0 + 4 it
+// sits at (kv_off(r0, .) ^ (it << 4)) + 1024 it) and stores them.  The stores
+// go through a buffer resource whose range ends at the chunk's last row:
+// the hardware drops those to rows >= the chunk length, so every store is an
+// unconditional instruction (a branch around each one would make the
+// compiler's memory-wait analysis assume they might not have been issued,
+// and wait for them at the next chunk's first Q^T use).
+__device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor &c, unsigned Os,
+                                           const OutLane &o) {
   const int L = (int)(c.c1 - c.c0);
-  const int r0 = 32 * ln.w + (ln.lane >> 4), c16 = ln.lane & 15;
-  bf16 *obase = (bf16 *)p.out + p.m.row_base(h, c.j) + (c.c0 + r0) * D + c16 * 8;
+  const int sub = o.G, c16 = o.i16;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (bf16 *)p.out + p.m.row_base(h, c.j) + c.c0 * D, 0, L * (D * 2), kRawBufferWord3);
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const u32x4 x = *(const u32x4 *)(Os + kv_off(r0 + 4 * it, c16 * 16));
-    if (r0 + 4 * it < L) *(u32x4 *)(obase + 4 * it * D) = x;
+  for (int bi = 0; bi < 2; ++bi) {
+    const int r0 = 16 * o.qblock(bi) + sub;
+    const unsigned rb = Os + kv_off(r0, c16 * 16);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const u32x4 x = lds_ld<u32x4>((rb ^ (it << 4)) + 1024 * it);
+      __builtin_amdgcn_raw_buffer_store_b128(x, rs, (r0 + 4 * it) * (D * 2) + c16 * 16, 0, 0);
+    }
   }
 }
 
 // LDS use of the chunk loop.  Chunk n of the walk uses buffer n % 2 (its K
 // tile, then its V tile); S^T follows the two buffers.  The tiles arrive by
-// direct loads: chunk n + 1's K tile from output waves 0 and 1 once their
-// (short) intra-block work for chunk n is done, chunk n + 2's V tile from the
-// state waves right after the barrier that closes chunk n (when that
-// buffer's V tile is free).  Every tile has a good part of a chunk period to
-// arrive, no single burst of loads outgrows what the CU keeps in flight, and
-// no wave with work on the critical path stalls on issuing them.  After chunk
-// n closes, its K tile holds the output waves' staged output rows until they
+// direct loads: chunk n + 1's K tile from the output waves right after the
+// barrier that opens chunk n (that buffer's staged output rows of chunk n - 1
+// have been written back by then), chunk n + 2's V tile from the state waves
+// right after the barrier that closes chunk n (when that buffer's V tile is
+// free).  Every tile has a good part of a chunk period to arrive and no
+// single burst of loads outgrows what the CU keeps in flight.  After chunk n
+// closes, its K tile holds the output waves' staged output rows until they
 // are written back.
 //
+// Per chunk, two barriers shared by both roles:
+//   A (opens the chunk): its K/V tiles and the S^T of the state entering it
+//     are in LDS.  Output waves: inter-block term, then intra-block term;
+//     state waves: the state update.
+//   B (closes it): every read of its K/V tiles and of S^T is done.  Output
+//     waves: stage and write back the outputs; state waves: publish the next
+//     S^T and start the V tile after next.
+// The inter-block term thus overlaps the state update instead of waiting
+// for it, and both heavy phases sit between A and B.
+//
+// The intra-block term runs on 16x16x32 MFMA tiles: output wave w owns the
+// 16-row query blocks w and 7 - w, so every wave has the same causal work
+// (nine 16-key blocks of K Q^T and five 32-key steps of V^T P^T).
+//
 // The chunk loop over segment [cur.c0, b) of head h, output side.  On entry
-// qf holds (or is loading) the first chunk's Q^T fragments.  Per chunk: two
-// barriers, shared with state_loop, which runs the same chunk sequence.
+// qn holds (or is loading) the first chunk's Q^T fragments.
 __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
-                                            u32x4 (&qf)[8], char *smem, const Decay &dc,
+                                            u32x4 (&qn)[2][4], char *smem, const Decay &dc,
                                             const Lanes &ln) {
-  const char *STs = smem + 2 * LDS_KV;
   const SeqMap &m = p.m;
-  const int w = ln.w, l32 = ln.l32, g = ln.g, row = ln.row;
+  const int w = ln.w;
   const float l2 = dc.l2;
   const bool fast = dc.fast;
-  const float a_row = fast_exp2((float)(row + 1) * l2);
-  // Tile offsets of this lane: rows 32kc + l32 (or 32jt + l32 of S^T),
-  // 16-byte granule 2ks + g (A operand of K Q^T and S^T Q^T); V rows
-  // 32kc + 16q2 + 4g + (0..3, 8..11), columns 32jt.. (transposed reads).
-  int ka[8], va0[4], va1[4];
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) ka[ks] = kv_off(l32, 32 * ks + 16 * g);
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    va0[jt] = tr_off(4 * g, jt, ln.G16, ln.i16);
-    va1[jt] = tr_off(4 * g + 8, jt, ln.G16, ln.i16);
-  }
-  f32x16 acc[4];
-  u32x4 qn[8];
+  const unsigned STs = lds_u32(smem + 2 * LDS_KV);
+  f32x4 acc[2][8];
+  u32x4 qf[2][4];
   int buf = 0;
-  __syncthreads();  // the first chunk's K/V and the entering S^T are in LDS
-  inter_term(acc, STs, qf, a_row, ka);
 
   while (true) {
     const Cursor nxt = next_chunk(m, cur, b, T);
-    const char *Ks = smem + buf * LDS_KV, *Vs = Ks + LDS_K;
-    __syncthreads();  // A: this chunk's K/V are in LDS
-    if (nxt.valid) issue_q_loads(p, h, nxt, qn, ln);
-    // Intra-block term over key sub-blocks kc <= w (causal).
-    for (int kc = 0; kc <= w; ++kc) {
-      // K Q^T as two interleaved MFMA chains (even and odd k steps), halving
-      // the dependent-issue latency of one 8-long chain.
-      f32x16 pt = {}, pt1 = {};
-      const char *kblk = Ks + 32 * kc * KV_ROW;
+    const unsigned Ks = lds_u32(smem + buf * LDS_KV), Vs = Ks + LDS_K;
+    __syncthreads();  // A: this chunk's K/V and entering S^T are in LDS
 #pragma unroll
-      for (int ks = 0; ks < 8; ks += 2) {
-        pt = mma(*(const bf16x8 *)(kblk + ka[ks]), as_bf16x8(qf[ks]), pt);
-        pt1 = mma(*(const bf16x8 *)(kblk + ka[ks + 1]), as_bf16x8(qf[ks + 1]), pt1);
-      }
-      pt += pt1;
-      // pt register 4q+mm: key c = 32kc + 8q + 4g + mm, query `row`.
+    for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n0 = row - (32 * kc + 8 * q + 4 * g);
-        if (fast) {
-          const float e = fast_exp2((float)(n0 - 3) * l2);
+      for (int ks = 0; ks < 4; ++ks) qf[bi][ks] = qn[bi][ks];
+    {
+      const OutLane o(ln.lane, w);
+      const int i16 = o.i16, G = o.G;
+      // Tile offsets of this lane (see lds_u32): rows 16 n + i16 (K or S^T),
+      // granule 4 ks + G (A operand of K Q^T and S^T Q^T): kq ^ (ks << 6);
+      // V rows 4 G + (0..3) (+ 16), columns 16 jt .. 16 jt + 15 (transposed
+      // reads): vq ^ (jt << 5).
+      const unsigned kq = kv_off(i16, 16 * G);
+      const unsigned vq = kv_off(4 * G + (i16 >> 2), 8 * (i16 & 3));
+      float a_row[2];
 #pragma unroll
-          for (int mm = 0; mm < 4; ++mm)
-            pt[4 * q + mm] = (n0 >= mm) ? pt[4 * q + mm] * (e * dc.tail[4 + mm]) : 0.f;
-        } else {
+      for (int bi = 0; bi < 2; ++bi)
+        a_row[bi] = fast_exp2((float)(16 * o.qblock(bi) + i16 + 1) * l2);
+
+      // Intra-block term of query block bi (rows 16 rb + i16) over the
+      // 32-key steps kp <= rb / 2: P^T = K Q^T for keys 32 kp + (0..15) (p0)
+      // and, when causal, 32 kp + 16 + (0..15) (p1); register r of p0 holds
+      // key 32 kp + 4 G + r, of p1 key 32 kp + 16 + 4 G + r.  Masked and
+      // decayed (lambda^(row - key), zero above the diagonal), then
+      // O^T += V^T P^T with V read in the same key order.
+      auto intra = [&](auto bic, int rb) {
+        constexpr int bi = decltype(bic)::value;
+        const int row = 16 * rb + i16;
+        for (int kp = 0; kp <= (rb >> 1); ++kp) {
+          const unsigned kb = Ks + 32 * kp * KV_ROW + kq;
+          f32x4 p0 = {}, p1 = {};
 #pragma unroll
-          for (int mm = 0; mm < 4; ++mm)
-            pt[4 * q + mm] = (n0 >= mm) ? pt[4 * q + mm] * fast_exp2((float)(n0 - mm) * l2) : 0.f;
+          for (int ks = 0; ks < 4; ++ks)
+            p0 = mma16(lds_ld<bf16x8>(kb ^ (ks << 6)), as_bf16x8(qf[bi][ks]), p0);
+          if (2 * kp + 1 <= rb) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+              p1 = mma16(lds_ld<bf16x8>((kb ^ (ks << 6)) + 16 * KV_ROW), as_bf16x8(qf[bi][ks]),
+                         p1);
+          }
+          const int n0 = row - (32 * kp + 4 * G), n1 = n0 - 16;
+          float pw[8];
+          if (fast) {
+            const float e0 = fast_exp2((float)(n0 - 3) * l2), e1 = fast_exp2((float)(n1 - 3) * l2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              pw[r] = (n0 >= r) ? p0[r] * (e0 * dc.tail[4 + r]) : 0.f;
+              pw[4 + r] = (n1 >= r) ? p1[r] * (e1 * dc.tail[4 + r]) : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              pw[r] = (n0 >= r) ? p0[r] * fast_exp2((float)(n0 - r) * l2) : 0.f;
+              pw[4 + r] = (n1 >= r) ? p1[r] * fast_exp2((float)(n1 - r) * l2) : 0.f;
+            }
+          }
+          const bf16x8 pb = cvt8(pw);
+          const unsigned vb = Vs + 32 * kp * KV_ROW + vq;
+#pragma unroll
+          for (int jt = 0; jt < 8; ++jt) {
+            const unsigned va = vb ^ (jt << 5);
+            acc[bi][jt] = mma16(tr_read8u(va, va + 16 * KV_ROW), pb, acc[bi][jt]);
+          }
+        }
+      };
+
+      // The next chunk's Q^T: block 0 now, block 1 once this chunk's block 0
+      // fragments are spent (keeps one 16-register set fewer alive).
+      if (nxt.valid) issue_q_loads(p, h, nxt, 0, qn[0], o);
+      inter_term(acc, STs + kq, qf, a_row);
+      intra(std::integral_constant<int, 0>{}, w);
+      if (nxt.valid) issue_q_loads(p, h, nxt, 1, qn[1], o);
+      intra(std::integral_constant<int, 1>{}, 7 - w);
+    }
+    __syncthreads();  // B: this chunk's K/V and S^T reads are done
+    {
+      // Stage the tile in this wave's rows of the chunk's K tile (acc[bi][jt]
+      // register r holds feature 16 jt + 4 G + r of row 16 qblock(bi) + i16:
+      // at kv_off(row, 8 G) ^ (jt << 5)), then write it back as whole rows.
+      const OutLane o(ln.lane, w);
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        const unsigned sb = Ks + kv_off(16 * o.qblock(bi) + o.i16, 8 * o.G);
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+          bf16x4 v = {(bf16)acc[bi][jt][0], (bf16)acc[bi][jt][1], (bf16)acc[bi][jt][2],
+                      (bf16)acc[bi][jt][3]};
+          lds_st<bf16x4>(sb ^ (jt << 5), v);
         }
       }
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        float pv8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv8[e] = pt[8 * q2 + e];
-        const bf16x8 pb = cvt8(pv8);
-        const char *vblk = Vs + (32 * kc + 16 * q2) * KV_ROW;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          bf16x8 vf = tr_read8(vblk, va0[jt], va1[jt]);
-          acc[jt] = mma(vf, pb, acc[jt]);
-        }
-      }
+      write_rows(p, h, cur, Ks, o);
     }
-    // Output waves 0 and 1 have the least intra-block work: they load the
-    // next chunk's K tile into the other buffer (free since the previous
-    // chunk's rows were written back).
-    if (w < 2 && nxt.valid) {
-      char *Kn = smem + (buf ^ 1) * LDS_KV;
-      dma_tile_rows(Kn, p.k, p, h, nxt, 2 * w, ln.lane);
-      dma_tile_rows(Kn, p.k, p, h, nxt, 2 * w + 1, ln.lane);
-    }
-    __syncthreads();  // B: this chunk's K/V reads are done; the next S^T is published
-    // Stage the tile in this wave's rows of the chunk's K tile (acc[jt]
-    // registers 4rq..4rq+3 hold features 32jt + 8rq + 4g + 0..3 of `row`).
-    char *Os = smem + buf * LDS_KV;
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 v = {(bf16)acc[jt][4 * rq], (bf16)acc[jt][4 * rq + 1], (bf16)acc[jt][4 * rq + 2],
-                    (bf16)acc[jt][4 * rq + 3]};
-        *(bf16x4 *)(Os + kv_off(row, (32 * jt + 8 * rq + 4 * g) * 2)) = v;
-      }
-    if (!nxt.valid) {
-      write_rows(p, h, cur, Os, ln);
-      break;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = qn[ks];
-    inter_term(acc, STs, qf, a_row, ka);
-    // The next chunk's K tile has landed before the barrier that hands it
-    // over (the loads were issued a good part of a chunk period ago).
-    if (w < 2) vm_wait<0>();
-    // The staged rows go out last, after every load this wave waits for
-    // before them (the memory counter retires in issue order).
-    write_rows(p, h, cur, Os, ln);
+    if (!nxt.valid) break;
     cur = nxt;
     buf ^= 1;
   }
 }
 
 // The chunk loop, state side.  On entry S holds the state entering the
-// segment.  Loads every K/V tile of the walk (see above), updates the state
-// and publishes it as S^T; writes every sequence end's final state inside
-// the segment.
+// segment.  Loads every K/V tile of the walk but the output waves' K tiles
+// (see above), updates the state and publishes it as S^T; writes every
+// sequence end's final state inside the segment.
 __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                            f32x16 (&S)[4], char *smem, const Decay &dc,
                                            const Lanes &ln) {
@@ -528,12 +628,14 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
   write_st(STs, S, w, l32, g);
   if (nxt.valid) vm_wait<8>();
   else vm_wait<0>();
-  __syncthreads();  // the first chunk's K/V and the entering S^T are in LDS
 
   while (true) {
     const int L = (int)(cur.c1 - cur.c0);
     char *Ks = smem + buf * LDS_KV, *Vs = Ks + LDS_K;
-    __syncthreads();  // A: this chunk's K/V are in LDS; the output side has read S^T
+    __syncthreads();  // A: this chunk's K/V and entering S^T are in LDS
+    // The next chunk's K tile goes into the other buffer, whose staged output
+    // rows were written back before A.
+    if (nxt.valid) dma_tile_rows(smem + (buf ^ 1) * LDS_KV, p.k, p, h, nxt, w, lane);
     const bool seq_done = (cur.c1 == cur.seq_end);
     const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
     if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
@@ -543,19 +645,15 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
       state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane);
       if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
     }
-    // (A new piece's state load sits in the same block as the S^T write that
-    // consumes it, so no path reaches the next chunk with those loads open.)
-    if (nxt.valid) {
-      if (new_piece)
-        load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, w, l32, g);
-      write_st(STs, S, w, l32, g);
-    }
-    __syncthreads();  // B: this chunk's K/V reads are done; the next S^T is published
+    __syncthreads();  // B: this chunk's K/V and S^T reads are done
     if (!nxt.valid) break;
+    if (new_piece)
+      load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, w, l32, g);
+    write_st(STs, S, w, l32, g);
     const Cursor nxt2 = next_chunk(m, nxt, b, T);
     if (nxt2.valid) {
       dma_tile_rows(Vs, p.v, p, h, nxt2, w, lane);
-      vm_wait<8>();  // the next chunk's V tile has landed (only these 8 may be open)
+      vm_wait<8>();  // the next chunk's K and V tiles have landed (only these 8 may be open)
     } else {
       vm_wait<0>();
     }
@@ -569,7 +667,7 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 // segment's entering state (scan result, initial state or zero).
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_chunk_kernel(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const Lanes ln;
   const SeqMap &m = p.m;
   const int H = m.H;
@@ -581,9 +679,11 @@ void prefill_chunk_kernel(FwdArgs p) {
   const Cursor cur = first_chunk(m, a, b, T);
   if (!cur.valid) return;
   if (ln.out_wave) {
-    u32x4 qf[8];
-    issue_q_loads(p, h, cur, qf, ln);
-    output_loop(p, h, b, cur, qf, smem, dc, ln);
+    u32x4 qn[2][4];
+    const OutLane o(ln.lane, ln.w);
+    issue_q_loads(p, h, cur, 0, qn[0], o);
+    issue_q_loads(p, h, cur, 1, qn[1], o);
+    output_loop(p, h, b, cur, qn, smem, dc, ln);
   } else {
     f32x16 S[4];
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
@@ -661,7 +761,7 @@ __device__ __forceinline__ void combine_states(f32x16 (&X)[4], const float *prev
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_fused_kernel(FusedArgs fa) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   // The ticket passes through the first word of the S^T area, which is not
   // written before the chunk loop starts.
   unsigned *sh_ticket = (unsigned *)(smem + 2 * LDS_KV);
@@ -715,8 +815,10 @@ void prefill_fused_kernel(FusedArgs fa) {
       }
     }
     // 2. The first chunk's Q loads go out while waiting for the entering state.
-    u32x4 qf[8];
-    issue_q_loads(p, h, cur, qf, ln);
+    u32x4 qn[2][4];
+    const OutLane o(ln.lane, ln.w);
+    issue_q_loads(p, h, cur, 0, qn[0], o);
+    issue_q_loads(p, h, cur, 1, qn[1], o);
     if (need_in && ln.tid == 0) {
       const unsigned *fl = fa.flags + (size_t)(s - 1) * H + h;
       int it = 0;
@@ -736,7 +838,7 @@ void prefill_fused_kernel(FusedArgs fa) {
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     // 3. Outputs from the entering state.
-    output_loop(p, h, b, cur, qf, smem, dc, ln);
+    output_loop(p, h, b, cur, qn, smem, dc, ln);
   } else {
     // 1. L = sum over the last piece of lambda^(b-1-c) k_c^T v_c.
     f32x16 S[4];

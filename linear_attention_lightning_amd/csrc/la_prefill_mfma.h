@@ -315,6 +315,10 @@ __device__ __forceinline__ void inter_term(f32x4 (&acc)[2][8], unsigned st,
   for (int jt = 0; jt < 8; ++jt) {
     acc[0][jt] *= a[0];
     acc[1][jt] *= a[1];
+    // Materialise the results here: left alone, the compiler sinks block 1's
+    // products past block 0's intra-block loop (to where they are first
+    // needed) and keeps the S^T fragments alive across it.
+    asm volatile("" : "+v"(acc[0][jt]), "+v"(acc[1][jt]));
   }
 }
 
@@ -494,13 +498,16 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 //
 // The chunk loop over segment [cur.c0, b) of head h, output side.  On entry
 // qn holds (or is loading) the first chunk's Q^T fragments.
+// FAST: the decay weights take the factored powers (see Decay); a template
+// parameter so that each chunk step is one basic block the scheduler can
+// interleave freely.
+template <bool FAST>
 __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                             u32x4 (&qn)[2][4], char *smem, const Decay &dc,
                                             const Lanes &ln) {
   const SeqMap &m = p.m;
   const int w = ln.w;
   const float l2 = dc.l2;
-  const bool fast = dc.fast;
   const unsigned STs = lds_u32(smem + 2 * LDS_KV);
   f32x4 acc[2][8];
   u32x4 qf[2][4];
@@ -530,10 +537,12 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
 
       // Intra-block term of query block bi (rows 16 rb + i16) over the
       // 32-key steps kp <= rb / 2: P^T = K Q^T for keys 32 kp + (0..15) (p0)
-      // and, when causal, 32 kp + 16 + (0..15) (p1); register r of p0 holds
-      // key 32 kp + 4 G + r, of p1 key 32 kp + 16 + 4 G + r.  Masked and
-      // decayed (lambda^(row - key), zero above the diagonal), then
-      // O^T += V^T P^T with V read in the same key order.
+      // and 32 kp + 16 + (0..15) (p1; wholly above the diagonal in the last
+      // step of an even block, where the mask zeroes it: computing it anyway
+      // keeps the step free of branches); register r of p0 holds key
+      // 32 kp + 4 G + r, of p1 key 32 kp + 16 + 4 G + r.  Masked and decayed
+      // (lambda^(row - key), zero above the diagonal), then O^T += V^T P^T
+      // with V read in the same key order.
       auto intra = [&](auto bic, int rb) {
         constexpr int bi = decltype(bic)::value;
         const int row = 16 * rb + i16;
@@ -541,17 +550,13 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
           const unsigned kb = Ks + 32 * kp * KV_ROW + kq;
           f32x4 p0 = {}, p1 = {};
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
+          for (int ks = 0; ks < 4; ++ks) {
             p0 = mma16(lds_ld<bf16x8>(kb ^ (ks << 6)), as_bf16x8(qf[bi][ks]), p0);
-          if (2 * kp + 1 <= rb) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-              p1 = mma16(lds_ld<bf16x8>((kb ^ (ks << 6)) + 16 * KV_ROW), as_bf16x8(qf[bi][ks]),
-                         p1);
+            p1 = mma16(lds_ld<bf16x8>((kb ^ (ks << 6)) + 16 * KV_ROW), as_bf16x8(qf[bi][ks]), p1);
           }
           const int n0 = row - (32 * kp + 4 * G), n1 = n0 - 16;
           float pw[8];
-          if (fast) {
+          if constexpr (FAST) {
             const float e0 = fast_exp2((float)(n0 - 3) * l2), e1 = fast_exp2((float)(n1 - 3) * l2);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -683,7 +688,10 @@ void prefill_chunk_kernel(FwdArgs p) {
     const OutLane o(ln.lane, ln.w);
     issue_q_loads(p, h, cur, 0, qn[0], o);
     issue_q_loads(p, h, cur, 1, qn[1], o);
-    output_loop(p, h, b, cur, qn, smem, dc, ln);
+    if (dc.fast)
+      output_loop<true>(p, h, b, cur, qn, smem, dc, ln);
+    else
+      output_loop<false>(p, h, b, cur, qn, smem, dc, ln);
   } else {
     f32x16 S[4];
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
@@ -838,7 +846,10 @@ void prefill_fused_kernel(FusedArgs fa) {
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     // 3. Outputs from the entering state.
-    output_loop(p, h, b, cur, qn, smem, dc, ln);
+    if (dc.fast)
+      output_loop<true>(p, h, b, cur, qn, smem, dc, ln);
+    else
+      output_loop<false>(p, h, b, cur, qn, smem, dc, ln);
   } else {
     // 1. L = sum over the last piece of lambda^(b-1-c) k_c^T v_c.
     f32x16 S[4];

@@ -16,7 +16,6 @@ namespace {
 using la::bf16;
 
 constexpr int kVersion = 100;    // 0.1.0
-constexpr int kTargetGroups = 512;  // aim for >= 2 workgroups per CU on 256 CUs
 
 bool valid_block(int b) { return b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
 bool valid_d(int d) { return d == 64 || d == 128; }
@@ -67,7 +66,13 @@ constexpr int64_t kFusedSeg = 8192;
 
 // Fixed-length plan.  Without a scan each sequence is one segment.  With
 // one, the token axis of every head is cut into equal segments so that
-// about kTargetGroups workgroups run per phase.
+// about target_groups(d, dt) workgroups run per phase.
+// Workgroups to aim for per phase: the MFMA chunk kernel (160 KB of LDS) runs
+// one workgroup per CU, and a single round over the 256 CUs with long
+// segments measured fastest (fewer, longer pipelines and less local-state
+// work); the vector-ALU kernels run several small workgroups per CU.
+int64_t target_groups(int d, la_dtype dt) { return use_mfma(d, dt) ? 256 : 512; }
+
 // Pieces per segment of the MFMA local-state pass: one small workgroup per
 // 8 or more 64-token chunks, at most 4, so that several workgroups share a
 // CU and hide one another's latency.  The vector-ALU pass uses one.
@@ -94,7 +99,7 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
     seg = segment_tokens;
   } else {
     const int64_t bh = (int64_t)B * H;
-    int64_t G = ceil_div(kTargetGroups, bh);
+    int64_t G = ceil_div(target_groups(d, dt), bh);
     const int64_t maxG = ceil_div(N, T);
     if (G > maxG) G = maxG;
     if (G > 1) {
@@ -120,7 +125,7 @@ Plan plan_varlen(int H, int64_t total, int d, la_dtype dt, int64_t segment_token
   const bool fused = want_fused(H, d, dt);
   int64_t seg = segment_tokens;
   if (seg <= 0) {
-    const int64_t G = ceil_div(kTargetGroups, H);
+    const int64_t G = ceil_div(target_groups(d, dt), H);
     seg = ceil_div(ceil_div(total, G), T) * T;
     if (fused && seg > kFusedSeg) seg = kFusedSeg;
   }

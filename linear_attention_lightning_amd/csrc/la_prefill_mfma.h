@@ -892,6 +892,11 @@ void prefill_fused_kernel(FusedArgs fa) {
 // CU hide one another's load and arithmetic latency.  Chunks before
 // first_weighted(ps, b) carry exactly zero weight and are skipped; a partial
 // that lies entirely before that point is not computed (nor read).
+// Grid: (nseg - 1) * r_split * H workgroups (the last segment hands no
+// state on), heads fastest, segments in reverse: the K/V read last are the
+// first segments', which the output pass reads first (Infinity Cache).
+// (Ordering the grid by decreasing decay, so that the long pieces of slowly
+// decaying heads start first, measured slower.)
 // Wave u owns state rows 32u..32u+31.
 __global__ __launch_bounds__(NT_LOCAL) __attribute__((amdgpu_waves_per_eu(3, 4)))
 void local_state_kernel(FwdArgs p) {
@@ -901,10 +906,8 @@ void local_state_kernel(FwdArgs p) {
   const int l32 = lane & 31, g = lane >> 5;
   const SeqMap &m = p.m;
   const int H = m.H, R = p.r_split;
-  // Segments (and pieces) in reverse dispatch order: the K/V read last are
-  // the first segments', which the output pass reads first (Infinity Cache).
   const int idx = (int)(blockIdx.x / H), h = blockIdx.x - (blockIdx.x / H) * H;
-  const int s = p.nseg - 1 - idx / R, r = R - 1 - idx % R;
+  const int s = p.nseg - 2 - idx / R, r = R - 1 - idx % R;
   const float l2 = uniform(log2f(p.decay[h]));
   const bool fast = l2 > kFastLog2;
   const int64_t a = (int64_t)s * p.seg_len;

@@ -26,7 +26,7 @@ struct ScanArgs {
   const float *init;
   float *fin;
   float *ws;     // [nseg][r_split][H][d][d]: partial local states in, S_in at slot (s, 0) out
-  int r_split;   // pieces per segment of the local-state pass: 1, 2 or 4
+  int r_split;   // pieces per segment of the local-state pass: 1, 2, 4, 8 or 16
   int C;         // chunk length of the local-state pass
 };
 
@@ -38,7 +38,7 @@ struct SegInfo {
   int hands_on;   // the segment's last sequence continues after it
   int live;       // bit r: piece r of the local-state pass was computed
   float gam;      // lambda^(length of the last piece)
-  float wt[4];    // lambda^(b - x1_r): weight of piece r in L_s
+  float wt[16];   // lambda^(b - x1_r): weight of piece r in L_s
 };
 
 __device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, int s,
@@ -60,7 +60,7 @@ __device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, 
   const int64_t n = (b - ps + p.C - 1) / p.C;
   d.live = 0;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 16; ++r) {
     const int64_t x0 = ps + ((r * n) >> lgR) * p.C;
     const int64_t e1 = ps + (((r + 1) * n) >> lgR) * p.C;
     const int64_t x1 = e1 < b ? e1 : b;
@@ -71,13 +71,16 @@ __device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, 
   return d;
 }
 
+// R = p.r_split, a template parameter so that the partial states of a block
+// of segments load into a register array of fixed size.
+template <int R>
 __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
-  constexpr int MAXS = 256;  // segments described per pass
-  constexpr int BLK = 4;     // segments whose partial states are loaded together
+  constexpr int MAXS = 256;              // segments described per pass
+  constexpr int BLK = R >= 16 ? 1 : R >= 8 ? 2 : 4;  // segments loaded together
+  constexpr int lgR = R == 16 ? 4 : R == 8 ? 3 : R == 4 ? 2 : R == 2 ? 1 : 0;
   __shared__ SegInfo info[MAXS];
   const SeqMap &m = p.m;
-  const int H = m.H, h = blockIdx.x, R = p.r_split;
-  const int lgR = R == 4 ? 2 : R == 2 ? 1 : 0;
+  const int H = m.H, h = blockIdx.x;
   const int64_t DD = (int64_t)p.d * p.d;
   const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
   const bool mine = e < DD;
@@ -96,11 +99,11 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
     for (int s0 = 0; s0 < cnt; s0 += BLK) {
       // Every partial-state load of the block goes out before the
       // (sequential, register-only) carry chain runs through it.
-      f32x4 pr[BLK][4];
+      f32x4 pr[BLK][R];
 #pragma unroll
       for (int i = 0; i < BLK; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < R; ++r) {
           const bool live = s0 + i < cnt && ((info[s0 + i].live >> r) & 1);
           pr[i][r] = live ? *(const f32x4 *)(p.ws +
                                              (((int64_t)(sb + s0 + i) * R + r) * H + h) * DD + e)
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
         *(f32x4 *)(p.ws + ((int64_t)(sb + s0 + i) * R * H + h) * DD + e) = sin;
         f32x4 loc = d.wt[0] * pr[i][0];
 #pragma unroll
-        for (int r = 1; r < 4; ++r) loc += d.wt[r] * pr[i][r];
+        for (int r = 1; r < R; ++r) loc += d.wt[r] * pr[i][r];
         const f32x4 base = d.init_base >= 0 ? init4(d.init_base) : sin;
         // When the segment's last sequence ends at b, the carry is unused:
         // the next segment starts a new sequence.

@@ -74,12 +74,14 @@ constexpr int64_t kFusedSeg = 8192;
 int64_t target_groups(int d, la_dtype dt) { return use_mfma(d, dt) ? 256 : 512; }
 
 // Pieces per segment of the MFMA local-state pass: one small workgroup per
-// 8 or more 64-token chunks, at most 4, so that several workgroups share a
-// CU and hide one another's latency.  The vector-ALU pass uses one.
+// 8 or more 64-token chunks, at most 8, so that several workgroups share a
+// CU and hide one another's latency, and a segment whose every chunk carries
+// weight is not walked by one workgroup with one chunk in flight.  The
+// vector-ALU pass uses one.
 int pieces(int64_t seg, int d, la_dtype dt) {
   if (!use_mfma(d, dt)) return 1;
   const int64_t r = seg / la::mfma::C_LOCAL / 8;
-  return r >= 4 ? 4 : r >= 2 ? 2 : 1;  // a power of two (the scan shifts by it)
+  return r >= 8 ? 8 : r >= 4 ? 4 : r >= 2 ? 2 : 1;  // a power of two (the scan shifts by it)
 }
 
 size_t phased_ws_bytes(const Plan &p, int H, int d) {
@@ -159,11 +161,15 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
                   bool phase_a) {
   dim3 grid((unsigned)(pl.nseg * a.m.H));
   if (use_mfma(d, dt)) {
-    if (phase_a)
-      hipLaunchKernelGGL(la::mfma::local_state_kernel, dim3(grid.x * (unsigned)a.r_split),
-                         dim3(la::mfma::NT_LOCAL), 0, st, a);
-    else
+    if (phase_a) {
+      // The last segment hands no state on: its local state is never needed.
+      if (pl.nseg > 1)
+        hipLaunchKernelGGL(la::mfma::local_state_kernel,
+                           dim3((unsigned)((pl.nseg - 1) * a.r_split * a.m.H)),
+                           dim3(la::mfma::NT_LOCAL), 0, st, a);
+    } else {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, a);
+    }
   } else if (dt == LA_BF16) {
     launch_simt<bf16, 64>(a, pl, st, phase_a);
   } else if (d == 64) {
@@ -187,8 +193,9 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
                        dim3(256), 0, st, words, nwords);
     if (has_empty) {
       la::ScanArgs s{a.m, a.decay, pl.seg, 0, d, a.init, a.fin, a.ws, 1, la::mfma::T};
-      hipLaunchKernelGGL(la::segment_scan_kernel, dim3((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024)),
-                         dim3(256), 0, st, s);
+      hipLaunchKernelGGL(la::segment_scan_kernel<1>,
+                         dim3((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024)), dim3(256), 0,
+                         st, s);
     }
     la::mfma::FusedArgs fa{a, words, words + pl.nseg * H, words + pl.nseg * H + 1};
     hipLaunchKernelGGL(la::mfma::prefill_fused_kernel, dim3((unsigned)(pl.nseg * H)),
@@ -211,7 +218,13 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
     s.r_split = pl.r_split;
     s.C = use_mfma(d, dt) ? la::mfma::C_LOCAL : la::simt::T;
     dim3 grid((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024));
-    hipLaunchKernelGGL(la::segment_scan_kernel, grid, dim3(256), 0, st, s);
+    switch (pl.r_split) {
+      case 16: hipLaunchKernelGGL(la::segment_scan_kernel<16>, grid, dim3(256), 0, st, s); break;
+      case 8: hipLaunchKernelGGL(la::segment_scan_kernel<8>, grid, dim3(256), 0, st, s); break;
+      case 4: hipLaunchKernelGGL(la::segment_scan_kernel<4>, grid, dim3(256), 0, st, s); break;
+      case 2: hipLaunchKernelGGL(la::segment_scan_kernel<2>, grid, dim3(256), 0, st, s); break;
+      default: hipLaunchKernelGGL(la::segment_scan_kernel<1>, grid, dim3(256), 0, st, s); break;
+    }
   }
   if (pl.nseg > 0) {
     if (!pl.scan) a.ws = nullptr;

@@ -112,7 +112,8 @@ def test_vector_alu_paths(d, dtype, N, seg):
                  lam=[0.999, 0.5, 0.9])
 
 
-@pytest.mark.parametrize("dtype,d,seg", [("bf16", 128, 2048), ("fp32", 64, 1024)])
+@pytest.mark.parametrize("dtype,d,seg", [("bf16", 128, 2048), ("bf16", 128, 4096),
+                                         ("fp32", 64, 1024)])
 def test_local_state_zero_weight_chunks(dtype, d, seg, prefill_path):
     """Local-state passes skip leading chunks whose decay weights are below
     2^-160 (exactly zero in float32).  The decays put that cut inside the
@@ -179,6 +180,13 @@ def run_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True):
 @pytest.mark.parametrize("seg", [0, 128, 200, 100000])
 def test_varlen_bf16(seg, prefill_path):
     run_varlen_case([300, 0, 1, 129, 1024, 5, 0, 640, 2000], 4, 128, "bf16", seed=70, seg=seg)
+
+
+def test_varlen_eight_pieces(prefill_path):
+    """4096-token segments: the local-state pass splits each segment's last
+    piece into 8 parts whose weighted sum the scan forms; the sequences cross
+    the segment cuts, so every part's weight reaches an entering state."""
+    run_varlen_case([5000, 0, 3000, 7000, 100, 4500], 3, 128, "bf16", seed=72, seg=4096)
 
 
 @pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])

@@ -55,8 +55,9 @@ def source_hash():
 
 
 def measured_traffic(workload):
-    """HBM bytes per step from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    """HBM bytes from the committed rocprofv3 counter summary (scaled FETCH_SIZE
+    + WRITE_SIZE), if it was taken on the current kernel sources; else None.
+    Returns {"step": bytes per step, kernel name: bytes per launch, ...}."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     try:
         with open(path) as f:
@@ -65,7 +66,9 @@ def measured_traffic(workload):
         return None
     if rec.get("source_hash") != source_hash():
         return None
-    return rec.get("bytes_per_step")
+    out = dict(rec.get("kernels", {}))
+    out["step"] = rec.get("bytes_per_step")
+    return out
 
 
 def time_steps(fn, steps, warmup, stream):
@@ -83,7 +86,15 @@ def time_steps(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per step
 
 
-def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup):
+def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup, phases=False):
+    """ms per step over `steps` timed steps after `warmup`.  With phases, also
+    the average ms of each of the library's three phases (local-state pass,
+    segment scan, output pass), from HIP events the library records between
+    its launches on the same stream, on every fifth timed step (the last one
+    if there are fewer than five).  Recording events between launches leaves
+    short gaps in which the clock recovers; sampling a few steps keeps the
+    sampled kernels in the same sustained state as the rest and the step time
+    nearly undisturbed (the step time includes those few gaps)."""
     import torch
     dev = torch.device("cuda:0")
     q, k, v = inputs.device_qkv((B, H, N, d), seed, "bf16", device=dev)
@@ -93,13 +104,31 @@ def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup):
     nws = la.lightning_attn_fwd_workspace_size(B, H, N, d, block)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    sampled = [i for i in range(steps) if (i + 1) % 5 == 0] or [steps - 1]
+    evs = {}
+    if phases:
+        for i in sampled:
+            evs[i] = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            for e in evs[i]:
+                e.record(stream)  # creates the event, so that its handle exists
+    calls = [0]
 
     def step():
-        la.lightning_attn_fwd(q, k, v, decay, block=block, out=out, final_state=fin,
-                              workspace=ws)
+        i = calls[0] - warmup
+        calls[0] += 1
+        if i in evs:
+            la.lightning_attn_fwd_timed(q, k, v, decay, [e.cuda_event for e in evs[i]],
+                                        block=block, out=out, final_state=fin, workspace=ws)
+        else:
+            la.lightning_attn_fwd(q, k, v, decay, block=block, out=out, final_state=fin,
+                                  workspace=ws)
 
     ms = time_steps(step, steps, warmup, stream)
-    return ms, (q, k, v, decay, out, fin)
+    phase_ms = None
+    if phases:
+        phase_ms = [sum(row[j].elapsed_time(row[j + 1]) for row in evs.values()) / len(evs)
+                    for j in range(3)]
+    return ms, phase_ms, (q, k, v, decay, out, fin)
 
 
 def bench_varlen(la, inputs, steps, warmup):
@@ -132,7 +161,7 @@ def bench_varlen(la, inputs, steps, warmup):
 def bench_million(la, inputs, steps, warmup):
     w = inputs.WORKLOADS["million_h8"]
     B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
-    ms, _ = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], steps, warmup)
+    ms, _, _ = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], steps, warmup)
     byt = prefill_bytes(B, H, N, d)
     return {"workload": "million_h8", "B": B, "H": H, "N": N, "block": block,
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
@@ -223,13 +252,19 @@ def main():
     la.load_library()
     w = inputs.WORKLOADS["layer_h64_n32k"]
     B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
-    ms, tensors = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], args.steps, args.warmup)
+    ms, phase_ms, tensors = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], args.steps,
+                                          args.warmup, phases=True)
     sec = ms * 1e-3
     flops = prefill_flops(B, H, N, d, block)
     tflops = flops / sec / 1e12
     alg = prefill_bytes(B, H, N, d)
     gbs = alg / sec / 1e9
-    traffic = measured_traffic("layer_h64_n32k")
+    traffic = measured_traffic("layer_h64_n32k") or {}
+    # The dominant kernel is the output pass (prefill_chunk_kernel): it reads
+    # q, k, v and writes out and the final states, i.e. the path's algorithmic
+    # bytes, once per launch.
+    chunk_s = phase_ms[2] * 1e-3
+    chunk_gbs = alg / chunk_s / 1e9
     res = {
         "metric": METRIC,
         "value": round(B * N / sec, 1),
@@ -247,11 +282,20 @@ def main():
                    "block": block, "state": "fp32"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": "whole prefill step (local-state, segment-scan and chunk "
-                               "kernels), algorithmic bytes %d per step" % alg},
+        "roofline": {"bound": "hbm", "achieved": round(chunk_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(chunk_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic.get("prefill_chunk_kernel"),
+                     "kernel": "la::mfma::prefill_chunk_kernel",
+                     "launch_us": round(phase_ms[2] * 1e3, 1),
+                     "algorithmic_bytes_per_launch": alg},
+        "phases_us": {"sampled_steps": max(1, args.steps // 5),
+                      "local_state_kernel": round(phase_ms[0] * 1e3, 1),
+                      "segment_scan_kernel": round(phase_ms[1] * 1e3, 1),
+                      "prefill_chunk_kernel": round(phase_ms[2] * 1e3, 1)},
+        "step_hbm": {"achieved": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic.get("step"), "unit": "GB/s",
+                     "note": "algorithmic bytes per step / step time; traffic = counter "
+                             "bytes of all three kernels per step"},
     }
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20

@@ -114,6 +114,31 @@ la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const 
                              void *hip_stream);
 
 /*
+ * lightning_attn_fwd with per-kernel timing (a measurement aid; the same
+ * computation as lightning_attn_fwd, for which phase_events == NULL).
+ *
+ *   phase_events : NULL, or an array of 4 hipEvent_t handles owned by the
+ *                  caller (created on the stream's device; timing-enabled if
+ *                  durations are wanted).  They are recorded on hip_stream:
+ *                  [0] before the first launch of the call, [1] after the
+ *                  segment local-state pass, [2] after the segment scan,
+ *                  [3] after the output pass.  A phase the plan does not run
+ *                  (no scan for single-segment sequences; the single-pass
+ *                  kernel does all three) records its event at the same point
+ *                  as the one before it.
+ *
+ * A call that launches nothing (B*H == 0, or N == 0 without final_state)
+ * records no event.  Returns LA_ERR_HIP if recording an event fails (after
+ * launching the work); otherwise as lightning_attn_fwd.
+ */
+la_status lightning_attn_fwd_timed(const void *q, const void *k, const void *v,
+                                   const float *decay, int B, int H, int64_t N, int d, int block,
+                                   la_dtype dt, const float *init_state, void *out,
+                                   float *final_state, int64_t segment_tokens, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream,
+                                   void *const *phase_events);
+
+/*
  * Prefill over packed variable-length sequences ("data packing", MiniMax-01
  * report section 3.2; varlen support for LASP+, section 3.2.2).  Sequence j
  * occupies tokens cu_seqlens[j] .. cu_seqlens[j+1]-1 of every head; the state

@@ -9,13 +9,15 @@ every call raises.
 
 Entry points (same names as the C ABI):
   lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, ...) -> (out, final_state)
+  lightning_attn_fwd_timed(q, k, v, decay, phase_events, ...) -> (out, final_state)
   lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, ...) -> (out, final_states)
   lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
 """
 import ctypes
 import os
 
-__all__ = ["lightning_attn_fwd", "lightning_attn_fwd_varlen", "lightning_attn_decode",
+__all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd_varlen",
+           "lightning_attn_decode",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
 
@@ -59,6 +61,9 @@ def load_library(path=None):
     lib.lightning_attn_fwd_workspace_size.restype = Z
     lib.lightning_attn_fwd.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P]
     lib.lightning_attn_fwd.restype = I
+    lib.lightning_attn_fwd_timed.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P,
+                                             ctypes.POINTER(P)]
+    lib.lightning_attn_fwd_timed.restype = I
     lib.lightning_attn_fwd_varlen_workspace_size.argtypes = [I, I, L, I, I, I, L]
     lib.lightning_attn_fwd_varlen_workspace_size.restype = Z
     lib.lightning_attn_fwd_varlen.argtypes = [P, P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P]
@@ -120,6 +125,25 @@ def lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, segment_token
     """Causal decayed linear attention over q, k, v [B, H, N, d] (bf16 or
     float32, contiguous, on one GPU).  decay: [H] float32.  Returns
     (out [B, H, N, d] in the input dtype, final_state [B, H, d, d] float32)."""
+    return _fwd(q, k, v, decay, block, init_state, segment_tokens, out, final_state, workspace,
+                None)
+
+
+def lightning_attn_fwd_timed(q, k, v, decay, phase_events, block=128, init_state=None,
+                             segment_tokens=0, out=None, final_state=None, workspace=None):
+    """lightning_attn_fwd that also records 4 caller-owned HIP events on the
+    current stream: before the first launch, after the local-state pass,
+    after the segment scan and after the output pass.  phase_events: 4 raw
+    hipEvent_t handles (for example torch.cuda.Event(...).cuda_event of
+    events recorded once beforehand, so that the handles exist)."""
+    if len(phase_events) != 4 or not all(phase_events):
+        raise ValueError("phase_events must hold 4 created hipEvent_t handles")
+    return _fwd(q, k, v, decay, block, init_state, segment_tokens, out, final_state, workspace,
+                phase_events)
+
+
+def _fwd(q, k, v, decay, block, init_state, segment_tokens, out, final_state, workspace,
+         phase_events):
     torch = _torch()
     lib = load_library()
     B, H, N, d = q.shape
@@ -141,11 +165,17 @@ def lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, segment_token
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.lightning_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), B, H, N, d, block, dt,
-                                _ptr(init_state), _ptr(out), _ptr(final_state), segment_tokens,
-                                _ptr(workspace), ws_have, _stream(dev))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(decay), B, H, N, d, block, dt, _ptr(init_state),
+            _ptr(out), _ptr(final_state), segment_tokens, _ptr(workspace), ws_have, _stream(dev))
+    if phase_events is None:
+        st = lib.lightning_attn_fwd(*args)
+        name = "lightning_attn_fwd"
+    else:
+        ev = (ctypes.c_void_p * 4)(*[int(e) for e in phase_events])
+        st = lib.lightning_attn_fwd_timed(*args, ev)
+        name = "lightning_attn_fwd_timed"
     if st != 0:
-        raise LightningAttnError(st, "lightning_attn_fwd")
+        raise LightningAttnError(st, name)
     return out, final_state
 
 

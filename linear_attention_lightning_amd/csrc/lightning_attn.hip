@@ -180,11 +180,29 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
 }
 
 // Runs the whole prefill for a planned problem (fixed or packed).
+// Records phase event i on st when the caller supplied events (a timing
+// diagnostic); remembers a failure for the call's status.
+struct PhaseEvents {
+  void *const *ev;
+  hipStream_t st;
+  bool failed = false;
+  void mark(int i) {
+    if (!ev) return;
+    const hipError_t e = hipEventRecord((hipEvent_t)ev[i], st);
+    if (e != hipSuccess) {
+      failed = true;
+      g_last_hip_error = e;
+    }
+  }
+};
+
 la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, bool has_empty,
-                  hipStream_t st) {
+                  hipStream_t st, void *const *events = nullptr) {
   la::FwdArgs a = base;
   const int H = a.m.H;
   a.r_split = pl.r_split;
+  PhaseEvents pe{events, st};
+  pe.mark(0);
   if (pl.fused && pl.nseg > 0) {
     // flags, ticket and error word live right after the end-state records
     unsigned *words = (unsigned *)((char *)a.ws + state_bytes(pl.nseg * H, d));
@@ -197,14 +215,19 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
                          dim3((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024)), dim3(256), 0,
                          st, s);
     }
+    pe.mark(1);
+    pe.mark(2);
     la::mfma::FusedArgs fa{a, words, words + pl.nseg * H, words + pl.nseg * H + 1};
     hipLaunchKernelGGL(la::mfma::prefill_fused_kernel, dim3((unsigned)(pl.nseg * H)),
                        dim3(la::mfma::NT), 0, st, fa);
-    return launch_status();
+    pe.mark(3);
+    const la_status ls = launch_status();
+    return ls != LA_OK ? ls : pe.failed ? LA_ERR_HIP : LA_OK;
   }
   if (pl.scan && pl.nseg > 0) {
     launch_phase(a, pl, d, dt, st, /*phase_a=*/true);
   }
+  pe.mark(1);
   if (pl.scan || has_empty) {
     la::ScanArgs s;
     s.m = a.m;
@@ -226,11 +249,14 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
       default: hipLaunchKernelGGL(la::segment_scan_kernel<1>, grid, dim3(256), 0, st, s); break;
     }
   }
+  pe.mark(2);
   if (pl.nseg > 0) {
     if (!pl.scan) a.ws = nullptr;
     launch_phase(a, pl, d, dt, st, /*phase_a=*/false);
   }
-  return launch_status();
+  pe.mark(3);
+  const la_status ls = launch_status();
+  return ls != LA_OK ? ls : pe.failed ? LA_ERR_HIP : LA_OK;
 }
 
 la_status check_common(int H, int d, int block, la_dtype dt, int64_t segment_tokens) {
@@ -272,6 +298,17 @@ la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const 
                              const float *init_state, void *out, float *final_state,
                              int64_t segment_tokens, void *workspace, size_t workspace_bytes,
                              void *hip_stream) {
+  return lightning_attn_fwd_timed(q, k, v, decay, B, H, N, d, block, dt, init_state, out,
+                                  final_state, segment_tokens, workspace, workspace_bytes,
+                                  hip_stream, nullptr);
+}
+
+la_status lightning_attn_fwd_timed(const void *q, const void *k, const void *v,
+                                   const float *decay, int B, int H, int64_t N, int d, int block,
+                                   la_dtype dt, const float *init_state, void *out,
+                                   float *final_state, int64_t segment_tokens, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream,
+                                   void *const *phase_events) {
   if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
   la_status st = check_common(H, d, block, dt, segment_tokens);
   if (st != LA_OK) return st;
@@ -302,7 +339,7 @@ la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const 
   a.init = init_state;
   a.fin = final_state;
   a.ws = (float *)workspace;
-  return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream);
+  return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream, phase_events);
 }
 
 size_t lightning_attn_fwd_varlen_workspace_size(int num_seqs, int H, int64_t total_N, int d,

@@ -207,10 +207,17 @@ __device__ __forceinline__ void write_st(char *STs, const f32x16 (&S)[4], int u,
 // this wave's state rows 32u..32u+31: wgt_c = lambda^(e0 - c) for chunk rows
 // c < L, else 0.
 // tail8[s] = lambda^(7 - s) (fast path only).
-template <int NKS = T / 16, bool PIPE = true>
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// hook(ks) runs at the start of step ks (PIPE path): the chunk loop issues
+// the next chunk's tile loads there, spread over the update.
+template <int NKS = T / 16, bool PIPE = true, typename Hook = NoHook>
 __device__ __forceinline__ void state_update(f32x16 (&S)[4], const char *Ks, const char *Vs,
                                              int L, int e0, float l2, bool fast,
-                                             const float (&tail8)[8], int u, int lane) {
+                                             const float (&tail8)[8], int u, int lane,
+                                             const Hook &hook = Hook()) {
   const int g = lane >> 5, G16 = lane >> 4, i16 = lane & 15;
   // Rows 16 ks + 8 g + (0..3, 4..7): K columns 32u.., V columns 32 nt..
   const int ko0 = tr_off(8 * g, u, G16, i16), ko1 = tr_off(8 * g + 4, u, G16, i16);
@@ -250,6 +257,7 @@ __device__ __forceinline__ void state_update(f32x16 (&S)[4], const char *Ks, con
     for (int ks = 0; ks < NKS; ++ks) {
       const int sl = ks & 1;
       if (ks + 1 < NKS) fetch(ks + 1, sl ^ 1);
+      hook(ks);
       const int c0 = 16 * ks + 8 * g;
       float wv[8];
       if (fast) {
@@ -430,18 +438,22 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, const char *lds) {
 // i % 16, so it reads logical granule (i % 16) ^ kv_swz(row).  Rows past the
 // chunk's end repeat its last row (finite values that every consumer masks).
 // Eight memory instructions per call.
-__device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const FwdArgs &p, int h,
-                                              const Cursor &c, int u, int lane) {
+// Instruction k (0..7) of the above: rows 32u + 4k .. 32u + 4k + 3.
+__device__ __forceinline__ void dma_tile_quad(char *tile, const void *src, const FwdArgs &p, int h,
+                                              const Cursor &c, int u, int lane, int k) {
   const int Lc = (int)(c.c1 - c.c0);
   const bf16 *base = (const bf16 *)src + p.m.row_base(h, c.j) + c.c0 * D;
   const int sub = lane >> 4, pg = lane & 15;
+  const int r = 32 * u + 4 * k + sub;
+  const int rr = r < Lc ? r : Lc - 1;
+  const bf16 *gp = base + (int64_t)rr * D + ((pg ^ kv_swz(r)) << 3);
+  lds_dma16(gp, tile + (32 * u + 4 * k) * KV_ROW);
+}
+
+__device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const FwdArgs &p, int h,
+                                              const Cursor &c, int u, int lane) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int r = 32 * u + 4 * k + sub;
-    const int rr = r < Lc ? r : Lc - 1;
-    const bf16 *gp = base + (int64_t)rr * D + ((pg ^ kv_swz(r)) << 3);
-    lds_dma16(gp, tile + (32 * u + 4 * k) * KV_ROW);
-  }
+  for (int k = 0; k < 8; ++k) dma_tile_quad(tile, src, p, h, c, u, lane, k);
 }
 
 // Writes this output wave's 32 staged rows of chunk c as whole rows: per
@@ -473,14 +485,13 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 
 // LDS use of the chunk loop.  Chunk n of the walk uses buffer n % 2 (its K
 // tile, then its V tile); S^T follows the two buffers.  The tiles arrive by
-// direct loads: chunk n + 1's K tile from the output waves right after the
-// barrier that opens chunk n (that buffer's staged output rows of chunk n - 1
-// have been written back by then), chunk n + 2's V tile from the state waves
-// right after the barrier that closes chunk n (when that buffer's V tile is
-// free).  Every tile has a good part of a chunk period to arrive and no
-// single burst of loads outgrows what the CU keeps in flight.  After chunk n
-// closes, its K tile holds the output waves' staged output rows until they
-// are written back.
+// direct loads from the state waves: chunk n + 1's K and V tiles go into the
+// other buffer during chunk n's state update, one instruction of each per
+// update step (by then that buffer's V tile has been read and its K tile's
+// staged output rows of chunk n - 1 written back), so the loads stream in
+// evenly through the busiest part of the chunk instead of in one burst that
+// backs up the CU's memory queue.  After chunk n closes, its K tile holds
+// the output waves' staged output rows until they are written back.
 //
 // Per chunk, two barriers shared by both roles:
 //   A (opens the chunk): its K/V tiles and the S^T of the state entering it
@@ -488,7 +499,7 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 //     state waves: the state update.
 //   B (closes it): every read of its K/V tiles and of S^T is done.  Output
 //     waves: stage and write back the outputs; state waves: publish the next
-//     S^T and start the V tile after next.
+//     S^T and wait for the next chunk's tiles.
 // The inter-block term thus overlaps the state update instead of waiting
 // for it, and both heavy phases sit between A and B.
 //
@@ -626,44 +637,50 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
   const int w = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane;
   const float l2 = dc.l2;
   int buf = 0;
-  Cursor nxt = next_chunk(m, cur, b, T);
   dma_tile_rows(smem, p.k, p, h, cur, w, lane);
   dma_tile_rows(smem + LDS_K, p.v, p, h, cur, w, lane);
-  if (nxt.valid) dma_tile_rows(smem + LDS_KV + LDS_K, p.v, p, h, nxt, w, lane);
   write_st(STs, S, w, l32, g);
-  if (nxt.valid) vm_wait<8>();
-  else vm_wait<0>();
+  vm_wait<0>();
 
   while (true) {
+    const Cursor nxt = next_chunk(m, cur, b, T);
     const int L = (int)(cur.c1 - cur.c0);
     char *Ks = smem + buf * LDS_KV, *Vs = Ks + LDS_K;
+    char *Kn = smem + (buf ^ 1) * LDS_KV, *Vn = Kn + LDS_K;
     __syncthreads();  // A: this chunk's K/V and entering S^T are in LDS
-    // The next chunk's K tile goes into the other buffer, whose staged output
-    // rows were written back before A.
-    if (nxt.valid) dma_tile_rows(smem + (buf ^ 1) * LDS_KV, p.k, p, h, nxt, w, lane);
+    // The next chunk's tiles, one K and one V instruction per update step.
+    // (The lane id passes through an empty asm statement at each step, so
+    // the per-lane address arithmetic is redone there instead of sixteen
+    // addresses being hoisted out of the update and held in registers.)
+    const auto issue_next = [&](int k) {
+      if (nxt.valid) {
+        int ll = lane;
+        asm volatile("" : "+v"(ll));
+        dma_tile_quad(Kn, p.k, p, h, nxt, w, ll, k);
+        dma_tile_quad(Vn, p.v, p, h, nxt, w, ll, k);
+      }
+    };
     const bool seq_done = (cur.c1 == cur.seq_end);
     const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
     if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
       const float gL = fast_exp2((float)L * l2);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) S[nt] *= gL;
-      state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane);
+      state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane, issue_next);
       if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) issue_next(k);
     }
     __syncthreads();  // B: this chunk's K/V and S^T reads are done
     if (!nxt.valid) break;
+    // (A new piece's state load sits in the same block as the S^T write that
+    // consumes it, so no path reaches the next chunk with those loads open.)
     if (new_piece)
       load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, w, l32, g);
     write_st(STs, S, w, l32, g);
-    const Cursor nxt2 = next_chunk(m, nxt, b, T);
-    if (nxt2.valid) {
-      dma_tile_rows(Vs, p.v, p, h, nxt2, w, lane);
-      vm_wait<8>();  // the next chunk's K and V tiles have landed (only these 8 may be open)
-    } else {
-      vm_wait<0>();
-    }
+    vm_wait<0>();  // the next chunk's tiles have landed
     cur = nxt;
-    nxt = nxt2;
     buf ^= 1;
   }
 }

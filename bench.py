@@ -131,6 +131,33 @@ def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup, phases=Fal
     return ms, phase_ms, (q, k, v, decay, out, fin)
 
 
+def bench_token_major(la, inputs, steps, warmup):
+    """The headline workload with q, k, v, out in [B, N, H, d] layout (a
+    projection's output, read in place through a row stride)."""
+    import torch
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["layer_h64_n32k"]
+    B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
+    q, k, v = (t.transpose(1, 2).contiguous()
+               for t in inputs.device_qkv((B, H, N, d), w["seed"], "bf16", device=dev))
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    out = torch.empty_like(q)
+    fin = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    nws = la.lightning_attn_fwd_workspace_size(B, H, N, d, block)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        la.lightning_attn_fwd_layout(q, k, v, decay, la.LA_TOKEN_MAJOR, block=block, out=out,
+                                     final_state=fin, workspace=ws)
+
+    ms = time_steps(step, steps, warmup, torch.cuda.current_stream(dev))
+    byt = prefill_bytes(B, H, N, d)
+    return {"workload": "layer_h64_n32k", "layout": "token-major [B, N, H, d]",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+            "hbm_gbs_algorithmic": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def bench_varlen(la, inputs, steps, warmup):
     import torch
     dev = torch.device("cuda:0")
@@ -231,7 +258,12 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # After start-up the GPU's clocks go through a transient of a few tens of
+    # milliseconds of back-to-back work (the chunk kernel measured 400 us in
+    # its first launches, up to 470 us a few steps later, and a steady 407-412
+    # us from about the 30th step on); the default warm-up covers it, so the
+    # timed steps measure the settled state.
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64)
@@ -316,6 +348,8 @@ def main():
         res["varlen"] = bench_varlen(la, inputs, steps=max(5, args.steps // 2), warmup=2)
         torch.cuda.empty_cache()
         res["million"] = bench_million(la, inputs, steps=5, warmup=1)
+        torch.cuda.empty_cache()
+        res["token_major"] = bench_token_major(la, inputs, steps=args.steps, warmup=args.warmup)
     print(json.dumps(res), flush=True)
 
 

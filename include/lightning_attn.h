@@ -67,6 +67,18 @@ typedef enum {
 
 typedef enum { LA_FP32 = 0, LA_BF16 = 1 } la_dtype;
 
+/* Memory layout of q, k, v and out for the *_layout entry points (the other
+ * prefill entry points take LA_HEAD_MAJOR).  LA_TOKEN_MAJOR is the layout a
+ * projection produces ([B][N][H*d], heads side by side in each token row),
+ * read and written as it is: the kernels address every token row through a
+ * row stride, so no layout pass runs in front of or behind the attention
+ * (MiniMax-01 report, section 3.3.1: the prefill front-end's layout
+ * adjustment is folded into the kernels that read Q, K and V). */
+typedef enum {
+  LA_HEAD_MAJOR = 0,  /* fixed: [B][H][N][d];  packed: [H][total_N][d] */
+  LA_TOKEN_MAJOR = 1  /* fixed: [B][N][H][d];  packed: [total_N][H][d] */
+} la_layout;
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *lightning_attn_status_string(la_status s);
 
@@ -139,6 +151,23 @@ la_status lightning_attn_fwd_timed(const void *q, const void *k, const void *v,
                                    void *const *phase_events);
 
 /*
+ * lightning_attn_fwd for either memory layout (la_layout): q, k, v and out
+ * are [B][H][N][d] for LA_HEAD_MAJOR (exactly lightning_attn_fwd) or
+ * [B][N][H][d] for LA_TOKEN_MAJOR, each row of d elements contiguous.
+ * init_state / final_state keep the [B][H][d][d] layout.  The workspace size
+ * does not depend on the layout.
+ *
+ * Returns LA_ERR_UNSUPPORTED for an unknown layout, or for LA_TOKEN_MAJOR
+ * when 128 token rows span 2^31 bytes or more (H * d >= 4194304); otherwise
+ * as lightning_attn_fwd.
+ */
+la_status lightning_attn_fwd_layout(const void *q, const void *k, const void *v,
+                                    const float *decay, int B, int H, int64_t N, int d, int block,
+                                    la_dtype dt, la_layout layout, const float *init_state,
+                                    void *out, float *final_state, int64_t segment_tokens,
+                                    void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * Prefill over packed variable-length sequences ("data packing", MiniMax-01
  * report section 3.2; varlen support for LASP+, section 3.2.2).  Sequence j
  * occupies tokens cu_seqlens[j] .. cu_seqlens[j+1]-1 of every head; the state
@@ -163,6 +192,20 @@ la_status lightning_attn_fwd_varlen(const void *q, const void *k, const void *v,
                                     const float *init_states, void *out, float *final_states,
                                     int64_t segment_tokens, void *workspace,
                                     size_t workspace_bytes, void *hip_stream);
+
+/*
+ * lightning_attn_fwd_varlen for either memory layout: q, k, v and out are
+ * [H][total_N][d] for LA_HEAD_MAJOR (exactly lightning_attn_fwd_varlen) or
+ * [total_N][H][d] for LA_TOKEN_MAJOR.  Errors as lightning_attn_fwd_layout.
+ */
+la_status lightning_attn_fwd_varlen_layout(const void *q, const void *k, const void *v,
+                                           const float *decay, const int32_t *cu_seqlens,
+                                           int num_seqs, int H, int64_t total_N, int d, int block,
+                                           la_dtype dt, la_layout layout,
+                                           const float *init_states, void *out,
+                                           float *final_states, int64_t segment_tokens,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *hip_stream);
 
 /*
  * One recurrent decode step (MiniMax-01 report, section 2.2.4, eq. 12;

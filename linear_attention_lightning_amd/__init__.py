@@ -10,20 +10,24 @@ every call raises.
 Entry points (same names as the C ABI):
   lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, ...) -> (out, final_state)
   lightning_attn_fwd_timed(q, k, v, decay, phase_events, ...) -> (out, final_state)
+  lightning_attn_fwd_layout(q, k, v, decay, layout, ...) -> (out, final_state)
+  lightning_attn_fwd_varlen_layout(q, k, v, decay, cu_seqlens, layout, ...) -> (out, final_states)
   lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, ...) -> (out, final_states)
   lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
 """
 import ctypes
 import os
 
-__all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd_varlen",
-           "lightning_attn_decode",
+__all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd_layout",
+           "lightning_attn_fwd_varlen", "lightning_attn_fwd_varlen_layout", "lightning_attn_decode",
+           "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightning_attn.so")
 
 LA_FP32, LA_BF16 = 0, 1
+LA_HEAD_MAJOR, LA_TOKEN_MAJOR = 0, 1  # la_layout
 _STATUS = {0: "LA_OK", 1: "LA_ERR_INVALID_ARG", 2: "LA_ERR_UNSUPPORTED", 3: "LA_ERR_WORKSPACE",
            4: "LA_ERR_HIP"}
 
@@ -64,6 +68,11 @@ def load_library(path=None):
     lib.lightning_attn_fwd_timed.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P,
                                              ctypes.POINTER(P)]
     lib.lightning_attn_fwd_timed.restype = I
+    lib.lightning_attn_fwd_layout.argtypes = [P, P, P, P, I, I, L, I, I, I, I, P, P, P, L, P, Z, P]
+    lib.lightning_attn_fwd_layout.restype = I
+    lib.lightning_attn_fwd_varlen_layout.argtypes = [P, P, P, P, P, I, I, L, I, I, I, I, P, P, P,
+                                                     L, P, Z, P]
+    lib.lightning_attn_fwd_varlen_layout.restype = I
     lib.lightning_attn_fwd_varlen_workspace_size.argtypes = [I, I, L, I, I, I, L]
     lib.lightning_attn_fwd_varlen_workspace_size.restype = Z
     lib.lightning_attn_fwd_varlen.argtypes = [P, P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P]
@@ -129,6 +138,16 @@ def lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, segment_token
                 None)
 
 
+def lightning_attn_fwd_layout(q, k, v, decay, layout, block=128, init_state=None,
+                              segment_tokens=0, out=None, final_state=None, workspace=None):
+    """lightning_attn_fwd for either layout: q, k, v [B, H, N, d] for
+    LA_HEAD_MAJOR, [B, N, H, d] for LA_TOKEN_MAJOR (a projection's output
+    viewed per head, read in place).  out has q's layout; final_state is
+    [B, H, d, d] float32 either way."""
+    return _fwd(q, k, v, decay, block, init_state, segment_tokens, out, final_state, workspace,
+                None, layout)
+
+
 def lightning_attn_fwd_timed(q, k, v, decay, phase_events, block=128, init_state=None,
                              segment_tokens=0, out=None, final_state=None, workspace=None):
     """lightning_attn_fwd that also records 4 caller-owned HIP events on the
@@ -143,10 +162,15 @@ def lightning_attn_fwd_timed(q, k, v, decay, phase_events, block=128, init_state
 
 
 def _fwd(q, k, v, decay, block, init_state, segment_tokens, out, final_state, workspace,
-         phase_events):
+         phase_events, layout=None):
     torch = _torch()
     lib = load_library()
-    B, H, N, d = q.shape
+    if layout == LA_TOKEN_MAJOR:
+        B, N, H, d = q.shape
+    elif layout in (None, LA_HEAD_MAJOR):
+        B, H, N, d = q.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
     dev = q.device
     _check(k, "k", q.shape, q.dtype, dev)
     _check(v, "v", q.shape, q.dtype, dev)
@@ -167,7 +191,10 @@ def _fwd(q, k, v, decay, block, init_state, segment_tokens, out, final_state, wo
     ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(decay), B, H, N, d, block, dt, _ptr(init_state),
             _ptr(out), _ptr(final_state), segment_tokens, _ptr(workspace), ws_have, _stream(dev))
-    if phase_events is None:
+    if layout is not None:
+        st = lib.lightning_attn_fwd_layout(*args[:10], layout, *args[10:])
+        name = "lightning_attn_fwd_layout"
+    elif phase_events is None:
         st = lib.lightning_attn_fwd(*args)
         name = "lightning_attn_fwd"
     else:
@@ -184,9 +211,29 @@ def lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, init_states
     """Packed variable-length form: q, k, v [H, total, d]; cu_seqlens int32
     [num_seqs + 1] on the same device (0 first, total last, non-decreasing).
     Returns (out [H, total, d], final_states [num_seqs, H, d, d] float32)."""
+    return _fwd_varlen(q, k, v, decay, cu_seqlens, block, init_states, segment_tokens, out,
+                       final_states, workspace, None)
+
+
+def lightning_attn_fwd_varlen_layout(q, k, v, decay, cu_seqlens, layout, block=128,
+                                     init_states=None, segment_tokens=0, out=None,
+                                     final_states=None, workspace=None):
+    """lightning_attn_fwd_varlen for either layout: q, k, v [H, total, d] for
+    LA_HEAD_MAJOR, [total, H, d] for LA_TOKEN_MAJOR."""
+    return _fwd_varlen(q, k, v, decay, cu_seqlens, block, init_states, segment_tokens, out,
+                       final_states, workspace, layout)
+
+
+def _fwd_varlen(q, k, v, decay, cu_seqlens, block, init_states, segment_tokens, out,
+                final_states, workspace, layout):
     torch = _torch()
     lib = load_library()
-    H, total, d = q.shape
+    if layout == LA_TOKEN_MAJOR:
+        total, H, d = q.shape
+    elif layout in (None, LA_HEAD_MAJOR):
+        H, total, d = q.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
     dev = q.device
     _check(k, "k", q.shape, q.dtype, dev)
     _check(v, "v", q.shape, q.dtype, dev)
@@ -210,12 +257,17 @@ def lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, init_states
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.lightning_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(cu_seqlens),
-                                       S, H, total, d, block, dt, _ptr(init_states), _ptr(out),
-                                       _ptr(final_states), segment_tokens, _ptr(workspace),
-                                       ws_have, _stream(dev))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(cu_seqlens), S, H, total, d, block, dt)
+    tail = (_ptr(init_states), _ptr(out), _ptr(final_states), segment_tokens, _ptr(workspace),
+            ws_have, _stream(dev))
+    if layout is None:
+        st = lib.lightning_attn_fwd_varlen(*head, *tail)
+        name = "lightning_attn_fwd_varlen"
+    else:
+        st = lib.lightning_attn_fwd_varlen_layout(*head, layout, *tail)
+        name = "lightning_attn_fwd_varlen_layout"
     if st != 0:
-        raise LightningAttnError(st, "lightning_attn_fwd_varlen")
+        raise LightningAttnError(st, name)
     return out, final_states
 
 

@@ -54,6 +54,8 @@ struct SeqMap {
   int64_t total;  // tokens per head
   int64_t head_stride;
   int64_t seq_extra;
+  int64_t rs;  // elements between consecutive tokens of one head: d (head-major
+               // layouts) or H*d (token-major layouts)
 
   __device__ __forceinline__ int64_t start(int j) const {
     return cu ? (int64_t)cu[j] : (int64_t)j * N;

@@ -131,20 +131,20 @@ __device__ __forceinline__ bf16x8 cvt8(const float (&v)[8]) {
   return r;
 }
 
-// Global -> registers: a 128 x 128 bf16 tile starting at src, of which rows
-// [0, L) are valid (L >= 1), moved by `nthr` threads (thread t of them moves
-// 16 bytes of row (it * nthr + t) / 16).  Rows >= L repeat row L - 1: every
+// Global -> registers: a 128 x 128 bf16 tile whose row i starts at
+// src + i * rs, of which rows [0, L) are valid (L >= 1), moved by `nthr`
+// threads (thread t of them moves 16 bytes of row (it * nthr + t) / 16).  Rows >= L repeat row L - 1: every
 // consumer masks those rows out or multiplies them by exact zeros, so any
 // finite values do, and the loads need no branches (a branch around a load
 // makes the compiler's memory-wait analysis far more conservative).
 template <int NTHR, int ROWS = T>
-__device__ __forceinline__ void load_tile(u32x4 (&r)[ROWS * 16 / NTHR], const bf16 *src, int L,
-                                          int t) {
+__device__ __forceinline__ void load_tile(u32x4 (&r)[ROWS * 16 / NTHR], const bf16 *src,
+                                          int64_t rs, int L, int t) {
 #pragma unroll
   for (int it = 0; it < ROWS * 16 / NTHR; ++it) {
     const int id = it * NTHR + t, row = id >> 4, c16 = id & 15;
     const int rr = row < L ? row : L - 1;
-    r[it] = *(const u32x4 *)(src + (int64_t)rr * D + c16 * 8);
+    r[it] = *(const u32x4 *)(src + (int64_t)rr * rs + c16 * 8);
   }
 }
 
@@ -394,7 +394,7 @@ __device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cur
   const int Lc = (int)(c.c1 - c.c0);
   const int row = 16 * o.qblock(bi) + o.i16;
   const bf16 *qrow = (const bf16 *)p.q + p.m.row_base(h, c.j) +
-                     (c.c0 + (row < Lc ? row : Lc - 1)) * D + 8 * o.G;
+                     (c.c0 + (row < Lc ? row : Lc - 1)) * p.m.rs + 8 * o.G;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const u32x4 *)(qrow + 32 * ks);
 }
@@ -404,9 +404,9 @@ __device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cur
 __device__ __forceinline__ void issue_kv_loads(const FwdArgs &p, int h, const Cursor &c,
                                                u32x4 (&pk)[8], u32x4 (&pv)[8], const Lanes &ln) {
   const int Lc = (int)(c.c1 - c.c0);
-  const int64_t base = p.m.row_base(h, c.j) + c.c0 * D;
-  load_tile<256>(pk, (const bf16 *)p.k + base, Lc, ln.ts);
-  load_tile<256>(pv, (const bf16 *)p.v + base, Lc, ln.ts);
+  const int64_t base = p.m.row_base(h, c.j) + c.c0 * p.m.rs;
+  load_tile<256>(pk, (const bf16 *)p.k + base, p.m.rs, Lc, ln.ts);
+  load_tile<256>(pv, (const bf16 *)p.v + base, p.m.rs, Lc, ln.ts);
 }
 
 // s_waitcnt vmcnt(N) (the other counters left alone).
@@ -442,11 +442,11 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, const char *lds) {
 __device__ __forceinline__ void dma_tile_quad(char *tile, const void *src, const FwdArgs &p, int h,
                                               const Cursor &c, int u, int lane, int k) {
   const int Lc = (int)(c.c1 - c.c0);
-  const bf16 *base = (const bf16 *)src + p.m.row_base(h, c.j) + c.c0 * D;
+  const bf16 *base = (const bf16 *)src + p.m.row_base(h, c.j) + c.c0 * p.m.rs;
   const int sub = lane >> 4, pg = lane & 15;
   const int r = 32 * u + 4 * k + sub;
   const int rr = r < Lc ? r : Lc - 1;
-  const bf16 *gp = base + (int64_t)rr * D + ((pg ^ kv_swz(r)) << 3);
+  const bf16 *gp = base + (int64_t)rr * p.m.rs + ((pg ^ kv_swz(r)) << 3);
   lds_dma16(gp, tile + (32 * u + 4 * k) * KV_ROW);
 }
 
@@ -469,8 +469,13 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
                                            const OutLane &o) {
   const int L = (int)(c.c1 - c.c0);
   const int sub = o.G, c16 = o.i16;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (bf16 *)p.out + p.m.row_base(h, c.j) + c.c0 * D, 0, L * (D * 2), kRawBufferWord3);
+  // Row r of the chunk starts at byte r * rsb; the range ends with row L - 1
+  // (a row stride is at least one row, so rows >= L fall outside it).  The
+  // host keeps 128 row strides within 2^31 bytes.
+  const int rsb = (int)(p.m.rs * 2);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (bf16 *)p.out + p.m.row_base(h, c.j) + c.c0 * p.m.rs, 0, (L - 1) * rsb + D * 2,
+      kRawBufferWord3);
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {
     const int r0 = 16 * o.qblock(bi) + sub;
@@ -478,7 +483,7 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const u32x4 x = lds_ld<u32x4>((rb ^ (it << 4)) + 1024 * it);
-      __builtin_amdgcn_raw_buffer_store_b128(x, rs, (r0 + 4 * it) * (D * 2) + c16 * 16, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, (r0 + 4 * it) * rsb + c16 * 16, 0, 0);
     }
   }
 }
@@ -823,8 +828,8 @@ void prefill_fused_kernel(FusedArgs fa) {
       u32x4 tk[8], tv[8];
       int64_t t0 = first_weighted(ps, b, dc.l2, T);
       int Lt = (int)((b - t0) < T ? (b - t0) : T);
-      load_tile<256>(tk, (const bf16 *)p.k + kvb + t0 * D, Lt, ln.tid);
-      load_tile<256>(tv, (const bf16 *)p.v + kvb + t0 * D, Lt, ln.tid);
+      load_tile<256>(tk, (const bf16 *)p.k + kvb + t0 * m.rs, m.rs, Lt, ln.tid);
+      load_tile<256>(tv, (const bf16 *)p.v + kvb + t0 * m.rs, m.rs, Lt, ln.tid);
       while (t0 < b) {
         store_tile<256>(Ks, tk, ln.tid);
         store_tile<256>(Vs, tv, ln.tid);
@@ -832,8 +837,8 @@ void prefill_fused_kernel(FusedArgs fa) {
         const int64_t t1 = t0 + T;
         if (t1 < b) {
           Lt = (int)((b - t1) < T ? (b - t1) : T);
-          load_tile<256>(tk, (const bf16 *)p.k + kvb + t1 * D, Lt, ln.tid);
-          load_tile<256>(tv, (const bf16 *)p.v + kvb + t1 * D, Lt, ln.tid);
+          load_tile<256>(tk, (const bf16 *)p.k + kvb + t1 * m.rs, m.rs, Lt, ln.tid);
+          load_tile<256>(tv, (const bf16 *)p.v + kvb + t1 * m.rs, m.rs, Lt, ln.tid);
         }
         __syncthreads();
         t0 = t1;
@@ -951,8 +956,8 @@ void local_state_kernel(FwdArgs p) {
   for (int nt = 0; nt < 4; ++nt) S[nt] = (f32x16){};
   u32x4 pk[C_LOCAL * 16 / NT_LOCAL], pv[C_LOCAL * 16 / NT_LOCAL];  // next chunk's K and V
   int L = (int)((x1 - r0) < C_LOCAL ? (x1 - r0) : C_LOCAL);
-  load_tile<NT_LOCAL, C_LOCAL>(pk, (const bf16 *)p.k + base + r0 * D, L, tid);
-  load_tile<NT_LOCAL, C_LOCAL>(pv, (const bf16 *)p.v + base + r0 * D, L, tid);
+  load_tile<NT_LOCAL, C_LOCAL>(pk, (const bf16 *)p.k + base + r0 * m.rs, m.rs, L, tid);
+  load_tile<NT_LOCAL, C_LOCAL>(pv, (const bf16 *)p.v + base + r0 * m.rs, m.rs, L, tid);
   for (int64_t t0 = r0; t0 < x1; t0 += C_LOCAL) {
     store_tile<NT_LOCAL, C_LOCAL>(Ks, pk, tid);
     store_tile<NT_LOCAL, C_LOCAL>(Vs, pv, tid);
@@ -961,8 +966,8 @@ void local_state_kernel(FwdArgs p) {
     const int64_t t1 = t0 + C_LOCAL;
     if (t1 < x1) {
       L = (int)((x1 - t1) < C_LOCAL ? (x1 - t1) : C_LOCAL);
-      load_tile<NT_LOCAL, C_LOCAL>(pk, (const bf16 *)p.k + base + t1 * D, L, tid);
-      load_tile<NT_LOCAL, C_LOCAL>(pv, (const bf16 *)p.v + base + t1 * D, L, tid);
+      load_tile<NT_LOCAL, C_LOCAL>(pk, (const bf16 *)p.k + base + t1 * m.rs, m.rs, L, tid);
+      load_tile<NT_LOCAL, C_LOCAL>(pv, (const bf16 *)p.v + base + t1 * m.rs, m.rs, L, tid);
     }
     // weight of chunk row c: lambda^(x1 - 1 - (t0 + c))
     state_update<C_LOCAL / 16, false>(S, Ks, Vs, Lc, (int)(x1 - 1 - t0), l2, fast, tail, u, lane);

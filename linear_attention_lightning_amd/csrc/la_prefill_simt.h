@@ -25,10 +25,10 @@ struct Smem {
 };
 
 template <typename Tin, int D>
-__device__ __forceinline__ void load_rows(float (*dst)[D], const Tin *src, int L, int tid) {
+__device__ __forceinline__ void load_rows(float (*dst)[D], const Tin *src, int64_t rs, int L, int tid) {
   for (int e = tid; e < T * D; e += NT) {
     int r = e / D, c = e - (e / D) * D;
-    dst[r][c] = r < L ? to_f32(src[(int64_t)r * D + c]) : 0.f;
+    dst[r][c] = r < L ? to_f32(src[(int64_t)r * rs + c]) : 0.f;
   }
 }
 
@@ -53,10 +53,10 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
   constexpr int RSTEP = NT / D;  // output rows handled per pass
   while (true) {
     const int L = (int)(cur.c1 - cur.c0);
-    const int64_t base = m.row_base(h, cur.j) + cur.c0 * D;
-    load_rows<Tin, D>(sm.Q, (const Tin *)p.q + base, L, tid);
-    load_rows<Tin, D>(sm.K, (const Tin *)p.k + base, L, tid);
-    load_rows<Tin, D>(sm.V, (const Tin *)p.v + base, L, tid);
+    const int64_t base = m.row_base(h, cur.j) + cur.c0 * m.rs;
+    load_rows<Tin, D>(sm.Q, (const Tin *)p.q + base, m.rs, L, tid);
+    load_rows<Tin, D>(sm.K, (const Tin *)p.k + base, m.rs, L, tid);
+    load_rows<Tin, D>(sm.V, (const Tin *)p.v + base, m.rs, L, tid);
     if (tid < T) sm.bw[tid] = tid < L ? pow_lam(log2lam, (float)(L - 1 - tid)) : 0.f;
     __syncthreads();
     // masked, decayed scores
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
         for (int i = 0; i < D; ++i) inter += sm.Q[r][i] * sm.S[i][j];
         float intra = 0.f;
         for (int c = 0; c <= r; ++c) intra += sm.P[r][c] * sm.V[c][j];
-        obase[(int64_t)r * D + j] = from_f32<Tin>(pow_lam(log2lam, (float)(r + 1)) * inter + intra);
+        obase[(int64_t)r * m.rs + j] = from_f32<Tin>(pow_lam(log2lam, (float)(r + 1)) * inter + intra);
       }
     }
     __syncthreads();
@@ -137,8 +137,8 @@ __global__ __launch_bounds__(NT) void local_state_kernel(FwdArgs p) {
   for (int u = 0; u < PER; ++u) acc[u] = 0.f;
   for (int64_t t0 = first_weighted(ps, b, log2lam, T); t0 < b; t0 += T) {
     const int L = (int)((b - t0) < T ? (b - t0) : T);
-    load_rows<Tin, D>(Ks, (const Tin *)p.k + base + t0 * D, L, tid);
-    load_rows<Tin, D>(Vs, (const Tin *)p.v + base + t0 * D, L, tid);
+    load_rows<Tin, D>(Ks, (const Tin *)p.k + base + t0 * m.rs, m.rs, L, tid);
+    load_rows<Tin, D>(Vs, (const Tin *)p.v + base + t0 * m.rs, m.rs, L, tid);
     if (tid < T) wv[tid] = tid < L ? pow_lam(log2lam, (float)(b - 1 - t0 - tid)) : 0.f;
     __syncthreads();
 #pragma unroll

@@ -265,6 +265,105 @@ la_status check_common(int H, int d, int block, la_dtype dt, int64_t segment_tok
   return LA_OK;
 }
 
+la_status check_layout(la_layout layout, int H, int d) {
+  if (layout != LA_HEAD_MAJOR && layout != LA_TOKEN_MAJOR) return LA_ERR_UNSUPPORTED;
+  // Output rows are stored through 32-bit byte offsets within a chunk: 128
+  // token-major row strides must stay below 2^31 bytes.
+  if (layout == LA_TOKEN_MAJOR && (int64_t)H * d * 4 * 128 >= ((int64_t)1 << 31))
+    return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+la_status fwd_fixed(const void *q, const void *k, const void *v, const float *decay, int B, int H,
+                    int64_t N, int d, int block, la_dtype dt, la_layout layout,
+                    const float *init_state, void *out, float *final_state,
+                    int64_t segment_tokens, void *workspace, size_t workspace_bytes,
+                    void *hip_stream, void *const *phase_events) {
+  if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st == LA_OK) st = check_layout(layout, H, d);
+  if (st != LA_OK) return st;
+  if ((int64_t)B * H == 0) return LA_OK;
+  if (!decay) return LA_ERR_INVALID_ARG;
+  if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+  if (N == 0 && !final_state) return LA_OK;
+
+  la::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.decay = decay;
+  a.m.cu = nullptr;
+  a.m.N = N;
+  a.m.num_seqs = B;
+  a.m.H = H;
+  a.m.total = (int64_t)B * N;
+  if (layout == LA_HEAD_MAJOR) {  // [B][H][N][d]: token t of sequence j, head h at
+    a.m.head_stride = N * d;      // ((j H + h) N + t) d = h N d + j (H - 1) N d + (j N + t) d
+    a.m.seq_extra = (int64_t)(H - 1) * N * d;
+    a.m.rs = d;
+  } else {                         // [B][N][H][d]: ((j N + t) H + h) d
+    a.m.head_stride = d;
+    a.m.seq_extra = 0;
+    a.m.rs = (int64_t)H * d;
+  }
+  a.seg_len = pl.seg;
+  a.nseg = (int)pl.nseg;
+  a.init = init_state;
+  a.fin = final_state;
+  a.ws = (float *)workspace;
+  return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream, phase_events);
+}
+
+la_status fwd_varlen(const void *q, const void *k, const void *v, const float *decay,
+                     const int32_t *cu_seqlens, int num_seqs, int H, int64_t total_N, int d,
+                     int block, la_dtype dt, la_layout layout, const float *init_states, void *out,
+                     float *final_states, int64_t segment_tokens, void *workspace,
+                     size_t workspace_bytes, void *hip_stream) {
+  if (num_seqs < 0 || total_N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st == LA_OK) st = check_layout(layout, H, d);
+  if (st != LA_OK) return st;
+  if ((int64_t)num_seqs * H == 0) return total_N == 0 ? LA_OK : LA_ERR_INVALID_ARG;
+  if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
+  if (total_N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_varlen(H, total_N, d, dt, segment_tokens);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+
+  la::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.decay = decay;
+  a.m.cu = cu_seqlens;
+  a.m.N = 0;
+  a.m.num_seqs = num_seqs;
+  a.m.H = H;
+  a.m.total = total_N;
+  a.m.seq_extra = 0;
+  if (layout == LA_HEAD_MAJOR) {  // [H][total_N][d]
+    a.m.head_stride = total_N * d;
+    a.m.rs = d;
+  } else {                         // [total_N][H][d]
+    a.m.head_stride = d;
+    a.m.rs = (int64_t)H * d;
+  }
+  a.seg_len = pl.seg;
+  a.nseg = (int)pl.nseg;
+  a.init = init_states;
+  a.fin = final_states;
+  a.ws = (float *)workspace;
+  return run_fwd(a, pl, d, dt, /*has_empty=*/true, (hipStream_t)hip_stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,9 +397,8 @@ la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const 
                              const float *init_state, void *out, float *final_state,
                              int64_t segment_tokens, void *workspace, size_t workspace_bytes,
                              void *hip_stream) {
-  return lightning_attn_fwd_timed(q, k, v, decay, B, H, N, d, block, dt, init_state, out,
-                                  final_state, segment_tokens, workspace, workspace_bytes,
-                                  hip_stream, nullptr);
+  return fwd_fixed(q, k, v, decay, B, H, N, d, block, dt, LA_HEAD_MAJOR, init_state, out,
+                   final_state, segment_tokens, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 la_status lightning_attn_fwd_timed(const void *q, const void *k, const void *v,
@@ -309,37 +407,18 @@ la_status lightning_attn_fwd_timed(const void *q, const void *k, const void *v,
                                    float *final_state, int64_t segment_tokens, void *workspace,
                                    size_t workspace_bytes, void *hip_stream,
                                    void *const *phase_events) {
-  if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
-  la_status st = check_common(H, d, block, dt, segment_tokens);
-  if (st != LA_OK) return st;
-  if ((int64_t)B * H == 0) return LA_OK;
-  if (!decay) return LA_ERR_INVALID_ARG;
-  if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
-  if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
-  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
-  if (N == 0 && !final_state) return LA_OK;
+  return fwd_fixed(q, k, v, decay, B, H, N, d, block, dt, LA_HEAD_MAJOR, init_state, out,
+                   final_state, segment_tokens, workspace, workspace_bytes, hip_stream,
+                   phase_events);
+}
 
-  la::FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.decay = decay;
-  a.m.cu = nullptr;
-  a.m.N = N;
-  a.m.num_seqs = B;
-  a.m.H = H;
-  a.m.total = (int64_t)B * N;
-  a.m.head_stride = N * d;
-  a.m.seq_extra = (int64_t)(H - 1) * N * d;
-  a.seg_len = pl.seg;
-  a.nseg = (int)pl.nseg;
-  a.init = init_state;
-  a.fin = final_state;
-  a.ws = (float *)workspace;
-  return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream, phase_events);
+la_status lightning_attn_fwd_layout(const void *q, const void *k, const void *v,
+                                    const float *decay, int B, int H, int64_t N, int d, int block,
+                                    la_dtype dt, la_layout layout, const float *init_state,
+                                    void *out, float *final_state, int64_t segment_tokens,
+                                    void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return fwd_fixed(q, k, v, decay, B, H, N, d, block, dt, layout, init_state, out, final_state,
+                   segment_tokens, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 size_t lightning_attn_fwd_varlen_workspace_size(int num_seqs, int H, int64_t total_N, int d,
@@ -356,36 +435,22 @@ la_status lightning_attn_fwd_varlen(const void *q, const void *k, const void *v,
                                     const float *init_states, void *out, float *final_states,
                                     int64_t segment_tokens, void *workspace,
                                     size_t workspace_bytes, void *hip_stream) {
-  if (num_seqs < 0 || total_N < 0) return LA_ERR_INVALID_ARG;
-  la_status st = check_common(H, d, block, dt, segment_tokens);
-  if (st != LA_OK) return st;
-  if ((int64_t)num_seqs * H == 0) return total_N == 0 ? LA_OK : LA_ERR_INVALID_ARG;
-  if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
-  if (total_N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
-  if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_varlen(H, total_N, d, dt, segment_tokens);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
-  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+  return fwd_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, block, dt, LA_HEAD_MAJOR,
+                    init_states, out, final_states, segment_tokens, workspace, workspace_bytes,
+                    hip_stream);
+}
 
-  la::FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out = out;
-  a.decay = decay;
-  a.m.cu = cu_seqlens;
-  a.m.N = 0;
-  a.m.num_seqs = num_seqs;
-  a.m.H = H;
-  a.m.total = total_N;
-  a.m.head_stride = total_N * d;
-  a.m.seq_extra = 0;
-  a.seg_len = pl.seg;
-  a.nseg = (int)pl.nseg;
-  a.init = init_states;
-  a.fin = final_states;
-  a.ws = (float *)workspace;
-  return run_fwd(a, pl, d, dt, /*has_empty=*/true, (hipStream_t)hip_stream);
+la_status lightning_attn_fwd_varlen_layout(const void *q, const void *k, const void *v,
+                                           const float *decay, const int32_t *cu_seqlens,
+                                           int num_seqs, int H, int64_t total_N, int d, int block,
+                                           la_dtype dt, la_layout layout,
+                                           const float *init_states, void *out,
+                                           float *final_states, int64_t segment_tokens,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *hip_stream) {
+  return fwd_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, block, dt, layout,
+                    init_states, out, final_states, segment_tokens, workspace, workspace_bytes,
+                    hip_stream);
 }
 
 la_status lightning_attn_decode(const void *q, const void *k, const void *v, const float *decay,

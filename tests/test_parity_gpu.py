@@ -62,16 +62,27 @@ def dev_inputs(shape, seed, dtype):
     return [torch.from_numpy(x).to("cuda").to(tdt) for x in (q, k, v)], (q, k, v)
 
 
-def run_fwd_case(B, H, N, d, dtype, seed, block=128, seg=0, with_init=False, lam=None):
+def run_fwd_case(B, H, N, d, dtype, seed, block=128, seg=0, with_init=False, lam=None,
+                 token_major=False):
     torch = torch_mod()
-    say("case fwd B=%d H=%d N=%d d=%d %s seg=%d init=%s" % (B, H, N, d, dtype, seg, with_init))
+    say("case fwd B=%d H=%d N=%d d=%d %s seg=%d init=%s token_major=%s"
+        % (B, H, N, d, dtype, seg, with_init, token_major))
     (tq, tk, tv), (q, k, v) = dev_inputs((B, H, N, d), seed, dtype)
     lam = inputs.decay_schedule(H) if lam is None else np.asarray(lam, np.float32)
     tl = torch.from_numpy(lam).to("cuda")
     init = inputs.host_state((B, H, d, d), seed + 1) if with_init else None
     ti = torch.from_numpy(init).to("cuda") if with_init else None
-    out, fin = la.lightning_attn_fwd(tq, tk, tv, tl, block=block, init_state=ti,
-                                     segment_tokens=seg)
+    if token_major:
+        # [B, N, H, d] copies; out starts as NaN so that an unwritten (or
+        # wrongly addressed) element fails the finiteness check below.
+        tq, tk, tv = (t.transpose(1, 2).contiguous() for t in (tq, tk, tv))
+        out = torch.full_like(tq, float("nan"))
+        out, fin = la.lightning_attn_fwd_layout(tq, tk, tv, tl, la.LA_TOKEN_MAJOR, block=block,
+                                                init_state=ti, segment_tokens=seg, out=out)
+        out = out.transpose(1, 2)
+    else:
+        out, fin = la.lightning_attn_fwd(tq, tk, tv, tl, block=block, init_state=ti,
+                                         segment_tokens=seg)
     torch.cuda.synchronize()
     o_ref, f_ref, _ = oracle.fwd(q, k, v, lam, init=init)
     eo, ef = rel_err(host(out), o_ref), rel_err(host(fin), f_ref)
@@ -157,24 +168,51 @@ def test_deterministic_bitwise(prefill_path):
 # ------------------------------------------------------------------ varlen
 
 
-def run_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True):
+def run_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True, token_major=False):
     torch = torch_mod()
-    say("case varlen lens=%s H=%d d=%d %s seg=%d" % (lens[:8], H, d, dtype, seg))
+    say("case varlen lens=%s H=%d d=%d %s seg=%d token_major=%s"
+        % (lens[:8], H, d, dtype, seg, token_major))
     cu = inputs.cu_seqlens(lens)
     total = int(cu[-1])
     (tq, tk, tv), (q, k, v) = dev_inputs((H, total, d), seed, dtype)
     lam = inputs.decay_schedule(H)
     init = inputs.host_state((len(lens), H, d, d), seed + 1) if with_init else None
     ti = torch.from_numpy(init).cuda() if with_init else None
-    out, fin = la.lightning_attn_fwd_varlen(tq, tk, tv, torch.from_numpy(lam).cuda(),
-                                            torch.from_numpy(cu).cuda(), init_states=ti,
-                                            segment_tokens=seg)
+    if token_major:
+        tq, tk, tv = (t.transpose(0, 1).contiguous() for t in (tq, tk, tv))  # [total, H, d]
+        out = torch.full_like(tq, float("nan"))
+        out, fin = la.lightning_attn_fwd_varlen_layout(
+            tq, tk, tv, torch.from_numpy(lam).cuda(), torch.from_numpy(cu).cuda(),
+            la.LA_TOKEN_MAJOR, init_states=ti, segment_tokens=seg, out=out)
+        out = out.transpose(0, 1)
+        assert bool(torch.isfinite(out).all())
+    else:
+        out, fin = la.lightning_attn_fwd_varlen(tq, tk, tv, torch.from_numpy(lam).cuda(),
+                                                torch.from_numpy(cu).cuda(), init_states=ti,
+                                                segment_tokens=seg)
     torch.cuda.synchronize()
     o_ref, f_ref, _ = oracle.fwd_varlen(q, k, v, lam, cu, init=init)
     eo = rel_err(host(out), o_ref) if total else 0.0
     ef = rel_err(host(fin), f_ref)
     say("   err out %.3e state %.3e" % (eo, ef))
     assert eo <= TOL[dtype] and ef <= TOL[dtype], (eo, ef)
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,seg", [
+    (2, 5, 1000, 128, "bf16", 0), (2, 5, 1000, 128, "bf16", 256), (1, 3, 4099, 128, "bf16", 1024),
+    (2, 3, 300, 64, "fp32", 0), (2, 3, 300, 128, "fp32", 96), (1, 4, 333, 64, "bf16", 0)])
+def test_token_major_layout(B, H, N, d, dtype, seg, prefill_path):
+    """[B, N, H, d] inputs and outputs (a projection's layout, read in place):
+    the oracle's result for every element, heads interleaved in each row,
+    every output element written."""
+    run_fwd_case(B, H, N, d, dtype, seed=110 + N + d, seg=seg, with_init=True,
+                 token_major=True)
+
+
+@pytest.mark.parametrize("d,dtype,seg", [(128, "bf16", 0), (128, "bf16", 200), (64, "fp32", 0)])
+def test_varlen_token_major_layout(d, dtype, seg, prefill_path):
+    run_varlen_case([300, 0, 1, 129, 1024, 5, 0, 640, 2000], 4, d, dtype, seed=120 + d, seg=seg,
+                    token_major=True)
 
 
 @pytest.mark.parametrize("seg", [0, 128, 200, 100000])
@@ -268,6 +306,31 @@ def test_full_layer_h64_n32k(prefill_path):
     q, k, v = (host(t[:, heads]) for t in (tq, tk, tv))
     o_ref, f_ref, _ = oracle.fwd(q, k, v, lam[heads])
     eo, ef = rel_err(host(out[:, heads]), o_ref), rel_err(host(fin[:, heads]), f_ref)
+    say("   err out %.3e state %.3e" % (eo, ef))
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+def test_full_layer_h64_n32k_token_major(prefill_path):
+    """The headline workload in [B, N, H, d] layout: bit-identical to the
+    head-major call (the same arithmetic, only the addressing differs), and
+    heads 0 and 63 against the oracle."""
+    torch = torch_mod()
+    w = inputs.WORKLOADS["layer_h64_n32k"]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    say("case full layer_h64_n32k token-major")
+    tq, tk, tv = inputs.device_qkv((B, H, N, d), w["seed"], "bf16")
+    tl = torch.from_numpy(inputs.decay_schedule(H)).cuda()
+    out_h, fin_h = la.lightning_attn_fwd(tq, tk, tv, tl, block=w["block"])
+    tq, tk, tv = (t.transpose(1, 2).contiguous() for t in (tq, tk, tv))
+    out_t, fin_t = la.lightning_attn_fwd_layout(tq, tk, tv, tl, la.LA_TOKEN_MAJOR,
+                                                block=w["block"])
+    torch.cuda.synchronize()
+    assert torch.equal(out_t.transpose(1, 2), out_h) and torch.equal(fin_t, fin_h)
+    heads = [0, 63]
+    q, k, v = (host(t[:, :, heads].transpose(1, 2)) for t in (tq, tk, tv))
+    o_ref, f_ref, _ = oracle.fwd(q, k, v, inputs.decay_schedule(H)[heads])
+    eo = rel_err(host(out_t[:, :, heads].transpose(1, 2)), o_ref)
+    ef = rel_err(host(fin_t[:, heads]), f_ref)
     say("   err out %.3e state %.3e" % (eo, ef))
     assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
 

@@ -920,7 +920,7 @@ void prefill_fused_kernel(FusedArgs fa) {
 // (Ordering the grid by decreasing decay, so that the long pieces of slowly
 // decaying heads start first, measured slower.)
 // Wave u owns state rows 32u..32u+31.
-__global__ __launch_bounds__(NT_LOCAL) __attribute__((amdgpu_waves_per_eu(3, 4)))
+__global__ __launch_bounds__(NT_LOCAL) __attribute__((amdgpu_waves_per_eu(2, 4)))
 void local_state_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C_LOCAL * KV_ROW];
   char *Ks = smem, *Vs = smem + C_LOCAL * KV_ROW;
@@ -954,25 +954,49 @@ void local_state_kernel(FwdArgs p) {
   f32x16 S[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) S[nt] = (f32x16){};
-  u32x4 pk[C_LOCAL * 16 / NT_LOCAL], pv[C_LOCAL * 16 / NT_LOCAL];  // next chunk's K and V
-  int L = (int)((x1 - r0) < C_LOCAL ? (x1 - r0) : C_LOCAL);
-  load_tile<NT_LOCAL, C_LOCAL>(pk, (const bf16 *)p.k + base + r0 * m.rs, m.rs, L, tid);
-  load_tile<NT_LOCAL, C_LOCAL>(pv, (const bf16 *)p.v + base + r0 * m.rs, m.rs, L, tid);
-  for (int64_t t0 = r0; t0 < x1; t0 += C_LOCAL) {
-    store_tile<NT_LOCAL, C_LOCAL>(Ks, pk, tid);
-    store_tile<NT_LOCAL, C_LOCAL>(Vs, pv, tid);
+  // Two chunks in flight: while chunk t is in LDS and being summed, chunks
+  // t + 1 and t + 2 are loading into two register sets.  Loads past the
+  // piece's end re-read its last chunk (still in L2; the data go unused), so
+  // every load is unconditional and the compiler's memory waits stay exact.
+  constexpr int PER = C_LOCAL * 16 / NT_LOCAL;
+  u32x4 pk[2][PER], pv[2][PER];
+  const int64_t last = r0 + (x1 - 1 - r0) / C_LOCAL * C_LOCAL;  // start of the last chunk
+  const bf16 *kb = (const bf16 *)p.k + base, *vb = (const bf16 *)p.v + base;
+  auto issue = [&](auto slot_c, int64_t t) {
+    constexpr int sl = decltype(slot_c)::value;
+    const int64_t tt = t < last ? t : last;
+    const int Lt = (int)((x1 - tt) < C_LOCAL ? (x1 - tt) : C_LOCAL);
+    load_tile<NT_LOCAL, C_LOCAL>(pk[sl], kb + tt * m.rs, m.rs, Lt, tid);
+    load_tile<NT_LOCAL, C_LOCAL>(pv[sl], vb + tt * m.rs, m.rs, Lt, tid);
+  };
+  // Sums the chunk at t0 held in register set sl, then reloads that set with
+  // the chunk two ahead.
+  auto step = [&](auto slot_c, int64_t t0) {
+    constexpr int sl = decltype(slot_c)::value;
+    store_tile<NT_LOCAL, C_LOCAL>(Ks, pk[sl], tid);
+    store_tile<NT_LOCAL, C_LOCAL>(Vs, pv[sl], tid);
     __syncthreads();
-    const int Lc = L;
-    const int64_t t1 = t0 + C_LOCAL;
-    if (t1 < x1) {
-      L = (int)((x1 - t1) < C_LOCAL ? (x1 - t1) : C_LOCAL);
-      load_tile<NT_LOCAL, C_LOCAL>(pk, (const bf16 *)p.k + base + t1 * m.rs, m.rs, L, tid);
-      load_tile<NT_LOCAL, C_LOCAL>(pv, (const bf16 *)p.v + base + t1 * m.rs, m.rs, L, tid);
-    }
+    issue(slot_c, t0 + 2 * C_LOCAL);
+    const int Lc = (int)((x1 - t0) < C_LOCAL ? (x1 - t0) : C_LOCAL);
     // weight of chunk row c: lambda^(x1 - 1 - (t0 + c))
     state_update<C_LOCAL / 16, false>(S, Ks, Vs, Lc, (int)(x1 - 1 - t0), l2, fast, tail, u, lane);
     __syncthreads();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // (No branch in the loop body and the two sets issued in order: either
+  // would make the compiler wait for every load at the top of the loop.)
+  issue(S0{}, r0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(S1{}, r0 + C_LOCAL);
+  int64_t t0 = r0;
+  for (; t0 + C_LOCAL < x1; t0 += 2 * C_LOCAL) {
+    step(S0{}, t0);
+    step(S1{}, t0 + C_LOCAL);
   }
+  if (t0 < x1) step(S0{}, t0);
+  // The last loads (past the piece's end) are waited for before the stores
+  // below are issued; they read memory the piece already read.
   store_state(p.ws + (((int64_t)s * R + r) * H + h) * (int64_t)D * D, S, u, l32, g);
 }
 

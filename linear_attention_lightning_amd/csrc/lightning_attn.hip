@@ -74,14 +74,14 @@ constexpr int64_t kFusedSeg = 8192;
 int64_t target_groups(int d, la_dtype dt) { return use_mfma(d, dt) ? 256 : 512; }
 
 // Pieces per segment of the MFMA local-state pass: one small workgroup per
-// 8 or more 64-token chunks, at most 8, so that several workgroups share a
-// CU and hide one another's latency, and a segment whose every chunk carries
-// weight is not walked by one workgroup with one chunk in flight.  The
-// vector-ALU pass uses one.
+// 8 or more 64-token chunks, at most 4, so that several workgroups share a
+// CU and hide one another's latency.  (8 or 16 pieces made the pass itself
+// faster but the scan, which reads every piece's partial state, slower by
+// more.)  The vector-ALU pass uses one.
 int pieces(int64_t seg, int d, la_dtype dt) {
   if (!use_mfma(d, dt)) return 1;
   const int64_t r = seg / la::mfma::C_LOCAL / 8;
-  return r >= 8 ? 8 : r >= 4 ? 4 : r >= 2 ? 2 : 1;  // a power of two (the scan shifts by it)
+  return r >= 4 ? 4 : r >= 2 ? 2 : 1;  // a power of two (the scan shifts by it)
 }
 
 size_t phased_ws_bytes(const Plan &p, int H, int d) {

@@ -42,11 +42,14 @@ def _bind(lib):
     lib.oracle_default_threads.restype = _I
     lib.oracle_fwd_f64.argtypes = [_P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _I]
     lib.oracle_fwd_varlen_f64.argtypes = [_P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _I]
+    lib.oracle_fwd_varlen_snap_f64.argtypes = [_P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P,
+                                               _L, _P, _P, _I]
     lib.oracle_decode_f64.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I]
     lib.oracle_bruteforce_f64.argtypes = [_P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _I]
     lib.oracle_rows_f64.argtypes = [_P, _P, _P, ctypes.c_float, _I, _P, _L, _P, _P, _I]
     lib.oracle_state_entries_f64.argtypes = [_P, _P, ctypes.c_float, _I, _L, _P, _L, _P, _P, _I]
-    for f in ("oracle_fwd_f64", "oracle_fwd_varlen_f64", "oracle_decode_f64",
+    for f in ("oracle_fwd_f64", "oracle_fwd_varlen_f64", "oracle_fwd_varlen_snap_f64",
+              "oracle_decode_f64",
               "oracle_bruteforce_f64", "oracle_rows_f64", "oracle_state_entries_f64"):
         getattr(lib, f).restype = _I
     return lib
@@ -92,6 +95,31 @@ def fwd_varlen(q, k, v, decay, cu_seqlens, init=None, want_out=True, nthreads=0,
     n = lib.oracle_fwd_varlen_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(cu), S, H, total,
                                   d, _ptr(init), _ptr(out), _ptr(fin), nthreads)
     return out, fin, n
+
+
+def fwd_varlen_snapshots(q, k, v, decay, cu_seqlens, interval, init=None, want_out=True,
+                         nthreads=0, lib=None):
+    """fwd_varlen that also returns the prefix states: snapshot m (from 1) of
+    sequence j is the state after its first m * interval tokens, at row
+    offsets[j] + m - 1, with offsets the exclusive prefix sum of
+    floor(n_j / interval).  Returns (out, final_states, snapshots
+    [rows, H, d, d], offsets [S + 1] int32)."""
+    lib = lib or load()
+    q, k, v, decay = _f32(q), _f32(k), _f32(v), _f32(decay)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    H, total, d = q.shape
+    S = cu.shape[0] - 1
+    assert interval >= 1
+    offs = np.zeros(S + 1, np.int32)
+    offs[1:] = np.cumsum(np.diff(cu.astype(np.int64)) // interval)
+    init = _f64(init)
+    out = np.empty((H, total, d), np.float64) if want_out else None
+    fin = np.empty((S, H, d, d), np.float64)
+    snaps = np.empty((int(offs[-1]), H, d, d), np.float64)
+    lib.oracle_fwd_varlen_snap_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(cu), S, H, total,
+                                   d, _ptr(init), _ptr(out), _ptr(fin), int(interval), _ptr(offs),
+                                   _ptr(snaps), nthreads)
+    return out, fin, snaps, offs
 
 
 def decode(q, k, v, decay, state, nthreads=0, lib=None):

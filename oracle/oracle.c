@@ -117,7 +117,7 @@ static int run_units(unit_fn fn, void *ctx, int64_t n_units, int nthreads) {
  * by the CPU test that checks the oracle's pins catch such mistakes.
  * 0 = correct; 1 = decay applied after the add; 2 = transposed outer product;
  * 3 = output read before the update; 4 = decay dropped; 5 = output contracts
- * the state's other index. */
+ * the state's other index; 6 = prefix-state snapshots taken one token early. */
 #ifndef ORACLE_PLANT
 #define ORACLE_PLANT 0
 #endif
@@ -210,6 +210,9 @@ typedef struct {
   int64_t total;
   const double *init;
   double *out, *fin;
+  int64_t snap_iv;         /* 0: no snapshots */
+  const int32_t *snap_off; /* [S + 1] first snapshot row of each sequence */
+  double *snaps;           /* [rows][H][d][d] */
 } var_ctx;
 
 static void var_unit(void *vctx, int64_t u) {
@@ -225,8 +228,26 @@ static void var_unit(void *vctx, int64_t u) {
   double *orow = (double *)malloc(sizeof(double) * (size_t)d);
   if (c->init) memcpy(S, c->init + sidx, sizeof(double) * (size_t)dd);
   else memset(S, 0, sizeof(double) * (size_t)dd);
-  recur_one(c->q + base, c->k + base, c->v + base, (double)c->decay[h], n, d, S,
-            c->out ? c->out + base : NULL, orow);
+  /* The recurrence runs in steps of snap_iv tokens (one step without
+   * snapshots); after each full step the state is the prefix state after
+   * that many tokens of the sequence, and is copied out. */
+  int64_t step = c->snap_iv > 0 ? c->snap_iv : (n > 0 ? n : 1);
+  for (int64_t t = 0, m = 0; t < n; t += step) {
+    int64_t len = n - t < step ? n - t : step;
+    int snap = c->snap_iv > 0 && len == step;
+    /* (plant 6 takes the snapshot one token short of its point) */
+    int64_t first = (ORACLE_PLANT == 6 && snap) ? len - 1 : len;
+    recur_one(c->q + base + t * d, c->k + base + t * d, c->v + base + t * d,
+              (double)c->decay[h], first, d, S, c->out ? c->out + base + t * d : NULL, orow);
+    if (snap) {
+      int64_t row = (int64_t)c->snap_off[j] + m++;
+      memcpy(c->snaps + (row * c->H + h) * dd, S, sizeof(double) * (size_t)dd);
+    }
+    if (first < len)
+      recur_one(c->q + base + (t + first) * d, c->k + base + (t + first) * d,
+                c->v + base + (t + first) * d, (double)c->decay[h], len - first, d, S,
+                c->out ? c->out + base + (t + first) * d : NULL, orow);
+  }
   if (c->fin) memcpy(c->fin + sidx, S, sizeof(double) * (size_t)dd);
   free(orow);
   free(S);
@@ -238,7 +259,23 @@ static void var_unit(void *vctx, int64_t u) {
 int oracle_fwd_varlen_f64(const float *q, const float *k, const float *v, const float *decay,
                           const int32_t *cu_seqlens, int num_seqs, int H, int64_t total, int d,
                           const double *init, double *out, double *fin, int nthreads) {
-  var_ctx c = {q, k, v, decay, cu_seqlens, num_seqs, H, d, total, init, out, fin};
+  var_ctx c = {q, k, v, decay, cu_seqlens, num_seqs, H, d, total, init, out, fin, 0, NULL, NULL};
+  return run_units(var_unit, &c, (int64_t)num_seqs * H, nthreads);
+}
+
+/* Packed prefill that also keeps prefix states (the K3 reading notes'
+ * inference-engine part: one prefix state per block, since a linear-attention
+ * state is rewritten at every token): snapshot m = 1, 2, ... of sequence j
+ * is the state after its first m * snap_iv tokens, S_{m snap_iv - 1} of the
+ * recurrence above (so it includes the sequence's initial state), stored at
+ * row snap_off[j] + m - 1 of snaps ([rows][H][d][d]).  snap_iv >= 1. */
+int oracle_fwd_varlen_snap_f64(const float *q, const float *k, const float *v, const float *decay,
+                               const int32_t *cu_seqlens, int num_seqs, int H, int64_t total,
+                               int d, const double *init, double *out, double *fin,
+                               int64_t snap_iv, const int32_t *snap_off, double *snaps,
+                               int nthreads) {
+  var_ctx c = {q, k, v, decay, cu_seqlens, num_seqs, H, d, total, init, out, fin,
+               snap_iv, snap_off, snaps};
   return run_units(var_unit, &c, (int64_t)num_seqs * H, nthreads);
 }
 

@@ -193,6 +193,71 @@ def test_varlen_equals_independent_sequences():
             assert np.array_equal(f[j], init[j])
 
 
+def _closed_form_state(k, v, lam, S0):
+    """S after all rows of k, v [n, d] as the decayed sum
+    lambda^n S0 + sum_s lambda^(n-1-s) k_s^T v_s, with numpy."""
+    n = k.shape[0]
+    w = float(lam) ** np.arange(n - 1, -1, -1, dtype=np.float64)
+    K, V = k.astype(np.float64), v.astype(np.float64)
+    S = (K * w[:, None]).T @ V
+    return S + float(lam) ** n * S0 if S0 is not None else S
+
+
+def _check_snapshots(q, k, v, lam, cu, iv, init, lib=None):
+    """Snapshots of fwd_varlen_snapshots against the numpy closed form of the
+    prefix state; its outputs and final states against fwd_varlen."""
+    o, f, snaps, offs = oracle.fwd_varlen_snapshots(q, k, v, lam, cu, iv, init=init, lib=lib)
+    o2, f2, _ = oracle.fwd_varlen(q, k, v, lam, cu, init=init, lib=lib)
+    ok = rel_err(o, o2) < 1e-13 and rel_err(f, f2) < 1e-13
+    H = q.shape[0]
+    for j in range(len(cu) - 1):
+        a, n = int(cu[j]), int(cu[j + 1] - cu[j])
+        ok = ok and int(offs[j + 1] - offs[j]) == n // iv
+        for m in range(1, n // iv + 1):
+            for h in range(H):
+                ref = _closed_form_state(k[h, a:a + m * iv], v[h, a:a + m * iv], lam[h],
+                                         None if init is None else init[j, h])
+                ok = ok and rel_err(snaps[offs[j] + m - 1, h], ref) < 1e-12
+    return ok
+
+
+@pytest.mark.parametrize("iv", [1, 3, 8, 16])
+def test_prefix_snapshots_are_closed_form_prefix_states(iv):
+    """Prefix-state snapshots (K3 notes, inference engine: one prefix state
+    per block): snapshot m of a sequence is the state after its first m*iv
+    tokens, i.e. lambda^(m iv) S_init + sum_s lambda^(m iv - 1 - s) k_s^T v_s
+    (numpy closed form), for ragged and zero-length sequences."""
+    H, d = 2, 6
+    lens = [17, 0, 3, 32, 1, 9]
+    cu = inputs.cu_seqlens(lens)
+    q, k, v = inputs.host_qkv((H, int(cu[-1]), d), 81, dtype="fp32")
+    lam = np.asarray([0.93, 0.6], np.float32)
+    init = inputs.host_state((len(lens), H, d, d), 82).astype(np.float64)
+    assert _check_snapshots(q, k, v, lam, cu, iv, init)
+    assert _check_snapshots(q, k, v, lam, cu, iv, None)
+
+
+def test_prefix_snapshot_continuation():
+    """A request that shares the first m*iv tokens continues from snapshot m:
+    prefilling only the rest from it gives the full run's outputs and final
+    state (the carried state of the block form, section 2.2.1; any chunking
+    gives the same result, K3 notes)."""
+    H, d, iv = 2, 8, 16
+    lens = [70, 48]
+    cu = inputs.cu_seqlens(lens)
+    q, k, v = inputs.host_qkv((H, int(cu[-1]), d), 83, dtype="fp32")
+    lam = np.asarray([0.97, 0.7], np.float32)
+    o, f, snaps, offs = oracle.fwd_varlen_snapshots(q, k, v, lam, cu, iv)
+    assert rel_err(snaps[offs[1] + 2], f[1]) < 1e-13  # 48 = 3 * 16: last snapshot = final
+    for j, m in ((0, 1), (0, 4), (1, 2)):
+        a, b = int(cu[j]) + m * iv, int(cu[j + 1])
+        oc, fc, _ = oracle.fwd_varlen(q[:, a:b], k[:, a:b], v[:, a:b], lam,
+                                      np.array([0, b - a], np.int32),
+                                      init=snaps[offs[j] + m - 1][None])
+        assert rel_err(oc, o[:, a:b]) < 1e-12
+        assert rel_err(fc[0], f[j]) < 1e-12
+
+
 def test_linearity_in_values():
     B, H, N, d = 1, 2, 30, 8
     q, k, v = rand_qkv(B, H, N, d, seed=51)
@@ -267,13 +332,16 @@ def _pins_pass(lib):
     Q, K, V = (x.astype(np.float64) for x in (rng_q, rng_k, rng_v))
     ref = ((Q @ K.transpose(0, 1, 3, 2)) * np.tril(np.ones((24, 24)))) @ V
     ok = ok and rel_err(o1, ref) < 1e-12
+    cu = inputs.cu_seqlens([11, 8])
+    sq, sk, sv = rand_qkv(1, 2, 19, 4, seed=72)
+    ok = ok and _check_snapshots(sq[0], sk[0], sv[0], lam, cu, 4, None, lib=lib)
     return ok
 
 
 def test_planted_mistakes_are_caught():
     assert _pins_pass(oracle.load())
     with tempfile.TemporaryDirectory() as tmp:
-        for plant in (1, 2, 3, 4, 5):
+        for plant in (1, 2, 3, 4, 5, 6):
             path = oracle_build.build(out=os.path.join(tmp, "lib%d.so" % plant), plant=plant)
             lib = oracle.load(path)
             assert not _pins_pass(lib), "planted mistake %d not caught" % plant

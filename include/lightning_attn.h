@@ -208,6 +208,53 @@ la_status lightning_attn_fwd_varlen_layout(const void *q, const void *k, const v
                                            void *hip_stream);
 
 /*
+ * lightning_attn_fwd_varlen_layout that also stores prefix-state snapshots:
+ * the state of every sequence after each multiple of snapshot_interval of
+ * its tokens, a prefix cache for linear attention (K3 reading notes,
+ * "inference engine" part: a linear-attention state is rewritten at every
+ * token, so keeping all of them defeats the method and keeping none loses
+ * prefix caching; the cache keeps one prefix state per block).  A request
+ * that shares the first m * snapshot_interval tokens of a cached sequence
+ * continues from snapshot m as its init_states row and prefills only the
+ * rest (MiniMax-01 report, sections 3.3.2-3.3.3: batches whose inputs carry
+ * a prefix cache).
+ *
+ *   snapshot_interval: tokens between snapshots, >= 1.  Snapshot m (m = 1 ..
+ *                  floor(n_j / snapshot_interval)) of sequence j, of length
+ *                  n_j, is the state after its token m * snapshot_interval - 1
+ *                  (counted from the sequence start, and including the
+ *                  sequence's init_states row); when snapshot_interval
+ *                  divides n_j the last snapshot equals the final state.
+ *                  Chunks are cut at snapshot points, so an interval that is
+ *                  a multiple of 128 tokens (bf16, d = 128) or 32 tokens
+ *                  (otherwise) keeps the kernels' chunks whole.
+ *   snapshot_offsets: [num_seqs + 1] int32 DEVICE array: snapshot m of
+ *                  sequence j goes to row snapshot_offsets[j] + m - 1.  A
+ *                  precondition (not checked, it lives on the device): the
+ *                  rows of different snapshots are distinct and lie inside
+ *                  `snapshots`, e.g. snapshot_offsets = the exclusive prefix
+ *                  sum of floor(n_j / snapshot_interval).
+ *   snapshots    : [rows][H][d][d] float32, written only at the rows above
+ *                  (one row is a whole [H][d][d] state set, usable directly
+ *                  as an init_states row).  Must not alias any other buffer.
+ *                  snapshots and snapshot_offsets may be NULL when
+ *                  snapshot_interval > total_N (no sequence reaches a
+ *                  snapshot point); then nothing is stored.
+ *   Other arguments and the workspace as for lightning_attn_fwd_varlen_layout
+ *   (the workspace size does not depend on the snapshots).
+ *
+ * Returns LA_ERR_INVALID_ARG if snapshot_interval < 1, or if snapshots or
+ * snapshot_offsets is NULL while snapshot_interval <= total_N; otherwise as
+ * lightning_attn_fwd_varlen_layout.
+ */
+la_status lightning_attn_fwd_varlen_snapshots(
+    const void *q, const void *k, const void *v, const float *decay, const int32_t *cu_seqlens,
+    int num_seqs, int H, int64_t total_N, int d, int block, la_dtype dt, la_layout layout,
+    const float *init_states, void *out, float *final_states, int64_t snapshot_interval,
+    const int32_t *snapshot_offsets, float *snapshots, int64_t segment_tokens, void *workspace,
+    size_t workspace_bytes, void *hip_stream);
+
+/*
  * One recurrent decode step (MiniMax-01 report, section 2.2.4, eq. 12;
  * section 3.3.1, fused decode state update):
  *     state <- lambda_h * state + k^T v,   out = q state   (updated state).

@@ -13,13 +13,16 @@ Entry points (same names as the C ABI):
   lightning_attn_fwd_layout(q, k, v, decay, layout, ...) -> (out, final_state)
   lightning_attn_fwd_varlen_layout(q, k, v, decay, cu_seqlens, layout, ...) -> (out, final_states)
   lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, ...) -> (out, final_states)
+  lightning_attn_fwd_varlen_snapshots(q, k, v, decay, cu_seqlens, snapshot_interval, ...)
+      -> (out, final_states, snapshots, snapshot_offsets)
   lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
 """
 import ctypes
 import os
 
 __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd_layout",
-           "lightning_attn_fwd_varlen", "lightning_attn_fwd_varlen_layout", "lightning_attn_decode",
+           "lightning_attn_fwd_varlen", "lightning_attn_fwd_varlen_layout",
+           "lightning_attn_fwd_varlen_snapshots", "snapshot_row_offsets", "lightning_attn_decode",
            "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
@@ -77,6 +80,9 @@ def load_library(path=None):
     lib.lightning_attn_fwd_varlen_workspace_size.restype = Z
     lib.lightning_attn_fwd_varlen.argtypes = [P, P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P]
     lib.lightning_attn_fwd_varlen.restype = I
+    lib.lightning_attn_fwd_varlen_snapshots.argtypes = [P, P, P, P, P, I, I, L, I, I, I, I, P, P,
+                                                        P, L, P, P, L, P, Z, P]
+    lib.lightning_attn_fwd_varlen_snapshots.restype = I
     lib.lightning_attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
     lib.lightning_attn_decode.restype = I
     if path is None:
@@ -224,8 +230,60 @@ def lightning_attn_fwd_varlen_layout(q, k, v, decay, cu_seqlens, layout, block=1
                        final_states, workspace, layout)
 
 
+def snapshot_row_offsets(cu_seqlens, snapshot_interval):
+    """Row offsets of each sequence's prefix-state snapshots in the packed
+    snapshot buffer: the exclusive prefix sum of floor(n_j / interval), as a
+    list of num_seqs + 1 Python ints (the last one is the row count)."""
+    if snapshot_interval < 1:
+        raise ValueError("snapshot_interval must be >= 1")
+    cu = [int(x) for x in cu_seqlens.tolist()]
+    offs = [0]
+    for j in range(len(cu) - 1):
+        offs.append(offs[-1] + (cu[j + 1] - cu[j]) // snapshot_interval)
+    return offs
+
+
+def lightning_attn_fwd_varlen_snapshots(q, k, v, decay, cu_seqlens, snapshot_interval,
+                                        layout=LA_HEAD_MAJOR, block=128, init_states=None,
+                                        segment_tokens=0, out=None, final_states=None,
+                                        snapshots=None, snapshot_offsets=None, workspace=None):
+    """lightning_attn_fwd_varlen_layout that also stores the state of every
+    sequence after each multiple of snapshot_interval of its tokens (a prefix
+    cache).  snapshot_offsets: int32 [num_seqs + 1] on the device (default:
+    the exclusive prefix sum of floor(n_j / interval), computed from
+    cu_seqlens on the host); snapshot m (from 1) of sequence j is row
+    snapshot_offsets[j] + m - 1 of snapshots [rows, H, d, d] float32.
+    Returns (out, final_states, snapshots, snapshot_offsets)."""
+    torch = _torch()
+    dev = q.device
+    if snapshot_offsets is None:
+        offs = snapshot_row_offsets(cu_seqlens, snapshot_interval)
+        snapshot_offsets = torch.tensor(offs, dtype=torch.int32, device=dev)
+        rows = offs[-1]
+    else:
+        rows = None
+    H = q.shape[1] if layout == LA_TOKEN_MAJOR else q.shape[0]
+    d = q.shape[2]
+    if snapshots is None:
+        if rows is None:
+            rows = int(snapshot_offsets[-1].item())
+        snapshots = torch.empty((rows, H, d, d), dtype=torch.float32, device=dev)
+    if snapshots.dim() != 4 or snapshots.shape[1:] != (H, d, d):
+        raise ValueError("snapshots must be [rows, H, d, d]")
+    _check(snapshots, "snapshots", snapshots.shape, torch.float32, dev)
+    _check(snapshot_offsets, "snapshot_offsets", (cu_seqlens.numel(),), torch.int32, dev)
+    iv = snapshot_interval
+    if snapshots.numel() == 0:
+        # no snapshot is due: an interval beyond every sequence stores none
+        iv = max(int(q.shape[0] if layout == LA_TOKEN_MAJOR else q.shape[1]), 0) + 1
+    out, final_states = _fwd_varlen(q, k, v, decay, cu_seqlens, block, init_states,
+                                    segment_tokens, out, final_states, workspace, layout,
+                                    (iv, snapshot_offsets, snapshots))
+    return out, final_states, snapshots, snapshot_offsets
+
+
 def _fwd_varlen(q, k, v, decay, cu_seqlens, block, init_states, segment_tokens, out,
-                final_states, workspace, layout):
+                final_states, workspace, layout, snap=None):
     torch = _torch()
     lib = load_library()
     if layout == LA_TOKEN_MAJOR:
@@ -260,7 +318,12 @@ def _fwd_varlen(q, k, v, decay, cu_seqlens, block, init_states, segment_tokens, 
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(cu_seqlens), S, H, total, d, block, dt)
     tail = (_ptr(init_states), _ptr(out), _ptr(final_states), segment_tokens, _ptr(workspace),
             ws_have, _stream(dev))
-    if layout is None:
+    if snap is not None:
+        iv, offs, rows = snap
+        st = lib.lightning_attn_fwd_varlen_snapshots(*head, layout, *tail[:3], iv, _ptr(offs),
+                                                     _ptr(rows), *tail[3:])
+        name = "lightning_attn_fwd_varlen_snapshots"
+    elif layout is None:
         st = lib.lightning_attn_fwd_varlen(*head, *tail)
         name = "lightning_attn_fwd_varlen"
     else:

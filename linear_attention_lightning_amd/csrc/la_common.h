@@ -56,6 +56,7 @@ struct SeqMap {
   int64_t seq_extra;
   int64_t rs;  // elements between consecutive tokens of one head: d (head-major
                // layouts) or H*d (token-major layouts)
+  int64_t snap_iv;  // prefix-state snapshot interval in tokens, 0 = none
 
   __device__ __forceinline__ int64_t start(int j) const {
     return cu ? (int64_t)cu[j] : (int64_t)j * N;
@@ -79,26 +80,45 @@ struct SeqMap {
 
 // A chunk [c0, c1) of at most T tokens inside segment [a, b), within the
 // piece of sequence j that the segment holds.  Chunks restart at every
-// sequence start and stop at every sequence end and at the segment end.
+// sequence start and stop at every sequence end, at the segment end and at
+// every snapshot point (a multiple of snap_iv tokens into the sequence), so
+// that the state after a snapshot point's last token exists at a chunk end.
 struct Cursor {
   int64_t c0, c1;
   int64_t pend;     // end of the current piece: min(b, seq_end)
   int64_t seq_end;  // start(j + 1)
+  int64_t snap;     // first snapshot point of sequence j after c0 (INT64_MAX: none)
   int j;
   bool valid;
 };
 
+constexpr int64_t kNoSnap = INT64_MAX;
+
+__device__ __forceinline__ int64_t min3(int64_t x, int64_t y, int64_t z) {
+  const int64_t t = x < y ? x : y;
+  return t < z ? t : z;
+}
+
+// SNAP = false compiles the snapshot cuts out (m.snap_iv is ignored), so
+// kernels without snapshots keep their scalar registers.
+template <bool SNAP>
 __device__ __forceinline__ Cursor first_chunk(const SeqMap &m, int64_t a, int64_t b, int T) {
   Cursor c;
   c.valid = a < b;
   c.j = c.valid ? m.seq_of(a) : 0;
   c.seq_end = c.valid ? m.start(c.j + 1) : b;
   c.pend = c.seq_end < b ? c.seq_end : b;
+  c.snap = kNoSnap;
+  if (SNAP && m.snap_iv > 0 && c.valid) {
+    const int64_t s0 = m.start(c.j);
+    c.snap = s0 + ((a - s0) / m.snap_iv + 1) * m.snap_iv;
+  }
   c.c0 = a;
-  c.c1 = (a + T < c.pend) ? a + T : c.pend;
+  c.c1 = SNAP ? min3(a + T, c.pend, c.snap) : (a + T < c.pend ? a + T : c.pend);
   return c;
 }
 
+template <bool SNAP>
 __device__ __forceinline__ Cursor next_chunk(const SeqMap &m, const Cursor &c, int64_t b, int T) {
   Cursor n = c;
   n.c0 = c.c1;
@@ -110,10 +130,22 @@ __device__ __forceinline__ Cursor next_chunk(const SeqMap &m, const Cursor &c, i
     n.j = m.seq_of(n.c0);
     n.seq_end = m.start(n.j + 1);
     n.pend = n.seq_end < b ? n.seq_end : b;
+    if (SNAP) n.snap = m.snap_iv > 0 ? n.c0 + m.snap_iv : kNoSnap;  // start(n.j) == n.c0
+  } else if (SNAP && n.c0 == c.snap) {
+    n.snap = c.snap + m.snap_iv;
   }
-  n.c1 = (n.c0 + T < n.pend) ? n.c0 + T : n.pend;
+  n.c1 = SNAP ? min3(n.c0 + T, n.pend, n.snap) : (n.c0 + T < n.pend ? n.c0 + T : n.pend);
   n.valid = true;
   return n;
+}
+
+// Row of `snaps` that receives the state after chunk c (which ends at the
+// snapshot point c.snap of sequence c.j): snapshot number
+// (c.snap - start(j)) / snap_iv, counted from 1, of that sequence.
+__device__ __forceinline__ int64_t snap_row(const SeqMap &m, const int32_t *snap_off,
+                                            const Cursor &c) {
+  const unsigned n = (unsigned)(c.snap - m.start(c.j)) / (unsigned)m.snap_iv;
+  return (int64_t)snap_off[c.j] + (int64_t)n - 1;
 }
 
 // First chunk of a local-state pass over [ps, b) (chunks of T tokens
@@ -142,6 +174,8 @@ struct FwdArgs {
   float *ws;         // segment states (scan mode) or nullptr: [nseg][r_split][H][d][d];
                      // the state entering segment s is at slot (s, 0)
   int r_split;       // pieces per segment of the local-state pass (>= 1)
+  float *snaps;      // prefix-state snapshots [rows][H][d][d] (m.snap_iv > 0), else nullptr
+  const int32_t *snap_off;  // [num_seqs + 1]: first snapshot row of each sequence
 };
 
 // Piece r of R of a local-state range [ps, b) cut into chunks of C tokens

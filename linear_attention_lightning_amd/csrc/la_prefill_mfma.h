@@ -517,7 +517,7 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 // FAST: the decay weights take the factored powers (see Decay); a template
 // parameter so that each chunk step is one basic block the scheduler can
 // interleave freely.
-template <bool FAST>
+template <bool FAST, bool SNAP>
 __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                             u32x4 (&qn)[2][4], char *smem, const Decay &dc,
                                             const Lanes &ln) {
@@ -530,7 +530,7 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
   int buf = 0;
 
   while (true) {
-    const Cursor nxt = next_chunk(m, cur, b, T);
+    const Cursor nxt = next_chunk<SNAP>(m, cur, b, T);
     const unsigned Ks = lds_u32(smem + buf * LDS_KV), Vs = Ks + LDS_K;
     __syncthreads();  // A: this chunk's K/V and entering S^T are in LDS
 #pragma unroll
@@ -631,7 +631,9 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
 // The chunk loop, state side.  On entry S holds the state entering the
 // segment.  Loads every K/V tile of the walk but the output waves' K tiles
 // (see above), updates the state and publishes it as S^T; writes every
-// sequence end's final state inside the segment.
+// sequence end's final state inside the segment, and the state at every
+// snapshot point the segment's chunks end on.
+template <bool SNAP>
 __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                            f32x16 (&S)[4], char *smem, const Decay &dc,
                                            const Lanes &ln) {
@@ -648,7 +650,7 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
   vm_wait<0>();
 
   while (true) {
-    const Cursor nxt = next_chunk(m, cur, b, T);
+    const Cursor nxt = next_chunk<SNAP>(m, cur, b, T);
     const int L = (int)(cur.c1 - cur.c0);
     char *Ks = smem + buf * LDS_KV, *Vs = Ks + LDS_K;
     char *Kn = smem + (buf ^ 1) * LDS_KV, *Vn = Kn + LDS_K;
@@ -667,12 +669,14 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
     };
     const bool seq_done = (cur.c1 == cur.seq_end);
     const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
-    if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
+    const bool snap_here = SNAP && (cur.c1 == cur.snap);
+    if ((nxt.valid && !new_piece) || (seq_done && p.fin) || snap_here) {
       const float gL = fast_exp2((float)L * l2);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) S[nt] *= gL;
       state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane, issue_next);
       if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
+      if (snap_here) store_state(p.snaps + (snap_row(m, p.snap_off, cur) * H + h) * DD, S, w, l32, g);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) issue_next(k);
@@ -692,6 +696,8 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 
 // Phase C: outputs (and final states) for one (segment, head), from the
 // segment's entering state (scan result, initial state or zero).
+// SNAP: the walk also stores prefix-state snapshots (p.m.snap_iv > 0).
+template <bool SNAP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_chunk_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -703,7 +709,7 @@ void prefill_chunk_kernel(FwdArgs p) {
   const int64_t a = (int64_t)s * p.seg_len;
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
   const int64_t DD = (int64_t)D * D;
-  const Cursor cur = first_chunk(m, a, b, T);
+  const Cursor cur = first_chunk<SNAP>(m, a, b, T);
   if (!cur.valid) return;
   if (ln.out_wave) {
     u32x4 qn[2][4];
@@ -711,15 +717,15 @@ void prefill_chunk_kernel(FwdArgs p) {
     issue_q_loads(p, h, cur, 0, qn[0], o);
     issue_q_loads(p, h, cur, 1, qn[1], o);
     if (dc.fast)
-      output_loop<true>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<true, SNAP>(p, h, b, cur, qn, smem, dc, ln);
     else
-      output_loop<false>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<false, SNAP>(p, h, b, cur, qn, smem, dc, ln);
   } else {
     f32x16 S[4];
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     load_state(S, s0, ln.w, ln.l32, ln.g);
-    state_loop(p, h, b, cur, S, smem, dc, ln);
+    state_loop<SNAP>(p, h, b, cur, S, smem, dc, ln);
   }
 }
 
@@ -789,6 +795,7 @@ __device__ __forceinline__ void combine_states(f32x16 (&X)[4], const float *prev
   }
 }
 
+template <bool SNAP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_fused_kernel(FusedArgs fa) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -808,7 +815,7 @@ void prefill_fused_kernel(FusedArgs fa) {
   const int64_t a = (int64_t)s * p.seg_len;
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
   const int64_t DD = (int64_t)D * D;
-  const Cursor cur = first_chunk(m, a, b, T);
+  const Cursor cur = first_chunk<SNAP>(m, a, b, T);
   if (!cur.valid) return;
   char *Ks = smem, *Vs = smem + LDS_K;
   const int jf = cur.j;
@@ -869,9 +876,9 @@ void prefill_fused_kernel(FusedArgs fa) {
     }
     // 3. Outputs from the entering state.
     if (dc.fast)
-      output_loop<true>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<true, SNAP>(p, h, b, cur, qn, smem, dc, ln);
     else
-      output_loop<false>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<false, SNAP>(p, h, b, cur, qn, smem, dc, ln);
   } else {
     // 1. L = sum over the last piece of lambda^(b-1-c) k_c^T v_c.
     f32x16 S[4];
@@ -900,7 +907,7 @@ void prefill_fused_kernel(FusedArgs fa) {
       __syncthreads();
     }
     // 3. Outputs from the entering state.
-    state_loop(p, h, b, cur, S, smem, dc, ln);
+    state_loop<SNAP>(p, h, b, cur, S, smem, dc, ln);
   }
 }
 

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
   const int64_t a = (int64_t)s * p.seg_len;
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
   const int64_t DD = (int64_t)D * D;
-  Cursor cur = first_chunk(m, a, b, T);
+  Cursor cur = first_chunk<true>(m, a, b, T);
   if (!cur.valid) return;
   {
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
@@ -83,10 +83,11 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
       }
     }
     __syncthreads();
-    const Cursor nxt = next_chunk(m, cur, b, T);
+    const Cursor nxt = next_chunk<true>(m, cur, b, T);
     const bool seq_done = (cur.c1 == cur.seq_end);
     const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
-    if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
+    const bool snap_here = (cur.c1 == cur.snap);
+    if ((nxt.valid && !new_piece) || (seq_done && p.fin) || snap_here) {
       const float gL = pow_lam(log2lam, (float)L);
       for (int e = tid; e < D * D; e += NT) {
         int i = e / D, j = e - (e / D) * D;
@@ -97,6 +98,10 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
       __syncthreads();
       if (seq_done && p.fin) {
         float *dst = p.fin + ((int64_t)cur.j * H + h) * DD;
+        for (int e = tid; e < D * D; e += NT) dst[e] = (&sm.S[0][0])[e];
+      }
+      if (snap_here) {
+        float *dst = p.snaps + (snap_row(m, p.snap_off, cur) * H + h) * DD;
         for (int e = tid; e < D * D; e += NT) dst[e] = (&sm.S[0][0])[e];
       }
     }

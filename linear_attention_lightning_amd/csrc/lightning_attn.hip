@@ -167,8 +167,10 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
         hipLaunchKernelGGL(la::mfma::local_state_kernel,
                            dim3((unsigned)((pl.nseg - 1) * a.r_split * a.m.H)),
                            dim3(la::mfma::NT_LOCAL), 0, st, a);
+    } else if (a.m.snap_iv > 0) {
+      hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<true>, grid, dim3(la::mfma::NT), 0, st, a);
     } else {
-      hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, a);
+      hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<false>, grid, dim3(la::mfma::NT), 0, st, a);
     }
   } else if (dt == LA_BF16) {
     launch_simt<bf16, 64>(a, pl, st, phase_a);
@@ -218,8 +220,12 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
     pe.mark(1);
     pe.mark(2);
     la::mfma::FusedArgs fa{a, words, words + pl.nseg * H, words + pl.nseg * H + 1};
-    hipLaunchKernelGGL(la::mfma::prefill_fused_kernel, dim3((unsigned)(pl.nseg * H)),
-                       dim3(la::mfma::NT), 0, st, fa);
+    if (a.m.snap_iv > 0)
+      hipLaunchKernelGGL(la::mfma::prefill_fused_kernel<true>, dim3((unsigned)(pl.nseg * H)),
+                         dim3(la::mfma::NT), 0, st, fa);
+    else
+      hipLaunchKernelGGL(la::mfma::prefill_fused_kernel<false>, dim3((unsigned)(pl.nseg * H)),
+                         dim3(la::mfma::NT), 0, st, fa);
     pe.mark(3);
     const la_status ls = launch_status();
     return ls != LA_OK ? ls : pe.failed ? LA_ERR_HIP : LA_OK;
@@ -303,6 +309,9 @@ la_status fwd_fixed(const void *q, const void *k, const void *v, const float *de
   a.m.num_seqs = B;
   a.m.H = H;
   a.m.total = (int64_t)B * N;
+  a.m.snap_iv = 0;
+  a.snaps = nullptr;
+  a.snap_off = nullptr;
   if (layout == LA_HEAD_MAJOR) {  // [B][H][N][d]: token t of sequence j, head h at
     a.m.head_stride = N * d;      // ((j H + h) N + t) d = h N d + j (H - 1) N d + (j N + t) d
     a.m.seq_extra = (int64_t)(H - 1) * N * d;
@@ -324,8 +333,10 @@ la_status fwd_varlen(const void *q, const void *k, const void *v, const float *d
                      const int32_t *cu_seqlens, int num_seqs, int H, int64_t total_N, int d,
                      int block, la_dtype dt, la_layout layout, const float *init_states, void *out,
                      float *final_states, int64_t segment_tokens, void *workspace,
-                     size_t workspace_bytes, void *hip_stream) {
-  if (num_seqs < 0 || total_N < 0) return LA_ERR_INVALID_ARG;
+                     size_t workspace_bytes, void *hip_stream, int64_t snap_iv = 0,
+                     const int32_t *snap_off = nullptr, float *snaps = nullptr) {
+  if (num_seqs < 0 || total_N < 0 || snap_iv < 0) return LA_ERR_INVALID_ARG;
+  if (snap_iv > 0 && snap_iv <= total_N && (!snap_off || !snaps)) return LA_ERR_INVALID_ARG;
   la_status st = check_common(H, d, block, dt, segment_tokens);
   if (st == LA_OK) st = check_layout(layout, H, d);
   if (st != LA_OK) return st;
@@ -349,6 +360,10 @@ la_status fwd_varlen(const void *q, const void *k, const void *v, const float *d
   a.m.H = H;
   a.m.total = total_N;
   a.m.seq_extra = 0;
+  // An interval longer than every sequence yields no snapshot.
+  a.m.snap_iv = (snap_iv > 0 && snap_iv <= total_N) ? snap_iv : 0;
+  a.snaps = a.m.snap_iv ? snaps : nullptr;
+  a.snap_off = a.m.snap_iv ? snap_off : nullptr;
   if (layout == LA_HEAD_MAJOR) {  // [H][total_N][d]
     a.m.head_stride = total_N * d;
     a.m.rs = d;
@@ -451,6 +466,18 @@ la_status lightning_attn_fwd_varlen_layout(const void *q, const void *k, const v
   return fwd_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, block, dt, layout,
                     init_states, out, final_states, segment_tokens, workspace, workspace_bytes,
                     hip_stream);
+}
+
+la_status lightning_attn_fwd_varlen_snapshots(
+    const void *q, const void *k, const void *v, const float *decay, const int32_t *cu_seqlens,
+    int num_seqs, int H, int64_t total_N, int d, int block, la_dtype dt, la_layout layout,
+    const float *init_states, void *out, float *final_states, int64_t snapshot_interval,
+    const int32_t *snapshot_offsets, float *snapshots, int64_t segment_tokens, void *workspace,
+    size_t workspace_bytes, void *hip_stream) {
+  if (snapshot_interval < 1) return LA_ERR_INVALID_ARG;
+  return fwd_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, block, dt, layout,
+                    init_states, out, final_states, segment_tokens, workspace, workspace_bytes,
+                    hip_stream, snapshot_interval, snapshot_offsets, snapshots);
 }
 
 la_status lightning_attn_decode(const void *q, const void *k, const void *v, const float *decay,

@@ -110,6 +110,32 @@ def test_varlen_rejects_bad_arguments(lib):
     assert need > 0
 
 
+def test_varlen_snapshots_rejects_bad_arguments(lib):
+    f = lib.lightning_attn_fwd_varlen_snapshots
+    names = ["q", "k", "v", "decay", "cu", "S", "H", "total", "d", "block", "dt", "layout",
+             "init", "out", "fin", "iv", "offs", "snaps", "seg", "ws", "wsb", "stream"]
+    args = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 3, 4, 1000, 128, 128, BF16, 0, None, DUMMY, DUMMY,
+            128, DUMMY, DUMMY, 0, None, 0, None]
+
+    def call(**kw):
+        a = list(args)
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+
+    assert call(iv=0) == INVALID
+    assert call(iv=-5) == INVALID
+    assert call(snaps=None) == INVALID
+    assert call(offs=None) == INVALID
+    # an interval beyond every sequence stores nothing: buffers may be NULL
+    # (then only the workspace is missing here)
+    assert call(iv=1001, snaps=None, offs=None) == WORKSPACE
+    assert call(layout=2) == UNSUPPORTED
+    assert call(d=32) == UNSUPPORTED
+    assert call() == WORKSPACE
+    assert call(S=0, total=0) == OK
+
+
 def test_decode_rejects_bad_arguments(lib):
     f = lib.lightning_attn_decode
     base = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 2, 4, 128, BF16, None]

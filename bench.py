@@ -8,7 +8,8 @@ inputs already resident in HBM.  W untimed steps, then K steps timed with
 HIP events on the stream the library launches on.  Prints ONE JSON line:
 the headline tokens/s, TFLOP/s and fraction of the bf16 MFMA peak, the HBM
 roofline of the step, the CPU oracle timed on a bounded sample, and (unless
---no-extras) the decode, packed varlen and million-token workloads.
+--no-extras) the decode, packed varlen, million-token, token-major, prefix-snapshot
+and mixed serving-step workloads.
 """
 import argparse
 import hashlib
@@ -234,6 +235,135 @@ def bench_decode(la, inputs, reps, warmup):
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def bench_snapshots(la, inputs, steps, warmup, interval=256):
+    """The packed 65536-token workload with a prefix-state snapshot every
+    `interval` tokens of each sequence (a prefix cache): time per step, and
+    the snapshot bytes it adds to the algorithmic traffic."""
+    import torch
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["layer_h64_varlen64k"]
+    H, total, d, block = w["H"], w["total"], w["d"], w["block"]
+    lens = inputs.varlen_lengths(total=total, seed=w["seed"])
+    cu = torch.from_numpy(inputs.cu_seqlens(lens)).to(dev)
+    q, k, v = inputs.device_qkv((H, total, d), w["seed"], "bf16", device=dev)
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    out = torch.empty_like(q)
+    fin = torch.empty((len(lens), H, d, d), dtype=torch.float32, device=dev)
+    nws = la.lightning_attn_fwd_varlen_workspace_size(len(lens), H, total, d, block)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    offs = la.snapshot_row_offsets(cu, interval)
+    toffs = torch.tensor(offs, dtype=torch.int32, device=dev)
+    snaps = torch.empty((offs[-1], H, d, d), dtype=torch.float32, device=dev)
+
+    def step():
+        la.lightning_attn_fwd_varlen_snapshots(q, k, v, decay, cu, interval, block=block,
+                                               out=out, final_states=fin, snapshots=snaps,
+                                               snapshot_offsets=toffs, workspace=ws)
+
+    ms = time_steps(step, steps, warmup, torch.cuda.current_stream(dev))
+    snap_bytes = offs[-1] * H * d * d * 4
+    byt = H * total * d * 8 + len(lens) * H * d * d * 4 + snap_bytes
+    return {"workload": "layer_h64_varlen64k", "snapshot_interval": interval,
+            "snapshot_rows": offs[-1], "snapshot_bytes": snap_bytes,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(total / (ms * 1e-3), 1),
+            "hbm_gbs_algorithmic": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def bench_serving(la, inputs, reps=200, P=50):
+    """A mixed serving step at the 64-head layer shape: 20 sequences with
+    prefix states, two continuing with P new tokens and eighteen decoding one.
+    Variants: the P-token prefill alone, the decode alone, both on one stream,
+    both on two streams (lightning_attn_mixed_step), and all twenty sequences
+    as one packed prefill.  Prefills take one segment per sequence.  Two
+    timings in microseconds per step: `eager` (median of single steps, each
+    launched from Python and synchronised, so host launch gaps count) and
+    `graph` (the step captured once as a HIP graph and replayed `reps` times
+    back to back)."""
+    import torch
+    dev = torch.device("cuda:0")
+    H, d, B = 64, 128, 18
+    seg = la.LA_SEGMENT_PER_SEQUENCE
+    plens = [P, P]
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    cu = torch.from_numpy(inputs.cu_seqlens(plens)).to(dev)
+    pq, pk, pv = inputs.device_qkv((H, sum(plens), d), 401, "bf16", device=dev)
+    dq, dk, dv = inputs.device_qkv((B, H, d), 402, "bf16", device=dev)
+    pinit = inputs.device_state((len(plens), H, d, d), 403, device=dev)
+    dstate0 = inputs.device_state((B, H, d, d), 404, device=dev)
+    dstate = dstate0.clone()
+    pout, pfin = torch.empty_like(pq), torch.empty_like(pinit)
+    dout = torch.empty_like(dq)
+    # all twenty as one packed prefill (decode tokens as 1-token sequences)
+    alens = plens + [1] * B
+    acu = torch.from_numpy(inputs.cu_seqlens(alens)).to(dev)
+    aq, ak, av = (torch.cat([x, y.transpose(0, 1)], dim=1).contiguous()
+                  for x, y in ((pq, dq), (pk, dk), (pv, dv)))
+    ainit = torch.cat([pinit, dstate0], dim=0).contiguous()
+    aout, afin = torch.empty_like(aq), torch.empty_like(ainit)
+    side = torch.cuda.Stream(device=dev)
+
+    def prefill():
+        la.lightning_attn_fwd_varlen(pq, pk, pv, decay, cu, init_states=pinit, out=pout,
+                                     final_states=pfin, segment_tokens=seg)
+
+    def decode():
+        la.lightning_attn_decode(dq, dk, dv, decay, dstate, out=dout)
+
+    def serial():
+        la.lightning_attn_mixed_step(decay, (pq, pk, pv), cu, (dq, dk, dv), dstate,
+                                     init_states=pinit, prefill_out=pout, final_states=pfin,
+                                     decode_out=dout, segment_tokens=seg)
+
+    def two_streams():
+        cur = torch.cuda.current_stream(dev)
+        side.wait_stream(cur)
+        la.lightning_attn_mixed_step(decay, (pq, pk, pv), cu, (dq, dk, dv), dstate,
+                                     init_states=pinit, prefill_out=pout, final_states=pfin,
+                                     decode_out=dout, segment_tokens=seg, decode_stream=side)
+        cur.wait_stream(side)
+
+    def one_varlen():
+        la.lightning_attn_fwd_varlen(aq, ak, av, decay, acu, init_states=ainit, out=aout,
+                                     final_states=afin, segment_tokens=seg)
+
+    res = {"workload": "serving_mix_h64", "H": H, "d": d,
+           "batch": "2 sequences x %d new tokens + 18 x 1 token, all from prefix states" % P,
+           "unit": "us per step"}
+    for name, fn in (("prefill_only", prefill), ("decode_only", decode),
+                     ("one_stream", serial), ("two_streams", two_streams),
+                     ("one_packed_prefill", one_varlen)):
+        for _ in range(5):  # warm-up (and lazy initialisation) outside the capture
+            fn()
+        torch.cuda.synchronize()
+        eager = []
+        for _ in range(50):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            eager.append(s.elapsed_time(e) * 1e3)
+        eager.sort()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(20):
+            g.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        res[name] = {"eager": round(eager[len(eager) // 2], 2),
+                     "graph": round(s.elapsed_time(e) * 1e3 / reps, 2)}
+        del g
+    dstate.copy_(dstate0)
+    return res
+
+
 def cpu_baseline(gpu_tensors, H, N, d, heads):
     """The oracle (untuned) on the host cores: `heads` of the H heads, all N
     tokens, on the same inputs; scaled to whole-workload tokens/s."""
@@ -350,6 +480,12 @@ def main():
         res["million"] = bench_million(la, inputs, steps=5, warmup=1)
         torch.cuda.empty_cache()
         res["token_major"] = bench_token_major(la, inputs, steps=args.steps, warmup=args.warmup)
+        torch.cuda.empty_cache()
+        res["snapshots"] = bench_snapshots(la, inputs, steps=max(5, args.steps // 2), warmup=2)
+        torch.cuda.empty_cache()
+        res["serving"] = bench_serving(la, inputs, P=50)
+        torch.cuda.empty_cache()
+        res["serving_long"] = bench_serving(la, inputs, P=2048)
     print(json.dumps(res), flush=True)
 
 

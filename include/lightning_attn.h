@@ -67,6 +67,14 @@ typedef enum {
 
 typedef enum { LA_FP32 = 0, LA_BF16 = 1 } la_dtype;
 
+/* segment_tokens value of the prefill entry points: every sequence is one
+ * segment, walked by one workgroup per head.  No state crosses a segment,
+ * so the output pass is the only launch and no workspace is needed (the
+ * workspace size queries return 0).  The choice for batches of many short
+ * sequences (serving), whose cost is the launch chain, not the arithmetic;
+ * a long sequence is then walked by a single workgroup per head. */
+enum { LA_SEGMENT_PER_SEQUENCE = -1 };
+
 /* Memory layout of q, k, v and out for the *_layout entry points (the other
  * prefill entry points take LA_HEAD_MAJOR).  LA_TOKEN_MAJOR is the layout a
  * projection produces ([B][N][H*d], heads side by side in each token row),
@@ -104,17 +112,20 @@ const char *lightning_attn_last_hip_error(void);
  *   init_state   : [B][H][d][d] float32, or NULL for a zero initial state.
  *   final_state  : [B][H][d][d] float32 state after token N-1 (equal to the
  *                  initial state when N == 0), or NULL if not wanted.
- *   segment_tokens: 0 = automatic.  Otherwise the length, in tokens, of the
- *                  independent segments the token axis is cut into (results
- *                  are identical up to rounding for every value).  A value
- *                  equal to N keeps every sequence in one segment and needs
- *                  no workspace.
+ *   segment_tokens: 0 = automatic.  LA_SEGMENT_PER_SEQUENCE: every
+ *                  sequence is one segment (for fixed lengths the same as N).
+ *                  Otherwise the length, in tokens, of the independent
+ *                  segments the token axis is cut into (results are
+ *                  identical up to rounding for every value).  A value equal
+ *                  to N keeps every sequence in one segment and needs no
+ *                  workspace.
  *   workspace    : device scratch of at least
  *                  lightning_attn_fwd_workspace_size(...) bytes (may be NULL
  *                  when that size is 0).  Its contents on entry do not matter.
  *
  * B, H >= 0, N >= 0, d in {64, 128}.  B*H == 0 is a no-op.  q, k, v, out may
- * be NULL only when N == 0.
+ * be NULL only when N == 0.  Returns LA_ERR_INVALID_ARG for a negative
+ * segment_tokens other than LA_SEGMENT_PER_SEQUENCE.
  */
 size_t lightning_attn_fwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
                                          int64_t segment_tokens);
@@ -181,6 +192,9 @@ la_status lightning_attn_fwd_layout(const void *q, const void *k, const void *v,
  *                  Zero-length sequences are allowed.
  *   init_states  : [num_seqs][H][d][d] float32 or NULL (zero).
  *   final_states : [num_seqs][H][d][d] float32 or NULL.
+ *   segment_tokens: as for lightning_attn_fwd; segments are cut on the
+ *                  concatenated token axis (they may start inside a
+ *                  sequence), except with LA_SEGMENT_PER_SEQUENCE.
  *   Other arguments as for lightning_attn_fwd.
  */
 size_t lightning_attn_fwd_varlen_workspace_size(int num_seqs, int H, int64_t total_N, int d,
@@ -266,6 +280,43 @@ la_status lightning_attn_fwd_varlen_snapshots(
 la_status lightning_attn_decode(const void *q, const void *k, const void *v, const float *decay,
                                 float *state, void *out, int B, int H, int d, la_dtype dt,
                                 void *hip_stream);
+
+/*
+ * One step of a mixed serving batch (MiniMax-01 report, section 3.3.2:
+ * inputs of one token are memory-bound and need few compute units, so they
+ * go to a kernel of their own, separate from the inputs of more than one
+ * token, and the two kernels run in parallel on two streams; section 3.3.1
+ * for the fused decode state update).  The caller splits its batch:
+ *
+ *   prefill part : sequences with more than one new token (or with a prefix
+ *                  to continue), as for lightning_attn_fwd_varlen_layout:
+ *                  prefill_q/k/v/out, cu_seqlens, num_seqs, total_N, layout,
+ *                  init_states (e.g. prefix-cache snapshots), final_states,
+ *                  segment_tokens and the workspace.  Launched on
+ *                  prefill_stream.
+ *   decode part  : decode_B sequences with one new token each, as for
+ *                  lightning_attn_decode: decode_q/k/v/out [decode_B][H][d],
+ *                  decode_state [decode_B][H][d][d] updated in place.
+ *                  Launched on decode_stream.
+ *   decay, H, d, block, dt are shared by both parts.
+ *
+ * The two parts must not share any output buffer; either may be empty
+ * (num_seqs == 0 and total_N == 0, or decode_B == 0).  The streams may be
+ * the same (the parts then run one after the other) or different (they run
+ * concurrently); the call returns once both parts are launched, and the
+ * caller synchronises each stream it passed.  Both parts are validated
+ * before anything is launched: any invalid argument launches nothing.
+ * Returns the first failing part's status, as the two entry points above
+ * define them.
+ */
+la_status lightning_attn_mixed_step(
+    const void *prefill_q, const void *prefill_k, const void *prefill_v,
+    const int32_t *cu_seqlens, int num_seqs, int64_t total_N, la_layout layout,
+    const float *init_states, void *prefill_out, float *final_states, int64_t segment_tokens,
+    void *workspace, size_t workspace_bytes, void *prefill_stream, const void *decode_q,
+    const void *decode_k, const void *decode_v, float *decode_state, void *decode_out,
+    int decode_B, void *decode_stream, const float *decay, int H, int d, int block,
+    la_dtype dt);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
   lightning_attn_fwd_varlen_snapshots(q, k, v, decay, cu_seqlens, snapshot_interval, ...)
       -> (out, final_states, snapshots, snapshot_offsets)
   lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
+  lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode_state, ...)
+      -> (prefill_out, final_states, decode_out)   (decode_state updated in place)
 """
 import ctypes
 import os
@@ -23,7 +25,8 @@ import os
 __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd_layout",
            "lightning_attn_fwd_varlen", "lightning_attn_fwd_varlen_layout",
            "lightning_attn_fwd_varlen_snapshots", "snapshot_row_offsets", "lightning_attn_decode",
-           "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR",
+           "lightning_attn_mixed_step",
+           "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
 
@@ -31,6 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightnin
 
 LA_FP32, LA_BF16 = 0, 1
 LA_HEAD_MAJOR, LA_TOKEN_MAJOR = 0, 1  # la_layout
+LA_SEGMENT_PER_SEQUENCE = -1          # segment_tokens: one segment per sequence
 _STATUS = {0: "LA_OK", 1: "LA_ERR_INVALID_ARG", 2: "LA_ERR_UNSUPPORTED", 3: "LA_ERR_WORKSPACE",
            4: "LA_ERR_HIP"}
 
@@ -83,6 +87,9 @@ def load_library(path=None):
     lib.lightning_attn_fwd_varlen_snapshots.argtypes = [P, P, P, P, P, I, I, L, I, I, I, I, P, P,
                                                         P, L, P, P, L, P, Z, P]
     lib.lightning_attn_fwd_varlen_snapshots.restype = I
+    lib.lightning_attn_mixed_step.argtypes = [P, P, P, P, I, L, I, P, P, P, L, P, Z, P,
+                                              P, P, P, P, P, I, P, P, I, I, I, I]
+    lib.lightning_attn_mixed_step.restype = I
     lib.lightning_attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
     lib.lightning_attn_decode.restype = I
     if path is None:
@@ -354,3 +361,73 @@ def lightning_attn_decode(q, k, v, decay, state, out=None):
     if st != 0:
         raise LightningAttnError(st, "lightning_attn_decode")
     return out
+
+
+def lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode_state,
+                              layout=LA_HEAD_MAJOR, block=128, init_states=None,
+                              segment_tokens=0, prefill_out=None, final_states=None,
+                              decode_out=None, workspace=None, prefill_stream=None,
+                              decode_stream=None):
+    """One mixed serving step: packed prefill of the sequences with several
+    new tokens (prefill_qkv: q, k, v [H, total, d], or [total, H, d] for
+    LA_TOKEN_MAJOR; cu_seqlens int32 [num_seqs + 1]) on prefill_stream, and
+    one decode step of decode_B single-token sequences (decode_qkv: q, k, v
+    [decode_B, H, d]; decode_state [decode_B, H, d, d] float32, updated in
+    place) on decode_stream, launched back to back so that they run
+    concurrently.  Streams are torch.cuda.Stream objects (default: the
+    current stream).  Returns (prefill_out, final_states, decode_out); the
+    caller waits on both streams before using them."""
+    torch = _torch()
+    lib = load_library()
+    pq, pk, pv = prefill_qkv
+    dq, dk, dv = decode_qkv
+    if layout == LA_TOKEN_MAJOR:
+        total, H, d = pq.shape
+    elif layout == LA_HEAD_MAJOR:
+        H, total, d = pq.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
+    dev = pq.device
+    for t, n in ((pk, "prefill k"), (pv, "prefill v"), (pq, "prefill q")):
+        _check(t, n, pq.shape, pq.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 offsets")
+    S = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32, dev)
+    B = dq.shape[0]
+    for t, n in ((dk, "decode k"), (dv, "decode v"), (dq, "decode q")):
+        _check(t, n, (B, H, d), pq.dtype, dev)
+    _check(decode_state, "decode_state", (B, H, d, d), torch.float32, dev)
+    if init_states is not None:
+        _check(init_states, "init_states", (S, H, d, d), torch.float32, dev)
+    cur = torch.cuda.current_stream(dev)
+    ps = prefill_stream or cur
+    ds = decode_stream or cur
+    if prefill_out is None:
+        prefill_out = torch.empty_like(pq)
+    if final_states is None:
+        final_states = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    if decode_out is None:
+        decode_out = torch.empty_like(dq)
+    _check(prefill_out, "prefill_out", pq.shape, pq.dtype, dev)
+    _check(final_states, "final_states", (S, H, d, d), torch.float32, dev)
+    _check(decode_out, "decode_out", dq.shape, dq.dtype, dev)
+    dt = _dtype_code(pq)
+    ws_bytes = lib.lightning_attn_fwd_varlen_workspace_size(S, H, total, d, block, dt,
+                                                            segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    # tensors made here on the current stream and used on another one
+    for t, s_ in ((prefill_out, ps), (final_states, ps), (workspace, ps), (decode_out, ds)):
+        if t is not None and s_ != cur:
+            t.record_stream(s_)
+    st = lib.lightning_attn_mixed_step(
+        _ptr(pq), _ptr(pk), _ptr(pv), _ptr(cu_seqlens), S, total, layout, _ptr(init_states),
+        _ptr(prefill_out), _ptr(final_states), segment_tokens, _ptr(workspace), ws_have,
+        ctypes.c_void_p(ps.cuda_stream), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(decode_state),
+        _ptr(decode_out), B, ctypes.c_void_p(ds.cuda_stream), _ptr(decay), H, d, block, dt)
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_mixed_step")
+    return prefill_out, final_states, decode_out

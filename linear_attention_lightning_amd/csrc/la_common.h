@@ -167,7 +167,7 @@ struct FwdArgs {
   void *out;
   const float *decay;
   SeqMap m;
-  int64_t seg_len;   // segment length in tokens
+  int64_t seg_len;   // segment length in tokens; 0: segment s is sequence s
   int nseg;          // segments per head
   const float *init; // [S][H][d][d] or nullptr
   float *fin;        // [S][H][d][d] or nullptr
@@ -177,6 +177,18 @@ struct FwdArgs {
   float *snaps;      // prefix-state snapshots [rows][H][d][d] (m.snap_iv > 0), else nullptr
   const int32_t *snap_off;  // [num_seqs + 1]: first snapshot row of each sequence
 };
+
+// Tokens [*a, *b) of segment s: equal cuts of the token axis, or sequence s
+// itself when seg_len is 0 (then no segment starts inside a sequence).
+__device__ __forceinline__ void segment_bounds(const FwdArgs &p, int s, int64_t *a, int64_t *b) {
+  if (p.seg_len == 0) {
+    *a = p.m.start(s);
+    *b = p.m.start(s + 1);
+  } else {
+    *a = (int64_t)s * p.seg_len;
+    *b = (*a + p.seg_len < p.m.total) ? *a + p.seg_len : p.m.total;
+  }
+}
 
 // Piece r of R of a local-state range [ps, b) cut into chunks of C tokens
 // aligned to ps: chunks [r n / R, (r + 1) n / R) of its n chunks, as tokens

@@ -696,8 +696,10 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 
 // Phase C: outputs (and final states) for one (segment, head), from the
 // segment's entering state (scan result, initial state or zero).
-// SNAP: the walk also stores prefix-state snapshots (p.m.snap_iv > 0).
-template <bool SNAP>
+// SERVE: the serving variant: the walk also stores prefix-state snapshots
+// (when p.m.snap_iv > 0) and takes one segment per sequence (when
+// p.seg_len == 0).  Without it the kernel keeps the plain walk's registers.
+template <bool SERVE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_chunk_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -706,26 +708,39 @@ void prefill_chunk_kernel(FwdArgs p) {
   const int H = m.H;
   const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
   const Decay dc(p.decay[h]);
-  const int64_t a = (int64_t)s * p.seg_len;
-  const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
+  int64_t a, b;
+  if (SERVE) {
+    segment_bounds(p, s, &a, &b);
+  } else {
+    a = (int64_t)s * p.seg_len;
+    b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
+  }
   const int64_t DD = (int64_t)D * D;
-  const Cursor cur = first_chunk<SNAP>(m, a, b, T);
-  if (!cur.valid) return;
+  const Cursor cur = first_chunk<SERVE>(m, a, b, T);
+  if (!cur.valid) {
+    // One segment per sequence: an empty sequence keeps its initial state.
+    if (SERVE && p.seg_len == 0 && p.fin) {
+      float *dst = p.fin + ((int64_t)s * H + h) * DD;
+      const float *src = p.init ? p.init + ((int64_t)s * H + h) * DD : nullptr;
+      for (int e = threadIdx.x; e < D * D; e += NT) dst[e] = src ? src[e] : 0.f;
+    }
+    return;
+  }
   if (ln.out_wave) {
     u32x4 qn[2][4];
     const OutLane o(ln.lane, ln.w);
     issue_q_loads(p, h, cur, 0, qn[0], o);
     issue_q_loads(p, h, cur, 1, qn[1], o);
     if (dc.fast)
-      output_loop<true, SNAP>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<true, SERVE>(p, h, b, cur, qn, smem, dc, ln);
     else
-      output_loop<false, SNAP>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<false, SERVE>(p, h, b, cur, qn, smem, dc, ln);
   } else {
     f32x16 S[4];
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     load_state(S, s0, ln.w, ln.l32, ln.g);
-    state_loop<SNAP>(p, h, b, cur, S, smem, dc, ln);
+    state_loop<SERVE>(p, h, b, cur, S, smem, dc, ln);
   }
 }
 

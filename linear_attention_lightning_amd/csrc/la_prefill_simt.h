@@ -40,11 +40,19 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
   const int H = m.H;
   const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
   const float log2lam = log2f(p.decay[h]);
-  const int64_t a = (int64_t)s * p.seg_len;
-  const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
+  int64_t a, b;
+  segment_bounds(p, s, &a, &b);
   const int64_t DD = (int64_t)D * D;
   Cursor cur = first_chunk<true>(m, a, b, T);
-  if (!cur.valid) return;
+  if (!cur.valid) {
+    // One segment per sequence: an empty sequence keeps its initial state.
+    if (p.seg_len == 0 && p.fin) {
+      float *dst = p.fin + ((int64_t)s * H + h) * DD;
+      const float *src = p.init ? p.init + ((int64_t)s * H + h) * DD : nullptr;
+      for (int e = tid; e < D * D; e += NT) dst[e] = src ? src[e] : 0.f;
+    }
+    return;
+  }
   {
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);

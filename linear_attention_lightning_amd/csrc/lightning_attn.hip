@@ -88,7 +88,11 @@ size_t phased_ws_bytes(const Plan &p, int H, int d) {
   return state_bytes(p.nseg * p.r_split * H, d);
 }
 
+// segment_tokens value: every sequence is one segment (see lightning_attn.h).
+constexpr int64_t kSegPerSeq = -1;
+
 Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tokens) {
+  if (segment_tokens == kSegPerSeq) segment_tokens = N;  // N == 0: automatic (nothing to cut)
   Plan p{N, B, false, false, 1, 0};
   const int64_t total = (int64_t)B * N;
   if (total == 0) {
@@ -120,7 +124,14 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
   return p;
 }
 
-Plan plan_varlen(int H, int64_t total, int d, la_dtype dt, int64_t segment_tokens) {
+// Packed plan.  Equal cuts of the token axis (seg > 0), with the segment
+// scan handing states across cuts; or, for kSegPerSeq, one segment per
+// sequence (seg == 0): no hand-off, so no local-state pass, no scan and no
+// workspace, and the output pass alone is launched (it also gives empty
+// sequences their final state).
+Plan plan_varlen(int num_seqs, int H, int64_t total, int d, la_dtype dt,
+                 int64_t segment_tokens) {
+  if (segment_tokens == kSegPerSeq) return Plan{0, num_seqs, false, false, 1, 0};
   Plan p{1, 0, true, false, 1, 0};
   if (total == 0) return p;
   const int T = chunk_tokens(d, dt);
@@ -167,7 +178,7 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
         hipLaunchKernelGGL(la::mfma::local_state_kernel,
                            dim3((unsigned)((pl.nseg - 1) * a.r_split * a.m.H)),
                            dim3(la::mfma::NT_LOCAL), 0, st, a);
-    } else if (a.m.snap_iv > 0) {
+    } else if (a.m.snap_iv > 0 || a.seg_len == 0) {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<true>, grid, dim3(la::mfma::NT), 0, st, a);
     } else {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<false>, grid, dim3(la::mfma::NT), 0, st, a);
@@ -266,7 +277,7 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
 }
 
 la_status check_common(int H, int d, int block, la_dtype dt, int64_t segment_tokens) {
-  if (H < 0 || segment_tokens < 0) return LA_ERR_INVALID_ARG;
+  if (H < 0 || (segment_tokens < 0 && segment_tokens != kSegPerSeq)) return LA_ERR_INVALID_ARG;
   if (!valid_dtype(dt) || !valid_d(d) || !valid_block(block)) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
@@ -329,12 +340,22 @@ la_status fwd_fixed(const void *q, const void *k, const void *v, const float *de
   return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream, phase_events);
 }
 
-la_status fwd_varlen(const void *q, const void *k, const void *v, const float *decay,
-                     const int32_t *cu_seqlens, int num_seqs, int H, int64_t total_N, int d,
-                     int block, la_dtype dt, la_layout layout, const float *init_states, void *out,
-                     float *final_states, int64_t segment_tokens, void *workspace,
-                     size_t workspace_bytes, void *hip_stream, int64_t snap_iv = 0,
-                     const int32_t *snap_off = nullptr, float *snaps = nullptr) {
+// A validated packed prefill, ready to launch.
+struct VarlenCall {
+  la::FwdArgs a;
+  Plan pl;
+  int d;
+  la_dtype dt;
+  bool launch;  // false: nothing to do
+};
+
+la_status prep_varlen(const void *q, const void *k, const void *v, const float *decay,
+                      const int32_t *cu_seqlens, int num_seqs, int H, int64_t total_N, int d,
+                      int block, la_dtype dt, la_layout layout, const float *init_states,
+                      void *out, float *final_states, int64_t segment_tokens, void *workspace,
+                      size_t workspace_bytes, int64_t snap_iv, const int32_t *snap_off,
+                      float *snaps, VarlenCall *c) {
+  c->launch = false;
   if (num_seqs < 0 || total_N < 0 || snap_iv < 0) return LA_ERR_INVALID_ARG;
   if (snap_iv > 0 && snap_iv <= total_N && (!snap_off || !snaps)) return LA_ERR_INVALID_ARG;
   la_status st = check_common(H, d, block, dt, segment_tokens);
@@ -344,11 +365,11 @@ la_status fwd_varlen(const void *q, const void *k, const void *v, const float *d
   if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
   if (total_N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_varlen(H, total_N, d, dt, segment_tokens);
+  const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
-  la::FwdArgs a;
+  la::FwdArgs &a = c->a;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -376,7 +397,63 @@ la_status fwd_varlen(const void *q, const void *k, const void *v, const float *d
   a.init = init_states;
   a.fin = final_states;
   a.ws = (float *)workspace;
-  return run_fwd(a, pl, d, dt, /*has_empty=*/true, (hipStream_t)hip_stream);
+  c->pl = pl;
+  c->d = d;
+  c->dt = dt;
+  c->launch = true;
+  return LA_OK;
+}
+
+// Zero-length sequences get their final state from the scan kernel, except
+// with one segment per sequence, where the output pass writes it.
+bool varlen_has_empty(const Plan &pl) { return pl.seg != 0; }
+
+la_status fwd_varlen(const void *q, const void *k, const void *v, const float *decay,
+                     const int32_t *cu_seqlens, int num_seqs, int H, int64_t total_N, int d,
+                     int block, la_dtype dt, la_layout layout, const float *init_states, void *out,
+                     float *final_states, int64_t segment_tokens, void *workspace,
+                     size_t workspace_bytes, void *hip_stream, int64_t snap_iv = 0,
+                     const int32_t *snap_off = nullptr, float *snaps = nullptr) {
+  VarlenCall c;
+  const la_status st = prep_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, block, dt,
+                                   layout, init_states, out, final_states, segment_tokens,
+                                   workspace, workspace_bytes, snap_iv, snap_off, snaps, &c);
+  if (st != LA_OK || !c.launch) return st;
+  return run_fwd(c.a, c.pl, c.d, c.dt, varlen_has_empty(c.pl), (hipStream_t)hip_stream);
+}
+
+// Decode: validation, then the launch.
+la_status check_decode(const void *q, const void *k, const void *v, const float *decay,
+                       const float *state, const void *out, int B, int H, int d, la_dtype dt) {
+  if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+  if (!valid_dtype(dt) || !valid_d(d)) return LA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H == 0) return LA_OK;
+  if (!q || !k || !v || !decay || !state || !out) return LA_ERR_INVALID_ARG;
+  if ((int64_t)B * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+void launch_decode(const void *q, const void *k, const void *v, const float *decay, float *state,
+                   void *out, int B, int H, int d, la_dtype dt, hipStream_t st) {
+  if ((int64_t)B * H == 0) return;
+  dim3 grid((unsigned)((int64_t)B * H));
+  if (dt == LA_BF16) {
+    if (d == 128)
+      hipLaunchKernelGGL((la::decode_kernel<bf16, 128>), grid, dim3(256), 0, st, (const bf16 *)q,
+                         (const bf16 *)k, (const bf16 *)v, decay, state, (bf16 *)out, H);
+    else
+      hipLaunchKernelGGL((la::decode_kernel<bf16, 64>), grid, dim3(256), 0, st, (const bf16 *)q,
+                         (const bf16 *)k, (const bf16 *)v, decay, state, (bf16 *)out, H);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((la::decode_kernel<float, 128>), grid, dim3(256), 0, st,
+                         (const float *)q, (const float *)k, (const float *)v, decay, state,
+                         (float *)out, H);
+    else
+      hipLaunchKernelGGL((la::decode_kernel<float, 64>), grid, dim3(256), 0, st,
+                         (const float *)q, (const float *)k, (const float *)v, decay, state,
+                         (float *)out, H);
+  }
 }
 
 }  // namespace
@@ -441,7 +518,7 @@ size_t lightning_attn_fwd_varlen_workspace_size(int num_seqs, int H, int64_t tot
   if (num_seqs < 0 || total_N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK)
     return 0;
   if ((int64_t)num_seqs * H == 0) return 0;
-  return plan_varlen(H, total_N, d, dt, segment_tokens).ws_bytes;
+  return plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens).ws_bytes;
 }
 
 la_status lightning_attn_fwd_varlen(const void *q, const void *k, const void *v,
@@ -483,31 +560,44 @@ la_status lightning_attn_fwd_varlen_snapshots(
 la_status lightning_attn_decode(const void *q, const void *k, const void *v, const float *decay,
                                 float *state, void *out, int B, int H, int d, la_dtype dt,
                                 void *hip_stream) {
-  if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
-  if (!valid_dtype(dt) || !valid_d(d)) return LA_ERR_UNSUPPORTED;
+  const la_status st = check_decode(q, k, v, decay, state, out, B, H, d, dt);
+  if (st != LA_OK) return st;
   if ((int64_t)B * H == 0) return LA_OK;
-  if (!q || !k || !v || !decay || !state || !out) return LA_ERR_INVALID_ARG;
-  if ((int64_t)B * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
-  hipStream_t st = (hipStream_t)hip_stream;
-  dim3 grid((unsigned)((int64_t)B * H));
-  if (dt == LA_BF16) {
-    if (d == 128)
-      hipLaunchKernelGGL((la::decode_kernel<bf16, 128>), grid, dim3(256), 0, st, (const bf16 *)q,
-                         (const bf16 *)k, (const bf16 *)v, decay, state, (bf16 *)out, H);
-    else
-      hipLaunchKernelGGL((la::decode_kernel<bf16, 64>), grid, dim3(256), 0, st, (const bf16 *)q,
-                         (const bf16 *)k, (const bf16 *)v, decay, state, (bf16 *)out, H);
-  } else {
-    if (d == 128)
-      hipLaunchKernelGGL((la::decode_kernel<float, 128>), grid, dim3(256), 0, st,
-                         (const float *)q, (const float *)k, (const float *)v, decay, state,
-                         (float *)out, H);
-    else
-      hipLaunchKernelGGL((la::decode_kernel<float, 64>), grid, dim3(256), 0, st,
-                         (const float *)q, (const float *)k, (const float *)v, decay, state,
-                         (float *)out, H);
-  }
+  launch_decode(q, k, v, decay, state, out, B, H, d, dt, (hipStream_t)hip_stream);
   return launch_status();
+}
+
+la_status lightning_attn_mixed_step(
+    const void *prefill_q, const void *prefill_k, const void *prefill_v,
+    const int32_t *cu_seqlens, int num_seqs, int64_t total_N, la_layout layout,
+    const float *init_states, void *prefill_out, float *final_states, int64_t segment_tokens,
+    void *workspace, size_t workspace_bytes, void *prefill_stream, const void *decode_q,
+    const void *decode_k, const void *decode_v, float *decode_state, void *decode_out,
+    int decode_B, void *decode_stream, const float *decay, int H, int d, int block,
+    la_dtype dt) {
+  // Both parts are validated before either launches.
+  VarlenCall c;
+  la_status st = prep_varlen(prefill_q, prefill_k, prefill_v, decay, cu_seqlens, num_seqs, H,
+                             total_N, d, block, dt, layout, init_states, prefill_out,
+                             final_states, segment_tokens, workspace, workspace_bytes, 0,
+                             nullptr, nullptr, &c);
+  if (st != LA_OK) return st;
+  st = check_decode(decode_q, decode_k, decode_v, decay, decode_state, decode_out, decode_B, H, d,
+                    dt);
+  if (st != LA_OK) return st;
+  // The prefill chain (up to three launches) goes first so that it starts
+  // at once; the decode kernel's many small workgroups fill the CUs the
+  // prefill leaves free.
+  la_status sp = LA_OK;
+  if (c.launch)
+    sp = run_fwd(c.a, c.pl, c.d, c.dt, varlen_has_empty(c.pl), (hipStream_t)prefill_stream);
+  la_status sd = LA_OK;
+  if ((int64_t)decode_B * H > 0) {
+    launch_decode(decode_q, decode_k, decode_v, decay, decode_state, decode_out, decode_B, H, d,
+                  dt, (hipStream_t)decode_stream);
+    sd = launch_status();
+  }
+  return sp != LA_OK ? sp : sd;
 }
 
 }  // extern "C"

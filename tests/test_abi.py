@@ -61,7 +61,7 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, B=-1) == INVALID
     assert fwd(lib, N=-5) == INVALID
     assert fwd(lib, H=-2) == INVALID
-    assert fwd(lib, seg=-1) == INVALID
+    assert fwd(lib, seg=-2) == INVALID  # -1 is LA_SEGMENT_PER_SEQUENCE
     assert fwd(lib, q=None) == INVALID
     assert fwd(lib, out=None) == INVALID
     assert fwd(lib, decay=None) == INVALID
@@ -78,6 +78,9 @@ def test_fwd_workspace_checks(lib):
     assert fwd(lib, H=8, N=1 << 20, block=256, ws=None, wsb=0) == WORKSPACE
     assert fwd(lib, H=8, N=1 << 20, block=256, ws=DUMMY, wsb=need - 1) == WORKSPACE
     # one segment per sequence needs none
+    assert lib.lightning_attn_fwd_workspace_size(1, 8, 1 << 20, 128, 256, BF16, -1) == 0
+    assert lib.lightning_attn_fwd_varlen_workspace_size(9, 64, 65536, 128, 128, BF16, -1) == 0
+    assert lib.lightning_attn_fwd_varlen_workspace_size(9, 64, 65536, 128, 128, BF16, -2) == 0
     assert lib.lightning_attn_fwd_workspace_size(4, 64, 4096, 128, 128, BF16, 4096) == 0
     # explicit segment lengths
     n = lib.lightning_attn_fwd_workspace_size(1, 2, 1000, 64, 64, FP32, 256)
@@ -134,6 +137,33 @@ def test_varlen_snapshots_rejects_bad_arguments(lib):
     assert call(d=32) == UNSUPPORTED
     assert call() == WORKSPACE
     assert call(S=0, total=0) == OK
+
+
+def test_mixed_step_rejects_bad_arguments(lib):
+    """Either part's invalid argument fails the call before anything is
+    launched (the stream handles here are never used)."""
+    f = lib.lightning_attn_mixed_step
+    names = ["pq", "pk", "pv", "cu", "S", "total", "layout", "init", "pout", "fin", "seg", "ws",
+             "wsb", "pstream", "dq", "dk", "dv", "dstate", "dout", "B", "dstream", "decay", "H",
+             "d", "block", "dt"]
+    args = [DUMMY, DUMMY, DUMMY, DUMMY, 2, 100, 0, None, DUMMY, DUMMY, 0, DUMMY, 1 << 30, None,
+            DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 18, None, DUMMY, 8, 128, 128, BF16]
+
+    def call(**kw):
+        a = list(args)
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+
+    assert call(B=-1) == INVALID          # decode part invalid: prefill not launched
+    assert call(dstate=None) == INVALID
+    assert call(S=-1) == INVALID          # prefill part invalid: decode not launched
+    assert call(cu=None) == INVALID
+    assert call(ws=None, wsb=0) == WORKSPACE
+    assert call(d=96) == UNSUPPORTED
+    assert call(layout=5) == UNSUPPORTED
+    assert call(decay=None) == INVALID
+    assert call(S=0, total=0, B=0) == OK  # both parts empty
 
 
 def test_decode_rejects_bad_arguments(lib):

@@ -102,7 +102,7 @@ def test_mid_bf16_workload():
     run_fwd_case(2, 8, 4096, 128, "bf16", seed=2, block=64)
 
 
-@pytest.mark.parametrize("seg", [4096, 128, 640, 1000, 8192])
+@pytest.mark.parametrize("seg", [4096, 128, 640, 1000, 8192, la.LA_SEGMENT_PER_SEQUENCE])
 def test_segment_split_invariance_bf16(seg, prefill_path):
     """Any cut of the token axis into segments (on-device LASP+ scan) gives
     the oracle's result: segments of one block, ragged segments, segments
@@ -215,7 +215,7 @@ def test_varlen_token_major_layout(d, dtype, seg, prefill_path):
                     token_major=True)
 
 
-@pytest.mark.parametrize("seg", [0, 128, 200, 100000])
+@pytest.mark.parametrize("seg", [0, 128, 200, 100000, la.LA_SEGMENT_PER_SEQUENCE])
 def test_varlen_bf16(seg, prefill_path):
     run_varlen_case([300, 0, 1, 129, 1024, 5, 0, 640, 2000], 4, 128, "bf16", seed=70, seg=seg)
 
@@ -228,11 +228,24 @@ def test_varlen_eight_pieces(prefill_path):
 
 
 @pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])
-def test_varlen_vector_alu(d, dtype):
-    run_varlen_case([33, 0, 64, 1, 100], 2, d, dtype, seed=71, seg=48)
+@pytest.mark.parametrize("seg", [48, la.LA_SEGMENT_PER_SEQUENCE])
+def test_varlen_vector_alu(d, dtype, seg):
+    run_varlen_case([33, 0, 64, 1, 100], 2, d, dtype, seed=71, seg=seg)
 
 
-def test_varlen_all_empty():
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "fp32")])
+def test_varlen_one_segment_per_sequence(d, dtype):
+    """LA_SEGMENT_PER_SEQUENCE: one workgroup per (sequence, head) and the
+    output pass alone; empty sequences (first, inside, last) get their initial
+    state as final state from it, with and without initial states."""
+    lens = [0, 300, 0, 1, 129, 2000, 5, 0]
+    run_varlen_case(lens, 3, d, dtype, seed=73, seg=la.LA_SEGMENT_PER_SEQUENCE)
+    run_varlen_case(lens, 3, d, dtype, seed=74, seg=la.LA_SEGMENT_PER_SEQUENCE, with_init=False)
+    run_varlen_case(lens, 3, d, dtype, seed=75, seg=la.LA_SEGMENT_PER_SEQUENCE, token_major=True)
+
+
+@pytest.mark.parametrize("seg", [0, la.LA_SEGMENT_PER_SEQUENCE])
+def test_varlen_all_empty(seg):
     torch = torch_mod()
     H, d = 2, 128
     cu = torch.zeros(4, dtype=torch.int32, device="cuda")
@@ -240,7 +253,7 @@ def test_varlen_all_empty():
     init = torch.randn(3, H, d, d, device="cuda")
     out, fin = la.lightning_attn_fwd_varlen(q, q.clone(), q.clone(),
                                             torch.from_numpy(inputs.decay_schedule(H)).cuda(), cu,
-                                            init_states=init)
+                                            init_states=init, segment_tokens=seg)
     torch.cuda.synchronize()
     assert torch.equal(fin, init)
 

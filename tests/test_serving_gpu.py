@@ -98,7 +98,7 @@ def run_snapshot_case(lens, H, d, dtype, seed, iv, seg=0, with_init=True, token_
 
 
 @pytest.mark.parametrize("iv", [128, 256, 96, 1000])
-@pytest.mark.parametrize("seg", [0, 200, 1000])
+@pytest.mark.parametrize("seg", [0, 200, 1000, la.LA_SEGMENT_PER_SEQUENCE])
 def test_snapshots_bf16(iv, seg, prefill_path):
     """Snapshot intervals that are multiples of the 128-token chunk and ones
     that are not (96, 1000), with segments that start inside sequences at
@@ -118,7 +118,7 @@ def test_snapshots_token_major(seg, prefill_path):
 
 
 @pytest.mark.parametrize("d,dtype,iv", [(64, "fp32", 32), (128, "fp32", 50), (64, "bf16", 64)])
-@pytest.mark.parametrize("seg", [0, 48])
+@pytest.mark.parametrize("seg", [0, 48, la.LA_SEGMENT_PER_SEQUENCE])
 def test_snapshots_vector_alu(d, dtype, iv, seg):
     run_snapshot_case([33, 0, 64, 1, 100, 160], 2, d, dtype, seed=230 + d + iv, iv=iv, seg=seg)
 
@@ -214,3 +214,119 @@ def test_full_varlen_h64_65536_snapshots():
     for j, n in enumerate(lens):
         if n and n % iv == 0:
             assert torch.equal(snaps[offs[j + 1] - 1], fin[j])
+
+
+# ------------------------------------------------------- mixed serving step
+
+
+def run_mixed_case(prefill_lens, decode_B, H, d, dtype, seed, two_streams=True,
+                   token_major=False, seg=0):
+    """Sequences with prefix states: the prefill part continues len > 1
+    prompts from their prefix states, the decode part takes one token for
+    each of decode_B others; both against the oracle (packed recurrence from
+    the prefix state; recurrent decode step)."""
+    torch = torch_mod()
+    say("case mixed prefill=%s decode_B=%d H=%d d=%d %s two_streams=%s token_major=%s seg=%d"
+        % (prefill_lens, decode_B, H, d, dtype, two_streams, token_major, seg))
+    cu = inputs.cu_seqlens(prefill_lens)
+    total = int(cu[-1])
+    (pq, pk, pv), (hq, hk, hv) = dev_inputs((H, total, d), seed, dtype)
+    (dq, dk, dv), (eq, ek, ev) = dev_inputs((decode_B, H, d), seed + 1, dtype)
+    lam = inputs.decay_schedule(H)
+    tl = torch.from_numpy(lam).cuda()
+    P0 = inputs.host_state((len(prefill_lens), H, d, d), seed + 2)
+    D0 = inputs.host_state((decode_B, H, d, d), seed + 3)
+    dstate = torch.from_numpy(D0).cuda()
+    layout = la.LA_HEAD_MAJOR
+    if token_major:
+        pq, pk, pv = (t.transpose(0, 1).contiguous() for t in (pq, pk, pv))
+        layout = la.LA_TOKEN_MAJOR
+    side = torch.cuda.Stream() if two_streams else None
+    torch.cuda.synchronize()
+    pout, fin, dout = la.lightning_attn_mixed_step(
+        tl, (pq, pk, pv), torch.from_numpy(cu).cuda(), (dq, dk, dv), dstate, layout=layout,
+        init_states=torch.from_numpy(P0).cuda(), decode_stream=side, segment_tokens=seg)
+    torch.cuda.synchronize()
+    if token_major:
+        pout = pout.transpose(0, 1)
+    o_ref, f_ref, _ = oracle.fwd_varlen(hq, hk, hv, lam, cu, init=P0)
+    S = D0.astype(np.float64)
+    d_ref, _ = oracle.decode(eq, ek, ev, lam, S)
+    eo = rel_err(host(pout), o_ref) if total else 0.0
+    ef = rel_err(host(fin), f_ref) if len(prefill_lens) else 0.0
+    ed = rel_err(host(dout), d_ref) if decode_B else 0.0
+    es = rel_err(host(dstate), S) if decode_B else 0.0
+    say("   err prefill out %.3e state %.3e; decode out %.3e state %.3e" % (eo, ef, ed, es))
+    assert max(eo, ef, ed, es) <= TOL[dtype], (eo, ef, ed, es)
+
+
+@pytest.mark.parametrize("two_streams", [True, False])
+@pytest.mark.parametrize("seg", [0, la.LA_SEGMENT_PER_SEQUENCE])
+def test_mixed_step_pages_scenario(two_streams, seg):
+    """Batch of 20 with prefix states: two inputs of 50 tokens, eighteen of
+    one token (the mix of MiniMax-01 report section 3.3.2), at the 64-head
+    layer shape."""
+    run_mixed_case([50, 50], 18, 64, 128, "bf16", seed=300, two_streams=two_streams, seg=seg)
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])
+def test_mixed_step_vector_alu(d, dtype):
+    run_mixed_case([7, 0, 40], 5, 4, d, dtype, seed=310 + d)
+    run_mixed_case([7, 0, 40], 5, 4, d, dtype, seed=311 + d, seg=la.LA_SEGMENT_PER_SEQUENCE)
+
+
+def test_mixed_step_token_major():
+    run_mixed_case([300, 1, 129], 9, 8, 128, "bf16", seed=320, token_major=True)
+
+
+def test_mixed_step_one_part_empty():
+    run_mixed_case([], 6, 8, 128, "bf16", seed=330)
+    run_mixed_case([64, 200], 0, 8, 128, "bf16", seed=331)
+
+
+def test_mixed_step_graph_replay():
+    """The two-stream step captured as a HIP graph (as a serving loop would
+    run it) gives the eager step's results, bit for bit, on every replay;
+    eager work and synchronisations run between the replays."""
+    torch = torch_mod()
+    H, d, B = 16, 128, 6
+    plens = [50, 50, 3]
+    say("case mixed step graph replay")
+    cu = torch.from_numpy(inputs.cu_seqlens(plens)).cuda()
+    (pq, pk, pv), _ = dev_inputs((H, sum(plens), d), 340, "bf16")
+    (dq, dk, dv), _ = dev_inputs((B, H, d), 341, "bf16")
+    tl = torch.from_numpy(inputs.decay_schedule(H)).cuda()
+    pinit = torch.from_numpy(inputs.host_state((len(plens), H, d, d), 342)).cuda()
+    D0 = torch.from_numpy(inputs.host_state((B, H, d, d), 343)).cuda()
+    dstate = D0.clone()
+    pout, pfin, dout = torch.empty_like(pq), torch.empty_like(pinit), torch.empty_like(dq)
+    nws = la.lightning_attn_fwd_varlen_workspace_size(len(plens), H, sum(plens), d, 128)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+
+    def step():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        la.lightning_attn_mixed_step(tl, (pq, pk, pv), cu, (dq, dk, dv), dstate,
+                                     init_states=pinit, prefill_out=pout, final_states=pfin,
+                                     decode_out=dout, workspace=ws, decode_stream=side)
+        cur.wait_stream(side)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (pout, pfin, dout, dstate)]
+    g = torch.cuda.CUDAGraph()
+    dstate.copy_(D0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        for t in (pout, pfin, dout):
+            t.fill_(float("nan"))
+        dstate.copy_(D0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("prefill out", "final states", "decode out", "state"),
+                                   (pout, pfin, dout, dstate), ref):
+            assert torch.equal(got, want), "replay %d: %s differs" % (r, name)

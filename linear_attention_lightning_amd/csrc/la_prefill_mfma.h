@@ -54,6 +54,12 @@ constexpr int KV_ROW = 2 * D;      // LDS row stride (bytes) of every 128 x 128 
 constexpr int LDS_K = T * KV_ROW;  // one K or V tile (32 KB, swizzled)
 constexpr int LDS_KV = 2 * LDS_K;  // the K and V tiles of one chunk
 constexpr int LDS_ST = D * KV_ROW; // S^T (32 KB, swizzled like the tiles)
+// Cache-policy operand of a buffer access: the non-temporal hint (CDNA3/4
+// "nt", the SLC bit of the encoding).  q, k, v and out are each touched once
+// per pass, so the streaming accesses of the output pass (Q loads, K/V tile
+// loads, output stores) carry it: measured 7-8% less time per headline step
+// than cached accesses.
+constexpr int kCpolNT = 2;
 // The chunk kernel: two chunks' K/V tiles (double buffer) and S^T: 160 KB.
 constexpr int LDS_BYTES = 2 * LDS_KV + LDS_ST;
 constexpr float kFastLog2 = -15.f;  // factored powers when log2(lambda) > this
@@ -387,7 +393,7 @@ struct OutLane {
 
 // Q^T fragments of chunk c for query block bi of this output wave, straight
 // from HBM (B operand of the 16x16x32 products: qf[ks] holds features
-// 32 ks + 8 G .. + 7 of query row 16 qblock(bi) + i16).
+// 32 ks + 8 G .. + 7 of query row 16 qblock(bi) + i16).  Non-temporal loads.
 __device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cursor &c, int bi,
                                               u32x4 (&qf)[4], const OutLane &o) {
   // Rows past the chunk's end read its last row: their outputs are never stored.
@@ -396,7 +402,8 @@ __device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cur
   const bf16 *qrow = (const bf16 *)p.q + p.m.row_base(h, c.j) +
                      (c.c0 + (row < Lc ? row : Lc - 1)) * p.m.rs + 8 * o.G;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qf[ks] = *(const u32x4 *)(qrow + 32 * ks);
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = __builtin_nontemporal_load((const u32x4 *)(qrow + 32 * ks));
 }
 
 // K and V rows of chunk c, spread over the 256 threads of a role (register
@@ -416,8 +423,8 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// One global_load_lds_dwordx4: each lane's 16 bytes at gptr land in LDS at
-// lds + 16 x lane.  Issued from inline assembly so that the compiler's
+// One global_load_lds_dwordx4 (non-temporal): each lane's 16 bytes at gptr
+// land in LDS at lds + 16 x lane.  Issued from inline assembly so that the compiler's
 // memory-wait analysis does not see an LDS write: it would otherwise wait for
 // the load before every later LDS read and every barrier, serialising the
 // prefetch.  The caller waits for these loads itself (vm_wait) before the
@@ -425,7 +432,7 @@ __device__ __forceinline__ void vm_wait() {
 // only over-count them, never under-count.
 __device__ __forceinline__ void lds_dma16(const void *gptr, const char *lds) {
   const unsigned a = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(const LA_LDS char *)lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(gptr), "s"(a)
                : "memory", "m0");
@@ -483,7 +490,8 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const u32x4 x = lds_ld<u32x4>((rb ^ (it << 4)) + 1024 * it);
-      __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, (r0 + 4 * it) * rsb + c16 * 16, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, (r0 + 4 * it) * rsb + c16 * 16, 0,
+                                             kCpolNT);
     }
   }
 }

@@ -44,11 +44,14 @@ def _bind(lib):
     lib.oracle_fwd_varlen_f64.argtypes = [_P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _I]
     lib.oracle_fwd_varlen_snap_f64.argtypes = [_P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P,
                                                _L, _P, _P, _I]
+    lib.oracle_bwd_f64.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _P,
+                                   _I]
     lib.oracle_decode_f64.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I]
     lib.oracle_bruteforce_f64.argtypes = [_P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _I]
     lib.oracle_rows_f64.argtypes = [_P, _P, _P, ctypes.c_float, _I, _P, _L, _P, _P, _I]
     lib.oracle_state_entries_f64.argtypes = [_P, _P, ctypes.c_float, _I, _L, _P, _L, _P, _P, _I]
     for f in ("oracle_fwd_f64", "oracle_fwd_varlen_f64", "oracle_fwd_varlen_snap_f64",
+              "oracle_bwd_f64",
               "oracle_decode_f64",
               "oracle_bruteforce_f64", "oracle_rows_f64", "oracle_state_entries_f64"):
         getattr(lib, f).restype = _I
@@ -120,6 +123,22 @@ def fwd_varlen_snapshots(q, k, v, decay, cu_seqlens, interval, init=None, want_o
                                    d, _ptr(init), _ptr(out), _ptr(fin), int(interval), _ptr(offs),
                                    _ptr(snaps), nthreads)
     return out, fin, snaps, offs
+
+
+def bwd(q, k, v, decay, dout, dfin=None, init=None, nthreads=0, lib=None):
+    """Gradients of fwd for q, k, v, dout [B, H, N, d]; dfin (gradient of the
+    final state) and init [B, H, d, d] or None.  Returns (dq, dk, dv, dinit)
+    in float64 (dinit [B, H, d, d])."""
+    lib = lib or load()
+    q, k, v, decay, dout = _f32(q), _f32(k), _f32(v), _f32(decay), _f32(dout)
+    B, H, N, d = q.shape
+    dfin, init = _f64(dfin), _f64(init)
+    dq, dk, dv = (np.empty((B, H, N, d), np.float64) for _ in range(3))
+    dinit = np.empty((B, H, d, d), np.float64)
+    lib.oracle_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout), _ptr(dfin),
+                       _ptr(init), B, H, N, d, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dinit),
+                       nthreads)
+    return dq, dk, dv, dinit
 
 
 def decode(q, k, v, decay, state, nthreads=0, lib=None):

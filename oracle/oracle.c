@@ -279,6 +279,103 @@ int oracle_fwd_varlen_snap_f64(const float *q, const float *k, const float *v, c
   return run_units(var_unit, &c, (int64_t)num_seqs * H, nthreads);
 }
 
+/* -------------------------------------------------------------- backward */
+
+/*
+ * Gradients of the prefill (training).  The pages give no backward
+ * derivation, so it is the derivative of the recurrence above, taken by
+ * hand: with do_t = dL/do_t and dS_fin = dL/dS_{N-1},
+ *
+ *   G_t  = dL/dS_t (through o_t and every later state)
+ *        = q_t^T do_t + lambda G_{t+1},    G_{N-1} = q_{N-1}^T do_{N-1} + dS_fin
+ *   dq_t = do_t S_t^T            (dq_t[i] = sum_j do_t[j] S_t[i][j], S_t from the recurrence)
+ *   dk_t = v_t G_t^T             (dk_t[i] = sum_j G_t[i][j] v_t[j])
+ *   dv_t = k_t G_t               (dv_t[j] = sum_i k_t[i] G_t[i][j])
+ *   dS_init = lambda G_0         (dS_fin itself when N == 0)
+ *
+ * Layout as oracle_fwd_f64; dfin, init and dinit may be NULL (zero / not
+ * wanted).
+ */
+#ifndef ORACLE_PLANT_BWD
+#define ORACLE_PLANT_BWD 0
+#endif
+
+typedef struct {
+  const float *q, *k, *v, *decay, *dout;
+  int H, d;
+  int64_t N;
+  const double *dfin, *init;
+  double *dq, *dk, *dv, *dinit;
+} bwd_ctx;
+
+static void bwd_unit(void *vctx, int64_t u) {
+  bwd_ctx *c = (bwd_ctx *)vctx;
+  int d = c->d;
+  int64_t N = c->N, dd = (int64_t)d * d, base = u * N * d;
+  double lam = (double)c->decay[u % c->H];
+  const float *q = c->q + base, *k = c->k + base, *v = c->v + base, *g = c->dout + base;
+  double *S = (double *)malloc(sizeof(double) * (size_t)dd);
+  /* dq: the forward recurrence, contracting each state with do_t */
+  if (c->init) memcpy(S, c->init + u * dd, sizeof(double) * (size_t)dd);
+  else memset(S, 0, sizeof(double) * (size_t)dd);
+  for (int64_t t = 0; t < N; ++t) {
+    const float *kt = k + t * d, *vt = v + t * d, *gt = g + t * d;
+    if (ORACLE_PLANT_BWD == 3) { /* reads the state before token t's update */
+      for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < d; ++j) acc += (double)gt[j] * S[(int64_t)i * d + j];
+        c->dq[base + t * d + i] = acc;
+      }
+    }
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j)
+        S[(int64_t)i * d + j] = lam * S[(int64_t)i * d + j] + (double)kt[i] * (double)vt[j];
+    if (ORACLE_PLANT_BWD != 3) {
+      for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < d; ++j) acc += (double)gt[j] * S[(int64_t)i * d + j];
+        c->dq[base + t * d + i] = acc;
+      }
+    }
+  }
+  /* dk, dv: G backwards from the last token */
+  double *G = S;
+  if (c->dfin) memcpy(G, c->dfin + u * dd, sizeof(double) * (size_t)dd);
+  else memset(G, 0, sizeof(double) * (size_t)dd);
+  for (int64_t t = N - 1; t >= 0; --t) {
+    const float *qt = q + t * d, *kt = k + t * d, *vt = v + t * d, *gt = g + t * d;
+    double f = (t == N - 1) ? 1.0 : lam;
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j)
+        G[(int64_t)i * d + j] = f * G[(int64_t)i * d + j] + (double)qt[i] * (double)gt[j];
+    for (int i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < d; ++j)
+        acc += (ORACLE_PLANT_BWD == 1 ? G[(int64_t)j * d + i] : G[(int64_t)i * d + j]) *
+               (double)vt[j];
+      c->dk[base + t * d + i] = acc;
+    }
+    for (int j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += (double)kt[i] * G[(int64_t)i * d + j];
+      c->dv[base + t * d + j] = acc;
+    }
+  }
+  if (c->dinit) {
+    double f = (N > 0 && ORACLE_PLANT_BWD != 2) ? lam : 1.0;
+    for (int64_t e = 0; e < dd; ++e) c->dinit[u * dd + e] = f * G[e];
+  }
+  free(S);
+}
+
+int oracle_bwd_f64(const float *q, const float *k, const float *v, const float *decay,
+                   const float *dout, const double *dfin, const double *init, int B, int H,
+                   int64_t N, int d, double *dq, double *dk, double *dv, double *dinit,
+                   int nthreads) {
+  bwd_ctx c = {q, k, v, decay, dout, H, d, N, dfin, init, dq, dk, dv, dinit};
+  return run_units(bwd_unit, &c, (int64_t)B * H, nthreads);
+}
+
 /* ---------------------------------------------------------------- decode */
 
 typedef struct {

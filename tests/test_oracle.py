@@ -258,6 +258,124 @@ def test_prefix_snapshot_continuation():
         assert rel_err(fc[0], f[j]) < 1e-12
 
 
+# ------------------------------------------------------------- backward
+
+
+def _bwd_closed_form(q, k, v, lam, do, dfin, S0):
+    """Gradients of one head's prefill in matrix form (numpy): with the
+    decayed causal mask M[t][s] = lambda^(t-s) (t >= s),
+      O = ((Q K^T) (.) M) V + diag(lambda^(t+1)) Q S0,
+      S_fin = lambda^N S0 + K^T diag(lambda^(N-1-s)) V,
+    and dP = dO V^T:
+      dQ = (dP (.) M) K + diag(lambda^(t+1)) dO S0^T
+      dK = (dP (.) M)^T Q + diag(lambda^(N-1-s)) V dS_fin^T
+      dV = ((Q K^T) (.) M)^T dO + diag(lambda^(N-1-s)) K dS_fin
+      dS0 = Q^T diag(lambda^(t+1)) dO + lambda^N dS_fin."""
+    Q, K, V, dO = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    N = Q.shape[0]
+    lam = float(lam)
+    t = np.arange(N)
+    M = np.where(t[:, None] >= t[None, :], lam ** np.maximum(t[:, None] - t[None, :], 0), 0.0)
+    a = lam ** (t + 1.0)
+    w = lam ** (N - 1.0 - t)
+    dP = dO @ V.T
+    dQ = (dP * M) @ K
+    dK = (dP * M).T @ Q
+    dV = ((Q @ K.T) * M).T @ dO
+    dS0 = Q.T @ (a[:, None] * dO)
+    if S0 is not None:
+        dQ = dQ + a[:, None] * (dO @ S0.T)
+    if dfin is not None:
+        dK = dK + w[:, None] * (V @ dfin.T)
+        dV = dV + w[:, None] * (K @ dfin)
+        dS0 = dS0 + lam ** N * dfin
+    return dQ, dK, dV, dS0
+
+
+def _check_bwd(B, H, N, d, lams, with_init, with_dfin, seed, lib=None):
+    q, k, v = rand_qkv(B, H, N, d, seed)
+    do, _, _ = rand_qkv(B, H, N, d, seed + 1)
+    lam = np.asarray(lams, np.float32)
+    init = inputs.host_state((B, H, d, d), seed + 2).astype(np.float64) if with_init else None
+    dfin = inputs.host_state((B, H, d, d), seed + 3).astype(np.float64) if with_dfin else None
+    dq, dk, dv, dS0 = oracle.bwd(q, k, v, lam, do, dfin=dfin, init=init, lib=lib)
+    ok = True
+    for b in range(B):
+        for h in range(H):
+            ref = _bwd_closed_form(q[b, h], k[b, h], v[b, h], lam[h], do[b, h],
+                                   None if dfin is None else dfin[b, h],
+                                   None if init is None else init[b, h])
+            for got, want in zip((dq[b, h], dk[b, h], dv[b, h], dS0[b, h]), ref):
+                ok = ok and rel_err(got, want) < 1e-12
+    return ok
+
+
+@pytest.mark.parametrize("N,d,lams", [(1, 4, [0.5]), (9, 3, [1.0, 0.3]), (40, 8, [0.996, 0.6]),
+                                      (70, 16, [0.9394, 1e-3])])
+@pytest.mark.parametrize("with_init,with_dfin", [(False, False), (True, False), (True, True),
+                                                 (False, True)])
+def test_bwd_equals_matrix_closed_form(N, d, lams, with_init, with_dfin):
+    """The backward recurrence against the gradient of the matrix (left
+    product) form of section 2.2.1 with the decay mask, written with numpy."""
+    assert _check_bwd(2, len(lams), N, d, lams, with_init, with_dfin, seed=90 + N + d)
+
+
+def test_bwd_directional_finite_differences():
+    """<grad, E> against a central difference of the forward oracle's
+    L = <O, R> + <S_fin, R_f> along a random direction E of each input.  L is
+    linear in each of q, k, v, S_init on its own, so the difference is exact
+    up to rounding; inputs and directions are multiples of powers of two that
+    keep x +- eps E exact in float32."""
+    B, H, N, d = 1, 2, 13, 5
+    lam = np.asarray([0.9, 0.55], np.float32)
+    q, k, v = (inputs.round_to_bf16(x) for x in rand_qkv(B, H, N, d, 101))
+    R, _, _ = rand_qkv(B, H, N, d, 102)
+    S0 = inputs.round_to_bf16(inputs.host_state((B, H, d, d), 103)).astype(np.float64)
+    Rf = inputs.host_state((B, H, d, d), 104).astype(np.float64)
+    dq, dk, dv, dS0 = oracle.bwd(q, k, v, lam, R, dfin=Rf, init=S0)
+
+    def L(q_, k_, v_, s_):
+        o, f, _ = oracle.fwd(q_, k_, v_, lam, init=s_)
+        return float((o * R).sum() + (f * Rf).sum())
+
+    eps = 2.0 ** -4
+    rng = np.random.default_rng(105)
+    for name, grad in (("q", dq), ("k", dk), ("v", dv), ("s", dS0)):
+        shape = S0.shape if name == "s" else q.shape
+        E = inputs.round_to_bf16(rng.standard_normal(shape).astype(np.float32))
+        args = {"q": q, "k": k, "v": v, "s": S0}
+        plus, minus = dict(args), dict(args)
+        base = args[name].astype(np.float64)
+        plus[name] = base + eps * E
+        minus[name] = base - eps * E
+        if name != "s":
+            for x in (plus[name], minus[name]):
+                assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+            plus[name] = plus[name].astype(np.float32)
+            minus[name] = minus[name].astype(np.float32)
+        fd = (L(plus["q"], plus["k"], plus["v"], plus["s"]) -
+              L(minus["q"], minus["k"], minus["v"], minus["s"])) / (2 * eps)
+        an = float((grad * E).sum())
+        assert abs(fd - an) <= 1e-9 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_bwd_empty_sequence_passes_state_gradient():
+    q = np.zeros((1, 2, 0, 4), np.float32)
+    dfin = inputs.host_state((1, 2, 4, 4), 106).astype(np.float64)
+    _, _, _, dS0 = oracle.bwd(q, q, q, np.asarray([0.5, 0.9], np.float32), q, dfin=dfin)
+    assert np.array_equal(dS0, dfin)
+
+
+def test_bwd_planted_mistakes_are_caught():
+    assert _check_bwd(1, 2, 12, 4, [0.8, 0.5], True, True, seed=107)
+    with tempfile.TemporaryDirectory() as tmp:
+        for plant in (1, 2, 3):
+            path = oracle_build.build(out=os.path.join(tmp, "libb%d.so" % plant), plant_bwd=plant)
+            lib = oracle.load(path)
+            assert not _check_bwd(1, 2, 12, 4, [0.8, 0.5], True, True, seed=107, lib=lib), \
+                "planted backward mistake %d not caught" % plant
+
+
 def test_linearity_in_values():
     B, H, N, d = 1, 2, 30, 8
     q, k, v = rand_qkv(B, H, N, d, seed=51)

@@ -8,8 +8,8 @@ inputs already resident in HBM.  W untimed steps, then K steps timed with
 HIP events on the stream the library launches on.  Prints ONE JSON line:
 the headline tokens/s, TFLOP/s and fraction of the bf16 MFMA peak, the HBM
 roofline of the step, the CPU oracle timed on a bounded sample, and (unless
---no-extras) the decode, packed varlen, million-token, token-major, prefix-snapshot
-and mixed serving-step workloads.
+--no-extras) the decode, packed varlen, million-token, token-major, backward,
+prefix-snapshot and mixed serving-step workloads.
 """
 import argparse
 import hashlib
@@ -233,6 +233,38 @@ def bench_decode(la, inputs, reps, warmup):
     return {"workload": "decode_b128_h64", "B": B, "H": H, "d": d, "steps": T,
             "ms_per_token_step": round(ms, 5), "state_gbs": round(gbs, 1),
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def bench_backward(la, inputs, steps, warmup):
+    """Backward pass (lightning_attn_bwd) at the headline shape, B=1 H=64
+    N=32768 d=128 bf16, with a final-state gradient and an initial state:
+    ms per step; algorithmic bytes = q, k, v, dout read and dq, dk, dv written
+    once (7 x B H N d x 2 bytes, plus the d x d states)."""
+    import torch
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["layer_h64_n32k"]
+    B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
+    q, k, v = inputs.device_qkv((B, H, N, d), w["seed"], "bf16", device=dev)
+    do, _, _ = inputs.device_qkv((B, H, N, d), w["seed"] + 7, "bf16", device=dev)
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    init = inputs.device_state((B, H, d, d), w["seed"] + 8, device=dev)
+    dfin = inputs.device_state((B, H, d, d), w["seed"] + 9, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dinit = torch.empty_like(init)
+    nws = la.lightning_attn_bwd_workspace_size(B, H, N, d, block)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        la.lightning_attn_bwd(q, k, v, decay, do, dfinal=dfin, init_state=init, block=block,
+                              dq=dq, dk=dk, dv=dv, dinit=dinit, workspace=ws)
+
+    ms = time_steps(step, steps, warmup, torch.cuda.current_stream(dev))
+    byt = 7 * B * H * N * d * 2 + 3 * B * H * d * d * 4
+    return {"workload": "layer_h64_n32k", "pass": "backward (dq, dk, dv, dinit)",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+            "tflops_3_passes": round(3 * prefill_flops(B, H, N, d, 128) / (ms * 1e-3) / 1e12, 2),
+            "hbm_gbs_algorithmic": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def bench_snapshots(la, inputs, steps, warmup, interval=256):
@@ -480,6 +512,8 @@ def main():
         res["million"] = bench_million(la, inputs, steps=5, warmup=1)
         torch.cuda.empty_cache()
         res["token_major"] = bench_token_major(la, inputs, steps=args.steps, warmup=args.warmup)
+        torch.cuda.empty_cache()
+        res["backward"] = bench_backward(la, inputs, steps=args.steps, warmup=20)
         torch.cuda.empty_cache()
         res["snapshots"] = bench_snapshots(la, inputs, steps=max(5, args.steps // 2), warmup=2)
         torch.cuda.empty_cache()

@@ -282,6 +282,47 @@ la_status lightning_attn_decode(const void *q, const void *k, const void *v, con
                                 void *hip_stream);
 
 /*
+ * Backward pass of the fixed-length prefill (training): the gradients of a
+ * scalar loss L with respect to q, k, v and the initial state, given
+ * dout = dL/dout and dfinal = dL/dfinal_state.  The pages train with
+ * lightning attention (MiniMax-01 report, section 2.2.2.4 and Fig. 8:
+ * training speed in tokens per GPU per second) but print no backward pass;
+ * this one is the derivative of the recurrence above.  With G_t = dL/dS_t
+ * (G_t = q_t^T do_t + lambda G_{t+1}, starting from dfinal):
+ *     dq_t = do_t S_t^T,   dk_t = v_t G_t^T,   dv_t = k_t G_t,
+ *     dinit = lambda G_0   (dfinal when N == 0).
+ * Each of dq, dk, dv is itself a decayed linear attention (dq causal over
+ * (do, v, k) from init^T; dv and dk anti-causal over (k, q, do) and
+ * (v, do, q) from dfinal), computed by the prefill kernels, the anti-causal
+ * ones over a time-reversed view of the same buffers.
+ *
+ *   q, k, v, dout        : as for lightning_attn_fwd_layout (layout selects
+ *                          [B][H][N][d] or [B][N][H][d]), of `dt`.
+ *   dfinal, init_state   : [B][H][d][d] float32, or NULL (zero).
+ *   dq, dk, dv           : outputs, q's layout and dtype.
+ *   dinit                : [B][H][d][d] float32 output, or NULL if not wanted.
+ *   workspace            : device scratch of at least
+ *                          lightning_attn_bwd_workspace_size(...) bytes (always
+ *                          nonzero: the backward keeps four state sets there).
+ *   Other arguments as for lightning_attn_fwd_layout.  The prefill schedule is
+ *   always the three-phase one (LIGHTNING_ATTN_PREFILL is ignored here).
+ *
+ * Preconditions (not checked): lambda > 0 with |dfinal| / lambda finite in
+ * float32 (the anti-causal passes start from dfinal / lambda).  Returns as
+ * lightning_attn_fwd_layout; LA_ERR_WORKSPACE if the workspace is NULL or
+ * smaller than the size above.
+ */
+size_t lightning_attn_bwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
+                                         int64_t segment_tokens);
+
+la_status lightning_attn_bwd(const void *q, const void *k, const void *v, const float *decay,
+                             const void *dout, const float *dfinal, const float *init_state,
+                             void *dq, void *dk, void *dv, float *dinit, int B, int H, int64_t N,
+                             int d, int block, la_dtype dt, la_layout layout,
+                             int64_t segment_tokens, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
+/*
  * One step of a mixed serving batch (MiniMax-01 report, section 3.3.2:
  * inputs of one token are memory-bound and need few compute units, so they
  * go to a kernel of their own, separate from the inputs of more than one

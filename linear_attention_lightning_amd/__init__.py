@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
   lightning_attn_fwd_varlen_snapshots(q, k, v, decay, cu_seqlens, snapshot_interval, ...)
       -> (out, final_states, snapshots, snapshot_offsets)
   lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
+  lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, ...)
+      -> (dq, dk, dv, dinit)
   lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode_state, ...)
       -> (prefill_out, final_states, decode_out)   (decode_state updated in place)
 """
@@ -25,7 +27,7 @@ import os
 __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd_layout",
            "lightning_attn_fwd_varlen", "lightning_attn_fwd_varlen_layout",
            "lightning_attn_fwd_varlen_snapshots", "snapshot_row_offsets", "lightning_attn_decode",
-           "lightning_attn_mixed_step",
+           "lightning_attn_mixed_step", "lightning_attn_bwd", "lightning_attn_bwd_workspace_size",
            "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
@@ -90,6 +92,11 @@ def load_library(path=None):
     lib.lightning_attn_mixed_step.argtypes = [P, P, P, P, I, L, I, P, P, P, L, P, Z, P,
                                               P, P, P, P, P, I, P, P, I, I, I, I]
     lib.lightning_attn_mixed_step.restype = I
+    lib.lightning_attn_bwd_workspace_size.argtypes = [I, I, L, I, I, I, L]
+    lib.lightning_attn_bwd_workspace_size.restype = Z
+    lib.lightning_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, L, I, I, I, I, L, P,
+                                       Z, P]
+    lib.lightning_attn_bwd.restype = I
     lib.lightning_attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
     lib.lightning_attn_decode.restype = I
     if path is None:
@@ -431,3 +438,54 @@ def lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode
     if st != 0:
         raise LightningAttnError(st, "lightning_attn_mixed_step")
     return prefill_out, final_states, decode_out
+
+
+def lightning_attn_bwd_workspace_size(B, H, N, d, block=128, dtype=LA_BF16, segment_tokens=0):
+    return load_library().lightning_attn_bwd_workspace_size(B, H, N, d, block, dtype,
+                                                             segment_tokens)
+
+
+def lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, layout=LA_HEAD_MAJOR,
+                       block=128, segment_tokens=0, want_dinit=True, dq=None, dk=None, dv=None,
+                       dinit=None, workspace=None):
+    """Gradients of lightning_attn_fwd_layout: q, k, v, dout [B, H, N, d]
+    (LA_HEAD_MAJOR) or [B, N, H, d] (LA_TOKEN_MAJOR); dfinal (gradient of the
+    final state) and init_state [B, H, d, d] float32 or None.  Returns
+    (dq, dk, dv, dinit) -- dinit [B, H, d, d] float32, or None when
+    want_dinit is false."""
+    torch = _torch()
+    lib = load_library()
+    if layout == LA_TOKEN_MAJOR:
+        B, N, H, d = q.shape
+    elif layout == LA_HEAD_MAJOR:
+        B, H, N, d = q.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (dout, "dout"), (q, "q")):
+        _check(t, n, q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    for t, n in ((dfinal, "dfinal"), (init_state, "init_state")):
+        if t is not None:
+            _check(t, n, (B, H, d, d), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, q.shape, q.dtype, dev)
+    if want_dinit and dinit is None:
+        dinit = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    if dinit is not None:
+        _check(dinit, "dinit", (B, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    ws_bytes = lib.lightning_attn_bwd_workspace_size(B, H, N, d, block, dt, segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout), _ptr(dfinal),
+                                _ptr(init_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dinit), B, H,
+                                N, d, block, dt, layout, segment_tokens, _ptr(workspace), ws_have,
+                                _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_bwd")
+    return dq, dk, dv, dinit

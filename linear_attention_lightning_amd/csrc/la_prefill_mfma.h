@@ -472,6 +472,11 @@ __device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const
 // unconditional instruction (a branch around each one would make the
 // compiler's memory-wait analysis assume they might not have been issued,
 // and wait for them at the next chunk's first Q^T use).
+// NEG: the row stride may be negative (a time-reversed view, rows at
+// decreasing addresses): the buffer then starts at the chunk's last row, the
+// lowest address, and row r sits at byte (L - 1 - r) * |rsb|; rows >= L are
+// given the offset 2^31, past the range (below 2^31 bytes), and dropped.
+template <bool NEG = false>
 __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor &c, unsigned Os,
                                            const OutLane &o) {
   const int L = (int)(c.c1 - c.c0);
@@ -480,8 +485,10 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
   // (a row stride is at least one row, so rows >= L fall outside it).  The
   // host keeps 128 row strides within 2^31 bytes.
   const int rsb = (int)(p.m.rs * 2);
+  const int flip = (NEG && rsb < 0) ? L - 1 : 0;
+  const int span = (NEG && rsb < 0) ? -rsb : rsb;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (bf16 *)p.out + p.m.row_base(h, c.j) + c.c0 * p.m.rs, 0, (L - 1) * rsb + D * 2,
+      (bf16 *)p.out + p.m.row_base(h, c.j) + (c.c0 + flip) * p.m.rs, 0, (L - 1) * span + D * 2,
       kRawBufferWord3);
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {
@@ -490,8 +497,9 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const u32x4 x = lds_ld<u32x4>((rb ^ (it << 4)) + 1024 * it);
-      __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, (r0 + 4 * it) * rsb + c16 * 16, 0,
-                                             kCpolNT);
+      const int r = r0 + 4 * it;
+      const int off = (NEG && r >= L) ? (int)0x80000000u : (r - flip) * rsb + c16 * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, off, 0, kCpolNT);
     }
   }
 }
@@ -628,7 +636,7 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
           lds_st<bf16x4>(sb ^ (jt << 5), v);
         }
       }
-      write_rows(p, h, cur, Ks, o);
+      write_rows<SNAP>(p, h, cur, Ks, o);
     }
     if (!nxt.valid) break;
     cur = nxt;
@@ -704,9 +712,10 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 
 // Phase C: outputs (and final states) for one (segment, head), from the
 // segment's entering state (scan result, initial state or zero).
-// SERVE: the serving variant: the walk also stores prefix-state snapshots
-// (when p.m.snap_iv > 0) and takes one segment per sequence (when
-// p.seg_len == 0).  Without it the kernel keeps the plain walk's registers.
+// SERVE: the general variant: the walk also stores prefix-state snapshots
+// (when p.m.snap_iv > 0), takes one segment per sequence (when p.seg_len ==
+// 0) and accepts a negative row stride (the time-reversed views of the
+// backward pass).  Without it the kernel keeps the plain walk's registers.
 template <bool SERVE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_chunk_kernel(FwdArgs p) {

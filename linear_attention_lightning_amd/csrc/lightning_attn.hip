@@ -10,6 +10,7 @@
 #include "la_prefill_mfma.h"
 #include "la_prefill_simt.h"
 #include "la_scan_decode.h"
+#include "la_backward.h"
 
 namespace {
 
@@ -91,7 +92,8 @@ size_t phased_ws_bytes(const Plan &p, int H, int d) {
 // segment_tokens value: every sequence is one segment (see lightning_attn.h).
 constexpr int64_t kSegPerSeq = -1;
 
-Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tokens) {
+Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tokens,
+                bool allow_fused = true) {
   if (segment_tokens == kSegPerSeq) segment_tokens = N;  // N == 0: automatic (nothing to cut)
   Plan p{N, B, false, false, 1, 0};
   const int64_t total = (int64_t)B * N;
@@ -113,7 +115,7 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
       if (seg >= N) seg = N;
     }
   }
-  const bool fused = want_fused(H, d, dt);
+  const bool fused = allow_fused && want_fused(H, d, dt);
   if (fused && segment_tokens <= 0 && seg != N && seg > kFusedSeg) seg = kFusedSeg;
   p.seg = seg;
   p.scan = (seg != N);
@@ -178,7 +180,7 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
         hipLaunchKernelGGL(la::mfma::local_state_kernel,
                            dim3((unsigned)((pl.nseg - 1) * a.r_split * a.m.H)),
                            dim3(la::mfma::NT_LOCAL), 0, st, a);
-    } else if (a.m.snap_iv > 0 || a.seg_len == 0) {
+    } else if (a.m.snap_iv > 0 || a.seg_len == 0 || a.m.rs < 0) {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<true>, grid, dim3(la::mfma::NT), 0, st, a);
     } else {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<false>, grid, dim3(la::mfma::NT), 0, st, a);
@@ -291,24 +293,15 @@ la_status check_layout(la_layout layout, int H, int d) {
   return LA_OK;
 }
 
-la_status fwd_fixed(const void *q, const void *k, const void *v, const float *decay, int B, int H,
-                    int64_t N, int d, int block, la_dtype dt, la_layout layout,
-                    const float *init_state, void *out, float *final_state,
-                    int64_t segment_tokens, void *workspace, size_t workspace_bytes,
-                    void *hip_stream, void *const *phase_events) {
-  if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
-  la_status st = check_common(H, d, block, dt, segment_tokens);
-  if (st == LA_OK) st = check_layout(layout, H, d);
-  if (st != LA_OK) return st;
-  if ((int64_t)B * H == 0) return LA_OK;
-  if (!decay) return LA_ERR_INVALID_ARG;
-  if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
-  if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
-  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
-  if (N == 0 && !final_state) return LA_OK;
-
+// Kernel arguments of a fixed-length prefill, [B][H][N][d] or [B][N][H][d].
+// reversed: a time-reversed view of the same buffers (token t of a sequence
+// read and written as token N - 1 - t): the row stride is negated and the
+// sequence base moved to the last token, which is still linear in the
+// sequence index, so the kernels' addressing is unchanged.
+la::FwdArgs fixed_args(const void *q, const void *k, const void *v, void *out, const float *decay,
+                       int B, int H, int64_t N, int d, la_dtype dt, la_layout layout,
+                       const float *init, float *fin, const Plan &pl, void *workspace,
+                       bool reversed) {
   la::FwdArgs a;
   a.q = q;
   a.k = k;
@@ -332,11 +325,47 @@ la_status fwd_fixed(const void *q, const void *k, const void *v, const float *de
     a.m.seq_extra = 0;
     a.m.rs = (int64_t)H * d;
   }
+  if (reversed && N > 0) {
+    // Virtual token j N + u is token N - 1 - u of sequence j: element offset
+    // base + h hs + j se + (j N + N - 1 - u) rs
+    //   = [base + (N - 1) rs] + h hs + j (se + 2 N rs) + (j N + u) (-rs).
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const int64_t shift = (N - 1) * a.m.rs * (int64_t)esz;
+    a.q = (const char *)q + shift;
+    a.k = (const char *)k + shift;
+    a.v = (const char *)v + shift;
+    a.out = (char *)out + shift;
+    a.m.seq_extra += 2 * N * a.m.rs;
+    a.m.rs = -a.m.rs;
+  }
   a.seg_len = pl.seg;
   a.nseg = (int)pl.nseg;
-  a.init = init_state;
-  a.fin = final_state;
+  a.init = init;
+  a.fin = fin;
   a.ws = (float *)workspace;
+  return a;
+}
+
+la_status fwd_fixed(const void *q, const void *k, const void *v, const float *decay, int B, int H,
+                    int64_t N, int d, int block, la_dtype dt, la_layout layout,
+                    const float *init_state, void *out, float *final_state,
+                    int64_t segment_tokens, void *workspace, size_t workspace_bytes,
+                    void *hip_stream, void *const *phase_events) {
+  if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st == LA_OK) st = check_layout(layout, H, d);
+  if (st != LA_OK) return st;
+  if ((int64_t)B * H == 0) return LA_OK;
+  if (!decay) return LA_ERR_INVALID_ARG;
+  if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+  if (N == 0 && !final_state) return LA_OK;
+
+  const la::FwdArgs a = fixed_args(q, k, v, out, decay, B, H, N, d, dt, layout, init_state,
+                                   final_state, pl, workspace, /*reversed=*/false);
   return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream, phase_events);
 }
 
@@ -456,9 +485,95 @@ void launch_decode(const void *q, const void *k, const void *v, const float *dec
   }
 }
 
+// Workspace of the backward pass: the passes' prefill workspace (reused by
+// all three, which run in stream order), then four state sets of B*H*d*d
+// floats: init^T, dS_fin / lambda, its transpose, and the dv pass's final
+// state.
+size_t bwd_ws_bytes(const Plan &pl, int B, int H, int d) {
+  const size_t al = 256;
+  return (pl.ws_bytes + al - 1) / al * al + 4 * state_bytes((int64_t)B * H, d);
+}
+
+la_status bwd_fixed(const void *q, const void *k, const void *v, const float *decay,
+                    const void *dout, const float *dfinal, const float *init, void *dq, void *dk,
+                    void *dv, float *dinit, int B, int H, int64_t N, int d, int block,
+                    la_dtype dt, la_layout layout, int64_t segment_tokens, void *workspace,
+                    size_t workspace_bytes, void *hip_stream) {
+  if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st == LA_OK) st = check_layout(layout, H, d);
+  if (st != LA_OK) return st;
+  if ((int64_t)B * H == 0) return LA_OK;
+  if (!decay) return LA_ERR_INVALID_ARG;
+  if (N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv)) return LA_ERR_INVALID_ARG;
+  if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  const size_t need = bwd_ws_bytes(pl, B, H, d);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)hip_stream;
+  const int64_t BH = (int64_t)B * H;
+  const dim3 sgrid((unsigned)BH, (unsigned)ceil_div((int64_t)d * d, 256));
+  if (N == 0) {  // no token: dS_init = dS_fin
+    if (dinit) {
+      hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, dfinal, decay, H, d, false,
+                         dinit);
+      return launch_status();
+    }
+    return LA_OK;
+  }
+  char *w = (char *)workspace;
+  const size_t st_b = state_bytes(BH, d);
+  float *initT = (float *)(w + (pl.ws_bytes + 255) / 256 * 256);
+  float *g = (float *)((char *)initT + st_b);
+  float *gT = (float *)((char *)g + st_b);
+  float *fin_dv = (float *)((char *)gT + st_b);
+  if (init || dfinal)
+    hipLaunchKernelGGL(la::bwd_prep_kernel, sgrid, dim3(256), 0, s, init, dfinal, decay, H, d,
+                       initT, g, gT);
+  // dq: causal, from S_init^T
+  la_status r = run_fwd(fixed_args(dout, v, k, dq, decay, B, H, N, d, dt, layout,
+                                   init ? initT : nullptr, nullptr, pl, workspace, false),
+                        pl, d, dt, false, s);
+  // dv: reversed, keys q and values do, from dS_fin / lambda; its final state is G_0
+  if (r == LA_OK)
+    r = run_fwd(fixed_args(k, q, dout, dv, decay, B, H, N, d, dt, layout,
+                           dfinal ? g : nullptr, dinit ? fin_dv : nullptr, pl, workspace, true),
+                pl, d, dt, false, s);
+  // dk: reversed, keys do and values q, from (dS_fin / lambda)^T
+  if (r == LA_OK)
+    r = run_fwd(fixed_args(v, dout, q, dk, decay, B, H, N, d, dt, layout,
+                           dfinal ? gT : nullptr, nullptr, pl, workspace, true),
+                pl, d, dt, false, s);
+  if (r == LA_OK && dinit) {
+    hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, fin_dv, decay, H, d, true,
+                       dinit);
+    r = launch_status();
+  }
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t lightning_attn_bwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
+                                         int64_t segment_tokens) {
+  if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
+  if ((int64_t)B * H == 0) return 0;
+  return bwd_ws_bytes(plan_fixed(B, H, N, d, dt, segment_tokens, false), B, H, d);
+}
+
+la_status lightning_attn_bwd(const void *q, const void *k, const void *v, const float *decay,
+                             const void *dout, const float *dfinal, const float *init_state,
+                             void *dq, void *dk, void *dv, float *dinit, int B, int H, int64_t N,
+                             int d, int block, la_dtype dt, la_layout layout,
+                             int64_t segment_tokens, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+  return bwd_fixed(q, k, v, decay, dout, dfinal, init_state, dq, dk, dv, dinit, B, H, N, d, block,
+                   dt, layout, segment_tokens, workspace, workspace_bytes, hip_stream);
+}
+
 
 const char *lightning_attn_status_string(la_status s) {
   switch (s) {

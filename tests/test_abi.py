@@ -166,6 +166,34 @@ def test_mixed_step_rejects_bad_arguments(lib):
     assert call(S=0, total=0, B=0) == OK  # both parts empty
 
 
+def test_bwd_rejects_bad_arguments(lib):
+    f = lib.lightning_attn_bwd
+    names = ["q", "k", "v", "decay", "dout", "dfin", "init", "dq", "dk", "dv", "dinit", "B", "H",
+             "N", "d", "block", "dt", "layout", "seg", "ws", "wsb", "stream"]
+    args = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, None, DUMMY, DUMMY, DUMMY, DUMMY, 1, 2, 256,
+            128, 128, BF16, 0, 0, None, 0, None]
+
+    def call(**kw):
+        a = list(args)
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+
+    assert call(d=96) == UNSUPPORTED
+    assert call(layout=3) == UNSUPPORTED
+    assert call(B=-1) == INVALID
+    assert call(seg=-3) == INVALID
+    assert call(dout=None) == INVALID
+    assert call(dk=None) == INVALID
+    assert call(decay=None) == INVALID
+    assert call() == WORKSPACE
+    need = lib.lightning_attn_bwd_workspace_size(1, 2, 256, 128, 128, BF16, 0)
+    assert need >= 4 * 2 * 128 * 128 * 4
+    assert call(ws=DUMMY, wsb=need - 1) == WORKSPACE
+    assert call(B=0) == OK
+    assert call(H=0, decay=None) == OK
+
+
 def test_decode_rejects_bad_arguments(lib):
     f = lib.lightning_attn_decode
     base = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 2, 4, 128, BF16, None]

@@ -1,0 +1,148 @@
+"""GPU parity of the backward pass (lightning_attn_bwd) against the CPU
+oracle's hand-derived gradient of the recurrence (oracle.bwd, pinned to the
+matrix-form gradient and to finite differences).
+
+Bar as for the forward pass: max |x - x_ref| / max |x_ref| <= 1e-4 for
+float32 inputs, <= 2e-2 for bf16 inputs, for each of dq, dk, dv and the
+initial-state gradient.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import linear_attention_lightning_amd as la
+from linear_attention_lightning_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.abs(b).max() if b.size else 0.0
+    return float(np.abs(a - b).max() / (den if den > 0 else 1.0)) if a.size else 0.0
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    torch = torch_mod()
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def run_bwd_case(B, H, N, d, dtype, seed, block=128, seg=0, with_init=True, with_dfin=True,
+                 lam=None, token_major=False):
+    torch = torch_mod()
+    say("case bwd B=%d H=%d N=%d d=%d %s seg=%d init=%s dfin=%s token_major=%s"
+        % (B, H, N, d, dtype, seg, with_init, with_dfin, token_major))
+    q, k, v = inputs.host_qkv((B, H, N, d), seed, dtype=dtype)
+    do, _, _ = inputs.host_qkv((B, H, N, d), seed + 1, dtype=dtype)
+    lam = inputs.decay_schedule(H) if lam is None else np.asarray(lam, np.float32)
+    init = inputs.host_state((B, H, d, d), seed + 2) if with_init else None
+    dfin = inputs.host_state((B, H, d, d), seed + 3) if with_dfin else None
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tq, tk, tv, tdo = (torch.from_numpy(x).cuda().to(tdt) for x in (q, k, v, do))
+    layout = la.LA_HEAD_MAJOR
+    if token_major:
+        tq, tk, tv, tdo = (t.transpose(1, 2).contiguous() for t in (tq, tk, tv, tdo))
+        layout = la.LA_TOKEN_MAJOR
+    outs = [torch.full_like(tq, float("nan")) for _ in range(3)]
+    dq, dk, dv, dinit = la.lightning_attn_bwd(
+        tq, tk, tv, torch.from_numpy(lam).cuda(), tdo,
+        dfinal=None if dfin is None else torch.from_numpy(dfin).cuda(),
+        init_state=None if init is None else torch.from_numpy(init).cuda(), layout=layout,
+        block=block, segment_tokens=seg, dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.synchronize()
+    if token_major:
+        dq, dk, dv = (t.transpose(1, 2) for t in (dq, dk, dv))
+    ref = oracle.bwd(q, k, v, lam, do, dfin=dfin, init=init)
+    errs = []
+    for name, got, want in zip(("dq", "dk", "dv", "dinit"), (dq, dk, dv, dinit), ref):
+        g = host(got)
+        assert np.isfinite(g).all(), name + " has unwritten or non-finite elements"
+        errs.append(rel_err(g, want))
+    say("   err dq %.3e dk %.3e dv %.3e dinit %.3e" % tuple(errs))
+    assert max(errs) <= TOL[dtype], errs
+
+
+def test_bwd_tiny_fp32():
+    run_bwd_case(1, 2, 256, 64, "fp32", seed=500, block=64)
+
+
+def test_bwd_mid_bf16():
+    run_bwd_case(2, 8, 4096, 128, "bf16", seed=501, block=64)
+
+
+@pytest.mark.parametrize("seg", [4096, 128, 640, 1000, la.LA_SEGMENT_PER_SEQUENCE])
+def test_bwd_segment_split_invariance(seg):
+    """The causal and the two time-reversed passes under every segment cut:
+    reversed segments start inside sequences and hand states backwards."""
+    run_bwd_case(2, 4, 4096, 128, "bf16", seed=502, seg=seg)
+
+
+@pytest.mark.parametrize("N", [1, 2, 127, 128, 129, 300, 1000])
+def test_bwd_ragged_tails(N):
+    run_bwd_case(2, 3, N, 128, "bf16", seed=510 + N, lam=[0.9961, 0.3997, 0.75])
+
+
+@pytest.mark.parametrize("with_init,with_dfin", [(False, False), (True, False), (False, True)])
+def test_bwd_optional_states(with_init, with_dfin):
+    run_bwd_case(1, 4, 1500, 128, "bf16", seed=520, with_init=with_init, with_dfin=with_dfin,
+                 seg=512)
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])
+@pytest.mark.parametrize("seg", [0, 64])
+def test_bwd_vector_alu(d, dtype, seg):
+    run_bwd_case(1, 3, 300, d, dtype, seed=530 + d, seg=seg, lam=[0.999, 0.5, 0.9])
+
+
+@pytest.mark.parametrize("d,dtype,seg", [(128, "bf16", 0), (128, "bf16", 256), (64, "fp32", 0)])
+def test_bwd_token_major(d, dtype, seg):
+    run_bwd_case(2, 5, 1000, d, dtype, seed=540 + d, seg=seg, token_major=True)
+
+
+def test_bwd_empty_sequences():
+    """N = 0: the initial-state gradient is dfinal."""
+    torch = torch_mod()
+    B, H, d = 2, 3, 128
+    q = torch.empty(B, H, 0, d, dtype=torch.bfloat16, device="cuda")
+    dfin = torch.randn(B, H, d, d, device="cuda")
+    lam = torch.from_numpy(inputs.decay_schedule(H)).cuda()
+    _, _, _, dinit = la.lightning_attn_bwd(q, q.clone(), q.clone(), lam, q.clone(), dfinal=dfin)
+    torch.cuda.synchronize()
+    assert torch.equal(dinit, dfin)
+
+
+def test_bwd_full_layer_h64_n32k():
+    """B=1 H=64 N=32768 d=128 (the prefill headline shape): heads 0, 31 and 63
+    in full, in the launch configuration the benchmark times."""
+    torch = torch_mod()
+    w = inputs.WORKLOADS["layer_h64_n32k"]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    say("case full bwd layer_h64_n32k")
+    tq, tk, tv = inputs.device_qkv((B, H, N, d), w["seed"], "bf16")
+    tdo, _, _ = inputs.device_qkv((B, H, N, d), w["seed"] + 7, "bf16")
+    lam = inputs.decay_schedule(H)
+    dq, dk, dv, dinit = la.lightning_attn_bwd(tq, tk, tv, torch.from_numpy(lam).cuda(), tdo,
+                                              block=w["block"])
+    torch.cuda.synchronize()
+    for h in (0, 31, H - 1):
+        sl = slice(h, h + 1)
+        ref = oracle.bwd(host(tq[:, sl]), host(tk[:, sl]), host(tv[:, sl]), lam[sl],
+                         host(tdo[:, sl]))
+        errs = [rel_err(host(g[:, sl]), r) for g, r in zip((dq, dk, dv, dinit), ref)]
+        say("   head %d err dq %.3e dk %.3e dv %.3e dinit %.3e" % ((h,) + tuple(errs)))
+        assert max(errs) <= TOL["bf16"], errs

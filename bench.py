@@ -432,6 +432,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this size once (a plain "
                          "copy kernel of known size, to scale HBM byte counters)")
+    ap.add_argument("--leg", choices=["backward", "serving", "snapshots"], default=None,
+                    help="time only this extra workload and print its JSON object (for "
+                         "profiling it on its own); the headline line is not printed")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
@@ -444,6 +447,12 @@ def main():
     from linear_attention_lightning_amd import inputs
 
     la.load_library()
+    if args.leg:
+        legs = {"backward": lambda: bench_backward(la, inputs, args.steps, 20),
+                "serving": lambda: bench_serving(la, inputs, P=50),
+                "snapshots": lambda: bench_snapshots(la, inputs, args.steps, 2)}
+        print(json.dumps(legs[args.leg]()), flush=True)
+        return
     w = inputs.WORKLOADS["layer_h64_n32k"]
     B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
     ms, phase_ms, tensors = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], args.steps,

@@ -44,6 +44,7 @@ def _bind(lib):
     lib.oracle_fwd_varlen_f64.argtypes = [_P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _I]
     lib.oracle_fwd_varlen_snap_f64.argtypes = [_P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P,
                                                _L, _P, _P, _I]
+    lib.oracle_fwd_chdecay_f64.argtypes = [_P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _I]
     lib.oracle_bwd_f64.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _P,
                                    _I]
     lib.oracle_decode_f64.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I]
@@ -51,7 +52,7 @@ def _bind(lib):
     lib.oracle_rows_f64.argtypes = [_P, _P, _P, ctypes.c_float, _I, _P, _L, _P, _P, _I]
     lib.oracle_state_entries_f64.argtypes = [_P, _P, ctypes.c_float, _I, _L, _P, _L, _P, _P, _I]
     for f in ("oracle_fwd_f64", "oracle_fwd_varlen_f64", "oracle_fwd_varlen_snap_f64",
-              "oracle_bwd_f64",
+              "oracle_bwd_f64", "oracle_fwd_chdecay_f64",
               "oracle_decode_f64",
               "oracle_bruteforce_f64", "oracle_rows_f64", "oracle_state_entries_f64"):
         getattr(lib, f).restype = _I
@@ -123,6 +124,21 @@ def fwd_varlen_snapshots(q, k, v, decay, cu_seqlens, interval, init=None, want_o
                                    d, _ptr(init), _ptr(out), _ptr(fin), int(interval), _ptr(offs),
                                    _ptr(snaps), nthreads)
     return out, fin, snaps, offs
+
+
+def fwd_chdecay(q, k, v, alpha, init=None, want_out=True, nthreads=0, lib=None):
+    """Channel-wise decay: alpha [H, d] float32 (one decay per key channel of
+    each head).  Returns (out [B,H,N,d] or None, final_state [B,H,d,d])."""
+    lib = lib or load()
+    q, k, v, alpha = _f32(q), _f32(k), _f32(v), _f32(alpha)
+    B, H, N, d = q.shape
+    assert alpha.shape == (H, d)
+    init = _f64(init)
+    out = np.empty((B, H, N, d), np.float64) if want_out else None
+    fin = np.empty((B, H, d, d), np.float64)
+    lib.oracle_fwd_chdecay_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), B, H, N, d, _ptr(init),
+                               _ptr(out), _ptr(fin), nthreads)
+    return out, fin
 
 
 def bwd(q, k, v, decay, dout, dfin=None, init=None, nthreads=0, lib=None):

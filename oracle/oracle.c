@@ -279,6 +279,69 @@ int oracle_fwd_varlen_snap_f64(const float *q, const float *k, const float *v, c
   return run_units(var_unit, &c, (int64_t)num_seqs * H, nthreads);
 }
 
+/* ------------------------------------------------- channel-wise decay */
+
+/*
+ * The channel-wise variant (K3 reading notes, "gated DeltaNet": the scalar
+ * decay replaced by one decay per channel, strictly more general since equal
+ * channels give back the scalar form; here without the delta rule): head h
+ * has a decay alpha[h][i] for every key channel i, and
+ *
+ *   S_t[i][j] = alpha_i S_{t-1}[i][j] + k_t[i] v_t[j],     o_t = q_t S_t,
+ *
+ * i.e. o_t[j] = sum_{s<=t} sum_i q_t[i] alpha_i^(t-s) k_s[i] v_s[j]
+ *             + sum_i q_t[i] alpha_i^(t+1) S_init[i][j].
+ * alpha is [H][d] float32 (widened to double); layout as oracle_fwd_f64.
+ */
+#ifndef ORACLE_PLANT_CH
+#define ORACLE_PLANT_CH 0 /* 1 = decay indexed by the value channel (a planted mistake) */
+#endif
+
+typedef struct {
+  const float *q, *k, *v, *alpha;
+  int H, d;
+  int64_t N;
+  const double *init;
+  double *out, *fin;
+} ch_ctx;
+
+static void ch_unit(void *vctx, int64_t u) {
+  ch_ctx *c = (ch_ctx *)vctx;
+  int d = c->d, h = (int)(u % c->H);
+  int64_t N = c->N, dd = (int64_t)d * d, base = u * N * d;
+  const float *al = c->alpha + (int64_t)h * d;
+  double *S = (double *)malloc(sizeof(double) * (size_t)dd);
+  if (c->init) memcpy(S, c->init + u * dd, sizeof(double) * (size_t)dd);
+  else memset(S, 0, sizeof(double) * (size_t)dd);
+  for (int64_t t = 0; t < N; ++t) {
+    const float *qt = c->q + base + t * d, *kt = c->k + base + t * d, *vt = c->v + base + t * d;
+    for (int i = 0; i < d; ++i) {
+      double a = (double)al[i], ki = (double)kt[i];
+      for (int j = 0; j < d; ++j) {
+        if (ORACLE_PLANT_CH == 1) a = (double)al[j];
+        S[(int64_t)i * d + j] = a * S[(int64_t)i * d + j] + ki * (double)vt[j];
+      }
+    }
+    if (c->out) {
+      double *o = c->out + base + t * d;
+      for (int j = 0; j < d; ++j) o[j] = 0.0;
+      for (int i = 0; i < d; ++i) {
+        double qi = (double)qt[i];
+        for (int j = 0; j < d; ++j) o[j] += qi * S[(int64_t)i * d + j];
+      }
+    }
+  }
+  if (c->fin) memcpy(c->fin + u * dd, S, sizeof(double) * (size_t)dd);
+  free(S);
+}
+
+int oracle_fwd_chdecay_f64(const float *q, const float *k, const float *v, const float *alpha,
+                           int B, int H, int64_t N, int d, const double *init, double *out,
+                           double *fin, int nthreads) {
+  ch_ctx c = {q, k, v, alpha, H, d, N, init, out, fin};
+  return run_units(ch_unit, &c, (int64_t)B * H, nthreads);
+}
+
 /* -------------------------------------------------------------- backward */
 
 /*

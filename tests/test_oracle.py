@@ -258,6 +258,77 @@ def test_prefix_snapshot_continuation():
         assert rel_err(fc[0], f[j]) < 1e-12
 
 
+# ------------------------------------------------- channel-wise decay
+
+
+def _chdecay_closed_form(q, k, v, alpha, S0):
+    """One head's channel-wise decayed attention written as a sum over
+    channels of rank-one scalar-decay products (numpy):
+      O = sum_i ((q_i k_i^T) (.) M_i) V + Q diag-weighted S0,
+    M_i[t][s] = alpha_i^(t-s) (t >= s); S_fin[i] = sum_s alpha_i^(N-1-s) k_s[i] v_s
+    + alpha_i^N S0[i]."""
+    Q, K, V = (np.asarray(x, np.float64) for x in (q, k, v))
+    N, d = Q.shape
+    t = np.arange(N)
+    O = np.zeros((N, d))
+    fin = np.zeros((d, d))
+    for i in range(d):
+        a = float(alpha[i])
+        M = np.where(t[:, None] >= t[None, :], a ** np.maximum(t[:, None] - t[None, :], 0), 0.0)
+        O += ((np.outer(Q[:, i], K[:, i])) * M) @ V
+        fin[i] = (a ** (N - 1.0 - t) * K[:, i]) @ V
+        if S0 is not None:
+            O += np.outer(Q[:, i] * a ** (t + 1.0), S0[i])
+            fin[i] += a ** N * S0[i]
+    return O, fin
+
+
+@pytest.mark.parametrize("N,d", [(1, 4), (17, 3), (60, 8)])
+@pytest.mark.parametrize("with_init", [False, True])
+def test_chdecay_equals_per_channel_closed_form(N, d, with_init):
+    """The channel-wise recurrence against the per-channel decomposition of the
+    decayed left product (numpy), with decays spread over (0, 1]."""
+    H = 2
+    q, k, v = rand_qkv(1, H, N, d, seed=120 + N)
+    rng = np.random.default_rng(121)
+    alpha = rng.uniform(0.05, 1.0, (H, d)).astype(np.float32)
+    alpha[0, 0] = 1.0
+    S0 = inputs.host_state((1, H, d, d), 122).astype(np.float64) if with_init else None
+    o, f = oracle.fwd_chdecay(q, k, v, alpha, init=S0)
+    for h in range(H):
+        ro, rf = _chdecay_closed_form(q[0, h], k[0, h], v[0, h], alpha[h],
+                                      None if S0 is None else S0[0, h])
+        assert rel_err(o[0, h], ro) < 1e-12 and rel_err(f[0, h], rf) < 1e-12
+
+
+def test_chdecay_with_equal_channels_is_the_scalar_decay():
+    """Equal per-channel decays reduce to the scalar-decay form (checked
+    against the scalar brute-force left product)."""
+    B, H, N, d = 1, 2, 33, 6
+    q, k, v = rand_qkv(B, H, N, d, seed=123)
+    lam = np.asarray([0.9, 0.45], np.float32)
+    alpha = np.repeat(lam[:, None], d, axis=1)
+    S0 = inputs.host_state((B, H, d, d), 124).astype(np.float64)
+    o, f = oracle.fwd_chdecay(q, k, v, alpha, init=S0)
+    ob, fb = oracle.bruteforce(q, k, v, lam, init=S0)
+    assert rel_err(o, ob) < 1e-12 and rel_err(f, fb) < 1e-12
+
+
+def test_chdecay_planted_mistake_is_caught():
+    q, k, v = rand_qkv(1, 1, 20, 5, seed=125)
+    alpha = np.asarray([[0.9, 0.3, 0.7, 0.99, 0.5]], np.float32)
+
+    def ok(lib):
+        o, f = oracle.fwd_chdecay(q, k, v, alpha, lib=lib)
+        ro, rf = _chdecay_closed_form(q[0, 0], k[0, 0], v[0, 0], alpha[0], None)
+        return rel_err(o[0, 0], ro) < 1e-12 and rel_err(f[0, 0], rf) < 1e-12
+
+    assert ok(None)
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = oracle.load(oracle_build.build(out=os.path.join(tmp, "libc.so"), plant_ch=1))
+        assert not ok(lib)
+
+
 # ------------------------------------------------------------- backward
 
 

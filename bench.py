@@ -267,6 +267,38 @@ def bench_backward(la, inputs, steps, warmup):
             "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def bench_chdecay(la, inputs, steps, warmup):
+    """Channel-wise decay prefill at the headline shape (B=1 H=64 N=32768
+    d=128 bf16, per-channel decays from inputs.chdecay_schedule): ms per step,
+    tokens/s, algorithmic HBM bytes (as the scalar prefill) and the bf16 MFMA
+    rate at the formula 4 d (C + d) per token-head with the kernel's
+    64-token chunk."""
+    import torch
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["layer_h64_n32k"]
+    B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
+    q, k, v = inputs.device_qkv((B, H, N, d), w["seed"], "bf16", device=dev)
+    alpha = torch.from_numpy(inputs.chdecay_schedule(H, d)).to(dev)
+    out = torch.empty_like(q)
+    fin = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    nws = la.lightning_attn_fwd_chdecay_workspace_size(B, H, N, d, block)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        la.lightning_attn_fwd_chdecay(q, k, v, alpha, block=block, out=out, final_state=fin,
+                                      workspace=ws)
+
+    ms = time_steps(step, steps, warmup, torch.cuda.current_stream(dev))
+    byt = prefill_bytes(B, H, N, d)
+    return {"workload": "layer_h64_n32k", "decay": "channel-wise [H, d]",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+            "tflops_chunk64": round(prefill_flops(B, H, N, d, 64) / (ms * 1e-3) / 1e12, 2),
+            "mfma_peak_frac": round(prefill_flops(B, H, N, d, 64) / (ms * 1e-3) / 1e12
+                                    / PEAK_BF16_TFLOPS, 4),
+            "hbm_gbs_algorithmic": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def bench_snapshots(la, inputs, steps, warmup, interval=256):
     """The packed 65536-token workload with a prefix-state snapshot every
     `interval` tokens of each sequence (a prefix cache): time per step, and
@@ -432,7 +464,7 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this size once (a plain "
                          "copy kernel of known size, to scale HBM byte counters)")
-    ap.add_argument("--leg", choices=["backward", "serving", "snapshots"], default=None,
+    ap.add_argument("--leg", choices=["backward", "serving", "snapshots", "chdecay"], default=None,
                     help="time only this extra workload and print its JSON object (for "
                          "profiling it on its own); the headline line is not printed")
     args = ap.parse_args()
@@ -450,7 +482,8 @@ def main():
     if args.leg:
         legs = {"backward": lambda: bench_backward(la, inputs, args.steps, 20),
                 "serving": lambda: bench_serving(la, inputs, P=50),
-                "snapshots": lambda: bench_snapshots(la, inputs, args.steps, 2)}
+                "snapshots": lambda: bench_snapshots(la, inputs, args.steps, 2),
+                "chdecay": lambda: bench_chdecay(la, inputs, args.steps, 20)}
         print(json.dumps(legs[args.leg]()), flush=True)
         return
     w = inputs.WORKLOADS["layer_h64_n32k"]
@@ -523,6 +556,8 @@ def main():
         res["token_major"] = bench_token_major(la, inputs, steps=args.steps, warmup=args.warmup)
         torch.cuda.empty_cache()
         res["backward"] = bench_backward(la, inputs, steps=args.steps, warmup=20)
+        torch.cuda.empty_cache()
+        res["chdecay"] = bench_chdecay(la, inputs, steps=args.steps, warmup=20)
         torch.cuda.empty_cache()
         res["snapshots"] = bench_snapshots(la, inputs, steps=max(5, args.steps // 2), warmup=2)
         torch.cuda.empty_cache()

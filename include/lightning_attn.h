@@ -282,6 +282,36 @@ la_status lightning_attn_decode(const void *q, const void *k, const void *v, con
                                 void *hip_stream);
 
 /*
+ * Prefill with channel-wise decay (K3 reading notes, "gated DeltaNet": the
+ * scalar decay replaced by one decay per channel, strictly more general,
+ * here without the delta rule): head h has a decay alpha[h][i] for every key
+ * channel i,
+ *     S_t[i][j] = alpha_i S_{t-1}[i][j] + k_t[i] v_t[j],   o_t = q_t S_t.
+ * With all channels equal it is lightning_attn_fwd_layout.
+ *
+ *   alpha        : [H][d] float32 DEVICE array (a precondition, not
+ *                  checked: 0 < alpha <= 1, and alpha >= 0.1 for bf16 with
+ *                  d = 128).
+ *   Other arguments as for lightning_attn_fwd_layout (workspace from
+ *   lightning_attn_fwd_chdecay_workspace_size).  bf16 with d = 128 runs on
+ *   MFMA in 64-token chunks, the decay inside a chunk written as an absolute
+ *   position around the chunk's middle row (Q scaled by alpha^(q-32), K by
+ *   alpha^(32-c); the K3 notes bound the decay over such a window so that
+ *   the factors stay inside the BF16 range, which alpha >= 0.1 does here).
+ *   Other inputs run on the vector-ALU kernels in float32 with tabulated
+ *   powers and no range limit.  Always the three-phase segment schedule
+ *   (LIGHTNING_ATTN_PREFILL is ignored).
+ */
+size_t lightning_attn_fwd_chdecay_workspace_size(int B, int H, int64_t N, int d, int block,
+                                                 la_dtype dt, int64_t segment_tokens);
+
+la_status lightning_attn_fwd_chdecay(const void *q, const void *k, const void *v,
+                                     const float *alpha, int B, int H, int64_t N, int d, int block,
+                                     la_dtype dt, la_layout layout, const float *init_state,
+                                     void *out, float *final_state, int64_t segment_tokens,
+                                     void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * Backward pass of the fixed-length prefill (training): the gradients of a
  * scalar loss L with respect to q, k, v and the initial state, given
  * dout = dL/dout and dfinal = dL/dfinal_state.  The pages train with

@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
   lightning_attn_fwd_varlen_snapshots(q, k, v, decay, cu_seqlens, snapshot_interval, ...)
       -> (out, final_states, snapshots, snapshot_offsets)
   lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
+  lightning_attn_fwd_chdecay(q, k, v, alpha, ...) -> (out, final_state)   (alpha [H, d])
   lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, ...)
       -> (dq, dk, dv, dinit)
   lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode_state, ...)
@@ -28,6 +29,7 @@ __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd
            "lightning_attn_fwd_varlen", "lightning_attn_fwd_varlen_layout",
            "lightning_attn_fwd_varlen_snapshots", "snapshot_row_offsets", "lightning_attn_decode",
            "lightning_attn_mixed_step", "lightning_attn_bwd", "lightning_attn_bwd_workspace_size",
+           "lightning_attn_fwd_chdecay", "lightning_attn_fwd_chdecay_workspace_size",
            "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
@@ -92,6 +94,11 @@ def load_library(path=None):
     lib.lightning_attn_mixed_step.argtypes = [P, P, P, P, I, L, I, P, P, P, L, P, Z, P,
                                               P, P, P, P, P, I, P, P, I, I, I, I]
     lib.lightning_attn_mixed_step.restype = I
+    lib.lightning_attn_fwd_chdecay_workspace_size.argtypes = [I, I, L, I, I, I, L]
+    lib.lightning_attn_fwd_chdecay_workspace_size.restype = Z
+    lib.lightning_attn_fwd_chdecay.argtypes = [P, P, P, P, I, I, L, I, I, I, I, P, P, P, L, P, Z,
+                                               P]
+    lib.lightning_attn_fwd_chdecay.restype = I
     lib.lightning_attn_bwd_workspace_size.argtypes = [I, I, L, I, I, I, L]
     lib.lightning_attn_bwd_workspace_size.restype = Z
     lib.lightning_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, L, I, I, I, I, L, P,
@@ -489,3 +496,47 @@ def lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, layou
     if st != 0:
         raise LightningAttnError(st, "lightning_attn_bwd")
     return dq, dk, dv, dinit
+
+
+def lightning_attn_fwd_chdecay_workspace_size(B, H, N, d, block=128, dtype=LA_BF16,
+                                              segment_tokens=0):
+    return load_library().lightning_attn_fwd_chdecay_workspace_size(B, H, N, d, block, dtype,
+                                                                     segment_tokens)
+
+
+def lightning_attn_fwd_chdecay(q, k, v, alpha, layout=LA_HEAD_MAJOR, block=128, init_state=None,
+                               segment_tokens=0, out=None, final_state=None, workspace=None):
+    """Channel-wise decay: alpha [H, d] float32 holds one decay per key
+    channel of each head.  q, k, v as for lightning_attn_fwd_layout.  Returns
+    (out, final_state [B, H, d, d] float32)."""
+    torch = _torch()
+    lib = load_library()
+    if layout == LA_TOKEN_MAJOR:
+        B, N, H, d = q.shape
+    elif layout == LA_HEAD_MAJOR:
+        B, H, N, d = q.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (q, "q")):
+        _check(t, n, q.shape, q.dtype, dev)
+    _check(alpha, "alpha", (H, d), torch.float32, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (B, H, d, d), torch.float32, dev)
+    out = torch.empty_like(q) if out is None else out
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", (B, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    ws_bytes = lib.lightning_attn_fwd_chdecay_workspace_size(B, H, N, d, block, dt,
+                                                             segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_fwd_chdecay(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), B, H, N, d, block,
+                                        dt, layout, _ptr(init_state), _ptr(out), _ptr(final_state),
+                                        segment_tokens, _ptr(workspace), ws_have, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd_chdecay")
+    return out, final_state

@@ -157,7 +157,8 @@ __device__ __forceinline__ int64_t snap_row(const SeqMap &m, const int32_t *snap
 // fast-decaying heads this leaves a few chunks of a segment; lambda = 1 skips
 // nothing.
 __device__ __forceinline__ int64_t first_weighted(int64_t ps, int64_t b, float log2lam, int T) {
-  const float far = (float)(b - ps) - 160.f / -log2lam;  // -inf when log2lam == 0
+  if (!(log2lam < 0.f)) return ps;  // lambda = 1: every token keeps weight 1
+  const float far = (float)(b - ps) + 160.f / log2lam;  // (b - ps) - 160 / |log2 lambda|
   return far >= (float)T ? ps + (int64_t)(far / (float)T) * T : ps;
 }
 
@@ -176,6 +177,7 @@ struct FwdArgs {
   int r_split;       // pieces per segment of the local-state pass (>= 1)
   float *snaps;      // prefix-state snapshots [rows][H][d][d] (m.snap_iv > 0), else nullptr
   const int32_t *snap_off;  // [num_seqs + 1]: first snapshot row of each sequence
+  const float *chdecay;     // [H][d] per-channel decays (channel-wise variant), else nullptr
 };
 
 // Tokens [*a, *b) of segment s: equal cuts of the token axis, or sequence s

@@ -959,6 +959,10 @@ void prefill_fused_kernel(FusedArgs fa) {
 // (Ordering the grid by decreasing decay, so that the long pieces of slowly
 // decaying heads start first, measured slower.)
 // Wave u owns state rows 32u..32u+31.
+// CH: channel-wise decay (p.chdecay): row c's K values are scaled by their
+// channel's alpha_i^(x1-1-c) on the way into LDS and the update runs with
+// unit weights; chunks are skipped with the slowest channel's decay.
+template <bool CH = false>
 __global__ __launch_bounds__(NT_LOCAL) __attribute__((amdgpu_waves_per_eu(2, 4)))
 void local_state_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C_LOCAL * KV_ROW];
@@ -969,7 +973,16 @@ void local_state_kernel(FwdArgs p) {
   const int H = m.H, R = p.r_split;
   const int idx = (int)(blockIdx.x / H), h = blockIdx.x - (blockIdx.x / H) * H;
   const int s = p.nseg - 2 - idx / R, r = R - 1 - idx % R;
-  const float l2 = uniform(log2f(p.decay[h]));
+  float l2max = 0.f, l2f[8];  // channel-wise: slowest channel, and this thread's 8 channels
+  if constexpr (CH) {
+    const float *al = p.chdecay + (int64_t)h * D;
+    l2max = -__builtin_huge_valf();
+    for (int i = 0; i < D; ++i) l2max = fmaxf(l2max, log2f(al[i]));
+    l2max = uniform(l2max);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) l2f[e] = log2f(al[8 * (tid & 15) + e]);
+  }
+  const float l2 = CH ? 0.f : uniform(log2f(p.decay[h]));  // CH: unit weights in the update
   const bool fast = l2 > kFastLog2;
   const int64_t a = (int64_t)s * p.seg_len;
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
@@ -983,7 +996,7 @@ void local_state_kernel(FwdArgs p) {
   const int64_t base = m.row_base(h, jl);
   int64_t x0, x1;
   piece_bounds(ps, b, C_LOCAL, R, r, &x0, &x1);
-  const int64_t tf = first_weighted(ps, b, l2, C_LOCAL);
+  const int64_t tf = first_weighted(ps, b, CH ? l2max : l2, C_LOCAL);
   const int64_t r0 = tf > x0 ? tf : x0;
   if (r0 >= x1) return;
   float tail[8];
@@ -1012,6 +1025,19 @@ void local_state_kernel(FwdArgs p) {
   // the chunk two ahead.
   auto step = [&](auto slot_c, int64_t t0) {
     constexpr int sl = decltype(slot_c)::value;
+    if constexpr (CH) {
+      // K[c][i] alpha_i^(x1-1-c) for the thread's rows c and channels i
+#pragma unroll
+      for (int it = 0; it < PER; ++it) {
+        const int row = (it * NT_LOCAL + tid) >> 4;
+        const float n = (float)(x1 - 1 - (t0 + row));
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, pk[sl][it]);
+        float ks[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ks[e] = (float)kv[e] * fast_exp2(n * l2f[e]);
+        pk[sl][it] = __builtin_bit_cast(u32x4, cvt8(ks));
+      }
+    }
     store_tile<NT_LOCAL, C_LOCAL>(Ks, pk[sl], tid);
     store_tile<NT_LOCAL, C_LOCAL>(Vs, pv[sl], tid);
     __syncthreads();

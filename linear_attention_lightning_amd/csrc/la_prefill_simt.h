@@ -24,6 +24,12 @@ struct Smem {
   float bw[T];
 };
 
+// Extra LDS of the channel-wise variant: pw[n][i] = alpha_i^n for n < T.
+template <int D>
+struct SmemCh {
+  float pw[T][D];
+};
+
 template <typename Tin, int D>
 __device__ __forceinline__ void load_rows(float (*dst)[D], const Tin *src, int64_t rs, int L, int tid) {
   for (int e = tid; e < T * D; e += NT) {
@@ -32,14 +38,26 @@ __device__ __forceinline__ void load_rows(float (*dst)[D], const Tin *src, int64
   }
 }
 
-template <typename Tin, int D>
+// CH: channel-wise decay (one decay alpha_i per key channel i, p.chdecay):
+//   P[r][c] = sum_i Q[r][i] K[c][i] alpha_i^(r-c),
+//   O = (Q (.) alpha^(r+1)) S + P V,
+//   S = diag(alpha^L) S + (K (.) alpha^(L-1-c))^T V,
+// with the powers alpha_i^n (n < T) tabulated once per workgroup.
+template <typename Tin, int D, bool CH = false>
 __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
   __shared__ Smem<D> sm;
+  __shared__ SmemCh<CH ? D : 1> sc;
   const int tid = threadIdx.x;
   const SeqMap &m = p.m;
   const int H = m.H;
   const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  const float log2lam = log2f(p.decay[h]);
+  const float log2lam = CH ? 0.f : log2f(p.decay[h]);
+  if constexpr (CH) {
+    for (int e = tid; e < T * D; e += NT) {
+      const int n = e / D, i = e - (e / D) * D;
+      sc.pw[n][i] = pow_lam(log2f(p.chdecay[(int64_t)h * D + i]), (float)n);
+    }
+  }
   int64_t a, b;
   segment_bounds(p, s, &a, &b);
   const int64_t DD = (int64_t)D * D;
@@ -72,8 +90,12 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
       int r = e / T, c = e - (e / T) * T;
       float acc = 0.f;
       if (c <= r && r < L) {
-        for (int i = 0; i < D; ++i) acc += sm.Q[r][i] * sm.K[c][i];
-        acc *= pow_lam(log2lam, (float)(r - c));
+        if constexpr (CH) {
+          for (int i = 0; i < D; ++i) acc += sm.Q[r][i] * sm.K[c][i] * sc.pw[r - c][i];
+        } else {
+          for (int i = 0; i < D; ++i) acc += sm.Q[r][i] * sm.K[c][i];
+          acc *= pow_lam(log2lam, (float)(r - c));
+        }
       }
       sm.P[r][c] = acc;
     }
@@ -84,10 +106,16 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
       Tin *obase = (Tin *)p.out + base;
       for (int r = tid / D; r < L; r += RSTEP) {
         float inter = 0.f;
-        for (int i = 0; i < D; ++i) inter += sm.Q[r][i] * sm.S[i][j];
+        if constexpr (CH) {
+          // alpha_i^(r+1) = alpha_i^r alpha_i^1
+          for (int i = 0; i < D; ++i) inter += sm.Q[r][i] * (sc.pw[r][i] * sc.pw[1][i]) * sm.S[i][j];
+        } else {
+          for (int i = 0; i < D; ++i) inter += sm.Q[r][i] * sm.S[i][j];
+          inter *= pow_lam(log2lam, (float)(r + 1));
+        }
         float intra = 0.f;
         for (int c = 0; c <= r; ++c) intra += sm.P[r][c] * sm.V[c][j];
-        obase[(int64_t)r * m.rs + j] = from_f32<Tin>(pow_lam(log2lam, (float)(r + 1)) * inter + intra);
+        obase[(int64_t)r * m.rs + j] = from_f32<Tin>(inter + intra);
       }
     }
     __syncthreads();
@@ -100,8 +128,14 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
       for (int e = tid; e < D * D; e += NT) {
         int i = e / D, j = e - (e / D) * D;
         float acc = 0.f;
-        for (int c = 0; c < L; ++c) acc += (sm.bw[c] * sm.K[c][i]) * sm.V[c][j];
-        sm.S[i][j] = gL * sm.S[i][j] + acc;
+        if constexpr (CH) {
+          // alpha_i^(L-1-c), and alpha_i^L = alpha_i^(L-1) alpha_i
+          for (int c = 0; c < L; ++c) acc += (sc.pw[L - 1 - c][i] * sm.K[c][i]) * sm.V[c][j];
+          sm.S[i][j] = (sc.pw[L - 1][i] * sc.pw[1][i]) * sm.S[i][j] + acc;
+        } else {
+          for (int c = 0; c < L; ++c) acc += (sm.bw[c] * sm.K[c][i]) * sm.V[c][j];
+          sm.S[i][j] = gL * sm.S[i][j] + acc;
+        }
       }
       __syncthreads();
       if (seq_done && p.fin) {
@@ -124,16 +158,28 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
 }
 
 // Local state of each segment's last piece, from zero (phase A).
-template <typename Tin, int D>
+// CH: channel-wise decay; token c weighs alpha_i^(b-1-c) in channel i, and
+// the zero-weight skip uses the slowest channel's decay.
+template <typename Tin, int D, bool CH = false>
 __global__ __launch_bounds__(NT) void local_state_kernel(FwdArgs p) {
   __shared__ float Ks[T][D];
   __shared__ float Vs[T][D];
   __shared__ float wv[T];
+  __shared__ float l2c[CH ? D : 1];
   const int tid = threadIdx.x;
   const SeqMap &m = p.m;
   const int H = m.H;
   const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  const float log2lam = log2f(p.decay[h]);
+  float log2lam;
+  if constexpr (CH) {
+    const float *al = p.chdecay + (int64_t)h * D;
+    log2lam = -__builtin_huge_valf();
+    for (int i = 0; i < D; ++i) log2lam = fmaxf(log2lam, log2f(al[i]));
+    for (int i = tid; i < D; i += NT) l2c[i] = log2f(al[i]);
+    __syncthreads();
+  } else {
+    log2lam = log2f(p.decay[h]);
+  }
   const int64_t a = (int64_t)s * p.seg_len;
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
   if (a >= b) return;
@@ -152,7 +198,15 @@ __global__ __launch_bounds__(NT) void local_state_kernel(FwdArgs p) {
     const int L = (int)((b - t0) < T ? (b - t0) : T);
     load_rows<Tin, D>(Ks, (const Tin *)p.k + base + t0 * m.rs, m.rs, L, tid);
     load_rows<Tin, D>(Vs, (const Tin *)p.v + base + t0 * m.rs, m.rs, L, tid);
-    if (tid < T) wv[tid] = tid < L ? pow_lam(log2lam, (float)(b - 1 - t0 - tid)) : 0.f;
+    if constexpr (CH) {
+      for (int e = tid; e < T * D; e += NT) {
+        const int c = e / D, i = e - (e / D) * D;
+        Ks[c][i] = c < L ? Ks[c][i] * pow_lam(l2c[i], (float)(b - 1 - t0 - c)) : 0.f;
+      }
+      if (tid < T) wv[tid] = 1.f;
+    } else {
+      if (tid < T) wv[tid] = tid < L ? pow_lam(log2lam, (float)(b - 1 - t0 - tid)) : 0.f;
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < PER; ++u) {

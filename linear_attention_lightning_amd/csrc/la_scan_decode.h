@@ -28,6 +28,7 @@ struct ScanArgs {
   float *ws;     // [nseg][r_split][H][d][d]: partial local states in, S_in at slot (s, 0) out
   int r_split;   // pieces per segment of the local-state pass: 1, 2, 4, 8 or 16
   int C;         // chunk length of the local-state pass
+  const float *chdecay;  // [H][d] per-channel decays, or nullptr (scalar decay)
 };
 
 // What the scan needs of segment s, computed once per workgroup.
@@ -39,6 +40,8 @@ struct SegInfo {
   int live;       // bit r: piece r of the local-state pass was computed
   float gam;      // lambda^(length of the last piece)
   float wt[16];   // lambda^(b - x1_r): weight of piece r in L_s
+  float gam_n;    // the exponents of gam and wt (channel-wise decay: each
+  float wt_n[16]; // state row raises its own decay to them)
 };
 
 __device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, int s,
@@ -54,6 +57,7 @@ __device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, 
   d.init_base = (ps == a) ? -1 : jl;
   d.hands_on = m.start(jl + 1) != b;
   d.gam = pow_lam(log2lam, (float)(b - ps));
+  d.gam_n = (float)(b - ps);
   // Pieces as in piece_bounds (R a power of two); a piece is computed when
   // some of it lies at or after first_weighted and the state is handed on.
   const int64_t tf = first_weighted(ps, b, log2lam, p.C);
@@ -67,6 +71,7 @@ __device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, 
     const bool live = d.hands_on && r < p.r_split && (tf > x0 ? tf : x0) < x1;
     d.live |= live ? (1 << r) : 0;
     d.wt[r] = live ? pow_lam(log2lam, (float)(b - x1)) : 0.f;
+    d.wt_n[r] = (float)(b - x1);
   }
   return d;
 }
@@ -84,7 +89,19 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
   const int64_t DD = (int64_t)p.d * p.d;
   const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
   const bool mine = e < DD;
-  const float log2lam = log2f(p.decay[h]);
+  // Channel-wise decay: segments are described with the slowest channel's
+  // decay (a piece is live if any channel weighs it), and this thread's
+  // state row (elements e..e+3 share row e / d) raises its own decay to the
+  // described exponents.
+  float log2lam, l2row = 0.f;
+  if (p.chdecay) {
+    const float *al = p.chdecay + (int64_t)h * p.d;
+    log2lam = -__builtin_huge_valf();
+    for (int i = 0; i < p.d; ++i) log2lam = fmaxf(log2lam, log2f(al[i]));
+    l2row = log2f(al[mine ? (int)(e / p.d) : 0]);
+  } else {
+    log2lam = log2f(p.decay[h]);
+  }
   auto init4 = [&](int j) -> f32x4 {
     if (!p.init || j < 0) return (f32x4){0.f, 0.f, 0.f, 0.f};
     return *(const f32x4 *)(p.init + ((int64_t)j * H + h) * DD + e);
@@ -115,13 +132,22 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
         const SegInfo &d = info[s0 + i];
         const f32x4 sin = d.init_in >= 0 ? init4(d.init_in) : carry;
         *(f32x4 *)(p.ws + ((int64_t)(sb + s0 + i) * R * H + h) * DD + e) = sin;
-        f32x4 loc = d.wt[0] * pr[i][0];
+        float wt[R], gam = d.gam;
 #pragma unroll
-        for (int r = 1; r < R; ++r) loc += d.wt[r] * pr[i][r];
+        for (int r = 0; r < R; ++r) wt[r] = d.wt[r];
+        if (p.chdecay) {
+          gam = pow_lam(l2row, d.gam_n);
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            wt[r] = ((d.live >> r) & 1) ? pow_lam(l2row, d.wt_n[r]) : 0.f;
+        }
+        f32x4 loc = wt[0] * pr[i][0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) loc += wt[r] * pr[i][r];
         const f32x4 base = d.init_base >= 0 ? init4(d.init_base) : sin;
         // When the segment's last sequence ends at b, the carry is unused:
         // the next segment starts a new sequence.
-        carry = d.hands_on ? d.gam * base + loc : (f32x4){0.f, 0.f, 0.f, 0.f};
+        carry = d.hands_on ? gam * base + loc : (f32x4){0.f, 0.f, 0.f, 0.f};
       }
     }
   }

@@ -8,6 +8,7 @@
 
 #include "la_common.h"
 #include "la_prefill_mfma.h"
+#include "la_prefill_chdecay.h"
 #include "la_prefill_simt.h"
 #include "la_scan_decode.h"
 #include "la_backward.h"
@@ -23,8 +24,12 @@ bool valid_d(int d) { return d == 64 || d == 128; }
 bool valid_dtype(la_dtype dt) { return dt == LA_FP32 || dt == LA_BF16; }
 
 // bf16 with d = 128 runs on MFMA; everything else on the vector ALUs.
-bool use_mfma(int d, la_dtype dt) { return dt == LA_BF16 && d == 128; }
-int chunk_tokens(int d, la_dtype dt) { return use_mfma(d, dt) ? la::mfma::T : la::simt::T; }
+// ch: the channel-wise decay variant (its own MFMA output pass, 64-token
+// chunks; the vector-ALU kernels otherwise).
+bool use_mfma(int d, la_dtype dt, bool ch = false) { (void)ch; return dt == LA_BF16 && d == 128; }
+int chunk_tokens(int d, la_dtype dt, bool ch = false) {
+  return use_mfma(d, dt, ch) ? (ch ? la::mfma::TC : la::mfma::T) : la::simt::T;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -53,9 +58,9 @@ size_t fused_ws_bytes(int64_t nseg, int H, int d) {
 // length (0.70 ms at B1 H64 N32768), so it is opt-in:
 // LIGHTNING_ATTN_PREFILL=fused selects it (MFMA path only), =phased forces
 // the default.  Results agree up to rounding.
-bool want_fused(int H, int d, la_dtype dt) {
+bool want_fused(int H, int d, la_dtype dt, bool ch = false) {
   (void)H;
-  if (!use_mfma(d, dt)) return false;
+  if (ch || !use_mfma(d, dt, ch)) return false;
   const char *e = getenv("LIGHTNING_ATTN_PREFILL");
   return e && strcmp(e, "fused") == 0;
 }
@@ -72,15 +77,17 @@ constexpr int64_t kFusedSeg = 8192;
 // one workgroup per CU, and a single round over the 256 CUs with long
 // segments measured fastest (fewer, longer pipelines and less local-state
 // work); the vector-ALU kernels run several small workgroups per CU.
-int64_t target_groups(int d, la_dtype dt) { return use_mfma(d, dt) ? 256 : 512; }
+int64_t target_groups(int d, la_dtype dt, bool ch = false) {
+  return use_mfma(d, dt, ch) ? 256 : 512;
+}
 
 // Pieces per segment of the MFMA local-state pass: one small workgroup per
 // 8 or more 64-token chunks, at most 4, so that several workgroups share a
 // CU and hide one another's latency.  (8 or 16 pieces made the pass itself
 // faster but the scan, which reads every piece's partial state, slower by
 // more.)  The vector-ALU pass uses one.
-int pieces(int64_t seg, int d, la_dtype dt) {
-  if (!use_mfma(d, dt)) return 1;
+int pieces(int64_t seg, int d, la_dtype dt, bool ch = false) {
+  if (!use_mfma(d, dt, ch)) return 1;
   const int64_t r = seg / la::mfma::C_LOCAL / 8;
   return r >= 4 ? 4 : r >= 2 ? 2 : 1;  // a power of two (the scan shifts by it)
 }
@@ -93,7 +100,7 @@ size_t phased_ws_bytes(const Plan &p, int H, int d) {
 constexpr int64_t kSegPerSeq = -1;
 
 Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tokens,
-                bool allow_fused = true) {
+                bool allow_fused = true, bool ch = false) {
   if (segment_tokens == kSegPerSeq) segment_tokens = N;  // N == 0: automatic (nothing to cut)
   Plan p{N, B, false, false, 1, 0};
   const int64_t total = (int64_t)B * N;
@@ -101,13 +108,13 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
     p.nseg = 0;
     return p;
   }
-  const int T = chunk_tokens(d, dt);
+  const int T = chunk_tokens(d, dt, ch);
   int64_t seg = N;
   if (segment_tokens > 0) {
     seg = segment_tokens;
   } else {
     const int64_t bh = (int64_t)B * H;
-    int64_t G = ceil_div(target_groups(d, dt), bh);
+    int64_t G = ceil_div(target_groups(d, dt, ch), bh);
     const int64_t maxG = ceil_div(N, T);
     if (G > maxG) G = maxG;
     if (G > 1) {
@@ -115,12 +122,12 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
       if (seg >= N) seg = N;
     }
   }
-  const bool fused = allow_fused && want_fused(H, d, dt);
+  const bool fused = allow_fused && want_fused(H, d, dt, ch);
   if (fused && segment_tokens <= 0 && seg != N && seg > kFusedSeg) seg = kFusedSeg;
   p.seg = seg;
   p.scan = (seg != N);
   p.fused = p.scan && fused;
-  p.r_split = (p.scan && !p.fused) ? pieces(seg, d, dt) : 1;
+  p.r_split = (p.scan && !p.fused) ? pieces(seg, d, dt, ch) : 1;
   p.nseg = ceil_div(total, seg);
   p.ws_bytes = !p.scan ? 0 : p.fused ? fused_ws_bytes(p.nseg, H, d) : phased_ws_bytes(p, H, d);
   return p;
@@ -160,32 +167,46 @@ la_status launch_status() {
   return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
-template <typename Tin, int D>
-void launch_simt(const la::FwdArgs &a, const Plan &pl, hipStream_t st, bool phase_a) {
+template <typename Tin, int D, bool CH>
+void launch_simt_ch(const la::FwdArgs &a, const Plan &pl, hipStream_t st, bool phase_a) {
   dim3 grid((unsigned)(pl.nseg * a.m.H));
   if (phase_a)
-    hipLaunchKernelGGL((la::simt::local_state_kernel<Tin, D>), grid, dim3(la::simt::NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((la::simt::prefill_chunk_kernel<Tin, D>), grid, dim3(la::simt::NT), 0, st,
+    hipLaunchKernelGGL((la::simt::local_state_kernel<Tin, D, CH>), grid, dim3(la::simt::NT), 0, st,
                        a);
+  else
+    hipLaunchKernelGGL((la::simt::prefill_chunk_kernel<Tin, D, CH>), grid, dim3(la::simt::NT), 0,
+                       st, a);
+}
+
+template <typename Tin, int D>
+void launch_simt(const la::FwdArgs &a, const Plan &pl, hipStream_t st, bool phase_a) {
+  if (a.chdecay)
+    launch_simt_ch<Tin, D, true>(a, pl, st, phase_a);
+  else
+    launch_simt_ch<Tin, D, false>(a, pl, st, phase_a);
 }
 
 void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipStream_t st,
                   bool phase_a) {
   dim3 grid((unsigned)(pl.nseg * a.m.H));
-  if (use_mfma(d, dt)) {
+  if (use_mfma(d, dt, a.chdecay != nullptr)) {
     if (phase_a) {
       // The last segment hands no state on: its local state is never needed.
-      if (pl.nseg > 1)
-        hipLaunchKernelGGL(la::mfma::local_state_kernel,
-                           dim3((unsigned)((pl.nseg - 1) * a.r_split * a.m.H)),
-                           dim3(la::mfma::NT_LOCAL), 0, st, a);
+      const dim3 lgrid((unsigned)((pl.nseg - 1) * a.r_split * a.m.H));
+      if (pl.nseg > 1 && a.chdecay)
+        hipLaunchKernelGGL(la::mfma::local_state_kernel<true>, lgrid, dim3(la::mfma::NT_LOCAL), 0,
+                           st, a);
+      else if (pl.nseg > 1)
+        hipLaunchKernelGGL(la::mfma::local_state_kernel<false>, lgrid, dim3(la::mfma::NT_LOCAL), 0,
+                           st, a);
+    } else if (a.chdecay) {
+      hipLaunchKernelGGL(la::mfma::chdecay_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, a);
     } else if (a.m.snap_iv > 0 || a.seg_len == 0 || a.m.rs < 0) {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<true>, grid, dim3(la::mfma::NT), 0, st, a);
     } else {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<false>, grid, dim3(la::mfma::NT), 0, st, a);
     }
-  } else if (dt == LA_BF16) {
+  } else if (dt == LA_BF16 && d == 64) {
     launch_simt<bf16, 64>(a, pl, st, phase_a);
   } else if (d == 64) {
     launch_simt<float, 64>(a, pl, st, phase_a);
@@ -225,7 +246,7 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
     hipLaunchKernelGGL(la::mfma::fused_reset_kernel, dim3((unsigned)ceil_div(nwords, 256)),
                        dim3(256), 0, st, words, nwords);
     if (has_empty) {
-      la::ScanArgs s{a.m, a.decay, pl.seg, 0, d, a.init, a.fin, a.ws, 1, la::mfma::T};
+      la::ScanArgs s{a.m, a.decay, pl.seg, 0, d, a.init, a.fin, a.ws, 1, la::mfma::T, nullptr};
       hipLaunchKernelGGL(la::segment_scan_kernel<1>,
                          dim3((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024)), dim3(256), 0,
                          st, s);
@@ -258,7 +279,8 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
     s.fin = a.fin;
     s.ws = a.ws;
     s.r_split = pl.r_split;
-    s.C = use_mfma(d, dt) ? la::mfma::C_LOCAL : la::simt::T;
+    s.C = use_mfma(d, dt, a.chdecay != nullptr) ? la::mfma::C_LOCAL : la::simt::T;
+    s.chdecay = a.chdecay;
     dim3 grid((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024));
     switch (pl.r_split) {
       case 16: hipLaunchKernelGGL(la::segment_scan_kernel<16>, grid, dim3(256), 0, st, s); break;
@@ -316,6 +338,7 @@ la::FwdArgs fixed_args(const void *q, const void *k, const void *v, void *out, c
   a.m.snap_iv = 0;
   a.snaps = nullptr;
   a.snap_off = nullptr;
+  a.chdecay = nullptr;
   if (layout == LA_HEAD_MAJOR) {  // [B][H][N][d]: token t of sequence j, head h at
     a.m.head_stride = N * d;      // ((j H + h) N + t) d = h N d + j (H - 1) N d + (j N + t) d
     a.m.seq_extra = (int64_t)(H - 1) * N * d;
@@ -399,6 +422,7 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
   la::FwdArgs &a = c->a;
+  a.chdecay = nullptr;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -485,6 +509,31 @@ void launch_decode(const void *q, const void *k, const void *v, const float *dec
   }
 }
 
+// Channel-wise decay prefill (fixed length): the vector-ALU kernels with
+// per-channel decays; the three-phase schedule (never the single-pass one).
+la_status fwd_chdecay(const void *q, const void *k, const void *v, const float *alpha, int B,
+                      int H, int64_t N, int d, int block, la_dtype dt, la_layout layout,
+                      const float *init_state, void *out, float *final_state,
+                      int64_t segment_tokens, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
+  if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st == LA_OK) st = check_layout(layout, H, d);
+  if (st != LA_OK) return st;
+  if ((int64_t)B * H == 0) return LA_OK;
+  if (!alpha) return LA_ERR_INVALID_ARG;
+  if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false, /*ch=*/true);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+  if (N == 0 && !final_state) return LA_OK;
+  la::FwdArgs a = fixed_args(q, k, v, out, nullptr, B, H, N, d, dt, layout, init_state,
+                             final_state, pl, workspace, /*reversed=*/false);
+  a.chdecay = alpha;
+  return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream);
+}
+
 // Workspace of the backward pass: the passes' prefill workspace (reused by
 // all three, which run in stream order), then four state sets of B*H*d*d
 // floats: init^T, dS_fin / lambda, its transpose, and the dv pass's final
@@ -556,6 +605,22 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
 }  // namespace
 
 extern "C" {
+
+size_t lightning_attn_fwd_chdecay_workspace_size(int B, int H, int64_t N, int d, int block,
+                                                 la_dtype dt, int64_t segment_tokens) {
+  if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
+  if ((int64_t)B * H == 0) return 0;
+  return plan_fixed(B, H, N, d, dt, segment_tokens, false, true).ws_bytes;
+}
+
+la_status lightning_attn_fwd_chdecay(const void *q, const void *k, const void *v,
+                                     const float *alpha, int B, int H, int64_t N, int d, int block,
+                                     la_dtype dt, la_layout layout, const float *init_state,
+                                     void *out, float *final_state, int64_t segment_tokens,
+                                     void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return fwd_chdecay(q, k, v, alpha, B, H, N, d, block, dt, layout, init_state, out, final_state,
+                     segment_tokens, workspace, workspace_bytes, hip_stream);
+}
 
 size_t lightning_attn_bwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
                                          int64_t segment_tokens) {

@@ -46,6 +46,20 @@ def decay_schedule(H):
     return np.asarray(lam, dtype=np.float64).astype(np.float32)
 
 
+def chdecay_schedule(H, d, seed=7):
+    """float32 per-channel decays [H, d] for the channel-wise variant: around
+    head h's scalar rate 2^(-8 (h+1) / H), channel i decays at that rate times
+    2^u_i with u_i ~ U(-3, 1) (seeded), alpha = exp(-rate) -- a head's
+    channels span 16x in decay rate, all alpha >= 0.15; channel 0 of every
+    head is exactly 1."""
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(-3.0, 1.0, (H, d))
+    rate = (2.0 ** (-8.0 * (np.arange(H)[:, None] + 1) / H)) * 2.0 ** u
+    a = np.exp(-rate)
+    a[:, 0] = 1.0
+    return a.astype(np.float32)
+
+
 def round_to_bf16(x):
     """Round float32 values to the nearest bf16 (ties to even); returns the
     rounded values as float32 (every bf16 is exactly a float32)."""

@@ -134,6 +134,15 @@ def test_local_state_zero_weight_chunks(dtype, d, seg, prefill_path):
                  lam=[0.3, 0.8, 0.93, 0.97, 0.99, 0.999])
 
 
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "fp32")])
+def test_decay_one_across_segments(d, dtype, prefill_path):
+    """lambda = 1 exactly (plain causal linear attention) in heads whose
+    sequences cross segment cuts: no token of a local-state pass may be
+    skipped as weightless."""
+    run_fwd_case(1, 3, 3000, d, dtype, seed=65 + d, seg=1024, with_init=True,
+                 lam=[1.0, 0.9, 1.0])
+
+
 def test_initial_state_bf16(prefill_path):
     run_fwd_case(1, 4, 2048, 128, "bf16", seed=50, with_init=True, seg=512)
     run_fwd_case(2, 40, 1500, 128, "bf16", seed=51, with_init=True)

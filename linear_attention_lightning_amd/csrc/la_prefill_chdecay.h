@@ -20,8 +20,9 @@
 //
 // Workgroup = (segment, head), 8 waves as in the scalar kernel: output waves
 // 0-3 each own query rows 16w..16w+15 of a chunk; state waves 4-7 own state
-// rows 32u..32u+31, load the next chunk's K and V through registers (scaling
-// K on the way into LDS) while they update the state, and publish S^T.
+// rows 32u..32u+31, load K and V two chunks ahead through registers (scaling
+// K on the way into LDS) while they update the state, and publish S^T; the
+// output waves load Q two chunks ahead likewise.
 #pragma once
 
 #include "la_prefill_mfma.h"
@@ -32,8 +33,9 @@ namespace mfma {
 constexpr int TC = 64;        // tokens per chunk of the channel-wise kernel
 constexpr int CH_PIVOT = 32;  // pivot row of the decay factorisation
 constexpr int LDS_CH_K = TC * KV_ROW;  // one 64 x 128 bf16 tile (16 KB)
-// K~ and V tiles, S^T, log2 alpha of the head's channels.
-constexpr int LDS_CH = 2 * LDS_CH_K + LDS_ST + D * 4;
+// K~ and V tiles, the output staging tile, S^T, log2 alpha of the head's
+// channels.
+constexpr int LDS_CH = 3 * LDS_CH_K + LDS_ST + D * 4;
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
@@ -119,8 +121,8 @@ __device__ __forceinline__ void ch_issue_q(u32x4 (&q)[4], const FwdArgs &p, int 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void chdecay_chunk_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_CH];
-  char *Ks = smem, *Vs = smem + LDS_CH_K, *STs = smem + 2 * LDS_CH_K;
-  float *l2a = (float *)(smem + 2 * LDS_CH_K + LDS_ST);
+  char *Ks = smem, *Vs = smem + LDS_CH_K, *Os = smem + 2 * LDS_CH_K, *STs = smem + 3 * LDS_CH_K;
+  float *l2a = (float *)(smem + 3 * LDS_CH_K + LDS_ST);
   const Lanes ln;
   const SeqMap &m = p.m;
   const int H = m.H;
@@ -140,17 +142,24 @@ void chdecay_chunk_kernel(FwdArgs p) {
     const unsigned vq = kv_off(4 * G + (i16 >> 2), 8 * (i16 & 3));
     const unsigned st = lds_u32(STs) + kq;
     const unsigned kbase = lds_u32(Ks), vbase = lds_u32(Vs);
-    u32x4 qn[4];
-    ch_issue_q(qn, p, h, cur, w, i16, G);
-    while (true) {
-      const Cursor nxt = next_chunk<false>(m, cur, b, TC);
+    // Q two chunks ahead in two register sets; loads past the segment's
+    // last chunk re-read it (never used), so every load is unconditional.
+    u32x4 qn[2][4];
+    Cursor nxt = next_chunk<false>(m, cur, b, TC);
+    ch_issue_q(qn[0], p, h, cur, w, i16, G);
+    ch_issue_q(qn[1], p, h, nxt.valid ? nxt : cur, w, i16, G);
+    // One chunk: Q of `c` is in set sl; reloads set sl with chunk c + 2.
+    // Returns false after the segment's last chunk.
+    auto step = [&](auto slot_c, const Cursor &c, const Cursor &n1) -> bool {
+      constexpr int sl = decltype(slot_c)::value;
+      const Cursor n2 = n1.valid ? next_chunk<false>(m, n1, b, TC) : n1;
       __syncthreads();  // A: K~, V and S^T of this chunk are in LDS
       // Q scaled twice: alpha^(row+1) for the inter term, alpha^(row-32)
       // for the intra term.
       bf16x8 qi[4], qt[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 qv = __builtin_bit_cast(bf16x8, qn[ks]);
+        const bf16x8 qv = __builtin_bit_cast(bf16x8, qn[sl][ks]);
         const f32x4 la = *(const f32x4 *)(l2a + 32 * ks + 8 * G);
         const f32x4 lb = *(const f32x4 *)(l2a + 32 * ks + 8 * G + 4);
         const float l2e[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
@@ -163,7 +172,7 @@ void chdecay_chunk_kernel(FwdArgs p) {
         qi[ks] = cvt8(vi);
         qt[ks] = cvt8(vt);
       }
-      if (nxt.valid) ch_issue_q(qn, p, h, nxt, w, i16, G);
+      ch_issue_q(qn[sl], p, h, n2.valid ? n2 : c, w, i16, G);
       f32x4 acc[8];
       // inter term: O^T = S^T (Q (.) alpha^(row+1))^T
 #pragma unroll
@@ -184,12 +193,12 @@ void chdecay_chunk_kernel(FwdArgs p) {
           p0 = mma16(lds_ld<bf16x8>(kb ^ (ks << 6)), qt[ks], p0);
           p1 = mma16(lds_ld<bf16x8>((kb ^ (ks << 6)) + 16 * KV_ROW), qt[ks], p1);
         }
-        const int n0 = row - (32 * kp + 4 * G), n1 = n0 - 16;
+        const int n0 = row - (32 * kp + 4 * G), nn1 = n0 - 16;
         float pw[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           pw[r] = (n0 >= r) ? p0[r] : 0.f;
-          pw[4 + r] = (n1 >= r) ? p1[r] : 0.f;
+          pw[4 + r] = (nn1 >= r) ? p1[r] : 0.f;
         }
         const bf16x8 pb = cvt8(pw);
         const unsigned vb = vbase + 32 * kp * KV_ROW + vq;
@@ -201,25 +210,42 @@ void chdecay_chunk_kernel(FwdArgs p) {
       }
       __syncthreads();  // B: this chunk's K~, V and S^T reads are done
       {
-        // acc[jt] register r: feature 16 jt + 4 G + r of chunk row `row`:
-        // 8-byte stores through a buffer whose range ends with row L - 1.
-        const int L = (int)(cur.c1 - cur.c0);
-        const int rsb = (int)(m.rs * 2);
-        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (bf16 *)p.out + m.row_base(h, cur.j) + cur.c0 * m.rs, 0, (L - 1) * rsb + D * 2,
-            kRawBufferWord3);
-        const int off = row < L ? row * rsb : (int)0x80000000u;
+        // acc[jt] register r: feature 16 jt + 4 G + r of chunk row `row`.
+        // Staged in this wave's 16 rows of the output tile, then stored as
+        // whole rows (16 lanes x 16 bytes per row; partial-line streaming
+        // stores would cost HBM write efficiency) through a buffer whose
+        // range ends with row L - 1.
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
           const bf16x4 o4 = {(bf16)acc[jt][0], (bf16)acc[jt][1], (bf16)acc[jt][2],
                              (bf16)acc[jt][3]};
-          const int o = row < L ? off + (16 * jt + 4 * G) * 2 : off;
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), rsrc, o, 0,
-                                                kCpolNT);
+          *(bf16x4 *)(Os + kv_off(row, (16 * jt + 4 * G) * 2)) = o4;
+        }
+        const int L = (int)(c.c1 - c.c0);
+        const int rsb = (int)(m.rs * 2);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (bf16 *)p.out + m.row_base(h, c.j) + c.c0 * m.rs, 0, (L - 1) * rsb + D * 2,
+            kRawBufferWord3);
+        const int c16 = ln.lane & 15;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = 16 * w + 4 * it + (ln.lane >> 4);
+          const u32x4 x = *(const u32x4 *)(Os + kv_off(r, 16 * c16));
+          const int o = r < L ? r * rsb + 16 * c16 : (int)0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, o, 0, kCpolNT);
         }
       }
-      if (!nxt.valid) break;
+      return n1.valid;
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    while (true) {
+      if (!step(S0{}, cur, nxt)) break;
       cur = nxt;
+      nxt = next_chunk<false>(m, cur, b, TC);
+      if (!step(S1{}, cur, nxt)) break;
+      cur = nxt;
+      nxt = next_chunk<false>(m, cur, b, TC);
     }
   } else {
     const int u = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane, ts = ln.ts;
@@ -234,32 +260,57 @@ void chdecay_chunk_kernel(FwdArgs p) {
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     load_state(S, s0, u, l32, g);
-    ChTiles t;
-    ch_load_tiles(t, p, h, cur, ts);
-    ch_store_tiles(Ks, Vs, t, (int)(cur.c1 - cur.c0), l2f, ts);
+    // K/V two chunks ahead in two register sets (unconditional loads, as
+    // on the output side).
+    ChTiles t[2];
+    Cursor nxt = next_chunk<false>(m, cur, b, TC);
+    ch_load_tiles(t[0], p, h, cur, ts);
+    ch_load_tiles(t[1], p, h, nxt.valid ? nxt : cur, ts);
+    ch_store_tiles(Ks, Vs, t[0], (int)(cur.c1 - cur.c0), l2f, ts);
     write_st(STs, S, u, l32, g);
-    while (true) {
-      const Cursor nxt = next_chunk<false>(m, cur, b, TC);
+    // One chunk: the tiles of c are in LDS and set sl^1 holds chunk n1;
+    // set sl (already stored) is reloaded with chunk c + 2.
+    auto step = [&](auto slot_c, const Cursor &c, const Cursor &n1) -> bool {
+      constexpr int sl = decltype(slot_c)::value;
+      const Cursor n2 = n1.valid ? next_chunk<false>(m, n1, b, TC) : n1;
       __syncthreads();  // A
-      if (nxt.valid) ch_load_tiles(t, p, h, nxt, ts);
-      const int L = (int)(cur.c1 - cur.c0);
-      const bool seq_done = (cur.c1 == cur.seq_end);
-      const bool new_piece = nxt.valid && (nxt.c0 >= cur.pend);
-      if ((nxt.valid && !new_piece) || (seq_done && p.fin)) {
+      ch_load_tiles(t[sl], p, h, n2.valid ? n2 : c, ts);
+      const int L = (int)(c.c1 - c.c0);
+      const bool seq_done = (c.c1 == c.seq_end);
+      const bool new_piece = n1.valid && (n1.c0 >= c.pend);
+      if ((n1.valid && !new_piece) || (seq_done && p.fin)) {
+        float gam[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gam[r] = fast_exp2((float)L * l2row[r]);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) S[nt][r] *= fast_exp2((float)L * l2row[r]);
+          for (int r = 0; r < 16; ++r) S[nt][r] *= gam[r];
         ch_state_update(S, Ks, Vs, fast_exp2((float)(L - 1 - CH_PIVOT) * l2ch), u, lane);
-        if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, u, l32, g);
+        if (seq_done && p.fin) store_state(p.fin + ((int64_t)c.j * H + h) * DD, S, u, l32, g);
       }
       __syncthreads();  // B
-      if (!nxt.valid) break;
-      if (new_piece)
-        load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, u, l32, g);
-      ch_store_tiles(Ks, Vs, t, (int)(nxt.c1 - nxt.c0), l2f, ts);
+      if (!n1.valid) return false;
+      if (new_piece) {
+        load_state(S, p.init ? p.init + ((int64_t)n1.j * H + h) * DD : nullptr, u, l32, g);
+        // Waited for here, on this rare path: left to the compiler, the wait
+        // for these loads would land after the join, on every chunk, and
+        // take the prefetched tiles with it.
+        vm_wait<0>();
+      }
+      ch_store_tiles(Ks, Vs, t[sl ^ 1], (int)(n1.c1 - n1.c0), l2f, ts);
       write_st(STs, S, u, l32, g);
+      return true;
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    while (true) {
+      if (!step(S0{}, cur, nxt)) break;
       cur = nxt;
+      nxt = next_chunk<false>(m, cur, b, TC);
+      if (!step(S1{}, cur, nxt)) break;
+      cur = nxt;
+      nxt = next_chunk<false>(m, cur, b, TC);
     }
   }
 }

@@ -536,11 +536,13 @@ la_status fwd_chdecay(const void *q, const void *k, const void *v, const float *
 
 // Workspace of the backward pass: the passes' prefill workspace (reused by
 // all three, which run in stream order), then four state sets of B*H*d*d
-// floats: init^T, dS_fin / lambda, its transpose, and the dv pass's final
-// state.
+// floats (init^T, dS_fin / lambda, its transpose, the dv pass's final
+// state), then the dk pass's segment entering states (nseg*H*d*d floats,
+// when the plan cuts segments).
 size_t bwd_ws_bytes(const Plan &pl, int B, int H, int d) {
   const size_t al = 256;
-  return (pl.ws_bytes + al - 1) / al * al + 4 * state_bytes((int64_t)B * H, d);
+  return (pl.ws_bytes + al - 1) / al * al + 4 * state_bytes((int64_t)B * H, d) +
+         (pl.scan ? state_bytes(pl.nseg * H, d) : 0);
 }
 
 la_status bwd_fixed(const void *q, const void *k, const void *v, const float *decay,
@@ -577,9 +579,16 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
   float *g = (float *)((char *)initT + st_b);
   float *gT = (float *)((char *)g + st_b);
   float *fin_dv = (float *)((char *)gT + st_b);
-  if (init || dfinal)
-    hipLaunchKernelGGL(la::bwd_prep_kernel, sgrid, dim3(256), 0, s, init, dfinal, decay, H, d,
-                       initT, g, gT);
+  float *dk_in = (float *)((char *)fin_dv + st_b);  // dk pass entering states (pl.scan)
+  const dim3 tgrid((unsigned)BH, (unsigned)(d / 32), (unsigned)(d / 32));
+  if (init)
+    hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, init, 1, H, d, decay,
+                       false, initT);
+  if (dfinal) {
+    hipLaunchKernelGGL(la::bwd_scale_kernel, sgrid, dim3(256), 0, s, dfinal, decay, H, d, g);
+    hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, dfinal, 1, H, d,
+                       decay, true, gT);
+  }
   // dq: causal, from S_init^T
   la_status r = run_fwd(fixed_args(dout, v, k, dq, decay, B, H, N, d, dt, layout,
                                    init ? initT : nullptr, nullptr, pl, workspace, false),
@@ -589,11 +598,26 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
     r = run_fwd(fixed_args(k, q, dout, dv, decay, B, H, N, d, dt, layout,
                            dfinal ? g : nullptr, dinit ? fin_dv : nullptr, pl, workspace, true),
                 pl, d, dt, false, s);
-  // dk: reversed, keys do and values q, from (dS_fin / lambda)^T
-  if (r == LA_OK)
-    r = run_fwd(fixed_args(v, dout, q, dk, decay, B, H, N, d, dt, layout,
-                           dfinal ? gT : nullptr, nullptr, pl, workspace, true),
-                pl, d, dt, false, s);
+  // dk: reversed, keys do and values q, from (dS_fin / lambda)^T.  Its
+  // state is G^T over the same segments as the dv pass, so with segments
+  // its entering states are the dv pass's (left in the workspace by the
+  // scan) transposed, and only its output pass runs.
+  if (r == LA_OK) {
+    la::FwdArgs a = fixed_args(v, dout, q, dk, decay, B, H, N, d, dt, layout,
+                               dfinal ? gT : nullptr, nullptr, pl, workspace, true);
+    if (pl.scan) {
+      hipLaunchKernelGGL(la::transpose_states_kernel,
+                         dim3((unsigned)(pl.nseg * H), (unsigned)(d / 32), (unsigned)(d / 32)),
+                         dim3(256), 0, s, (const float *)workspace, pl.r_split, H, d, decay,
+                         false, dk_in);
+      a.ws = dk_in;
+      a.r_split = 1;
+      launch_phase(a, pl, d, dt, s, /*phase_a=*/false);
+      r = launch_status();
+    } else {
+      r = run_fwd(a, pl, d, dt, false, s);
+    }
+  }
   if (r == LA_OK && dinit) {
     hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, fin_dv, decay, H, d, true,
                        dinit);

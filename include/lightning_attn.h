@@ -312,6 +312,17 @@ la_status lightning_attn_fwd_chdecay(const void *q, const void *k, const void *v
                                      void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * One recurrent decode step with channel-wise decay (the decode counterpart
+ * of lightning_attn_fwd_chdecay):
+ *     state[i][j] <- alpha[h][i] state[i][j] + k[i] v[j],   out = q state.
+ *   alpha : [H][d] float32 DEVICE array.  Other arguments, layouts and errors
+ *           as for lightning_attn_decode.
+ */
+la_status lightning_attn_decode_chdecay(const void *q, const void *k, const void *v,
+                                        const float *alpha, float *state, void *out, int B, int H,
+                                        int d, la_dtype dt, void *hip_stream);
+
+/*
  * Backward pass of the fixed-length prefill (training): the gradients of a
  * scalar loss L with respect to q, k, v and the initial state, given
  * dout = dL/dout and dfinal = dL/dfinal_state.  The pages train with

@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
       -> (out, final_states, snapshots, snapshot_offsets)
   lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
   lightning_attn_fwd_chdecay(q, k, v, alpha, ...) -> (out, final_state)   (alpha [H, d])
+  lightning_attn_decode_chdecay(q, k, v, alpha, state, out=None) -> out
   lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, ...)
       -> (dq, dk, dv, dinit)
   lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode_state, ...)
@@ -30,6 +31,7 @@ __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd
            "lightning_attn_fwd_varlen_snapshots", "snapshot_row_offsets", "lightning_attn_decode",
            "lightning_attn_mixed_step", "lightning_attn_bwd", "lightning_attn_bwd_workspace_size",
            "lightning_attn_fwd_chdecay", "lightning_attn_fwd_chdecay_workspace_size",
+           "lightning_attn_decode_chdecay",
            "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
@@ -105,6 +107,8 @@ def load_library(path=None):
                                        Z, P]
     lib.lightning_attn_bwd.restype = I
     lib.lightning_attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
+    lib.lightning_attn_decode_chdecay.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
+    lib.lightning_attn_decode_chdecay.restype = I
     lib.lightning_attn_decode.restype = I
     if path is None:
         _lib = lib
@@ -355,9 +359,19 @@ def _fwd_varlen(q, k, v, decay, cu_seqlens, block, init_states, segment_tokens, 
     return out, final_states
 
 
+def lightning_attn_decode_chdecay(q, k, v, alpha, state, out=None):
+    """One decode step with channel-wise decay: alpha [H, d] float32; state
+    [B, H, d, d] float32 is updated in place (row i decays by alpha[h][i])."""
+    return _decode(q, k, v, alpha, state, out, channelwise=True)
+
+
 def lightning_attn_decode(q, k, v, decay, state, out=None):
     """One decode step: q, k, v [B, H, d]; state [B, H, d, d] float32 is
     updated in place (state <- lambda state + k^T v); returns out = q state."""
+    return _decode(q, k, v, decay, state, out, channelwise=False)
+
+
+def _decode(q, k, v, decay, state, out, channelwise):
     torch = _torch()
     lib = load_library()
     B, H, d = q.shape
@@ -365,15 +379,18 @@ def lightning_attn_decode(q, k, v, decay, state, out=None):
     _check(k, "k", q.shape, q.dtype, dev)
     _check(v, "v", q.shape, q.dtype, dev)
     _check(q, "q", q.shape, q.dtype, dev)
-    _check(decay, "decay", (H,), torch.float32, dev)
+    _check(decay, "alpha" if channelwise else "decay", (H, d) if channelwise else (H,),
+           torch.float32, dev)
     _check(state, "state", (B, H, d, d), torch.float32, dev)
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", q.shape, q.dtype, dev)
-    st = lib.lightning_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state), _ptr(out),
-                                   B, H, d, _dtype_code(q), _stream(dev))
+    fn = lib.lightning_attn_decode_chdecay if channelwise else lib.lightning_attn_decode
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(state), _ptr(out), B, H, d,
+            _dtype_code(q), _stream(dev))
     if st != 0:
-        raise LightningAttnError(st, "lightning_attn_decode")
+        raise LightningAttnError(st, "lightning_attn_decode_chdecay" if channelwise
+                                 else "lightning_attn_decode")
     return out
 
 

@@ -167,7 +167,9 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
 // stores are non-temporal: each byte is touched once per step and a batch's
 // state (512 MiB at 128 x 64 heads) is larger than the 256 MB Infinity Cache,
 // so keeping it out of the caches frees them for everything else.
-template <typename Tin, int D>
+// CH: channel-wise decay, decay is [H][D] and row i of the state decays by
+// decay[h][i] (S <- diag(alpha) S + k^T v).
+template <typename Tin, int D, bool CH = false>
 __global__ __launch_bounds__(256) void decode_kernel(const Tin *__restrict__ q,
                                                      const Tin *__restrict__ k,
                                                      const Tin *__restrict__ v,
@@ -175,15 +177,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const Tin *__restrict__ q,
                                                      float *__restrict__ state, Tin *__restrict__ out,
                                                      int H) {
   constexpr int CG = D / 4, RG = 256 / CG, RPT = D / RG;
-  __shared__ float qs[D], ks[D];
+  __shared__ float qs[D], ks[D], as[CH ? D : 1];
   __shared__ float red[RG][D];
   const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
   const int64_t bh = blockIdx.x;
   const int h = (int)(bh % H);
-  const float lam = decay[h];
+  const float lam = CH ? 1.f : decay[h];
   if (tid < D) {
     qs[tid] = to_f32(q[bh * D + tid]);
     ks[tid] = to_f32(k[bh * D + tid]);
+    if constexpr (CH) as[tid] = decay[(int64_t)h * D + tid];
   }
   f32x4 vv;
 #pragma unroll
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const Tin *__restrict__ q,
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const int i = rg * RPT + r;
-    sv[r] = lam * sv[r] + ks[i] * vv;
+    sv[r] = (CH ? as[i] : lam) * sv[r] + ks[i] * vv;
     o += qs[i] * sv[r];
     __builtin_nontemporal_store(sv[r], &S[i * CG + cg]);
   }

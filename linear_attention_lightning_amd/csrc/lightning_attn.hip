@@ -486,27 +486,35 @@ la_status check_decode(const void *q, const void *k, const void *v, const float 
   return LA_OK;
 }
 
-void launch_decode(const void *q, const void *k, const void *v, const float *decay, float *state,
-                   void *out, int B, int H, int d, la_dtype dt, hipStream_t st) {
+template <bool CH>
+void launch_decode_t(const void *q, const void *k, const void *v, const float *decay,
+                     float *state, void *out, int B, int H, int d, la_dtype dt, hipStream_t st) {
   if ((int64_t)B * H == 0) return;
   dim3 grid((unsigned)((int64_t)B * H));
   if (dt == LA_BF16) {
     if (d == 128)
-      hipLaunchKernelGGL((la::decode_kernel<bf16, 128>), grid, dim3(256), 0, st, (const bf16 *)q,
-                         (const bf16 *)k, (const bf16 *)v, decay, state, (bf16 *)out, H);
+      hipLaunchKernelGGL((la::decode_kernel<bf16, 128, CH>), grid, dim3(256), 0, st,
+                         (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, decay, state,
+                         (bf16 *)out, H);
     else
-      hipLaunchKernelGGL((la::decode_kernel<bf16, 64>), grid, dim3(256), 0, st, (const bf16 *)q,
-                         (const bf16 *)k, (const bf16 *)v, decay, state, (bf16 *)out, H);
+      hipLaunchKernelGGL((la::decode_kernel<bf16, 64, CH>), grid, dim3(256), 0, st,
+                         (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, decay, state,
+                         (bf16 *)out, H);
   } else {
     if (d == 128)
-      hipLaunchKernelGGL((la::decode_kernel<float, 128>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((la::decode_kernel<float, 128, CH>), grid, dim3(256), 0, st,
                          (const float *)q, (const float *)k, (const float *)v, decay, state,
                          (float *)out, H);
     else
-      hipLaunchKernelGGL((la::decode_kernel<float, 64>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((la::decode_kernel<float, 64, CH>), grid, dim3(256), 0, st,
                          (const float *)q, (const float *)k, (const float *)v, decay, state,
                          (float *)out, H);
   }
+}
+
+void launch_decode(const void *q, const void *k, const void *v, const float *decay, float *state,
+                   void *out, int B, int H, int d, la_dtype dt, hipStream_t st) {
+  launch_decode_t<false>(q, k, v, decay, state, out, B, H, d, dt, st);
 }
 
 // Channel-wise decay prefill (fixed length): the vector-ALU kernels with
@@ -768,6 +776,16 @@ la_status lightning_attn_decode(const void *q, const void *k, const void *v, con
   if (st != LA_OK) return st;
   if ((int64_t)B * H == 0) return LA_OK;
   launch_decode(q, k, v, decay, state, out, B, H, d, dt, (hipStream_t)hip_stream);
+  return launch_status();
+}
+
+la_status lightning_attn_decode_chdecay(const void *q, const void *k, const void *v,
+                                        const float *alpha, float *state, void *out, int B, int H,
+                                        int d, la_dtype dt, void *hip_stream) {
+  const la_status st = check_decode(q, k, v, alpha, state, out, B, H, d, dt);
+  if (st != LA_OK) return st;
+  if ((int64_t)B * H == 0) return LA_OK;
+  launch_decode_t<true>(q, k, v, alpha, state, out, B, H, d, dt, (hipStream_t)hip_stream);
   return launch_status();
 }
 

@@ -140,3 +140,61 @@ def test_chdecay_full_layer_h64_n32k():
         eo, ef = rel_err(host(out[:, sl]), o_ref), rel_err(host(fin[:, sl]), f_ref)
         say("   head %d err out %.3e state %.3e" % (h, eo, ef))
         assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (128, "fp32"), (64, "fp32")])
+def test_chdecay_decode_steps(d, dtype):
+    """Channel-wise decode steps (state row i decays by alpha_i) against the
+    oracle's channel-wise recurrence run one token at a time from the state."""
+    torch = torch_mod()
+    B, H, steps = 3, 4, 10
+    say("case chdecay decode B=%d H=%d d=%d %s" % (B, H, d, dtype))
+    q, k, v = inputs.host_qkv((steps, B, H, d), 650 + d, dtype=dtype)
+    alpha = inputs.chdecay_schedule(H, d, 651)
+    S0 = inputs.host_state((B, H, d, d), 652)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tq, tk, tv = (torch.from_numpy(x).cuda().to(tdt) for x in (q, k, v))
+    st = torch.from_numpy(S0).cuda()
+    ta = torch.from_numpy(alpha).cuda()
+    S = S0.astype(np.float64)
+    worst = 0.0
+    for t in range(steps):
+        o = la.lightning_attn_decode_chdecay(tq[t], tk[t], tv[t], ta, st)
+        o_ref, S = oracle.fwd_chdecay(q[t][:, :, None], k[t][:, :, None], v[t][:, :, None], alpha,
+                                      init=S)
+        worst = max(worst, rel_err(host(o), o_ref[:, :, 0]))
+    torch.cuda.synchronize()
+    es = rel_err(host(st), S)
+    say("   err out %.3e state %.3e" % (worst, es))
+    assert worst <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_chdecay_decode_continues_prefill():
+    """Decoding token N-1 from the channel-wise prefill's state after N-1
+    tokens reproduces the prefill's row N-1 (recurrent form)."""
+    torch = torch_mod()
+    B, H, N, d = 2, 4, 300, 128
+    tq, tk, tv = inputs.device_qkv((B, H, N, d), 660, "bf16")
+    ta = torch.from_numpy(inputs.chdecay_schedule(H, d, 661)).cuda()
+    out, _ = la.lightning_attn_fwd_chdecay(tq, tk, tv, ta, segment_tokens=128)
+    _, st = la.lightning_attn_fwd_chdecay(tq[:, :, :N - 1].contiguous(),
+                                          tk[:, :, :N - 1].contiguous(),
+                                          tv[:, :, :N - 1].contiguous(), ta, segment_tokens=128)
+    o = la.lightning_attn_decode_chdecay(tq[:, :, N - 1].contiguous(),
+                                         tk[:, :, N - 1].contiguous(),
+                                         tv[:, :, N - 1].contiguous(), ta, st)
+    torch.cuda.synchronize()
+    e = rel_err(host(o), host(out[:, :, N - 1]))
+    say("   decode vs prefill row: %.3e" % e)
+    assert e <= TOL["bf16"]
+
+
+def test_chdecay_empty_sequences_keep_the_state():
+    torch = torch_mod()
+    B, H, d = 2, 3, 128
+    q = torch.empty(B, H, 0, d, dtype=torch.bfloat16, device="cuda")
+    init = torch.randn(B, H, d, d, device="cuda")
+    ta = torch.from_numpy(inputs.chdecay_schedule(H, d)).cuda()
+    _, fin = la.lightning_attn_fwd_chdecay(q, q.clone(), q.clone(), ta, init_state=init)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, init)

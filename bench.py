@@ -441,8 +441,14 @@ def cpu_baseline(gpu_tensors, H, N, d, heads):
     _, _, used = oracle.fwd(q, k, v, lam)
     dt = time.perf_counter() - t0
     frac = heads / H
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(N / (dt / frac), 1), "unit": "tokens/s", "cores": used,
-            "kind": "oracle",
+            "cpu_model": model, "kind": "oracle",
             "sample": "%d of %d heads, all %d tokens of the B=1 H=64 N=32768 d=128 workload "
                       "(double-precision recurrence), %.1f s wall; scaled to all heads"
                       % (heads, H, N, dt)}

@@ -717,13 +717,11 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 // 0) and accepts a negative row stride (the time-reversed views of the
 // backward pass).  Without it the kernel keeps the plain walk's registers.
 template <bool SERVE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_chunk_kernel(FwdArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+__device__ __forceinline__ void chunk_workgroup(const FwdArgs &p, int bid, char *smem) {
   const Lanes ln;
   const SeqMap &m = p.m;
   const int H = m.H;
-  const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  const int s = bid / H, h = bid - (bid / H) * H;
   const Decay dc(p.decay[h]);
   int64_t a, b;
   if (SERVE) {
@@ -759,6 +757,24 @@ void prefill_chunk_kernel(FwdArgs p) {
     load_state(S, s0, ln.w, ln.l32, ln.g);
     state_loop<SERVE>(p, h, b, cur, S, smem, dc, ln);
   }
+}
+
+template <bool SERVE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_chunk_kernel(FwdArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  chunk_workgroup<SERVE>(p, blockIdx.x, smem);
+}
+
+// Two output passes of the same plan in one grid (the backward's dv and dk
+// passes): workgroup 2i runs workgroup i of pass a, 2i + 1 workgroup i of
+// pass b.  The two workgroups of a pair walk the same chunks of the same
+// (segment, head) side by side, so the inputs the passes share are read
+// from HBM once and found in the Infinity Cache by the other.
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_chunk_pair_kernel(FwdArgs a, FwdArgs b) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  chunk_workgroup<true>((blockIdx.x & 1) ? b : a, blockIdx.x >> 1, smem);
 }
 
 // Single-pass prefill with the segment scan folded in (MiniMax-01 report,

@@ -232,8 +232,10 @@ struct PhaseEvents {
   }
 };
 
+// out_pass = false: only the local-state pass and the scan (the segment
+// entering states), for a caller that launches the output pass itself.
 la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, bool has_empty,
-                  hipStream_t st, void *const *events = nullptr) {
+                  hipStream_t st, void *const *events = nullptr, bool out_pass = true) {
   la::FwdArgs a = base;
   const int H = a.m.H;
   a.r_split = pl.r_split;
@@ -291,7 +293,7 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
     }
   }
   pe.mark(2);
-  if (pl.nseg > 0) {
+  if (pl.nseg > 0 && out_pass) {
     if (!pl.scan) a.ws = nullptr;
     launch_phase(a, pl, d, dt, st, /*phase_a=*/false);
   }
@@ -601,30 +603,40 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
   la_status r = run_fwd(fixed_args(dout, v, k, dq, decay, B, H, N, d, dt, layout,
                                    init ? initT : nullptr, nullptr, pl, workspace, false),
                         pl, d, dt, false, s);
-  // dv: reversed, keys q and values do, from dS_fin / lambda; its final state is G_0
-  if (r == LA_OK)
-    r = run_fwd(fixed_args(k, q, dout, dv, decay, B, H, N, d, dt, layout,
-                           dfinal ? g : nullptr, dinit ? fin_dv : nullptr, pl, workspace, true),
-                pl, d, dt, false, s);
-  // dk: reversed, keys do and values q, from (dS_fin / lambda)^T.  Its
-  // state is G^T over the same segments as the dv pass, so with segments
-  // its entering states are the dv pass's (left in the workspace by the
-  // scan) transposed, and only its output pass runs.
+  // dv: reversed, keys q and values do, from dS_fin / lambda; its final
+  // state is G_0.  dk: reversed, keys do and values q, from
+  // (dS_fin / lambda)^T.  The dk pass's state is G^T over the same segments,
+  // so with segments its entering states are the dv pass's (left in the
+  // workspace by the scan) transposed: only the dv pass runs the local-state
+  // pass and the scan.
+  la::FwdArgs av = fixed_args(k, q, dout, dv, decay, B, H, N, d, dt, layout,
+                              dfinal ? g : nullptr, dinit ? fin_dv : nullptr, pl, workspace, true);
+  la::FwdArgs ak = fixed_args(v, dout, q, dk, decay, B, H, N, d, dt, layout,
+                              dfinal ? gT : nullptr, nullptr, pl, workspace, true);
+  if (r == LA_OK) r = run_fwd(av, pl, d, dt, false, s, nullptr, /*out_pass=*/false);
   if (r == LA_OK) {
-    la::FwdArgs a = fixed_args(v, dout, q, dk, decay, B, H, N, d, dt, layout,
-                               dfinal ? gT : nullptr, nullptr, pl, workspace, true);
     if (pl.scan) {
       hipLaunchKernelGGL(la::transpose_states_kernel,
                          dim3((unsigned)(pl.nseg * H), (unsigned)(d / 32), (unsigned)(d / 32)),
                          dim3(256), 0, s, (const float *)workspace, pl.r_split, H, d, decay,
                          false, dk_in);
-      a.ws = dk_in;
-      a.r_split = 1;
-      launch_phase(a, pl, d, dt, s, /*phase_a=*/false);
-      r = launch_status();
+      av.r_split = pl.r_split;
+      ak.ws = dk_in;
+      ak.r_split = 1;
     } else {
-      r = run_fwd(a, pl, d, dt, false, s);
+      av.ws = nullptr;
+      ak.ws = nullptr;
     }
+    if (use_mfma(d, dt)) {
+      // Both output passes in one grid, paired workgroup by workgroup, so
+      // that q and do (read by both) come from HBM about once.
+      hipLaunchKernelGGL(la::mfma::prefill_chunk_pair_kernel,
+                         dim3((unsigned)(2 * pl.nseg * H)), dim3(la::mfma::NT), 0, s, av, ak);
+    } else {
+      launch_phase(av, pl, d, dt, s, /*phase_a=*/false);
+      launch_phase(ak, pl, d, dt, s, /*phase_a=*/false);
+    }
+    r = launch_status();
   }
   if (r == LA_OK && dinit) {
     hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, fin_dv, decay, H, d, true,

@@ -364,6 +364,29 @@ la_status lightning_attn_bwd(const void *q, const void *k, const void *v, const 
                              void *hip_stream);
 
 /*
+ * lightning_attn_bwd for packed variable-length sequences (training on
+ * packed data, MiniMax-01 report section 3.2): q, k, v, dout, dq, dk, dv as
+ * for lightning_attn_fwd_varlen_layout; dfinals, init_states and dinits are
+ * [num_seqs][H][d][d] float32 (dfinals and init_states may be NULL, dinits
+ * NULL when not wanted).  Every sequence is independent; a zero-length
+ * sequence gets dinits = dfinals.  The anti-causal passes run over a
+ * time-reversed view of each sequence in place.  Workspace from
+ * lightning_attn_bwd_varlen_workspace_size; other arguments, preconditions
+ * and errors as for lightning_attn_bwd and lightning_attn_fwd_varlen_layout.
+ */
+size_t lightning_attn_bwd_varlen_workspace_size(int num_seqs, int H, int64_t total_N, int d,
+                                                int block, la_dtype dt, int64_t segment_tokens);
+
+la_status lightning_attn_bwd_varlen(const void *q, const void *k, const void *v,
+                                    const float *decay, const void *dout,
+                                    const int32_t *cu_seqlens, int num_seqs, int H,
+                                    int64_t total_N, int d, int block, la_dtype dt,
+                                    la_layout layout, const float *dfinals,
+                                    const float *init_states, void *dq, void *dk, void *dv,
+                                    float *dinits, int64_t segment_tokens, void *workspace,
+                                    size_t workspace_bytes, void *hip_stream);
+
+/*
  * One step of a mixed serving batch (MiniMax-01 report, section 3.3.2:
  * inputs of one token are memory-bound and need few compute units, so they
  * go to a kernel of their own, separate from the inputs of more than one

@@ -20,6 +20,7 @@ Entry points (same names as the C ABI):
   lightning_attn_decode_chdecay(q, k, v, alpha, state, out=None) -> out
   lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, ...)
       -> (dq, dk, dv, dinit)
+  lightning_attn_bwd_varlen(q, k, v, decay, dout, cu_seqlens, ...) -> (dq, dk, dv, dinits)
   lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode_state, ...)
       -> (prefill_out, final_states, decode_out)   (decode_state updated in place)
 """
@@ -31,7 +32,8 @@ __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd
            "lightning_attn_fwd_varlen_snapshots", "snapshot_row_offsets", "lightning_attn_decode",
            "lightning_attn_mixed_step", "lightning_attn_bwd", "lightning_attn_bwd_workspace_size",
            "lightning_attn_fwd_chdecay", "lightning_attn_fwd_chdecay_workspace_size",
-           "lightning_attn_decode_chdecay",
+           "lightning_attn_decode_chdecay", "lightning_attn_bwd_varlen",
+           "lightning_attn_bwd_varlen_workspace_size",
            "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
@@ -68,6 +70,11 @@ def load_library(path=None):
     if not os.path.exists(p):
         raise RuntimeError("HIP library %s is not built; run "
                            "`python -m linear_attention_lightning_amd.build`" % p)
+    # The library and PyTorch must use one HIP runtime (streams and device
+    # pointers cross between them).  PyTorch ships its own libamdhip64 with
+    # the same soname as the system one the library links, and the copy that
+    # loads first serves both: importing torch first makes that PyTorch's.
+    _torch()
     lib = ctypes.CDLL(p)
     P, I, L, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
     lib.lightning_attn_status_string.argtypes = [I]
@@ -106,6 +113,11 @@ def load_library(path=None):
     lib.lightning_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, L, I, I, I, I, L, P,
                                        Z, P]
     lib.lightning_attn_bwd.restype = I
+    lib.lightning_attn_bwd_varlen_workspace_size.argtypes = [I, I, L, I, I, I, L]
+    lib.lightning_attn_bwd_varlen_workspace_size.restype = Z
+    lib.lightning_attn_bwd_varlen.argtypes = [P, P, P, P, P, P, I, I, L, I, I, I, I, P, P, P, P,
+                                              P, P, L, P, Z, P]
+    lib.lightning_attn_bwd_varlen.restype = I
     lib.lightning_attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
     lib.lightning_attn_decode_chdecay.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
     lib.lightning_attn_decode_chdecay.restype = I
@@ -557,3 +569,60 @@ def lightning_attn_fwd_chdecay(q, k, v, alpha, layout=LA_HEAD_MAJOR, block=128, 
     if st != 0:
         raise LightningAttnError(st, "lightning_attn_fwd_chdecay")
     return out, final_state
+
+
+def lightning_attn_bwd_varlen_workspace_size(num_seqs, H, total, d, block=128, dtype=LA_BF16,
+                                             segment_tokens=0):
+    return load_library().lightning_attn_bwd_varlen_workspace_size(num_seqs, H, total, d, block,
+                                                                    dtype, segment_tokens)
+
+
+def lightning_attn_bwd_varlen(q, k, v, decay, dout, cu_seqlens, layout=LA_HEAD_MAJOR, block=128,
+                              dfinals=None, init_states=None, segment_tokens=0, want_dinit=True,
+                              dq=None, dk=None, dv=None, dinits=None, workspace=None):
+    """Gradients of lightning_attn_fwd_varlen_layout: q, k, v, dout
+    [H, total, d] (LA_HEAD_MAJOR) or [total, H, d] (LA_TOKEN_MAJOR);
+    cu_seqlens int32 [num_seqs + 1]; dfinals and init_states
+    [num_seqs, H, d, d] float32 or None.  Returns (dq, dk, dv, dinits)."""
+    torch = _torch()
+    lib = load_library()
+    if layout == LA_TOKEN_MAJOR:
+        total, H, d = q.shape
+    elif layout == LA_HEAD_MAJOR:
+        H, total, d = q.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (dout, "dout"), (q, "q")):
+        _check(t, n, q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 offsets")
+    S = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32, dev)
+    for t, n in ((dfinals, "dfinals"), (init_states, "init_states")):
+        if t is not None:
+            _check(t, n, (S, H, d, d), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, q.shape, q.dtype, dev)
+    if want_dinit and dinits is None:
+        dinits = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    if dinits is not None:
+        _check(dinits, "dinits", (S, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    ws_bytes = lib.lightning_attn_bwd_varlen_workspace_size(S, H, total, d, block, dt,
+                                                             segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout),
+                                       _ptr(cu_seqlens), S, H, total, d, block, dt, layout,
+                                       _ptr(dfinals), _ptr(init_states), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), _ptr(dinits), segment_tokens, _ptr(workspace),
+                                       ws_have, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_bwd_varlen")
+    return dq, dk, dv, dinits

@@ -46,6 +46,9 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 //                              seq_extra = (H - 1) N d.
 //   packed [H][total][d]     : start(j) = cu[j], head_stride = total d,
 //                              seq_extra = 0.
+// A time-reversed packed view (virtual token start(j) + u is token
+// start(j+1) - 1 - u) negates rs and adds (start(j) + start(j+1) - 1) times
+// the forward row stride (rev_rs) to row_base.
 struct SeqMap {
   const int32_t *cu;  // device cu_seqlens, or nullptr for uniform length N
   int64_t N;
@@ -57,6 +60,8 @@ struct SeqMap {
   int64_t rs;  // elements between consecutive tokens of one head: d (head-major
                // layouts) or H*d (token-major layouts)
   int64_t snap_iv;  // prefix-state snapshot interval in tokens, 0 = none
+  int64_t rev_rs;   // time-reversed packed view (0: none): the row stride of the
+                    // forward layout; sequence j's base moves to its last token
 
   __device__ __forceinline__ int64_t start(int j) const {
     return cu ? (int64_t)cu[j] : (int64_t)j * N;
@@ -73,8 +78,13 @@ struct SeqMap {
     }
     return lo;
   }
+  // REV = false: the caller never sees a time-reversed packed view (rev_rs
+  // is 0) and keeps the plain address arithmetic.
+  template <bool REV = true>
   __device__ __forceinline__ int64_t row_base(int h, int j) const {
-    return (int64_t)h * head_stride + (int64_t)j * seq_extra;
+    int64_t r = (int64_t)h * head_stride + (int64_t)j * seq_extra;
+    if (REV && rev_rs) r += (start(j) + start(j + 1) - 1) * rev_rs;
+    return r;
   }
 };
 

@@ -48,7 +48,7 @@ struct ChTiles {
 __device__ __forceinline__ void ch_load_tiles(ChTiles &t, const FwdArgs &p, int h,
                                               const Cursor &c, int ts) {
   const int Lc = (int)(c.c1 - c.c0);
-  const int64_t base = p.m.row_base(h, c.j) + c.c0 * p.m.rs;
+  const int64_t base = p.m.row_base<false>(h, c.j) + c.c0 * p.m.rs;
   const bf16 *kb = (const bf16 *)p.k + base, *vb = (const bf16 *)p.v + base;
   const int c16 = ts & 15;
 #pragma unroll
@@ -111,7 +111,7 @@ __device__ __forceinline__ void ch_issue_q(u32x4 (&q)[4], const FwdArgs &p, int 
                                            const Cursor &c, int w, int i16, int G) {
   const int Lc = (int)(c.c1 - c.c0);
   const int row = 16 * w + i16;
-  const bf16 *qrow = (const bf16 *)p.q + p.m.row_base(h, c.j) +
+  const bf16 *qrow = (const bf16 *)p.q + p.m.row_base<false>(h, c.j) +
                      (c.c0 + (row < Lc ? row : Lc - 1)) * p.m.rs + 8 * G;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -224,7 +224,7 @@ void chdecay_chunk_kernel(FwdArgs p) {
         const int L = (int)(c.c1 - c.c0);
         const int rsb = (int)(m.rs * 2);
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (bf16 *)p.out + m.row_base(h, c.j) + c.c0 * m.rs, 0, (L - 1) * rsb + D * 2,
+            (bf16 *)p.out + m.row_base<false>(h, c.j) + c.c0 * m.rs, 0, (L - 1) * rsb + D * 2,
             kRawBufferWord3);
         const int c16 = ln.lane & 15;
 #pragma unroll

@@ -394,12 +394,13 @@ struct OutLane {
 // Q^T fragments of chunk c for query block bi of this output wave, straight
 // from HBM (B operand of the 16x16x32 products: qf[ks] holds features
 // 32 ks + 8 G .. + 7 of query row 16 qblock(bi) + i16).  Non-temporal loads.
+template <bool REV = false>
 __device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cursor &c, int bi,
                                               u32x4 (&qf)[4], const OutLane &o) {
   // Rows past the chunk's end read its last row: their outputs are never stored.
   const int Lc = (int)(c.c1 - c.c0);
   const int row = 16 * o.qblock(bi) + o.i16;
-  const bf16 *qrow = (const bf16 *)p.q + p.m.row_base(h, c.j) +
+  const bf16 *qrow = (const bf16 *)p.q + p.m.row_base<REV>(h, c.j) +
                      (c.c0 + (row < Lc ? row : Lc - 1)) * p.m.rs + 8 * o.G;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -411,7 +412,7 @@ __device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cur
 __device__ __forceinline__ void issue_kv_loads(const FwdArgs &p, int h, const Cursor &c,
                                                u32x4 (&pk)[8], u32x4 (&pv)[8], const Lanes &ln) {
   const int Lc = (int)(c.c1 - c.c0);
-  const int64_t base = p.m.row_base(h, c.j) + c.c0 * p.m.rs;
+  const int64_t base = p.m.row_base<false>(h, c.j) + c.c0 * p.m.rs;
   load_tile<256>(pk, (const bf16 *)p.k + base, p.m.rs, Lc, ln.ts);
   load_tile<256>(pv, (const bf16 *)p.v + base, p.m.rs, Lc, ln.ts);
 }
@@ -446,10 +447,11 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, const char *lds) {
 // chunk's end repeat its last row (finite values that every consumer masks).
 // Eight memory instructions per call.
 // Instruction k (0..7) of the above: rows 32u + 4k .. 32u + 4k + 3.
+template <bool REV = false>
 __device__ __forceinline__ void dma_tile_quad(char *tile, const void *src, const FwdArgs &p, int h,
                                               const Cursor &c, int u, int lane, int k) {
   const int Lc = (int)(c.c1 - c.c0);
-  const bf16 *base = (const bf16 *)src + p.m.row_base(h, c.j) + c.c0 * p.m.rs;
+  const bf16 *base = (const bf16 *)src + p.m.row_base<REV>(h, c.j) + c.c0 * p.m.rs;
   const int sub = lane >> 4, pg = lane & 15;
   const int r = 32 * u + 4 * k + sub;
   const int rr = r < Lc ? r : Lc - 1;
@@ -457,10 +459,11 @@ __device__ __forceinline__ void dma_tile_quad(char *tile, const void *src, const
   lds_dma16(gp, tile + (32 * u + 4 * k) * KV_ROW);
 }
 
+template <bool REV = false>
 __device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const FwdArgs &p, int h,
                                               const Cursor &c, int u, int lane) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) dma_tile_quad(tile, src, p, h, c, u, lane, k);
+  for (int k = 0; k < 8; ++k) dma_tile_quad<REV>(tile, src, p, h, c, u, lane, k);
 }
 
 // Writes this output wave's 32 staged rows of chunk c as whole rows: per
@@ -476,7 +479,8 @@ __device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const
 // decreasing addresses): the buffer then starts at the chunk's last row, the
 // lowest address, and row r sits at byte (L - 1 - r) * |rsb|; rows >= L are
 // given the offset 2^31, past the range (below 2^31 bytes), and dropped.
-template <bool NEG = false>
+// REV: the view may be a time-reversed packed view (see SeqMap::row_base).
+template <bool NEG = false, bool REV = false>
 __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor &c, unsigned Os,
                                            const OutLane &o) {
   const int L = (int)(c.c1 - c.c0);
@@ -488,7 +492,7 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
   const int flip = (NEG && rsb < 0) ? L - 1 : 0;
   const int span = (NEG && rsb < 0) ? -rsb : rsb;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (bf16 *)p.out + p.m.row_base(h, c.j) + (c.c0 + flip) * p.m.rs, 0, (L - 1) * span + D * 2,
+      (bf16 *)p.out + p.m.row_base<REV>(h, c.j) + (c.c0 + flip) * p.m.rs, 0, (L - 1) * span + D * 2,
       kRawBufferWord3);
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {
@@ -533,7 +537,7 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 // FAST: the decay weights take the factored powers (see Decay); a template
 // parameter so that each chunk step is one basic block the scheduler can
 // interleave freely.
-template <bool FAST, bool SNAP>
+template <bool FAST, bool SNAP, bool REV = false>
 __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                             u32x4 (&qn)[2][4], char *smem, const Decay &dc,
                                             const Lanes &ln) {
@@ -614,10 +618,10 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
 
       // The next chunk's Q^T: block 0 now, block 1 once this chunk's block 0
       // fragments are spent (keeps one 16-register set fewer alive).
-      if (nxt.valid) issue_q_loads(p, h, nxt, 0, qn[0], o);
+      if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 0, qn[0], o);
       inter_term(acc, STs + kq, qf, a_row);
       intra(std::integral_constant<int, 0>{}, w);
-      if (nxt.valid) issue_q_loads(p, h, nxt, 1, qn[1], o);
+      if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 1, qn[1], o);
       intra(std::integral_constant<int, 1>{}, 7 - w);
     }
     __syncthreads();  // B: this chunk's K/V and S^T reads are done
@@ -636,7 +640,7 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
           lds_st<bf16x4>(sb ^ (jt << 5), v);
         }
       }
-      write_rows<SNAP>(p, h, cur, Ks, o);
+      write_rows<SNAP, REV>(p, h, cur, Ks, o);
     }
     if (!nxt.valid) break;
     cur = nxt;
@@ -649,7 +653,7 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
 // (see above), updates the state and publishes it as S^T; writes every
 // sequence end's final state inside the segment, and the state at every
 // snapshot point the segment's chunks end on.
-template <bool SNAP>
+template <bool SNAP, bool REV = false>
 __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                            f32x16 (&S)[4], char *smem, const Decay &dc,
                                            const Lanes &ln) {
@@ -660,8 +664,8 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
   const int w = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane;
   const float l2 = dc.l2;
   int buf = 0;
-  dma_tile_rows(smem, p.k, p, h, cur, w, lane);
-  dma_tile_rows(smem + LDS_K, p.v, p, h, cur, w, lane);
+  dma_tile_rows<REV>(smem, p.k, p, h, cur, w, lane);
+  dma_tile_rows<REV>(smem + LDS_K, p.v, p, h, cur, w, lane);
   write_st(STs, S, w, l32, g);
   vm_wait<0>();
 
@@ -679,8 +683,8 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
       if (nxt.valid) {
         int ll = lane;
         asm volatile("" : "+v"(ll));
-        dma_tile_quad(Kn, p.k, p, h, nxt, w, ll, k);
-        dma_tile_quad(Vn, p.v, p, h, nxt, w, ll, k);
+        dma_tile_quad<REV>(Kn, p.k, p, h, nxt, w, ll, k);
+        dma_tile_quad<REV>(Vn, p.v, p, h, nxt, w, ll, k);
       }
     };
     const bool seq_done = (cur.c1 == cur.seq_end);
@@ -716,7 +720,9 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 // (when p.m.snap_iv > 0), takes one segment per sequence (when p.seg_len ==
 // 0) and accepts a negative row stride (the time-reversed views of the
 // backward pass).  Without it the kernel keeps the plain walk's registers.
-template <bool SERVE>
+// REV (with SERVE): the views may also be time-reversed packed views (the
+// backward pass over packed sequences, SeqMap::rev_rs).
+template <bool SERVE, bool REV = false>
 __device__ __forceinline__ void chunk_workgroup(const FwdArgs &p, int bid, char *smem) {
   const Lanes ln;
   const SeqMap &m = p.m;
@@ -744,18 +750,18 @@ __device__ __forceinline__ void chunk_workgroup(const FwdArgs &p, int bid, char 
   if (ln.out_wave) {
     u32x4 qn[2][4];
     const OutLane o(ln.lane, ln.w);
-    issue_q_loads(p, h, cur, 0, qn[0], o);
-    issue_q_loads(p, h, cur, 1, qn[1], o);
+    issue_q_loads<REV>(p, h, cur, 0, qn[0], o);
+    issue_q_loads<REV>(p, h, cur, 1, qn[1], o);
     if (dc.fast)
-      output_loop<true, SERVE>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<true, SERVE, REV>(p, h, b, cur, qn, smem, dc, ln);
     else
-      output_loop<false, SERVE>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<false, SERVE, REV>(p, h, b, cur, qn, smem, dc, ln);
   } else {
     f32x16 S[4];
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     load_state(S, s0, ln.w, ln.l32, ln.g);
-    state_loop<SERVE>(p, h, b, cur, S, smem, dc, ln);
+    state_loop<SERVE, REV>(p, h, b, cur, S, smem, dc, ln);
   }
 }
 
@@ -771,10 +777,13 @@ void prefill_chunk_kernel(FwdArgs p) {
 // pass b.  The two workgroups of a pair walk the same chunks of the same
 // (segment, head) side by side, so the inputs the passes share are read
 // from HBM once and found in the Infinity Cache by the other.
+// REV: the passes are time-reversed packed views (SeqMap::rev_rs may be
+// non-zero); without it the address arithmetic leaves that term out.
+template <bool REV>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_chunk_pair_kernel(FwdArgs a, FwdArgs b) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-  chunk_workgroup<true>((blockIdx.x & 1) ? b : a, blockIdx.x >> 1, smem);
+  chunk_workgroup<true, REV>((blockIdx.x & 1) ? b : a, blockIdx.x >> 1, smem);
 }
 
 // Single-pass prefill with the segment scan folded in (MiniMax-01 report,
@@ -872,7 +881,7 @@ void prefill_fused_kernel(FusedArgs fa) {
   const int64_t ps0 = m.start(jl);
   const int64_t ps = ps0 > a ? ps0 : a;   // start of the segment's last piece
   const bool need_out = m.start(jl + 1) > b;  // that sequence continues after b
-  const int64_t kvb = m.row_base(h, jl);
+  const int64_t kvb = m.row_base<false>(h, jl);
 
   // Both roles pass the same barriers: two per tile of step 1, one after the
   // wait of step 2, one more after the record stores when publishing, then

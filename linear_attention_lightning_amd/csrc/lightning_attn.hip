@@ -139,12 +139,12 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
 // workspace, and the output pass alone is launched (it also gives empty
 // sequences their final state).
 Plan plan_varlen(int num_seqs, int H, int64_t total, int d, la_dtype dt,
-                 int64_t segment_tokens) {
+                 int64_t segment_tokens, bool allow_fused = true) {
   if (segment_tokens == kSegPerSeq) return Plan{0, num_seqs, false, false, 1, 0};
   Plan p{1, 0, true, false, 1, 0};
   if (total == 0) return p;
   const int T = chunk_tokens(d, dt);
-  const bool fused = want_fused(H, d, dt);
+  const bool fused = allow_fused && want_fused(H, d, dt);
   int64_t seg = segment_tokens;
   if (seg <= 0) {
     const int64_t G = ceil_div(target_groups(d, dt), H);
@@ -239,6 +239,10 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
   la::FwdArgs a = base;
   const int H = a.m.H;
   a.r_split = pl.r_split;
+  // A time-reversed packed view's output pass runs only in the paired
+  // backward kernel (the single-pass chunk kernels leave that term out).
+  if (a.m.rev_rs != 0 && (pl.fused || (out_pass && use_mfma(d, dt, a.chdecay != nullptr))))
+    return LA_ERR_UNSUPPORTED;
   PhaseEvents pe{events, st};
   pe.mark(0);
   if (pl.fused && pl.nseg > 0) {
@@ -338,6 +342,7 @@ la::FwdArgs fixed_args(const void *q, const void *k, const void *v, void *out, c
   a.m.H = H;
   a.m.total = (int64_t)B * N;
   a.m.snap_iv = 0;
+  a.m.rev_rs = 0;
   a.snaps = nullptr;
   a.snap_off = nullptr;
   a.chdecay = nullptr;
@@ -436,6 +441,7 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   a.m.H = H;
   a.m.total = total_N;
   a.m.seq_extra = 0;
+  a.m.rev_rs = 0;
   // An interval longer than every sequence yields no snapshot.
   a.m.snap_iv = (snap_iv > 0 && snap_iv <= total_N) ? snap_iv : 0;
   a.snaps = a.m.snap_iv ? snaps : nullptr;
@@ -555,6 +561,92 @@ size_t bwd_ws_bytes(const Plan &pl, int B, int H, int d) {
          (pl.scan ? state_bytes(pl.nseg * H, d) : 0);
 }
 
+// The backward pass on a planned problem.  args(q', k', v', out', init,
+// fin, reversed) builds the kernel arguments of one pass over the caller's
+// buffers (reversed: the time-reversed view); S = number of state sets
+// (batch entries or sequences); has_empty: a scan must also give empty
+// sequences their states.
+template <typename ArgFn>
+la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dtype dt,
+                   const float *decay, const void *q, const void *k, const void *v,
+                   const void *dout, const float *dfinal, const float *init, void *dq, void *dk,
+                   void *dv, float *dinit, bool any_token, bool has_empty, void *workspace,
+                   hipStream_t s) {
+  const int64_t SH = (int64_t)S * H;
+  const dim3 sgrid((unsigned)SH, (unsigned)ceil_div((int64_t)d * d, 256));
+  if (!any_token) {  // no token at all: dS_init = dS_fin
+    if (dinit) {
+      hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, dfinal, decay, H, d, false,
+                         dinit);
+      return launch_status();
+    }
+    return LA_OK;
+  }
+  char *w = (char *)workspace;
+  const size_t st_b = state_bytes(SH, d);
+  float *initT = (float *)(w + (pl.ws_bytes + 255) / 256 * 256);
+  float *g = (float *)((char *)initT + st_b);
+  float *gT = (float *)((char *)g + st_b);
+  float *fin_dv = (float *)((char *)gT + st_b);
+  float *dk_in = (float *)((char *)fin_dv + st_b);  // dk pass entering states (pl.scan)
+  const dim3 tgrid((unsigned)SH, (unsigned)(d / 32), (unsigned)(d / 32));
+  if (init)
+    hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, init, 1, H, d, decay,
+                       false, initT);
+  if (dfinal) {
+    hipLaunchKernelGGL(la::bwd_scale_kernel, sgrid, dim3(256), 0, s, dfinal, decay, H, d, g);
+    hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, dfinal, 1, H, d,
+                       decay, true, gT);
+  }
+  // dq: causal, from S_init^T
+  la_status r = run_fwd(args(dout, v, k, dq, init ? initT : nullptr, nullptr, false), pl, d, dt,
+                        has_empty, s);
+  // dv: reversed, keys q and values do, from dS_fin / lambda; its final
+  // state is G_0.  dk: reversed, keys do and values q, from
+  // (dS_fin / lambda)^T.  The dk pass's state is G^T over the same segments,
+  // so with segments its entering states are the dv pass's (left in the
+  // workspace by the scan) transposed: only the dv pass runs the local-state
+  // pass and the scan.
+  la::FwdArgs av = args(k, q, dout, dv, dfinal ? g : nullptr, dinit ? fin_dv : nullptr, true);
+  la::FwdArgs ak = args(v, dout, q, dk, dfinal ? gT : nullptr, nullptr, true);
+  if (r == LA_OK) r = run_fwd(av, pl, d, dt, has_empty, s, nullptr, /*out_pass=*/false);
+  if (r == LA_OK) {
+    if (pl.scan) {
+      hipLaunchKernelGGL(la::transpose_states_kernel,
+                         dim3((unsigned)(pl.nseg * H), (unsigned)(d / 32), (unsigned)(d / 32)),
+                         dim3(256), 0, s, (const float *)workspace, pl.r_split, H, d, decay,
+                         false, dk_in);
+      av.r_split = pl.r_split;
+      ak.ws = dk_in;
+      ak.r_split = 1;
+    } else {
+      av.ws = nullptr;
+      ak.ws = nullptr;
+    }
+    if (pl.nseg > 0) {
+      if (use_mfma(d, dt)) {
+        // Both output passes in one grid, workgroups paired (one launch).
+        if (av.m.rev_rs != 0)
+          hipLaunchKernelGGL(la::mfma::prefill_chunk_pair_kernel<true>,
+                             dim3((unsigned)(2 * pl.nseg * H)), dim3(la::mfma::NT), 0, s, av, ak);
+        else
+          hipLaunchKernelGGL(la::mfma::prefill_chunk_pair_kernel<false>,
+                             dim3((unsigned)(2 * pl.nseg * H)), dim3(la::mfma::NT), 0, s, av, ak);
+      } else {
+        launch_phase(av, pl, d, dt, s, /*phase_a=*/false);
+        launch_phase(ak, pl, d, dt, s, /*phase_a=*/false);
+      }
+    }
+    r = launch_status();
+  }
+  if (r == LA_OK && dinit) {
+    hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, fin_dv, decay, H, d, true,
+                       dinit);
+    r = launch_status();
+  }
+  return r;
+}
+
 la_status bwd_fixed(const void *q, const void *k, const void *v, const float *decay,
                     const void *dout, const float *dfinal, const float *init, void *dq, void *dk,
                     void *dv, float *dinit, int B, int H, int64_t N, int d, int block,
@@ -570,80 +662,75 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
-  const size_t need = bwd_ws_bytes(pl, B, H, d);
-  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)hip_stream;
-  const int64_t BH = (int64_t)B * H;
-  const dim3 sgrid((unsigned)BH, (unsigned)ceil_div((int64_t)d * d, 256));
-  if (N == 0) {  // no token: dS_init = dS_fin
-    if (dinit) {
-      hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, dfinal, decay, H, d, false,
-                         dinit);
-      return launch_status();
+  if (!workspace || workspace_bytes < bwd_ws_bytes(pl, B, H, d)) return LA_ERR_WORKSPACE;
+  auto args = [&](const void *q_, const void *k_, const void *v_, void *o_, const float *init_,
+                  float *fin_, bool reversed) {
+    return fixed_args(q_, k_, v_, o_, decay, B, H, N, d, dt, layout, init_, fin_, pl, workspace,
+                      reversed);
+  };
+  return bwd_core(args, pl, B, H, d, dt, decay, q, k, v, dout, dfinal, init, dq, dk, dv, dinit,
+                  N > 0, /*has_empty=*/false, workspace, (hipStream_t)hip_stream);
+}
+
+la_status bwd_varlen(const void *q, const void *k, const void *v, const float *decay,
+                     const void *dout, const int32_t *cu_seqlens, int num_seqs, int H,
+                     int64_t total_N, int d, int block, la_dtype dt, la_layout layout,
+                     const float *dfinals, const float *inits, void *dq, void *dk, void *dv,
+                     float *dinits, int64_t segment_tokens, void *workspace,
+                     size_t workspace_bytes, void *hip_stream) {
+  if (num_seqs < 0 || total_N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st == LA_OK) st = check_layout(layout, H, d);
+  if (st != LA_OK) return st;
+  if ((int64_t)num_seqs * H == 0) return total_N == 0 ? LA_OK : LA_ERR_INVALID_ARG;
+  if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
+  if (total_N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv)) return LA_ERR_INVALID_ARG;
+  if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, /*allow_fused=*/false);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < bwd_ws_bytes(pl, num_seqs, H, d)) return LA_ERR_WORKSPACE;
+  la::FwdArgs base;
+  base.decay = decay;
+  base.chdecay = nullptr;
+  base.snaps = nullptr;
+  base.snap_off = nullptr;
+  base.r_split = 1;
+  base.m.cu = cu_seqlens;
+  base.m.N = 0;
+  base.m.num_seqs = num_seqs;
+  base.m.H = H;
+  base.m.total = total_N;
+  base.m.seq_extra = 0;
+  base.m.snap_iv = 0;
+  base.m.rev_rs = 0;
+  if (layout == LA_HEAD_MAJOR) {  // [H][total_N][d]
+    base.m.head_stride = total_N * d;
+    base.m.rs = d;
+  } else {                         // [total_N][H][d]
+    base.m.head_stride = d;
+    base.m.rs = (int64_t)H * d;
+  }
+  auto args = [&](const void *q_, const void *k_, const void *v_, void *o_, const float *init_,
+                  float *fin_, bool reversed) {
+    la::FwdArgs a = base;
+    a.q = q_;
+    a.k = k_;
+    a.v = v_;
+    a.out = o_;
+    a.init = init_;
+    a.fin = fin_;
+    a.seg_len = pl.seg;
+    a.nseg = (int)pl.nseg;
+    a.ws = (float *)workspace;
+    if (reversed) {  // token u of sequence j read as token start(j+1) - 1 - u
+      a.m.rev_rs = a.m.rs;
+      a.m.rs = -a.m.rs;
     }
-    return LA_OK;
-  }
-  char *w = (char *)workspace;
-  const size_t st_b = state_bytes(BH, d);
-  float *initT = (float *)(w + (pl.ws_bytes + 255) / 256 * 256);
-  float *g = (float *)((char *)initT + st_b);
-  float *gT = (float *)((char *)g + st_b);
-  float *fin_dv = (float *)((char *)gT + st_b);
-  float *dk_in = (float *)((char *)fin_dv + st_b);  // dk pass entering states (pl.scan)
-  const dim3 tgrid((unsigned)BH, (unsigned)(d / 32), (unsigned)(d / 32));
-  if (init)
-    hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, init, 1, H, d, decay,
-                       false, initT);
-  if (dfinal) {
-    hipLaunchKernelGGL(la::bwd_scale_kernel, sgrid, dim3(256), 0, s, dfinal, decay, H, d, g);
-    hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, dfinal, 1, H, d,
-                       decay, true, gT);
-  }
-  // dq: causal, from S_init^T
-  la_status r = run_fwd(fixed_args(dout, v, k, dq, decay, B, H, N, d, dt, layout,
-                                   init ? initT : nullptr, nullptr, pl, workspace, false),
-                        pl, d, dt, false, s);
-  // dv: reversed, keys q and values do, from dS_fin / lambda; its final
-  // state is G_0.  dk: reversed, keys do and values q, from
-  // (dS_fin / lambda)^T.  The dk pass's state is G^T over the same segments,
-  // so with segments its entering states are the dv pass's (left in the
-  // workspace by the scan) transposed: only the dv pass runs the local-state
-  // pass and the scan.
-  la::FwdArgs av = fixed_args(k, q, dout, dv, decay, B, H, N, d, dt, layout,
-                              dfinal ? g : nullptr, dinit ? fin_dv : nullptr, pl, workspace, true);
-  la::FwdArgs ak = fixed_args(v, dout, q, dk, decay, B, H, N, d, dt, layout,
-                              dfinal ? gT : nullptr, nullptr, pl, workspace, true);
-  if (r == LA_OK) r = run_fwd(av, pl, d, dt, false, s, nullptr, /*out_pass=*/false);
-  if (r == LA_OK) {
-    if (pl.scan) {
-      hipLaunchKernelGGL(la::transpose_states_kernel,
-                         dim3((unsigned)(pl.nseg * H), (unsigned)(d / 32), (unsigned)(d / 32)),
-                         dim3(256), 0, s, (const float *)workspace, pl.r_split, H, d, decay,
-                         false, dk_in);
-      av.r_split = pl.r_split;
-      ak.ws = dk_in;
-      ak.r_split = 1;
-    } else {
-      av.ws = nullptr;
-      ak.ws = nullptr;
-    }
-    if (use_mfma(d, dt)) {
-      // Both output passes in one grid, paired workgroup by workgroup, so
-      // that q and do (read by both) come from HBM about once.
-      hipLaunchKernelGGL(la::mfma::prefill_chunk_pair_kernel,
-                         dim3((unsigned)(2 * pl.nseg * H)), dim3(la::mfma::NT), 0, s, av, ak);
-    } else {
-      launch_phase(av, pl, d, dt, s, /*phase_a=*/false);
-      launch_phase(ak, pl, d, dt, s, /*phase_a=*/false);
-    }
-    r = launch_status();
-  }
-  if (r == LA_OK && dinit) {
-    hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, fin_dv, decay, H, d, true,
-                       dinit);
-    r = launch_status();
-  }
-  return r;
+    return a;
+  };
+  return bwd_core(args, pl, num_seqs, H, d, dt, decay, q, k, v, dout, dfinals, inits, dq, dk, dv,
+                  dinits, total_N > 0, varlen_has_empty(pl), workspace,
+                  (hipStream_t)hip_stream);
 }
 
 }  // namespace
@@ -671,6 +758,28 @@ size_t lightning_attn_bwd_workspace_size(int B, int H, int64_t N, int d, int blo
   if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
   if ((int64_t)B * H == 0) return 0;
   return bwd_ws_bytes(plan_fixed(B, H, N, d, dt, segment_tokens, false), B, H, d);
+}
+
+size_t lightning_attn_bwd_varlen_workspace_size(int num_seqs, int H, int64_t total_N, int d,
+                                                int block, la_dtype dt, int64_t segment_tokens) {
+  if (num_seqs < 0 || total_N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK)
+    return 0;
+  if ((int64_t)num_seqs * H == 0) return 0;
+  return bwd_ws_bytes(plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, false), num_seqs,
+                      H, d);
+}
+
+la_status lightning_attn_bwd_varlen(const void *q, const void *k, const void *v,
+                                    const float *decay, const void *dout,
+                                    const int32_t *cu_seqlens, int num_seqs, int H,
+                                    int64_t total_N, int d, int block, la_dtype dt,
+                                    la_layout layout, const float *dfinals,
+                                    const float *init_states, void *dq, void *dk, void *dv,
+                                    float *dinits, int64_t segment_tokens, void *workspace,
+                                    size_t workspace_bytes, void *hip_stream) {
+  return bwd_varlen(q, k, v, decay, dout, cu_seqlens, num_seqs, H, total_N, d, block, dt, layout,
+                    dfinals, init_states, dq, dk, dv, dinits, segment_tokens, workspace,
+                    workspace_bytes, hip_stream);
 }
 
 la_status lightning_attn_bwd(const void *q, const void *k, const void *v, const float *decay,

@@ -146,3 +146,65 @@ def test_bwd_full_layer_h64_n32k():
         errs = [rel_err(host(g[:, sl]), r) for g, r in zip((dq, dk, dv, dinit), ref)]
         say("   head %d err dq %.3e dk %.3e dv %.3e dinit %.3e" % ((h,) + tuple(errs)))
         assert max(errs) <= TOL["bf16"], errs
+
+
+def run_bwd_varlen_case(lens, H, d, dtype, seed, seg=0, with_states=True, token_major=False):
+    """Packed backward against the oracle's backward run on each sequence."""
+    torch = torch_mod()
+    say("case bwd varlen lens=%s H=%d d=%d %s seg=%d states=%s token_major=%s"
+        % (lens[:8], H, d, dtype, seg, with_states, token_major))
+    cu = inputs.cu_seqlens(lens)
+    total = int(cu[-1])
+    q, k, v = inputs.host_qkv((H, total, d), seed, dtype=dtype)
+    do, _, _ = inputs.host_qkv((H, total, d), seed + 1, dtype=dtype)
+    lam = inputs.decay_schedule(H)
+    S = len(lens)
+    init = inputs.host_state((S, H, d, d), seed + 2) if with_states else None
+    dfin = inputs.host_state((S, H, d, d), seed + 3) if with_states else None
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tq, tk, tv, tdo = (torch.from_numpy(x).cuda().to(tdt) for x in (q, k, v, do))
+    layout = la.LA_HEAD_MAJOR
+    if token_major:
+        tq, tk, tv, tdo = (t.transpose(0, 1).contiguous() for t in (tq, tk, tv, tdo))
+        layout = la.LA_TOKEN_MAJOR
+    outs = [torch.full_like(tq, float("nan")) for _ in range(3)]
+    dq, dk, dv, dinit = la.lightning_attn_bwd_varlen(
+        tq, tk, tv, torch.from_numpy(lam).cuda(), tdo, torch.from_numpy(cu).cuda(),
+        layout=layout, dfinals=None if dfin is None else torch.from_numpy(dfin).cuda(),
+        init_states=None if init is None else torch.from_numpy(init).cuda(), segment_tokens=seg,
+        dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.synchronize()
+    if token_major:
+        dq, dk, dv = (t.transpose(0, 1) for t in (dq, dk, dv))
+    hq, hk, hv, hi = (host(t) for t in (dq, dk, dv, dinit))
+    refs = [np.zeros((H, total, d)) for _ in range(3)] + [np.zeros((S, H, d, d))]
+    for j in range(S):
+        a, b = int(cu[j]), int(cu[j + 1])
+        r = oracle.bwd(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], lam, do[None, :, a:b],
+                       dfin=None if dfin is None else dfin[j][None],
+                       init=None if init is None else init[j][None])
+        for t in range(3):
+            refs[t][:, a:b] = r[t][0]
+        refs[3][j] = r[3][0]
+    errs = [rel_err(g, ref) for g, ref in zip((hq, hk, hv, hi), refs)]
+    assert all(np.isfinite(x).all() for x in (hq, hk, hv, hi))
+    say("   err dq %.3e dk %.3e dv %.3e dinit %.3e" % tuple(errs))
+    assert max(errs) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("seg", [0, 200, 1000, la.LA_SEGMENT_PER_SEQUENCE])
+def test_bwd_varlen(seg):
+    """Packed sequences (empty ones first, inside and last; segments that cut
+    sequences and hand states across the cut in both directions)."""
+    run_bwd_varlen_case([0, 300, 0, 1, 129, 1024, 5, 640, 0], 4, 128, "bf16", seed=550 + seg,
+                        seg=seg)
+
+
+def test_bwd_varlen_token_major_no_states():
+    run_bwd_varlen_case([300, 1, 129, 1024, 5], 4, 128, "bf16", seed=560, seg=256,
+                        with_states=False, token_major=True)
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])
+def test_bwd_varlen_vector_alu(d, dtype):
+    run_bwd_varlen_case([33, 0, 64, 1, 100], 2, d, dtype, seed=570 + d, seg=48)

@@ -448,3 +448,83 @@ def test_full_decode_b128_h64():
     es = rel_err(host(state[bi, hi])[None], S)
     say("   err out %.3e state %.3e" % (worst, es))
     assert worst <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("prefill_path", ["auto", "fused"], indirect=True)
+def test_offsets_beyond_int32(prefill_path):
+    """B=1 H=3 N=2^23+4099 d=128 bf16: every element of head 2 lies past
+    2^31 elements (6.4 GB per tensor), so its loads, stores and state
+    addresses need 64-bit offsets.  Decays 0.9, 0.999, 0.999: a token n rows
+    back weighs at most 0.999^n, so an oracle run over a window of 2^17
+    tokens before the compared rows, from a zero state, differs from the full
+    recurrence by a factor 0.999^131072 < 1e-56 of the state: exact in double.
+    Compared: head 2's first 4096 rows (no truncation), 1024 rows around the
+    middle and the last 1024 rows with the final state; head 0's last rows."""
+    torch = torch_mod()
+    B, H, N, d = 1, 3, (1 << 23) + 4099, 128
+    say("case offsets beyond int32 B=%d H=%d N=%d d=%d path=%s" % (B, H, N, d, prefill_path))
+    assert 2 * N * d > 2 ** 31
+    tq, tk, tv = inputs.device_qkv((B, H, N, d), 4242, "bf16")
+    lam = np.array([0.9, 0.999, 0.999], np.float32)
+    out = torch.full_like(tq, float("nan"))
+    out, fin = la.lightning_attn_fwd(tq, tk, tv, torch.from_numpy(lam).cuda(), out=out)
+    torch.cuda.synchronize()
+    W = 1 << 17
+
+    def window(h, a, b, cmp_from, want_state=False):
+        q, k, v = (host(t[:, h:h + 1, a:b]) for t in (tq, tk, tv))
+        o_ref, f_ref, _ = oracle.fwd(q, k, v, lam[h:h + 1])
+        o = host(out[:, h:h + 1, cmp_from:b])
+        assert np.isfinite(o).all()
+        e = rel_err(o, o_ref[:, :, cmp_from - a:])
+        es = rel_err(host(fin[:, h:h + 1]), f_ref) if want_state else 0.0
+        say("   head %d rows [%d, %d) err out %.3e state %.3e" % (h, cmp_from, b, e, es))
+        assert e <= TOL["bf16"] and es <= TOL["bf16"], (e, es)
+
+    window(2, 0, 4096, 0)
+    mid = N // 2
+    window(2, mid - 512 - W, mid + 512, mid - 512)
+    window(2, N - 1024 - W, N, N - 1024, want_state=True)
+    window(0, N - 1024 - W, N, N - 1024, want_state=True)
+
+
+@pytest.mark.parametrize("prefill_path", ["auto", "fused"], indirect=True)
+def test_varlen_offsets_beyond_int32(prefill_path):
+    """Packed [H, total, d] with H=3 and total = 2^23 + 4099 (head 2 past 2^31
+    elements), five sequences, one of them empty, decays 0.9, 0.999, 0.999:
+    per sequence, its first rows (exact) and its last 1024 rows from an
+    oracle window of at most 2^17 tokens (see test_offsets_beyond_int32),
+    and its final state."""
+    torch = torch_mod()
+    H, d = 3, 128
+    cu = np.array([0, 1000, 3_000_000, 3_000_000, 6_500_017, (1 << 23) + 4099], np.int64)
+    total = int(cu[-1])
+    say("case varlen offsets beyond int32 H=%d total=%d seqs=%d path=%s"
+        % (H, total, len(cu) - 1, prefill_path))
+    tq, tk, tv = (t[0] for t in inputs.device_qkv((1, H, total, d), 4243, "bf16"))
+    lam = np.array([0.9, 0.999, 0.999], np.float32)
+    tcu = torch.from_numpy(cu.astype(np.int32)).cuda()
+    out = torch.full_like(tq, float("nan"))
+    out, fins = la.lightning_attn_fwd_varlen(tq, tk, tv, torch.from_numpy(lam).cuda(), tcu, out=out)
+    torch.cuda.synchronize()
+    W = 1 << 17
+    for j in range(len(cu) - 1):
+        s0, s1 = int(cu[j]), int(cu[j + 1])
+        for h in (0, 2):
+            if s1 == s0:
+                e = rel_err(host(fins[j, h]), np.zeros((d, d)))
+                say("   seq %d head %d empty: state err %.3e" % (j, h, e))
+                assert e == 0.0
+                continue
+            spans = [(s0, min(s1, s0 + 2048), s0)]
+            tail = max(s0, s1 - 1024)
+            spans.append((max(s0, tail - W), s1, tail))
+            for a, b, c in spans:
+                q, k, v = (host(t[h:h + 1, a:b])[None] for t in (tq, tk, tv))
+                o_ref, f_ref, _ = oracle.fwd(q, k, v, lam[h:h + 1])
+                o = host(out[h:h + 1, c:b])[None]
+                assert np.isfinite(o).all()
+                e = rel_err(o, o_ref[:, :, c - a:])
+                es = rel_err(host(fins[j, h]), f_ref[0, 0]) if b == s1 else 0.0
+                say("   seq %d head %d rows [%d, %d) err out %.3e state %.3e" % (j, h, c, b, e, es))
+                assert e <= TOL["bf16"] and es <= TOL["bf16"], (e, es)

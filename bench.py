@@ -475,9 +475,9 @@ def main():
                          "profiling it on its own); the headline line is not printed")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(shard (batch, head) pairs or sequence segments across GPUs as DESIGN.md "
-              "describes)" % args.gpus, file=sys.stderr)
+        print("bench.py: the library runs on one GPU only; --gpus %d is not supported "
+              "(across GPUs, (batch, head) pairs or sequence segments would be sharded, "
+              "each GPU running this path on its share)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -259,12 +259,26 @@ def bench_backward(la, inputs, steps, warmup):
                               dq=dq, dk=dk, dv=dv, dinit=dinit, workspace=ws)
 
     ms = time_steps(step, steps, warmup, torch.cuda.current_stream(dev))
+    # The training pair: the forward keeps its segment entering states, and
+    # the backward's dq pass skips its local-state pass and scan.
+    _, _, saved = la.lightning_attn_fwd_save(q, k, v, decay, block=block, init_state=init,
+                                             workspace=ws)
+
+    def step_saved():
+        la.lightning_attn_bwd_saved(q, k, v, decay, do, saved, dfinal=dfin, init_state=init,
+                                    block=block, dq=dq, dk=dk, dv=dv, dinit=dinit, workspace=ws)
+
+    ms_saved = time_steps(step_saved, steps, warmup, torch.cuda.current_stream(dev))
     byt = 7 * B * H * N * d * 2 + 3 * B * H * d * d * 4
     return {"workload": "layer_h64_n32k", "pass": "backward (dq, dk, dv, dinit)",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
             "tflops_3_passes": round(3 * prefill_flops(B, H, N, d, 128) / (ms * 1e-3) / 1e12, 2),
             "hbm_gbs_algorithmic": round(byt / (ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "with_saved_states": {"ms_per_step": round(ms_saved, 4),
+                                  "tokens_per_s": round(B * N / (ms_saved * 1e-3), 1),
+                                  "hbm_frac": round(byt / (ms_saved * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                    4)}}
 
 
 def bench_chdecay(la, inputs, steps, warmup):

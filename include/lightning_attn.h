@@ -364,6 +364,50 @@ la_status lightning_attn_bwd(const void *q, const void *k, const void *v, const 
                              void *hip_stream);
 
 /*
+ * A forward / backward pair for training (MiniMax-01 report, section
+ * 2.2.2.4, the trained lightning attention).  The backward's dq pass is
+ * itself a causal decayed linear attention whose state is S_t^T, so its
+ * segment entering states are the forward's, transposed: a forward that
+ * keeps them lets the backward skip that pass's local-state pass and scan.
+ *
+ * lightning_attn_saved_states_size: bytes of `saved` for these arguments
+ * ([nseg][H][d][d] float32 for the backward's segment plan), 0 when the plan
+ * cuts no sequence (nothing to keep; `saved` may then be NULL).
+ *
+ * lightning_attn_fwd_save: lightning_attn_fwd_layout on the backward's
+ * segment plan (always the three-phase schedule; LIGHTNING_ATTN_PREFILL is
+ * ignored), which also writes the transposed entering state of every
+ * segment into `saved` (device, caller-owned, saved_bytes at least the size
+ * above).  The workspace must hold lightning_attn_bwd_workspace_size(...)
+ * bytes for the same arguments (the pair can share one workspace).  Returns
+ * LA_ERR_INVALID_ARG for a missing or short `saved`, otherwise as
+ * lightning_attn_fwd_layout.
+ *
+ * lightning_attn_bwd_saved: lightning_attn_bwd, taking the dq pass's
+ * segment entering states from `saved`, which must come from a
+ * lightning_attn_fwd_save call with the same q, k, v, decay, init_state and
+ * shape arguments (segment_tokens included) and be unchanged since;
+ * anything else gives wrong dq without an error.  dk, dv and dinit do not
+ * use it.  Results equal lightning_attn_bwd's to float32 rounding.
+ */
+size_t lightning_attn_saved_states_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
+                                        int64_t segment_tokens);
+
+la_status lightning_attn_fwd_save(const void *q, const void *k, const void *v, const float *decay,
+                                  int B, int H, int64_t N, int d, int block, la_dtype dt,
+                                  la_layout layout, const float *init_state, void *out,
+                                  float *final_state, int64_t segment_tokens, float *saved,
+                                  size_t saved_bytes, void *workspace, size_t workspace_bytes,
+                                  void *hip_stream);
+
+la_status lightning_attn_bwd_saved(const void *q, const void *k, const void *v, const float *decay,
+                                   const void *dout, const float *dfinal, const float *init_state,
+                                   void *dq, void *dk, void *dv, float *dinit, int B, int H,
+                                   int64_t N, int d, int block, la_dtype dt, la_layout layout,
+                                   int64_t segment_tokens, const float *saved, size_t saved_bytes,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * lightning_attn_bwd for packed variable-length sequences (training on
  * packed data, MiniMax-01 report section 3.2): q, k, v, dout, dq, dk, dv as
  * for lightning_attn_fwd_varlen_layout; dfinals, init_states and dinits are

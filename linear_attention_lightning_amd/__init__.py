@@ -21,6 +21,8 @@ Entry points (same names as the C ABI):
   lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, ...)
       -> (dq, dk, dv, dinit)
   lightning_attn_bwd_varlen(q, k, v, decay, dout, cu_seqlens, ...) -> (dq, dk, dv, dinits)
+  lightning_attn_fwd_save(q, k, v, decay, ...) -> (out, final_state, saved)
+  lightning_attn_bwd_saved(q, k, v, decay, dout, saved, ...) -> (dq, dk, dv, dinit)
   lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode_state, ...)
       -> (prefill_out, final_states, decode_out)   (decode_state updated in place)
 """
@@ -33,7 +35,8 @@ __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd
            "lightning_attn_mixed_step", "lightning_attn_bwd", "lightning_attn_bwd_workspace_size",
            "lightning_attn_fwd_chdecay", "lightning_attn_fwd_chdecay_workspace_size",
            "lightning_attn_decode_chdecay", "lightning_attn_bwd_varlen",
-           "lightning_attn_bwd_varlen_workspace_size",
+           "lightning_attn_bwd_varlen_workspace_size", "lightning_attn_saved_states_size",
+           "lightning_attn_fwd_save", "lightning_attn_bwd_saved",
            "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
@@ -113,6 +116,14 @@ def load_library(path=None):
     lib.lightning_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, L, I, I, I, I, L, P,
                                        Z, P]
     lib.lightning_attn_bwd.restype = I
+    lib.lightning_attn_saved_states_size.argtypes = [I, I, L, I, I, I, L]
+    lib.lightning_attn_saved_states_size.restype = Z
+    lib.lightning_attn_fwd_save.argtypes = [P, P, P, P, I, I, L, I, I, I, I, P, P, P, L, P, Z, P, Z,
+                                            P]
+    lib.lightning_attn_fwd_save.restype = I
+    lib.lightning_attn_bwd_saved.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, L, I, I, I, I,
+                                             L, P, Z, P, Z, P]
+    lib.lightning_attn_bwd_saved.restype = I
     lib.lightning_attn_bwd_varlen_workspace_size.argtypes = [I, I, L, I, I, I, L]
     lib.lightning_attn_bwd_varlen_workspace_size.restype = Z
     lib.lightning_attn_bwd_varlen.argtypes = [P, P, P, P, P, P, I, I, L, I, I, I, I, P, P, P, P,
@@ -489,6 +500,72 @@ def lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, layou
     final state) and init_state [B, H, d, d] float32 or None.  Returns
     (dq, dk, dv, dinit) -- dinit [B, H, d, d] float32, or None when
     want_dinit is false."""
+    return _bwd_fixed(q, k, v, decay, dout, dfinal, init_state, layout, block, segment_tokens,
+                      want_dinit, dq, dk, dv, dinit, workspace, False, None)
+
+
+def lightning_attn_bwd_saved(q, k, v, decay, dout, saved, dfinal=None, init_state=None,
+                             layout=LA_HEAD_MAJOR, block=128, segment_tokens=0, want_dinit=True,
+                             dq=None, dk=None, dv=None, dinit=None, workspace=None):
+    """lightning_attn_bwd with the segment states `saved` kept by
+    lightning_attn_fwd_save on the same inputs and arguments (None when
+    lightning_attn_saved_states_size is 0)."""
+    return _bwd_fixed(q, k, v, decay, dout, dfinal, init_state, layout, block, segment_tokens,
+                      want_dinit, dq, dk, dv, dinit, workspace, True, saved)
+
+
+def lightning_attn_saved_states_size(B, H, N, d, block=128, dtype=LA_BF16, segment_tokens=0):
+    return load_library().lightning_attn_saved_states_size(B, H, N, d, block, dtype,
+                                                            segment_tokens)
+
+
+def lightning_attn_fwd_save(q, k, v, decay, layout=LA_HEAD_MAJOR, block=128, init_state=None,
+                            segment_tokens=0, out=None, final_state=None, saved=None,
+                            workspace=None):
+    """The forward of a training pair: lightning_attn_fwd_layout that also
+    keeps, for lightning_attn_bwd_saved, the transposed state entering every
+    segment of the backward's plan.  Returns (out, final_state, saved) --
+    saved a float32 device tensor, or None when nothing needs keeping.  The
+    workspace is sized by lightning_attn_bwd_workspace_size."""
+    torch = _torch()
+    lib = load_library()
+    if layout == LA_TOKEN_MAJOR:
+        B, N, H, d = q.shape
+    elif layout == LA_HEAD_MAJOR:
+        B, H, N, d = q.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (q, "q")):
+        _check(t, n, q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (B, H, d, d), torch.float32, dev)
+    out = torch.empty_like(q) if out is None else out
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", (B, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    sv_bytes = lib.lightning_attn_saved_states_size(B, H, N, d, block, dt, segment_tokens)
+    if saved is None and sv_bytes:
+        saved = torch.empty(sv_bytes // 4, dtype=torch.float32, device=dev)
+    sv_have = saved.numel() * saved.element_size() if saved is not None else 0
+    ws_bytes = lib.lightning_attn_bwd_workspace_size(B, H, N, d, block, dt, segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), B, H, N, d, block, dt,
+                                     layout, _ptr(init_state), _ptr(out), _ptr(final_state),
+                                     segment_tokens, _ptr(saved), sv_have, _ptr(workspace),
+                                     ws_have, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd_save")
+    return out, final_state, saved
+
+
+def _bwd_fixed(q, k, v, decay, dout, dfinal, init_state, layout, block, segment_tokens,
+               want_dinit, dq, dk, dv, dinit, workspace, with_saved, saved):
     torch = _torch()
     lib = load_library()
     if layout == LA_TOKEN_MAJOR:
@@ -518,12 +595,24 @@ def lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, layou
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.lightning_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout), _ptr(dfinal),
-                                _ptr(init_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dinit), B, H,
-                                N, d, block, dt, layout, segment_tokens, _ptr(workspace), ws_have,
-                                _stream(dev))
+    if with_saved:
+        if saved is not None:
+            _check(saved, "saved", saved.shape, torch.float32, dev)
+        sv_have = saved.numel() * saved.element_size() if saved is not None else 0
+        st = lib.lightning_attn_bwd_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout),
+                                          _ptr(dfinal), _ptr(init_state), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _ptr(dinit), B, H, N, d, block, dt, layout,
+                                          segment_tokens, _ptr(saved), sv_have, _ptr(workspace),
+                                          ws_have, _stream(dev))
+        name = "lightning_attn_bwd_saved"
+    else:
+        st = lib.lightning_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout),
+                                    _ptr(dfinal), _ptr(init_state), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(dinit), B, H, N, d, block, dt, layout, segment_tokens,
+                                    _ptr(workspace), ws_have, _stream(dev))
+        name = "lightning_attn_bwd"
     if st != 0:
-        raise LightningAttnError(st, "lightning_attn_bwd")
+        raise LightningAttnError(st, name)
     return dq, dk, dv, dinit
 
 

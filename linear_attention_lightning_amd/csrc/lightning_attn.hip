@@ -555,6 +555,13 @@ la_status fwd_chdecay(const void *q, const void *k, const void *v, const float *
 // floats (init^T, dS_fin / lambda, its transpose, the dv pass's final
 // state), then the dk pass's segment entering states (nseg*H*d*d floats,
 // when the plan cuts segments).
+// The segment entering states a forward keeps for its backward (transposed,
+// [nseg][H][d][d]); none when the plan has no scan (every segment starts a
+// sequence, from its initial state).
+size_t saved_states_bytes(const Plan &pl, int H, int d) {
+  return pl.scan ? state_bytes(pl.nseg * H, d) : 0;
+}
+
 size_t bwd_ws_bytes(const Plan &pl, int B, int H, int d) {
   const size_t al = 256;
   return (pl.ws_bytes + al - 1) / al * al + 4 * state_bytes((int64_t)B * H, d) +
@@ -571,7 +578,7 @@ la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dt
                    const float *decay, const void *q, const void *k, const void *v,
                    const void *dout, const float *dfinal, const float *init, void *dq, void *dk,
                    void *dv, float *dinit, bool any_token, bool has_empty, void *workspace,
-                   hipStream_t s) {
+                   hipStream_t s, const float *saved = nullptr) {
   const int64_t SH = (int64_t)S * H;
   const dim3 sgrid((unsigned)SH, (unsigned)ceil_div((int64_t)d * d, 256));
   if (!any_token) {  // no token at all: dS_init = dS_fin
@@ -598,9 +605,19 @@ la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dt
     hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, dfinal, 1, H, d,
                        decay, true, gT);
   }
-  // dq: causal, from S_init^T
-  la_status r = run_fwd(args(dout, v, k, dq, init ? initT : nullptr, nullptr, false), pl, d, dt,
-                        has_empty, s);
+  // dq: causal, from S_init^T.  Its state is S_t^T, so with the forward's
+  // saved segment entering states (transposed) only its output pass runs.
+  la_status r;
+  if (saved && pl.scan) {
+    la::FwdArgs aq = args(dout, v, k, dq, init ? initT : nullptr, nullptr, false);
+    aq.ws = const_cast<float *>(saved);
+    aq.r_split = 1;
+    if (pl.nseg > 0) launch_phase(aq, pl, d, dt, s, /*phase_a=*/false);
+    r = launch_status();
+  } else {
+    r = run_fwd(args(dout, v, k, dq, init ? initT : nullptr, nullptr, false), pl, d, dt,
+                has_empty, s);
+  }
   // dv: reversed, keys q and values do, from dS_fin / lambda; its final
   // state is G_0.  dk: reversed, keys do and values q, from
   // (dS_fin / lambda)^T.  The dk pass's state is G^T over the same segments,
@@ -651,7 +668,8 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
                     const void *dout, const float *dfinal, const float *init, void *dq, void *dk,
                     void *dv, float *dinit, int B, int H, int64_t N, int d, int block,
                     la_dtype dt, la_layout layout, int64_t segment_tokens, void *workspace,
-                    size_t workspace_bytes, void *hip_stream) {
+                    size_t workspace_bytes, void *hip_stream, bool with_saved = false,
+                    const float *saved = nullptr, size_t saved_bytes = 0) {
   if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
   la_status st = check_common(H, d, block, dt, segment_tokens);
   if (st == LA_OK) st = check_layout(layout, H, d);
@@ -663,13 +681,16 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < bwd_ws_bytes(pl, B, H, d)) return LA_ERR_WORKSPACE;
+  if (with_saved && saved_bytes < saved_states_bytes(pl, H, d)) return LA_ERR_INVALID_ARG;
+  if (with_saved && saved_states_bytes(pl, H, d) > 0 && !saved) return LA_ERR_INVALID_ARG;
   auto args = [&](const void *q_, const void *k_, const void *v_, void *o_, const float *init_,
                   float *fin_, bool reversed) {
     return fixed_args(q_, k_, v_, o_, decay, B, H, N, d, dt, layout, init_, fin_, pl, workspace,
                       reversed);
   };
   return bwd_core(args, pl, B, H, d, dt, decay, q, k, v, dout, dfinal, init, dq, dk, dv, dinit,
-                  N > 0, /*has_empty=*/false, workspace, (hipStream_t)hip_stream);
+                  N > 0, /*has_empty=*/false, workspace, (hipStream_t)hip_stream,
+                  with_saved ? saved : nullptr);
 }
 
 la_status bwd_varlen(const void *q, const void *k, const void *v, const float *decay,
@@ -751,6 +772,69 @@ la_status lightning_attn_fwd_chdecay(const void *q, const void *k, const void *v
                                      void *workspace, size_t workspace_bytes, void *hip_stream) {
   return fwd_chdecay(q, k, v, alpha, B, H, N, d, block, dt, layout, init_state, out, final_state,
                      segment_tokens, workspace, workspace_bytes, hip_stream);
+}
+
+// The forward of a training pair: the three-phase schedule of the backward's
+// plan, then the scan's segment entering states, transposed, into saved.
+la_status fwd_save(const void *q, const void *k, const void *v, const float *decay, int B, int H,
+                   int64_t N, int d, int block, la_dtype dt, la_layout layout,
+                   const float *init_state, void *out, float *final_state,
+                   int64_t segment_tokens, float *saved, size_t saved_bytes, void *workspace,
+                   size_t workspace_bytes, void *hip_stream) {
+  if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
+  la_status st = check_common(H, d, block, dt, segment_tokens);
+  if (st == LA_OK) st = check_layout(layout, H, d);
+  if (st != LA_OK) return st;
+  if ((int64_t)B * H == 0) return LA_OK;
+  if (!decay) return LA_ERR_INVALID_ARG;
+  if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
+  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false);
+  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  const size_t need = saved_states_bytes(pl, H, d);
+  if (saved_bytes < need || (need > 0 && !saved)) return LA_ERR_INVALID_ARG;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+  if (N == 0 && !final_state) return LA_OK;
+  const la::FwdArgs a = fixed_args(q, k, v, out, decay, B, H, N, d, dt, layout, init_state,
+                                   final_state, pl, workspace, /*reversed=*/false);
+  const hipStream_t s = (hipStream_t)hip_stream;
+  la_status r = run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, s);
+  if (r == LA_OK && need > 0) {
+    hipLaunchKernelGGL(la::transpose_states_kernel,
+                       dim3((unsigned)(pl.nseg * H), (unsigned)(d / 32), (unsigned)(d / 32)),
+                       dim3(256), 0, s, (const float *)workspace, pl.r_split, H, d, decay, false,
+                       saved);
+    r = launch_status();
+  }
+  return r;
+}
+
+size_t lightning_attn_saved_states_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
+                                        int64_t segment_tokens) {
+  if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
+  if ((int64_t)B * H == 0) return 0;
+  return saved_states_bytes(plan_fixed(B, H, N, d, dt, segment_tokens, false), H, d);
+}
+
+la_status lightning_attn_fwd_save(const void *q, const void *k, const void *v, const float *decay,
+                                  int B, int H, int64_t N, int d, int block, la_dtype dt,
+                                  la_layout layout, const float *init_state, void *out,
+                                  float *final_state, int64_t segment_tokens, float *saved,
+                                  size_t saved_bytes, void *workspace, size_t workspace_bytes,
+                                  void *hip_stream) {
+  return fwd_save(q, k, v, decay, B, H, N, d, block, dt, layout, init_state, out, final_state,
+                  segment_tokens, saved, saved_bytes, workspace, workspace_bytes, hip_stream);
+}
+
+la_status lightning_attn_bwd_saved(const void *q, const void *k, const void *v, const float *decay,
+                                   const void *dout, const float *dfinal, const float *init_state,
+                                   void *dq, void *dk, void *dv, float *dinit, int B, int H,
+                                   int64_t N, int d, int block, la_dtype dt, la_layout layout,
+                                   int64_t segment_tokens, const float *saved, size_t saved_bytes,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return bwd_fixed(q, k, v, decay, dout, dfinal, init_state, dq, dk, dv, dinit, B, H, N, d, block,
+                   dt, layout, segment_tokens, workspace, workspace_bytes, hip_stream,
+                   /*with_saved=*/true, saved, saved_bytes);
 }
 
 size_t lightning_attn_bwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,

@@ -194,6 +194,40 @@ def test_bwd_rejects_bad_arguments(lib):
     assert call(H=0, decay=None) == OK
 
 
+def test_training_pair_sizes_and_rejections(lib):
+    """Saved-state sizes follow the backward's segment plan; a missing or
+    short `saved` is rejected before anything launches."""
+    size = lib.lightning_attn_saved_states_size
+    assert size(1, 2, 128, 128, 128, BF16, 0) == 0            # one chunk: nothing kept
+    assert size(1, 2, 256, 128, 128, BF16, 0) == 2 * 2 * 128 * 128 * 4  # automatic: 2 segments
+    assert size(1, 2, 256, 128, 128, BF16, -1) == 0           # one segment per sequence
+    assert size(1, 2, 1024, 128, 128, BF16, 256) == 4 * 2 * 128 * 128 * 4
+    assert size(1, 64, 32768, 128, 128, BF16, 0) == 4 * 64 * 128 * 128 * 4  # 4 segments
+    assert size(1, 2, 256, 96, 128, BF16, 0) == 0             # unsupported d
+    need = size(1, 2, 1024, 128, 128, BF16, 256)
+    ws = lib.lightning_attn_bwd_workspace_size(1, 2, 1024, 128, 128, BF16, 256)
+    fwd = lib.lightning_attn_fwd_save
+    base = [DUMMY, DUMMY, DUMMY, DUMMY, 1, 2, 1024, 128, 128, BF16, 0, None, DUMMY, DUMMY, 256,
+            DUMMY, need, DUMMY, ws, None]
+    a = list(base); a[15] = None
+    assert fwd(*a) == INVALID
+    a = list(base); a[16] = need - 1
+    assert fwd(*a) == INVALID
+    a = list(base); a[17] = None
+    assert fwd(*a) == WORKSPACE
+    a = list(base); a[7] = 96
+    assert fwd(*a) == UNSUPPORTED
+    bwd = lib.lightning_attn_bwd_saved
+    bbase = [DUMMY] * 5 + [None, None] + [DUMMY] * 4 + [1, 2, 1024, 128, 128, BF16, 0, 256,
+                                                         DUMMY, need, DUMMY, ws, None]
+    a = list(bbase); a[19] = None
+    assert bwd(*a) == INVALID
+    a = list(bbase); a[20] = need - 1
+    assert bwd(*a) == INVALID
+    a = list(bbase); a[21] = None
+    assert bwd(*a) == WORKSPACE
+
+
 def test_decode_rejects_bad_arguments(lib):
     f = lib.lightning_attn_decode
     base = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 2, 4, 128, BF16, None]

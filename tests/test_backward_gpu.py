@@ -43,10 +43,14 @@ def host(t):
 
 
 def run_bwd_case(B, H, N, d, dtype, seed, block=128, seg=0, with_init=True, with_dfin=True,
-                 lam=None, token_major=False):
+                 lam=None, token_major=False, saved=False):
+    """saved: the training pair -- lightning_attn_fwd_save (its out and final
+    state checked against the oracle's forward), then lightning_attn_bwd_saved,
+    whose dk, dv and dinit must also equal lightning_attn_bwd's bit for bit
+    (same kernels on the same inputs; only dq takes the saved states)."""
     torch = torch_mod()
-    say("case bwd B=%d H=%d N=%d d=%d %s seg=%d init=%s dfin=%s token_major=%s"
-        % (B, H, N, d, dtype, seg, with_init, with_dfin, token_major))
+    say("case bwd B=%d H=%d N=%d d=%d %s seg=%d init=%s dfin=%s token_major=%s saved=%s"
+        % (B, H, N, d, dtype, seg, with_init, with_dfin, token_major, saved))
     q, k, v = inputs.host_qkv((B, H, N, d), seed, dtype=dtype)
     do, _, _ = inputs.host_qkv((B, H, N, d), seed + 1, dtype=dtype)
     lam = inputs.decay_schedule(H) if lam is None else np.asarray(lam, np.float32)
@@ -59,11 +63,31 @@ def run_bwd_case(B, H, N, d, dtype, seed, block=128, seg=0, with_init=True, with
         tq, tk, tv, tdo = (t.transpose(1, 2).contiguous() for t in (tq, tk, tv, tdo))
         layout = la.LA_TOKEN_MAJOR
     outs = [torch.full_like(tq, float("nan")) for _ in range(3)]
-    dq, dk, dv, dinit = la.lightning_attn_bwd(
-        tq, tk, tv, torch.from_numpy(lam).cuda(), tdo,
-        dfinal=None if dfin is None else torch.from_numpy(dfin).cuda(),
-        init_state=None if init is None else torch.from_numpy(init).cuda(), layout=layout,
-        block=block, segment_tokens=seg, dq=outs[0], dk=outs[1], dv=outs[2])
+    tl = torch.from_numpy(lam).cuda()
+    td = None if dfin is None else torch.from_numpy(dfin).cuda()
+    ti = None if init is None else torch.from_numpy(init).cuda()
+    if saved:
+        out, fin, sv = la.lightning_attn_fwd_save(tq, tk, tv, tl, layout=layout, block=block,
+                                                  init_state=ti, segment_tokens=seg)
+        nsv = la.lightning_attn_saved_states_size(B, H, N, d, block, la._dtype_code(tq), seg)
+        assert (sv is None) == (nsv == 0)
+        dq, dk, dv, dinit = la.lightning_attn_bwd_saved(
+            tq, tk, tv, tl, tdo, sv, dfinal=td, init_state=ti, layout=layout, block=block,
+            segment_tokens=seg, dq=outs[0], dk=outs[1], dv=outs[2])
+        _, pk, pv, pinit = la.lightning_attn_bwd(tq, tk, tv, tl, tdo, dfinal=td, init_state=ti,
+                                                 layout=layout, block=block, segment_tokens=seg)
+        torch.cuda.synchronize()
+        assert torch.equal(dk, pk) and torch.equal(dv, pv) and torch.equal(dinit, pinit)
+        if token_major:
+            out = out.transpose(1, 2)
+        o_ref, f_ref, _ = oracle.fwd(q, k, v, lam, init=init)
+        eo, ef = rel_err(host(out), o_ref), rel_err(host(fin), f_ref)
+        say("   saved %d bytes; forward err out %.3e state %.3e" % (nsv, eo, ef))
+        assert eo <= TOL[dtype] and ef <= TOL[dtype], (eo, ef)
+    else:
+        dq, dk, dv, dinit = la.lightning_attn_bwd(
+            tq, tk, tv, tl, tdo, dfinal=td, init_state=ti, layout=layout, block=block,
+            segment_tokens=seg, dq=outs[0], dk=outs[1], dv=outs[2])
     torch.cuda.synchronize()
     if token_major:
         dq, dk, dv = (t.transpose(1, 2) for t in (dq, dk, dv))
@@ -114,6 +138,28 @@ def test_bwd_token_major(d, dtype, seg):
     run_bwd_case(2, 5, 1000, d, dtype, seed=540 + d, seg=seg, token_major=True)
 
 
+@pytest.mark.parametrize("seg", [0, 128, 1000, la.LA_SEGMENT_PER_SEQUENCE])
+def test_bwd_saved_states(seg):
+    """The training pair under segment cuts (one segment per sequence keeps
+    nothing: saved is None)."""
+    run_bwd_case(2, 4, 4096, 128, "bf16", seed=560, seg=seg, saved=True)
+
+
+@pytest.mark.parametrize("with_init,with_dfin", [(False, False), (True, True)])
+def test_bwd_saved_optional_states(with_init, with_dfin):
+    run_bwd_case(1, 4, 1500, 128, "bf16", seed=561, with_init=with_init, with_dfin=with_dfin,
+                 seg=512, saved=True)
+
+
+@pytest.mark.parametrize("d,dtype,seg,token_major", [(64, "fp32", 64, False),
+                                                     (128, "fp32", 64, False),
+                                                     (64, "bf16", 64, True),
+                                                     (128, "bf16", 256, True)])
+def test_bwd_saved_layouts_and_vector_alu(d, dtype, seg, token_major):
+    run_bwd_case(2, 3, 700, d, dtype, seed=562 + d, seg=seg, lam=[0.999, 0.5, 0.9],
+                 token_major=token_major, saved=True)
+
+
 def test_bwd_empty_sequences():
     """N = 0: the initial-state gradient is dfinal."""
     torch = torch_mod()
@@ -126,18 +172,24 @@ def test_bwd_empty_sequences():
     assert torch.equal(dinit, dfin)
 
 
-def test_bwd_full_layer_h64_n32k():
+@pytest.mark.parametrize("saved", [False, True])
+def test_bwd_full_layer_h64_n32k(saved):
     """B=1 H=64 N=32768 d=128 (the prefill headline shape): heads 0, 31 and 63
-    in full, in the launch configuration the benchmark times."""
+    in full, in the launch configuration the benchmark times (saved: through
+    lightning_attn_fwd_save and lightning_attn_bwd_saved)."""
     torch = torch_mod()
     w = inputs.WORKLOADS["layer_h64_n32k"]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
-    say("case full bwd layer_h64_n32k")
+    say("case full bwd layer_h64_n32k saved=%s" % saved)
     tq, tk, tv = inputs.device_qkv((B, H, N, d), w["seed"], "bf16")
     tdo, _, _ = inputs.device_qkv((B, H, N, d), w["seed"] + 7, "bf16")
     lam = inputs.decay_schedule(H)
-    dq, dk, dv, dinit = la.lightning_attn_bwd(tq, tk, tv, torch.from_numpy(lam).cuda(), tdo,
-                                              block=w["block"])
+    tl = torch.from_numpy(lam).cuda()
+    if saved:
+        _, _, sv = la.lightning_attn_fwd_save(tq, tk, tv, tl, block=w["block"])
+        dq, dk, dv, dinit = la.lightning_attn_bwd_saved(tq, tk, tv, tl, tdo, sv, block=w["block"])
+    else:
+        dq, dk, dv, dinit = la.lightning_attn_bwd(tq, tk, tv, tl, tdo, block=w["block"])
     torch.cuda.synchronize()
     for h in (0, 31, H - 1):
         sl = slice(h, h + 1)

@@ -408,6 +408,36 @@ la_status lightning_attn_bwd_saved(const void *q, const void *k, const void *v, 
                                    void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * The training pair for packed variable-length sequences: as above, with the
+ * arguments of lightning_attn_fwd_varlen_layout and lightning_attn_bwd_varlen
+ * (workspace from lightning_attn_bwd_varlen_workspace_size; `saved` sized by
+ * lightning_attn_varlen_saved_states_size, 0 when no segment cuts a
+ * sequence, as with LA_SEGMENT_PER_SEQUENCE).  cu_seqlens must be the same
+ * in both calls.
+ */
+size_t lightning_attn_varlen_saved_states_size(int num_seqs, int H, int64_t total_N, int d,
+                                               int block, la_dtype dt, int64_t segment_tokens);
+
+la_status lightning_attn_fwd_varlen_save(const void *q, const void *k, const void *v,
+                                         const float *decay, const int32_t *cu_seqlens,
+                                         int num_seqs, int H, int64_t total_N, int d, int block,
+                                         la_dtype dt, la_layout layout, const float *init_states,
+                                         void *out, float *final_states, int64_t segment_tokens,
+                                         float *saved, size_t saved_bytes, void *workspace,
+                                         size_t workspace_bytes, void *hip_stream);
+
+la_status lightning_attn_bwd_varlen_saved(const void *q, const void *k, const void *v,
+                                          const float *decay, const void *dout,
+                                          const int32_t *cu_seqlens, int num_seqs, int H,
+                                          int64_t total_N, int d, int block, la_dtype dt,
+                                          la_layout layout, const float *dfinals,
+                                          const float *init_states, void *dq, void *dk, void *dv,
+                                          float *dinits, int64_t segment_tokens,
+                                          const float *saved, size_t saved_bytes,
+                                          void *workspace, size_t workspace_bytes,
+                                          void *hip_stream);
+
+/*
  * lightning_attn_bwd for packed variable-length sequences (training on
  * packed data, MiniMax-01 report section 3.2): q, k, v, dout, dq, dk, dv as
  * for lightning_attn_fwd_varlen_layout; dfinals, init_states and dinits are

@@ -23,6 +23,9 @@ Entry points (same names as the C ABI):
   lightning_attn_bwd_varlen(q, k, v, decay, dout, cu_seqlens, ...) -> (dq, dk, dv, dinits)
   lightning_attn_fwd_save(q, k, v, decay, ...) -> (out, final_state, saved)
   lightning_attn_bwd_saved(q, k, v, decay, dout, saved, ...) -> (dq, dk, dv, dinit)
+  lightning_attn_fwd_varlen_save(q, k, v, decay, cu_seqlens, ...) -> (out, final_states, saved)
+  lightning_attn_bwd_varlen_saved(q, k, v, decay, dout, cu_seqlens, saved, ...)
+      -> (dq, dk, dv, dinits)
   lightning_attn_mixed_step(decay, prefill_qkv, cu_seqlens, decode_qkv, decode_state, ...)
       -> (prefill_out, final_states, decode_out)   (decode_state updated in place)
 """
@@ -37,6 +40,8 @@ __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd
            "lightning_attn_decode_chdecay", "lightning_attn_bwd_varlen",
            "lightning_attn_bwd_varlen_workspace_size", "lightning_attn_saved_states_size",
            "lightning_attn_fwd_save", "lightning_attn_bwd_saved",
+           "lightning_attn_varlen_saved_states_size", "lightning_attn_fwd_varlen_save",
+           "lightning_attn_bwd_varlen_saved",
            "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
@@ -124,6 +129,14 @@ def load_library(path=None):
     lib.lightning_attn_bwd_saved.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, L, I, I, I, I,
                                              L, P, Z, P, Z, P]
     lib.lightning_attn_bwd_saved.restype = I
+    lib.lightning_attn_varlen_saved_states_size.argtypes = [I, I, L, I, I, I, L]
+    lib.lightning_attn_varlen_saved_states_size.restype = Z
+    lib.lightning_attn_fwd_varlen_save.argtypes = [P, P, P, P, P, I, I, L, I, I, I, I, P, P, P, L,
+                                                   P, Z, P, Z, P]
+    lib.lightning_attn_fwd_varlen_save.restype = I
+    lib.lightning_attn_bwd_varlen_saved.argtypes = [P, P, P, P, P, P, I, I, L, I, I, I, I, P, P,
+                                                    P, P, P, P, L, P, Z, P, Z, P]
+    lib.lightning_attn_bwd_varlen_saved.restype = I
     lib.lightning_attn_bwd_varlen_workspace_size.argtypes = [I, I, L, I, I, I, L]
     lib.lightning_attn_bwd_varlen_workspace_size.restype = Z
     lib.lightning_attn_bwd_varlen.argtypes = [P, P, P, P, P, P, I, I, L, I, I, I, I, P, P, P, P,
@@ -673,6 +686,78 @@ def lightning_attn_bwd_varlen(q, k, v, decay, dout, cu_seqlens, layout=LA_HEAD_M
     [H, total, d] (LA_HEAD_MAJOR) or [total, H, d] (LA_TOKEN_MAJOR);
     cu_seqlens int32 [num_seqs + 1]; dfinals and init_states
     [num_seqs, H, d, d] float32 or None.  Returns (dq, dk, dv, dinits)."""
+    return _bwd_varlen(q, k, v, decay, dout, cu_seqlens, layout, block, dfinals, init_states,
+                       segment_tokens, want_dinit, dq, dk, dv, dinits, workspace, False, None)
+
+
+def lightning_attn_bwd_varlen_saved(q, k, v, decay, dout, cu_seqlens, saved, layout=LA_HEAD_MAJOR,
+                                    block=128, dfinals=None, init_states=None, segment_tokens=0,
+                                    want_dinit=True, dq=None, dk=None, dv=None, dinits=None,
+                                    workspace=None):
+    """lightning_attn_bwd_varlen with the segment states `saved` kept by
+    lightning_attn_fwd_varlen_save on the same inputs and arguments."""
+    return _bwd_varlen(q, k, v, decay, dout, cu_seqlens, layout, block, dfinals, init_states,
+                       segment_tokens, want_dinit, dq, dk, dv, dinits, workspace, True, saved)
+
+
+def lightning_attn_varlen_saved_states_size(num_seqs, H, total, d, block=128, dtype=LA_BF16,
+                                            segment_tokens=0):
+    return load_library().lightning_attn_varlen_saved_states_size(num_seqs, H, total, d, block,
+                                                                   dtype, segment_tokens)
+
+
+def lightning_attn_fwd_varlen_save(q, k, v, decay, cu_seqlens, layout=LA_HEAD_MAJOR, block=128,
+                                   init_states=None, segment_tokens=0, out=None,
+                                   final_states=None, saved=None, workspace=None):
+    """The packed forward of a training pair (see lightning_attn_fwd_save).
+    Returns (out, final_states, saved); the workspace is sized by
+    lightning_attn_bwd_varlen_workspace_size."""
+    torch = _torch()
+    lib = load_library()
+    if layout == LA_TOKEN_MAJOR:
+        total, H, d = q.shape
+    elif layout == LA_HEAD_MAJOR:
+        H, total, d = q.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (q, "q")):
+        _check(t, n, q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 offsets")
+    S = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32, dev)
+    if init_states is not None:
+        _check(init_states, "init_states", (S, H, d, d), torch.float32, dev)
+    out = torch.empty_like(q) if out is None else out
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_states is None:
+        final_states = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_states, "final_states", (S, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    sv_bytes = lib.lightning_attn_varlen_saved_states_size(S, H, total, d, block, dt,
+                                                           segment_tokens)
+    if saved is None and sv_bytes:
+        saved = torch.empty(sv_bytes // 4, dtype=torch.float32, device=dev)
+    sv_have = saved.numel() * saved.element_size() if saved is not None else 0
+    ws_bytes = lib.lightning_attn_bwd_varlen_workspace_size(S, H, total, d, block, dt,
+                                                             segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_fwd_varlen_save(_ptr(q), _ptr(k), _ptr(v), _ptr(decay),
+                                            _ptr(cu_seqlens), S, H, total, d, block, dt, layout,
+                                            _ptr(init_states), _ptr(out), _ptr(final_states),
+                                            segment_tokens, _ptr(saved), sv_have,
+                                            _ptr(workspace), ws_have, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd_varlen_save")
+    return out, final_states, saved
+
+
+def _bwd_varlen(q, k, v, decay, dout, cu_seqlens, layout, block, dfinals, init_states,
+                segment_tokens, want_dinit, dq, dk, dv, dinits, workspace, with_saved, saved):
     torch = _torch()
     lib = load_library()
     if layout == LA_TOKEN_MAJOR:
@@ -707,11 +792,24 @@ def lightning_attn_bwd_varlen(q, k, v, decay, dout, cu_seqlens, layout=LA_HEAD_M
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.lightning_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout),
-                                       _ptr(cu_seqlens), S, H, total, d, block, dt, layout,
-                                       _ptr(dfinals), _ptr(init_states), _ptr(dq), _ptr(dk),
-                                       _ptr(dv), _ptr(dinits), segment_tokens, _ptr(workspace),
-                                       ws_have, _stream(dev))
+    if with_saved:
+        if saved is not None:
+            _check(saved, "saved", saved.shape, torch.float32, dev)
+        sv_have = saved.numel() * saved.element_size() if saved is not None else 0
+        st = lib.lightning_attn_bwd_varlen_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(decay),
+                                                 _ptr(dout), _ptr(cu_seqlens), S, H, total, d,
+                                                 block, dt, layout, _ptr(dfinals),
+                                                 _ptr(init_states), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                 _ptr(dinits), segment_tokens, _ptr(saved),
+                                                 sv_have, _ptr(workspace), ws_have, _stream(dev))
+        name = "lightning_attn_bwd_varlen_saved"
+    else:
+        st = lib.lightning_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(dout),
+                                           _ptr(cu_seqlens), S, H, total, d, block, dt, layout,
+                                           _ptr(dfinals), _ptr(init_states), _ptr(dq), _ptr(dk),
+                                           _ptr(dv), _ptr(dinits), segment_tokens,
+                                           _ptr(workspace), ws_have, _stream(dev))
+        name = "lightning_attn_bwd_varlen"
     if st != 0:
-        raise LightningAttnError(st, "lightning_attn_bwd_varlen")
+        raise LightningAttnError(st, name)
     return dq, dk, dv, dinits

@@ -413,7 +413,7 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
                       int block, la_dtype dt, la_layout layout, const float *init_states,
                       void *out, float *final_states, int64_t segment_tokens, void *workspace,
                       size_t workspace_bytes, int64_t snap_iv, const int32_t *snap_off,
-                      float *snaps, VarlenCall *c) {
+                      float *snaps, VarlenCall *c, bool allow_fused = true) {
   c->launch = false;
   if (num_seqs < 0 || total_N < 0 || snap_iv < 0) return LA_ERR_INVALID_ARG;
   if (snap_iv > 0 && snap_iv <= total_N && (!snap_off || !snaps)) return LA_ERR_INVALID_ARG;
@@ -424,7 +424,7 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
   if (total_N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens);
+  const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
@@ -698,7 +698,8 @@ la_status bwd_varlen(const void *q, const void *k, const void *v, const float *d
                      int64_t total_N, int d, int block, la_dtype dt, la_layout layout,
                      const float *dfinals, const float *inits, void *dq, void *dk, void *dv,
                      float *dinits, int64_t segment_tokens, void *workspace,
-                     size_t workspace_bytes, void *hip_stream) {
+                     size_t workspace_bytes, void *hip_stream, bool with_saved = false,
+                     const float *saved = nullptr, size_t saved_bytes = 0) {
   if (num_seqs < 0 || total_N < 0) return LA_ERR_INVALID_ARG;
   la_status st = check_common(H, d, block, dt, segment_tokens);
   if (st == LA_OK) st = check_layout(layout, H, d);
@@ -710,6 +711,8 @@ la_status bwd_varlen(const void *q, const void *k, const void *v, const float *d
   const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, /*allow_fused=*/false);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < bwd_ws_bytes(pl, num_seqs, H, d)) return LA_ERR_WORKSPACE;
+  if (with_saved && saved_bytes < saved_states_bytes(pl, H, d)) return LA_ERR_INVALID_ARG;
+  if (with_saved && saved_states_bytes(pl, H, d) > 0 && !saved) return LA_ERR_INVALID_ARG;
   la::FwdArgs base;
   base.decay = decay;
   base.chdecay = nullptr;
@@ -751,27 +754,7 @@ la_status bwd_varlen(const void *q, const void *k, const void *v, const float *d
   };
   return bwd_core(args, pl, num_seqs, H, d, dt, decay, q, k, v, dout, dfinals, inits, dq, dk, dv,
                   dinits, total_N > 0, varlen_has_empty(pl), workspace,
-                  (hipStream_t)hip_stream);
-}
-
-}  // namespace
-
-extern "C" {
-
-size_t lightning_attn_fwd_chdecay_workspace_size(int B, int H, int64_t N, int d, int block,
-                                                 la_dtype dt, int64_t segment_tokens) {
-  if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
-  if ((int64_t)B * H == 0) return 0;
-  return plan_fixed(B, H, N, d, dt, segment_tokens, false, true).ws_bytes;
-}
-
-la_status lightning_attn_fwd_chdecay(const void *q, const void *k, const void *v,
-                                     const float *alpha, int B, int H, int64_t N, int d, int block,
-                                     la_dtype dt, la_layout layout, const float *init_state,
-                                     void *out, float *final_state, int64_t segment_tokens,
-                                     void *workspace, size_t workspace_bytes, void *hip_stream) {
-  return fwd_chdecay(q, k, v, alpha, B, H, N, d, block, dt, layout, init_state, out, final_state,
-                     segment_tokens, workspace, workspace_bytes, hip_stream);
+                  (hipStream_t)hip_stream, with_saved ? saved : nullptr);
 }
 
 // The forward of a training pair: the three-phase schedule of the backward's
@@ -809,6 +792,52 @@ la_status fwd_save(const void *q, const void *k, const void *v, const float *dec
   return r;
 }
 
+// The packed forward of a training pair (as fwd_save).
+la_status fwd_varlen_save(const void *q, const void *k, const void *v, const float *decay,
+                          const int32_t *cu_seqlens, int num_seqs, int H, int64_t total_N, int d,
+                          int block, la_dtype dt, la_layout layout, const float *init_states,
+                          void *out, float *final_states, int64_t segment_tokens, float *saved,
+                          size_t saved_bytes, void *workspace, size_t workspace_bytes,
+                          void *hip_stream) {
+  VarlenCall c;
+  la_status st = prep_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, block, dt,
+                             layout, init_states, out, final_states, segment_tokens, workspace,
+                             workspace_bytes, 0, nullptr, nullptr, &c, /*allow_fused=*/false);
+  if (st != LA_OK || !c.launch) return st;
+  const size_t need = saved_states_bytes(c.pl, H, d);
+  if (saved_bytes < need || (need > 0 && !saved)) return LA_ERR_INVALID_ARG;
+  const hipStream_t s = (hipStream_t)hip_stream;
+  st = run_fwd(c.a, c.pl, d, dt, varlen_has_empty(c.pl), s);
+  if (st == LA_OK && need > 0) {
+    hipLaunchKernelGGL(la::transpose_states_kernel,
+                       dim3((unsigned)(c.pl.nseg * H), (unsigned)(d / 32), (unsigned)(d / 32)),
+                       dim3(256), 0, s, (const float *)workspace, c.pl.r_split, H, d, decay,
+                       false, saved);
+    st = launch_status();
+  }
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lightning_attn_fwd_chdecay_workspace_size(int B, int H, int64_t N, int d, int block,
+                                                 la_dtype dt, int64_t segment_tokens) {
+  if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
+  if ((int64_t)B * H == 0) return 0;
+  return plan_fixed(B, H, N, d, dt, segment_tokens, false, true).ws_bytes;
+}
+
+la_status lightning_attn_fwd_chdecay(const void *q, const void *k, const void *v,
+                                     const float *alpha, int B, int H, int64_t N, int d, int block,
+                                     la_dtype dt, la_layout layout, const float *init_state,
+                                     void *out, float *final_state, int64_t segment_tokens,
+                                     void *workspace, size_t workspace_bytes, void *hip_stream) {
+  return fwd_chdecay(q, k, v, alpha, B, H, N, d, block, dt, layout, init_state, out, final_state,
+                     segment_tokens, workspace, workspace_bytes, hip_stream);
+}
+
 size_t lightning_attn_saved_states_size(int B, int H, int64_t N, int d, int block, la_dtype dt,
                                         int64_t segment_tokens) {
   if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
@@ -835,6 +864,42 @@ la_status lightning_attn_bwd_saved(const void *q, const void *k, const void *v, 
   return bwd_fixed(q, k, v, decay, dout, dfinal, init_state, dq, dk, dv, dinit, B, H, N, d, block,
                    dt, layout, segment_tokens, workspace, workspace_bytes, hip_stream,
                    /*with_saved=*/true, saved, saved_bytes);
+}
+
+size_t lightning_attn_varlen_saved_states_size(int num_seqs, int H, int64_t total_N, int d,
+                                               int block, la_dtype dt, int64_t segment_tokens) {
+  if (num_seqs < 0 || total_N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK)
+    return 0;
+  if ((int64_t)num_seqs * H == 0) return 0;
+  return saved_states_bytes(plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, false), H,
+                            d);
+}
+
+la_status lightning_attn_fwd_varlen_save(const void *q, const void *k, const void *v,
+                                         const float *decay, const int32_t *cu_seqlens,
+                                         int num_seqs, int H, int64_t total_N, int d, int block,
+                                         la_dtype dt, la_layout layout, const float *init_states,
+                                         void *out, float *final_states, int64_t segment_tokens,
+                                         float *saved, size_t saved_bytes, void *workspace,
+                                         size_t workspace_bytes, void *hip_stream) {
+  return fwd_varlen_save(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, block, dt, layout,
+                         init_states, out, final_states, segment_tokens, saved, saved_bytes,
+                         workspace, workspace_bytes, hip_stream);
+}
+
+la_status lightning_attn_bwd_varlen_saved(const void *q, const void *k, const void *v,
+                                          const float *decay, const void *dout,
+                                          const int32_t *cu_seqlens, int num_seqs, int H,
+                                          int64_t total_N, int d, int block, la_dtype dt,
+                                          la_layout layout, const float *dfinals,
+                                          const float *init_states, void *dq, void *dk, void *dv,
+                                          float *dinits, int64_t segment_tokens,
+                                          const float *saved, size_t saved_bytes,
+                                          void *workspace, size_t workspace_bytes,
+                                          void *hip_stream) {
+  return bwd_varlen(q, k, v, decay, dout, cu_seqlens, num_seqs, H, total_N, d, block, dt, layout,
+                    dfinals, init_states, dq, dk, dv, dinits, segment_tokens, workspace,
+                    workspace_bytes, hip_stream, /*with_saved=*/true, saved, saved_bytes);
 }
 
 size_t lightning_attn_bwd_workspace_size(int B, int H, int64_t N, int d, int block, la_dtype dt,

@@ -36,6 +36,21 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_exports_only_declared_symbols():
+    """The library's dynamic symbol table holds the declared entry points and
+    nothing else of its own (internal helpers keep internal linkage)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    res = subprocess.run([nm, "-D", "--defined-only", la.LIB_PATH], capture_output=True,
+                         text=True, check=True)
+    syms = {ln.split()[-1] for ln in res.stdout.splitlines() if ln.strip()}
+    ours = {n for n in syms if not n.startswith("_Z") and not n.startswith("__hip_cuid")}
+    assert ours == set(declared_functions()), sorted(ours ^ set(declared_functions()))
+
+
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.lightning_attn_status_string(s)

@@ -200,11 +200,13 @@ def test_bwd_full_layer_h64_n32k(saved):
         assert max(errs) <= TOL["bf16"], errs
 
 
-def run_bwd_varlen_case(lens, H, d, dtype, seed, seg=0, with_states=True, token_major=False):
-    """Packed backward against the oracle's backward run on each sequence."""
+def run_bwd_varlen_case(lens, H, d, dtype, seed, seg=0, with_states=True, token_major=False,
+                        saved=False):
+    """Packed backward against the oracle's backward run on each sequence
+    (saved: through the packed training pair, as in run_bwd_case)."""
     torch = torch_mod()
-    say("case bwd varlen lens=%s H=%d d=%d %s seg=%d states=%s token_major=%s"
-        % (lens[:8], H, d, dtype, seg, with_states, token_major))
+    say("case bwd varlen lens=%s H=%d d=%d %s seg=%d states=%s token_major=%s saved=%s"
+        % (lens[:8], H, d, dtype, seg, with_states, token_major, saved))
     cu = inputs.cu_seqlens(lens)
     total = int(cu[-1])
     q, k, v = inputs.host_qkv((H, total, d), seed, dtype=dtype)
@@ -220,11 +222,33 @@ def run_bwd_varlen_case(lens, H, d, dtype, seed, seg=0, with_states=True, token_
         tq, tk, tv, tdo = (t.transpose(0, 1).contiguous() for t in (tq, tk, tv, tdo))
         layout = la.LA_TOKEN_MAJOR
     outs = [torch.full_like(tq, float("nan")) for _ in range(3)]
-    dq, dk, dv, dinit = la.lightning_attn_bwd_varlen(
-        tq, tk, tv, torch.from_numpy(lam).cuda(), tdo, torch.from_numpy(cu).cuda(),
-        layout=layout, dfinals=None if dfin is None else torch.from_numpy(dfin).cuda(),
-        init_states=None if init is None else torch.from_numpy(init).cuda(), segment_tokens=seg,
-        dq=outs[0], dk=outs[1], dv=outs[2])
+    tl, tcu = torch.from_numpy(lam).cuda(), torch.from_numpy(cu).cuda()
+    td = None if dfin is None else torch.from_numpy(dfin).cuda()
+    ti = None if init is None else torch.from_numpy(init).cuda()
+    if saved:
+        out, fins, sv = la.lightning_attn_fwd_varlen_save(tq, tk, tv, tl, tcu, layout=layout,
+                                                          init_states=ti, segment_tokens=seg)
+        nsv = la.lightning_attn_varlen_saved_states_size(S, H, total, d, 128, la._dtype_code(tq),
+                                                         seg)
+        assert (sv is None) == (nsv == 0)
+        dq, dk, dv, dinit = la.lightning_attn_bwd_varlen_saved(
+            tq, tk, tv, tl, tdo, tcu, sv, layout=layout, dfinals=td, init_states=ti,
+            segment_tokens=seg, dq=outs[0], dk=outs[1], dv=outs[2])
+        _, pk, pv, pinit = la.lightning_attn_bwd_varlen(tq, tk, tv, tl, tdo, tcu, layout=layout,
+                                                        dfinals=td, init_states=ti,
+                                                        segment_tokens=seg)
+        torch.cuda.synchronize()
+        assert torch.equal(dk, pk) and torch.equal(dv, pv) and torch.equal(dinit, pinit)
+        if token_major:
+            out = out.transpose(0, 1)
+        o_ref, f_ref, _ = oracle.fwd_varlen(q, k, v, lam, cu, init=init)
+        eo, ef = rel_err(host(out), o_ref), rel_err(host(fins), f_ref)
+        say("   saved %d bytes; forward err out %.3e state %.3e" % (nsv, eo, ef))
+        assert eo <= TOL[dtype] and ef <= TOL[dtype], (eo, ef)
+    else:
+        dq, dk, dv, dinit = la.lightning_attn_bwd_varlen(
+            tq, tk, tv, tl, tdo, tcu, layout=layout, dfinals=td, init_states=ti,
+            segment_tokens=seg, dq=outs[0], dk=outs[1], dv=outs[2])
     torch.cuda.synchronize()
     if token_major:
         dq, dk, dv = (t.transpose(0, 1) for t in (dq, dk, dv))
@@ -260,3 +284,16 @@ def test_bwd_varlen_token_major_no_states():
 @pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])
 def test_bwd_varlen_vector_alu(d, dtype):
     run_bwd_varlen_case([33, 0, 64, 1, 100], 2, d, dtype, seed=570 + d, seg=48)
+
+
+@pytest.mark.parametrize("seg", [0, 200, la.LA_SEGMENT_PER_SEQUENCE])
+def test_bwd_varlen_saved_states(seg):
+    """The packed training pair, with empty sequences among the packed ones."""
+    run_bwd_varlen_case([300, 0, 1000, 7, 0, 2000, 129], 4, 128, "bf16", seed=620, seg=seg,
+                        saved=True)
+
+
+@pytest.mark.parametrize("d,dtype,token_major", [(128, "bf16", True), (64, "fp32", False)])
+def test_bwd_varlen_saved_layouts(d, dtype, token_major):
+    run_bwd_varlen_case([500, 1, 700], 3, d, dtype, seed=621, seg=128, token_major=token_major,
+                        saved=True)

@@ -550,11 +550,6 @@ la_status fwd_chdecay(const void *q, const void *k, const void *v, const float *
   return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream);
 }
 
-// Workspace of the backward pass: the passes' prefill workspace (reused by
-// all three, which run in stream order), then four state sets of B*H*d*d
-// floats (init^T, dS_fin / lambda, its transpose, the dv pass's final
-// state), then the dk pass's segment entering states (nseg*H*d*d floats,
-// when the plan cuts segments).
 // The segment entering states a forward keeps for its backward (transposed,
 // [nseg][H][d][d]); none when the plan has no scan (every segment starts a
 // sequence, from its initial state).
@@ -562,6 +557,11 @@ size_t saved_states_bytes(const Plan &pl, int H, int d) {
   return pl.scan ? state_bytes(pl.nseg * H, d) : 0;
 }
 
+// Workspace of the backward pass: the passes' prefill workspace (reused by
+// all three, which run in stream order), then four state sets of B*H*d*d
+// floats (init^T, dS_fin / lambda, its transpose, the dv pass's final
+// state), then the dk pass's segment entering states (nseg*H*d*d floats,
+// when the plan cuts segments).
 size_t bwd_ws_bytes(const Plan &pl, int B, int H, int d) {
   const size_t al = 256;
   return (pl.ws_bytes + al - 1) / al * al + 4 * state_bytes((int64_t)B * H, d) +

@@ -312,6 +312,26 @@ la_status lightning_attn_fwd_chdecay(const void *q, const void *k, const void *v
                                      void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * Channel-wise decay over packed variable-length sequences: the arguments
+ * of lightning_attn_fwd_varlen_layout with alpha [H][d] (as above) in place
+ * of the per-head decay; workspace from
+ * lightning_attn_fwd_chdecay_varlen_workspace_size.  LA_SEGMENT_PER_SEQUENCE
+ * is not offered here (LA_ERR_UNSUPPORTED).
+ */
+size_t lightning_attn_fwd_chdecay_varlen_workspace_size(int num_seqs, int H, int64_t total_N,
+                                                        int d, int block, la_dtype dt,
+                                                        int64_t segment_tokens);
+
+la_status lightning_attn_fwd_chdecay_varlen(const void *q, const void *k, const void *v,
+                                            const float *alpha, const int32_t *cu_seqlens,
+                                            int num_seqs, int H, int64_t total_N, int d,
+                                            int block, la_dtype dt, la_layout layout,
+                                            const float *init_states, void *out,
+                                            float *final_states, int64_t segment_tokens,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *hip_stream);
+
+/*
  * One recurrent decode step with channel-wise decay (the decode counterpart
  * of lightning_attn_fwd_chdecay):
  *     state[i][j] <- alpha[h][i] state[i][j] + k[i] v[j],   out = q state.

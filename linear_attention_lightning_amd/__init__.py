@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
       -> (out, final_states, snapshots, snapshot_offsets)
   lightning_attn_decode(q, k, v, decay, state, out=None) -> out   (state updated in place)
   lightning_attn_fwd_chdecay(q, k, v, alpha, ...) -> (out, final_state)   (alpha [H, d])
+  lightning_attn_fwd_chdecay_varlen(q, k, v, alpha, cu_seqlens, ...) -> (out, final_states)
   lightning_attn_decode_chdecay(q, k, v, alpha, state, out=None) -> out
   lightning_attn_bwd(q, k, v, decay, dout, dfinal=None, init_state=None, ...)
       -> (dq, dk, dv, dinit)
@@ -41,7 +42,8 @@ __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd
            "lightning_attn_bwd_varlen_workspace_size", "lightning_attn_saved_states_size",
            "lightning_attn_fwd_save", "lightning_attn_bwd_saved",
            "lightning_attn_varlen_saved_states_size", "lightning_attn_fwd_varlen_save",
-           "lightning_attn_bwd_varlen_saved",
+           "lightning_attn_bwd_varlen_saved", "lightning_attn_fwd_chdecay_varlen",
+           "lightning_attn_fwd_chdecay_varlen_workspace_size",
            "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
@@ -116,6 +118,11 @@ def load_library(path=None):
     lib.lightning_attn_fwd_chdecay.argtypes = [P, P, P, P, I, I, L, I, I, I, I, P, P, P, L, P, Z,
                                                P]
     lib.lightning_attn_fwd_chdecay.restype = I
+    lib.lightning_attn_fwd_chdecay_varlen_workspace_size.argtypes = [I, I, L, I, I, I, L]
+    lib.lightning_attn_fwd_chdecay_varlen_workspace_size.restype = Z
+    lib.lightning_attn_fwd_chdecay_varlen.argtypes = [P, P, P, P, P, I, I, L, I, I, I, I, P, P, P,
+                                                      L, P, Z, P]
+    lib.lightning_attn_fwd_chdecay_varlen.restype = I
     lib.lightning_attn_bwd_workspace_size.argtypes = [I, I, L, I, I, I, L]
     lib.lightning_attn_bwd_workspace_size.restype = Z
     lib.lightning_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, L, I, I, I, I, L, P,
@@ -671,6 +678,58 @@ def lightning_attn_fwd_chdecay(q, k, v, alpha, layout=LA_HEAD_MAJOR, block=128, 
     if st != 0:
         raise LightningAttnError(st, "lightning_attn_fwd_chdecay")
     return out, final_state
+
+
+def lightning_attn_fwd_chdecay_varlen_workspace_size(num_seqs, H, total, d, block=128,
+                                                     dtype=LA_BF16, segment_tokens=0):
+    return load_library().lightning_attn_fwd_chdecay_varlen_workspace_size(
+        num_seqs, H, total, d, block, dtype, segment_tokens)
+
+
+def lightning_attn_fwd_chdecay_varlen(q, k, v, alpha, cu_seqlens, layout=LA_HEAD_MAJOR, block=128,
+                                      init_states=None, segment_tokens=0, out=None,
+                                      final_states=None, workspace=None):
+    """Channel-wise decay over packed sequences: q, k, v [H, total, d]
+    (LA_HEAD_MAJOR) or [total, H, d] (LA_TOKEN_MAJOR), alpha [H, d] float32,
+    cu_seqlens int32 [num_seqs + 1].  Returns (out, final_states
+    [num_seqs, H, d, d] float32)."""
+    torch = _torch()
+    lib = load_library()
+    if layout == LA_TOKEN_MAJOR:
+        total, H, d = q.shape
+    elif layout == LA_HEAD_MAJOR:
+        H, total, d = q.shape
+    else:
+        raise ValueError("layout must be LA_HEAD_MAJOR or LA_TOKEN_MAJOR")
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (q, "q")):
+        _check(t, n, q.shape, q.dtype, dev)
+    _check(alpha, "alpha", (H, d), torch.float32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 offsets")
+    S = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32, dev)
+    if init_states is not None:
+        _check(init_states, "init_states", (S, H, d, d), torch.float32, dev)
+    out = torch.empty_like(q) if out is None else out
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_states is None:
+        final_states = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_states, "final_states", (S, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    ws_bytes = lib.lightning_attn_fwd_chdecay_varlen_workspace_size(S, H, total, d, block, dt,
+                                                                     segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_fwd_chdecay_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                               _ptr(cu_seqlens), S, H, total, d, block, dt, layout,
+                                               _ptr(init_states), _ptr(out), _ptr(final_states),
+                                               segment_tokens, _ptr(workspace), ws_have,
+                                               _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd_chdecay_varlen")
+    return out, final_states
 
 
 def lightning_attn_bwd_varlen_workspace_size(num_seqs, H, total, d, block=128, dtype=LA_BF16,

@@ -139,21 +139,21 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
 // workspace, and the output pass alone is launched (it also gives empty
 // sequences their final state).
 Plan plan_varlen(int num_seqs, int H, int64_t total, int d, la_dtype dt,
-                 int64_t segment_tokens, bool allow_fused = true) {
+                 int64_t segment_tokens, bool allow_fused = true, bool ch = false) {
   if (segment_tokens == kSegPerSeq) return Plan{0, num_seqs, false, false, 1, 0};
   Plan p{1, 0, true, false, 1, 0};
   if (total == 0) return p;
-  const int T = chunk_tokens(d, dt);
-  const bool fused = allow_fused && want_fused(H, d, dt);
+  const int T = chunk_tokens(d, dt, ch);
+  const bool fused = allow_fused && want_fused(H, d, dt, ch);
   int64_t seg = segment_tokens;
   if (seg <= 0) {
-    const int64_t G = ceil_div(target_groups(d, dt), H);
+    const int64_t G = ceil_div(target_groups(d, dt, ch), H);
     seg = ceil_div(ceil_div(total, G), T) * T;
     if (fused && seg > kFusedSeg) seg = kFusedSeg;
   }
   p.seg = seg;
   p.fused = fused;
-  p.r_split = fused ? 1 : pieces(seg, d, dt);
+  p.r_split = fused ? 1 : pieces(seg, d, dt, ch);
   p.nseg = ceil_div(total, seg);
   p.ws_bytes = fused ? fused_ws_bytes(p.nseg, H, d) : phased_ws_bytes(p, H, d);
   return p;
@@ -413,7 +413,8 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
                       int block, la_dtype dt, la_layout layout, const float *init_states,
                       void *out, float *final_states, int64_t segment_tokens, void *workspace,
                       size_t workspace_bytes, int64_t snap_iv, const int32_t *snap_off,
-                      float *snaps, VarlenCall *c, bool allow_fused = true) {
+                      float *snaps, VarlenCall *c, bool allow_fused = true,
+                      bool ch = false) {
   c->launch = false;
   if (num_seqs < 0 || total_N < 0 || snap_iv < 0) return LA_ERR_INVALID_ARG;
   if (snap_iv > 0 && snap_iv <= total_N && (!snap_off || !snaps)) return LA_ERR_INVALID_ARG;
@@ -424,7 +425,7 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
   if (total_N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused);
+  const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused, ch);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
 
@@ -548,6 +549,29 @@ la_status fwd_chdecay(const void *q, const void *k, const void *v, const float *
                              final_state, pl, workspace, /*reversed=*/false);
   a.chdecay = alpha;
   return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream);
+}
+
+// Channel-wise decay over packed sequences: the packed prefill's arguments
+// with alpha [H][d] in place of the per-head decay.  One segment per
+// sequence is not offered (the channel-wise output pass takes plain
+// segments only).
+la_status fwd_chdecay_varlen(const void *q, const void *k, const void *v, const float *alpha,
+                             const int32_t *cu_seqlens, int num_seqs, int H, int64_t total_N,
+                             int d, int block, la_dtype dt, la_layout layout,
+                             const float *init_states, void *out, float *final_states,
+                             int64_t segment_tokens, void *workspace, size_t workspace_bytes,
+                             void *hip_stream) {
+  if (segment_tokens == kSegPerSeq) return LA_ERR_UNSUPPORTED;
+  VarlenCall c;
+  // (alpha is validated where the packed prefill validates the decay)
+  const la_status st = prep_varlen(q, k, v, alpha, cu_seqlens, num_seqs, H, total_N, d, block,
+                                   dt, layout, init_states, out, final_states, segment_tokens,
+                                   workspace, workspace_bytes, 0, nullptr, nullptr, &c,
+                                   /*allow_fused=*/false, /*ch=*/true);
+  if (st != LA_OK || !c.launch) return st;
+  c.a.decay = nullptr;
+  c.a.chdecay = alpha;
+  return run_fwd(c.a, c.pl, c.d, c.dt, varlen_has_empty(c.pl), (hipStream_t)hip_stream);
 }
 
 // The segment entering states a forward keeps for its backward (transposed,
@@ -821,6 +845,28 @@ la_status fwd_varlen_save(const void *q, const void *k, const void *v, const flo
 }  // namespace
 
 extern "C" {
+
+size_t lightning_attn_fwd_chdecay_varlen_workspace_size(int num_seqs, int H, int64_t total_N,
+                                                        int d, int block, la_dtype dt,
+                                                        int64_t segment_tokens) {
+  if (num_seqs < 0 || total_N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK)
+    return 0;
+  if ((int64_t)num_seqs * H == 0 || segment_tokens == kSegPerSeq) return 0;
+  return plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, false, true).ws_bytes;
+}
+
+la_status lightning_attn_fwd_chdecay_varlen(const void *q, const void *k, const void *v,
+                                            const float *alpha, const int32_t *cu_seqlens,
+                                            int num_seqs, int H, int64_t total_N, int d,
+                                            int block, la_dtype dt, la_layout layout,
+                                            const float *init_states, void *out,
+                                            float *final_states, int64_t segment_tokens,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *hip_stream) {
+  return fwd_chdecay_varlen(q, k, v, alpha, cu_seqlens, num_seqs, H, total_N, d, block, dt,
+                            layout, init_states, out, final_states, segment_tokens, workspace,
+                            workspace_bytes, hip_stream);
+}
 
 size_t lightning_attn_fwd_chdecay_workspace_size(int B, int H, int64_t N, int d, int block,
                                                  la_dtype dt, int64_t segment_tokens) {

@@ -198,3 +198,69 @@ def test_chdecay_empty_sequences_keep_the_state():
     _, fin = la.lightning_attn_fwd_chdecay(q, q.clone(), q.clone(), ta, init_state=init)
     torch.cuda.synchronize()
     assert torch.equal(fin, init)
+
+
+def run_ch_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True, token_major=False):
+    """Packed channel-wise prefill against the oracle's channel-wise
+    recurrence run on each sequence on its own."""
+    torch = torch_mod()
+    say("case chdecay varlen lens=%s H=%d d=%d %s seg=%d init=%s token_major=%s"
+        % (lens[:8], H, d, dtype, seg, with_init, token_major))
+    cu = inputs.cu_seqlens(lens)
+    total, S = int(cu[-1]), len(lens)
+    q, k, v = inputs.host_qkv((H, total, d), seed, dtype=dtype)
+    alpha = inputs.chdecay_schedule(H, d, seed + 1)
+    init = inputs.host_state((S, H, d, d), seed + 2) if with_init else None
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tq, tk, tv = (torch.from_numpy(x).cuda().to(tdt) for x in (q, k, v))
+    layout = la.LA_HEAD_MAJOR
+    if token_major:
+        tq, tk, tv = (t.transpose(0, 1).contiguous() for t in (tq, tk, tv))
+        layout = la.LA_TOKEN_MAJOR
+    out = torch.full_like(tq, float("nan"))
+    out, fins = la.lightning_attn_fwd_chdecay_varlen(
+        tq, tk, tv, torch.from_numpy(alpha).cuda(), torch.from_numpy(cu).cuda(), layout=layout,
+        init_states=None if init is None else torch.from_numpy(init).cuda(), segment_tokens=seg,
+        out=out)
+    torch.cuda.synchronize()
+    if token_major:
+        out = out.transpose(0, 1)
+    ho, hf = host(out), host(fins)
+    assert np.isfinite(ho).all()
+    o_ref = np.zeros((H, total, d))
+    f_ref = np.zeros((S, H, d, d))
+    for j in range(S):
+        a, b = int(cu[j]), int(cu[j + 1])
+        oj, fj = oracle.fwd_chdecay(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], alpha,
+                                    init=None if init is None else init[j][None])
+        o_ref[:, a:b] = oj[0]
+        f_ref[j] = fj[0]
+    eo, ef = rel_err(ho, o_ref), rel_err(hf, f_ref)
+    say("   err out %.3e state %.3e" % (eo, ef))
+    assert eo <= TOL[dtype] and ef <= TOL[dtype], (eo, ef)
+
+
+@pytest.mark.parametrize("seg", [0, 64, 200, 1000])
+def test_chdecay_varlen(seg):
+    """Packed sequences with empty ones among them, under segment cuts that
+    fall inside sequences and inside 64-token chunks."""
+    run_ch_varlen_case([300, 0, 1000, 7, 0, 2000, 129], 4, 128, "bf16", seed=700, seg=seg)
+
+
+@pytest.mark.parametrize("d,dtype,token_major,with_init", [(128, "bf16", True, False),
+                                                           (64, "fp32", False, True),
+                                                           (128, "fp32", True, True)])
+def test_chdecay_varlen_layouts_and_vector_alu(d, dtype, token_major, with_init):
+    run_ch_varlen_case([500, 1, 700, 64], 3, d, dtype, seed=701, seg=128,
+                       token_major=token_major, with_init=with_init)
+
+
+def test_chdecay_varlen_rejects_one_segment_per_sequence():
+    torch = torch_mod()
+    H, d = 2, 128
+    q = torch.zeros(H, 10, d, dtype=torch.bfloat16, device="cuda")
+    alpha = torch.full((H, d), 0.9, device="cuda")
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32, device="cuda")
+    with pytest.raises(la.LightningAttnError, match="LA_ERR_UNSUPPORTED"):
+        la.lightning_attn_fwd_chdecay_varlen(q, q.clone(), q.clone(), alpha, cu,
+                                             segment_tokens=la.LA_SEGMENT_PER_SEQUENCE)

@@ -297,3 +297,27 @@ def test_bwd_varlen_saved_states(seg):
 def test_bwd_varlen_saved_layouts(d, dtype, token_major):
     run_bwd_varlen_case([500, 1, 700], 3, d, dtype, seed=621, seg=128, token_major=token_major,
                         saved=True)
+
+
+def test_bwd_saved_states_are_what_dq_uses():
+    """The dq pass of lightning_attn_bwd_saved really starts its segments
+    from `saved`: with the forward's states zeroed, dq changes in every
+    segment but the first (whose entering state is the initial state's, also
+    zeroed here, which is the case where it is zero anyway) and stays put in
+    the first; dk and dv do not depend on it."""
+    torch = torch_mod()
+    B, H, N, d, seg = 1, 2, 1024, 128, 256
+    say("case bwd saved states are used")
+    q, k, v = inputs.device_qkv((B, H, N, d), 640, "bf16")
+    do, _, _ = inputs.device_qkv((B, H, N, d), 641, "bf16")
+    lam = torch.tensor([0.999, 0.99], dtype=torch.float32, device="cuda")
+    _, _, sv = la.lightning_attn_fwd_save(q, k, v, lam, segment_tokens=seg)
+    dq, dk, dv, _ = la.lightning_attn_bwd_saved(q, k, v, lam, do, sv, segment_tokens=seg)
+    zq, zk, zv, _ = la.lightning_attn_bwd_saved(q, k, v, lam, do, torch.zeros_like(sv),
+                                                segment_tokens=seg)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, zk) and torch.equal(dv, zv)
+    assert torch.equal(dq[:, :, :seg], zq[:, :, :seg])
+    for s in range(1, N // seg):
+        part = slice(s * seg, (s + 1) * seg)
+        assert not torch.equal(dq[:, :, part], zq[:, :, part]), s

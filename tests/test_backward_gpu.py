@@ -321,3 +321,49 @@ def test_bwd_saved_states_are_what_dq_uses():
     for s in range(1, N // seg):
         part = slice(s * seg, (s + 1) * seg)
         assert not torch.equal(dq[:, :, part], zq[:, :, part]), s
+
+
+def test_training_pair_graph_replay():
+    """lightning_attn_fwd_save followed by lightning_attn_bwd_saved, captured
+    as one HIP graph (a training step's attention), gives the eager results
+    bit for bit on every replay, with eager work and synchronisations between
+    the replays."""
+    torch = torch_mod()
+    B, H, N, d, seg = 1, 4, 2048, 128, 512
+    say("case training pair graph replay")
+    q, k, v = inputs.device_qkv((B, H, N, d), 650, "bf16")
+    do, _, _ = inputs.device_qkv((B, H, N, d), 651, "bf16")
+    lam = torch.from_numpy(inputs.decay_schedule(H)).cuda()
+    init = inputs.device_state((B, H, d, d), 652)
+    dfin = inputs.device_state((B, H, d, d), 653)
+    out, fin = torch.empty_like(q), torch.empty_like(init)
+    dq, dk, dv, dinit = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q),
+                         torch.empty_like(init))
+    nsv = la.lightning_attn_saved_states_size(B, H, N, d, 128, la.LA_BF16, seg)
+    sv = torch.empty(nsv // 4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(la.lightning_attn_bwd_workspace_size(B, H, N, d, 128, la.LA_BF16, seg),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        la.lightning_attn_fwd_save(q, k, v, lam, init_state=init, segment_tokens=seg, out=out,
+                                   final_state=fin, saved=sv, workspace=ws)
+        la.lightning_attn_bwd_saved(q, k, v, lam, do, sv, dfinal=dfin, init_state=init,
+                                    segment_tokens=seg, dq=dq, dk=dk, dv=dv, dinit=dinit,
+                                    workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    outs = (out, fin, sv, dq, dk, dv, dinit)
+    ref = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("out", "final", "saved", "dq", "dk", "dv", "dinit"), outs,
+                                   ref):
+            assert torch.equal(got, want), "replay %d: %s differs" % (r, name)

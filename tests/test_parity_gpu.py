@@ -528,3 +528,47 @@ def test_varlen_offsets_beyond_int32(prefill_path):
                 es = rel_err(host(fins[j, h]), f_ref[0, 0]) if b == s1 else 0.0
                 say("   seq %d head %d rows [%d, %d) err out %.3e state %.3e" % (j, h, c, b, e, es))
                 assert e <= TOL["bf16"] and es <= TOL["bf16"], (e, es)
+
+
+def test_side_stream_and_concurrent_host_threads():
+    """The library launches on the caller's current stream and keeps no
+    per-call state: the same prefill issued on a side stream, and from two
+    host threads at once (each on its own stream, with its own workspace),
+    gives the default-stream result bit for bit."""
+    import threading
+    torch = torch_mod()
+    B, H, N, d = 1, 8, 4096, 128
+    say("case side stream and concurrent host threads")
+    tq, tk, tv = inputs.device_qkv((B, H, N, d), 660, "bf16")
+    lam = torch.from_numpy(inputs.decay_schedule(H)).cuda()
+    ref_out, ref_fin = la.lightning_attn_fwd(tq, tk, tv, lam, segment_tokens=512)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        out, fin = la.lightning_attn_fwd(tq, tk, tv, lam, segment_tokens=512)
+    side.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin)
+
+    results, errors = {}, []
+
+    def worker(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                res = []
+                for _ in range(10):
+                    res.append(la.lightning_attn_fwd(tq, tk, tv, lam, segment_tokens=512))
+            st.synchronize()
+            results[i] = res
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i in range(2):
+        for o, f in results[i]:
+            assert torch.equal(o, ref_out) and torch.equal(f, ref_fin)

@@ -32,7 +32,10 @@
  *     size queries included, so keep it fixed between a query and the call
  *     it sizes; default phased); both give the same results up to rounding.
  *   - Arrays are dense and row-major with d fastest.  Outputs must not alias
- *     inputs (decode's `state` is read-modify-write by design).
+ *     inputs (decode's `state` is read-modify-write by design).  Every
+ *     tensor, state, snapshot and workspace pointer must be 16-byte aligned
+ *     (the kernels move 16 bytes per access); a misaligned one is
+ *     LA_ERR_INVALID_ARG.
  *   - q, k, v and out share one element type: LA_BF16 (bfloat16) or LA_FP32.
  *     States (init, final, decode state) are always float32, laid out
  *     S[i][j] with i the key feature (row) and j the value feature.

@@ -3,8 +3,11 @@
 #include "lightning_attn.h"
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <initializer_list>
 
 #include "la_common.h"
 #include "la_prefill_mfma.h"
@@ -306,6 +309,15 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
   return ls != LA_OK ? ls : pe.failed ? LA_ERR_HIP : LA_OK;
 }
 
+// Tensors the kernels access with 16-byte vector loads and stores (inputs,
+// outputs, states, workspace) must start on a 16-byte boundary; NULL (an
+// absent optional tensor) passes.
+bool aligned16(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (((uintptr_t)p & 15u) != 0) return false;
+  return true;
+}
+
 la_status check_common(int H, int d, int block, la_dtype dt, int64_t segment_tokens) {
   if (H < 0 || (segment_tokens < 0 && segment_tokens != kSegPerSeq)) return LA_ERR_INVALID_ARG;
   if (!valid_dtype(dt) || !valid_d(d) || !valid_block(block)) return LA_ERR_UNSUPPORTED;
@@ -388,6 +400,7 @@ la_status fwd_fixed(const void *q, const void *k, const void *v, const float *de
   if ((int64_t)B * H == 0) return LA_OK;
   if (!decay) return LA_ERR_INVALID_ARG;
   if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, out, init_state, final_state, workspace})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
@@ -424,6 +437,8 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   if ((int64_t)num_seqs * H == 0) return total_N == 0 ? LA_OK : LA_ERR_INVALID_ARG;
   if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
   if (total_N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, out, init_states, final_states, workspace, snaps}))
+    return LA_ERR_INVALID_ARG;
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused, ch);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
@@ -491,6 +506,7 @@ la_status check_decode(const void *q, const void *k, const void *v, const float 
   if (!valid_dtype(dt) || !valid_d(d)) return LA_ERR_UNSUPPORTED;
   if ((int64_t)B * H == 0) return LA_OK;
   if (!q || !k || !v || !decay || !state || !out) return LA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, state, out})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
@@ -540,6 +556,7 @@ la_status fwd_chdecay(const void *q, const void *k, const void *v, const float *
   if ((int64_t)B * H == 0) return LA_OK;
   if (!alpha) return LA_ERR_INVALID_ARG;
   if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, out, init_state, final_state, workspace})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false, /*ch=*/true);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
@@ -701,6 +718,8 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
   if ((int64_t)B * H == 0) return LA_OK;
   if (!decay) return LA_ERR_INVALID_ARG;
   if (N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv)) return LA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, dout, dq, dk, dv, dfinal, init, dinit, workspace, saved}))
+    return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
@@ -731,6 +750,8 @@ la_status bwd_varlen(const void *q, const void *k, const void *v, const float *d
   if ((int64_t)num_seqs * H == 0) return total_N == 0 ? LA_OK : LA_ERR_INVALID_ARG;
   if (!decay || !cu_seqlens) return LA_ERR_INVALID_ARG;
   if (total_N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv)) return LA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, dout, dq, dk, dv, dfinals, inits, dinits, workspace, saved}))
+    return LA_ERR_INVALID_ARG;
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, /*allow_fused=*/false);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
@@ -795,11 +816,13 @@ la_status fwd_save(const void *q, const void *k, const void *v, const float *dec
   if ((int64_t)B * H == 0) return LA_OK;
   if (!decay) return LA_ERR_INVALID_ARG;
   if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, out, init_state, final_state, workspace})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   const size_t need = saved_states_bytes(pl, H, d);
-  if (saved_bytes < need || (need > 0 && !saved)) return LA_ERR_INVALID_ARG;
+  if (saved_bytes < need || (need > 0 && !saved) || !aligned16({saved}))
+    return LA_ERR_INVALID_ARG;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
   if (N == 0 && !final_state) return LA_OK;
   const la::FwdArgs a = fixed_args(q, k, v, out, decay, B, H, N, d, dt, layout, init_state,
@@ -829,7 +852,8 @@ la_status fwd_varlen_save(const void *q, const void *k, const void *v, const flo
                              workspace_bytes, 0, nullptr, nullptr, &c, /*allow_fused=*/false);
   if (st != LA_OK || !c.launch) return st;
   const size_t need = saved_states_bytes(c.pl, H, d);
-  if (saved_bytes < need || (need > 0 && !saved)) return LA_ERR_INVALID_ARG;
+  if (saved_bytes < need || (need > 0 && !saved) || !aligned16({saved}))
+    return LA_ERR_INVALID_ARG;
   const hipStream_t s = (hipStream_t)hip_stream;
   st = run_fwd(c.a, c.pl, d, dt, varlen_has_empty(c.pl), s);
   if (st == LA_OK && need > 0) {

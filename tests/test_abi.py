@@ -243,6 +243,24 @@ def test_training_pair_sizes_and_rejections(lib):
     assert bwd(*a) == WORKSPACE
 
 
+def test_misaligned_pointers_are_rejected(lib):
+    """Every tensor pointer must be 16-byte aligned; a misaligned one fails
+    validation (nothing is launched: the pointers are never dereferenced)."""
+    odd = ctypes.c_void_p(0x1002)
+    assert fwd(lib, q=odd) == INVALID
+    assert fwd(lib, out=odd) == INVALID
+    assert fwd(lib, fin=odd) == INVALID
+    need = lib.lightning_attn_fwd_workspace_size(1, 2, 256, 128, 128, BF16, 0)
+    assert fwd(lib, ws=odd, wsb=need) == INVALID
+    base = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 2, 4, 128, BF16, None]
+    a = list(base); a[4] = odd                      # decode state
+    assert lib.lightning_attn_decode(*a) == INVALID
+    bwd = lib.lightning_attn_bwd
+    args = [DUMMY, DUMMY, DUMMY, DUMMY, odd, None, None, DUMMY, DUMMY, DUMMY, DUMMY, 1, 2, 256,
+            128, 128, BF16, 0, 0, DUMMY, 1 << 30, None]
+    assert bwd(*args) == INVALID                    # dout
+
+
 def test_decode_rejects_bad_arguments(lib):
     f = lib.lightning_attn_decode
     base = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 2, 4, 128, BF16, None]

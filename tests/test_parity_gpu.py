@@ -572,3 +572,18 @@ def test_side_stream_and_concurrent_host_threads():
     for i in range(2):
         for o, f in results[i]:
             assert torch.equal(o, ref_out) and torch.equal(f, ref_fin)
+
+
+def test_misaligned_tensor_raises():
+    """A contiguous view that starts 2 bytes past a 16-byte boundary is
+    refused before any launch (LA_ERR_INVALID_ARG through the binding)."""
+    torch = torch_mod()
+    B, H, N, d = 1, 2, 256, 128
+    n = B * H * N * d
+    flat = torch.zeros(n + 8, dtype=torch.bfloat16, device="cuda")
+    q = flat[1:n + 1].view(B, H, N, d)
+    assert q.is_contiguous() and q.data_ptr() % 16 == 2
+    k = torch.zeros(B, H, N, d, dtype=torch.bfloat16, device="cuda")
+    lam = torch.full((H,), 0.9, device="cuda")
+    with pytest.raises(la.LightningAttnError, match="LA_ERR_INVALID_ARG"):
+        la.lightning_attn_fwd(q, k, k.clone(), lam)

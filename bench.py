@@ -228,11 +228,16 @@ def bench_decode(la, inputs, reps, warmup):
         e.record(stream)
         torch.cuda.synchronize()
         times.append(s.elapsed_time(e))
-    ms = min(times) / T
+    times.sort()
+    ms = times[len(times) // 2] / T      # median repetition
+    ms_min = times[0] / T
     gbs = decode_bytes(B, H, d) / (ms * 1e-3) / 1e9
+    gbs_max = decode_bytes(B, H, d) / (ms_min * 1e-3) / 1e9
     return {"workload": "decode_b128_h64", "B": B, "H": H, "d": d, "steps": T,
-            "ms_per_token_step": round(ms, 5), "state_gbs": round(gbs, 1),
-            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+            "repetitions": reps, "ms_per_token_step": round(ms, 5),
+            "ms_per_token_step_min": round(ms_min, 5), "state_gbs": round(gbs, 1),
+            "state_gbs_best": round(gbs_max, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "median (and best) of the repetitions, each 256 steps"}
 
 
 def bench_backward(la, inputs, steps, warmup):
@@ -444,7 +449,9 @@ def bench_serving(la, inputs, reps=200, P=50):
 
 def cpu_baseline(gpu_tensors, H, N, d, heads):
     """The oracle (untuned) on the host cores: `heads` of the H heads, all N
-    tokens, on the same inputs; scaled to whole-workload tokens/s."""
+    tokens, on the same inputs; scaled to whole-workload tokens/s.  Also the
+    parity of the timed run's own output and final state against it (the
+    whole-tensor metric over the heads the oracle ran)."""
     import numpy as np
     import torch
     import oracle
@@ -452,8 +459,23 @@ def cpu_baseline(gpu_tensors, H, N, d, heads):
     q, k, v = (t[:, :heads].float().cpu().numpy() for t in gpu_tensors[:3])
     lam = inputs.decay_schedule(H)[:heads]
     t0 = time.perf_counter()
-    _, _, used = oracle.fwd(q, k, v, lam)
+    o_ref, f_ref, used = oracle.fwd(q, k, v, lam)
     dt = time.perf_counter() - t0
+    del q, k, v
+    out, fin = gpu_tensors[4], gpu_tensors[5]
+    num = den = 0.0
+    for h in range(heads):
+        a = out[:, h].float().cpu().numpy().astype(np.float64)
+        if not np.isfinite(a).all():
+            num = float("inf")
+            break
+        num = max(num, float(np.abs(a - o_ref[:, h]).max()))
+        den = max(den, float(np.abs(o_ref[:, h]).max()))
+    fs = fin[:, :heads].cpu().numpy().astype(np.float64)
+    parity = {"out": num / den, "state": float(np.abs(fs - f_ref).max() / np.abs(f_ref).max()),
+              "tolerance": 2e-2, "metric": "max|x - x_ref| / max|x_ref| over every element",
+              "compared": "the last timed step's out and final_state, %d of %d heads, all %d "
+                          "tokens, against the double-precision oracle" % (heads, H, N)}
     frac = heads / H
     model = ""
     try:
@@ -465,7 +487,62 @@ def cpu_baseline(gpu_tensors, H, N, d, heads):
             "cpu_model": model, "kind": "oracle",
             "sample": "%d of %d heads, all %d tokens of the B=1 H=64 N=32768 d=128 workload "
                       "(double-precision recurrence), %.1f s wall; scaled to all heads"
-                      % (heads, H, N, dt)}
+                      % (heads, H, N, dt)}, parity
+
+
+def copy_ceiling(mib=1024, reps=10):
+    """A device-to-device torch copy of `mib` MiB, timed with HIP events:
+    the practical ceiling of a 1:1 read/write stream on this GPU (median of
+    `reps` copies; bytes read plus bytes written per second)."""
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src)
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    times.sort()
+    ms = times[len(times) // 2]
+    gbs = 2 * (mib << 20) / (ms * 1e-3) / 1e9
+    del src, dst
+    return {"bytes_copied": mib << 20, "ms": round(ms, 4), "gbs_read_plus_write": round(gbs, 1),
+            "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "torch device copy, median of %d; the chunk kernel reads 3 bytes for each "
+                    "byte it writes" % reps}
+
+
+def run_metadata(seed):
+    """Device, software versions and the input seed of this run."""
+    import ctypes
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    md = {"device": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+          "hbm_bytes": p.total_memory, "torch": torch.__version__, "hip": torch.version.hip,
+          "seed": seed, "timing": "HIP events on the library's stream"}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            md["rocm"] = f.read().strip()
+    except OSError:
+        md["rocm"] = None
+    try:
+        # hipDeviceGetAttribute: 5 = clock rate, 60 = memory clock rate (kHz;
+        # the peak figures the runtime reports, not the clock during the run)
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int()
+        for name, attr in (("peak_sclk_mhz", 5), ("peak_mclk_mhz", 60)):
+            md[name] = (v.value // 1000
+                        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0 else None)
+    except OSError:
+        pass
+    return md
 
 
 def main():
@@ -553,6 +630,8 @@ def main():
                      "note": "algorithmic bytes per step / step time; traffic = counter "
                              "bytes of all three kernels per step"},
     }
+    res["run"] = run_metadata(w["seed"])
+    res["copy_ceiling"] = copy_ceiling()
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
@@ -563,11 +642,11 @@ def main():
         res["copy_calibration_bytes"] = nbytes
         del src, dst
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(tensors, H, N, d, min(args.cpu_heads, H))
+        res["cpu_baseline"], res["parity"] = cpu_baseline(tensors, H, N, d, min(args.cpu_heads, H))
     del tensors
     torch.cuda.empty_cache()
     if not args.no_extras:
-        res["decode"] = bench_decode(la, inputs, reps=3, warmup=1)
+        res["decode"] = bench_decode(la, inputs, reps=5, warmup=1)
         torch.cuda.empty_cache()
         res["varlen"] = bench_varlen(la, inputs, steps=max(5, args.steps // 2), warmup=2)
         torch.cuda.empty_cache()

@@ -13,11 +13,6 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
-def pytest_collection_modifyitems(config, items):
-    # Run GPU tests in file order but after everything else in each file.
-    pass
-
-
 @pytest.fixture(scope="session")
 def oracle_lib():
     import oracle

@@ -31,6 +31,11 @@
  *     LIGHTNING_ATTN_PREFILL=phased|fused (read at each call, the workspace
  *     size queries included, so keep it fixed between a query and the call
  *     it sizes; default phased); both give the same results up to rounding.
+ *     The fused schedule hands states between workgroups through flags in
+ *     the workspace; a wait that exceeds its bound (a stalled GPU, never a
+ *     normal run) gives up rather than hang and makes the outputs and final
+ *     states of the affected head NaN from that segment on, so such a failure
+ *     is never a silently wrong result.
  *   - Arrays are dense and row-major with d fastest.  Outputs must not alias
  *     inputs (decode's `state` is read-modify-write by design).  Every
  *     tensor, state, snapshot and workspace pointer must be 16-byte aligned

@@ -798,8 +798,17 @@ void prefill_chunk_pair_kernel(FwdArgs a, FwdArgs b) {
 //      from the Infinity Cache, since segments are short enough for every
 //      resident workgroup's K/V to stay there.
 // A workgroup only ever waits on a lower ticket, which a running workgroup
-// already holds, so the waits cannot deadlock; a wait that exceeds
-// kSpinLimit polls gives up, sets *err and continues (wrong output, no hang).
+// already holds, so the waits cannot deadlock.  A wait that still exceeds
+// kSpinLimit polls (a safety net: it would take a stalled GPU) gives up, sets
+// *err and continues from a NaN entering state, so that the segment's
+// outputs, its end state and every later segment of the head come out NaN:
+// never a silently wrong result, and never a hang.
+// Ordering: the records are written with agent-scope atomic stores and
+// waited for (s_waitcnt) before a workgroup barrier; the flag is then
+// published after an agent-scope release fence.  One lane of the waiting
+// workgroup polls the flag with relaxed loads; behind the next barrier every
+// state wave loads it once more with agent-scope acquire ordering before it
+// reads the record.
 struct FusedArgs {
   FwdArgs f;         // f.ws: end-state records [nseg][H][D][D]
   unsigned *flags;   // [nseg * H], zero on entry: record published
@@ -814,10 +823,10 @@ __global__ void fused_reset_kernel(unsigned *words, int n) {
   if (i < n) words[i] = 0u;
 }
 
-// Hand-off records and flags use device-scope (agent) atomic accesses, which
-// bypass the XCD-private L2, so publishing one needs no L2-wide write-back
-// and reading one no L2-wide invalidation -- both of which would stall every
-// workgroup on the XCD.
+// Hand-off records use device-scope (agent) atomic accesses, which are
+// coherent across the XCD-private L2 caches; the flag that publishes a
+// record is ordered after it by the release fence and the acquire load
+// described above (one of each per workgroup).
 __device__ __forceinline__ float load_handoff(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -830,10 +839,12 @@ __device__ __forceinline__ void store_handoff(float *p, float v) {
 // sequence's initial state, or zero when NULL).  When `publish`, also writes
 // gamma * base + L to the record `rec`, with base = the entering state
 // (from_prev) or the last piece's own initial state `ini_last`.
+// poison: the entering state is NaN (a timed-out wait).
 __device__ __forceinline__ void combine_states(f32x16 (&X)[4], const float *prev,
                                                bool prev_is_record, const float *ini_last,
                                                bool from_prev, bool publish, float gam,
-                                               float *rec, int u, int l32, int g) {
+                                               float *rec, int u, int l32, int g, bool poison) {
+  const float nan = __builtin_nanf("");
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int off = (32 * u + 8 * q + 4 * g) * D + l32;
@@ -842,7 +853,8 @@ __device__ __forceinline__ void combine_states(f32x16 (&X)[4], const float *prev
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
         const int o = off + mm * D + 32 * nt;
-        const float in = !prev ? 0.f : prev_is_record ? load_handoff(prev + o) : prev[o];
+        const float in = poison ? nan
+                         : !prev ? 0.f : prev_is_record ? load_handoff(prev + o) : prev[o];
         if (publish) {
           const float base = from_prev ? in : (ini_last ? ini_last[o] : 0.f);
           store_handoff(rec + o, gam * base + X[nt][4 * q + mm]);
@@ -918,7 +930,7 @@ void prefill_fused_kernel(FusedArgs fa) {
       int it = 0;
       while (__hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
         if (++it > kSpinLimit) {
-          *fa.err = 1u;
+          __hip_atomic_store(fa.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -927,9 +939,11 @@ void prefill_fused_kernel(FusedArgs fa) {
     __syncthreads();  // the state waves' record loads are issued after the flag was seen
     if (need_out) {
       __syncthreads();  // the state waves' record stores have completed
-      if (ln.tid == 0)
+      if (ln.tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __hip_atomic_store(fa.flags + (size_t)s * H + h, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     // 3. Outputs from the entering state.
     if (dc.fast)
@@ -957,8 +971,14 @@ void prefill_fused_kernel(FusedArgs fa) {
                                 : (p.init ? p.init + ((int64_t)jf * H + h) * DD : nullptr);
     const float *ini_last = p.init ? p.init + ((int64_t)jl * H + h) * DD : nullptr;
     const float gam = fast_exp2((float)(b - ps) * dc.l2);
+    // The flag, read again with acquire ordering, makes the record visible;
+    // still unset, the wait above timed out and the entering state is poisoned.
+    const bool poisoned =
+        need_in && __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                       fa.flags + (size_t)(s - 1) * H + h, __ATOMIC_ACQUIRE,
+                       __HIP_MEMORY_SCOPE_AGENT)) == 0u;
     combine_states(S, prev, need_in, ini_last, ps == a, need_out, gam,
-                   p.ws + ((int64_t)s * H + h) * DD, ln.w, ln.l32, ln.g);
+                   p.ws + ((int64_t)s * H + h) * DD, ln.w, ln.l32, ln.g, poisoned);
     if (need_out) {
       __builtin_amdgcn_s_waitcnt(0);  // this wave's record stores have completed
       __syncthreads();

@@ -145,6 +145,38 @@ la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const 
                              void *hip_stream);
 
 /*
+ * lightning_attn_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same computation, arguments and results as
+ * lightning_attn_fwd, without the workspace: the prefill's scratch (the
+ * segment states) lives in a device array inside the library,
+ * lightning_attn_noalloc_scratch_bytes() bytes (64 MiB) on every GPU the
+ * library runs on, held from its first use until the process ends.  The
+ * call allocates nothing; the device address of that array is looked up on
+ * the first call on a device, which must be the current device (the one
+ * hip_stream belongs to).
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (nothing in it needs to start at zero; the single-pass schedule
+ * clears its flags with a kernel).  Calls that overlap on one GPU (other
+ * streams, other host threads) race on it and give wrong results: order
+ * them on one stream, or use lightning_attn_fwd with a workspace each.
+ *
+ * Returns LA_ERR_WORKSPACE, launching nothing, when the call needs more
+ * scratch than the array holds, i.e. when lightning_attn_fwd_workspace_size
+ * for the same arguments exceeds lightning_attn_noalloc_scratch_bytes()
+ * (e.g. many short segments over many heads); LA_ERR_HIP if the array's
+ * address cannot be obtained; otherwise as lightning_attn_fwd.
+ */
+size_t lightning_attn_noalloc_scratch_bytes(void);
+
+la_status lightning_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                                     const float *decay, int B, int H, int64_t N, int d,
+                                     int block, la_dtype dt, const float *init_state, void *out,
+                                     float *final_state, int64_t segment_tokens,
+                                     void *hip_stream);
+
+/*
  * lightning_attn_fwd with per-kernel timing (a measurement aid; the same
  * computation as lightning_attn_fwd, for which phase_events == NULL).
  *

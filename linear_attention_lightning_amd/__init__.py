@@ -10,6 +10,7 @@ every call raises.
 Entry points (same names as the C ABI):
   lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, ...) -> (out, final_state)
   lightning_attn_fwd_timed(q, k, v, decay, phase_events, ...) -> (out, final_state)
+  lightning_attn_fwd_noalloc(q, k, v, decay, ...) -> (out, final_state)   (no workspace)
   lightning_attn_fwd_layout(q, k, v, decay, layout, ...) -> (out, final_state)
   lightning_attn_fwd_varlen_layout(q, k, v, decay, cu_seqlens, layout, ...) -> (out, final_states)
   lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, ...) -> (out, final_states)
@@ -34,6 +35,7 @@ import ctypes
 import os
 
 __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd_layout",
+           "lightning_attn_fwd_noalloc", "lightning_attn_noalloc_scratch_bytes",
            "lightning_attn_fwd_varlen", "lightning_attn_fwd_varlen_layout",
            "lightning_attn_fwd_varlen_snapshots", "snapshot_row_offsets", "lightning_attn_decode",
            "lightning_attn_mixed_step", "lightning_attn_bwd", "lightning_attn_bwd_workspace_size",
@@ -98,6 +100,10 @@ def load_library(path=None):
     lib.lightning_attn_fwd_timed.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P,
                                              ctypes.POINTER(P)]
     lib.lightning_attn_fwd_timed.restype = I
+    lib.lightning_attn_noalloc_scratch_bytes.argtypes = []
+    lib.lightning_attn_noalloc_scratch_bytes.restype = Z
+    lib.lightning_attn_fwd_noalloc.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P]
+    lib.lightning_attn_fwd_noalloc.restype = I
     lib.lightning_attn_fwd_layout.argtypes = [P, P, P, P, I, I, L, I, I, I, I, P, P, P, L, P, Z, P]
     lib.lightning_attn_fwd_layout.restype = I
     lib.lightning_attn_fwd_varlen_layout.argtypes = [P, P, P, P, P, I, I, L, I, I, I, I, P, P, P,
@@ -220,6 +226,42 @@ def lightning_attn_fwd_layout(q, k, v, decay, layout, block=128, init_state=None
     [B, H, d, d] float32 either way."""
     return _fwd(q, k, v, decay, block, init_state, segment_tokens, out, final_state, workspace,
                 None, layout)
+
+
+def lightning_attn_noalloc_scratch_bytes():
+    """Bytes of the library's own per-GPU scratch array, which
+    lightning_attn_fwd_noalloc uses in place of a workspace."""
+    return load_library().lightning_attn_noalloc_scratch_bytes()
+
+
+def lightning_attn_fwd_noalloc(q, k, v, decay, block=128, init_state=None, segment_tokens=0,
+                               out=None, final_state=None):
+    """lightning_attn_fwd without a workspace: the library keeps the
+    prefill's scratch in its own device array (see the C header for the
+    limit and for calls that overlap on one GPU).  The C call allocates
+    nothing; pass `out` and `final_state` to allocate nothing here either."""
+    torch = _torch()
+    lib = load_library()
+    B, H, N, d = q.shape
+    dev = q.device
+    _check(k, "k", q.shape, q.dtype, dev)
+    _check(v, "v", q.shape, q.dtype, dev)
+    _check(q, "q", q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (B, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", (B, H, d, d), torch.float32, dev)
+    st = lib.lightning_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), B, H, N, d, block,
+                                        _dtype_code(q), _ptr(init_state), _ptr(out),
+                                        _ptr(final_state), segment_tokens, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd_noalloc")
+    return out, final_state
 
 
 def lightning_attn_fwd_timed(q, k, v, decay, phase_events, block=128, init_state=None,

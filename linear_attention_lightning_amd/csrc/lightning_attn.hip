@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "la_common.h"
 #include "la_prefill_mfma.h"
@@ -866,9 +867,62 @@ la_status fwd_varlen_save(const void *q, const void *k, const void *v, const flo
   return st;
 }
 
+// Scratch of lightning_attn_fwd_noalloc: the workspace of a prefill, held in
+// the library instead of coming from the caller (64 MiB: the partial states
+// of the local-state pass at the 64-head 32768-token layer shape, 4 segments
+// x 4 pieces x 64 heads x 64 KiB, and likewise at the 1M-token 8-head and
+// the packed 65536-token 64-head shapes).  Every GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address comes
+// from hipGetSymbolAddress, once per device (scratch_address below).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the
+// first call on that device (with that device current) and kept.
+la_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = e;
+    return LA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return LA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      g_last_hip_error = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return LA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t lightning_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+la_status lightning_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                                     const float *decay, int B, int H, int64_t N, int d,
+                                     int block, la_dtype dt, const float *init_state, void *out,
+                                     float *final_state, int64_t segment_tokens,
+                                     void *hip_stream) {
+  void *ws = nullptr;
+  const la_status st = scratch_address(&ws);
+  if (st != LA_OK) return st;
+  return fwd_fixed(q, k, v, decay, B, H, N, d, block, dt, LA_HEAD_MAJOR, init_state, out,
+                   final_state, segment_tokens, ws, kScratchBytes, hip_stream, nullptr);
+}
 
 size_t lightning_attn_fwd_chdecay_varlen_workspace_size(int num_seqs, int H, int64_t total_N,
                                                         int d, int block, la_dtype dt,

@@ -51,6 +51,18 @@ def test_exports_only_declared_symbols():
     assert ours == set(declared_functions()), sorted(ours ^ set(declared_functions()))
 
 
+def test_noalloc_scratch_size(lib):
+    """The allocation-free prefill's per-GPU scratch array: 64 MiB, enough
+    for the plans of the 64-head 32768-token, packed 65536-token and
+    1M-token 8-head workloads."""
+    assert lib.lightning_attn_noalloc_scratch_bytes() == 64 << 20
+    for B, H, N in ((1, 64, 32768), (1, 8, 1 << 20)):
+        assert (lib.lightning_attn_fwd_workspace_size(B, H, N, 128, 128, BF16, 0)
+                <= lib.lightning_attn_noalloc_scratch_bytes())
+    assert (lib.lightning_attn_fwd_varlen_workspace_size(25, 64, 65536, 128, 128, BF16, 0)
+            <= lib.lightning_attn_noalloc_scratch_bytes())
+
+
 def test_status_strings_and_version(lib):
     for s in range(5):
         assert lib.lightning_attn_status_string(s)

@@ -65,15 +65,20 @@
 extern "C" {
 #endif
 
+/* Each enum ends with a *_FORCE_INT32 value that is never used: it makes
+ * every int a valid value of the type, so an out-of-range code a C caller
+ * passes is rejected as documented (LA_ERR_UNSUPPORTED, "unknown status")
+ * rather than being undefined in the C++ implementation. */
 typedef enum {
   LA_OK = 0,
   LA_ERR_INVALID_ARG = 1,  /* NULL pointer where data is needed, negative size */
   LA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, block not in {16..256}, dtype */
   LA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than *_workspace_size */
-  LA_ERR_HIP = 4           /* a HIP launch reported an error */
+  LA_ERR_HIP = 4,          /* a HIP launch reported an error */
+  LA_STATUS_FORCE_INT32 = 0x7fffffff
 } la_status;
 
-typedef enum { LA_FP32 = 0, LA_BF16 = 1 } la_dtype;
+typedef enum { LA_FP32 = 0, LA_BF16 = 1, LA_DTYPE_FORCE_INT32 = 0x7fffffff } la_dtype;
 
 /* segment_tokens value of the prefill entry points: every sequence is one
  * segment, walked by one workgroup per head.  No state crosses a segment,
@@ -92,7 +97,8 @@ enum { LA_SEGMENT_PER_SEQUENCE = -1 };
  * adjustment is folded into the kernels that read Q, K and V). */
 typedef enum {
   LA_HEAD_MAJOR = 0,  /* fixed: [B][H][N][d];  packed: [H][total_N][d] */
-  LA_TOKEN_MAJOR = 1  /* fixed: [B][N][H][d];  packed: [total_N][H][d] */
+  LA_TOKEN_MAJOR = 1, /* fixed: [B][N][H][d];  packed: [total_N][H][d] */
+  LA_LAYOUT_FORCE_INT32 = 0x7fffffff
 } la_layout;
 
 /* Human-readable name of a status code (static storage; never NULL). */

@@ -74,11 +74,12 @@ class LightningAttnError(RuntimeError):
 
 def load_library(path=None):
     """Loads liblightning_attn.so (built in-tree by
-    `python -m linear_attention_lightning_amd.build`)."""
+    `python -m linear_attention_lightning_amd.build`), or the build at
+    `path` or at $LIGHTNING_ATTN_LIB (e.g. one with host-side sanitizers)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("LIGHTNING_ATTN_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError("HIP library %s is not built; run "
                            "`python -m linear_attention_lightning_amd.build`" % p)

@@ -1073,6 +1073,7 @@ const char *lightning_attn_status_string(la_status s) {
     case LA_ERR_UNSUPPORTED: return "unsupported configuration";
     case LA_ERR_WORKSPACE: return "workspace missing or too small";
     case LA_ERR_HIP: return "HIP launch error";
+    default: break;
   }
   return "unknown status";
 }

@@ -27,10 +27,13 @@ def _ptr(a):
 
 
 def load(path=None):
-    """Loads (building first if absent) liboracle.so, or the library at path."""
+    """Loads (building first if absent) liboracle.so, or the library at path
+    (or at $ORACLE_LIB, e.g. a sanitizer build of oracle.c)."""
     global _LIB
     if path is not None:
         return _bind(ctypes.CDLL(path))
+    if _LIB is None and os.environ.get("ORACLE_LIB"):
+        _LIB = _bind(ctypes.CDLL(os.environ["ORACLE_LIB"]))
     if _LIB is None:
         if not os.path.exists(_build.LIB):
             _build.build()

@@ -87,7 +87,7 @@ def time_steps(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps  # ms per step
 
 
-def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup, phases=False):
+def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup, phases=False, trace=None):
     """ms per step over `steps` timed steps after `warmup`.  With phases, also
     the average ms of each of the library's three phases (local-state pass,
     segment scan, output pass), from HIP events the library records between
@@ -124,7 +124,22 @@ def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup, phases=Fal
             la.lightning_attn_fwd(q, k, v, decay, block=block, out=out, final_state=fin,
                                   workspace=ws)
 
-    ms = time_steps(step, steps, warmup, stream)
+    run = step
+    if trace is not None:
+        # An event after every step, the warm-up included (diagnostic: the
+        # records between launches leave short gaps of their own).
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(warmup + steps + 1)]
+
+        def run():
+            step()
+            marks[calls[0]].record(stream)
+
+        torch.cuda.synchronize()
+        marks[0].record(stream)
+    ms = time_steps(run, steps, warmup, stream)
+    if trace is not None:
+        trace.extend(round(marks[i].elapsed_time(marks[i + 1]) * 1e3, 1)
+                     for i in range(warmup + steps))
     phase_ms = None
     if phases:
         phase_ms = [sum(row[j].elapsed_time(row[j + 1]) for row in evs.values()) / len(evs)
@@ -561,7 +576,11 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this size once (a plain "
                          "copy kernel of known size, to scale HBM byte counters)")
-    ap.add_argument("--leg", choices=["backward", "serving", "snapshots", "chdecay"], default=None,
+    ap.add_argument("--trace", action="store_true",
+                    help="also report the time of every headline step (warm-up and timed), "
+                         "from HIP events between the steps")
+    ap.add_argument("--leg", choices=["backward", "serving", "snapshots", "chdecay", "million",
+                                      "varlen", "decode"], default=None,
                     help="time only this extra workload and print its JSON object (for "
                          "profiling it on its own); the headline line is not printed")
     args = ap.parse_args()
@@ -580,13 +599,17 @@ def main():
         legs = {"backward": lambda: bench_backward(la, inputs, args.steps, 20),
                 "serving": lambda: bench_serving(la, inputs, P=50),
                 "snapshots": lambda: bench_snapshots(la, inputs, args.steps, 2),
-                "chdecay": lambda: bench_chdecay(la, inputs, args.steps, 20)}
+                "chdecay": lambda: bench_chdecay(la, inputs, args.steps, 20),
+                "million": lambda: bench_million(la, inputs, args.steps, 2),
+                "varlen": lambda: bench_varlen(la, inputs, args.steps, 2),
+                "decode": lambda: bench_decode(la, inputs, reps=5, warmup=1)}
         print(json.dumps(legs[args.leg]()), flush=True)
         return
     w = inputs.WORKLOADS["layer_h64_n32k"]
     B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
+    trace = [] if args.trace else None
     ms, phase_ms, tensors = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], args.steps,
-                                          args.warmup, phases=True)
+                                          args.warmup, phases=True, trace=trace)
     sec = ms * 1e-3
     flops = prefill_flops(B, H, N, d, block)
     tflops = flops / sec / 1e12
@@ -630,6 +653,8 @@ def main():
                      "note": "algorithmic bytes per step / step time; traffic = counter "
                              "bytes of all three kernels per step"},
     }
+    if trace is not None:
+        res["per_step_us"] = trace
     res["run"] = run_metadata(w["seed"])
     res["copy_ceiling"] = copy_ceiling()
     if args.copy_calibration_mib > 0:

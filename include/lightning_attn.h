@@ -156,7 +156,7 @@ la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const 
  * allocation.  The same computation, arguments and results as
  * lightning_attn_fwd, without the workspace: the prefill's scratch (the
  * segment states) lives in a device array inside the library,
- * lightning_attn_noalloc_scratch_bytes() bytes (64 MiB) on every GPU the
+ * lightning_attn_noalloc_scratch_bytes() bytes (256 MiB) on every GPU the
  * library runs on, held from its first use until the process ends.  The
  * call allocates nothing; the device address of that array is looked up on
  * the first call on a device, which must be the current device (the one

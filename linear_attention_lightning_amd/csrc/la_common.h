@@ -172,6 +172,22 @@ __device__ __forceinline__ int64_t first_weighted(int64_t ps, int64_t b, float l
   return far >= (float)T ? ps + (int64_t)(far / (float)T) * T : ps;
 }
 
+// XCD-aware work order.  MI355X dispatches workgroup i of a launch to XCD
+// i mod 8 (8 XCDs of 32 CUs, each with its own L2 and its own share of the
+// memory bandwidth).  A grid whose items are ordered heads fastest thus puts
+// every item of head h on XCD h mod 8: with 8 heads, a slowly decaying
+// head's whole local-state pass (its long pieces) on one XCD.  Kernels whose
+// items carry unequal work take item xcd_spread(i, n) in workgroup i
+// instead: inside each group of 8 consecutive workgroups the items are
+// rotated by the group's index, so items 8 apart (the same head) land on
+// different XCDs.  A bijection of [0, n) (the last, partial group keeps its
+// order).
+__device__ __forceinline__ int xcd_spread(int i, int n) {
+  const int j = i >> 3, x = i & 7;
+  if ((j + 1) * 8 > n) return i;
+  return (j << 3) | ((x + j) & 7);
+}
+
 // Arguments shared by the prefill kernels.
 struct FwdArgs {
   const void *q, *k, *v;
@@ -202,14 +218,37 @@ __device__ __forceinline__ void segment_bounds(const FwdArgs &p, int s, int64_t 
   }
 }
 
-// Piece r of R of a local-state range [ps, b) cut into chunks of C tokens
-// aligned to ps: chunks [r n / R, (r + 1) n / R) of its n chunks, as tokens
-// [*x0, *x1) (x1 capped at b).  Pieces may be empty when n < R.
-__device__ __forceinline__ void piece_bounds(int64_t ps, int64_t b, int C, int R, int r,
-                                             int64_t *x0, int64_t *x1) {
+// The pieces of a local-state range [ps, b), chunks of C tokens aligned to
+// ps: its weighted part [tf, b) (tf = first_weighted) is cut into 2^lg
+// pieces of whole chunks, one workgroup each.  A range weighted throughout
+// gets R pieces (the plan's piece count, a power of two); one whose leading
+// chunks carry zero weight (a faster decay) gets proportionally fewer, so
+// that every piece is about as long as a piece of a fully weighted range.
+struct Pieces {
+  int64_t tf;  // first weighted token (a chunk boundary)
+  int64_t nw;  // weighted chunks
+  int lg;      // log2 of the piece count
+};
+
+__device__ __forceinline__ Pieces piece_plan(int64_t ps, int64_t b, float log2lam, int C, int R) {
+  Pieces P;
+  P.tf = first_weighted(ps, b, log2lam, C);
   const int64_t n = (b - ps + C - 1) / C;
-  *x0 = ps + ((int64_t)r * n / R) * C;
-  const int64_t e = ps + ((int64_t)(r + 1) * n / R) * C;
+  P.nw = (b - P.tf + C - 1) / C;
+  const int64_t want = n > 0 ? (P.nw * R + n - 1) / n : 1;
+  int lg = 0;
+  while ((1 << lg) < want && (1 << lg) < R) ++lg;
+  P.lg = lg;
+  return P;
+}
+
+// Piece r (< 2^P.lg) of that cut: chunks [r nw / 2^lg, (r + 1) nw / 2^lg) of
+// the weighted part, as tokens [*x0, *x1) (x1 capped at b).  A piece may be
+// empty (x0 == x1) when the weighted part has fewer chunks than pieces.
+__device__ __forceinline__ void piece_range(const Pieces &P, int64_t b, int C, int r, int64_t *x0,
+                                            int64_t *x1) {
+  *x0 = P.tf + (((int64_t)r * P.nw) >> P.lg) * C;
+  const int64_t e = P.tf + ((((int64_t)r + 1) * P.nw) >> P.lg) * C;
   *x1 = e < b ? e : b;
 }
 

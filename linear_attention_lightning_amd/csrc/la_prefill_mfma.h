@@ -990,17 +990,20 @@ void prefill_fused_kernel(FusedArgs fa) {
 
 // Phase A: the local state of each segment's last piece, from zero:
 //   L_s = sum_{c in [ps, b)} lambda^(b-1-c) k_c^T v_c, one decayed MFMA sum.
-// The piece is cut into p.r_split sub-ranges [x0, x1) of whole 64-token
-// chunks (piece_bounds); one workgroup computes each partial state
+// Chunks before first_weighted(ps, b) carry exactly zero weight and are left
+// out; the weighted part is cut into up to p.r_split sub-ranges [x0, x1) of
+// whole 64-token chunks (piece_plan: fewer for a head whose weighted part is
+// short, so that no workgroup walks much more than a piece of a slowly
+// decaying head); one workgroup computes each partial state
 //   P_r = sum_{c in [x0, x1)} lambda^(x1-1-c) k_c^T v_c
 // into slot (s, r), and the scan forms L_s = sum_r lambda^(b - x1_r) P_r.
-// Small workgroups (4 waves, 32 KB of LDS, one chunk in flight) several to a
-// CU hide one another's load and arithmetic latency.  Chunks before
-// first_weighted(ps, b) carry exactly zero weight and are skipped; a partial
-// that lies entirely before that point is not computed (nor read).
+// Small workgroups (4 waves, 32 KB of LDS, two chunks in flight) several to
+// a CU hide one another's load and arithmetic latency.
 // Grid: (nseg - 1) * r_split * H workgroups (the last segment hands no
-// state on), heads fastest, segments in reverse: the K/V read last are the
-// first segments', which the output pass reads first (Infinity Cache).
+// state on), items heads fastest, segments in reverse: the K/V read last are
+// the first segments', which the output pass reads first (Infinity Cache);
+// items spread over the XCDs by xcd_spread (a head's pieces are long or
+// short with its decay).
 // (Ordering the grid by decreasing decay, so that the long pieces of slowly
 // decaying heads start first, measured slower.)
 // Wave u owns state rows 32u..32u+31.
@@ -1016,7 +1019,8 @@ void local_state_kernel(FwdArgs p) {
   const int l32 = lane & 31, g = lane >> 5;
   const SeqMap &m = p.m;
   const int H = m.H, R = p.r_split;
-  const int idx = (int)(blockIdx.x / H), h = blockIdx.x - (blockIdx.x / H) * H;
+  const int item = xcd_spread((int)blockIdx.x, (int)gridDim.x);
+  const int idx = item / H, h = item - idx * H;
   const int s = p.nseg - 2 - idx / R, r = R - 1 - idx % R;
   float l2max = 0.f, l2f[8];  // channel-wise: slowest channel, and this thread's 8 channels
   if constexpr (CH) {
@@ -1039,10 +1043,10 @@ void local_state_kernel(FwdArgs p) {
   const int64_t ps0 = m.start(jl);
   const int64_t ps = ps0 > a ? ps0 : a;
   const int64_t base = m.row_base(h, jl);
-  int64_t x0, x1;
-  piece_bounds(ps, b, C_LOCAL, R, r, &x0, &x1);
-  const int64_t tf = first_weighted(ps, b, CH ? l2max : l2, C_LOCAL);
-  const int64_t r0 = tf > x0 ? tf : x0;
+  const Pieces P = piece_plan(ps, b, CH ? l2max : l2, C_LOCAL, R);
+  if (r >= (1 << P.lg)) return;
+  int64_t r0, x1;
+  piece_range(P, b, C_LOCAL, r, &r0, &x1);
   if (r0 >= x1) return;
   float tail[8];
 #pragma unroll

@@ -169,7 +169,10 @@ __global__ __launch_bounds__(NT) void local_state_kernel(FwdArgs p) {
   const int tid = threadIdx.x;
   const SeqMap &m = p.m;
   const int H = m.H;
-  const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
+  // (items spread over the XCDs: a head's weighted range is long or short
+  // with its decay)
+  const int item = xcd_spread((int)blockIdx.x, (int)gridDim.x);
+  const int s = item / H, h = item - s * H;
   float log2lam;
   if constexpr (CH) {
     const float *al = p.chdecay + (int64_t)h * D;

@@ -16,7 +16,8 @@ namespace la {
 // states of each segment's pieces on entry (L_s is their decayed sum) and
 // S_in[s] at the segment's first slot on exit.  Also writes final states of
 // zero-length sequences.
-// Grid: (H, d*d / 1024); each thread owns 4 consecutive state elements.
+// Grid: (H, d*d / 1024), items spread over the XCDs (xcd_spread); each
+// thread owns 4 consecutive state elements.
 struct ScanArgs {
   SeqMap m;
   const float *decay;
@@ -45,7 +46,7 @@ struct SegInfo {
 };
 
 __device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, int s,
-                                            float log2lam, int lgR) {
+                                            float log2lam) {
   SegInfo d;
   const int64_t a = (int64_t)s * p.seg_len;
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
@@ -58,17 +59,15 @@ __device__ __forceinline__ SegInfo describe(const ScanArgs &p, const SeqMap &m, 
   d.hands_on = m.start(jl + 1) != b;
   d.gam = pow_lam(log2lam, (float)(b - ps));
   d.gam_n = (float)(b - ps);
-  // Pieces as in piece_bounds (R a power of two); a piece is computed when
-  // some of it lies at or after first_weighted and the state is handed on.
-  const int64_t tf = first_weighted(ps, b, log2lam, p.C);
-  const int64_t n = (b - ps + p.C - 1) / p.C;
+  // Pieces as the local-state pass cut them (piece_plan); a piece was
+  // computed when it is not empty and the state is handed on.
+  const Pieces P = piece_plan(ps, b, log2lam, p.C, p.r_split);
   d.live = 0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int64_t x0 = ps + ((r * n) >> lgR) * p.C;
-    const int64_t e1 = ps + (((r + 1) * n) >> lgR) * p.C;
-    const int64_t x1 = e1 < b ? e1 : b;
-    const bool live = d.hands_on && r < p.r_split && (tf > x0 ? tf : x0) < x1;
+    int64_t x0 = b, x1 = b;
+    if (r < (1 << P.lg)) piece_range(P, b, p.C, r, &x0, &x1);
+    const bool live = d.hands_on && x0 < x1;
     d.live |= live ? (1 << r) : 0;
     d.wt[r] = live ? pow_lam(log2lam, (float)(b - x1)) : 0.f;
     d.wt_n[r] = (float)(b - x1);
@@ -82,12 +81,15 @@ template <int R>
 __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
   constexpr int MAXS = 256;              // segments described per pass
   constexpr int BLK = R >= 16 ? 1 : R >= 8 ? 2 : 4;  // segments loaded together
-  constexpr int lgR = R == 16 ? 4 : R == 8 ? 3 : R == 4 ? 2 : R == 2 ? 1 : 0;
   __shared__ SegInfo info[MAXS];
   const SeqMap &m = p.m;
-  const int H = m.H, h = blockIdx.x;
+  // Items (head, element block), heads fastest, spread over the XCDs (a
+  // slowly decaying head has more live pieces to read).
+  const int item = xcd_spread((int)(blockIdx.y * gridDim.x + blockIdx.x),
+                              (int)(gridDim.x * gridDim.y));
+  const int H = m.H, h = item % H;
   const int64_t DD = (int64_t)p.d * p.d;
-  const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+  const int64_t e = ((int64_t)(item / H) * 256 + threadIdx.x) * 4;
   const bool mine = e < DD;
   // Channel-wise decay: segments are described with the slowest channel's
   // decay (a piece is live if any channel weighs it), and this thread's
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
   for (int sb = 0; sb < p.nseg; sb += MAXS) {
     const int cnt = (p.nseg - sb) < MAXS ? (p.nseg - sb) : MAXS;
     __syncthreads();
-    if ((int)threadIdx.x < cnt) info[threadIdx.x] = describe(p, m, sb + threadIdx.x, log2lam, lgR);
+    if ((int)threadIdx.x < cnt) info[threadIdx.x] = describe(p, m, sb + threadIdx.x, log2lam);
     __syncthreads();
     if (!mine) continue;
     for (int s0 = 0; s0 < cnt; s0 += BLK) {

@@ -85,15 +85,22 @@ int64_t target_groups(int d, la_dtype dt, bool ch = false) {
   return use_mfma(d, dt, ch) ? 256 : 512;
 }
 
-// Pieces per segment of the MFMA local-state pass: one small workgroup per
-// 8 or more 64-token chunks, at most 4, so that several workgroups share a
-// CU and hide one another's latency.  (8 or 16 pieces made the pass itself
-// faster but the scan, which reads every piece's partial state, slower by
-// more.)  The vector-ALU pass uses one.
+// Pieces per segment of the MFMA local-state pass (for a head whose whole
+// segment carries weight; piece_plan gives a faster-decaying head fewer):
+// 4 pieces of at least 8 chunks of 64 tokens for segments up to 8192 tokens,
+// so that several workgroups share a CU and hide one another's latency (8 or
+// 16 there made the pass faster but the scan, which reads every piece's
+// partial state, slower by more); longer segments keep the pieces at 2048
+// tokens, up to 16, since a piece is walked serially by one workgroup (at
+// the 1M-token 8-head shape four 8192-token pieces per segment left the
+// slowest heads' workgroups walking 128 chunks each).  A power of two (the
+// pieces are cut by shifts).  The vector-ALU pass uses one.
 int pieces(int64_t seg, int d, la_dtype dt, bool ch = false) {
   if (!use_mfma(d, dt, ch)) return 1;
   const int64_t r = seg / la::mfma::C_LOCAL / 8;
-  return r >= 4 ? 4 : r >= 2 ? 2 : 1;  // a power of two (the scan shifts by it)
+  int n = r >= 4 ? 4 : r >= 2 ? 2 : 1;
+  while (n < 16 && (int64_t)n * 2048 < seg) n *= 2;
+  return n;
 }
 
 size_t phased_ws_bytes(const Plan &p, int H, int d) {
@@ -868,14 +875,13 @@ la_status fwd_varlen_save(const void *q, const void *k, const void *v, const flo
 }
 
 // Scratch of lightning_attn_fwd_noalloc: the workspace of a prefill, held in
-// the library instead of coming from the caller (64 MiB: the partial states
-// of the local-state pass at the 64-head 32768-token layer shape, 4 segments
-// x 4 pieces x 64 heads x 64 KiB, and likewise at the 1M-token 8-head and
-// the packed 65536-token 64-head shapes).  Every GPU the library runs on
+// the library instead of coming from the caller (256 MiB: the partial states
+// of the local-state pass at the 1M-token 8-head shape, 32 segments x 16
+// pieces x 8 heads x 64 KiB; 64 MiB at the 64-head 32768-token shape).  Every GPU the library runs on
 // holds its own copy until the process ends.  In host code `scratch` names a
 // host-side stand-in, never the device memory: its device address comes
 // from hipGetSymbolAddress, once per device (scratch_address below).
-constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr size_t kScratchBytes = (size_t)256 << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;

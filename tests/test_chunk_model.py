@@ -42,8 +42,38 @@ def seq_of(cu, tok):
     return int(np.searchsorted(cu, tok, side="right") - 1)
 
 
-def model(qh, kh, vh, lam, cu, T, seg, init=None, scan=True, bf16=False):
+def piece_plan(ps, b, lam, C, R):
+    """The local-state pass's cut of [ps, b): chunks of C tokens aligned to
+    ps; those before the first one that can carry a nonzero float32 weight
+    (lambda^n < 2^-160) are left out, and the rest is cut into 2^lg pieces,
+    2^lg the power of two covering R times the weighted share (at most R).
+    Returns the list of pieces [x0, x1)."""
+    l2 = np.float32(np.log2(np.float32(lam)))
+    tf = ps
+    if l2 < 0:
+        far = np.float32(b - ps) + np.float32(160.0) / l2
+        if far >= np.float32(C):
+            tf = ps + int(far / np.float32(C)) * C
+    n = -(-(b - ps) // C)
+    nw = -(-(b - tf) // C)
+    want = -(-(nw * R) // n) if n > 0 else 1
+    lg = 0
+    while (1 << lg) < want and (1 << lg) < R:
+        lg += 1
+    out = []
+    for r in range(1 << lg):
+        x0 = tf + ((r * nw) >> lg) * C
+        x1 = min(b, tf + (((r + 1) * nw) >> lg) * C)
+        if x0 < x1:
+            out.append((x0, x1))
+    return out
+
+
+def model(qh, kh, vh, lam, cu, T, seg, init=None, scan=True, bf16=False, pieces=None, C=64):
     """qh, kh, vh: [H, total, d] float64; cu: int64 [S+1]; init [S, H, d, d].
+    pieces: None (phase A as one decayed sum), or R: phase A as the
+    local-state pass runs it -- partial states of the pieces piece_plan cuts
+    (chunks of C tokens), each weighted by lambda^(b - x1) in the scan.
     Returns (out [H, total, d], final [S, H, d, d])."""
     H, total, d = qh.shape
     S_n = len(cu) - 1
@@ -62,8 +92,15 @@ def model(qh, kh, vh, lam, cu, T, seg, init=None, scan=True, bf16=False):
             a, b = s * seg, min(total, (s + 1) * seg)
             jl = seq_of(cu, b - 1)
             ps = max(a, int(cu[jl]))
-            w = L_ ** (b - 1 - np.arange(ps, b))
-            loc.append((kh[h, ps:b] * w[:, None]).T @ vh[h, ps:b])
+            if pieces is None:
+                w = L_ ** (b - 1 - np.arange(ps, b))
+                loc.append((kh[h, ps:b] * w[:, None]).T @ vh[h, ps:b])
+            else:
+                acc = np.zeros((d, d))
+                for x0, x1 in piece_plan(ps, b, lam[h], C, pieces):
+                    w = L_ ** (x1 - 1 - np.arange(x0, x1))
+                    acc += L_ ** (b - x1) * ((kh[h, x0:x1] * w[:, None]).T @ vh[h, x0:x1])
+                loc.append(acc)
             gam.append(L_ ** (b - ps))
         # phase B
         s_in = []
@@ -162,3 +199,36 @@ def test_bf16_rounding_budget_is_inside_tolerance():
                    bf16=True)
     eo, ef = rel_err(mo, fixed_to_packed(o)), rel_err(mf, f)
     assert eo < 2e-2 / 4 and ef < 2e-2 / 4, (eo, ef)
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 16])
+def test_local_state_pieces_model_matches_oracle(R):
+    """Phase A computed as the local-state pass cuts it: the weighted part of
+    each segment's last piece split into up to R pieces (fewer for the fast
+    decays, whose leading chunks carry zero float32 weight and are left out),
+    the partial states weighted by lambda^(b - x1) -- equal to the oracle."""
+    lens = [700, 0, 1300, 64, 2000]
+    cu = inputs.cu_seqlens(lens).astype(np.int64)
+    H, d = 4, 8
+    q, k, v = inputs.host_qkv((H, int(cu[-1]), d), 11, dtype="fp32")
+    lam = np.asarray([0.999, 0.97, 0.6, 1.0], np.float32)
+    init = inputs.host_state((len(lens), H, d, d), 12).astype(np.float64)
+    o, f, _ = oracle.fwd_varlen(q, k, v, lam, cu.astype(np.int32), init=init)
+    mo, mf = model(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), lam, cu, 32,
+                   512, init=init, pieces=R, C=8)
+    assert rel_err(mo, o) < 1e-12
+    assert rel_err(mf, f) < 1e-12
+
+
+def test_piece_plan_cuts():
+    """A segment weighted throughout gets R pieces; a fast decay fewer (or
+    one); no piece is empty or overlaps, and they end at the segment end."""
+    full = piece_plan(0, 32768, 0.996, 64, 16)
+    assert len(full) == 16 and full[-1][1] == 32768
+    fast = piece_plan(0, 32768, 0.6065, 64, 16)
+    assert len(fast) == 1 and fast[0][1] == 32768 and fast[0][0] > 32000
+    mid = piece_plan(0, 32768, 0.98, 64, 16)
+    assert 1 < len(mid) < 16
+    for cut in (full, fast, mid):
+        assert all(x0 < x1 for x0, x1 in cut)
+        assert all(cut[i][1] == cut[i + 1][0] for i in range(len(cut) - 1))

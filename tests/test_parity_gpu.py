@@ -231,11 +231,14 @@ def test_varlen_bf16(seg, prefill_path):
     run_varlen_case([300, 0, 1, 129, 1024, 5, 0, 640, 2000], 4, 128, "bf16", seed=70, seg=seg)
 
 
-def test_varlen_eight_pieces(prefill_path):
-    """4096-token segments: the local-state pass splits each segment's last
-    piece into 8 parts whose weighted sum the scan forms; the sequences cross
-    the segment cuts, so every part's weight reaches an entering state."""
-    run_varlen_case([5000, 0, 3000, 7000, 100, 4500], 3, 128, "bf16", seed=72, seg=4096)
+@pytest.mark.parametrize("seg", [4096, 16384, 32768])
+def test_varlen_many_pieces(seg, prefill_path):
+    """Segments of 4096, 16384 and 32768 tokens: the local-state pass cuts the
+    weighted part of each segment's last piece into 4, 8 and 16 parts for the
+    slowest head (fewer for the faster ones) whose weighted sum the scan
+    forms; the sequences cross the segment cuts, so every part's weight
+    reaches an entering state."""
+    run_varlen_case([20000, 0, 3000, 37000, 100, 4500], 3, 128, "bf16", seed=72, seg=seg)
 
 
 @pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])

@@ -72,18 +72,18 @@ def test_noalloc_vector_alu_path():
 
 
 def test_noalloc_refuses_beyond_scratch():
-    """64-token segments over 64 heads need 256 MiB of partial states: the
+    """32-token segments over 64 heads need 512 MiB of partial states: the
     call returns LA_ERR_WORKSPACE and writes nothing."""
     torch = torch_mod()
     B, H, N, d = 1, 64, 4096, 128
-    need = la.lightning_attn_fwd_workspace_size(B, H, N, d, 128, 1, 64)
+    need = la.lightning_attn_fwd_workspace_size(B, H, N, d, 128, 1, 32)
     assert need > la.lightning_attn_noalloc_scratch_bytes()
     tq, tk, tv = inputs.device_qkv((B, H, N, d), 15, "bf16")
     tl = torch.from_numpy(inputs.decay_schedule(H)).cuda()
     out = torch.full_like(tq, float("nan"))
     fin = torch.full((B, H, d, d), float("nan"), device="cuda")
-    assert noalloc_c(tq, tk, tv, tl, out, fin, seg=64) == 3
+    assert noalloc_c(tq, tk, tv, tl, out, fin, seg=32) == 3
     torch.cuda.synchronize()
     assert bool(torch.isnan(out).all()) and bool(torch.isnan(fin).all())
     with pytest.raises(la.LightningAttnError, match="LA_ERR_WORKSPACE"):
-        la.lightning_attn_fwd_noalloc(tq, tk, tv, tl, segment_tokens=64)
+        la.lightning_attn_fwd_noalloc(tq, tk, tv, tl, segment_tokens=32)

@@ -335,18 +335,18 @@ la_status lightning_attn_decode(const void *q, const void *k, const void *v, con
  *     S_t[i][j] = alpha_i S_{t-1}[i][j] + k_t[i] v_t[j],   o_t = q_t S_t.
  * With all channels equal it is lightning_attn_fwd_layout.
  *
- *   alpha        : [H][d] float32 DEVICE array (a precondition, not
- *                  checked: 0 < alpha <= 1, and alpha >= 0.1 for bf16 with
- *                  d = 128).
+ *   alpha        : [H][d] float32 DEVICE array, 0 < alpha <= 1 (a
+ *                  precondition, not checked: it lives on the device).
  *   Other arguments as for lightning_attn_fwd_layout (workspace from
  *   lightning_attn_fwd_chdecay_workspace_size).  bf16 with d = 128 runs on
  *   MFMA in 64-token chunks, the decay inside a chunk written as an absolute
  *   position around the chunk's middle row (Q scaled by alpha^(q-32), K by
  *   alpha^(32-c); the K3 notes bound the decay over such a window so that
- *   the factors stay inside the BF16 range, which alpha >= 0.1 does here).
- *   Other inputs run on the vector-ALU kernels in float32 with tabulated
- *   powers and no range limit.  Always the three-phase segment schedule
- *   (LIGHTNING_ATTN_PREFILL is ignored).
+ *   the factors stay inside the BF16 range).  A head whose smallest alpha is
+ *   below 1/8 (where those factors would pass 2^96) runs its output pass on
+ *   the vector-ALU kernel instead, in float32 with tabulated powers and no
+ *   range limit (slower); so does every head for other inputs.  Always the
+ *   three-phase segment schedule (LIGHTNING_ATTN_PREFILL is ignored).
  */
 size_t lightning_attn_fwd_chdecay_workspace_size(int B, int H, int64_t N, int d, int block,
                                                  la_dtype dt, int64_t segment_tokens);

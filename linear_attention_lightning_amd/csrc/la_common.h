@@ -204,7 +204,25 @@ struct FwdArgs {
   float *snaps;      // prefix-state snapshots [rows][H][d][d] (m.snap_iv > 0), else nullptr
   const int32_t *snap_off;  // [num_seqs + 1]: first snapshot row of each sequence
   const float *chdecay;     // [H][d] per-channel decays (channel-wise variant), else nullptr
+  int ch_split = 0;         // channel-wise output pass: 0 = every head, 1 = only the heads
+                            // whose smallest decay is >= 2^kChMinLog2, 2 = only the others
 };
+
+// The channel-wise MFMA output pass writes the decay inside a 64-token
+// chunk as alpha^(q-32) (queries) times alpha^(32-c) (keys): factors up to
+// alpha^-32, which must stay inside the bf16 range (2^128) with room for the
+// inputs themselves.  Heads whose smallest decay is below 2^kChMinLog2 (the
+// factors would pass 2^96) run their output pass on the vector-ALU kernel,
+// which tabulates the powers and has no such limit.
+constexpr float kChMinLog2 = -3.0f;
+
+// True when the smallest of head h's D channel decays is below
+// 2^kChMinLog2 (the same value in every lane of the workgroup).
+__device__ __forceinline__ bool ch_small_head(const float *alpha_h, int D) {
+  float mn = 1.f;
+  for (int i = 0; i < D; ++i) mn = fminf(mn, alpha_h[i]);
+  return log2f(mn) < kChMinLog2;
+}
 
 // Tokens [*a, *b) of segment s: equal cuts of the token axis, or sequence s
 // itself when seg_len is 0 (then no segment starts inside a sequence).

@@ -16,7 +16,8 @@
 // K (.) alpha^(L-1-c) = K~ (.) alpha^(L-33), one factor per channel.  The
 // pivot in the middle of a 64-token chunk keeps every factor within
 // alpha^(+-32) (the notes bound the window so that the factors stay inside
-// the BF16 range): alpha >= 0.1 keeps them below 10^32.
+// the BF16 range): heads whose smallest alpha is at least 1/8 (factors below
+// 2^96) run here, the others on the vector-ALU kernel (kChMinLog2).
 //
 // Workgroup = (segment, head), 8 waves as in the scalar kernel: output waves
 // 0-3 each own query rows 16w..16w+15 of a chunk; state waves 4-7 own state
@@ -131,6 +132,8 @@ void chdecay_chunk_kernel(FwdArgs p) {
   const int64_t b = (a + p.seg_len < m.total) ? a + p.seg_len : m.total;
   const int64_t DD = (int64_t)D * D;
   const float *alpha = p.chdecay + (int64_t)h * D;
+  // A head with a decay below 2^kChMinLog2 is the vector-ALU kernel's.
+  if (p.ch_split == 1 && ch_small_head(alpha, D)) return;
   Cursor cur = first_chunk<false>(m, a, b, TC);
   if (!cur.valid) return;
   if (ln.tid < D) l2a[ln.tid] = log2f(alpha[ln.tid]);  // read after the first barrier

@@ -53,6 +53,8 @@ __global__ __launch_bounds__(NT) void prefill_chunk_kernel(FwdArgs p) {
   const int s = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
   const float log2lam = CH ? 0.f : log2f(p.decay[h]);
   if constexpr (CH) {
+    // Beside the MFMA output pass: only the heads it leaves out.
+    if (p.ch_split == 2 && !ch_small_head(p.chdecay + (int64_t)h * D, D)) return;
     for (int e = tid; e < T * D; e += NT) {
       const int n = e / D, i = e - (e / D) * D;
       sc.pw[n][i] = pow_lam(log2f(p.chdecay[(int64_t)h * D + i]), (float)n);

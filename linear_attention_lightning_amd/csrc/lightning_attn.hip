@@ -211,7 +211,14 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
         hipLaunchKernelGGL(la::mfma::local_state_kernel<false>, lgrid, dim3(la::mfma::NT_LOCAL), 0,
                            st, a);
     } else if (a.chdecay) {
-      hipLaunchKernelGGL(la::mfma::chdecay_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, a);
+      // Heads whose smallest decay is at least 1/8 on MFMA, the others on
+      // the vector-ALU kernel (same segments, same entering states).
+      la::FwdArgs am = a, av = a;
+      am.ch_split = 1;
+      av.ch_split = 2;
+      hipLaunchKernelGGL(la::mfma::chdecay_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, am);
+      hipLaunchKernelGGL((la::simt::prefill_chunk_kernel<bf16, 128, true>), grid,
+                         dim3(la::simt::NT), 0, st, av);
     } else if (a.m.snap_iv > 0 || a.seg_len == 0 || a.m.rs < 0) {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<true>, grid, dim3(la::mfma::NT), 0, st, a);
     } else {

@@ -90,10 +90,42 @@ def test_chdecay_ragged(N):
     run_ch_case(2, 2, N, 128, "bf16", seed=620 + N, seg=64)
 
 
+def small_alpha(H, d, seed):
+    """Per-channel decays with small values: head 1 has every third channel
+    at 0.05, head 2 every other channel at 0.01, head 3 every channel at 1e-3
+    but channel 0 at 1, head 4 channels from exactly 1/8 (the smallest decay
+    the MFMA output pass takes: its largest factor alpha^-32 is 2^96) to 1,
+    head 5 one channel just below 1/8; heads 0 and 6+ from the schedule."""
+    alpha = inputs.chdecay_schedule(H, d, seed).copy()
+    alpha[1, ::3] = 0.05
+    alpha[2, ::2] = 0.01
+    alpha[3, :] = 1e-3
+    alpha[3, 0] = 1.0
+    alpha[4] = np.linspace(0.125, 1.0, d)
+    alpha[5, 5] = 0.1249
+    return alpha.astype(np.float32)
+
+
+@pytest.mark.parametrize("seg", [0, 256, la.LA_SEGMENT_PER_SEQUENCE])
+def test_chdecay_small_alpha(seg):
+    """Heads whose smallest decay is below 1/8 (0.05, 0.01, 1e-3, 0.1249) run
+    their output pass on the vector-ALU kernel beside the MFMA heads (1/8
+    exactly and the schedule's): every output finite and within the bar, with
+    segment cuts (the local-state pass and the scan take every head) and
+    without."""
+    run_ch_case(1, 7, 1500, 128, "bf16", seed=650, seg=seg, alpha=small_alpha(7, 128, 651))
+
+
+def test_chdecay_small_alpha_varlen():
+    run_ch_varlen_case([300, 0, 1000, 7, 0, 2000, 129], 7, 128, "bf16", seed=660, seg=200,
+                       alpha=small_alpha(7, 128, 661))
+
+
 @pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "fp32")])
 def test_chdecay_range_edges(d, dtype):
-    """Channels at the documented lower bound 0.1 (the largest factors of the
-    MFMA path, alpha^(+-32)), at 1, and in between, across segment cuts."""
+    """Channels at 0.1 (with bf16 and d = 128 below the MFMA pass's 1/8, so
+    that head takes the vector-ALU output pass), at 1, and in between, across
+    segment cuts."""
     H = 2
     alpha = np.empty((H, d), np.float32)
     alpha[0] = np.linspace(0.1, 1.0, d)
@@ -202,7 +234,8 @@ def test_chdecay_empty_sequences_keep_the_state():
     assert torch.equal(fin, init)
 
 
-def run_ch_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True, token_major=False):
+def run_ch_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True, token_major=False,
+                       alpha=None):
     """Packed channel-wise prefill against the oracle's channel-wise
     recurrence run on each sequence on its own."""
     torch = torch_mod()
@@ -211,7 +244,7 @@ def run_ch_varlen_case(lens, H, d, dtype, seed, seg=0, with_init=True, token_maj
     cu = inputs.cu_seqlens(lens)
     total, S = int(cu[-1]), len(lens)
     q, k, v = inputs.host_qkv((H, total, d), seed, dtype=dtype)
-    alpha = inputs.chdecay_schedule(H, d, seed + 1)
+    alpha = inputs.chdecay_schedule(H, d, seed + 1) if alpha is None else alpha
     init = inputs.host_state((S, H, d, d), seed + 2) if with_init else None
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     tq, tk, tv = (torch.from_numpy(x).cuda().to(tdt) for x in (q, k, v))

@@ -48,6 +48,8 @@ def _bind(lib):
     lib.oracle_fwd_varlen_snap_f64.argtypes = [_P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P,
                                                _L, _P, _P, _I]
     lib.oracle_fwd_chdecay_f64.argtypes = [_P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _I]
+    lib.oracle_fwd_gated_f64.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_double, _I, _I, _I, _L,
+                                         _I, _P, _P, _P, _I]
     lib.oracle_bwd_f64.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _L, _I, _P, _P, _P, _P,
                                    _I]
     lib.oracle_decode_f64.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I]
@@ -55,7 +57,7 @@ def _bind(lib):
     lib.oracle_rows_f64.argtypes = [_P, _P, _P, ctypes.c_float, _I, _P, _L, _P, _P, _I]
     lib.oracle_state_entries_f64.argtypes = [_P, _P, ctypes.c_float, _I, _L, _P, _L, _P, _P, _I]
     for f in ("oracle_fwd_f64", "oracle_fwd_varlen_f64", "oracle_fwd_varlen_snap_f64",
-              "oracle_bwd_f64", "oracle_fwd_chdecay_f64",
+              "oracle_bwd_f64", "oracle_fwd_chdecay_f64", "oracle_fwd_gated_f64",
               "oracle_decode_f64",
               "oracle_bruteforce_f64", "oracle_rows_f64", "oracle_state_entries_f64"):
         getattr(lib, f).restype = _I
@@ -141,6 +143,33 @@ def fwd_chdecay(q, k, v, alpha, init=None, want_out=True, nthreads=0, lib=None):
     fin = np.empty((B, H, d, d), np.float64)
     lib.oracle_fwd_chdecay_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), B, H, N, d, _ptr(init),
                                _ptr(out), _ptr(fin), nthreads)
+    return out, fin
+
+
+SILU_Q, SILU_K, SILU_V, NORM, GATE = 1, 2, 4, 8, 16
+
+
+def fwd_gated(q, k, v, decay, flags, gate=None, weight=None, eps=1e-6, init=None, nthreads=0,
+              lib=None):
+    """The normalisation / SiLU / gate reading around the recurrence (see
+    oracle.c): flags from SILU_Q, SILU_K, SILU_V, NORM, GATE; gate [B,H,N,d]
+    (with GATE), weight [H, d] or None.  Returns (out [B,H,N,d], final_state
+    [B,H,d,d])."""
+    lib = lib or load()
+    q, k, v, decay = _f32(q), _f32(k), _f32(v), _f32(decay)
+    B, H, N, d = q.shape
+    if flags & GATE:
+        gate = _f32(gate)
+        assert gate.shape == q.shape
+    else:
+        gate = None
+    weight = None if weight is None else _f32(weight)
+    init = _f64(init)
+    out = np.empty((B, H, N, d), np.float64)
+    fin = np.empty((B, H, d, d), np.float64)
+    lib.oracle_fwd_gated_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(gate), _ptr(weight),
+                             float(eps), int(flags), B, H, N, d, _ptr(init), _ptr(out), _ptr(fin),
+                             nthreads)
     return out, fin
 
 

@@ -13,7 +13,7 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(out=LIB, plant=0, plant_bwd=0, plant_ch=0):
+def build(out=LIB, plant=0, plant_bwd=0, plant_ch=0, plant_gated=0):
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
            "-fno-fast-math", "-Wall", "-Wextra", "-o", out + ".tmp", SRC, "-lm"]
     if plant:
@@ -22,6 +22,8 @@ def build(out=LIB, plant=0, plant_bwd=0, plant_ch=0):
         cmd.insert(1, "-DORACLE_PLANT_BWD=%d" % int(plant_bwd))
     if plant_ch:
         cmd.insert(1, "-DORACLE_PLANT_CH=%d" % int(plant_ch))
+    if plant_gated:
+        cmd.insert(1, "-DORACLE_PLANT_GATED=%d" % int(plant_gated))
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out

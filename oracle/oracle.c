@@ -593,3 +593,130 @@ int oracle_state_entries_f64(const float *k, const float *v, float decay, int d,
   ent_ctx c = {k, v, (double)decay, d, N, ij, init, out};
   return run_units(ent_unit, &c, n, nthreads);
 }
+
+/* ------------------------------------------ normalisation, SiLU and gate */
+
+/*
+ * The MiniMax-01 report (section 2.2.1, before the lightning-attention
+ * derivation) names normalisation, a SiLU activation and a gating mechanism
+ * around the attention of its TransNormer blocks and leaves them out of the
+ * derivation; the pages give no formula for any of them.  The reading
+ * computed here (each part selected by a bit of `flags`):
+ *
+ *   bit 0, 1, 2  q', k', v' = SiLU(q), SiLU(k), SiLU(v), SiLU(x) = x / (1 + e^-x),
+ *                elementwise on the inputs (else the inputs themselves);
+ *   o_t          the decayed recurrence above over q', k', v';
+ *   bit 3        o_t <- o_t / sqrt(mean_j o_t[j]^2 + eps) * w[h][j]: RMS
+ *                normalisation over each head's d channels with a
+ *                per-channel weight w [H][d] (NULL = all ones);
+ *   bit 4        o_t <- o_t * sigmoid(g_t), sigmoid(x) = 1 / (1 + e^-x), with
+ *                g [B][H][N][d] the gate input (an output gate).
+ *
+ * The final state is the recurrence's over q', k', v'.  Layout as
+ * oracle_fwd_f64.
+ */
+#ifndef ORACLE_PLANT_GATED
+#define ORACLE_PLANT_GATED 0 /* 1 = norm over tokens, not channels; 2 = gate without the
+                                sigmoid; 3 = SiLU as x / (1 + e^x) (planted mistakes) */
+#endif
+
+#define ORACLE_SILU_Q 1
+#define ORACLE_SILU_K 2
+#define ORACLE_SILU_V 4
+#define ORACLE_NORM 8
+#define ORACLE_GATE 16
+
+static double silu(double x) {
+  return ORACLE_PLANT_GATED == 3 ? x / (1.0 + exp(x)) : x / (1.0 + exp(-x));
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+typedef struct {
+  const float *q, *k, *v, *decay, *gate, *weight;
+  double eps;
+  int flags, H, d;
+  int64_t N;
+  const double *init;
+  double *out, *fin;
+} gated_ctx;
+
+static void gated_unit(void *vctx, int64_t u) {
+  gated_ctx *c = (gated_ctx *)vctx;
+  int d = c->d, h = (int)(u % c->H);
+  int64_t N = c->N, dd = (int64_t)d * d, base = u * N * d;
+  double lam = (double)c->decay[h];
+  double *S = (double *)malloc(sizeof(double) * (size_t)dd);
+  double *qa = (double *)malloc(sizeof(double) * (size_t)d);
+  double *ka = (double *)malloc(sizeof(double) * (size_t)d);
+  double *va = (double *)malloc(sizeof(double) * (size_t)d);
+  if (c->init) memcpy(S, c->init + u * dd, sizeof(double) * (size_t)dd);
+  else memset(S, 0, sizeof(double) * (size_t)dd);
+  for (int64_t t = 0; t < N; ++t) {
+    const float *qt = c->q + base + t * d, *kt = c->k + base + t * d, *vt = c->v + base + t * d;
+    for (int i = 0; i < d; ++i) {
+      qa[i] = (c->flags & ORACLE_SILU_Q) ? silu((double)qt[i]) : (double)qt[i];
+      ka[i] = (c->flags & ORACLE_SILU_K) ? silu((double)kt[i]) : (double)kt[i];
+      va[i] = (c->flags & ORACLE_SILU_V) ? silu((double)vt[i]) : (double)vt[i];
+    }
+    /* S_t = lambda S_{t-1} + k'_t^T v'_t */
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) S[(int64_t)i * d + j] = lam * S[(int64_t)i * d + j] + ka[i] * va[j];
+    if (!c->out) continue;
+    /* o_t = q'_t S_t */
+    double *o = c->out + base + t * d;
+    for (int j = 0; j < d; ++j) o[j] = 0.0;
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) o[j] += qa[i] * S[(int64_t)i * d + j];
+  }
+  if (c->out && (c->flags & ORACLE_NORM)) {
+    /* RMS over each row's d channels (the planted mistake: over each channel's
+     * N tokens), all of them taken before any row is rescaled. */
+    double *rms = (double *)malloc(sizeof(double) * (size_t)(ORACLE_PLANT_GATED == 1 ? d : N));
+    if (ORACLE_PLANT_GATED == 1) {
+      for (int j = 0; j < d; ++j) {
+        double ms = 0.0;
+        for (int64_t s = 0; s < N; ++s) ms += c->out[base + s * d + j] * c->out[base + s * d + j];
+        rms[j] = sqrt(ms / (double)N + c->eps);
+      }
+    } else {
+      for (int64_t t = 0; t < N; ++t) {
+        const double *o = c->out + base + t * d;
+        double ms = 0.0;
+        for (int j = 0; j < d; ++j) ms += o[j] * o[j];
+        rms[t] = sqrt(ms / (double)d + c->eps);
+      }
+    }
+    for (int64_t t = 0; t < N; ++t) {
+      double *o = c->out + base + t * d;
+      for (int j = 0; j < d; ++j) {
+        double w = c->weight ? (double)c->weight[(int64_t)h * d + j] : 1.0;
+        o[j] = o[j] / rms[ORACLE_PLANT_GATED == 1 ? j : t] * w;
+      }
+    }
+    free(rms);
+  }
+  if (c->out && (c->flags & ORACLE_GATE)) {
+    for (int64_t t = 0; t < N; ++t) {
+      double *o = c->out + base + t * d;
+      const float *g = c->gate + base + t * d;
+      for (int j = 0; j < d; ++j)
+        o[j] *= ORACLE_PLANT_GATED == 2 ? (double)g[j] : sigmoid((double)g[j]);
+    }
+  }
+  if (c->fin) memcpy(c->fin + u * dd, S, sizeof(double) * (size_t)dd);
+  free(va);
+  free(ka);
+  free(qa);
+  free(S);
+}
+
+/* The gated reading over [B][H][N][d]; gate [B][H][N][d] (needed with bit
+ * 4), weight [H][d] or NULL, eps >= 0.  Returns the number of threads used. */
+int oracle_fwd_gated_f64(const float *q, const float *k, const float *v, const float *decay,
+                         const float *gate, const float *weight, double eps, int flags, int B,
+                         int H, int64_t N, int d, const double *init, double *out, double *fin,
+                         int nthreads) {
+  gated_ctx c = {q, k, v, decay, gate, weight, eps, flags, H, d, N, init, out, fin};
+  return run_units(gated_unit, &c, (int64_t)B * H, nthreads);
+}

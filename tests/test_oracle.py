@@ -534,3 +534,70 @@ def test_planted_mistakes_are_caught():
             path = oracle_build.build(out=os.path.join(tmp, "lib%d.so" % plant), plant=plant)
             lib = oracle.load(path)
             assert not _pins_pass(lib), "planted mistake %d not caught" % plant
+
+
+# ----------------------------------- normalisation, SiLU and gate (reading)
+# MiniMax-01 report, section 2.2.1: normalisation, SiLU activation and a gate
+# surround the attention and are left out of the derivation; oracle.c states
+# the reading.  Pins from the mathematics of each part, not from its formula.
+
+def _gated_case(seed, B=1, H=2, N=40, d=6):
+    q, k, v = inputs.host_qkv((B, H, N, d), seed, dtype="fp32")
+    g, _, _ = inputs.host_qkv((B, H, N, d), seed + 1, dtype="fp32")
+    lam = np.asarray([0.9, 0.6][:H], np.float32)
+    return q * 4, k * 4, v * 4, g * 8, lam
+
+
+def _gated_pins_pass(lib):
+    ok = True
+    q, k, v, g, lam = _gated_case(900)
+    B, H, N, d = q.shape
+    plain, pfin, _ = oracle.fwd(q, k, v, lam, lib=lib)
+    # no part selected: the plain recurrence
+    o0, f0 = oracle.fwd_gated(q, k, v, lam, 0, lib=lib)
+    ok &= np.array_equal(o0, plain) and np.array_equal(f0, pfin)
+    # SiLU(x) - SiLU(-x) = x (x (s(x) + s(-x)) = x), and the output is linear
+    # in each of q, k and v on its own: the difference of the outputs for x
+    # and -x is the plain output
+    for flag, sel in ((oracle.SILU_Q, 0), (oracle.SILU_K, 1), (oracle.SILU_V, 2)):
+        a = [q, k, v]
+        b = [q, k, v]
+        b[sel] = -b[sel]
+        oa, _ = oracle.fwd_gated(*a, lam, flag, lib=lib)
+        ob, _ = oracle.fwd_gated(*b, lam, flag, lib=lib)
+        ok &= rel_err(oa - ob, plain) < 1e-12
+    # SiLU(0) = 0 and SiLU(x) -> x for large x
+    oz, _ = oracle.fwd_gated(np.zeros_like(q), k, v, lam, oracle.SILU_Q, lib=lib)
+    ok &= np.abs(oz).max() == 0.0
+    ol, _ = oracle.fwd_gated(q * 0 + 40.0, k, v, lam, oracle.SILU_Q, lib=lib)
+    pl, _, _ = oracle.fwd(q * 0 + 40.0, k, v, lam, lib=lib)
+    ok &= rel_err(ol, pl) < 1e-12
+    # RMS normalisation over each row's channels: every row has mean square 1
+    # (weight 1, eps 0), and scaling v (the output is linear in it) changes
+    # nothing
+    on, _ = oracle.fwd_gated(q, k, v, lam, oracle.NORM, eps=0.0, lib=lib)
+    ok &= np.abs((on ** 2).mean(axis=-1) - 1.0).max() < 1e-12
+    os_, _ = oracle.fwd_gated(q, k, v * 8.0, lam, oracle.NORM, eps=0.0, lib=lib)
+    ok &= rel_err(os_, on) < 1e-12
+    # the weight multiplies each channel
+    w = (np.arange(H * d, dtype=np.float32).reshape(H, d) / 7.0 - 1.0).astype(np.float32)
+    ow, _ = oracle.fwd_gated(q, k, v, lam, oracle.NORM, weight=w, eps=0.0, lib=lib)
+    ok &= rel_err(ow, on * w[None, :, None, :]) < 1e-12
+    # gate: sigmoid(g) + sigmoid(-g) = 1, and sigmoid(0) = 1/2
+    og, _ = oracle.fwd_gated(q, k, v, lam, oracle.GATE, gate=g, lib=lib)
+    om, _ = oracle.fwd_gated(q, k, v, lam, oracle.GATE, gate=-g, lib=lib)
+    ok &= rel_err(og + om, plain) < 1e-12
+    oh, _ = oracle.fwd_gated(q, k, v, lam, oracle.GATE, gate=np.zeros_like(g), lib=lib)
+    ok &= rel_err(oh, plain / 2) < 1e-12
+    return bool(ok)
+
+
+def test_gated_pins():
+    assert _gated_pins_pass(oracle.load())
+
+
+def test_gated_planted_mistakes_are_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        for plant in (1, 2, 3):
+            path = oracle_build.build(out=os.path.join(tmp, "libg%d.so" % plant), plant_gated=plant)
+            assert not _gated_pins_pass(oracle.load(path)), "planted gated mistake %d" % plant

@@ -120,9 +120,15 @@ const char *lightning_attn_last_hip_error(void);
  *   block        : block (chunk) length of the blockwise form, one of
  *                  16, 32, 64, 128, 256.  Any block length gives the same
  *                  result up to rounding (K3 notes, CP for linear
- *                  attention); the kernels run 128-token chunks for bf16 and
- *                  32-token chunks for float32, so `block` is validated and
- *                  otherwise does not change the arithmetic.
+ *                  attention).  It chooses the kernel the way the MiniMax-01
+ *                  report's multi-level padding (section 3.3.3) chooses a
+ *                  block by input length: for bf16 with d = 128, 128 and 256
+ *                  run 128-token chunks (one workgroup per CU), 64 runs
+ *                  64-token and 16 or 32 run 32-token chunks (two workgroups
+ *                  per CU, the choice for short inputs: decode-like and
+ *                  prefix-continuation batches).  float32 inputs and d = 64
+ *                  run 32-token chunks for every block.  The workspace size
+ *                  query takes the same block.
  *   init_state   : [B][H][d][d] float32, or NULL for a zero initial state.
  *   final_state  : [B][H][d][d] float32 state after token N-1 (equal to the
  *                  initial state when N == 0), or NULL if not wanted.
@@ -313,6 +319,73 @@ la_status lightning_attn_fwd_varlen_snapshots(
     const float *init_states, void *out, float *final_states, int64_t snapshot_interval,
     const int32_t *snapshot_offsets, float *snapshots, int64_t segment_tokens, void *workspace,
     size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Prefill with the normalisation, SiLU activation and gate that the
+ * MiniMax-01 report places around the attention of its TransNormer blocks
+ * and leaves out of its derivation (section 2.2.1; it gives no formula).
+ * The reading computed here, each part selected by a bit of `flags`:
+ *
+ *   LA_SILU_Q, LA_SILU_K, LA_SILU_V : q, k, v replaced by SiLU(x) =
+ *        x / (1 + e^-x), elementwise, as they are read (the recurrence and
+ *        the final state use the activated values);
+ *   LA_NORM : every output row divided by its RMS over the head's d
+ *        channels, sqrt(mean_j o[j]^2 + eps), then multiplied by
+ *        norm_weight[h][j] (NULL: ones);
+ *   LA_GATE : every output element multiplied by sigmoid(gate) =
+ *        1 / (1 + e^-gate), gate laid out like out (an output gate computed
+ *        by the caller, e.g. a projection of the layer input).
+ *
+ * Fused into the prefill: the activations are applied to the tiles as they
+ * are loaded, the normalisation to the float32 accumulators of each output
+ * row, weight and gate to the row as it is stored; nothing else reads or
+ * writes out.  With flags == 0 this is lightning_attn_fwd_layout with
+ * block 64.
+ *
+ *   flags        : any combination of LA_SILU_Q, LA_SILU_K, LA_SILU_V,
+ *                  LA_NORM, LA_GATE (other bits: LA_ERR_INVALID_ARG).
+ *   gate         : like out (q's layout and dtype); needed with LA_GATE,
+ *                  else may be NULL.
+ *   norm_weight  : [H][d] float32 or NULL; used with LA_NORM.
+ *   eps          : >= 0 and finite; used with LA_NORM.
+ *   Other arguments as for lightning_attn_fwd_layout, without `block`: the
+ *   path runs 64-token chunks (a row's d channels then sit in one wave);
+ *   workspace from lightning_attn_fwd_gated_workspace_size (that of
+ *   lightning_attn_fwd_workspace_size with block 64).  bf16 with d = 128 only
+ *   (otherwise LA_ERR_UNSUPPORTED).
+ */
+enum { LA_SILU_Q = 1, LA_SILU_K = 2, LA_SILU_V = 4, LA_NORM = 8, LA_GATE = 16 };
+
+size_t lightning_attn_fwd_gated_workspace_size(int B, int H, int64_t N, int d, la_dtype dt,
+                                               int64_t segment_tokens);
+
+la_status lightning_attn_fwd_gated(const void *q, const void *k, const void *v,
+                                   const float *decay, int B, int H, int64_t N, int d,
+                                   la_dtype dt, la_layout layout, int flags, const void *gate,
+                                   const float *norm_weight, float eps,
+                                   const float *init_state, void *out, float *final_state,
+                                   int64_t segment_tokens, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream);
+
+/*
+ * lightning_attn_fwd_gated over packed variable-length sequences: the
+ * arguments of lightning_attn_fwd_varlen_layout (without `block`) and the
+ * gated ones above; gate laid out like out ([H][total_N][d] or
+ * [total_N][H][d]); workspace from
+ * lightning_attn_fwd_varlen_gated_workspace_size.
+ */
+size_t lightning_attn_fwd_varlen_gated_workspace_size(int num_seqs, int H, int64_t total_N, int d,
+                                                      la_dtype dt, int64_t segment_tokens);
+
+la_status lightning_attn_fwd_varlen_gated(const void *q, const void *k, const void *v,
+                                          const float *decay, const int32_t *cu_seqlens,
+                                          int num_seqs, int H, int64_t total_N, int d,
+                                          la_dtype dt, la_layout layout, int flags,
+                                          const void *gate, const float *norm_weight, float eps,
+                                          const float *init_states, void *out,
+                                          float *final_states, int64_t segment_tokens,
+                                          void *workspace, size_t workspace_bytes,
+                                          void *hip_stream);
 
 /*
  * One recurrent decode step (MiniMax-01 report, section 2.2.4, eq. 12;

@@ -11,6 +11,9 @@ Entry points (same names as the C ABI):
   lightning_attn_fwd(q, k, v, decay, block=128, init_state=None, ...) -> (out, final_state)
   lightning_attn_fwd_timed(q, k, v, decay, phase_events, ...) -> (out, final_state)
   lightning_attn_fwd_noalloc(q, k, v, decay, ...) -> (out, final_state)   (no workspace)
+  lightning_attn_fwd_gated(q, k, v, decay, flags, gate=None, norm_weight=None, eps=1e-6, ...)
+      -> (out, final_state)   (SiLU on q/k/v, per-head RMS norm, sigmoid gate; LA_* flags)
+  lightning_attn_fwd_varlen_gated(q, k, v, decay, cu_seqlens, flags, ...) -> (out, final_states)
   lightning_attn_fwd_layout(q, k, v, decay, layout, ...) -> (out, final_state)
   lightning_attn_fwd_varlen_layout(q, k, v, decay, cu_seqlens, layout, ...) -> (out, final_states)
   lightning_attn_fwd_varlen(q, k, v, decay, cu_seqlens, block=128, ...) -> (out, final_states)
@@ -36,6 +39,10 @@ import os
 
 __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd_layout",
            "lightning_attn_fwd_noalloc", "lightning_attn_noalloc_scratch_bytes",
+           "lightning_attn_fwd_gated", "lightning_attn_fwd_varlen_gated",
+           "lightning_attn_fwd_gated_workspace_size",
+           "lightning_attn_fwd_varlen_gated_workspace_size",
+           "LA_SILU_Q", "LA_SILU_K", "LA_SILU_V", "LA_NORM", "LA_GATE",
            "lightning_attn_fwd_varlen", "lightning_attn_fwd_varlen_layout",
            "lightning_attn_fwd_varlen_snapshots", "snapshot_row_offsets", "lightning_attn_decode",
            "lightning_attn_mixed_step", "lightning_attn_bwd", "lightning_attn_bwd_workspace_size",
@@ -55,6 +62,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightnin
 LA_FP32, LA_BF16 = 0, 1
 LA_HEAD_MAJOR, LA_TOKEN_MAJOR = 0, 1  # la_layout
 LA_SEGMENT_PER_SEQUENCE = -1          # segment_tokens: one segment per sequence
+LA_SILU_Q, LA_SILU_K, LA_SILU_V, LA_NORM, LA_GATE = 1, 2, 4, 8, 16  # gated-path flags
 _STATUS = {0: "LA_OK", 1: "LA_ERR_INVALID_ARG", 2: "LA_ERR_UNSUPPORTED", 3: "LA_ERR_WORKSPACE",
            4: "LA_ERR_HIP"}
 
@@ -101,6 +109,16 @@ def load_library(path=None):
     lib.lightning_attn_fwd_timed.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P, Z, P,
                                              ctypes.POINTER(P)]
     lib.lightning_attn_fwd_timed.restype = I
+    lib.lightning_attn_fwd_gated_workspace_size.argtypes = [I, I, L, I, I, L]
+    lib.lightning_attn_fwd_gated_workspace_size.restype = Z
+    lib.lightning_attn_fwd_gated.argtypes = [P, P, P, P, I, I, L, I, I, I, I, P, P,
+                                             ctypes.c_float, P, P, P, L, P, Z, P]
+    lib.lightning_attn_fwd_gated.restype = I
+    lib.lightning_attn_fwd_varlen_gated_workspace_size.argtypes = [I, I, L, I, I, L]
+    lib.lightning_attn_fwd_varlen_gated_workspace_size.restype = Z
+    lib.lightning_attn_fwd_varlen_gated.argtypes = [P, P, P, P, P, I, I, L, I, I, I, I, P, P,
+                                                    ctypes.c_float, P, P, P, L, P, Z, P]
+    lib.lightning_attn_fwd_varlen_gated.restype = I
     lib.lightning_attn_noalloc_scratch_bytes.argtypes = []
     lib.lightning_attn_noalloc_scratch_bytes.restype = Z
     lib.lightning_attn_fwd_noalloc.argtypes = [P, P, P, P, I, I, L, I, I, I, P, P, P, L, P]
@@ -227,6 +245,113 @@ def lightning_attn_fwd_layout(q, k, v, decay, layout, block=128, init_state=None
     [B, H, d, d] float32 either way."""
     return _fwd(q, k, v, decay, block, init_state, segment_tokens, out, final_state, workspace,
                 None, layout)
+
+
+def lightning_attn_fwd_gated_workspace_size(B, H, N, d, dtype=LA_BF16, segment_tokens=0):
+    return load_library().lightning_attn_fwd_gated_workspace_size(B, H, N, d, dtype,
+                                                                   segment_tokens)
+
+
+def lightning_attn_fwd_varlen_gated_workspace_size(num_seqs, H, total, d, dtype=LA_BF16,
+                                                   segment_tokens=0):
+    return load_library().lightning_attn_fwd_varlen_gated_workspace_size(num_seqs, H, total, d,
+                                                                          dtype, segment_tokens)
+
+
+def _gated_extras(q, flags, gate, norm_weight, H, d, dev):
+    torch = _torch()
+    if flags & LA_GATE:
+        if gate is None:
+            raise ValueError("LA_GATE needs a gate tensor")
+        _check(gate, "gate", q.shape, q.dtype, dev)
+    if norm_weight is not None:
+        _check(norm_weight, "norm_weight", (H, d), torch.float32, dev)
+
+
+def lightning_attn_fwd_gated(q, k, v, decay, flags, gate=None, norm_weight=None, eps=1e-6,
+                             layout=LA_HEAD_MAJOR, init_state=None, segment_tokens=0, out=None,
+                             final_state=None, workspace=None):
+    """Prefill with the SiLU / normalisation / gate reading around the
+    attention (see the C header): flags from LA_SILU_Q, LA_SILU_K, LA_SILU_V,
+    LA_NORM, LA_GATE; gate like q (with LA_GATE); norm_weight [H, d] float32
+    or None.  q, k, v [B, H, N, d] (LA_HEAD_MAJOR) or [B, N, H, d]
+    (LA_TOKEN_MAJOR), bf16, d = 128.  Returns (out, final_state)."""
+    torch = _torch()
+    lib = load_library()
+    if layout == LA_TOKEN_MAJOR:
+        B, N, H, d = q.shape
+    else:
+        B, H, N, d = q.shape
+    dev = q.device
+    _check(k, "k", q.shape, q.dtype, dev)
+    _check(v, "v", q.shape, q.dtype, dev)
+    _check(q, "q", q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    _gated_extras(q, flags, gate, norm_weight, H, d, dev)
+    if init_state is not None:
+        _check(init_state, "init_state", (B, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", (B, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    ws_bytes = lib.lightning_attn_fwd_gated_workspace_size(B, H, N, d, dt, segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), B, H, N, d, dt,
+                                      layout, int(flags), _ptr(gate), _ptr(norm_weight),
+                                      float(eps), _ptr(init_state), _ptr(out), _ptr(final_state),
+                                      segment_tokens, _ptr(workspace), ws_have, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd_gated")
+    return out, final_state
+
+
+def lightning_attn_fwd_varlen_gated(q, k, v, decay, cu_seqlens, flags, gate=None,
+                                    norm_weight=None, eps=1e-6, layout=LA_HEAD_MAJOR,
+                                    init_states=None, segment_tokens=0, out=None,
+                                    final_states=None, workspace=None):
+    """Packed form of lightning_attn_fwd_gated: q, k, v [H, total, d]
+    (LA_HEAD_MAJOR) or [total, H, d] (LA_TOKEN_MAJOR); gate like q.  Returns
+    (out, final_states [num_seqs, H, d, d])."""
+    torch = _torch()
+    lib = load_library()
+    if layout == LA_TOKEN_MAJOR:
+        total, H, d = q.shape
+    else:
+        H, total, d = q.shape
+    dev = q.device
+    _check(k, "k", q.shape, q.dtype, dev)
+    _check(v, "v", q.shape, q.dtype, dev)
+    _check(q, "q", q.shape, q.dtype, dev)
+    _check(decay, "decay", (H,), torch.float32, dev)
+    _gated_extras(q, flags, gate, norm_weight, H, d, dev)
+    S = cu_seqlens.numel() - 1
+    _check(cu_seqlens, "cu_seqlens", (S + 1,), torch.int32, dev)
+    if init_states is not None:
+        _check(init_states, "init_states", (S, H, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.shape, q.dtype, dev)
+    if final_states is None:
+        final_states = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    _check(final_states, "final_states", (S, H, d, d), torch.float32, dev)
+    dt = _dtype_code(q)
+    ws_bytes = lib.lightning_attn_fwd_varlen_gated_workspace_size(S, H, total, d, dt,
+                                                                  segment_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lightning_attn_fwd_varlen_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(cu_seqlens), S, H, total, d, dt, layout,
+        int(flags), _ptr(gate), _ptr(norm_weight), float(eps), _ptr(init_states), _ptr(out),
+        _ptr(final_states), segment_tokens, _ptr(workspace), ws_have, _stream(dev))
+    if st != 0:
+        raise LightningAttnError(st, "lightning_attn_fwd_varlen_gated")
+    return out, final_states
 
 
 def lightning_attn_noalloc_scratch_bytes():

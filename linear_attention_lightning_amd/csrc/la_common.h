@@ -206,6 +206,10 @@ struct FwdArgs {
   const float *chdecay;     // [H][d] per-channel decays (channel-wise variant), else nullptr
   int ch_split = 0;         // channel-wise output pass: 0 = every head, 1 = only the heads
                             // whose smallest decay is >= 2^kChMinLog2, 2 = only the others
+  int flags = 0;            // gated path: SiLU on q / k / v, normalisation, gate (GF_*)
+  const void *gate = nullptr;      // gate input, laid out like out (GF_GATE)
+  const float *norm_w = nullptr;   // [H][d] normalisation weight, or nullptr (ones)
+  float eps = 0.f;                 // normalisation epsilon
 };
 
 // The channel-wise MFMA output pass writes the decay inside a 64-token

@@ -137,6 +137,24 @@ __device__ __forceinline__ bf16x8 cvt8(const float (&v)[8]) {
   return r;
 }
 
+// FwdArgs::flags of the gated path (normalisation, SiLU and gate around the
+// attention; see la_prefill_short.h).
+enum : int { GF_SILU_Q = 1, GF_SILU_K = 2, GF_SILU_V = 4, GF_NORM = 8, GF_GATE = 16 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// x / (1 + e^-x) for each of 8 bf16 values, in float32, rounded to bf16.
+__device__ __forceinline__ u32x4 silu8(u32x4 x) {
+  const bf16x8 v = __builtin_bit_cast(bf16x8, x);
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float f = (float)v[e];
+    r[e] = f * __builtin_amdgcn_rcpf(1.f + fast_exp2(-f * kLog2e));
+  }
+  return __builtin_bit_cast(u32x4, cvt8(r));
+}
+
 // Global -> registers: a 128 x 128 bf16 tile whose row i starts at
 // src + i * rs, of which rows [0, L) are valid (L >= 1), moved by `nthr`
 // threads (thread t of them moves 16 bytes of row (it * nthr + t) / 16).  Rows >= L repeat row L - 1: every
@@ -1010,7 +1028,9 @@ void prefill_fused_kernel(FusedArgs fa) {
 // CH: channel-wise decay (p.chdecay): row c's K values are scaled by their
 // channel's alpha_i^(x1-1-c) on the way into LDS and the update runs with
 // unit weights; chunks are skipped with the slowest channel's decay.
-template <bool CH = false>
+// SILU: the gated path's SiLU on K and V (p.flags) is applied as they are
+// staged.
+template <bool CH = false, bool SILU = false>
 __global__ __launch_bounds__(NT_LOCAL) __attribute__((amdgpu_waves_per_eu(2, 4)))
 void local_state_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C_LOCAL * KV_ROW];
@@ -1086,6 +1106,14 @@ void local_state_kernel(FwdArgs p) {
         for (int e = 0; e < 8; ++e) ks[e] = (float)kv[e] * fast_exp2(n * l2f[e]);
         pk[sl][it] = __builtin_bit_cast(u32x4, cvt8(ks));
       }
+    }
+    if constexpr (SILU) {
+      if (p.flags & GF_SILU_K)
+#pragma unroll
+        for (int it = 0; it < PER; ++it) pk[sl][it] = silu8(pk[sl][it]);
+      if (p.flags & GF_SILU_V)
+#pragma unroll
+        for (int it = 0; it < PER; ++it) pv[sl][it] = silu8(pv[sl][it]);
     }
     store_tile<NT_LOCAL, C_LOCAL>(Ks, pk[sl], tid);
     store_tile<NT_LOCAL, C_LOCAL>(Vs, pv[sl], tid);

@@ -12,6 +12,7 @@
 
 #include "la_common.h"
 #include "la_prefill_mfma.h"
+#include "la_prefill_short.h"
 #include "la_prefill_chdecay.h"
 #include "la_prefill_simt.h"
 #include "la_scan_decode.h"
@@ -44,7 +45,22 @@ struct Plan {
   bool fused;    // single-pass kernel hands states on itself (else 3 phases)
   int r_split;   // pieces per segment of the local-state pass
   size_t ws_bytes;
+  int chunk;     // tokens per chunk of the output pass (bf16 MFMA: 128, or 64 / 32
+                 // on the short-chunk kernel)
 };
+
+// Chunk of the output pass.  bf16 with d = 128 walks 128-token chunks on
+// the MFMA kernel that takes a whole CU per workgroup; a forward prefill
+// (short_ok) whose block is at most 64 tokens walks 64- or 32-token chunks
+// on the short-chunk kernel instead, two workgroups per CU (the MiniMax-01
+// report's multi-level padding to 32/64/128/256 tokens by input length,
+// section 3.3.3, with the block length as the level: short inputs do not pay
+// for a long block).  The backward, prefix snapshots and the channel-wise
+// variant keep their own chunks.
+int out_chunk(int d, la_dtype dt, bool ch, int block, bool short_ok) {
+  if (short_ok && !ch && use_mfma(d, dt) && block <= 64) return block <= 32 ? 32 : 64;
+  return chunk_tokens(d, dt, ch);
+}
 
 size_t state_bytes(int64_t count, int d) { return (size_t)count * (size_t)d * (size_t)d * 4; }
 
@@ -81,8 +97,8 @@ constexpr int64_t kFusedSeg = 8192;
 // one workgroup per CU, and a single round over the 256 CUs with long
 // segments measured fastest (fewer, longer pipelines and less local-state
 // work); the vector-ALU kernels run several small workgroups per CU.
-int64_t target_groups(int d, la_dtype dt, bool ch = false) {
-  return use_mfma(d, dt, ch) ? 256 : 512;
+int64_t target_groups(int d, la_dtype dt, bool ch = false, int chunk = 128) {
+  return use_mfma(d, dt, ch) && chunk == la::mfma::T ? 256 : 512;
 }
 
 // Pieces per segment of the MFMA local-state pass (for a head whose whole
@@ -111,21 +127,22 @@ size_t phased_ws_bytes(const Plan &p, int H, int d) {
 constexpr int64_t kSegPerSeq = -1;
 
 Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tokens,
-                bool allow_fused = true, bool ch = false) {
+                bool allow_fused = true, bool ch = false, int block = 128,
+                bool short_ok = false) {
   if (segment_tokens == kSegPerSeq) segment_tokens = N;  // N == 0: automatic (nothing to cut)
-  Plan p{N, B, false, false, 1, 0};
+  const int T = out_chunk(d, dt, ch, block, short_ok);
+  Plan p{N, B, false, false, 1, 0, T};
   const int64_t total = (int64_t)B * N;
   if (total == 0) {
     p.nseg = 0;
     return p;
   }
-  const int T = chunk_tokens(d, dt, ch);
   int64_t seg = N;
   if (segment_tokens > 0) {
     seg = segment_tokens;
   } else {
     const int64_t bh = (int64_t)B * H;
-    int64_t G = ceil_div(target_groups(d, dt, ch), bh);
+    int64_t G = ceil_div(target_groups(d, dt, ch, T), bh);
     const int64_t maxG = ceil_div(N, T);
     if (G > maxG) G = maxG;
     if (G > 1) {
@@ -133,7 +150,7 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
       if (seg >= N) seg = N;
     }
   }
-  const bool fused = allow_fused && want_fused(H, d, dt, ch);
+  const bool fused = allow_fused && T == la::mfma::T && want_fused(H, d, dt, ch);
   if (fused && segment_tokens <= 0 && seg != N && seg > kFusedSeg) seg = kFusedSeg;
   p.seg = seg;
   p.scan = (seg != N);
@@ -150,15 +167,16 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
 // workspace, and the output pass alone is launched (it also gives empty
 // sequences their final state).
 Plan plan_varlen(int num_seqs, int H, int64_t total, int d, la_dtype dt,
-                 int64_t segment_tokens, bool allow_fused = true, bool ch = false) {
-  if (segment_tokens == kSegPerSeq) return Plan{0, num_seqs, false, false, 1, 0};
-  Plan p{1, 0, true, false, 1, 0};
+                 int64_t segment_tokens, bool allow_fused = true, bool ch = false,
+                 int block = 128, bool short_ok = false) {
+  const int T = out_chunk(d, dt, ch, block, short_ok);
+  if (segment_tokens == kSegPerSeq) return Plan{0, num_seqs, false, false, 1, 0, T};
+  Plan p{1, 0, true, false, 1, 0, T};
   if (total == 0) return p;
-  const int T = chunk_tokens(d, dt, ch);
-  const bool fused = allow_fused && want_fused(H, d, dt, ch);
+  const bool fused = allow_fused && T == la::mfma::T && want_fused(H, d, dt, ch);
   int64_t seg = segment_tokens;
   if (seg <= 0) {
-    const int64_t G = ceil_div(target_groups(d, dt, ch), H);
+    const int64_t G = ceil_div(target_groups(d, dt, ch, T), H);
     seg = ceil_div(ceil_div(total, G), T) * T;
     if (fused && seg > kFusedSeg) seg = kFusedSeg;
   }
@@ -204,12 +222,28 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
     if (phase_a) {
       // The last segment hands no state on: its local state is never needed.
       const dim3 lgrid((unsigned)((pl.nseg - 1) * a.r_split * a.m.H));
+      const bool silu_kv = (a.flags & (la::mfma::GF_SILU_K | la::mfma::GF_SILU_V)) != 0;
       if (pl.nseg > 1 && a.chdecay)
-        hipLaunchKernelGGL(la::mfma::local_state_kernel<true>, lgrid, dim3(la::mfma::NT_LOCAL), 0,
-                           st, a);
+        hipLaunchKernelGGL((la::mfma::local_state_kernel<true, false>), lgrid,
+                           dim3(la::mfma::NT_LOCAL), 0, st, a);
+      else if (pl.nseg > 1 && silu_kv)
+        hipLaunchKernelGGL((la::mfma::local_state_kernel<false, true>), lgrid,
+                           dim3(la::mfma::NT_LOCAL), 0, st, a);
       else if (pl.nseg > 1)
-        hipLaunchKernelGGL(la::mfma::local_state_kernel<false>, lgrid, dim3(la::mfma::NT_LOCAL), 0,
-                           st, a);
+        hipLaunchKernelGGL((la::mfma::local_state_kernel<false, false>), lgrid,
+                           dim3(la::mfma::NT_LOCAL), 0, st, a);
+    } else if (pl.chunk < la::mfma::T && !a.chdecay) {
+      // Short chunks (and the gated path): two 4-wave workgroups per CU.
+      const bool epi = (a.flags & (la::mfma::GF_NORM | la::mfma::GF_GATE)) != 0;
+      if (pl.chunk == 32)
+        hipLaunchKernelGGL((la::mfma::prefill_short_kernel<32, false>), grid,
+                           dim3(la::mfma::NT_S), 0, st, a);
+      else if (epi)
+        hipLaunchKernelGGL((la::mfma::prefill_short_kernel<64, true>), grid,
+                           dim3(la::mfma::NT_S), 0, st, a);
+      else
+        hipLaunchKernelGGL((la::mfma::prefill_short_kernel<64, false>), grid,
+                           dim3(la::mfma::NT_S), 0, st, a);
     } else if (a.chdecay) {
       // Heads whose smallest decay is at least 1/8 on MFMA, the others on
       // the vector-ALU kernel (same segments, same entering states).
@@ -403,11 +437,36 @@ la::FwdArgs fixed_args(const void *q, const void *k, const void *v, void *out, c
   return a;
 }
 
+// The gated path's extras (normalisation, SiLU, gate): none by default.
+struct Gated {
+  int flags = 0;
+  const void *gate = nullptr;
+  const float *norm_w = nullptr;
+  float eps = 0.f;
+};
+
+la_status check_gated(const Gated &gt, int d, la_dtype dt) {
+  if (gt.flags & ~(LA_SILU_Q | LA_SILU_K | LA_SILU_V | LA_NORM | LA_GATE))
+    return LA_ERR_INVALID_ARG;
+  if ((gt.flags & LA_GATE) && !gt.gate) return LA_ERR_INVALID_ARG;
+  if (!(gt.eps >= 0.f) || !(gt.eps < __builtin_huge_valf())) return LA_ERR_INVALID_ARG;
+  if (!aligned16({gt.gate, gt.norm_w})) return LA_ERR_INVALID_ARG;
+  if (!(dt == LA_BF16 && d == 128)) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+void apply_gated(la::FwdArgs &a, const Gated &gt) {
+  a.flags = gt.flags;
+  a.gate = gt.gate;
+  a.norm_w = gt.norm_w;
+  a.eps = gt.eps;
+}
+
 la_status fwd_fixed(const void *q, const void *k, const void *v, const float *decay, int B, int H,
                     int64_t N, int d, int block, la_dtype dt, la_layout layout,
                     const float *init_state, void *out, float *final_state,
                     int64_t segment_tokens, void *workspace, size_t workspace_bytes,
-                    void *hip_stream, void *const *phase_events) {
+                    void *hip_stream, void *const *phase_events, const Gated &gt = Gated()) {
   if (B < 0 || N < 0) return LA_ERR_INVALID_ARG;
   la_status st = check_common(H, d, block, dt, segment_tokens);
   if (st == LA_OK) st = check_layout(layout, H, d);
@@ -417,13 +476,14 @@ la_status fwd_fixed(const void *q, const void *k, const void *v, const float *de
   if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
   if (!aligned16({q, k, v, out, init_state, final_state, workspace})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens);
+  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, true, false, block, true);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
   if (N == 0 && !final_state) return LA_OK;
 
-  const la::FwdArgs a = fixed_args(q, k, v, out, decay, B, H, N, d, dt, layout, init_state,
-                                   final_state, pl, workspace, /*reversed=*/false);
+  la::FwdArgs a = fixed_args(q, k, v, out, decay, B, H, N, d, dt, layout, init_state,
+                             final_state, pl, workspace, /*reversed=*/false);
+  apply_gated(a, gt);
   return run_fwd(a, pl, d, dt, /*has_empty=*/N == 0, (hipStream_t)hip_stream, phase_events);
 }
 
@@ -442,7 +502,7 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
                       void *out, float *final_states, int64_t segment_tokens, void *workspace,
                       size_t workspace_bytes, int64_t snap_iv, const int32_t *snap_off,
                       float *snaps, VarlenCall *c, bool allow_fused = true,
-                      bool ch = false) {
+                      bool ch = false, bool short_ok = false, const Gated &gt = Gated()) {
   c->launch = false;
   if (num_seqs < 0 || total_N < 0 || snap_iv < 0) return LA_ERR_INVALID_ARG;
   if (snap_iv > 0 && snap_iv <= total_N && (!snap_off || !snaps)) return LA_ERR_INVALID_ARG;
@@ -455,9 +515,13 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   if (!aligned16({q, k, v, out, init_states, final_states, workspace, snaps}))
     return LA_ERR_INVALID_ARG;
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused, ch);
+  Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused, ch, block,
+                        short_ok);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
+  // Prefix snapshots are stored by the 128-token kernel; the segments (and
+  // so the workspace) stay those of the size query for the same block.
+  if (snap_iv > 0 && pl.chunk < la::mfma::T) pl.chunk = la::mfma::T;
 
   la::FwdArgs &a = c->a;
   a.chdecay = nullptr;
@@ -489,6 +553,7 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   a.init = init_states;
   a.fin = final_states;
   a.ws = (float *)workspace;
+  apply_gated(a, gt);
   c->pl = pl;
   c->d = d;
   c->dt = dt;
@@ -505,11 +570,13 @@ la_status fwd_varlen(const void *q, const void *k, const void *v, const float *d
                      int block, la_dtype dt, la_layout layout, const float *init_states, void *out,
                      float *final_states, int64_t segment_tokens, void *workspace,
                      size_t workspace_bytes, void *hip_stream, int64_t snap_iv = 0,
-                     const int32_t *snap_off = nullptr, float *snaps = nullptr) {
+                     const int32_t *snap_off = nullptr, float *snaps = nullptr,
+                     const Gated &gt = Gated()) {
   VarlenCall c;
   const la_status st = prep_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, block, dt,
                                    layout, init_states, out, final_states, segment_tokens,
-                                   workspace, workspace_bytes, snap_iv, snap_off, snaps, &c);
+                                   workspace, workspace_bytes, snap_iv, snap_off, snaps, &c,
+                                   /*allow_fused=*/true, /*ch=*/false, /*short_ok=*/true, gt);
   if (st != LA_OK || !c.launch) return st;
   return run_fwd(c.a, c.pl, c.d, c.dt, varlen_has_empty(c.pl), (hipStream_t)hip_stream);
 }
@@ -1101,7 +1168,7 @@ size_t lightning_attn_fwd_workspace_size(int B, int H, int64_t N, int d, int blo
                                          int64_t segment_tokens) {
   if (B < 0 || N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK) return 0;
   if ((int64_t)B * H == 0) return 0;
-  return plan_fixed(B, H, N, d, dt, segment_tokens).ws_bytes;
+  return plan_fixed(B, H, N, d, dt, segment_tokens, true, false, block, true).ws_bytes;
 }
 
 la_status lightning_attn_fwd(const void *q, const void *k, const void *v, const float *decay,
@@ -1138,7 +1205,8 @@ size_t lightning_attn_fwd_varlen_workspace_size(int num_seqs, int H, int64_t tot
   if (num_seqs < 0 || total_N < 0 || check_common(H, d, block, dt, segment_tokens) != LA_OK)
     return 0;
   if ((int64_t)num_seqs * H == 0) return 0;
-  return plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens).ws_bytes;
+  return plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, true, false, block, true)
+      .ws_bytes;
 }
 
 la_status lightning_attn_fwd_varlen(const void *q, const void *k, const void *v,
@@ -1210,7 +1278,8 @@ la_status lightning_attn_mixed_step(
   la_status st = prep_varlen(prefill_q, prefill_k, prefill_v, decay, cu_seqlens, num_seqs, H,
                              total_N, d, block, dt, layout, init_states, prefill_out,
                              final_states, segment_tokens, workspace, workspace_bytes, 0,
-                             nullptr, nullptr, &c);
+                             nullptr, nullptr, &c, /*allow_fused=*/true, /*ch=*/false,
+                             /*short_ok=*/true);
   if (st != LA_OK) return st;
   st = check_decode(decode_q, decode_k, decode_v, decay, decode_state, decode_out, decode_B, H, d,
                     dt);
@@ -1228,6 +1297,57 @@ la_status lightning_attn_mixed_step(
     sd = launch_status();
   }
   return sp != LA_OK ? sp : sd;
+}
+
+size_t lightning_attn_fwd_gated_workspace_size(int B, int H, int64_t N, int d, la_dtype dt,
+                                               int64_t segment_tokens) {
+  return lightning_attn_fwd_workspace_size(B, H, N, d, 64, dt, segment_tokens);
+}
+
+la_status lightning_attn_fwd_gated(const void *q, const void *k, const void *v,
+                                   const float *decay, int B, int H, int64_t N, int d,
+                                   la_dtype dt, la_layout layout, int flags, const void *gate,
+                                   const float *norm_weight, float eps,
+                                   const float *init_state, void *out, float *final_state,
+                                   int64_t segment_tokens, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream) {
+  Gated gt;
+  gt.flags = flags;
+  gt.gate = gate;
+  gt.norm_w = norm_weight;
+  gt.eps = eps;
+  if (B < 0 || N < 0 || H < 0) return LA_ERR_INVALID_ARG;
+  const la_status st = check_gated(gt, d, dt);
+  if (st != LA_OK) return st;
+  return fwd_fixed(q, k, v, decay, B, H, N, d, 64, dt, layout, init_state, out, final_state,
+                   segment_tokens, workspace, workspace_bytes, hip_stream, nullptr, gt);
+}
+
+size_t lightning_attn_fwd_varlen_gated_workspace_size(int num_seqs, int H, int64_t total_N, int d,
+                                                      la_dtype dt, int64_t segment_tokens) {
+  return lightning_attn_fwd_varlen_workspace_size(num_seqs, H, total_N, d, 64, dt, segment_tokens);
+}
+
+la_status lightning_attn_fwd_varlen_gated(const void *q, const void *k, const void *v,
+                                          const float *decay, const int32_t *cu_seqlens,
+                                          int num_seqs, int H, int64_t total_N, int d,
+                                          la_dtype dt, la_layout layout, int flags,
+                                          const void *gate, const float *norm_weight, float eps,
+                                          const float *init_states, void *out,
+                                          float *final_states, int64_t segment_tokens,
+                                          void *workspace, size_t workspace_bytes,
+                                          void *hip_stream) {
+  Gated gt;
+  gt.flags = flags;
+  gt.gate = gate;
+  gt.norm_w = norm_weight;
+  gt.eps = eps;
+  if (num_seqs < 0 || total_N < 0 || H < 0) return LA_ERR_INVALID_ARG;
+  const la_status st = check_gated(gt, d, dt);
+  if (st != LA_OK) return st;
+  return fwd_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, 64, dt, layout,
+                    init_states, out, final_states, segment_tokens, workspace, workspace_bytes,
+                    hip_stream, 0, nullptr, nullptr, gt);
 }
 
 }  // extern "C"

@@ -368,6 +368,51 @@ def bench_snapshots(la, inputs, steps, warmup, interval=256):
             "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def bench_short_gated(la, inputs, steps, warmup):
+    """The B=1 H=64 N=32768 layer on the short-chunk kernel (block 64 and 32)
+    and through the gated path (SiLU on q, k, v, normalisation with a weight,
+    sigmoid gate: every part; and none), ms per step beside block 128.
+    Algorithmic bytes as the headline (the gated path also reads the gate:
+    +2 bytes per element)."""
+    import torch
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["layer_h64_n32k"]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    q, k, v = inputs.device_qkv((B, H, N, d), w["seed"], "bf16", device=dev)
+    g, _, _ = inputs.device_qkv((B, H, N, d), w["seed"] + 9, "bf16", device=dev)
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    wgt = torch.ones((H, d), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    fin = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {"workload": "layer_h64_n32k", "unit": "ms per step"}
+    for block in (128, 64, 32):
+        nws = la.lightning_attn_fwd_workspace_size(B, H, N, d, block)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            la.lightning_attn_fwd(q, k, v, decay, block=block, out=out, final_state=fin,
+                                  workspace=ws)
+
+        ms = time_steps(step, steps, warmup, stream)
+        res["block_%d" % block] = {"ms_per_step": round(ms, 4),
+                                   "hbm_frac": round(prefill_bytes(B, H, N, d) / (ms * 1e-3) / 1e9
+                                                     / PEAK_HBM_GBS, 4)}
+    allf = la.LA_SILU_Q | la.LA_SILU_K | la.LA_SILU_V | la.LA_NORM | la.LA_GATE
+    nws = la.lightning_attn_fwd_gated_workspace_size(B, H, N, d)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    for name, flags in (("gated_all", allf), ("gated_none", 0)):
+        def step():
+            la.lightning_attn_fwd_gated(q, k, v, decay, flags, gate=g, norm_weight=wgt, out=out,
+                                        final_state=fin, workspace=ws)
+
+        ms = time_steps(step, steps, warmup, stream)
+        byt = prefill_bytes(B, H, N, d) + (B * H * N * d * 2 if flags else 0)
+        res[name] = {"ms_per_step": round(ms, 4),
+                     "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return res
+
+
 def bench_serving(la, inputs, reps=200, P=50):
     """A mixed serving step at the 64-head layer shape: 20 sequences with
     prefix states, two continuing with P new tokens and eighteen decoding one.
@@ -401,9 +446,11 @@ def bench_serving(la, inputs, reps=200, P=50):
     aout, afin = torch.empty_like(aq), torch.empty_like(ainit)
     side = torch.cuda.Stream(device=dev)
 
+    blk = [128]
+
     def prefill():
         la.lightning_attn_fwd_varlen(pq, pk, pv, decay, cu, init_states=pinit, out=pout,
-                                     final_states=pfin, segment_tokens=seg)
+                                     final_states=pfin, segment_tokens=seg, block=blk[0])
 
     def decode():
         la.lightning_attn_decode(dq, dk, dv, decay, dstate, out=dout)
@@ -423,14 +470,20 @@ def bench_serving(la, inputs, reps=200, P=50):
 
     def one_varlen():
         la.lightning_attn_fwd_varlen(aq, ak, av, decay, acu, init_states=ainit, out=aout,
-                                     final_states=afin, segment_tokens=seg)
+                                     final_states=afin, segment_tokens=seg, block=blk[0])
 
     res = {"workload": "serving_mix_h64", "H": H, "d": d,
            "batch": "2 sequences x %d new tokens + 18 x 1 token, all from prefix states" % P,
            "unit": "us per step"}
-    for name, fn in (("prefill_only", prefill), ("decode_only", decode),
-                     ("one_stream", serial), ("two_streams", two_streams),
-                     ("one_packed_prefill", one_varlen)):
+    variants = [("prefill_only", prefill, 128), ("decode_only", decode, 128),
+                ("one_stream", serial, 128), ("two_streams", two_streams, 128),
+                ("one_packed_prefill", one_varlen, 128)]
+    # the short-chunk kernel (block 64 and 32) for the prefill parts
+    for b in (64, 32):
+        variants += [("prefill_only_block%d" % b, prefill, b),
+                     ("one_packed_prefill_block%d" % b, one_varlen, b)]
+    for name, fn, b in variants:
+        blk[0] = b
         for _ in range(5):  # warm-up (and lazy initialisation) outside the capture
             fn()
         torch.cuda.synchronize()
@@ -458,6 +511,7 @@ def bench_serving(la, inputs, reps=200, P=50):
         res[name] = {"eager": round(eager[len(eager) // 2], 2),
                      "graph": round(s.elapsed_time(e) * 1e3 / reps, 2)}
         del g
+    blk[0] = 128
     dstate.copy_(dstate0)
     return res
 
@@ -580,7 +634,7 @@ def main():
                     help="also report the time of every headline step (warm-up and timed), "
                          "from HIP events between the steps")
     ap.add_argument("--leg", choices=["backward", "serving", "snapshots", "chdecay", "million",
-                                      "varlen", "decode"], default=None,
+                                      "varlen", "decode", "short_gated"], default=None,
                     help="time only this extra workload and print its JSON object (for "
                          "profiling it on its own); the headline line is not printed")
     args = ap.parse_args()
@@ -602,7 +656,8 @@ def main():
                 "chdecay": lambda: bench_chdecay(la, inputs, args.steps, 20),
                 "million": lambda: bench_million(la, inputs, args.steps, 2),
                 "varlen": lambda: bench_varlen(la, inputs, args.steps, 2),
-                "decode": lambda: bench_decode(la, inputs, reps=5, warmup=1)}
+                "decode": lambda: bench_decode(la, inputs, reps=5, warmup=1),
+                "short_gated": lambda: bench_short_gated(la, inputs, args.steps, 20)}
         print(json.dumps(legs[args.leg]()), flush=True)
         return
     w = inputs.WORKLOADS["layer_h64_n32k"]
@@ -684,6 +739,8 @@ def main():
         res["chdecay"] = bench_chdecay(la, inputs, steps=args.steps, warmup=20)
         torch.cuda.empty_cache()
         res["snapshots"] = bench_snapshots(la, inputs, steps=max(5, args.steps // 2), warmup=2)
+        torch.cuda.empty_cache()
+        res["short_gated"] = bench_short_gated(la, inputs, steps=args.steps, warmup=20)
         torch.cuda.empty_cache()
         res["serving"] = bench_serving(la, inputs, P=50)
         torch.cuda.empty_cache()

@@ -1120,8 +1120,9 @@ void local_state_kernel(FwdArgs p) {
     __syncthreads();
     issue(slot_c, t0 + 2 * C_LOCAL);
     const int Lc = (int)((x1 - t0) < C_LOCAL ? (x1 - t0) : C_LOCAL);
-    // weight of chunk row c: lambda^(x1 - 1 - (t0 + c))
-    state_update<C_LOCAL / 16, false>(S, Ks, Vs, Lc, (int)(x1 - 1 - t0), l2, fast, tail, u, lane);
+    // weight of chunk row c: lambda^(x1 - 1 - (t0 + c)); the pipelined update
+    // (LDS reads a step ahead) fits the two-waves-per-SIMD register budget
+    state_update<C_LOCAL / 16, true>(S, Ks, Vs, Lc, (int)(x1 - 1 - t0), l2, fast, tail, u, lane);
     __syncthreads();
   };
   using S0 = std::integral_constant<int, 0>;

@@ -354,6 +354,43 @@ __device__ __forceinline__ void inter_term(f32x4 (&acc)[2][8], unsigned st,
   }
 }
 
+// The same product with the published tile read transposed: the tile holds
+// M^T (row j = column j of M, as write_st lays out S^T) and the A operand is
+// M itself, so this is O^T = M Q^T for the state M = S^T.  Fragment (jt, ks)
+// of M (rows 16 jt + i16, columns 32 ks + 8 G ..) is column 16 jt + i16 of
+// tile rows 32 ks + 8 G + (0..7): two ds_read_b64_tr_b16 over rows
+// 32 ks + 8 G + (0..3) and + (4..7), at (t0 + 8192 ks) ^ (jt << 5) and
+// (t1 + 8192 ks) ^ (jt << 5), where t0 and t1 are the tile's LDS address plus
+// kv_off(8 G + i16 / 4, 8 (i16 % 4)) and kv_off(8 G + 4 + i16 / 4, ..).
+__device__ __forceinline__ void inter_term_tr(f32x4 (&acc)[2][8], unsigned t0, unsigned t1,
+                                              const u32x4 (&qf)[2][4], const float (&a)[2]) {
+  bf16x8 sf[2][4];
+  auto fetch = [&](int jt, int slot) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      sf[slot][ks] = tr_read8u((t0 + 8192 * ks) ^ (jt << 5), (t1 + 8192 * ks) ^ (jt << 5));
+  };
+  fetch(0, 0);
+#pragma unroll
+  for (int jt = 0; jt < 8; ++jt) {
+    if (jt + 1 < 8) fetch(jt + 1, (jt + 1) & 1);
+    acc[0][jt] = (f32x4){};
+    acc[1][jt] = (f32x4){};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      acc[0][jt] = mma16(sf[jt & 1][ks], as_bf16x8(qf[0][ks]), acc[0][jt]);
+      acc[1][jt] = mma16(sf[jt & 1][ks], as_bf16x8(qf[1][ks]), acc[1][jt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int jt = 0; jt < 8; ++jt) {
+    acc[0][jt] *= a[0];
+    acc[1][jt] *= a[1];
+    asm volatile("" : "+v"(acc[0][jt]), "+v"(acc[1][jt]));
+  }
+}
+
 // Per-workgroup constants and lane coordinates of the 8-wave layout.  The
 // wave index lives in a scalar register, so the role test is a scalar branch
 // and each role runs a loop of its own.  (With one exec-masked instruction
@@ -550,6 +587,72 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
 // 16-row query blocks w and 7 - w, so every wave has the same causal work
 // (nine 16-key blocks of K Q^T and five 32-key steps of V^T P^T).
 //
+// Intra-block term of query block bi (rows 16 rb + i16) over the 32-key
+// steps kp <= rb / 2: P^T = K Q^T for keys 32 kp + (0..15) (p0) and
+// 32 kp + 16 + (0..15) (p1; wholly above the diagonal in the last step of an
+// even block, where the mask zeroes it: computing it anyway keeps the step
+// free of branches); register r of p0 holds key 32 kp + 4 G + r, of p1 key
+// 32 kp + 16 + 4 G + r.  Masked and decayed (lambda^(row - key), zero above
+// the diagonal), then O^T += V^T P^T with V read in the same key order.
+// Ks, Vs: LDS addresses of the chunk's K and V tiles; kq, vq: this lane's
+// tile offsets (see output_loop).
+template <bool FAST, int BI>
+__device__ __forceinline__ void intra_block(f32x4 (&acc)[2][8], const u32x4 (&qf)[2][4],
+                                            unsigned Ks, unsigned Vs, unsigned kq, unsigned vq,
+                                            int i16, int G, int rb, const Decay &dc) {
+  const float l2 = dc.l2;
+  const int row = 16 * rb + i16;
+  for (int kp = 0; kp <= (rb >> 1); ++kp) {
+    const unsigned kb = Ks + 32 * kp * KV_ROW + kq;
+    f32x4 p0 = {}, p1 = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      p0 = mma16(lds_ld<bf16x8>(kb ^ (ks << 6)), as_bf16x8(qf[BI][ks]), p0);
+      p1 = mma16(lds_ld<bf16x8>((kb ^ (ks << 6)) + 16 * KV_ROW), as_bf16x8(qf[BI][ks]), p1);
+    }
+    const int n0 = row - (32 * kp + 4 * G), n1 = n0 - 16;
+    float pw[8];
+    if constexpr (FAST) {
+      const float e0 = fast_exp2((float)(n0 - 3) * l2), e1 = fast_exp2((float)(n1 - 3) * l2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pw[r] = (n0 >= r) ? p0[r] * (e0 * dc.tail[4 + r]) : 0.f;
+        pw[4 + r] = (n1 >= r) ? p1[r] * (e1 * dc.tail[4 + r]) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pw[r] = (n0 >= r) ? p0[r] * fast_exp2((float)(n0 - r) * l2) : 0.f;
+        pw[4 + r] = (n1 >= r) ? p1[r] * fast_exp2((float)(n1 - r) * l2) : 0.f;
+      }
+    }
+    const bf16x8 pb = cvt8(pw);
+    const unsigned vb = Vs + 32 * kp * KV_ROW + vq;
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      const unsigned va = vb ^ (jt << 5);
+      acc[BI][jt] = mma16(tr_read8u(va, va + 16 * KV_ROW), pb, acc[BI][jt]);
+    }
+  }
+}
+
+// Stages this output wave's accumulators (acc[bi][jt] register r holds
+// feature 16 jt + 4 G + r of row 16 qblock(bi) + i16) as bf16 in the
+// swizzled tile at LDS address Os: at kv_off(row, 8 G) ^ (jt << 5).
+__device__ __forceinline__ void stage_rows(const f32x4 (&acc)[2][8], unsigned Os,
+                                           const OutLane &o) {
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    const unsigned sb = Os + kv_off(16 * o.qblock(bi) + o.i16, 8 * o.G);
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      bf16x4 v = {(bf16)acc[bi][jt][0], (bf16)acc[bi][jt][1], (bf16)acc[bi][jt][2],
+                  (bf16)acc[bi][jt][3]};
+      lds_st<bf16x4>(sb ^ (jt << 5), v);
+    }
+  }
+}
+
 // The chunk loop over segment [cur.c0, b) of head h, output side.  On entry
 // qn holds (or is loading) the first chunk's Q^T fragments.
 // FAST: the decay weights take the factored powers (see Decay); a template
@@ -589,75 +692,20 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
       for (int bi = 0; bi < 2; ++bi)
         a_row[bi] = fast_exp2((float)(16 * o.qblock(bi) + i16 + 1) * l2);
 
-      // Intra-block term of query block bi (rows 16 rb + i16) over the
-      // 32-key steps kp <= rb / 2: P^T = K Q^T for keys 32 kp + (0..15) (p0)
-      // and 32 kp + 16 + (0..15) (p1; wholly above the diagonal in the last
-      // step of an even block, where the mask zeroes it: computing it anyway
-      // keeps the step free of branches); register r of p0 holds key
-      // 32 kp + 4 G + r, of p1 key 32 kp + 16 + 4 G + r.  Masked and decayed
-      // (lambda^(row - key), zero above the diagonal), then O^T += V^T P^T
-      // with V read in the same key order.
-      auto intra = [&](auto bic, int rb) {
-        constexpr int bi = decltype(bic)::value;
-        const int row = 16 * rb + i16;
-        for (int kp = 0; kp <= (rb >> 1); ++kp) {
-          const unsigned kb = Ks + 32 * kp * KV_ROW + kq;
-          f32x4 p0 = {}, p1 = {};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            p0 = mma16(lds_ld<bf16x8>(kb ^ (ks << 6)), as_bf16x8(qf[bi][ks]), p0);
-            p1 = mma16(lds_ld<bf16x8>((kb ^ (ks << 6)) + 16 * KV_ROW), as_bf16x8(qf[bi][ks]), p1);
-          }
-          const int n0 = row - (32 * kp + 4 * G), n1 = n0 - 16;
-          float pw[8];
-          if constexpr (FAST) {
-            const float e0 = fast_exp2((float)(n0 - 3) * l2), e1 = fast_exp2((float)(n1 - 3) * l2);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              pw[r] = (n0 >= r) ? p0[r] * (e0 * dc.tail[4 + r]) : 0.f;
-              pw[4 + r] = (n1 >= r) ? p1[r] * (e1 * dc.tail[4 + r]) : 0.f;
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              pw[r] = (n0 >= r) ? p0[r] * fast_exp2((float)(n0 - r) * l2) : 0.f;
-              pw[4 + r] = (n1 >= r) ? p1[r] * fast_exp2((float)(n1 - r) * l2) : 0.f;
-            }
-          }
-          const bf16x8 pb = cvt8(pw);
-          const unsigned vb = Vs + 32 * kp * KV_ROW + vq;
-#pragma unroll
-          for (int jt = 0; jt < 8; ++jt) {
-            const unsigned va = vb ^ (jt << 5);
-            acc[bi][jt] = mma16(tr_read8u(va, va + 16 * KV_ROW), pb, acc[bi][jt]);
-          }
-        }
-      };
-
       // The next chunk's Q^T: block 0 now, block 1 once this chunk's block 0
       // fragments are spent (keeps one 16-register set fewer alive).
       if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 0, qn[0], o);
       inter_term(acc, STs + kq, qf, a_row);
-      intra(std::integral_constant<int, 0>{}, w);
+      intra_block<FAST, 0>(acc, qf, Ks, Vs, kq, vq, i16, G, w, dc);
       if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 1, qn[1], o);
-      intra(std::integral_constant<int, 1>{}, 7 - w);
+      intra_block<FAST, 1>(acc, qf, Ks, Vs, kq, vq, i16, G, 7 - w, dc);
     }
     __syncthreads();  // B: this chunk's K/V and S^T reads are done
     {
-      // Stage the tile in this wave's rows of the chunk's K tile (acc[bi][jt]
-      // register r holds feature 16 jt + 4 G + r of row 16 qblock(bi) + i16:
-      // at kv_off(row, 8 G) ^ (jt << 5)), then write it back as whole rows.
+      // Stage the tile in this wave's rows of the chunk's K tile, then write
+      // it back as whole rows.
       const OutLane o(ln.lane, w);
-#pragma unroll
-      for (int bi = 0; bi < 2; ++bi) {
-        const unsigned sb = Ks + kv_off(16 * o.qblock(bi) + o.i16, 8 * o.G);
-#pragma unroll
-        for (int jt = 0; jt < 8; ++jt) {
-          bf16x4 v = {(bf16)acc[bi][jt][0], (bf16)acc[bi][jt][1], (bf16)acc[bi][jt][2],
-                      (bf16)acc[bi][jt][3]};
-          lds_st<bf16x4>(sb ^ (jt << 5), v);
-        }
-      }
+      stage_rows(acc, Ks, o);
       write_rows<SNAP, REV>(p, h, cur, Ks, o);
     }
     if (!nxt.valid) break;
@@ -671,7 +719,9 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
 // (see above), updates the state and publishes it as S^T; writes every
 // sequence end's final state inside the segment, and the state at every
 // snapshot point the segment's chunks end on.
-template <bool SNAP, bool REV = false>
+// MID: the output side closes a third barrier in the middle of each chunk
+// (the fused dk/dv loop), and the next chunk's tiles go out after it.
+template <bool SNAP, bool REV = false, bool MID = false>
 __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                            f32x16 (&S)[4], char *smem, const Decay &dc,
                                            const Lanes &ln) {
@@ -712,10 +762,18 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
       const float gL = fast_exp2((float)L * l2);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) S[nt] *= gL;
-      state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane, issue_next);
+      if constexpr (MID)
+        state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane);
+      else
+        state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane, issue_next);
       if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
       if (snap_here) store_state(p.snaps + (snap_row(m, p.snap_off, cur) * H + h) * DD, S, w, l32, g);
-    } else {
+    } else if constexpr (!MID) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) issue_next(k);
+    }
+    if constexpr (MID) {
+      __syncthreads();  // M: the other buffer's K tile is free again
 #pragma unroll
       for (int k = 0; k < 8; ++k) issue_next(k);
     }
@@ -790,18 +848,147 @@ void prefill_chunk_kernel(FwdArgs p) {
   chunk_workgroup<SERVE>(p, blockIdx.x, smem);
 }
 
-// Two output passes of the same plan in one grid (the backward's dv and dk
-// passes): workgroup 2i runs workgroup i of pass a, 2i + 1 workgroup i of
-// pass b.  The two workgroups of a pair walk the same chunks of the same
-// (segment, head) side by side, so the inputs the passes share are read
-// from HBM once and found in the Infinity Cache by the other.
-// REV: the passes are time-reversed packed views (SeqMap::rev_rs may be
-// non-zero); without it the address arithmetic leaves that term out.
+// The backward's dv and dk output passes in one workgroup per (segment,
+// head).  Both passes walk the same time-reversed chunks with the same tiles:
+// the dv pass has keys q and values do (queries k), the dk pass keys do and
+// values q (queries v), and the dk pass's state is the transpose of the dv
+// pass's (G^T against G, see la_backward.h).  So the state waves run the dv
+// pass's walk once (tiles q and do, state G, published as G^T), and the
+// output waves compute, per chunk,
+//   dv^T = diag(a) (G^T K^T) + do^T ((q K^T) (.) D^T)       queries K = k,
+//   dk^T = diag(a) (G V^T)   + q^T ((do V^T) (.) D^T)       queries V = v,
+// the second with the tiles' roles swapped and the published G^T read
+// transposed.  q and do are read once instead of twice, and the state is
+// updated once.
+// Per chunk the output side has three barriers: A (opens the chunk), M
+// (dv is computed, staged in the other buffer's K tile and written back;
+// the state waves then start the next chunk's tiles into that buffer) and
+// B (every read of the chunk's tiles and of G^T is done; dk is staged in
+// the chunk's K tile and written back).  dk's queries load while dv
+// computes, the next chunk's dv queries while dk computes.
+template <bool FAST, bool REV>
+__device__ __forceinline__ void dkdv_output_loop(const FwdArgs &pv, const FwdArgs &pk, int h,
+                                                 int64_t b, Cursor cur, u32x4 (&qn)[2][4],
+                                                 char *smem, const Decay &dc, const Lanes &ln) {
+  const SeqMap &m = pv.m;
+  const int w = ln.w;
+  const float l2 = dc.l2;
+  const unsigned STs = lds_u32(smem + 2 * LDS_KV);
+  f32x4 acc[2][8];
+  u32x4 qf[2][4];
+  int buf = 0;
+
+  while (true) {
+    const Cursor nxt = next_chunk<true>(m, cur, b, T);
+    const unsigned Ks = lds_u32(smem + buf * LDS_KV), Vs = Ks + LDS_K;
+    const unsigned Xs = lds_u32(smem + (buf ^ 1) * LDS_KV);
+    __syncthreads();  // A: this chunk's tiles and entering G^T are in LDS
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[bi][ks] = qn[bi][ks];
+    {
+      const OutLane o(ln.lane, w);
+      const int i16 = o.i16, G = o.G;
+      const unsigned kq = kv_off(i16, 16 * G);
+      const unsigned vq = kv_off(4 * G + (i16 >> 2), 8 * (i16 & 3));
+      float a_row[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+        a_row[bi] = fast_exp2((float)(16 * o.qblock(bi) + i16 + 1) * l2);
+      issue_q_loads<REV>(pk, h, cur, 0, qn[0], o);
+      inter_term(acc, STs + kq, qf, a_row);
+      intra_block<FAST, 0>(acc, qf, Ks, Vs, kq, vq, i16, G, w, dc);
+      issue_q_loads<REV>(pk, h, cur, 1, qn[1], o);
+      intra_block<FAST, 1>(acc, qf, Ks, Vs, kq, vq, i16, G, 7 - w, dc);
+    }
+    {
+      const OutLane o(ln.lane, w);
+      stage_rows(acc, Xs, o);
+      write_rows<true, REV>(pv, h, cur, Xs, o);
+    }
+    __syncthreads();  // M: dv is out of the other buffer
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[bi][ks] = qn[bi][ks];
+    {
+      const OutLane o(ln.lane, w);
+      const int i16 = o.i16, G = o.G;
+      const unsigned kq = kv_off(i16, 16 * G);
+      const unsigned vq = kv_off(4 * G + (i16 >> 2), 8 * (i16 & 3));
+      const unsigned t0 = STs + kv_off(8 * G + (i16 >> 2), 8 * (i16 & 3));
+      const unsigned t1 = STs + kv_off(8 * G + 4 + (i16 >> 2), 8 * (i16 & 3));
+      float a_row[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+        a_row[bi] = fast_exp2((float)(16 * o.qblock(bi) + i16 + 1) * l2);
+      if (nxt.valid) issue_q_loads<REV>(pv, h, nxt, 0, qn[0], o);
+      inter_term_tr(acc, t0, t1, qf, a_row);
+      intra_block<FAST, 0>(acc, qf, Vs, Ks, kq, vq, i16, G, w, dc);
+      if (nxt.valid) issue_q_loads<REV>(pv, h, nxt, 1, qn[1], o);
+      intra_block<FAST, 1>(acc, qf, Vs, Ks, kq, vq, i16, G, 7 - w, dc);
+    }
+    __syncthreads();  // B: this chunk's tile and G^T reads are done
+    {
+      const OutLane o(ln.lane, w);
+      stage_rows(acc, Ks, o);
+      write_rows<true, REV>(pk, h, cur, Ks, o);
+    }
+    if (!nxt.valid) break;
+    cur = nxt;
+    buf ^= 1;
+  }
+}
+
+// One (segment, head) of the fused dv/dk pass: pv is the dv pass (q = k,
+// k = q, v = do, out = dv; its entering states, initial state and final
+// state), pk supplies the dk pass's queries (q = v) and output (out = dk)
+// over the same time-reversed view.
+template <bool REV>
+__device__ __forceinline__ void dkdv_workgroup(const FwdArgs &pv, const FwdArgs &pk, int bid,
+                                               char *smem) {
+  const Lanes ln;
+  const SeqMap &m = pv.m;
+  const int H = m.H;
+  const int s = bid / H, h = bid - (bid / H) * H;
+  const Decay dc(pv.decay[h]);
+  int64_t a, b;
+  segment_bounds(pv, s, &a, &b);
+  const int64_t DD = (int64_t)D * D;
+  const Cursor cur = first_chunk<true>(m, a, b, T);
+  if (!cur.valid) {
+    // One segment per sequence: an empty sequence keeps its initial state.
+    if (pv.seg_len == 0 && pv.fin) {
+      float *dst = pv.fin + ((int64_t)s * H + h) * DD;
+      const float *src = pv.init ? pv.init + ((int64_t)s * H + h) * DD : nullptr;
+      for (int e = threadIdx.x; e < D * D; e += NT) dst[e] = src ? src[e] : 0.f;
+    }
+    return;
+  }
+  if (ln.out_wave) {
+    u32x4 qn[2][4];
+    const OutLane o(ln.lane, ln.w);
+    issue_q_loads<REV>(pv, h, cur, 0, qn[0], o);
+    issue_q_loads<REV>(pv, h, cur, 1, qn[1], o);
+    if (dc.fast)
+      dkdv_output_loop<true, REV>(pv, pk, h, b, cur, qn, smem, dc, ln);
+    else
+      dkdv_output_loop<false, REV>(pv, pk, h, b, cur, qn, smem, dc, ln);
+  } else {
+    f32x16 S[4];
+    const float *s0 = pv.ws ? pv.ws + ((int64_t)s * pv.r_split * H + h) * DD
+                            : (pv.init ? pv.init + ((int64_t)cur.j * H + h) * DD : nullptr);
+    load_state(S, s0, ln.w, ln.l32, ln.g);
+    state_loop<true, REV, true>(pv, h, b, cur, S, smem, dc, ln);
+  }
+}
+
 template <bool REV>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_chunk_pair_kernel(FwdArgs a, FwdArgs b) {
+void prefill_dkdv_kernel(FwdArgs pv, FwdArgs pk) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-  chunk_workgroup<true, REV>((blockIdx.x & 1) ? b : a, blockIdx.x >> 1, smem);
+  dkdv_workgroup<REV>(pv, pk, blockIdx.x, smem);
 }
 
 // Single-pass prefill with the segment scan folded in (MiniMax-01 report,

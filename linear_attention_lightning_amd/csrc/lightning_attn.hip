@@ -720,13 +720,18 @@ la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dt
   float *fin_dv = (float *)((char *)gT + st_b);
   float *dk_in = (float *)((char *)fin_dv + st_b);  // dk pass entering states (pl.scan)
   const dim3 tgrid((unsigned)SH, (unsigned)(d / 32), (unsigned)(d / 32));
+  // MFMA path: dv and dk come from one fused pass whose dk side reads the
+  // dv pass's state transposed, so the dk pass's own states (gT, dk_in) are
+  // not formed.
+  const bool fused_dkdv = use_mfma(d, dt);
   if (init)
     hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, init, 1, H, d, decay,
                        false, initT);
   if (dfinal) {
     hipLaunchKernelGGL(la::bwd_scale_kernel, sgrid, dim3(256), 0, s, dfinal, decay, H, d, g);
-    hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, dfinal, 1, H, d,
-                       decay, true, gT);
+    if (!fused_dkdv)
+      hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, dfinal, 1, H, d,
+                         decay, true, gT);
   }
   // dq: causal, from S_init^T.  Its state is S_t^T, so with the forward's
   // saved segment entering states (transposed) only its output pass runs.
@@ -752,10 +757,11 @@ la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dt
   if (r == LA_OK) r = run_fwd(av, pl, d, dt, has_empty, s, nullptr, /*out_pass=*/false);
   if (r == LA_OK) {
     if (pl.scan) {
-      hipLaunchKernelGGL(la::transpose_states_kernel,
-                         dim3((unsigned)(pl.nseg * H), (unsigned)(d / 32), (unsigned)(d / 32)),
-                         dim3(256), 0, s, (const float *)workspace, pl.r_split, H, d, decay,
-                         false, dk_in);
+      if (!fused_dkdv)
+        hipLaunchKernelGGL(la::transpose_states_kernel,
+                           dim3((unsigned)(pl.nseg * H), (unsigned)(d / 32), (unsigned)(d / 32)),
+                           dim3(256), 0, s, (const float *)workspace, pl.r_split, H, d, decay,
+                           false, dk_in);
       av.r_split = pl.r_split;
       ak.ws = dk_in;
       ak.r_split = 1;
@@ -764,14 +770,14 @@ la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dt
       ak.ws = nullptr;
     }
     if (pl.nseg > 0) {
-      if (use_mfma(d, dt)) {
-        // Both output passes in one grid, workgroups paired (one launch).
+      if (fused_dkdv) {
+        // Both output passes in one workgroup per (segment, head).
         if (av.m.rev_rs != 0)
-          hipLaunchKernelGGL(la::mfma::prefill_chunk_pair_kernel<true>,
-                             dim3((unsigned)(2 * pl.nseg * H)), dim3(la::mfma::NT), 0, s, av, ak);
+          hipLaunchKernelGGL(la::mfma::prefill_dkdv_kernel<true>, dim3((unsigned)(pl.nseg * H)),
+                             dim3(la::mfma::NT), 0, s, av, ak);
         else
-          hipLaunchKernelGGL(la::mfma::prefill_chunk_pair_kernel<false>,
-                             dim3((unsigned)(2 * pl.nseg * H)), dim3(la::mfma::NT), 0, s, av, ak);
+          hipLaunchKernelGGL(la::mfma::prefill_dkdv_kernel<false>, dim3((unsigned)(pl.nseg * H)),
+                             dim3(la::mfma::NT), 0, s, av, ak);
       } else {
         launch_phase(av, pl, d, dt, s, /*phase_a=*/false);
         launch_phase(ak, pl, d, dt, s, /*phase_a=*/false);

@@ -93,12 +93,15 @@ constexpr int64_t kFusedSeg = 8192;
 // Fixed-length plan.  Without a scan each sequence is one segment.  With
 // one, the token axis of every head is cut into equal segments so that
 // about target_groups(d, dt) workgroups run per phase.
-// Workgroups to aim for per phase: the MFMA chunk kernel (160 KB of LDS) runs
-// one workgroup per CU, and a single round over the 256 CUs with long
-// segments measured fastest (fewer, longer pipelines and less local-state
-// work); the vector-ALU kernels run several small workgroups per CU.
+// Workgroups to aim for per phase: the MFMA chunk kernel (160 KB of LDS) and
+// the channel-wise one (82 KB) run one workgroup per CU, and a single round
+// over the 256 CUs with long segments measured fastest (fewer, longer
+// pipelines and less local-state work: for the channel-wise kernel 4
+// segments per head instead of 8 took its 64-head 32768-token step from
+// 770 to 716 us); the short-chunk kernel (two per CU) and the vector-ALU
+// kernels run several workgroups per CU.
 int64_t target_groups(int d, la_dtype dt, bool ch = false, int chunk = 128) {
-  return use_mfma(d, dt, ch) && chunk == la::mfma::T ? 256 : 512;
+  return use_mfma(d, dt, ch) && (chunk == la::mfma::T || ch) ? 256 : 512;
 }
 
 // Pieces per segment of the MFMA local-state pass (for a head whose whole

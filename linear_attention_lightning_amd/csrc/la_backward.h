@@ -7,8 +7,10 @@
 // G_t = q_t^T do_t + lambda G_{t+1} runs backwards from dS_fin, so a reversed
 // pass starts from dS_fin / lambda (its kernels decay an initial state once
 // more than G needs), and dS_init = lambda G_0 = lambda x (the dv pass's final
-// state).  These kernels form those states, and transpose the dv pass's
-// segment entering states into the dk pass's (G and G^T share segments).
+// state).  These kernels form those states, and (for the vector-ALU path,
+// which runs the dk pass on its own) transpose the dv pass's segment entering
+// states into the dk pass's (G and G^T share segments); on MFMA the dv and dk
+// passes run as one (prefill_dkdv_kernel), the dk side reading G transposed.
 #pragma once
 
 #include "la_common.h"

@@ -1226,9 +1226,16 @@ void local_state_kernel(FwdArgs p) {
   const int l32 = lane & 31, g = lane >> 5;
   const SeqMap &m = p.m;
   const int H = m.H, R = p.r_split;
+  // Items piece-major from the last piece down, heads fastest (spread over
+  // the XCDs): the slowly decaying heads' extra pieces, all of full length,
+  // go out first, and every head's first piece -- among them the short
+  // single pieces of fast heads -- last, where they fill the gaps of the
+  // final round instead of starting a round of long pieces of their own.
   const int item = xcd_spread((int)blockIdx.x, (int)gridDim.x);
-  const int idx = item / H, h = item - idx * H;
-  const int s = p.nseg - 2 - idx / R, r = R - 1 - idx % R;
+  const int per_r = (p.nseg - 1) * H;
+  const int rr = item / per_r, rem = item - rr * per_r;
+  const int idx = rem / H, h = rem - idx * H;
+  const int s = p.nseg - 2 - idx, r = R - 1 - rr;
   float l2max = 0.f, l2f[8];  // channel-wise: slowest channel, and this thread's 8 channels
   if constexpr (CH) {
     const float *al = p.chdecay + (int64_t)h * D;

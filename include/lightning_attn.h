@@ -340,7 +340,7 @@ la_status lightning_attn_fwd_varlen_snapshots(
  * are loaded, the normalisation to the float32 accumulators of each output
  * row, weight and gate to the row as it is stored; nothing else reads or
  * writes out.  With flags == 0 this is lightning_attn_fwd_layout with
- * block 64.
+ * block 128 (bit for bit), always in the three-phase schedule.
  *
  *   flags        : any combination of LA_SILU_Q, LA_SILU_K, LA_SILU_V,
  *                  LA_NORM, LA_GATE (other bits: LA_ERR_INVALID_ARG).
@@ -349,10 +349,10 @@ la_status lightning_attn_fwd_varlen_snapshots(
  *   norm_weight  : [H][d] float32 or NULL; used with LA_NORM.
  *   eps          : >= 0 and finite; used with LA_NORM.
  *   Other arguments as for lightning_attn_fwd_layout, without `block`: the
- *   path runs 64-token chunks (a row's d channels then sit in one wave);
- *   workspace from lightning_attn_fwd_gated_workspace_size (that of
- *   lightning_attn_fwd_workspace_size with block 64).  bf16 with d = 128 only
- *   (otherwise LA_ERR_UNSUPPORTED).
+ *   path runs 128-token chunks (a row's d channels sit in four lanes of one
+ *   wave); workspace from lightning_attn_fwd_gated_workspace_size (the
+ *   three-phase plan at block 128, whatever LIGHTNING_ATTN_PREFILL says).
+ *   bf16 with d = 128 only (otherwise LA_ERR_UNSUPPORTED).
  */
 enum { LA_SILU_Q = 1, LA_SILU_K = 2, LA_SILU_V = 4, LA_NORM = 8, LA_GATE = 16 };
 

@@ -137,8 +137,14 @@ __device__ __forceinline__ bf16x8 cvt8(const float (&v)[8]) {
   return r;
 }
 
-// FwdArgs::flags of the gated path (normalisation, SiLU and gate around the
-// attention; see la_prefill_short.h).
+// FwdArgs::flags of the gated path: the normalisation, SiLU activation and
+// gate the MiniMax-01 report places around its attention and leaves out of
+// its derivation (section 2.2.1).  The reading computed here, each part
+// selected by a flag: SiLU(x) = x / (1 + e^-x) on q, k and/or v as they are
+// read; RMS normalisation of every output row over the head's 128 channels,
+// o / sqrt(mean(o^2) + eps), times a per-channel weight [H][128]; an output
+// gate o * sigmoid(g), g laid out like the output.  The normalisation runs on
+// the float32 accumulators, weight and gate on the row as it is stored.
 enum : int { GF_SILU_Q = 1, GF_SILU_K = 2, GF_SILU_V = 4, GF_NORM = 8, GF_GATE = 16 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -535,9 +541,19 @@ __device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const
 // lowest address, and row r sits at byte (L - 1 - r) * |rsb|; rows >= L are
 // given the offset 2^31, past the range (below 2^31 bytes), and dropped.
 // REV: the view may be a time-reversed packed view (see SeqMap::row_base).
-template <bool NEG = false, bool REV = false>
+// Gated epilogue (GF_NORM / GF_GATE): before the store, every row is
+// multiplied by the head's normalisation weight (wt: this lane's 8 channels
+// 8 c16 .., ones without a weight) and by sigmoid of its gate values (gr:
+// this lane's 16 bytes of the gate rows written, in write order).
+struct Epi {
+  float wt[8];
+  u32x4 gr[8];
+  bool gate;
+};
+
+template <bool NEG = false, bool REV = false, bool EPI = false>
 __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor &c, unsigned Os,
-                                           const OutLane &o) {
+                                           const OutLane &o, const Epi *ep = nullptr) {
   const int L = (int)(c.c1 - c.c0);
   const int sub = o.G, c16 = o.i16;
   // Row r of the chunk starts at byte r * rsb; the range ends with row L - 1
@@ -555,11 +571,58 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
     const unsigned rb = Os + kv_off(r0, c16 * 16);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const u32x4 x = lds_ld<u32x4>((rb ^ (it << 4)) + 1024 * it);
+      u32x4 x = lds_ld<u32x4>((rb ^ (it << 4)) + 1024 * it);
+      if constexpr (EPI) {
+        const bf16x8 o8 = __builtin_bit_cast(bf16x8, x);
+        const bf16x8 g8 = __builtin_bit_cast(bf16x8, ep->gr[4 * bi + it]);
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float gate =
+              ep->gate ? __builtin_amdgcn_rcpf(1.f + fast_exp2(-(float)g8[e] * kLog2e)) : 1.f;
+          y[e] = (float)o8[e] * ep->wt[e] * gate;
+        }
+        x = __builtin_bit_cast(u32x4, cvt8(y));
+      }
       const int r = r0 + 4 * it;
       const int off = (NEG && r >= L) ? (int)0x80000000u : (r - flip) * rsb + c16 * 16;
       __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, off, 0, kCpolNT);
     }
+  }
+}
+
+// The gate values write_rows<.., EPI> applies to chunk c's rows (rows past
+// the chunk's end read its last row: their outputs are never stored).
+__device__ __forceinline__ void issue_gate_loads(const FwdArgs &p, int h, const Cursor &c,
+                                                 u32x4 (&gr)[8], const OutLane &o) {
+  const int Lc = (int)(c.c1 - c.c0);
+  const bf16 *base = (const bf16 *)p.gate + p.m.row_base<false>(h, c.j) + c.c0 * p.m.rs + 8 * o.i16;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = 16 * o.qblock(bi) + o.G + 4 * it;
+      gr[4 * bi + it] =
+          __builtin_nontemporal_load((const u32x4 *)(base + (int64_t)(r < Lc ? r : Lc - 1) * p.m.rs));
+    }
+}
+
+// RMS normalisation of this lane's two query rows (acc[bi][jt] register r:
+// feature 16 jt + 4 G + r; the row's other features sit in the lanes with
+// the same i16, lane ^ 16, ^ 32, ^ 48).
+__device__ __forceinline__ void rms_rows(f32x4 (&acc)[2][8], float eps) {
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    float ss = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss += acc[bi][jt][r] * acc[bi][jt][r];
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float inv = __builtin_amdgcn_rsqf(ss * (1.f / D) + eps);
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) acc[bi][jt] *= inv;
   }
 }
 
@@ -658,7 +721,10 @@ __device__ __forceinline__ void stage_rows(const f32x4 (&acc)[2][8], unsigned Os
 // FAST: the decay weights take the factored powers (see Decay); a template
 // parameter so that each chunk step is one basic block the scheduler can
 // interleave freely.
-template <bool FAST, bool SNAP, bool REV = false>
+// EPI: the gated reading's parts (FwdArgs::flags): SiLU on Q^T as it is
+// used, RMS normalisation of the float32 rows, weight and gate at the store
+// (the state waves apply the SiLU to the K/V tiles).
+template <bool FAST, bool SNAP, bool REV = false, bool EPI = false>
 __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                             u32x4 (&qn)[2][4], char *smem, const Decay &dc,
                                             const Lanes &ln) {
@@ -669,6 +735,15 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
   f32x4 acc[2][8];
   u32x4 qf[2][4];
   int buf = 0;
+  Epi ep;
+  if constexpr (EPI) {
+    // this lane's 8 channels 8 i16 .. of the weight, for the whole walk
+    const OutLane o(ln.lane, w);
+    const bool wn = (p.flags & GF_NORM) && p.norm_w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ep.wt[e] = wn ? p.norm_w[(int64_t)h * D + 8 * o.i16 + e] : 1.f;
+    ep.gate = (p.flags & GF_GATE) != 0;
+  }
 
   while (true) {
     const Cursor nxt = next_chunk<SNAP>(m, cur, b, T);
@@ -677,7 +752,8 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[bi][ks] = qn[bi][ks];
+      for (int ks = 0; ks < 4; ++ks)
+        qf[bi][ks] = (EPI && (p.flags & GF_SILU_Q)) ? silu8(qn[bi][ks]) : qn[bi][ks];
     {
       const OutLane o(ln.lane, w);
       const int i16 = o.i16, G = o.G;
@@ -698,7 +774,16 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
       inter_term(acc, STs + kq, qf, a_row);
       intra_block<FAST, 0>(acc, qf, Ks, Vs, kq, vq, i16, G, w, dc);
       if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 1, qn[1], o);
+      if constexpr (EPI) {
+        // (the scheduling barrier keeps the gate loads out of the products
+        // above, where their registers would be live)
+        __builtin_amdgcn_sched_barrier(0);
+        if (ep.gate) issue_gate_loads(p, h, cur, ep.gr, o);
+      }
       intra_block<FAST, 1>(acc, qf, Ks, Vs, kq, vq, i16, G, 7 - w, dc);
+      if constexpr (EPI) {
+        if (p.flags & GF_NORM) rms_rows(acc, p.eps);
+      }
     }
     __syncthreads();  // B: this chunk's K/V and S^T reads are done
     {
@@ -706,7 +791,7 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
       // it back as whole rows.
       const OutLane o(ln.lane, w);
       stage_rows(acc, Ks, o);
-      write_rows<SNAP, REV>(p, h, cur, Ks, o);
+      write_rows<SNAP, REV, EPI>(p, h, cur, Ks, o, &ep);
     }
     if (!nxt.valid) break;
     cur = nxt;
@@ -721,7 +806,10 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
 // snapshot point the segment's chunks end on.
 // MID: the output side closes a third barrier in the middle of each chunk
 // (the fused dk/dv loop), and the next chunk's tiles go out after it.
-template <bool SNAP, bool REV = false, bool MID = false>
+// EPI: the gated reading's SiLU on K and/or V (FwdArgs::flags), applied in
+// LDS to the rows this wave loaded, once they have landed: the next chunk's
+// tiles after this chunk's update (while the output waves finish it).
+template <bool SNAP, bool REV = false, bool MID = false, bool EPI = false>
 __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, Cursor cur,
                                            f32x16 (&S)[4], char *smem, const Decay &dc,
                                            const Lanes &ln) {
@@ -732,10 +820,25 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
   const int w = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane;
   const float l2 = dc.l2;
   int buf = 0;
+  // SiLU in place on this wave's rows 32 w .. 32 w + 31 of a K or V tile
+  // (elementwise, so the swizzle does not matter).
+  const auto silu_rows = [&](char *tile) {
+    const unsigned base = lds_u32(tile) + 32 * w * KV_ROW;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned a = base + 16 * (lane + 64 * i);
+      lds_st<u32x4>(a, silu8(lds_ld<u32x4>(a)));
+    }
+  };
+  const int silu_k = EPI ? (p.flags & GF_SILU_K) : 0, silu_v = EPI ? (p.flags & GF_SILU_V) : 0;
   dma_tile_rows<REV>(smem, p.k, p, h, cur, w, lane);
   dma_tile_rows<REV>(smem + LDS_K, p.v, p, h, cur, w, lane);
   write_st(STs, S, w, l32, g);
   vm_wait<0>();
+  if constexpr (EPI) {
+    if (silu_k) silu_rows(smem);
+    if (silu_v) silu_rows(smem + LDS_K);
+  }
 
   while (true) {
     const Cursor nxt = next_chunk<SNAP>(m, cur, b, T);
@@ -777,6 +880,13 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 #pragma unroll
       for (int k = 0; k < 8; ++k) issue_next(k);
     }
+    if constexpr (EPI) {
+      if (nxt.valid && (silu_k | silu_v)) {
+        vm_wait<0>();  // this wave's rows of the next tiles have landed
+        if (silu_k) silu_rows(Kn);
+        if (silu_v) silu_rows(Vn);
+      }
+    }
     __syncthreads();  // B: this chunk's K/V and S^T reads are done
     if (!nxt.valid) break;
     // (A new piece's state load sits in the same block as the S^T write that
@@ -798,7 +908,7 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 // backward pass).  Without it the kernel keeps the plain walk's registers.
 // REV (with SERVE): the views may also be time-reversed packed views (the
 // backward pass over packed sequences, SeqMap::rev_rs).
-template <bool SERVE, bool REV = false>
+template <bool SERVE, bool REV = false, bool EPI = false>
 __device__ __forceinline__ void chunk_workgroup(const FwdArgs &p, int bid, char *smem) {
   const Lanes ln;
   const SeqMap &m = p.m;
@@ -829,23 +939,24 @@ __device__ __forceinline__ void chunk_workgroup(const FwdArgs &p, int bid, char 
     issue_q_loads<REV>(p, h, cur, 0, qn[0], o);
     issue_q_loads<REV>(p, h, cur, 1, qn[1], o);
     if (dc.fast)
-      output_loop<true, SERVE, REV>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<true, SERVE, REV, EPI>(p, h, b, cur, qn, smem, dc, ln);
     else
-      output_loop<false, SERVE, REV>(p, h, b, cur, qn, smem, dc, ln);
+      output_loop<false, SERVE, REV, EPI>(p, h, b, cur, qn, smem, dc, ln);
   } else {
     f32x16 S[4];
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     load_state(S, s0, ln.w, ln.l32, ln.g);
-    state_loop<SERVE, REV>(p, h, b, cur, S, smem, dc, ln);
+    state_loop<SERVE, REV, false, EPI>(p, h, b, cur, S, smem, dc, ln);
   }
 }
 
-template <bool SERVE>
+// EPI: the gated reading's SiLU, normalisation and gate (FwdArgs::flags).
+template <bool SERVE, bool EPI = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_chunk_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-  chunk_workgroup<SERVE>(p, blockIdx.x, smem);
+  chunk_workgroup<SERVE, false, EPI>(p, blockIdx.x, smem);
 }
 
 // The backward's dv and dk output passes in one workgroup per (segment,

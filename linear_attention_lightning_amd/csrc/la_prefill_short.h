@@ -1,5 +1,4 @@
-// bf16 prefill on gfx950 MFMA with short chunks (32 or 64 tokens), d = 128,
-// and the optional SiLU / normalisation / gate around the attention.
+// bf16 prefill on gfx950 MFMA with short chunks (32 or 64 tokens), d = 128.
 //
 // The MiniMax-01 report pads its inputs to 32, 64, 128 or 256 tokens by
 // length (section 3.3.3, multi-level padding), so that short inputs do not
@@ -14,20 +13,9 @@
 // state), but one workgroup of 4 waves does both in turn: wave w owns query
 // rows 16w..16w+15 of a 64-token chunk (a 32-token chunk: rows 16(w&1).. and
 // features 64(w>>1)..) and state rows 32w..32w+31.  K and V come through
-// registers one chunk ahead (so the SiLU prologue can act on them before they
-// reach LDS), Q likewise; outputs are staged in LDS and written back as whole
-// rows at the start of the next chunk, behind its first barrier.
-//
-// Normalisation, SiLU and gate: the report names them around its attention
-// and leaves them out of its derivation (section 2.2.1); the reading here,
-// each part selected by a flag (FwdArgs::flags):
-//   SiLU on q, k, v as they are read (x / (1 + e^-x));
-//   RMS normalisation of every output row over the head's 128 channels,
-//     o / sqrt(mean(o^2) + eps), times a per-channel weight [H][128];
-//   an output gate o * sigmoid(g), g read like the output ([.., N, .., 128]).
-// The normalisation runs on the float32 accumulators (a row's 128 features
-// sit in 4 lanes of one wave with 64-token chunks); weight and gate are
-// applied to the staged row as it is written.
+// registers one chunk ahead, Q likewise; outputs are staged in LDS and
+// written back as whole rows at the start of the next chunk, behind its
+// first barrier.
 #pragma once
 
 #include "la_prefill_mfma.h"
@@ -67,22 +55,10 @@ __device__ __forceinline__ void short_load_q(u32x4 (&q)[4], const FwdArgs &p, in
     q[ks] = __builtin_nontemporal_load((const u32x4 *)(qrow + 32 * ks));
 }
 
-// Gate values of the rows this thread writes back (rows (it * 256 + t) / 16,
-// features 8 (t % 16) ..).
 template <int TS>
-__device__ __forceinline__ void short_load_gate(u32x4 (&gr)[TS / 16], const FwdArgs &p, int h,
-                                                const Cursor &c, int t) {
-  const int Lc = (int)(c.c1 - c.c0);
-  load_tile<NT_S, TS>(gr, (const bf16 *)p.gate + p.m.row_base<false>(h, c.j) + c.c0 * p.m.rs,
-                      p.m.rs, Lc, t);
-}
-
-// EPI: the normalisation and gate are compiled in (64-token chunks only).
-template <int TS, bool EPI>
 __global__ __launch_bounds__(NT_S) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_short_kernel(FwdArgs p) {
   static_assert(TS == 32 || TS == 64, "chunk of 32 or 64 tokens");
-  static_assert(!EPI || TS == 64, "the normalisation needs a row's 128 features in one wave");
   using LY = ShortLds<TS>;
   constexpr int PT = TS / 16;              // 16-byte pieces per thread of one tile
   constexpr int NJ = TS == 64 ? 8 : 4;     // 16-feature tiles of a wave's output
@@ -111,7 +87,6 @@ void prefill_short_kernel(FwdArgs p) {
     }
     return;
   }
-  const int flags = p.flags;
   const int qb = TS == 64 ? w : (w & 1);   // this wave's 16-row query block
   const int j0 = TS == 64 ? 0 : 4 * (w >> 1);
   const int row0 = 16 * qb + (lane & 15);  // this lane's query row in a chunk
@@ -125,21 +100,9 @@ void prefill_short_kernel(FwdArgs p) {
   u32x4 kr[PT], vr[PT], qf[4];
   short_load_kv<TS>(kr, vr, p, h, cur, tid);
   short_load_q(qf, p, h, cur, row0, lane >> 4);
-  if (flags & GF_SILU_K)
-#pragma unroll
-    for (int i = 0; i < PT; ++i) kr[i] = silu8(kr[i]);
-  if (flags & GF_SILU_V)
-#pragma unroll
-    for (int i = 0; i < PT; ++i) vr[i] = silu8(vr[i]);
   store_tile<NT_S, TS>(Ks, kr, tid);
   store_tile<NT_S, TS>(Vs, vr, tid);
   write_st(STs, S, w, l32, g);
-
-  // Write-back side of the epilogue: the gate of the chunk whose outputs are
-  // staged (loaded after that chunk's products, so that it is not live
-  // through them).
-  u32x4 gr[PT];
-  const bool wnorm = EPI && (flags & GF_NORM) && p.norm_w;
 
   // Writes the staged outputs of chunk c (rows (it * 256 + t) / 16, granule
   // t % 16) as whole rows, through a buffer whose range ends with the chunk's
@@ -154,25 +117,7 @@ void prefill_short_kernel(FwdArgs p) {
 #pragma unroll
     for (int it = 0; it < PT; ++it) {
       const int r = (it * NT_S + tid) >> 4;
-      u32x4 x = lds_ld<u32x4>(Ou + kv_off(r, 16 * c16));
-      if constexpr (EPI) {
-        // this thread's 8 channels of the weight (a small array, cached)
-        const float *wp = p.norm_w + (int64_t)h * D + 8 * c16;
-        const f32x4 w0 = wnorm ? *(const f32x4 *)wp : (f32x4){1.f, 1.f, 1.f, 1.f};
-        const f32x4 w1 = wnorm ? *(const f32x4 *)(wp + 4) : (f32x4){1.f, 1.f, 1.f, 1.f};
-        const float wt[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        const bf16x8 o8 = __builtin_bit_cast(bf16x8, x);
-        const bf16x8 g8 = __builtin_bit_cast(bf16x8, gr[it]);
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float gate = (flags & GF_GATE)
-                                 ? __builtin_amdgcn_rcpf(1.f + fast_exp2(-(float)g8[e] * kLog2e))
-                                 : 1.f;
-          y[e] = (float)o8[e] * wt[e] * gate;
-        }
-        x = __builtin_bit_cast(u32x4, cvt8(y));
-      }
+      const u32x4 x = lds_ld<u32x4>(Ou + kv_off(r, 16 * c16));
       __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, r * rsb + 16 * c16, 0, kCpolNT);
     }
   };
@@ -206,15 +151,13 @@ void prefill_short_kernel(FwdArgs p) {
       const float gL = fast_exp2((float)L * l2);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) S[nt] *= gL;
-      // (the epilogue's kernel takes the unpipelined update: fewer registers)
-      state_update<TS / 16, !EPI>(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lid);
+      state_update<TS / 16, true>(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lid);
       if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
     }
     // Outputs of query rows 16 qb + (0..15), features 16 (j0 + j) + 4 G + r.
     bf16x8 qv[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qv[ks] = as_bf16x8((flags & GF_SILU_Q) ? silu8(qf[ks]) : qf[ks]);
+    for (int ks = 0; ks < 4; ++ks) qv[ks] = as_bf16x8(qf[ks]);
     f32x4 acc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -252,29 +195,6 @@ void prefill_short_kernel(FwdArgs p) {
         acc[j] = mma16(tr_read8u(va, va + 16 * KV_ROW), pb, acc[j]);
       }
     }
-    if constexpr (EPI) {
-      if (flags & GF_NORM) {
-        // RMS over the row's 128 features: 32 in this lane, the rest in the
-        // lanes with the same i16 (G = 0..3).
-        float ss = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ss += acc[j][r] * acc[j][r];
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        const float inv = __builtin_amdgcn_rsqf(ss * (1.f / D) + p.eps);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] *= inv;
-      }
-    }
-
-    if constexpr (EPI) {
-      // (the scheduling barrier keeps these loads from being hoisted into the
-      // products above, where their registers would be live)
-      __builtin_amdgcn_sched_barrier(0);
-      if (flags & GF_GATE) short_load_gate<TS>(gr, p, h, cur, tid);
-    }
     __syncthreads();  // B: every read of this chunk's tiles, of S^T and of the staging is done
     // Stage the outputs (acc[j] register r: feature 16 (j0 + j) + 4 G + r of row `row`).
     {
@@ -291,12 +211,6 @@ void prefill_short_kernel(FwdArgs p) {
     if (new_piece)
       load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, w, l32, g);
     write_st(STs, S, w, l32, g);
-    if (flags & GF_SILU_K)
-#pragma unroll
-      for (int i = 0; i < PT; ++i) kr[i] = silu8(kr[i]);
-    if (flags & GF_SILU_V)
-#pragma unroll
-      for (int i = 0; i < PT; ++i) vr[i] = silu8(vr[i]);
     store_tile<NT_S, TS>(Ks, kr, tid);
     store_tile<NT_S, TS>(Vs, vr, tid);
 #pragma unroll

@@ -236,17 +236,13 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
         hipLaunchKernelGGL((la::mfma::local_state_kernel<false, false>), lgrid,
                            dim3(la::mfma::NT_LOCAL), 0, st, a);
     } else if (pl.chunk < la::mfma::T && !a.chdecay) {
-      // Short chunks (and the gated path): two 4-wave workgroups per CU.
-      const bool epi = (a.flags & (la::mfma::GF_NORM | la::mfma::GF_GATE)) != 0;
+      // Short chunks: two 4-wave workgroups per CU.
       if (pl.chunk == 32)
-        hipLaunchKernelGGL((la::mfma::prefill_short_kernel<32, false>), grid,
-                           dim3(la::mfma::NT_S), 0, st, a);
-      else if (epi)
-        hipLaunchKernelGGL((la::mfma::prefill_short_kernel<64, true>), grid,
-                           dim3(la::mfma::NT_S), 0, st, a);
+        hipLaunchKernelGGL((la::mfma::prefill_short_kernel<32>), grid, dim3(la::mfma::NT_S), 0,
+                           st, a);
       else
-        hipLaunchKernelGGL((la::mfma::prefill_short_kernel<64, false>), grid,
-                           dim3(la::mfma::NT_S), 0, st, a);
+        hipLaunchKernelGGL((la::mfma::prefill_short_kernel<64>), grid, dim3(la::mfma::NT_S), 0,
+                           st, a);
     } else if (a.chdecay) {
       // Heads whose smallest decay is at least 1/8 on MFMA, the others on
       // the vector-ALU kernel (same segments, same entering states).
@@ -256,6 +252,15 @@ void launch_phase(const la::FwdArgs &a, const Plan &pl, int d, la_dtype dt, hipS
       hipLaunchKernelGGL(la::mfma::chdecay_chunk_kernel, grid, dim3(la::mfma::NT), 0, st, am);
       hipLaunchKernelGGL((la::simt::prefill_chunk_kernel<bf16, 128, true>), grid,
                          dim3(la::simt::NT), 0, st, av);
+    } else if (a.flags) {
+      // The gated reading's parts compiled in (their own kernels, so that the
+      // plain path keeps its registers).
+      if (a.seg_len == 0)
+        hipLaunchKernelGGL((la::mfma::prefill_chunk_kernel<true, true>), grid, dim3(la::mfma::NT),
+                           0, st, a);
+      else
+        hipLaunchKernelGGL((la::mfma::prefill_chunk_kernel<false, true>), grid, dim3(la::mfma::NT),
+                           0, st, a);
     } else if (a.m.snap_iv > 0 || a.seg_len == 0 || a.m.rs < 0) {
       hipLaunchKernelGGL(la::mfma::prefill_chunk_kernel<true>, grid, dim3(la::mfma::NT), 0, st, a);
     } else {
@@ -446,6 +451,7 @@ struct Gated {
   const void *gate = nullptr;
   const float *norm_w = nullptr;
   float eps = 0.f;
+  bool entry = false;  // a gated entry point: always the three-phase plan
 };
 
 la_status check_gated(const Gated &gt, int d, la_dtype dt) {
@@ -479,7 +485,7 @@ la_status fwd_fixed(const void *q, const void *k, const void *v, const float *de
   if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
   if (!aligned16({q, k, v, out, init_state, final_state, workspace})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, true, false, block, true);
+  const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, !gt.entry, false, block, true);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
   if (N == 0 && !final_state) return LA_OK;
@@ -518,8 +524,8 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   if (!aligned16({q, k, v, out, init_states, final_states, workspace, snaps}))
     return LA_ERR_INVALID_ARG;
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
-  Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused, ch, block,
-                        short_ok);
+  Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused && !gt.entry,
+                        ch, block, short_ok);
   if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
   // Prefix snapshots are stored by the 128-token kernel; the segments (and
@@ -1308,9 +1314,15 @@ la_status lightning_attn_mixed_step(
   return sp != LA_OK ? sp : sd;
 }
 
+// The gated entry points run the 128-token kernel (the normalisation and
+// gate compiled into it) in the three-phase schedule.
+constexpr int kGatedBlock = 128;
+
 size_t lightning_attn_fwd_gated_workspace_size(int B, int H, int64_t N, int d, la_dtype dt,
                                                int64_t segment_tokens) {
-  return lightning_attn_fwd_workspace_size(B, H, N, d, 64, dt, segment_tokens);
+  if (B < 0 || N < 0 || check_common(H, d, kGatedBlock, dt, segment_tokens) != LA_OK) return 0;
+  if ((int64_t)B * H == 0) return 0;
+  return plan_fixed(B, H, N, d, dt, segment_tokens, false, false, kGatedBlock, true).ws_bytes;
 }
 
 la_status lightning_attn_fwd_gated(const void *q, const void *k, const void *v,
@@ -1325,16 +1337,23 @@ la_status lightning_attn_fwd_gated(const void *q, const void *k, const void *v,
   gt.gate = gate;
   gt.norm_w = norm_weight;
   gt.eps = eps;
+  gt.entry = true;
   if (B < 0 || N < 0 || H < 0) return LA_ERR_INVALID_ARG;
   const la_status st = check_gated(gt, d, dt);
   if (st != LA_OK) return st;
-  return fwd_fixed(q, k, v, decay, B, H, N, d, 64, dt, layout, init_state, out, final_state,
-                   segment_tokens, workspace, workspace_bytes, hip_stream, nullptr, gt);
+  return fwd_fixed(q, k, v, decay, B, H, N, d, kGatedBlock, dt, layout, init_state, out,
+                   final_state, segment_tokens, workspace, workspace_bytes, hip_stream, nullptr,
+                   gt);
 }
 
 size_t lightning_attn_fwd_varlen_gated_workspace_size(int num_seqs, int H, int64_t total_N, int d,
                                                       la_dtype dt, int64_t segment_tokens) {
-  return lightning_attn_fwd_varlen_workspace_size(num_seqs, H, total_N, d, 64, dt, segment_tokens);
+  if (num_seqs < 0 || total_N < 0 ||
+      check_common(H, d, kGatedBlock, dt, segment_tokens) != LA_OK)
+    return 0;
+  if ((int64_t)num_seqs * H == 0) return 0;
+  return plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, false, false, kGatedBlock, true)
+      .ws_bytes;
 }
 
 la_status lightning_attn_fwd_varlen_gated(const void *q, const void *k, const void *v,
@@ -1351,10 +1370,11 @@ la_status lightning_attn_fwd_varlen_gated(const void *q, const void *k, const vo
   gt.gate = gate;
   gt.norm_w = norm_weight;
   gt.eps = eps;
+  gt.entry = true;
   if (num_seqs < 0 || total_N < 0 || H < 0) return LA_ERR_INVALID_ARG;
   const la_status st = check_gated(gt, d, dt);
   if (st != LA_OK) return st;
-  return fwd_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, 64, dt, layout,
+  return fwd_varlen(q, k, v, decay, cu_seqlens, num_seqs, H, total_N, d, kGatedBlock, dt, layout,
                     init_states, out, final_states, segment_tokens, workspace, workspace_bytes,
                     hip_stream, 0, nullptr, nullptr, gt);
 }

@@ -211,10 +211,12 @@ def test_gated_flags(flags, seg):
     assert eo <= TOL and ef <= TOL, (eo, ef)
 
 
+@pytest.mark.parametrize("seg", [200, la.LA_SEGMENT_PER_SEQUENCE])
 @pytest.mark.parametrize("token_major", [False, True])
-def test_gated_varlen(token_major):
+def test_gated_varlen(token_major, seg):
     """Packed sequences (empty ones included) with every part of the reading,
-    against the oracle run on each sequence."""
+    against the oracle run on each sequence; segments cut inside sequences,
+    or one segment per sequence."""
     torch = torch_mod()
     lens = [300, 0, 1, 129, 1024, 5, 0, 640]
     H, d = 3, 128
@@ -232,7 +234,7 @@ def test_gated_varlen(token_major):
     out, fin = la.lightning_attn_fwd_varlen_gated(tq, tk, tv, dev(lam, False), dev(cu, False),
                                                   ALL, gate=tg, norm_weight=dev(wgt, False),
                                                   layout=layout, init_states=dev(init, False),
-                                                  segment_tokens=200)
+                                                  segment_tokens=seg)
     torch.cuda.synchronize()
     if token_major:
         out = out.transpose(0, 1)
@@ -249,6 +251,23 @@ def test_gated_varlen(token_major):
     eo, ef = rel_err(ho, o_ref), rel_err(hf, f_ref)
     say("   err out %.3e state %.3e" % (eo, ef))
     assert eo <= TOL and ef <= TOL, (eo, ef)
+
+
+@pytest.mark.parametrize("seg", [0, 256])
+def test_gated_nothing_selected_is_the_plain_prefill(seg):
+    """With no part selected the gated entry point runs the plain prefill:
+    bit for bit lightning_attn_fwd at block 128."""
+    torch = torch_mod()
+    B, H, N, d = 1, len(LAMS), 1000, 128
+    q, k, v, g = gated_inputs((B, H, N, d), 870)
+    lam = np.asarray(LAMS, np.float32)
+    init = inputs.host_state((B, H, d, d), 871)
+    o1, f1 = la.lightning_attn_fwd_gated(dev(q), dev(k), dev(v), dev(lam, False), 0,
+                                         init_state=dev(init, False), segment_tokens=seg)
+    o2, f2 = la.lightning_attn_fwd(dev(q), dev(k), dev(v), dev(lam, False), block=128,
+                                   init_state=dev(init, False), segment_tokens=seg)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
 def test_gated_rejects_bad_arguments():

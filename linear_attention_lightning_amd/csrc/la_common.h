@@ -96,6 +96,7 @@ struct SeqMap {
 struct Cursor {
   int64_t c0, c1;
   int64_t pend;     // end of the current piece: min(b, seq_end)
+  int64_t seq_start;  // start(j)
   int64_t seq_end;  // start(j + 1)
   int64_t snap;     // first snapshot point of sequence j after c0 (INT64_MAX: none)
   int j;
@@ -116,13 +117,12 @@ __device__ __forceinline__ Cursor first_chunk(const SeqMap &m, int64_t a, int64_
   Cursor c;
   c.valid = a < b;
   c.j = c.valid ? m.seq_of(a) : 0;
+  c.seq_start = c.valid ? m.start(c.j) : a;
   c.seq_end = c.valid ? m.start(c.j + 1) : b;
   c.pend = c.seq_end < b ? c.seq_end : b;
   c.snap = kNoSnap;
-  if (SNAP && m.snap_iv > 0 && c.valid) {
-    const int64_t s0 = m.start(c.j);
-    c.snap = s0 + ((a - s0) / m.snap_iv + 1) * m.snap_iv;
-  }
+  if (SNAP && m.snap_iv > 0 && c.valid)
+    c.snap = c.seq_start + ((a - c.seq_start) / m.snap_iv + 1) * m.snap_iv;
   c.c0 = a;
   c.c1 = SNAP ? min3(a + T, c.pend, c.snap) : (a + T < c.pend ? a + T : c.pend);
   return c;
@@ -138,6 +138,7 @@ __device__ __forceinline__ Cursor next_chunk(const SeqMap &m, const Cursor &c, i
   }
   if (n.c0 >= c.pend) {  // the piece ended at a sequence end: next sequence
     n.j = m.seq_of(n.c0);
+    n.seq_start = n.c0;  // start(n.j): seq_of skips empty sequences
     n.seq_end = m.start(n.j + 1);
     n.pend = n.seq_end < b ? n.seq_end : b;
     if (SNAP) n.snap = m.snap_iv > 0 ? n.c0 + m.snap_iv : kNoSnap;  // start(n.j) == n.c0
@@ -147,6 +148,16 @@ __device__ __forceinline__ Cursor next_chunk(const SeqMap &m, const Cursor &c, i
   n.c1 = SNAP ? min3(n.c0 + T, n.pend, n.snap) : (n.c0 + T < n.pend ? n.c0 + T : n.pend);
   n.valid = true;
   return n;
+}
+
+// SeqMap::row_base(h, c.j) from the bounds the cursor already holds: no
+// load of the sequence table (in a chunk loop such a scalar load's wait
+// would also wait for every LDS access in flight).
+template <bool REV>
+__device__ __forceinline__ int64_t chunk_row_base(const SeqMap &m, int h, const Cursor &c) {
+  int64_t r = (int64_t)h * m.head_stride + (int64_t)c.j * m.seq_extra;
+  if (REV && m.rev_rs) r += (c.seq_start + c.seq_end - 1) * m.rev_rs;
+  return r;
 }
 
 // Row of `snaps` that receives the state after chunk c (which ends at the

@@ -461,7 +461,7 @@ __device__ __forceinline__ void issue_q_loads(const FwdArgs &p, int h, const Cur
   // Rows past the chunk's end read its last row: their outputs are never stored.
   const int Lc = (int)(c.c1 - c.c0);
   const int row = 16 * o.qblock(bi) + o.i16;
-  const bf16 *qrow = (const bf16 *)p.q + p.m.row_base<REV>(h, c.j) +
+  const bf16 *qrow = (const bf16 *)p.q + chunk_row_base<REV>(p.m, h, c) +
                      (c.c0 + (row < Lc ? row : Lc - 1)) * p.m.rs + 8 * o.G;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -512,7 +512,7 @@ template <bool REV = false>
 __device__ __forceinline__ void dma_tile_quad(char *tile, const void *src, const FwdArgs &p, int h,
                                               const Cursor &c, int u, int lane, int k) {
   const int Lc = (int)(c.c1 - c.c0);
-  const bf16 *base = (const bf16 *)src + p.m.row_base<REV>(h, c.j) + c.c0 * p.m.rs;
+  const bf16 *base = (const bf16 *)src + chunk_row_base<REV>(p.m, h, c) + c.c0 * p.m.rs;
   const int sub = lane >> 4, pg = lane & 15;
   const int r = 32 * u + 4 * k + sub;
   const int rr = r < Lc ? r : Lc - 1;
@@ -563,7 +563,7 @@ __device__ __forceinline__ void write_rows(const FwdArgs &p, int h, const Cursor
   const int flip = (NEG && rsb < 0) ? L - 1 : 0;
   const int span = (NEG && rsb < 0) ? -rsb : rsb;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (bf16 *)p.out + p.m.row_base<REV>(h, c.j) + (c.c0 + flip) * p.m.rs, 0, (L - 1) * span + D * 2,
+      (bf16 *)p.out + chunk_row_base<REV>(p.m, h, c) + (c.c0 + flip) * p.m.rs, 0, (L - 1) * span + D * 2,
       kRawBufferWord3);
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {

@@ -301,6 +301,56 @@ def bench_backward(la, inputs, steps, warmup):
                                                     4)}}
 
 
+def bench_backward_varlen(la, inputs, steps, warmup):
+    """Packed backward (lightning_attn_bwd_varlen) over the 65536-token
+    packed workload at 64 heads (lognormal lengths, as the packed prefill),
+    with final-state gradients and initial states, plain and with the
+    forward's saved states: ms per step; algorithmic bytes as the
+    fixed-length backward's."""
+    import torch
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["layer_h64_varlen64k"]
+    H, total, d, block = w["H"], w["total"], w["d"], w["block"]
+    lens = inputs.varlen_lengths(total=total, seed=w["seed"])
+    S = len(lens)
+    cu = torch.from_numpy(inputs.cu_seqlens(lens)).to(dev)
+    q, k, v = inputs.device_qkv((H, total, d), w["seed"], "bf16", device=dev)
+    do, _, _ = inputs.device_qkv((H, total, d), w["seed"] + 7, "bf16", device=dev)
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    init = inputs.device_state((S, H, d, d), w["seed"] + 8, device=dev)
+    dfin = inputs.device_state((S, H, d, d), w["seed"] + 9, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dinit = torch.empty_like(init)
+    nws = la.lightning_attn_bwd_varlen_workspace_size(S, H, total, d, block)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        la.lightning_attn_bwd_varlen(q, k, v, decay, do, cu, block=block, dfinals=dfin,
+                                     init_states=init, dq=dq, dk=dk, dv=dv, dinits=dinit,
+                                     workspace=ws)
+
+    ms = time_steps(step, steps, warmup, torch.cuda.current_stream(dev))
+    _, _, saved = la.lightning_attn_fwd_varlen_save(q, k, v, decay, cu, block=block,
+                                                    init_states=init, workspace=ws)
+
+    def step_saved():
+        la.lightning_attn_bwd_varlen_saved(q, k, v, decay, do, cu, saved, block=block,
+                                           dfinals=dfin, init_states=init, dq=dq, dk=dk, dv=dv,
+                                           dinits=dinit, workspace=ws)
+
+    ms_saved = time_steps(step_saved, steps, warmup, torch.cuda.current_stream(dev))
+    byt = 7 * H * total * d * 2 + 3 * S * H * d * d * 4
+    return {"workload": "layer_h64_varlen64k", "pass": "packed backward (dq, dk, dv, dinit)",
+            "num_seqs": S, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(total / (ms * 1e-3), 1),
+            "hbm_gbs_algorithmic": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "with_saved_states": {"ms_per_step": round(ms_saved, 4),
+                                  "tokens_per_s": round(total / (ms_saved * 1e-3), 1),
+                                  "hbm_frac": round(byt / (ms_saved * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                    4)}}
+
+
 def bench_chdecay(la, inputs, steps, warmup):
     """Channel-wise decay prefill at the headline shape (B=1 H=64 N=32768
     d=128 bf16, per-channel decays from inputs.chdecay_schedule): ms per step,
@@ -633,8 +683,9 @@ def main():
     ap.add_argument("--trace", action="store_true",
                     help="also report the time of every headline step (warm-up and timed), "
                          "from HIP events between the steps")
-    ap.add_argument("--leg", choices=["backward", "serving", "snapshots", "chdecay", "million",
-                                      "varlen", "decode", "short_gated"], default=None,
+    ap.add_argument("--leg", choices=["backward", "backward_varlen", "serving", "snapshots",
+                                      "chdecay", "million", "varlen", "decode", "short_gated"],
+                    default=None,
                     help="time only this extra workload and print its JSON object (for "
                          "profiling it on its own); the headline line is not printed")
     args = ap.parse_args()
@@ -651,6 +702,7 @@ def main():
     la.load_library()
     if args.leg:
         legs = {"backward": lambda: bench_backward(la, inputs, args.steps, 20),
+                "backward_varlen": lambda: bench_backward_varlen(la, inputs, args.steps, 5),
                 "serving": lambda: bench_serving(la, inputs, P=50),
                 "snapshots": lambda: bench_snapshots(la, inputs, args.steps, 2),
                 "chdecay": lambda: bench_chdecay(la, inputs, args.steps, 20),
@@ -735,6 +787,9 @@ def main():
         res["token_major"] = bench_token_major(la, inputs, steps=args.steps, warmup=args.warmup)
         torch.cuda.empty_cache()
         res["backward"] = bench_backward(la, inputs, steps=args.steps, warmup=20)
+        torch.cuda.empty_cache()
+        res["backward_varlen"] = bench_backward_varlen(la, inputs, steps=max(5, args.steps // 2),
+                                                       warmup=5)
         torch.cuda.empty_cache()
         res["chdecay"] = bench_chdecay(la, inputs, steps=args.steps, warmup=20)
         torch.cuda.empty_cache()

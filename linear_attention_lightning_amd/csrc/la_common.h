@@ -221,6 +221,9 @@ struct FwdArgs {
   const void *gate = nullptr;      // gate input, laid out like out (GF_GATE)
   const float *norm_w = nullptr;   // [H][d] normalisation weight, or nullptr (ones)
   float eps = 0.f;                 // normalisation epsilon
+  int state_scale = 0;  // backward's dv pass (fused dv/dk kernel and scan): bit 0, an initial
+                        // state is read as init / lambda_h; bit 1, a final state is written
+                        // as lambda_h times the state
 };
 
 // The channel-wise MFMA output pass writes the decay inside a 64-token

@@ -869,7 +869,18 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
         state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane);
       else
         state_update(S, Ks, Vs, L, L - 1, l2, dc.fast, dc.tail, w, lane, issue_next);
-      if (seq_done && p.fin) store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
+      if (seq_done && p.fin) {
+        if constexpr (MID) {
+          // the backward's dv pass may write lambda times its final state
+          // (the walk then starts a new sequence, whose state is loaded)
+          if (p.state_scale & 2) {
+            const float f = p.decay[h];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) S[nt] *= f;
+          }
+        }
+        store_state(p.fin + ((int64_t)cur.j * H + h) * DD, S, w, l32, g);
+      }
       if (snap_here) store_state(p.snaps + (snap_row(m, p.snap_off, cur) * H + h) * DD, S, w, l32, g);
     } else if constexpr (!MID) {
 #pragma unroll
@@ -891,8 +902,16 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
     if (!nxt.valid) break;
     // (A new piece's state load sits in the same block as the S^T write that
     // consumes it, so no path reaches the next chunk with those loads open.)
-    if (new_piece)
+    if (new_piece) {
       load_state(S, p.init ? p.init + ((int64_t)nxt.j * H + h) * DD : nullptr, w, l32, g);
+      if constexpr (MID) {
+        if (p.state_scale & 1) {
+          const float f = 1.f / p.decay[h];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) S[nt] *= f;
+        }
+      }
+    }
     write_st(STs, S, w, l32, g);
     vm_wait<0>();  // the next chunk's tiles have landed
     cur = nxt;
@@ -1068,12 +1087,16 @@ __device__ __forceinline__ void dkdv_workgroup(const FwdArgs &pv, const FwdArgs 
   segment_bounds(pv, s, &a, &b);
   const int64_t DD = (int64_t)D * D;
   const Cursor cur = first_chunk<true>(m, a, b, T);
+  // pv.state_scale: the initial state enters as init / lambda, the final
+  // state leaves as lambda times the state.
+  const float init_f = (pv.state_scale & 1) ? 1.f / pv.decay[h] : 1.f;
+  const float fin_f = (pv.state_scale & 2) ? pv.decay[h] : 1.f;
   if (!cur.valid) {
     // One segment per sequence: an empty sequence keeps its initial state.
     if (pv.seg_len == 0 && pv.fin) {
       float *dst = pv.fin + ((int64_t)s * H + h) * DD;
       const float *src = pv.init ? pv.init + ((int64_t)s * H + h) * DD : nullptr;
-      for (int e = threadIdx.x; e < D * D; e += NT) dst[e] = src ? src[e] : 0.f;
+      for (int e = threadIdx.x; e < D * D; e += NT) dst[e] = src ? fin_f * (init_f * src[e]) : 0.f;
     }
     return;
   }
@@ -1091,6 +1114,9 @@ __device__ __forceinline__ void dkdv_workgroup(const FwdArgs &pv, const FwdArgs 
     const float *s0 = pv.ws ? pv.ws + ((int64_t)s * pv.r_split * H + h) * DD
                             : (pv.init ? pv.init + ((int64_t)cur.j * H + h) * DD : nullptr);
     load_state(S, s0, ln.w, ln.l32, ln.g);
+    if (!pv.ws && (pv.state_scale & 1))  // (the scan's entering states are already scaled)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) S[nt] *= init_f;
     state_loop<true, REV, true>(pv, h, b, cur, S, smem, dc, ln);
   }
 }

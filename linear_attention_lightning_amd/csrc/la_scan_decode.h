@@ -30,6 +30,7 @@ struct ScanArgs {
   int r_split;   // pieces per segment of the local-state pass: 1, 2, 4, 8 or 16
   int C;         // chunk length of the local-state pass
   const float *chdecay;  // [H][d] per-channel decays, or nullptr (scalar decay)
+  int state_scale;       // as FwdArgs::state_scale (0 unless set)
 };
 
 // What the scan needs of segment s, computed once per workgroup.
@@ -104,9 +105,11 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
   } else {
     log2lam = log2f(p.decay[h]);
   }
+  // state_scale bit 0: initial states enter as init / lambda_h.
+  const float init_f = (p.state_scale & 1) ? 1.f / p.decay[h] : 1.f;
   auto init4 = [&](int j) -> f32x4 {
     if (!p.init || j < 0) return (f32x4){0.f, 0.f, 0.f, 0.f};
-    return *(const f32x4 *)(p.init + ((int64_t)j * H + h) * DD + e);
+    return init_f * *(const f32x4 *)(p.init + ((int64_t)j * H + h) * DD + e);
   };
   f32x4 carry = {0.f, 0.f, 0.f, 0.f};
   for (int sb = 0; sb < p.nseg; sb += MAXS) {
@@ -154,9 +157,11 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ScanArgs p) {
     }
   }
   if (p.fin && mine) {
+    // (bit 1: final states leave as lambda_h times the state)
+    const float fin_f = (p.state_scale & 2) ? p.decay[h] : 1.f;
     for (int j = 0; j < m.num_seqs; ++j)
       if (m.start(j) == m.start(j + 1))
-        *(f32x4 *)(p.fin + ((int64_t)j * H + h) * DD + e) = init4(j);
+        *(f32x4 *)(p.fin + ((int64_t)j * H + h) * DD + e) = fin_f * init4(j);
   }
 }
 

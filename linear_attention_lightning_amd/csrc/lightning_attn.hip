@@ -347,6 +347,7 @@ la_status run_fwd(const la::FwdArgs &base, const Plan &pl, int d, la_dtype dt, b
     s.r_split = pl.r_split;
     s.C = use_mfma(d, dt, a.chdecay != nullptr) ? la::mfma::C_LOCAL : la::simt::T;
     s.chdecay = a.chdecay;
+    s.state_scale = a.state_scale;
     dim3 grid((unsigned)H, (unsigned)ceil_div((int64_t)d * d, 1024));
     switch (pl.r_split) {
       case 16: hipLaunchKernelGGL(la::segment_scan_kernel<16>, grid, dim3(256), 0, st, s); break;
@@ -736,11 +737,12 @@ la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dt
   if (init)
     hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, init, 1, H, d, decay,
                        false, initT);
-  if (dfinal) {
+  // (The fused pass takes dS_fin itself and applies 1 / lambda as it reads
+  // it, and lambda as it writes d init: no separate scaling launches.)
+  if (dfinal && !fused_dkdv) {
     hipLaunchKernelGGL(la::bwd_scale_kernel, sgrid, dim3(256), 0, s, dfinal, decay, H, d, g);
-    if (!fused_dkdv)
-      hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, dfinal, 1, H, d,
-                         decay, true, gT);
+    hipLaunchKernelGGL(la::transpose_states_kernel, tgrid, dim3(256), 0, s, dfinal, 1, H, d,
+                       decay, true, gT);
   }
   // dq: causal, from S_init^T.  Its state is S_t^T, so with the forward's
   // saved segment entering states (transposed) only its output pass runs.
@@ -761,7 +763,10 @@ la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dt
   // so with segments its entering states are the dv pass's (left in the
   // workspace by the scan) transposed: only the dv pass runs the local-state
   // pass and the scan.
-  la::FwdArgs av = args(k, q, dout, dv, dfinal ? g : nullptr, dinit ? fin_dv : nullptr, true);
+  la::FwdArgs av = fused_dkdv ? args(k, q, dout, dv, dfinal, dinit, true)
+                              : args(k, q, dout, dv, dfinal ? g : nullptr, dinit ? fin_dv : nullptr,
+                                     true);
+  if (fused_dkdv) av.state_scale = 3;
   la::FwdArgs ak = args(v, dout, q, dk, dfinal ? gT : nullptr, nullptr, true);
   if (r == LA_OK) r = run_fwd(av, pl, d, dt, has_empty, s, nullptr, /*out_pass=*/false);
   if (r == LA_OK) {
@@ -794,7 +799,7 @@ la_status bwd_core(const ArgFn &args, const Plan &pl, int S, int H, int d, la_dt
     }
     r = launch_status();
   }
-  if (r == LA_OK && dinit) {
+  if (r == LA_OK && dinit && !fused_dkdv) {
     hipLaunchKernelGGL(la::bwd_dinit_kernel, sgrid, dim3(256), 0, s, fin_dv, decay, H, d, true,
                        dinit);
     r = launch_status();

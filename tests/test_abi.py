@@ -293,3 +293,25 @@ def test_decode_rejects_bad_arguments(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         la.load_library(str(tmp_path / "missing.so"))
+
+
+def test_header_is_c99_and_a_c_caller_links(tmp_path):
+    """The public header compiles as strict C99, and a plain C program
+    (tests/c_abi_check.c) links against the library and gets the documented
+    results from the calls that need no GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    subprocess.run([gcc, "-x", "c", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-fsyntax-only", HEADER], check=True)
+    exe = str(tmp_path / "c_abi_check")
+    libdir = os.path.dirname(la.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                    os.path.join(ROOT, "include"), "-o", exe,
+                    os.path.join(ROOT, "tests", "c_abi_check.c"), "-L", libdir,
+                    "-l:" + os.path.basename(la.LIB_PATH), "-Wl,-rpath," + libdir], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 failure(s)" in r.stdout

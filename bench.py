@@ -9,7 +9,9 @@ HIP events on the stream the library launches on.  Prints ONE JSON line:
 the headline tokens/s, TFLOP/s and fraction of the bf16 MFMA peak, the HBM
 roofline of the step, the CPU oracle timed on a bounded sample, and (unless
 --no-extras) the decode, packed varlen, million-token, token-major, backward,
-prefix-snapshot and mixed serving-step workloads.
+channel-wise, prefix-snapshot, short-chunk/gated and mixed serving-step
+workloads, and last the headline step re-timed after all of them
+(steady_state: the settled clock, with the per-step median and minimum).
 """
 import argparse
 import hashlib
@@ -145,6 +147,44 @@ def bench_prefill(la, inputs, B, H, N, d, block, seed, steps, warmup, phases=Fal
         phase_ms = [sum(row[j].elapsed_time(row[j + 1]) for row in evs.values()) / len(evs)
                     for j in range(3)]
     return ms, phase_ms, (q, k, v, decay, out, fin)
+
+
+STEADY_WARMUP = 60
+
+
+def bench_steady(la, inputs, w, steps):
+    """The headline step again at the end of the run, after STEADY_WARMUP
+    warm-up steps: past the clock transient that follows the start of
+    sustained work (it recurs after the light serving legs, so the warm-up is
+    its own, not --warmup).  The same number of timed steps as the headline,
+    with the phases sampled the same way; then as many steps again, each
+    between two HIP events, for the per-step median and minimum (the event
+    records between steps leave short gaps of their own, so those come from a
+    loop of their own)."""
+    warmup = STEADY_WARMUP
+    B, H, N, d, block = w["B"], w["H"], w["N"], w["d"], w["block"]
+    ms, phase_ms, tensors = bench_prefill(la, inputs, B, H, N, d, block, w["seed"], steps,
+                                          warmup, phases=True)
+    del tensors
+    trace = []
+    bench_prefill(la, inputs, B, H, N, d, block, w["seed"], steps, 0, trace=trace)
+    per_step = sorted(trace)
+    alg = prefill_bytes(B, H, N, d)
+    median = per_step[len(per_step) // 2] if len(per_step) % 2 else \
+        0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
+    return {"workload": "layer_h64_n32k", "when": "after every other leg",
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+            "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "chunk_kernel_us": round(phase_ms[2] * 1e3, 1),
+            "chunk_kernel_frac": round(alg / (phase_ms[2] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "local_state_us": round(phase_ms[0] * 1e3, 1),
+            "scan_us": round(phase_ms[1] * 1e3, 1),
+            "per_step_ms_median": round(median * 1e-3, 4),
+            "per_step_ms_min": round(per_step[0] * 1e-3, 4),
+            "note": "the headline step re-timed at the end of the run after its own "
+                    "warm-up; value and roofline above are the first measurement, straight "
+                    "after start-up with --warmup steps"}
 
 
 def bench_token_major(la, inputs, steps, warmup):
@@ -668,11 +708,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # After start-up the GPU's clocks go through a transient of a few tens of
-    # milliseconds of back-to-back work (the chunk kernel measured 400 us in
-    # its first launches, up to 470 us a few steps later, and a steady 407-412
-    # us from about the 30th step on); the default warm-up covers it, so the
-    # timed steps measure the settled state.
+    # After start-up the GPU's clock goes through a transient under
+    # back-to-back work: the chunk kernel takes about 370 us in its first
+    # launches, up to 530 us a few steps later, and recovers to 380-390 us
+    # over the following tens of launches.  The default warm-up covers it;
+    # with a short one (say 5 steps) the timed steps fall into the slow part,
+    # and the steady_state object (the same step at the end of the run, after
+    # a warm-up of its own) shows the settled figure beside it.
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
@@ -800,6 +842,8 @@ def main():
         res["serving"] = bench_serving(la, inputs, P=50)
         torch.cuda.empty_cache()
         res["serving_long"] = bench_serving(la, inputs, P=2048)
+        torch.cuda.empty_cache()
+        res["steady_state"] = bench_steady(la, inputs, w, args.steps)
     print(json.dumps(res), flush=True)
 
 

@@ -18,8 +18,10 @@
  * ones), section 3.3.1-3.3.2 (fused prefill front end; fused decode state
  * update; prefill and decode as separate kernels); K3 reading notes
  * (cutenote.app), "position decay term" and "CP for linear attention" (any
- * chunking gives the same result).  Normalisation, SiLU and the output gate
- * are outside this library (the report leaves them out of the derivation).
+ * chunking gives the same result).  The report leaves normalisation, SiLU
+ * and the output gate out of the derivation; the plain entry points compute
+ * the recurrence alone, and lightning_attn_fwd_gated adds one stated reading
+ * of those steps around it.
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers owned by the caller.  The library
@@ -50,10 +52,15 @@
  *     a float32 state (the state and the masked scores are rounded to bf16 as
  *     MFMA operands); float32 inputs run in float32 throughout.
  *   - Errors: arguments are validated before anything is launched; a failed
- *     validation launches nothing and leaves every buffer untouched.  After
- *     the launches, a HIP launch error maps to LA_ERR_HIP.  Faults inside a
- *     kernel surface at the caller's next synchronisation, as usual for HIP.
- *     No C++ exception crosses this interface.
+ *     validation launches nothing and leaves every buffer untouched.  Sizes
+ *     beyond what one launch can hold are LA_ERR_UNSUPPORTED: more than 2^40
+ *     tokens, a plan with more than 2^23 - 1 (segment, head) pairs (a HIP
+ *     launch holds at most 2^32 - 1 work-items; the output pass runs 512
+ *     threads per pair), or a decode step over more than 2^24 - 1
+ *     (sequence, head) pairs.  After the launches, a HIP launch error maps to
+ *     LA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as usual for HIP.  No C++ exception crosses this
+ *     interface.
  */
 #ifndef LIGHTNING_ATTN_H
 #define LIGHTNING_ATTN_H

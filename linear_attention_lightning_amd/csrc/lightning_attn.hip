@@ -74,8 +74,8 @@ size_t fused_ws_bytes(int64_t nseg, int H, int d) {
 // default.  The single-pass kernel (hand-offs between segments through the
 // workspace, K/V re-reads from the Infinity Cache) moves a third less HBM
 // traffic but serialises each workgroup's local-state pass, hand-off and
-// outputs; on MI355X it measured level with the default at its best segment
-// length (0.70 ms at B1 H64 N32768), so it is opt-in:
+// outputs; on MI355X it measured slower than the default (604 against 541 us
+// per step at B1 H64 N32768 with 8192-token segments), so it is opt-in:
 // LIGHTNING_ATTN_PREFILL=fused selects it (MFMA path only), =phased forces
 // the default.  Results agree up to rounding.
 bool want_fused(int H, int d, la_dtype dt, bool ch = false) {
@@ -120,6 +120,17 @@ int pieces(int64_t seg, int d, la_dtype dt, bool ch = false) {
   int n = r >= 4 ? 4 : r >= 2 ? 2 : 1;
   while (n < 16 && (int64_t)n * 2048 < seg) n *= 2;
   return n;
+}
+
+// A launch holds at most 2^32 - 1 work-items (workgroups times their
+// threads).  The widest grids of a plan: one workgroup of up to 512 threads
+// per (segment, head) in the output pass, and r_split workgroups of 256
+// threads per (segment, head) in the local-state pass.  Plans beyond that are
+// refused before anything is launched.
+bool plan_fits(const Plan &p, int H) {
+  const int64_t groups = p.nseg * (int64_t)H;
+  const int64_t lim = (int64_t)0xffffffff;
+  return groups <= lim / 512 && groups <= lim / 256 / (p.r_split > 0 ? p.r_split : 1);
 }
 
 size_t phased_ws_bytes(const Plan &p, int H, int d) {
@@ -487,7 +498,7 @@ la_status fwd_fixed(const void *q, const void *k, const void *v, const float *de
   if (!aligned16({q, k, v, out, init_state, final_state, workspace})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, !gt.entry, false, block, true);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (!plan_fits(pl, H)) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
   if (N == 0 && !final_state) return LA_OK;
 
@@ -527,7 +538,7 @@ la_status prep_varlen(const void *q, const void *k, const void *v, const float *
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, allow_fused && !gt.entry,
                         ch, block, short_ok);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (!plan_fits(pl, H)) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
   // Prefix snapshots are stored by the 128-token kernel; the segments (and
   // so the workspace) stay those of the size query for the same block.
@@ -599,7 +610,7 @@ la_status check_decode(const void *q, const void *k, const void *v, const float 
   if ((int64_t)B * H == 0) return LA_OK;
   if (!q || !k || !v || !decay || !state || !out) return LA_ERR_INVALID_ARG;
   if (!aligned16({q, k, v, state, out})) return LA_ERR_INVALID_ARG;
-  if ((int64_t)B * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > (int64_t)0xffffffff / 256) return LA_ERR_UNSUPPORTED;  // grid x 256
   return LA_OK;
 }
 
@@ -651,7 +662,7 @@ la_status fwd_chdecay(const void *q, const void *k, const void *v, const float *
   if (!aligned16({q, k, v, out, init_state, final_state, workspace})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false, /*ch=*/true);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (!plan_fits(pl, H)) return LA_ERR_UNSUPPORTED;
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return LA_ERR_WORKSPACE;
   if (N == 0 && !final_state) return LA_OK;
   la::FwdArgs a = fixed_args(q, k, v, out, nullptr, B, H, N, d, dt, layout, init_state,
@@ -824,7 +835,7 @@ la_status bwd_fixed(const void *q, const void *k, const void *v, const float *de
     return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (!plan_fits(pl, H)) return LA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < bwd_ws_bytes(pl, B, H, d)) return LA_ERR_WORKSPACE;
   if (with_saved && saved_bytes < saved_states_bytes(pl, H, d)) return LA_ERR_INVALID_ARG;
   if (with_saved && saved_states_bytes(pl, H, d) > 0 && !saved) return LA_ERR_INVALID_ARG;
@@ -856,7 +867,7 @@ la_status bwd_varlen(const void *q, const void *k, const void *v, const float *d
     return LA_ERR_INVALID_ARG;
   if (total_N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_varlen(num_seqs, H, total_N, d, dt, segment_tokens, /*allow_fused=*/false);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (!plan_fits(pl, H)) return LA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < bwd_ws_bytes(pl, num_seqs, H, d)) return LA_ERR_WORKSPACE;
   if (with_saved && saved_bytes < saved_states_bytes(pl, H, d)) return LA_ERR_INVALID_ARG;
   if (with_saved && saved_states_bytes(pl, H, d) > 0 && !saved) return LA_ERR_INVALID_ARG;
@@ -921,7 +932,7 @@ la_status fwd_save(const void *q, const void *k, const void *v, const float *dec
   if (!aligned16({q, k, v, out, init_state, final_state, workspace})) return LA_ERR_INVALID_ARG;
   if ((int64_t)B * N > ((int64_t)1 << 40)) return LA_ERR_UNSUPPORTED;
   const Plan pl = plan_fixed(B, H, N, d, dt, segment_tokens, /*allow_fused=*/false);
-  if (pl.nseg * H > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+  if (!plan_fits(pl, H)) return LA_ERR_UNSUPPORTED;
   const size_t need = saved_states_bytes(pl, H, d);
   if (saved_bytes < need || (need > 0 && !saved) || !aligned16({saved}))
     return LA_ERR_INVALID_ARG;

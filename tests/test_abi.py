@@ -115,6 +115,29 @@ def test_fwd_workspace_checks(lib):
     assert lib.lightning_attn_fwd_workspace_size(1, 2, 1000, 96, 64, FP32, 256) == 0
 
 
+def test_launch_size_limits(lib):
+    # A plan with more (segment, head) pairs than one launch can hold
+    # (2^23 - 1 workgroups of 512 threads) is refused before anything runs;
+    # one segment per token of a 2^20-token sequence on 8 or 64 heads is over.
+    assert fwd(lib, H=8, N=1 << 20, seg=1, ws=DUMMY, wsb=1 << 62) == UNSUPPORTED
+    assert fwd(lib, H=64, N=1 << 17, seg=1, ws=DUMMY, wsb=1 << 62) == UNSUPPORTED
+    # just below the limit the plan passes (and then wants its workspace)
+    assert fwd(lib, H=8, N=(1 << 20) - 8, seg=1, ws=None, wsb=0) == WORKSPACE
+    assert fwd(lib, B=1 << 21, N=1 << 20) == UNSUPPORTED  # 2^41 tokens
+    # the packed form: one segment per sequence, 2^17 sequences x 64 heads
+    cu = DUMMY
+    assert lib.lightning_attn_fwd_varlen(DUMMY, DUMMY, DUMMY, DUMMY, cu, 1 << 17, 64, 1 << 17,
+                                         128, 128, BF16, None, DUMMY, DUMMY, -1, None, 0,
+                                         None) == UNSUPPORTED
+    # the backward shares the plan check
+    assert lib.lightning_attn_bwd(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, None, DUMMY, DUMMY,
+                                  DUMMY, DUMMY, 1, 64, 1 << 17, 128, 128, BF16, 0, 1, DUMMY,
+                                  1 << 62, None) == UNSUPPORTED
+    # decode: one 256-thread workgroup per (sequence, head), at most 2^24 - 1
+    assert lib.lightning_attn_decode(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 18, 64, 128,
+                                     BF16, None) == UNSUPPORTED
+
+
 def test_varlen_rejects_bad_arguments(lib):
     f = lib.lightning_attn_fwd_varlen
     args = [DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 3, 4, 1000, 128, 128, BF16, None, DUMMY, DUMMY, 0,

@@ -1330,6 +1330,31 @@ void prefill_fused_kernel(FusedArgs fa) {
   }
 }
 
+// The head of rank k when heads are ordered by decreasing decay (ties by
+// index), for H <= NT_LOCAL.  Ranks compare the decays' bit patterns, a
+// strict order for any values, so every head has exactly one rank.  Called
+// by every thread of the workgroup; kept out of line so that the caller's
+// register allocation is that of its own loop.
+__device__ __attribute__((noinline)) int head_by_decay_rank(const float *decay, int H, int k) {
+  __shared__ unsigned lam_bits[NT_LOCAL];
+  __shared__ int ranked;
+  const int tid = threadIdx.x;
+  if (tid < H) lam_bits[tid] = __float_as_uint(decay[tid]);
+  if (tid == 0) ranked = k;
+  __syncthreads();
+  if (tid < H) {
+    const unsigned x = lam_bits[tid];
+    int rank = 0;
+    for (int j = 0; j < H; ++j) {
+      const unsigned y = lam_bits[j];
+      rank += (y > x || (y == x && j < tid)) ? 1 : 0;
+    }
+    if (rank == k) ranked = tid;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(ranked);
+}
+
 // Phase A: the local state of each segment's last piece, from zero:
 //   L_s = sum_{c in [ps, b)} lambda^(b-1-c) k_c^T v_c, one decayed MFMA sum.
 // Chunks before first_weighted(ps, b) carry exactly zero weight and are left
@@ -1342,12 +1367,13 @@ void prefill_fused_kernel(FusedArgs fa) {
 // Small workgroups (4 waves, 32 KB of LDS, two chunks in flight) several to
 // a CU hide one another's load and arithmetic latency.
 // Grid: (nseg - 1) * r_split * H workgroups (the last segment hands no
-// state on), items heads fastest, segments in reverse: the K/V read last are
-// the first segments', which the output pass reads first (Infinity Cache);
-// items spread over the XCDs by xcd_spread (a head's pieces are long or
-// short with its decay).
-// (Ordering the grid by decreasing decay, so that the long pieces of slowly
-// decaying heads start first, measured slower.)
+// state on), piece-major from the last piece down; within a piece index
+// heads fastest, segments in reverse (the K/V read last are the first
+// segments', which the output pass reads first: Infinity Cache), except the
+// first pieces, which go slowest head first (below); items spread over the
+// XCDs by xcd_spread (a head's pieces are long or short with its decay).
+// (Ordering the whole grid by decreasing decay, before the piece-major
+// order, measured slower.)
 // Wave u owns state rows 32u..32u+31.
 // CH: channel-wise decay (p.chdecay): row c's K values are scaled by their
 // channel's alpha_i^(x1-1-c) on the way into LDS and the update runs with
@@ -1368,11 +1394,25 @@ void local_state_kernel(FwdArgs p) {
   // go out first, and every head's first piece -- among them the short
   // single pieces of fast heads -- last, where they fill the gaps of the
   // final round instead of starting a round of long pieces of their own.
+  // Among the first pieces the slowest heads go first (longest first), so
+  // that the shortest are the very last: 3-7% off the pass at 16-64 heads of
+  // 131K-512K tokens, level at 8 heads x 1M tokens and at the 64-head
+  // 32K-token layer.
   const int item = xcd_spread((int)blockIdx.x, (int)gridDim.x);
   const int per_r = (p.nseg - 1) * H;
   const int rr = item / per_r, rem = item - rr * per_r;
-  const int idx = rem / H, h = rem - idx * H;
-  const int s = p.nseg - 2 - idx, r = R - 1 - rr;
+  const int r = R - 1 - rr;
+  int idx = rem / H, h = rem - idx * H;
+  if (!CH && r == 0 && H <= NT_LOCAL) {
+    // The first pieces, slowest heads first (segments fastest): a slowly
+    // decaying head's first piece is as long as its others, a fast head's
+    // single piece short.  (The channel-wise pass would need every channel's
+    // decay to rank a head; it keeps the plain order.)
+    const int k = rem / (p.nseg - 1);
+    idx = rem - k * (p.nseg - 1);
+    h = head_by_decay_rank(p.decay, H, k);
+  }
+  const int s = p.nseg - 2 - idx;
   float l2max = 0.f, l2f[8];  // channel-wise: slowest channel, and this thread's 8 channels
   if constexpr (CH) {
     const float *al = p.chdecay + (int64_t)h * D;

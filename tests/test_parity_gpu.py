@@ -144,6 +144,15 @@ def test_decay_one_across_segments(d, dtype, prefill_path):
                  lam=[1.0, 0.9, 1.0])
 
 
+def test_tied_decays_across_heads(prefill_path):
+    """The local-state pass hands out the heads' first pieces in order of
+    decreasing decay, ties broken by head index: heads with equal decays
+    (three groups of four here, several segments and pieces each) must each
+    still get every piece computed exactly once."""
+    run_fwd_case(1, 12, 20000, 128, "bf16", seed=71, seg=4096, with_init=True,
+                 lam=[0.99] * 4 + [0.9] * 4 + [0.999] * 4)
+
+
 def test_initial_state_bf16(prefill_path):
     run_fwd_case(1, 4, 2048, 128, "bf16", seed=50, with_init=True, seg=512)
     run_fwd_case(2, 40, 1500, 128, "bf16", seed=51, with_init=True)

@@ -572,6 +572,9 @@ def bench_serving(la, inputs, reps=200, P=50):
     for b in (64, 32):
         variants += [("prefill_only_block%d" % b, prefill, b),
                      ("one_packed_prefill_block%d" % b, one_varlen, b)]
+    # the level the library picks from the mean input length (LA_BLOCK_AUTO)
+    variants += [("prefill_only_block_auto", prefill, la.LA_BLOCK_AUTO),
+                 ("one_packed_prefill_block_auto", one_varlen, la.LA_BLOCK_AUTO)]
     for name, fn, b in variants:
         blk[0] = b
         for _ in range(5):  # warm-up (and lazy initialisation) outside the capture
@@ -603,6 +606,53 @@ def bench_serving(la, inputs, reps=200, P=50):
         del g
     blk[0] = 128
     dstate.copy_(dstate0)
+    if P == 50:
+        res["block_levels"] = bench_block_levels(la, inputs)
+    return res
+
+
+def bench_block_levels(la, inputs, S=32, reps=50):
+    """Packed prefill of S equal sequences (64 heads, prefix states, one
+    segment per sequence) at each block level, by sequence length: graph
+    replays, microseconds per call.  The measurement behind the levels
+    LA_BLOCK_AUTO picks from the mean length."""
+    import torch
+    dev = torch.device("cuda:0")
+    H, d = 64, 128
+    decay = torch.from_numpy(inputs.decay_schedule(H)).to(dev)
+    init = inputs.device_state((S, H, d, d), 411, device=dev)
+    fin = torch.empty_like(init)
+    res = {"workload": "%d sequences x L tokens, H64, from prefix states" % S,
+           "unit": "us per call (graph)"}
+    for L in (8, 24, 32, 48, 64, 96, 128, 192):
+        cu = torch.from_numpy(inputs.cu_seqlens([L] * S)).to(dev)
+        q, k, v = inputs.device_qkv((H, S * L, d), 412 + L, "bf16", device=dev)
+        out = torch.empty_like(q)
+        row = {}
+        for b in (32, 64, 128, la.LA_BLOCK_AUTO):
+            def fn():
+                la.lightning_attn_fwd_varlen(q, k, v, decay, cu, init_states=init, out=out,
+                                             final_states=fin,
+                                             segment_tokens=la.LA_SEGMENT_PER_SEQUENCE, block=b)
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            for _ in range(10):
+                g.replay()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                g.replay()
+            e.record()
+            torch.cuda.synchronize()
+            row["auto" if b == la.LA_BLOCK_AUTO else str(b)] = round(
+                s.elapsed_time(e) * 1e3 / reps, 2)
+            del g
+        res["L%d" % L] = row
     return res
 
 

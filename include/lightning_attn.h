@@ -79,7 +79,8 @@ extern "C" {
 typedef enum {
   LA_OK = 0,
   LA_ERR_INVALID_ARG = 1,  /* NULL pointer where data is needed, negative size */
-  LA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, block not in {16..256}, dtype */
+  LA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, block not LA_BLOCK_AUTO or one of
+                              16, 32, 64, 128, 256, dtype */
   LA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than *_workspace_size */
   LA_ERR_HIP = 4,          /* a HIP launch reported an error */
   LA_STATUS_FORCE_INT32 = 0x7fffffff
@@ -94,6 +95,15 @@ typedef enum { LA_FP32 = 0, LA_BF16 = 1, LA_DTYPE_FORCE_INT32 = 0x7fffffff } la_
  * sequences (serving), whose cost is the launch chain, not the arithmetic;
  * a long sequence is then walked by a single workgroup per head. */
 enum { LA_SEGMENT_PER_SEQUENCE = -1 };
+
+/* block value of every entry point that takes one: the library picks the
+ * level from the mean input length of the call, as the MiniMax-01 report's
+ * multi-level padding (section 3.3.3) picks 32, 64, 128 or 256 by length.
+ * The mean is N for fixed-length calls and ceil(total_N / num_seqs) for
+ * packed ones (both known on the host): at most 32 tokens -> block 32, at
+ * most 64 -> 64, longer -> 128.  Deterministic for given sizes, and the
+ * workspace size queries resolve it the same way. */
+enum { LA_BLOCK_AUTO = 0 };
 
 /* Memory layout of q, k, v and out for the *_layout entry points (the other
  * prefill entry points take LA_HEAD_MAJOR).  LA_TOKEN_MAJOR is the layout a
@@ -125,7 +135,8 @@ const char *lightning_attn_last_hip_error(void);
  *   q, k, v, out : [B][H][N][d] of `dt`.
  *   decay        : [H] float32.
  *   block        : block (chunk) length of the blockwise form, one of
- *                  16, 32, 64, 128, 256.  Any block length gives the same
+ *                  16, 32, 64, 128, 256, or LA_BLOCK_AUTO (the level from
+ *                  the mean input length).  Any block length gives the same
  *                  result up to rounding (K3 notes, CP for linear
  *                  attention).  It chooses the kernel the way the MiniMax-01
  *                  report's multi-level padding (section 3.3.3) chooses a

@@ -53,7 +53,7 @@ __all__ = ["lightning_attn_fwd", "lightning_attn_fwd_timed", "lightning_attn_fwd
            "lightning_attn_varlen_saved_states_size", "lightning_attn_fwd_varlen_save",
            "lightning_attn_bwd_varlen_saved", "lightning_attn_fwd_chdecay_varlen",
            "lightning_attn_fwd_chdecay_varlen_workspace_size",
-           "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE",
+           "LA_HEAD_MAJOR", "LA_TOKEN_MAJOR", "LA_SEGMENT_PER_SEQUENCE", "LA_BLOCK_AUTO",
            "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_varlen_workspace_size",
            "LightningAttnError", "load_library", "LIB_PATH"]
 
@@ -62,6 +62,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblightnin
 LA_FP32, LA_BF16 = 0, 1
 LA_HEAD_MAJOR, LA_TOKEN_MAJOR = 0, 1  # la_layout
 LA_SEGMENT_PER_SEQUENCE = -1          # segment_tokens: one segment per sequence
+LA_BLOCK_AUTO = 0                     # block: level from the mean input length
 LA_SILU_Q, LA_SILU_K, LA_SILU_V, LA_NORM, LA_GATE = 1, 2, 4, 8, 16  # gated-path flags
 _STATUS = {0: "LA_OK", 1: "LA_ERR_INVALID_ARG", 2: "LA_ERR_UNSUPPORTED", 3: "LA_ERR_WORKSPACE",
            4: "LA_ERR_HIP"}

@@ -24,7 +24,18 @@ using la::bf16;
 
 constexpr int kVersion = 100;    // 0.1.0
 
-bool valid_block(int b) { return b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
+bool valid_block(int b) {
+  return b == LA_BLOCK_AUTO || b == 16 || b == 32 || b == 64 || b == 128 || b == 256;
+}
+
+// LA_BLOCK_AUTO: the block level from the call's mean input length (the
+// MiniMax-01 report's multi-level padding, section 3.3.3, pads each input
+// to the smallest of 32, 64, 128, 256 tokens that holds it).  Levels of 128
+// and 256 run the same kernel, so 128 stands for both.
+int level_block(int block, int64_t mean_len) {
+  if (block != LA_BLOCK_AUTO) return block;
+  return mean_len <= 32 ? 32 : mean_len <= 64 ? 64 : 128;
+}
 bool valid_d(int d) { return d == 64 || d == 128; }
 bool valid_dtype(la_dtype dt) { return dt == LA_FP32 || dt == LA_BF16; }
 
@@ -144,7 +155,7 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
                 bool allow_fused = true, bool ch = false, int block = 128,
                 bool short_ok = false) {
   if (segment_tokens == kSegPerSeq) segment_tokens = N;  // N == 0: automatic (nothing to cut)
-  const int T = out_chunk(d, dt, ch, block, short_ok);
+  const int T = out_chunk(d, dt, ch, level_block(block, N), short_ok);
   Plan p{N, B, false, false, 1, 0, T};
   const int64_t total = (int64_t)B * N;
   if (total == 0) {
@@ -183,7 +194,9 @@ Plan plan_fixed(int B, int H, int64_t N, int d, la_dtype dt, int64_t segment_tok
 Plan plan_varlen(int num_seqs, int H, int64_t total, int d, la_dtype dt,
                  int64_t segment_tokens, bool allow_fused = true, bool ch = false,
                  int block = 128, bool short_ok = false) {
-  const int T = out_chunk(d, dt, ch, block, short_ok);
+  const int T = out_chunk(d, dt, ch,
+                          level_block(block, num_seqs > 0 ? ceil_div(total, num_seqs) : total),
+                          short_ok);
   if (segment_tokens == kSegPerSeq) return Plan{0, num_seqs, false, false, 1, 0, T};
   Plan p{1, 0, true, false, 1, 0, T};
   if (total == 0) return p;

@@ -83,6 +83,7 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, d=96) == UNSUPPORTED
     assert fwd(lib, d=256) == UNSUPPORTED
     assert fwd(lib, block=48) == UNSUPPORTED
+    assert fwd(lib, block=-1) == UNSUPPORTED
     assert fwd(lib, block=512) == UNSUPPORTED
     assert fwd(lib, dt=7) == UNSUPPORTED
     assert fwd(lib, B=-1) == INVALID
@@ -113,6 +114,27 @@ def test_fwd_workspace_checks(lib):
     n = lib.lightning_attn_fwd_workspace_size(1, 2, 1000, 64, 64, FP32, 256)
     assert n == 4 * 2 * 64 * 64 * 4
     assert lib.lightning_attn_fwd_workspace_size(1, 2, 1000, 96, 64, FP32, 256) == 0
+
+
+def test_block_auto_resolves_by_mean_length(lib):
+    """LA_BLOCK_AUTO (0) takes the level the mean input length falls in
+    (MiniMax-01 report, section 3.3.3, multi-level padding to 32/64/128/256):
+    the workspace size query, which runs the same plan as the call, must give
+    the chosen level's figure, and the levels must differ here for that to
+    say anything."""
+    fs, vs = lib.lightning_attn_fwd_workspace_size, lib.lightning_attn_fwd_varlen_workspace_size
+    # fixed length: B=1, H=4, N = mean
+    for N, level in ((20, 32), (32, 32), (33, 64), (64, 64), (65, 128), (3000, 128)):
+        assert fs(1, 4, N, 128, 0, BF16, 0) == fs(1, 4, N, 128, level, BF16, 0), N
+    assert fs(1, 4, 3000, 128, 32, BF16, 0) != fs(1, 4, 3000, 128, 128, BF16, 0)
+    # packed: mean = ceil(total / num_seqs)
+    for S, total, level in ((20, 118, 32), (20, 640, 32), (20, 641, 64), (20, 1280, 64),
+                            (20, 1281, 128), (20, 2000, 128), (20, 4114, 128)):
+        assert vs(S, 64, total, 128, 0, BF16, 0) == vs(S, 64, total, 128, level, BF16, 0), total
+    assert vs(20, 64, 2000, 128, 32, BF16, 0) != vs(20, 64, 2000, 128, 128, BF16, 0)
+    # float32 has one kernel for every level: auto is accepted there too
+    assert fs(1, 2, 1000, 64, 0, FP32, 256) == fs(1, 2, 1000, 64, 64, FP32, 256)
+    assert fwd(lib, block=0, ws=None, wsb=0) in (OK, WORKSPACE)
 
 
 def test_launch_size_limits(lib):

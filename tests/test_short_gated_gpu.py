@@ -131,6 +131,58 @@ def test_block_selects_the_kernel():
         assert rel_err(host(o), o_ref) <= TOL and rel_err(host(f), f_ref) <= TOL, b
 
 
+@pytest.mark.parametrize("N,level", [(20, 32), (50, 64), (64, 64), (300, 128)])
+def test_block_auto_fixed(N, level):
+    """LA_BLOCK_AUTO on a fixed-length call runs the level its length falls
+    in (multi-level padding by input length): bit-identical to that level,
+    and within the bar against the oracle."""
+    torch = torch_mod()
+    B, H, d = 3, len(LAMS), 128
+    say("case block auto fixed N=%d level=%d" % (N, level))
+    tq, tk, tv = inputs.device_qkv((B, H, N, d), 840 + N, "bf16")
+    lam = torch.from_numpy(np.asarray(LAMS, np.float32)).cuda()
+    init = dev(inputs.host_state((B, H, d, d), 841), False)
+    oa, fa = la.lightning_attn_fwd(tq, tk, tv, lam, block=la.LA_BLOCK_AUTO, init_state=init)
+    ol, fl = la.lightning_attn_fwd(tq, tk, tv, lam, block=level, init_state=init)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ol) and torch.equal(fa, fl)
+    o_ref, f_ref, _ = oracle.fwd(host(tq), host(tk), host(tv), np.asarray(LAMS, np.float32),
+                                 init=host(init))
+    assert rel_err(host(oa), o_ref) <= TOL and rel_err(host(fa), f_ref) <= TOL
+
+
+@pytest.mark.parametrize("lens,level", [([50, 50] + [1] * 18, 32), ([40] * 10 + [100] * 2, 64),
+                                        ([2048, 2048] + [1] * 18, 128)])
+def test_block_auto_varlen(lens, level):
+    """LA_BLOCK_AUTO on packed batches (mean length = ceil(total / sequences)):
+    the serving mix of 2 x 50 + 18 x 1 tokens takes block 32, a mean of 50
+    takes 64, 2 x 2048 + 18 x 1 takes 128; bit-identical to that level with
+    initial states and one segment per sequence, within the bar against the
+    oracle."""
+    torch = torch_mod()
+    H, d = len(LAMS), 128
+    cu = inputs.cu_seqlens(lens)
+    total = int(cu[-1])
+    say("case block auto varlen total=%d seqs=%d level=%d" % (total, len(lens), level))
+    q, k, v = inputs.host_qkv((H, total, d), 850 + level, dtype="bf16")
+    lam = np.asarray(LAMS, np.float32)
+    init = inputs.host_state((len(lens), H, d, d), 851)
+    args = (dev(q), dev(k), dev(v), dev(lam, False), dev(cu, False))
+    res = {}
+    for b in (la.LA_BLOCK_AUTO, level):
+        for seg in (0, la.LA_SEGMENT_PER_SEQUENCE):
+            res[b, seg] = la.lightning_attn_fwd_varlen(*args, block=b,
+                                                       init_states=dev(init, False),
+                                                       segment_tokens=seg)
+    torch.cuda.synchronize()
+    o_ref, f_ref, _ = oracle.fwd_varlen(q, k, v, lam, cu, init=init)
+    for seg in (0, la.LA_SEGMENT_PER_SEQUENCE):
+        oa, fa = res[la.LA_BLOCK_AUTO, seg]
+        ol, fl = res[level, seg]
+        assert torch.equal(oa, ol) and torch.equal(fa, fl), seg
+        assert rel_err(host(oa), o_ref) <= TOL and rel_err(host(fa), f_ref) <= TOL, seg
+
+
 def test_short_deterministic():
     torch = torch_mod()
     tq, tk, tv = inputs.device_qkv((1, 8, 4096, 128), 830, "bf16")

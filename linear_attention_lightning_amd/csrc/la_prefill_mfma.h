@@ -659,13 +659,40 @@ __device__ __forceinline__ void rms_rows(f32x4 (&acc)[2][8], float eps) {
 // the diagonal), then O^T += V^T P^T with V read in the same key order.
 // Ks, Vs: LDS addresses of the chunk's K and V tiles; kq, vq: this lane's
 // tile offsets (see output_loop).
+// Masked, decayed scores of one 32-key step as the B operand of V^T P^T:
+// p0 holds keys 32 kp + 4 G + r, p1 keys 32 kp + 16 + 4 G + r (r = 0..3) of
+// query row `row`; n0 = row - (32 kp + 4 G).  Weight lambda^(row - key),
+// zero above the diagonal.
+template <bool FAST>
+__device__ __forceinline__ bf16x8 decay_mask(const f32x4 &p0, const f32x4 &p1, int n0,
+                                             const Decay &dc) {
+  const float l2 = dc.l2;
+  const int n1 = n0 - 16;
+  float pw[8];
+  if constexpr (FAST) {
+    const float e0 = fast_exp2((float)(n0 - 3) * l2), e1 = fast_exp2((float)(n1 - 3) * l2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pw[r] = (n0 >= r) ? p0[r] * (e0 * dc.tail[4 + r]) : 0.f;
+      pw[4 + r] = (n1 >= r) ? p1[r] * (e1 * dc.tail[4 + r]) : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pw[r] = (n0 >= r) ? p0[r] * fast_exp2((float)(n0 - r) * l2) : 0.f;
+      pw[4 + r] = (n1 >= r) ? p1[r] * fast_exp2((float)(n1 - r) * l2) : 0.f;
+    }
+  }
+  return cvt8(pw);
+}
+
 template <bool FAST, int BI>
 __device__ __forceinline__ void intra_block(f32x4 (&acc)[2][8], const u32x4 (&qf)[2][4],
                                             unsigned Ks, unsigned Vs, unsigned kq, unsigned vq,
-                                            int i16, int G, int rb, const Decay &dc) {
-  const float l2 = dc.l2;
+                                            int i16, int G, int rb, const Decay &dc,
+                                            int kp0 = 0) {
   const int row = 16 * rb + i16;
-  for (int kp = 0; kp <= (rb >> 1); ++kp) {
+  for (int kp = kp0; kp <= (rb >> 1); ++kp) {
     const unsigned kb = Ks + 32 * kp * KV_ROW + kq;
     f32x4 p0 = {}, p1 = {};
 #pragma unroll
@@ -673,23 +700,7 @@ __device__ __forceinline__ void intra_block(f32x4 (&acc)[2][8], const u32x4 (&qf
       p0 = mma16(lds_ld<bf16x8>(kb ^ (ks << 6)), as_bf16x8(qf[BI][ks]), p0);
       p1 = mma16(lds_ld<bf16x8>((kb ^ (ks << 6)) + 16 * KV_ROW), as_bf16x8(qf[BI][ks]), p1);
     }
-    const int n0 = row - (32 * kp + 4 * G), n1 = n0 - 16;
-    float pw[8];
-    if constexpr (FAST) {
-      const float e0 = fast_exp2((float)(n0 - 3) * l2), e1 = fast_exp2((float)(n1 - 3) * l2);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pw[r] = (n0 >= r) ? p0[r] * (e0 * dc.tail[4 + r]) : 0.f;
-        pw[4 + r] = (n1 >= r) ? p1[r] * (e1 * dc.tail[4 + r]) : 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pw[r] = (n0 >= r) ? p0[r] * fast_exp2((float)(n0 - r) * l2) : 0.f;
-        pw[4 + r] = (n1 >= r) ? p1[r] * fast_exp2((float)(n1 - r) * l2) : 0.f;
-      }
-    }
-    const bf16x8 pb = cvt8(pw);
+    const bf16x8 pb = decay_mask<FAST>(p0, p1, row - (32 * kp + 4 * G), dc);
     const unsigned vb = Vs + 32 * kp * KV_ROW + vq;
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) {
@@ -697,6 +708,45 @@ __device__ __forceinline__ void intra_block(f32x4 (&acc)[2][8], const u32x4 (&qf
       acc[BI][jt] = mma16(tr_read8u(va, va + 16 * KV_ROW), pb, acc[BI][jt]);
     }
   }
+}
+
+// Both query blocks of an output wave, w and 7 - w: the key steps of block w
+// are the first steps of block 7 - w, so those steps read each K and V
+// fragment once for both blocks (two independent product chains per
+// fragment); block 7 - w then runs its remaining steps alone.  mid() runs
+// between the two parts, once block w's Q^T fragments are spent.
+template <bool FAST, typename Mid>
+__device__ __forceinline__ void intra_pair(f32x4 (&acc)[2][8], const u32x4 (&qf)[2][4],
+                                           unsigned Ks, unsigned Vs, unsigned kq, unsigned vq,
+                                           int i16, int G, int w, const Decay &dc,
+                                           const Mid &mid) {
+  const int row0 = 16 * w + i16, row1 = 16 * (7 - w) + i16;
+  for (int kp = 0; kp <= (w >> 1); ++kp) {
+    const unsigned kb = Ks + 32 * kp * KV_ROW + kq;
+    f32x4 a0 = {}, a1 = {}, b0 = {}, b1 = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 k0 = lds_ld<bf16x8>(kb ^ (ks << 6));
+      const bf16x8 k1 = lds_ld<bf16x8>((kb ^ (ks << 6)) + 16 * KV_ROW);
+      a0 = mma16(k0, as_bf16x8(qf[0][ks]), a0);
+      a1 = mma16(k1, as_bf16x8(qf[0][ks]), a1);
+      b0 = mma16(k0, as_bf16x8(qf[1][ks]), b0);
+      b1 = mma16(k1, as_bf16x8(qf[1][ks]), b1);
+    }
+    const int n0 = -(32 * kp + 4 * G);
+    const bf16x8 pa = decay_mask<FAST>(a0, a1, row0 + n0, dc);
+    const bf16x8 pb = decay_mask<FAST>(b0, b1, row1 + n0, dc);
+    const unsigned vb = Vs + 32 * kp * KV_ROW + vq;
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      const unsigned va = vb ^ (jt << 5);
+      const bf16x8 vf = tr_read8u(va, va + 16 * KV_ROW);
+      acc[0][jt] = mma16(vf, pa, acc[0][jt]);
+      acc[1][jt] = mma16(vf, pb, acc[1][jt]);
+    }
+  }
+  mid();
+  intra_block<FAST, 1>(acc, qf, Ks, Vs, kq, vq, i16, G, 7 - w, dc, (w >> 1) + 1);
 }
 
 // Stages this output wave's accumulators (acc[bi][jt] register r holds
@@ -772,15 +822,15 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
       // fragments are spent (keeps one 16-register set fewer alive).
       if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 0, qn[0], o);
       inter_term(acc, STs + kq, qf, a_row);
-      intra_block<FAST, 0>(acc, qf, Ks, Vs, kq, vq, i16, G, w, dc);
-      if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 1, qn[1], o);
-      if constexpr (EPI) {
-        // (the scheduling barrier keeps the gate loads out of the products
-        // above, where their registers would be live)
-        __builtin_amdgcn_sched_barrier(0);
-        if (ep.gate) issue_gate_loads(p, h, cur, ep.gr, o);
-      }
-      intra_block<FAST, 1>(acc, qf, Ks, Vs, kq, vq, i16, G, 7 - w, dc);
+      intra_pair<FAST>(acc, qf, Ks, Vs, kq, vq, i16, G, w, dc, [&] {
+        if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 1, qn[1], o);
+        if constexpr (EPI) {
+          // (the scheduling barrier keeps the gate loads out of the products
+          // above, where their registers would be live)
+          __builtin_amdgcn_sched_barrier(0);
+          if (ep.gate) issue_gate_loads(p, h, cur, ep.gr, o);
+        }
+      });
       if constexpr (EPI) {
         if (p.flags & GF_NORM) rms_rows(acc, p.eps);
       }
@@ -1028,9 +1078,8 @@ __device__ __forceinline__ void dkdv_output_loop(const FwdArgs &pv, const FwdArg
         a_row[bi] = fast_exp2((float)(16 * o.qblock(bi) + i16 + 1) * l2);
       issue_q_loads<REV>(pk, h, cur, 0, qn[0], o);
       inter_term(acc, STs + kq, qf, a_row);
-      intra_block<FAST, 0>(acc, qf, Ks, Vs, kq, vq, i16, G, w, dc);
-      issue_q_loads<REV>(pk, h, cur, 1, qn[1], o);
-      intra_block<FAST, 1>(acc, qf, Ks, Vs, kq, vq, i16, G, 7 - w, dc);
+      intra_pair<FAST>(acc, qf, Ks, Vs, kq, vq, i16, G, w, dc,
+                       [&] { issue_q_loads<REV>(pk, h, cur, 1, qn[1], o); });
     }
     {
       const OutLane o(ln.lane, w);
@@ -1055,9 +1104,9 @@ __device__ __forceinline__ void dkdv_output_loop(const FwdArgs &pv, const FwdArg
         a_row[bi] = fast_exp2((float)(16 * o.qblock(bi) + i16 + 1) * l2);
       if (nxt.valid) issue_q_loads<REV>(pv, h, nxt, 0, qn[0], o);
       inter_term_tr(acc, t0, t1, qf, a_row);
-      intra_block<FAST, 0>(acc, qf, Vs, Ks, kq, vq, i16, G, w, dc);
-      if (nxt.valid) issue_q_loads<REV>(pv, h, nxt, 1, qn[1], o);
-      intra_block<FAST, 1>(acc, qf, Vs, Ks, kq, vq, i16, G, 7 - w, dc);
+      intra_pair<FAST>(acc, qf, Vs, Ks, kq, vq, i16, G, w, dc, [&] {
+        if (nxt.valid) issue_q_loads<REV>(pv, h, nxt, 1, qn[1], o);
+      });
     }
     __syncthreads();  // B: this chunk's tile and G^T reads are done
     {

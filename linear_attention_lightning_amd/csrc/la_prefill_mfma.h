@@ -45,6 +45,24 @@
 namespace la {
 namespace mfma {
 
+// Phase timing of the chunk kernel (built only with -DLA_PHASE_PROBE, by
+// phase_probe.py; the library itself has no such code): lane 0 of output
+// wave 0 and of state wave 4 records the shader clock (s_memtime) at the
+// barriers and phase ends of each chunk, for the first 256 workgroups and
+// 64 chunks of a launch, at [workgroup][chunk][slot].
+#ifdef LA_PHASE_PROBE
+__device__ unsigned long long g_phase_probe[256 * 64 * 16];
+#endif
+__device__ __forceinline__ void phase_mark(bool on, int ci, int slot, int lane) {
+#ifdef LA_PHASE_PROBE
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  const int bid = blockIdx.x;
+  if (on && lane == 0 && bid < 256 && ci < 64) g_phase_probe[(bid * 64 + ci) * 16 + slot] = t;
+#else
+  (void)on, (void)ci, (void)slot, (void)lane;
+#endif
+}
+
 constexpr int D = 128;
 constexpr int T = 128;           // tokens per chunk
 constexpr int NT = 512;          // threads per workgroup of the chunk kernel (8 waves)
@@ -785,6 +803,8 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
   f32x4 acc[2][8];
   u32x4 qf[2][4];
   int buf = 0;
+  int ci = 0;  // chunk count (phase marks only)
+  const bool pm = !SNAP && !REV && !EPI && w == 0;
   Epi ep;
   if constexpr (EPI) {
     // this lane's 8 channels 8 i16 .. of the weight, for the whole walk
@@ -799,6 +819,7 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
     const Cursor nxt = next_chunk<SNAP>(m, cur, b, T);
     const unsigned Ks = lds_u32(smem + buf * LDS_KV), Vs = Ks + LDS_K;
     __syncthreads();  // A: this chunk's K/V and entering S^T are in LDS
+    phase_mark(pm, ci, 0, ln.lane);
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -822,7 +843,9 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
       // fragments are spent (keeps one 16-register set fewer alive).
       if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 0, qn[0], o);
       inter_term(acc, STs + kq, qf, a_row);
+      phase_mark(pm, ci, 1, ln.lane);
       intra_pair<FAST>(acc, qf, Ks, Vs, kq, vq, i16, G, w, dc, [&] {
+        phase_mark(pm, ci, 2, ln.lane);
         if (nxt.valid) issue_q_loads<REV>(p, h, nxt, 1, qn[1], o);
         if constexpr (EPI) {
           // (the scheduling barrier keeps the gate loads out of the products
@@ -831,11 +854,13 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
           if (ep.gate) issue_gate_loads(p, h, cur, ep.gr, o);
         }
       });
+      phase_mark(pm, ci, 3, ln.lane);
       if constexpr (EPI) {
         if (p.flags & GF_NORM) rms_rows(acc, p.eps);
       }
     }
     __syncthreads();  // B: this chunk's K/V and S^T reads are done
+    phase_mark(pm, ci, 4, ln.lane);
     {
       // Stage the tile in this wave's rows of the chunk's K tile, then write
       // it back as whole rows.
@@ -843,6 +868,7 @@ __device__ __forceinline__ void output_loop(const FwdArgs &p, int h, int64_t b, 
       stage_rows(acc, Ks, o);
       write_rows<SNAP, REV, EPI>(p, h, cur, Ks, o, &ep);
     }
+    phase_mark(pm, ci++, 5, ln.lane);
     if (!nxt.valid) break;
     cur = nxt;
     buf ^= 1;
@@ -870,6 +896,8 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
   const int w = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane;
   const float l2 = dc.l2;
   int buf = 0;
+  int ci = 0;  // chunk count (phase marks only)
+  const bool pm = !SNAP && !REV && !EPI && !MID && w == 0;
   // SiLU in place on this wave's rows 32 w .. 32 w + 31 of a K or V tile
   // (elementwise, so the swizzle does not matter).
   const auto silu_rows = [&](char *tile) {
@@ -896,6 +924,7 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
     char *Ks = smem + buf * LDS_KV, *Vs = Ks + LDS_K;
     char *Kn = smem + (buf ^ 1) * LDS_KV, *Vn = Kn + LDS_K;
     __syncthreads();  // A: this chunk's K/V and entering S^T are in LDS
+    phase_mark(pm, ci, 8, lane);
     // The next chunk's tiles, one K and one V instruction per update step.
     // (The lane id passes through an empty asm statement at each step, so
     // the per-lane address arithmetic is redone there instead of sixteen
@@ -936,6 +965,7 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
 #pragma unroll
       for (int k = 0; k < 8; ++k) issue_next(k);
     }
+    phase_mark(pm, ci, 9, lane);
     if constexpr (MID) {
       __syncthreads();  // M: the other buffer's K tile is free again
 #pragma unroll
@@ -949,6 +979,7 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
       }
     }
     __syncthreads();  // B: this chunk's K/V and S^T reads are done
+    phase_mark(pm, ci, 10, lane);
     if (!nxt.valid) break;
     // (A new piece's state load sits in the same block as the S^T write that
     // consumes it, so no path reaches the next chunk with those loads open.)
@@ -963,7 +994,9 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
       }
     }
     write_st(STs, S, w, l32, g);
+    phase_mark(pm, ci, 11, lane);
     vm_wait<0>();  // the next chunk's tiles have landed
+    phase_mark(pm, ci++, 12, lane);
     cur = nxt;
     buf ^= 1;
   }

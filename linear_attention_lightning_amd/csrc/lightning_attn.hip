@@ -1409,3 +1409,18 @@ la_status lightning_attn_fwd_varlen_gated(const void *q, const void *k, const vo
 }
 
 }  // extern "C"
+
+#ifdef LA_PHASE_PROBE
+// The phase-timing build's two extra entry points (not in the public header:
+// the library proper is built without them).
+extern "C" int lightning_attn_phase_probe_copy(void *dst, size_t bytes) {
+  if (bytes > sizeof(la::mfma::g_phase_probe)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(la::mfma::g_phase_probe), bytes, 0,
+                                  hipMemcpyDeviceToHost);
+}
+extern "C" int lightning_attn_phase_probe_clear(void) {
+  static const unsigned long long zeros[256 * 64 * 16] = {};
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(la::mfma::g_phase_probe), zeros, sizeof(zeros), 0,
+                                hipMemcpyHostToDevice);
+}
+#endif

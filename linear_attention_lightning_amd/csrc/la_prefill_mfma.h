@@ -50,8 +50,11 @@ namespace mfma {
 // wave 0 and of state wave 4 records the shader clock (s_memtime) at the
 // barriers and phase ends of each chunk, for the first 256 workgroups and
 // 64 chunks of a launch, at [workgroup][chunk][slot].
+// The local-state pass likewise: thread 0 of each of the first 1024
+// workgroups, at the steps of its first 40 chunks, at [workgroup][chunk][slot].
 #ifdef LA_PHASE_PROBE
 __device__ unsigned long long g_phase_probe[256 * 64 * 16];
+__device__ unsigned long long g_phase_probe_local[1024 * 40 * 4];
 #endif
 __device__ __forceinline__ void phase_mark(bool on, int ci, int slot, int lane) {
 #ifdef LA_PHASE_PROBE
@@ -60,6 +63,15 @@ __device__ __forceinline__ void phase_mark(bool on, int ci, int slot, int lane) 
   if (on && lane == 0 && bid < 256 && ci < 64) g_phase_probe[(bid * 64 + ci) * 16 + slot] = t;
 #else
   (void)on, (void)ci, (void)slot, (void)lane;
+#endif
+}
+__device__ __forceinline__ void phase_mark_local(bool on, int ci, int slot, int tid) {
+#ifdef LA_PHASE_PROBE
+  const unsigned long long t = __builtin_amdgcn_s_memtime();
+  const int bid = blockIdx.x;
+  if (on && tid == 0 && bid < 1024 && ci < 40) g_phase_probe_local[(bid * 40 + ci) * 4 + slot] = t;
+#else
+  (void)on, (void)ci, (void)slot, (void)tid;
 #endif
 }
 
@@ -1545,8 +1557,11 @@ void local_state_kernel(FwdArgs p) {
   };
   // Sums the chunk at t0 held in register set sl, then reloads that set with
   // the chunk two ahead.
+  int ci = 0;  // chunk count (phase marks only)
+  const bool pm = !CH && !SILU;
   auto step = [&](auto slot_c, int64_t t0) {
     constexpr int sl = decltype(slot_c)::value;
+    phase_mark_local(pm, ci, 0, tid);
     if constexpr (CH) {
       // K[c][i] alpha_i^(x1-1-c) for the thread's rows c and channels i
 #pragma unroll
@@ -1571,12 +1586,15 @@ void local_state_kernel(FwdArgs p) {
     store_tile<NT_LOCAL, C_LOCAL>(Ks, pk[sl], tid);
     store_tile<NT_LOCAL, C_LOCAL>(Vs, pv[sl], tid);
     __syncthreads();
+    phase_mark_local(pm, ci, 1, tid);
     issue(slot_c, t0 + 2 * C_LOCAL);
     const int Lc = (int)((x1 - t0) < C_LOCAL ? (x1 - t0) : C_LOCAL);
     // weight of chunk row c: lambda^(x1 - 1 - (t0 + c)); the pipelined update
     // (LDS reads a step ahead) fits the two-waves-per-SIMD register budget
     state_update<C_LOCAL / 16, true>(S, Ks, Vs, Lc, (int)(x1 - 1 - t0), l2, fast, tail, u, lane);
+    phase_mark_local(pm, ci, 2, tid);
     __syncthreads();
+    phase_mark_local(pm, ci++, 3, tid);
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;

@@ -1411,16 +1411,25 @@ la_status lightning_attn_fwd_varlen_gated(const void *q, const void *k, const vo
 }  // extern "C"
 
 #ifdef LA_PHASE_PROBE
-// The phase-timing build's two extra entry points (not in the public header:
+// The phase-timing build's extra entry points (not in the public header:
 // the library proper is built without them).
 extern "C" int lightning_attn_phase_probe_copy(void *dst, size_t bytes) {
   if (bytes > sizeof(la::mfma::g_phase_probe)) return (int)hipErrorInvalidValue;
   return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(la::mfma::g_phase_probe), bytes, 0,
                                   hipMemcpyDeviceToHost);
 }
+extern "C" int lightning_attn_phase_probe_copy_local(void *dst, size_t bytes) {
+  if (bytes > sizeof(la::mfma::g_phase_probe_local)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(la::mfma::g_phase_probe_local), bytes, 0,
+                                  hipMemcpyDeviceToHost);
+}
 extern "C" int lightning_attn_phase_probe_clear(void) {
-  static const unsigned long long zeros[256 * 64 * 16] = {};
-  return (int)hipMemcpyToSymbol(HIP_SYMBOL(la::mfma::g_phase_probe), zeros, sizeof(zeros), 0,
-                                hipMemcpyHostToDevice);
+  static const unsigned long long zeros[256 * 64 * 16] = {};  // the larger of the two records
+  static_assert(sizeof(zeros) >= sizeof(la::mfma::g_phase_probe_local), "record sizes");
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(la::mfma::g_phase_probe), zeros,
+                                   sizeof(la::mfma::g_phase_probe), 0, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return (int)e;
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(la::mfma::g_phase_probe_local), zeros,
+                                sizeof(la::mfma::g_phase_probe_local), 0, hipMemcpyHostToDevice);
 }
 #endif

@@ -14,7 +14,11 @@ the record, runs one more step and prints, per phase, the median and 10th /
 90th percentiles over workgroups and chunks (the first and last chunk of each
 walk left out) in shader-clock cycles.
 
-Phases (one chunk, between barrier A that opens it and the next chunk's A):
+The local-state pass (first 1024 workgroups, first 40 of its 64-token chunks, thread 0) is
+recorded in the same step: chunk start -> tiles stored and first barrier -> state update ->
+second barrier.
+
+Phases of the chunk kernel (one chunk, between barrier A that opens it and the next chunk's A):
   output wave: A -> inter-block term done -> steps shared by both query
   blocks done -> remaining steps done -> B -> rows staged and written -> A
   state wave:  A -> state update done -> B -> S^T published -> next tiles
@@ -35,6 +39,9 @@ OUT_PHASES = [(0, 1, "out: A -> inter-block term"),
               (2, 3, "out: -> remaining key steps (block 7-w)"),
               (3, 4, "out: -> barrier B passed"),
               (4, 5, "out: -> rows staged and written")]
+LOCAL_PHASES = [(0, 1, "local: chunk start -> tiles stored, barrier"),
+                (1, 2, "local: -> state update"),
+                (2, 3, "local: -> second barrier")]
 STATE_PHASES = [(8, 9, "state: A -> state update"),
                 (9, 10, "state: -> barrier B passed"),
                 (10, 11, "state: -> S^T published"),
@@ -60,6 +67,7 @@ def run(warmup):
     if not hasattr(lib, "lightning_attn_phase_probe_copy"):
         raise RuntimeError("the binding had already loaded another library")
     lib.lightning_attn_phase_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.lightning_attn_phase_probe_copy_local.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     B, H, N, d = 1, 64, 32768, 128
     dev = torch.device("cuda:0")
     q, k, v = inputs.device_qkv((B, H, N, d), 3, "bf16", device=dev)
@@ -106,6 +114,23 @@ def run(warmup):
     res["phases"]["state: tiles landed -> next A"] = stats(P[:, 2:63, 8] - P[:, 1:62, 12])
     res["phases"]["chunk period (A to A)"] = stats(P[:, 2:63, 0] - P[:, 1:62, 0])
     res["workgroup_walk_cycles"] = stats(P[:, 63, 5] - P[:, 0, 0])
+    # the local-state pass: workgroups with at least three chunks, chunks from the second on
+    loc = np.zeros(1024 * 40 * 4, np.uint64)
+    if lib.lightning_attn_phase_probe_copy_local(loc.ctypes.data, loc.nbytes) != 0:
+        raise RuntimeError("local-pass phase record could not be read")
+    Q = loc.reshape(1024, 40, 4).astype(np.int64)
+    nch = (Q[:, :, 3] > 0).sum(1)
+    sel = [(w, c) for w in range(1024) for c in range(1, nch[w]) if nch[w] >= 3]
+    lp = {}
+    for a, b, name in LOCAL_PHASES:
+        lp[name] = stats([Q[w, c, b] - Q[w, c, a] for w, c in sel])
+    lp["chunk period"] = stats([Q[w, c, 0] - Q[w, c - 1, 0] for w, c in sel])
+    full = [w for w in range(1024) if nch[w] == nch.max()]
+    res["local_pass"] = {"workgroups_with_work": int((nch > 0).sum()),
+                         "chunks_per_workgroup_max": int(nch.max()),
+                         "workgroups_at_max": len(full),
+                         "walk_cycles_at_max": stats([Q[w, nch[w] - 1, 3] - Q[w, 0, 0] for w in full]),
+                         "phases": lp}
     return res
 
 
@@ -126,6 +151,13 @@ def main():
     st = res["workgroup_walk_cycles"]
     print("%-44s median %7.0f   p10 %7.0f   p90 %7.0f" % ("whole walk of a workgroup", st["median"],
                                                             st["p10"], st["p90"]))
+    lp = res["local_pass"]
+    print("local-state pass: %d workgroups with work, %d walk the most chunks (%d), median walk %.0f cycles"
+          % (lp["workgroups_with_work"], lp["workgroups_at_max"], lp["chunks_per_workgroup_max"],
+             lp["walk_cycles_at_max"]["median"]))
+    for name, st in lp["phases"].items():
+        print("%-44s median %7.0f   p10 %7.0f   p90 %7.0f" % (name, st["median"], st["p10"],
+                                                                st["p90"]))
     if args.json:
         with open(args.json, "w") as f:
             json.dump(res, f, indent=1)

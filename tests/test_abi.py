@@ -134,6 +134,11 @@ def test_block_auto_resolves_by_mean_length(lib):
     assert vs(20, 64, 2000, 128, 32, BF16, 0) != vs(20, 64, 2000, 128, 128, BF16, 0)
     # float32 has one kernel for every level: auto is accepted there too
     assert fs(1, 2, 1000, 64, 0, FP32, 256) == fs(1, 2, 1000, 64, 64, FP32, 256)
+    # entry points whose chunk does not follow the block (backward, training pair,
+    # channel-wise) accept the automatic level and plan as at block 128
+    for q in (lib.lightning_attn_bwd_workspace_size, lib.lightning_attn_saved_states_size,
+              lib.lightning_attn_fwd_chdecay_workspace_size):
+        assert q(1, 64, 32768, 128, 0, BF16, 0) == q(1, 64, 32768, 128, 128, BF16, 0) > 0
     assert fwd(lib, block=0, ws=None, wsb=0) in (OK, WORKSPACE)
 
 

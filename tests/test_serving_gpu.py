@@ -220,7 +220,7 @@ def test_full_varlen_h64_65536_snapshots():
 
 
 def run_mixed_case(prefill_lens, decode_B, H, d, dtype, seed, two_streams=True,
-                   token_major=False, seg=0):
+                   token_major=False, seg=0, block=128):
     """Sequences with prefix states: the prefill part continues len > 1
     prompts from their prefix states, the decode part takes one token for
     each of decode_B others; both against the oracle (packed recurrence from
@@ -245,7 +245,8 @@ def run_mixed_case(prefill_lens, decode_B, H, d, dtype, seed, two_streams=True,
     torch.cuda.synchronize()
     pout, fin, dout = la.lightning_attn_mixed_step(
         tl, (pq, pk, pv), torch.from_numpy(cu).cuda(), (dq, dk, dv), dstate, layout=layout,
-        init_states=torch.from_numpy(P0).cuda(), decode_stream=side, segment_tokens=seg)
+        init_states=torch.from_numpy(P0).cuda(), decode_stream=side, segment_tokens=seg,
+        block=block)
     torch.cuda.synchronize()
     if token_major:
         pout = pout.transpose(0, 1)
@@ -267,6 +268,17 @@ def test_mixed_step_pages_scenario(two_streams, seg):
     one token (the mix of MiniMax-01 report section 3.3.2), at the 64-head
     layer shape."""
     run_mixed_case([50, 50], 18, 64, 128, "bf16", seed=300, two_streams=two_streams, seg=seg)
+
+
+@pytest.mark.parametrize("two_streams", [True, False])
+def test_mixed_step_block_auto(two_streams):
+    """The pages' mix with the prefill part's block level picked from its mean
+    length (LA_BLOCK_AUTO: 2 x 50 tokens -> block 64), and a mix of longer
+    continuations (mean 300 -> block 128)."""
+    run_mixed_case([50, 50], 18, 64, 128, "bf16", seed=305, two_streams=two_streams,
+                   seg=la.LA_SEGMENT_PER_SEQUENCE, block=la.LA_BLOCK_AUTO)
+    run_mixed_case([300, 1, 599], 9, 8, 128, "bf16", seed=306, two_streams=two_streams,
+                   block=la.LA_BLOCK_AUTO)
 
 
 @pytest.mark.parametrize("d,dtype", [(64, "fp32"), (128, "fp32"), (64, "bf16")])

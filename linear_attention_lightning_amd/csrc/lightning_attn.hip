@@ -1424,12 +1424,11 @@ extern "C" int lightning_attn_phase_probe_copy_local(void *dst, size_t bytes) {
                                   hipMemcpyDeviceToHost);
 }
 extern "C" int lightning_attn_phase_probe_clear(void) {
-  static const unsigned long long zeros[256 * 64 * 16] = {};  // the larger of the two records
-  static_assert(sizeof(zeros) >= sizeof(la::mfma::g_phase_probe_local), "record sizes");
-  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(la::mfma::g_phase_probe), zeros,
-                                   sizeof(la::mfma::g_phase_probe), 0, hipMemcpyHostToDevice);
-  if (e != hipSuccess) return (int)e;
-  return (int)hipMemcpyToSymbol(HIP_SYMBOL(la::mfma::g_phase_probe_local), zeros,
-                                sizeof(la::mfma::g_phase_probe_local), 0, hipMemcpyHostToDevice);
+  void *a = nullptr, *b = nullptr;
+  hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(la::mfma::g_phase_probe));
+  if (e == hipSuccess) e = hipGetSymbolAddress(&b, HIP_SYMBOL(la::mfma::g_phase_probe_local));
+  if (e == hipSuccess) e = hipMemset(a, 0, sizeof(la::mfma::g_phase_probe));
+  if (e == hipSuccess) e = hipMemset(b, 0, sizeof(la::mfma::g_phase_probe_local));
+  return (int)e;
 }
 #endif

@@ -1,4 +1,4 @@
-// bf16 prefill on gfx950 MFMA (v_mfma_f32_32x32x16_bf16), d = 128.
+// bf16 prefill on gfx950 MFMA (v_mfma_f32_16x16x32_bf16 and 32x32x16), d = 128.
 //
 // One workgroup owns one (segment, head) and walks it in chunks of at most
 // 128 tokens (MiniMax-01 report, section 2.2.1: left product inside a block,
@@ -7,22 +7,25 @@
 // b_c = lambda^(L-1-c):
 //     O^T = diag(a) (S^T Q^T)  +  V^T ((K Q^T) (.) D^T)
 //     S   = lambda^L S + (diag(b) K)^T V
-// The workgroup has 8 waves in two roles that run side by side:
-//   output waves 0-3: wave w owns query rows 32w..32w+31 of the chunk; its
-//     Q^T fragments come straight from HBM into registers (next chunk's
-//     prefetched during this one); it computes the inter-block term of the
-//     NEXT chunk while the state waves store that chunk's K/V tiles;
-//   state waves 4-7: wave 4+u owns state rows 32u..32u+31 in float32 MFMA
-//     accumulators; they stream K/V tiles HBM -> registers -> LDS one chunk
-//     ahead, update the state, and publish it as bf16 S^T in LDS (written
-//     after the output waves have read the previous one for this chunk's
-//     inter term, read after the end-of-chunk barrier for the next one).
+// The workgroup has 8 waves in two roles that run side by side, with two
+// barriers per chunk: A opens it (its K/V tiles and the S^T of the state
+// entering it are in LDS), B closes it (every read of those is done).
+//   output waves 0-3: wave w owns the 16-row query blocks w and 7 - w (the
+//     same causal work for every wave) and runs 16x16x32 MFMAs; its Q^T
+//     fragments come straight from HBM into registers a chunk ahead.  After
+//     A it computes the inter-block term from the published S^T, then the
+//     intra-block term (the key steps both blocks share read each K and V
+//     fragment once for both); after B it stages its rows in the chunk's
+//     now free K tile and writes them back as whole 256-byte rows.
+//   state waves 4-7: wave 4+u owns state rows 32u..32u+31 in float32
+//     32x32x16 MFMA accumulators.  After A they update the state, issuing
+//     the next chunk's K/V tiles HBM -> LDS by DMA (global_load_lds, no
+//     registers) as they go; after B they publish the new state as bf16 S^T
+//     and wait for the next tiles to land.
 // Everything is computed transposed so the query row is each lane's fixed
 // MFMA column: the K Q^T accumulator (register quads hold 4 consecutive
 // keys) feeds V^T (K Q^T) directly as the B operand, with V read in the same
-// key order by ds_read_b64_tr_b16; a_r is one scalar per lane.  Each output
-// wave stages its 32 x 128 output tile in a private LDS region and writes it
-// back as whole rows (16-byte stores, 8 KB contiguous per wave).
+// key order by ds_read_b64_tr_b16; a_r is one scalar per lane.
 //
 // MFMA 32x32x16 operand layout (lane l, l32 = l % 32, g = l / 32):
 //   A[m][k]: lane holds m = l32, k = 8g .. 8g+7

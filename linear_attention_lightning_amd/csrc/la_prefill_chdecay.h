@@ -62,10 +62,11 @@ __device__ __forceinline__ void ch_load_tiles(ChTiles &t, const FwdArgs &p, int 
 }
 
 // K~ = K (.) alpha^(32 - row) and V into the swizzled LDS tiles; rows >= L
-// are stored as zeros, so they add nothing to any product.  l2f: log2 alpha
-// of this thread's 8 channels.
+// are stored as zeros, so they add nothing to any product.  kf[it][e]:
+// alpha^(32 - row) of this thread's row (ts >> 4) + 16 it and channel e of
+// its 8 channels, the same for every chunk (see ch_tile_factors).
 __device__ __forceinline__ void ch_store_tiles(char *Ks, char *Vs, const ChTiles &t, int L,
-                                               const float (&l2f)[8], int ts) {
+                                               const float (&kf)[4][8], int ts) {
   const int c16 = ts & 15;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -74,11 +75,20 @@ __device__ __forceinline__ void ch_store_tiles(char *Ks, char *Vs, const ChTiles
     const bf16x8 kv = __builtin_bit_cast(bf16x8, t.k[it]);
     float ks[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      ks[e] = live ? (float)kv[e] * fast_exp2((float)(CH_PIVOT - row) * l2f[e]) : 0.f;
+    for (int e = 0; e < 8; ++e) ks[e] = live ? (float)kv[e] * kf[it][e] : 0.f;
     *(bf16x8 *)(Ks + kv_off(row, 16 * c16)) = cvt8(ks);
     *(u32x4 *)(Vs + kv_off(row, 16 * c16)) = live ? t.v[it] : (u32x4){0u, 0u, 0u, 0u};
   }
+}
+
+// The factors of ch_store_tiles: alpha_e^(32 - row) for this thread's rows
+// (ts >> 4) + 16 it and channels (l2f: their log2 alpha).
+__device__ __forceinline__ void ch_tile_factors(float (&kf)[4][8], const float (&l2f)[8], int ts) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      kf[it][e] = fast_exp2((float)(CH_PIVOT - ((ts >> 4) + 16 * it)) * l2f[e]);
 }
 
 // S += (f K~)^T V over the chunk's TC rows, for state rows 32u..32u+31; f is
@@ -151,26 +161,41 @@ void chdecay_chunk_kernel(FwdArgs p) {
     Cursor nxt = next_chunk<false>(m, cur, b, TC);
     ch_issue_q(qn[0], p, h, cur, w, i16, G);
     ch_issue_q(qn[1], p, h, nxt.valid ? nxt : cur, w, i16, G);
+    // The two scalings of this lane's Q features (32 ks + 8 G + e of query
+    // row `row`): alpha^(row+1) for the inter term, alpha^(row-32) for the
+    // intra term.  The same for every chunk, so taken once (after the first
+    // barrier, once l2a is in LDS) instead of 64 exponentials per chunk.
+    float fi[4][8], ft[4][8];
+    bool have_f = false;
     // One chunk: Q of `c` is in set sl; reloads set sl with chunk c + 2.
     // Returns false after the segment's last chunk.
     auto step = [&](auto slot_c, const Cursor &c, const Cursor &n1) -> bool {
       constexpr int sl = decltype(slot_c)::value;
       const Cursor n2 = n1.valid ? next_chunk<false>(m, n1, b, TC) : n1;
       __syncthreads();  // A: K~, V and S^T of this chunk are in LDS
-      // Q scaled twice: alpha^(row+1) for the inter term, alpha^(row-32)
-      // for the intra term.
+      if (!have_f) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const f32x4 la = *(const f32x4 *)(l2a + 32 * ks + 8 * G);
+          const f32x4 lb = *(const f32x4 *)(l2a + 32 * ks + 8 * G + 4);
+          const float l2e[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            fi[ks][e] = fast_exp2((float)(row + 1) * l2e[e]);
+            ft[ks][e] = fast_exp2((float)(row - CH_PIVOT) * l2e[e]);
+          }
+        }
+        have_f = true;
+      }
       bf16x8 qi[4], qt[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 qv = __builtin_bit_cast(bf16x8, qn[sl][ks]);
-        const f32x4 la = *(const f32x4 *)(l2a + 32 * ks + 8 * G);
-        const f32x4 lb = *(const f32x4 *)(l2a + 32 * ks + 8 * G + 4);
-        const float l2e[8] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
         float vi[8], vt[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          vi[e] = (float)qv[e] * fast_exp2((float)(row + 1) * l2e[e]);
-          vt[e] = (float)qv[e] * fast_exp2((float)(row - CH_PIVOT) * l2e[e]);
+          vi[e] = (float)qv[e] * fi[ks][e];
+          vt[e] = (float)qv[e] * ft[ks][e];
         }
         qi[ks] = cvt8(vi);
         qt[ks] = cvt8(vt);
@@ -252,9 +277,10 @@ void chdecay_chunk_kernel(FwdArgs p) {
     }
   } else {
     const int u = ln.w, l32 = ln.l32, g = ln.g, lane = ln.lane, ts = ln.ts;
-    float l2f[8];
+    float l2f[8], kf[4][8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) l2f[e] = log2f(alpha[8 * (ts & 15) + e]);
+    ch_tile_factors(kf, l2f, ts);
     const float l2ch = log2f(alpha[32 * u + l32]);  // this lane's A-operand channel
     float l2row[16];  // accumulator register r: state row 32u + 8(r/4) + 4g + r%4
 #pragma unroll
@@ -269,7 +295,7 @@ void chdecay_chunk_kernel(FwdArgs p) {
     Cursor nxt = next_chunk<false>(m, cur, b, TC);
     ch_load_tiles(t[0], p, h, cur, ts);
     ch_load_tiles(t[1], p, h, nxt.valid ? nxt : cur, ts);
-    ch_store_tiles(Ks, Vs, t[0], (int)(cur.c1 - cur.c0), l2f, ts);
+    ch_store_tiles(Ks, Vs, t[0], (int)(cur.c1 - cur.c0), kf, ts);
     write_st(STs, S, u, l32, g);
     // One chunk: the tiles of c are in LDS and set sl^1 holds chunk n1;
     // set sl (already stored) is reloaded with chunk c + 2.
@@ -301,7 +327,7 @@ void chdecay_chunk_kernel(FwdArgs p) {
         // take the prefetched tiles with it.
         vm_wait<0>();
       }
-      ch_store_tiles(Ks, Vs, t[sl ^ 1], (int)(n1.c1 - n1.c0), l2f, ts);
+      ch_store_tiles(Ks, Vs, t[sl ^ 1], (int)(n1.c1 - n1.c0), kf, ts);
       write_st(STs, S, u, l32, g);
       return true;
     };

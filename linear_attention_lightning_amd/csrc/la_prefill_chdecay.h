@@ -285,6 +285,9 @@ void chdecay_chunk_kernel(FwdArgs p) {
     float l2row[16];  // accumulator register r: state row 32u + 8(r/4) + 4g + r%4
 #pragma unroll
     for (int r = 0; r < 16; ++r) l2row[r] = log2f(alpha[32 * u + 8 * (r >> 2) + 4 * g + (r & 3)]);
+    float gam_full[16];  // alpha^TC of those rows (a whole chunk's state decay)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) gam_full[r] = fast_exp2((float)TC * l2row[r]);
     f32x16 S[4];
     const float *s0 = p.ws ? p.ws + ((int64_t)s * p.r_split * H + h) * DD
                            : (p.init ? p.init + ((int64_t)cur.j * H + h) * DD : nullptr);
@@ -308,13 +311,21 @@ void chdecay_chunk_kernel(FwdArgs p) {
       const bool seq_done = (c.c1 == c.seq_end);
       const bool new_piece = n1.valid && (n1.c0 >= c.pend);
       if ((n1.valid && !new_piece) || (seq_done && p.fin)) {
-        float gam[16];
+        // alpha^L per state row: a whole chunk's factors are taken once
+        if (L == TC) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) gam[r] = fast_exp2((float)L * l2row[r]);
+          for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+            for (int r = 0; r < 16; ++r) S[nt][r] *= gam_full[r];
+        } else {
+          float gam[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) S[nt][r] *= gam[r];
+          for (int r = 0; r < 16; ++r) gam[r] = fast_exp2((float)L * l2row[r]);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[nt][r] *= gam[r];
+        }
         ch_state_update(S, Ks, Vs, fast_exp2((float)(L - 1 - CH_PIVOT) * l2ch), u, lane);
         if (seq_done && p.fin) store_state(p.fin + ((int64_t)c.j * H + h) * DD, S, u, l32, g);
       }

@@ -553,6 +553,34 @@ __device__ __forceinline__ void dma_tile_quad(char *tile, const void *src, const
   lds_dma16(gp, tile + (32 * u + 4 * k) * KV_ROW);
 }
 
+// lds_dma16 with a uniform base (SGPR pair) and a 32-bit lane offset: the
+// address is base + off.  The base is moved to scalar registers explicitly.
+__device__ __forceinline__ void lds_dma16_s(const char *base, unsigned off, const char *lds) {
+  const unsigned a = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(const LA_LDS char *)lds);
+  // (readfirstlane returns int: each half goes through unsigned, or a low
+  // word with bit 31 set would sign-extend over the high word)
+  const uint64_t bb = (uint64_t)(size_t)base;
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(bb >> 32));
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)bb);
+  const uint64_t sb = (hi << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(off), "s"((const char *)(size_t)sb), "s"(a)
+               : "memory", "m0");
+}
+
+// Instruction k of dma_tile_quad for a whole chunk of a plain view (positive
+// row stride, every row of the tile inside the chunk): `base` points at the
+// chunk's first row, row r's 16-byte granules start at byte r * rsb, so a
+// lane's address is one 32-bit offset from a uniform base instead of 64-bit
+// arithmetic per load.
+__device__ __forceinline__ void dma_quad_whole(char *tile, const char *base, int rsb, int u,
+                                               int lane, int k) {
+  const int sub = lane >> 4, pg = lane & 15;
+  const int r = 32 * u + 4 * k + sub;
+  lds_dma16_s(base, (unsigned)(r * rsb + ((pg ^ kv_swz(r)) << 4)), tile + (32 * u + 4 * k) * KV_ROW);
+}
+
 template <bool REV = false>
 __device__ __forceinline__ void dma_tile_rows(char *tile, const void *src, const FwdArgs &p, int h,
                                               const Cursor &c, int u, int lane) {
@@ -913,6 +941,12 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
   int buf = 0;
   int ci = 0;  // chunk count (phase marks only)
   const bool pm = !SNAP && !REV && !EPI && !MID && w == 0;
+  // Forward views without snapshots: a chunk's row r sits at its first row
+  // plus r * rs elements (rs is d or H d), and a whole tile's byte offsets
+  // fit 31 bits for any row stride below 2^23 elements.
+  constexpr bool PLAIN = !SNAP && !REV;
+  const bool plain = PLAIN && m.rs > 0 && m.rs < (int64_t(1) << 23);
+  const int rsb = (int)(m.rs * 2);
   // SiLU in place on this wave's rows 32 w .. 32 w + 31 of a K or V tile
   // (elementwise, so the swizzle does not matter).
   const auto silu_rows = [&](char *tile) {
@@ -944,12 +978,23 @@ __device__ __forceinline__ void state_loop(const FwdArgs &p, int h, int64_t b, C
     // (The lane id passes through an empty asm statement at each step, so
     // the per-lane address arithmetic is redone there instead of sixteen
     // addresses being hoisted out of the update and held in registers.)
+    // A whole chunk of a plain view goes out from uniform row bases with
+    // 32-bit lane offsets (dma_quad_whole).
+    const bool whole = plain && nxt.valid && (nxt.c1 - nxt.c0) == T;
+    const int64_t nrow = whole ? chunk_row_base<REV>(m, h, nxt) + nxt.c0 * m.rs : 0;
+    const char *kbn = (const char *)((const bf16 *)p.k + nrow);
+    const char *vbn = (const char *)((const bf16 *)p.v + nrow);
     const auto issue_next = [&](int k) {
       if (nxt.valid) {
         int ll = lane;
         asm volatile("" : "+v"(ll));
-        dma_tile_quad<REV>(Kn, p.k, p, h, nxt, w, ll, k);
-        dma_tile_quad<REV>(Vn, p.v, p, h, nxt, w, ll, k);
+        if (whole) {
+          dma_quad_whole(Kn, kbn, rsb, w, ll, k);
+          dma_quad_whole(Vn, vbn, rsb, w, ll, k);
+        } else {
+          dma_tile_quad<REV>(Kn, p.k, p, h, nxt, w, ll, k);
+          dma_tile_quad<REV>(Vn, p.v, p, h, nxt, w, ll, k);
+        }
       }
     };
     const bool seq_done = (cur.c1 == cur.seq_end);

@@ -184,6 +184,37 @@ def test_deterministic_bitwise(prefill_path):
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
+@pytest.mark.parametrize("low_word", [0x40000000, 0x80000100, 0xFFFF4000])
+def test_tile_addresses_any_low_word(low_word, prefill_path):
+    """K and V placed so that the low 32 bits of their addresses sit below
+    2^31, at or above it, and 48 KiB under 2^32 (the second 128-token chunk
+    of head 0 then straddles a 4 GiB line).  The tile loads form a 64-bit
+    base plus a 32-bit lane offset, which must neither sign-extend the low
+    word nor wrap at 4 GiB.  The outputs must be bit-identical to the same
+    inputs in ordinary allocations (and within the oracle bar)."""
+    torch = torch_mod()
+    B, H, N, d = 1, 2, 2048, 128
+    (tq, tk, tv), (q, k, v) = dev_inputs((B, H, N, d), 70, "bf16")
+    tl = torch.from_numpy(inputs.decay_schedule(H)).cuda()
+    o_ref, f_ref = la.lightning_attn_fwd(tq, tk, tv, tl)
+    n = tk.numel()
+    pool = torch.empty((1 << 32) + (64 << 20), dtype=torch.uint8, device="cuda")
+    off = (low_word - pool.data_ptr()) % (1 << 32)
+    say("case tile addresses: k at low word %#x (pool offset %d)" % (low_word, off))
+    flat = pool[off:off + 4 * n + 8192].view(torch.bfloat16)
+    pk = flat[:n].view(B, H, N, d)
+    pv = flat[n + 2048:2 * n + 2048].view(B, H, N, d)
+    pk.copy_(tk)
+    pv.copy_(tv)
+    assert pk.data_ptr() & 0xFFFFFFFF == low_word
+    out, fin = la.lightning_attn_fwd(tq, pk, pv, tl)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_ref) and torch.equal(fin, f_ref)
+    o_or, f_or, _ = oracle.fwd(q, k, v, inputs.decay_schedule(H))
+    assert rel_err(host(out), o_or) <= TOL["bf16"] and rel_err(host(fin), f_or) <= TOL["bf16"]
+    del pool, flat, pk, pv
+
+
 # ------------------------------------------------------------------ varlen
 
 
